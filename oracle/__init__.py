@@ -1,0 +1,42 @@
+"""CPU oracle for the INT8 W8A8 attention forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute anything under ``oracle/``; only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with
+the HIP library: no kernels, headers, helpers, tables or pre/post-processing.
+
+The method it defines comes from the "SuperL8" README (the page titled
+"SuperL8 - DP4A FlashAttention-2 and GEMM for Volta GPUs"):
+
+* *Attention kernels* table, row ``attn_int8_fwd``: W8A8 FlashAttention-2
+  forward, causal, GQA/MQA, head dims 32/64/128/256.
+* *Attention kernels* table, row ``attn_varlen_fwd``: variable-length
+  (ragged, non-tile-multiple) prefill.
+* *Supporting kernels* table, row ``quant_rowwise``: symmetric per-row int8
+  quantization.
+* *Quantization* table, rows "Per-row int8" (symmetric, K-smoothing) and
+  "V per-channel / per-token" (V is quantized per token here).
+* *Quick start*: ``attn_int8_fwd(q, k, v, causal=True)`` takes fp16
+  ``q[B,Hq,S,D]``, ``k/v[B,Hkv,S,D]`` and quantizes internally.
+
+Where the page is silent the oracle takes the readings listed in the
+module docstring of :mod:`oracle.attn_ref`.
+
+Pinning status: every public function is pinned by ``tests/test_oracle_pins.py``
+against exact rational arithmetic, brute force, library routines or closed
+forms, except the fp32 rounding of the fp16 output, which only the stated
+tolerance constrains.
+"""
+
+from .attn_ref import (  # noqa: F401
+    SCALE_SIGNIFICAND_BITS,
+    default_softmax_scale,
+    kmean,
+    quant_rows,
+    quantize_qkv,
+    qk_int32,
+    attn_core,
+    attn_int8_fwd,
+    attn_int8_varlen_fwd,
+    attn_exact,
+)

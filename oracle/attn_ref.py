@@ -1,0 +1,231 @@
+"""Plain, slow CPU definition of the INT8 W8A8 attention forward (fp64).
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring.  Imported only by
+tests, the smoke check and the CPU-baseline leg of the benchmark.
+
+What is computed follows the "SuperL8" README: the *Attention kernels* table
+(``attn_int8_fwd``: W8A8 FlashAttention-2, causal, GQA/MQA, head dims
+32/64/128/256; ``attn_varlen_fwd``: ragged prefill), the *Supporting kernels*
+table (``quant_rowwise``: symmetric per-row int8), the *Quantization* table
+("Per-row int8: symmetric, K-smoothing"; "V per-channel / per-token") and the
+*Quick start* call, which takes fp16 q/k/v and quantizes internally.
+
+The page prints no formulas, so each step below is the plainest reading of
+those rows.  Readings taken where the page is silent:
+
+R1  Codes are symmetric: integers in [-127, 127]; -128 is never produced.
+R2  Row scale: ``t = fp32(absmax / 127)`` (IEEE round-to-nearest-even), then
+    rounded *up* to the next value whose significand has 11 bits (the
+    precision of an fp16 number), stored as fp32.  The 11-bit significand
+    lets a consumer fold the V scale into an fp16 softmax weight without
+    rounding when that weight is 1 (the row maximum); rounding up keeps every
+    ``|x| / scale`` at most 127.
+R3  ``code = clamp(rint(fp32(x / scale)), -127, 127)`` with a correctly
+    rounded fp32 division and round-half-to-even.
+R4  An all-zero row gets scale 0 and codes 0.
+R5  K-smoothing subtracts, per (batch, kv head, channel), the mean of K over
+    all tokens of that sequence (future tokens included under the causal
+    mask).  The mean is the exact sum (fp16 values are integer multiples of
+    2^-24), divided in fp64, rounded to fp32; K rows are quantized from the
+    fp32 difference ``fp32(k) - mean``.
+R6  Q and V are quantized per row (per token and head) with the same rule;
+    V is per token, the "per-token" choice of the *Quantization* table.
+R7  Scores are the exact integer dot products of the codes; logits are
+    ``S32 * sq_i * sk_j * softmax_scale``; the softmax scale defaults to
+    ``fp32(1 / sqrt(D))`` and is not folded into Q before quantization.
+R8  Causal means equal query and key lengths and query i sees keys j <= i.
+R9  GQA/MQA: query head h reads kv head ``h // (Hq / Hkv)``.
+R10 Output ``O = softmax(logits) @ (sv * v8)``, exact softmax over the whole
+    row, in fp64 and left unrounded (a GPU result is compared against it).
+R11 Varlen input is packed ``[T, H, D]`` with ``cu_seqlens[nseq + 1]``; every
+    sequence is an independent causal (or full) attention with its own K mean.
+
+Quantization steps are emulated op for op in numpy float32, which is IEEE
+single precision with round-to-nearest-even; everything after the integer
+codes is exact or fp64.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+#: Significand width (implicit bit included) of every row scale, reading R2.
+SCALE_SIGNIFICAND_BITS = 11
+_DROP_BITS = 24 - SCALE_SIGNIFICAND_BITS  # fp32 has a 24-bit significand
+_ROUND_ADD = np.uint32((1 << _DROP_BITS) - 1)
+_ROUND_MASK = np.uint32(0xFFFFFFFF ^ ((1 << _DROP_BITS) - 1))
+
+_ROW_BLOCK = 512  # query rows per block: keeps the [rows, keys] logits small
+
+
+def default_softmax_scale(d: int) -> np.float32:
+    """fp32(1/sqrt(D)), reading R7."""
+    return np.float32(1.0 / np.sqrt(np.float64(d)))
+
+
+def kmean(k16: np.ndarray) -> np.ndarray:
+    """Per-channel mean of K over the token axis (K-smoothing statistic, R5).
+
+    ``k16`` is fp16 ``[..., L, D]`` with L >= 1; returns fp32 ``[..., D]``.
+    Every fp16 value times 2^24 is an integer of magnitude below 2^40, so the
+    int64 sum is exact for any L below 2^23.
+    """
+    if k16.dtype != np.float16:
+        raise TypeError("kmean expects fp16 input")
+    L = k16.shape[-2]
+    if L < 1:
+        raise ValueError("kmean needs at least one token")
+    fixed = (k16.astype(np.float64) * 2.0**24).astype(np.int64)
+    isum = fixed.sum(axis=-2)
+    return (isum.astype(np.float64) / (np.float64(L) * 2.0**24)).astype(np.float32)
+
+
+def _round_up_significand(t: np.ndarray) -> np.ndarray:
+    """Smallest fp32 with an 11-bit significand that is >= t (t >= 0, finite)."""
+    u = np.ascontiguousarray(t, dtype=np.float32).view(np.uint32)
+    r = ((u + _ROUND_ADD) & _ROUND_MASK).astype(np.uint32)
+    return r.view(np.float32)
+
+
+def quant_rows(x32: np.ndarray):
+    """Symmetric per-row int8 quantization of fp32 rows (R1-R4).
+
+    ``x32`` is fp32 ``[..., D]``.  Returns ``(codes int8 [..., D],
+    scales fp32 [...])``.
+    """
+    x32 = np.asarray(x32)
+    if x32.dtype != np.float32:
+        raise TypeError("quant_rows expects fp32 rows")
+    a = np.max(np.abs(x32), axis=-1)
+    t = a / np.float32(127.0)
+    assert t.dtype == np.float32
+    scale = _round_up_significand(t)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    ratio = x32 / safe[..., None]
+    assert ratio.dtype == np.float32
+    codes = np.clip(np.rint(ratio), -127, 127)
+    codes = np.where(scale[..., None] > 0, codes, 0).astype(np.int8)
+    return codes, scale.astype(np.float32)
+
+
+def quantize_qkv(q16, k16, v16):
+    """Quantize dense BHSD q/k/v as the forward does internally.
+
+    Returns a dict with ``q8, sq, k8, sk, v8, sv, kmean``.
+    """
+    q8, sq = quant_rows(q16.astype(np.float32))
+    m = kmean(k16)  # [B, Hkv, D]
+    ksm = k16.astype(np.float32) - m[..., None, :]
+    assert ksm.dtype == np.float32
+    k8, sk = quant_rows(ksm)
+    v8, sv = quant_rows(v16.astype(np.float32))
+    return dict(q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, kmean=m)
+
+
+def qk_int32(q8: np.ndarray, k8: np.ndarray) -> np.ndarray:
+    """Exact integer scores ``q8 @ k8.T`` for one head (R7).
+
+    Computed with an fp64 matrix product, which is exact here: every partial
+    sum is an integer of magnitude at most 127*127*256 < 2^53.
+    """
+    s = q8.astype(np.float64) @ k8.astype(np.float64).T
+    return s.astype(np.int64)
+
+
+def attn_core(q8, sq, k8, sk, v8, sv, softmax_scale, causal, rows=None):
+    """Attention of one head on quantized operands (R7, R8, R10).
+
+    ``q8 [Sq, D]``, ``k8/v8 [Sk, D]`` int8; ``sq [Sq]``, ``sk/sv [Sk]`` fp32.
+    ``rows`` optionally selects query rows (each row is independent).
+    Returns fp64 ``[len(rows), D]``.
+    """
+    Sq, Sk = q8.shape[0], k8.shape[0]
+    if causal and Sq != Sk:
+        raise ValueError("causal attention needs equal query and key lengths")
+    rows = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    sm = np.float64(np.float32(softmax_scale))
+    vhat = sv.astype(np.float64)[:, None] * v8.astype(np.float64)
+    kk = k8.astype(np.float64)
+    skd = sk.astype(np.float64)
+    out = np.empty((rows.size, q8.shape[1]), dtype=np.float64)
+    for r0 in range(0, rows.size, _ROW_BLOCK):
+        rr = rows[r0:r0 + _ROW_BLOCK]
+        s32 = q8[rr].astype(np.float64) @ kk.T  # exact integers
+        logits = s32 * sq.astype(np.float64)[rr][:, None] * skd[None, :] * sm
+        if causal:
+            logits = np.where(np.arange(Sk)[None, :] <= rr[:, None], logits, -np.inf)
+        mx = logits.max(axis=1, keepdims=True)
+        p = np.exp(logits - mx)
+        p /= p.sum(axis=1, keepdims=True)
+        out[r0:r0 + rr.size] = p @ vhat
+    return out
+
+
+def attn_int8_fwd(q16, k16, v16, causal=True, softmax_scale=None, heads=None, rows=None):
+    """The dense forward: fp16 ``q[B,Hq,S,D]``, ``k/v[B,Hkv,S,D]`` -> fp64 O.
+
+    ``heads`` (list of (b, h)) and ``rows`` restrict the output to a sample;
+    the result then has shape ``[len(heads), len(rows), D]``, otherwise
+    ``[B, Hq, S, D]``.
+    """
+    B, Hq, S, D = q16.shape
+    Hkv = k16.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    sm = default_softmax_scale(D) if softmax_scale is None else np.float32(softmax_scale)
+    qz = quantize_qkv(q16, k16, v16)
+    sel = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
+    outs = []
+    for b, h in sel:
+        g = h // G
+        outs.append(attn_core(qz["q8"][b, h], qz["sq"][b, h], qz["k8"][b, g], qz["sk"][b, g],
+                              qz["v8"][b, g], qz["sv"][b, g], sm, causal, rows))
+    o = np.stack(outs)
+    if heads is None and rows is None:
+        o = o.reshape(B, Hq, S, D)
+    return o
+
+
+def attn_int8_varlen_fwd(q16, k16, v16, cu_seqlens, causal=True, softmax_scale=None):
+    """The varlen forward (R11): packed ``q[T,Hq,D]``, ``k/v[T,Hkv,D]``.
+
+    Each sequence ``cu[i]:cu[i+1]`` is quantized (its own K mean) and attended
+    independently.  Returns fp64 ``[T, Hq, D]``.
+    """
+    T, Hq, D = q16.shape
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for i in range(cu.size - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if b == a:
+            continue
+        qs = np.ascontiguousarray(q16[a:b].transpose(1, 0, 2))[None]
+        ks = np.ascontiguousarray(k16[a:b].transpose(1, 0, 2))[None]
+        vs = np.ascontiguousarray(v16[a:b].transpose(1, 0, 2))[None]
+        o = attn_int8_fwd(qs, ks, vs, causal, softmax_scale)[0]
+        out[a:b] = o.transpose(1, 0, 2)
+    return out
+
+
+def attn_exact(q, k, v, causal=True, softmax_scale=None):
+    """Unquantized attention in fp64 (reference for the quantization bound).
+
+    ``q[B,Hq,S,D]``, ``k/v[B,Hkv,S,D]`` of any float dtype.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, S, D = q.shape
+    G = Hq // k.shape[1]
+    sm = np.float64(default_softmax_scale(D) if softmax_scale is None else np.float32(softmax_scale))
+    out = np.empty_like(q)
+    for b in range(B):
+        for h in range(Hq):
+            lg = (q[b, h] @ k[b, h // G].T) * sm
+            if causal:
+                lg = np.where(np.tril(np.ones((S, k.shape[2]), dtype=bool)), lg, -np.inf)
+            p = np.exp(lg - lg.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            out[b, h] = p @ v[b, h // G]
+    return out

@@ -1,0 +1,358 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Every check here compares the oracle with exact rational arithmetic, brute
+force, a library routine (torch's CPU fp64 scaled-dot-product attention), an
+invariance the method must have, a closed form, or a value derived by hand
+(``tests/golden``).  None of them re-types the oracle's own formulas.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from int8_w8a8_flashattention_amd import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- helpers
+
+def rn32(f: Fraction) -> Fraction:
+    """Exact value of the fp32 nearest to f (ties to even), from first principles."""
+    if f == 0:
+        return Fraction(0)
+    sign = -1 if f < 0 else 1
+    a = abs(f)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    ulp = Fraction(2) ** (e - 23)
+    n = round(a / ulp)  # Python rounds a Fraction half to even
+    return sign * n * ulp
+
+
+def smallest_11bit_at_least(t: Fraction) -> Fraction:
+    """Smallest number >= t whose binary significand fits in 11 bits."""
+    if t == 0:
+        return Fraction(0)
+    e = t.numerator.bit_length() - t.denominator.bit_length()
+    if Fraction(2) ** e > t:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= t:
+        e += 1
+    step = Fraction(2) ** (e - 10)
+    return math.ceil(t / step) * step
+
+
+def exact_quant_row(row):
+    """Quantize one fp32 row with rational arithmetic; returns (scale, codes)."""
+    xs = [Fraction(float(x)) for x in row]
+    a = max(abs(x) for x in xs)
+    if a == 0:
+        return Fraction(0), [0] * len(xs)
+    t = rn32(a / 127)
+    s = smallest_11bit_at_least(t)
+    codes = []
+    for x in xs:
+        r = rn32(x / s)
+        c = round(r)  # half to even
+        codes.append(max(-127, min(127, c)))
+    return s, codes
+
+
+def dequant(codes, scales):
+    return scales.astype(np.float64)[..., None] * codes.astype(np.float64)
+
+
+def sdpa64(q, k, v, causal, scale):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))  # noqa: E731
+    return torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), is_causal=causal, scale=float(scale)).numpy()
+
+
+def rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+# ---------------------------------------------------------------- K mean
+
+@pytest.mark.parametrize("L", [1, 3, 17, 128, 1000])
+def test_kmean_equals_exact_rational_mean(L):
+    g = rng(100 + L)
+    D = 8
+    k = (g.standard_normal((2, L, D)) * np.exp(g.uniform(-12, 10, (2, L, D)))).astype(np.float16)
+    k[0, 0, 0] = np.float16(6e-8)  # a subnormal
+    m = oracle.kmean(k)
+    for h in range(2):
+        for d in range(D):
+            exact = sum(Fraction(float(x)) for x in k[h, :, d]) / L
+            want = np.float32(float(exact))  # float(Fraction) is correctly rounded
+            assert m[h, d] == want, (h, d)
+
+
+# ---------------------------------------------------------------- quantization
+
+def _rows_for_quant():
+    g = rng(7)
+    rows = [g.standard_normal(64).astype(np.float16).astype(np.float32) for _ in range(30)]
+    rows += [(g.standard_normal(16) * 1e-3).astype(np.float16).astype(np.float32) for _ in range(10)]
+    # K-smoothing-like rows: fp16 values minus an arbitrary fp32 mean
+    for _ in range(20):
+        m = np.float32(g.uniform(-3, 3))
+        rows.append(g.standard_normal(32).astype(np.float16).astype(np.float32) - m)
+    # rows built to hit exact .5 ties of x/scale
+    s = np.float32(1033 / 65536)
+    tie = np.array([2.0, 0.5 * 1033 / 65536, 2.5 * 1033 / 65536, -3.5 * 1033 / 65536], np.float32)
+    assert np.float32(np.float32(tie[1]) / s) == np.float32(0.5)
+    rows.append(tie)
+    rows.append(np.zeros(8, np.float32))
+    rows.append(np.array([65504.0, -65504.0, 1.0], np.float32))
+    return rows
+
+
+def test_quant_rows_match_exact_rational_rule():
+    for row in _rows_for_quant():
+        codes, scale = oracle.quant_rows(row[None, :])
+        s, c = exact_quant_row(row)
+        assert Fraction(float(scale[0])) == s
+        assert codes[0].tolist() == c
+
+
+def test_quant_rows_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "quant_rows_worked.json")))
+    for case in g["cases"]:
+        codes, scale = oracle.quant_rows(np.array([case["x"]], np.float32))
+        assert Fraction(float(scale[0])) == Fraction(case["scale_num"], case["scale_den"])
+        assert codes[0].tolist() == case["codes"]
+    kc = g["kmean_case"]
+    k = np.array(kc["k"], np.float16)[None]  # [1, L, D]
+    m = oracle.kmean(k)[0]
+    assert m.tolist() == kc["mean"]
+    codes, scale = oracle.quant_rows(k.astype(np.float32)[0] - m[None, :])
+    for r in kc["rows"]:
+        assert Fraction(float(scale[r["row"]])) == Fraction(r["scale_num"], r["scale_den"])
+        assert codes[r["row"]].tolist() == r["codes"]
+
+
+def test_quant_rows_properties():
+    g = rng(11)
+    x = g.standard_normal((200, 128)).astype(np.float16).astype(np.float32)
+    x[5] = 0
+    codes, scale = oracle.quant_rows(x)
+    nz = scale > 0
+    assert not nz[5] and np.all(codes[5] == 0)
+    # the row maximum always maps to +-127 (the scale is at most 2^-10 above absmax/127)
+    assert np.all(np.abs(codes[nz]).max(axis=1) == 127)
+    # |x/scale - code| <= 1/2 (up to the fp32 rounding of the quotient)
+    r = x[nz].astype(np.float64) / scale[nz, None].astype(np.float64)
+    assert np.all(np.abs(r - codes[nz]) <= 0.5 + 1e-5)
+    # scale >= absmax/127 and significand fits in 11 bits
+    a = np.abs(x[nz]).max(axis=1).astype(np.float64)
+    assert np.all(scale[nz].astype(np.float64) >= a / 127 * (1 - 2**-23))
+    mant = scale[nz].view(np.uint32) & 0x7FFFFF
+    assert np.all(mant & 0x1FFF == 0)
+    # power-of-two scaling is exact: same codes, scale times 2^k
+    for kexp in (-7, 3):
+        c2, s2 = oracle.quant_rows((x * np.float32(2.0**kexp)).astype(np.float32))
+        assert np.array_equal(c2, codes)
+        assert np.array_equal(s2, (scale * np.float32(2.0**kexp)).astype(np.float32))
+
+
+# ---------------------------------------------------------------- integer scores
+
+def test_qk_int32_brute_force():
+    g = rng(3)
+    q8 = g.integers(-127, 128, (5, 7)).astype(np.int8)
+    k8 = g.integers(-127, 128, (6, 7)).astype(np.int8)
+    s = oracle.qk_int32(q8, k8)
+    for i in range(5):
+        for j in range(6):
+            assert s[i, j] == sum(int(q8[i, d]) * int(k8[j, d]) for d in range(7))
+
+
+def test_qk_int32_extremes_d256():
+    q8 = np.full((2, 256), 127, np.int8)
+    k8 = np.full((3, 256), -127, np.int8)
+    s = oracle.qk_int32(q8, k8)
+    assert np.all(s == -127 * 127 * 256)
+    g = rng(4)
+    a = g.integers(-127, 128, (64, 256)).astype(np.int8)
+    b = g.integers(-127, 128, (80, 256)).astype(np.int8)
+    assert np.array_equal(oracle.qk_int32(a, b), np.einsum("id,jd->ij", a.astype(np.int64), b.astype(np.int64)))
+
+
+# ---------------------------------------------------------------- attention on quantized operands
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("Hq,Hkv,S,D", [(4, 2, 37, 32), (2, 1, 64, 64), (3, 3, 20, 128)])
+def test_forward_equals_library_attention_on_dequantized(causal, Hq, Hkv, S, D):
+    w = workloads.dense(21, 2, Hq, Hkv, S, D, causal, k_offset=2.0)
+    out = oracle.attn_int8_fwd(w.q, w.k, w.v, causal)
+    z = oracle.quantize_qkv(w.q, w.k, w.v)
+    G = Hq // Hkv
+    qh = dequant(z["q8"], z["sq"])
+    kh = np.repeat(dequant(z["k8"], z["sk"]), G, axis=1)
+    vh = np.repeat(dequant(z["v8"], z["sv"]), G, axis=1)
+    ref = sdpa64(qh, kh, vh, causal, oracle.default_softmax_scale(D))
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_exact_attention_equals_library():
+    w = workloads.dense(22, 1, 4, 2, 33, 64, True)
+    ref = sdpa64(w.q, np.repeat(w.k, 2, 1), np.repeat(w.v, 2, 1), True, oracle.default_softmax_scale(64))
+    np.testing.assert_allclose(oracle.attn_exact(w.q, w.k, w.v, True), ref, rtol=1e-11, atol=1e-12)
+
+
+def test_k_smoothing_exact_invariance_unquantized():
+    w = workloads.dense(23, 1, 2, 1, 50, 32, True, k_offset=3.0)
+    k = w.k.astype(np.float64)
+    ks = k - k.mean(axis=2, keepdims=True)
+    a = oracle.attn_exact(w.q, k, w.v, True)
+    b = oracle.attn_exact(w.q, ks, w.v, True)
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
+def test_k_smoothing_removes_channel_offsets():
+    """With K-smoothing a per-channel K offset changes nothing: codes, scales
+    and outputs are bit-identical.  Inputs are chosen so every step is exact
+    (K on a 2^-4 grid, integer offsets, 16 tokens)."""
+    g = rng(24)
+    B, H, S, D = 1, 2, 16, 32
+    q = g.standard_normal((B, H, S, D)).astype(np.float16)
+    v = g.standard_normal((B, H, S, D)).astype(np.float16)
+    k = (np.round(g.uniform(-4, 4, (B, H, S, D)) * 16) / 16).astype(np.float16)
+    off = g.integers(-3, 4, (1, H, 1, D)).astype(np.float16)
+    k2 = (k.astype(np.float32) + off).astype(np.float16)
+    assert np.array_equal(k2.astype(np.float32) - off, k.astype(np.float32))
+    za, zb = oracle.quantize_qkv(q, k, v), oracle.quantize_qkv(q, k2, v)
+    assert np.array_equal(za["k8"], zb["k8"]) and np.array_equal(za["sk"], zb["sk"])
+    assert np.array_equal(oracle.attn_int8_fwd(q, k, v, True), oracle.attn_int8_fwd(q, k2, v, True))
+    # without the subtraction the codes would differ
+    c_raw, _ = oracle.quant_rows(k2.astype(np.float32))
+    assert not np.array_equal(c_raw, za["k8"])
+
+
+def test_causal_rows_equal_prefix_attention():
+    g = rng(25)
+    S, D = 40, 64
+    q8 = g.integers(-127, 128, (S, D)).astype(np.int8)
+    k8 = g.integers(-127, 128, (S, D)).astype(np.int8)
+    v8 = g.integers(-127, 128, (S, D)).astype(np.int8)
+    sq, sk, sv = (g.uniform(0.001, 0.03, S).astype(np.float32) for _ in range(3))
+    sm = oracle.default_softmax_scale(D)
+    full = oracle.attn_core(q8, sq, k8, sk, v8, sv, sm, True)
+    for i in (0, 1, 7, S - 1):
+        pre = oracle.attn_core(q8[i:i + 1], sq[i:i + 1], k8[:i + 1], sk[:i + 1], v8[:i + 1], sv[:i + 1], sm, False)
+        np.testing.assert_allclose(full[i], pre[0], rtol=1e-13, atol=1e-15)
+    # row 0 sees one key: exactly that key's dequantized value
+    assert np.array_equal(full[0], sv[0].astype(np.float64) * v8[0].astype(np.float64))
+
+
+def test_gqa_equals_repeated_heads():
+    w = workloads.dense(26, 2, 6, 2, 45, 32, True, k_offset=1.0)
+    a = oracle.attn_int8_fwd(w.q, w.k, w.v, True)
+    b = oracle.attn_int8_fwd(w.q, np.repeat(w.k, 3, 1), np.repeat(w.v, 3, 1), True)
+    assert np.array_equal(a, b)
+
+
+def test_varlen_equal_lengths_equals_dense():
+    w = workloads.dense(27, 3, 4, 2, 30, 32, True)
+    B, Hq, S, D = w.q.shape
+    tq = w.q.transpose(0, 2, 1, 3).reshape(B * S, Hq, D)
+    tk = w.k.transpose(0, 2, 1, 3).reshape(B * S, 2, D)
+    tv = w.v.transpose(0, 2, 1, 3).reshape(B * S, 2, D)
+    cu = np.arange(0, B * S + 1, S, dtype=np.int32)
+    a = oracle.attn_int8_varlen_fwd(tq, tk, tv, cu, True)
+    b = oracle.attn_int8_fwd(w.q, w.k, w.v, True).transpose(0, 2, 1, 3).reshape(B * S, Hq, D)
+    assert np.array_equal(a, b)
+
+
+def test_varlen_sequences_are_independent():
+    w = workloads.varlen(28, 4, 30, 4, 2, 32, True, lengths=[5, 0, 30, 1])
+    a = oracle.attn_int8_varlen_fwd(w.q, w.k, w.v, w.cu_seqlens, True)
+    # changing one sequence leaves every other sequence's rows unchanged
+    k2 = w.k.copy()
+    k2[5:35] = (k2[5:35].astype(np.float32) * 3).astype(np.float16)
+    b = oracle.attn_int8_varlen_fwd(w.q, k2, w.v, w.cu_seqlens, True)
+    assert np.array_equal(a[:5], b[:5]) and np.array_equal(a[35:], b[35:])
+    assert not np.array_equal(a[5:35], b[5:35])
+
+
+def test_zero_queries_give_prefix_means():
+    g = rng(29)
+    B, H, S, D = 1, 1, 25, 32
+    q = np.zeros((B, H, S, D), np.float16)
+    k = g.standard_normal((B, H, S, D)).astype(np.float16)
+    v = g.standard_normal((B, H, S, D)).astype(np.float16)
+    out = oracle.attn_int8_fwd(q, k, v, True)[0, 0]
+    v8, sv = oracle.quant_rows(v.astype(np.float32)[0, 0])
+    vh = dequant(v8, sv)
+    want = np.cumsum(vh, axis=0) / np.arange(1, S + 1)[:, None]
+    np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-14)
+    out_nc = oracle.attn_int8_fwd(q, k, v, False)[0, 0]
+    np.testing.assert_allclose(out_nc, np.broadcast_to(vh.mean(axis=0), out_nc.shape), rtol=1e-12, atol=1e-14)
+
+
+def test_dominant_key_gives_its_value():
+    g = rng(30)
+    S, D = 20, 64
+    q = g.standard_normal((1, 1, S, D)).astype(np.float16)
+    k = (g.standard_normal((1, 1, S, D)) * 0.01).astype(np.float16)
+    j = 13
+    k[0, 0, j] = (q[0, 0, S - 1].astype(np.float32) * 40).astype(np.float16)
+    v = g.standard_normal((1, 1, S, D)).astype(np.float16)
+    out = oracle.attn_int8_fwd(q, k, v, False)[0, 0, S - 1]
+    v8, sv = oracle.quant_rows(v.astype(np.float32)[0, 0])
+    np.testing.assert_allclose(out, dequant(v8, sv)[j], rtol=0, atol=1e-9)
+
+
+def test_noncausal_key_permutation_invariance():
+    w = workloads.dense(31, 1, 2, 2, 24, 32, False, k_offset=1.0)
+    perm = rng(31).permutation(24)
+    a = oracle.attn_int8_fwd(w.q, w.k, w.v, False)
+    b = oracle.attn_int8_fwd(w.q, w.k[:, :, perm], w.v[:, :, perm], False)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- whole method vs exact attention
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_quantized_forward_within_a_posteriori_bound(causal):
+    """|O_int8 - O_exact| <= max_j|dv_jd| + (exp(2 eps_i) - 1) max_j|v_jd| with
+    eps_i = sm * max_j sum_d(|q||dk| + |dq||k| + |dq||dk|), the dequantization
+    errors measured on the actual inputs (a score perturbation of at most eps
+    moves every softmax weight by a factor within exp(+-2 eps))."""
+    w = workloads.cfg1() if causal else workloads.dense(32, 1, 2, 1, 96, 32, False, outlier_frac=0.05)
+    q = w.q.astype(np.float64)
+    z = oracle.quantize_qkv(w.q, w.k, w.v)
+    ks = (w.k.astype(np.float32) - z["kmean"][..., None, :]).astype(np.float64)
+    v = w.v.astype(np.float64)
+    dq = dequant(z["q8"], z["sq"]) - q
+    dk = dequant(z["k8"], z["sk"]) - ks
+    dv = dequant(z["v8"], z["sv"]) - v
+    o = oracle.attn_int8_fwd(w.q, w.k, w.v, causal)
+    ex = oracle.attn_exact(q, ks, v, causal)
+    D = q.shape[-1]
+    sm = float(oracle.default_softmax_scale(D))
+    B, Hq, S, _ = q.shape
+    G = Hq // w.k.shape[1]
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            e = (np.abs(q[b, h]) @ np.abs(dk[b, g]).T + np.abs(dq[b, h]) @ np.abs(ks[b, g]).T
+                 + np.abs(dq[b, h]) @ np.abs(dk[b, g]).T) * sm
+            for i in range(S):
+                jmax = i + 1 if causal else S
+                eps = e[i, :jmax].max()
+                bound = (np.abs(dv[b, g, :jmax]).max(axis=0)
+                         + np.expm1(2 * eps) * np.abs(v[b, g, :jmax]).max(axis=0))
+                assert np.all(np.abs(o[b, h, i] - ex[b, h, i]) <= bound + 1e-12), (b, h, i)
