@@ -29,7 +29,8 @@ tolerance constrains.
 """
 
 from .attn_ref import (  # noqa: F401
-    SCALE_SIGNIFICAND_BITS,
+    QK_SCALE_BITS,
+    V_SCALE_BITS,
     default_softmax_scale,
     kmean,
     quant_rows,

@@ -14,12 +14,13 @@ The page prints no formulas, so each step below is the plainest reading of
 those rows.  Readings taken where the page is silent:
 
 R1  Codes are symmetric: integers in [-127, 127]; -128 is never produced.
-R2  Row scale: ``t = fp32(absmax / 127)`` (IEEE round-to-nearest-even), then
-    rounded *up* to the next value whose significand has 11 bits (the
-    precision of an fp16 number), stored as fp32.  The 11-bit significand
-    lets a consumer fold the V scale into an fp16 softmax weight without
-    rounding when that weight is 1 (the row maximum); rounding up keeps every
-    ``|x| / scale`` at most 127.
+R2  Row scale of Q and K: ``fp32(absmax / 127)`` (IEEE round-to-nearest-even),
+    stored as fp32.  Row scale of V (the per-token choice of the
+    *Quantization* table's "V per-channel / per-token" row): the same value
+    rounded *up* to the next number whose significand has 4 bits.  Then every
+    dequantized value ``code * scale`` (7-bit code times 4-bit significand)
+    is exactly an fp16 number, so the fp16 P.V product can consume V without
+    rounding it; rounding up keeps every ``|x| / scale`` at most 127.
 R3  ``code = clamp(rint(fp32(x / scale)), -127, 127)`` with a correctly
     rounded fp32 division and round-half-to-even.
 R4  An all-zero row gets scale 0 and codes 0.
@@ -28,8 +29,8 @@ R5  K-smoothing subtracts, per (batch, kv head, channel), the mean of K over
     mask).  The mean is the exact sum (fp16 values are integer multiples of
     2^-24), divided in fp64, rounded to fp32; K rows are quantized from the
     fp32 difference ``fp32(k) - mean``.
-R6  Q and V are quantized per row (per token and head) with the same rule;
-    V is per token, the "per-token" choice of the *Quantization* table.
+R6  Q and V are quantized per row (per token and head) like K, without the
+    mean subtraction; V uses its 4-bit scale (R2).
 R7  Scores are the exact integer dot products of the codes; logits are
     ``S32 * sq_i * sk_j * softmax_scale``; the softmax scale defaults to
     ``fp32(1 / sqrt(D))`` and is not folded into Q before quantization.
@@ -49,11 +50,9 @@ from __future__ import annotations
 
 import numpy as np
 
-#: Significand width (implicit bit included) of every row scale, reading R2.
-SCALE_SIGNIFICAND_BITS = 11
-_DROP_BITS = 24 - SCALE_SIGNIFICAND_BITS  # fp32 has a 24-bit significand
-_ROUND_ADD = np.uint32((1 << _DROP_BITS) - 1)
-_ROUND_MASK = np.uint32(0xFFFFFFFF ^ ((1 << _DROP_BITS) - 1))
+#: Significand width (implicit bit included) of the row scales, reading R2.
+QK_SCALE_BITS = 24  # a plain fp32 scale
+V_SCALE_BITS = 4
 
 _ROW_BLOCK = 512  # query rows per block: keeps the [rows, keys] logits small
 
@@ -80,18 +79,20 @@ def kmean(k16: np.ndarray) -> np.ndarray:
     return (isum.astype(np.float64) / (np.float64(L) * 2.0**24)).astype(np.float32)
 
 
-def _round_up_significand(t: np.ndarray) -> np.ndarray:
-    """Smallest fp32 with an 11-bit significand that is >= t (t >= 0, finite)."""
-    u = np.ascontiguousarray(t, dtype=np.float32).view(np.uint32)
-    r = ((u + _ROUND_ADD) & _ROUND_MASK).astype(np.uint32)
+def _round_up_significand(t: np.ndarray, bits: int) -> np.ndarray:
+    """Smallest fp32 with a ``bits``-bit significand that is >= t (t >= 0,
+    finite, normal or zero)."""
+    drop = 24 - bits  # fp32 has a 24-bit significand
+    u = np.ascontiguousarray(t, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + ((1 << drop) - 1)) & (0xFFFFFFFF ^ ((1 << drop) - 1))).astype(np.uint32)
     return r.view(np.float32)
 
 
-def quant_rows(x32: np.ndarray):
+def quant_rows(x32: np.ndarray, scale_bits: int = QK_SCALE_BITS):
     """Symmetric per-row int8 quantization of fp32 rows (R1-R4).
 
-    ``x32`` is fp32 ``[..., D]``.  Returns ``(codes int8 [..., D],
-    scales fp32 [...])``.
+    ``x32`` is fp32 ``[..., D]``; ``scale_bits`` is 24 for Q and K rows and 4
+    for V rows.  Returns ``(codes int8 [..., D], scales fp32 [...])``.
     """
     x32 = np.asarray(x32)
     if x32.dtype != np.float32:
@@ -99,7 +100,7 @@ def quant_rows(x32: np.ndarray):
     a = np.max(np.abs(x32), axis=-1)
     t = a / np.float32(127.0)
     assert t.dtype == np.float32
-    scale = _round_up_significand(t)
+    scale = _round_up_significand(t, scale_bits) if scale_bits < 24 else t
     safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
     ratio = x32 / safe[..., None]
     assert ratio.dtype == np.float32
@@ -118,7 +119,7 @@ def quantize_qkv(q16, k16, v16):
     ksm = k16.astype(np.float32) - m[..., None, :]
     assert ksm.dtype == np.float32
     k8, sk = quant_rows(ksm)
-    v8, sv = quant_rows(v16.astype(np.float32))
+    v8, sv = quant_rows(v16.astype(np.float32), V_SCALE_BITS)
     return dict(q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, kmean=m)
 
 

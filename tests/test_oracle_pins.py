@@ -40,8 +40,8 @@ def rn32(f: Fraction) -> Fraction:
     return sign * n * ulp
 
 
-def smallest_11bit_at_least(t: Fraction) -> Fraction:
-    """Smallest number >= t whose binary significand fits in 11 bits."""
+def smallest_at_least(t: Fraction, bits: int) -> Fraction:
+    """Smallest number >= t whose binary significand fits in ``bits`` bits."""
     if t == 0:
         return Fraction(0)
     e = t.numerator.bit_length() - t.denominator.bit_length()
@@ -49,18 +49,18 @@ def smallest_11bit_at_least(t: Fraction) -> Fraction:
         e -= 1
     while Fraction(2) ** (e + 1) <= t:
         e += 1
-    step = Fraction(2) ** (e - 10)
+    step = Fraction(2) ** (e - bits + 1)
     return math.ceil(t / step) * step
 
 
-def exact_quant_row(row):
+def exact_quant_row(row, bits=24):
     """Quantize one fp32 row with rational arithmetic; returns (scale, codes)."""
     xs = [Fraction(float(x)) for x in row]
     a = max(abs(x) for x in xs)
     if a == 0:
         return Fraction(0), [0] * len(xs)
     t = rn32(a / 127)
-    s = smallest_11bit_at_least(t)
+    s = smallest_at_least(t, bits)
     codes = []
     for x in xs:
         r = rn32(x / s)
@@ -109,30 +109,31 @@ def _rows_for_quant():
     for _ in range(20):
         m = np.float32(g.uniform(-3, 3))
         rows.append(g.standard_normal(32).astype(np.float16).astype(np.float32) - m)
-    # rows built to hit exact .5 ties of x/scale
-    s = np.float32(1033 / 65536)
-    tie = np.array([2.0, 0.5 * 1033 / 65536, 2.5 * 1033 / 65536, -3.5 * 1033 / 65536], np.float32)
-    assert np.float32(np.float32(tie[1]) / s) == np.float32(0.5)
+    # rows built to hit exact .5 ties of x/scale (scale of absmax 127/64 is 1/64)
+    tie = np.array([127 / 64, 0.5 / 64, 2.5 / 64, -3.5 / 64, 6.5 / 64], np.float32)
+    assert np.float32(tie[0] / np.float32(127)) == np.float32(1 / 64)
     rows.append(tie)
     rows.append(np.zeros(8, np.float32))
     rows.append(np.array([65504.0, -65504.0, 1.0], np.float32))
     return rows
 
 
-def test_quant_rows_match_exact_rational_rule():
+@pytest.mark.parametrize("bits", [oracle.QK_SCALE_BITS, oracle.V_SCALE_BITS])
+def test_quant_rows_match_exact_rational_rule(bits):
     for row in _rows_for_quant():
-        codes, scale = oracle.quant_rows(row[None, :])
-        s, c = exact_quant_row(row)
+        codes, scale = oracle.quant_rows(row[None, :], bits)
+        s, c = exact_quant_row(row, bits)
         assert Fraction(float(scale[0])) == s
         assert codes[0].tolist() == c
 
 
 def test_quant_rows_worked_example():
     g = json.load(open(os.path.join(GOLDEN, "quant_rows_worked.json")))
-    for case in g["cases"]:
-        codes, scale = oracle.quant_rows(np.array([case["x"]], np.float32))
-        assert Fraction(float(scale[0])) == Fraction(case["scale_num"], case["scale_den"])
-        assert codes[0].tolist() == case["codes"]
+    for key, bits in (("qk_cases", oracle.QK_SCALE_BITS), ("v_cases", oracle.V_SCALE_BITS)):
+        for case in g[key]:
+            codes, scale = oracle.quant_rows(np.array([case["x"]], np.float32), bits)
+            assert Fraction(float(scale[0])) == Fraction(case["scale_num"], case["scale_den"])
+            assert codes[0].tolist() == case["codes"]
     kc = g["kmean_case"]
     k = np.array(kc["k"], np.float16)[None]  # [1, L, D]
     m = oracle.kmean(k)[0]
@@ -150,21 +151,37 @@ def test_quant_rows_properties():
     codes, scale = oracle.quant_rows(x)
     nz = scale > 0
     assert not nz[5] and np.all(codes[5] == 0)
-    # the row maximum always maps to +-127 (the scale is at most 2^-10 above absmax/127)
+    # the row maximum maps to +-127
     assert np.all(np.abs(codes[nz]).max(axis=1) == 127)
     # |x/scale - code| <= 1/2 (up to the fp32 rounding of the quotient)
     r = x[nz].astype(np.float64) / scale[nz, None].astype(np.float64)
     assert np.all(np.abs(r - codes[nz]) <= 0.5 + 1e-5)
-    # scale >= absmax/127 and significand fits in 11 bits
+    # the scale is absmax/127 to fp32 precision
     a = np.abs(x[nz]).max(axis=1).astype(np.float64)
-    assert np.all(scale[nz].astype(np.float64) >= a / 127 * (1 - 2**-23))
-    mant = scale[nz].view(np.uint32) & 0x7FFFFF
-    assert np.all(mant & 0x1FFF == 0)
+    np.testing.assert_allclose(scale[nz].astype(np.float64), a / 127, rtol=2**-24, atol=0)
     # power-of-two scaling is exact: same codes, scale times 2^k
     for kexp in (-7, 3):
         c2, s2 = oracle.quant_rows((x * np.float32(2.0**kexp)).astype(np.float32))
         assert np.array_equal(c2, codes)
         assert np.array_equal(s2, (scale * np.float32(2.0**kexp)).astype(np.float32))
+
+
+def test_v_quant_dequantizes_to_exact_fp16():
+    """V rows: 4-bit scale significand, row max maps to at least 113, and every
+    code * scale is exactly an fp16 number (including fp16 subnormals for
+    rows whose scale is at least 2^-21)."""
+    g = rng(12)
+    x = (g.standard_normal((300, 64)) * np.exp(g.uniform(-9, 9, (300, 1)))).astype(np.float16)
+    x = x.astype(np.float32)
+    codes, scale = oracle.quant_rows(x, oracle.V_SCALE_BITS)
+    assert np.all(scale.view(np.uint32) & 0xFFFFF == 0)
+    a = np.abs(x).max(axis=1).astype(np.float64)
+    assert np.all(scale >= a / 127 * (1 - 2**-23))
+    assert np.all(scale <= a / 127 * 1.125 * (1 + 2**-23))
+    assert np.all(np.abs(codes).max(axis=1) >= 113)
+    ok = scale >= 2.0**-21
+    vhat = scale[ok, None].astype(np.float64) * codes[ok].astype(np.float64)
+    assert np.array_equal(vhat.astype(np.float16).astype(np.float64), vhat)
 
 
 # ---------------------------------------------------------------- integer scores
@@ -294,7 +311,7 @@ def test_zero_queries_give_prefix_means():
     k = g.standard_normal((B, H, S, D)).astype(np.float16)
     v = g.standard_normal((B, H, S, D)).astype(np.float16)
     out = oracle.attn_int8_fwd(q, k, v, True)[0, 0]
-    v8, sv = oracle.quant_rows(v.astype(np.float32)[0, 0])
+    v8, sv = oracle.quant_rows(v.astype(np.float32)[0, 0], oracle.V_SCALE_BITS)
     vh = dequant(v8, sv)
     want = np.cumsum(vh, axis=0) / np.arange(1, S + 1)[:, None]
     np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-14)
@@ -311,7 +328,7 @@ def test_dominant_key_gives_its_value():
     k[0, 0, j] = (q[0, 0, S - 1].astype(np.float32) * 40).astype(np.float16)
     v = g.standard_normal((1, 1, S, D)).astype(np.float16)
     out = oracle.attn_int8_fwd(q, k, v, False)[0, 0, S - 1]
-    v8, sv = oracle.quant_rows(v.astype(np.float32)[0, 0])
+    v8, sv = oracle.quant_rows(v.astype(np.float32)[0, 0], oracle.V_SCALE_BITS)
     np.testing.assert_allclose(out, dequant(v8, sv)[j], rtol=0, atol=1e-9)
 
 
