@@ -1,0 +1,191 @@
+"""Benchmark of the INT8 W8A8 attention forward on one MI355X.
+
+One step = one ``attn_int8_fwd`` call on the causal GQA workload B=1, Hq=32,
+Hkv=8, S=4096, D=128 (fp16 q/k/v ~ N(0,1), seeded): K-smoothing mean, K/V
+quantization, Q quantization and the attention itself, every kernel the call
+launches.  Inputs, output and workspace are resident in HBM before timing starts.
+
+Prints one JSON line.  ``value`` is effective TOPS = algorithmic ops / time per
+step, with ops = 4*D*Hq*S^2/2 (two products of 2*D ops per (query, key) pair,
+S^2/2 causal pairs per head, the usual FlashAttention count).  ``roofline``
+describes the attention kernel alone (timed with HIP events on the stream it runs
+on) against the 5.0 POPS dense int8 MFMA peak.  ``cpu_baseline`` times the CPU
+oracle on a bounded sample of the same workload.
+
+Only one GPU is used: ``--gpus`` above 1 exits with a message.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POPS
+WORKLOAD = dict(B=1, Hq=32, Hkv=8, S=4096, D=128, causal=True)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_cfg2_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the CPU oracle on whole heads of the same workload until the budget is
+    spent; ops per second scaled to TOPS."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    B, Hq, S, D = w.q.shape
+    t0 = time.perf_counter()
+    z = oracle.quantize_qkv(w.q, w.k, w.v)  # quantization of the whole input
+    G = Hq // w.k.shape[1]
+    heads = 0
+    for h in range(Hq):
+        g = h // G
+        oracle.attn_core(z["q8"][0, h], z["sq"][0, h], z["k8"][0, g], z["sk"][0, g],
+                         z["v8"][0, g], z["sv"][0, g], oracle.default_softmax_scale(D), True)
+        heads += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    ops = 4.0 * D * heads * S * S / 2.0
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"{heads} of {Hq} query heads (all {S} rows each) plus the quantization "
+                      f"of the whole input, {dt:.1f} s; numpy fp64 BLAS with {blas_threads} "
+                      f"threads, the rest single-threaded; host has {os.cpu_count()} CPUs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of CPU oracle work for the cpu_baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward shards by kv-head groups with no communication; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import int8_w8a8_flashattention_amd as i8
+    from int8_w8a8_flashattention_amd import workloads
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    i8.load_library()
+    dev = torch.device("cuda:0")
+    w = workloads.cfg2()
+    B, Hq, Hkv, S, D = (WORKLOAD[k] for k in ("B", "Hq", "Hkv", "S", "D"))
+    assert w.q.shape == (B, Hq, S, D) and w.k.shape == (B, Hkv, S, D)
+    q, k, v = (torch.from_numpy(a).to(dev) for a in (w.q, w.k, w.v))
+    out = torch.empty_like(q)
+    ws = torch.empty(i8.attn_int8_workspace_bytes(B, Hq, Hkv, S, D), dtype=torch.uint8, device=dev)
+    ops = workloads.attn_ops(Hq, D, [S] * B, True)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        i8.attn_int8_fwd(q, k, v, True, out=out, workspace=ws)
+
+    log(f"bench: warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"bench: {args.steps} steps, {ms_step * 1e3:.1f} us/step (host wall {t_wall * 1e3 / args.steps:.1f} us/step)")
+
+    # The phases alone: K/V preparation, then the attention kernel (dominant).
+    i8.attn_int8_prepare_kv(k, v, Hq, workspace=ws)
+    for _ in range(args.warmup):
+        i8.attn_int8_fwd_prepared(q, Hkv, ws, True, out=out)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        i8.attn_int8_fwd_prepared(q, Hkv, ws, True, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_attn = e0.elapsed_time(e1) / args.steps
+    e0.record(stream)
+    for _ in range(args.steps):
+        i8.attn_int8_prepare_kv(k, v, Hq, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_prep = e0.elapsed_time(e1) / args.steps
+    log(f"bench: attention kernel {ms_attn * 1e3:.1f} us, K/V preparation {ms_prep * 1e3:.1f} us")
+
+    # quick parity guard on the benchmarked output (sampled rows of two heads)
+    import oracle
+    i8.attn_int8_fwd(q, k, v, True, out=out, workspace=ws)
+    rows = np.array([0, 1, 127, 128, 2047, 4095])
+    ref = oracle.attn_int8_fwd(w.q, w.k, w.v, True, heads=[(0, 0), (0, 31)], rows=rows)
+    got = out[0, [0, 31]][:, rows].float().cpu().numpy()
+    max_abs = float(np.abs(got - ref).max())
+    if not max_abs <= 2e-3:
+        raise RuntimeError(f"benchmarked output differs from the oracle: max_abs={max_abs}")
+
+    value = ops / (ms_step * 1e-3) / 1e12
+    achieved = ops / (ms_attn * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            traffic = json.load(open(TRAFFIC_FILE)).get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    res = {
+        "metric": "INT8 attn fwd effective TOPS & % int8 MFMA peak, Hq32/Hkv8 S4096 D128 causal",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+fp16",
+        "data": "synthetic",
+        "config": {"workload": "causal GQA attention B1 Hq32 Hkv8 S4096 D128, fp16 N(0,1), seed 2",
+                   "B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "D": D, "causal": True,
+                   "algorithmic_ops": ops},
+        "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
+        "attn_kernel_us": round(ms_attn * 1e3, 2),
+        "prep_us": round(ms_prep * 1e3, 2),
+        "parity_sample_max_abs": max_abs,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        log(f"bench: timing the CPU oracle (~{args.cpu_budget:.0f} s)")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

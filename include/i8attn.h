@@ -1,0 +1,184 @@
+/*
+ * i8attn.h - C ABI of the INT8 W8A8 FlashAttention forward for AMD MI355X (gfx950).
+ *
+ * The method is the one the "SuperL8" README describes for its attn_int8_fwd kernel
+ * (Attention kernels table: "W8A8 ... FlashAttention-2. Causal, GQA/MQA, head dims
+ * 32/64/128/256") with its attn_varlen_fwd variant (same table: ragged,
+ * non-tile-multiple prefill) and its quant_rowwise helper (Supporting kernels table:
+ * symmetric per-row int8).  Per the Quantization table, K is smoothed by subtracting
+ * its per-channel mean over the sequence before it is quantized; V is quantized per
+ * token.  Per the Quick start, the forward takes fp16 q, k, v and quantizes
+ * internally.
+ *
+ * Arithmetic of one forward call (every step runs in HIP kernels):
+ *   kmean[b,g,:]   = mean over the sequence's tokens of k[b,g,:,:] (exact sum, fp64
+ *                    divide, rounded to fp32)
+ *   q8,sq = quant(q)          sq = fp32(absmax/127)
+ *   k8,sk = quant(k - kmean)  sk = fp32(absmax/127), x = fp32(k) - kmean in fp32
+ *   v8,sv = quant(v)          sv = fp32(absmax/127) rounded up to a 4-bit significand
+ *   quant(x): code = clamp(rint(fp32(x / scale)), -127, 127); all-zero row -> scale 0
+ *   S32 = q8 . k8^T (int8 MFMA, exact int32)
+ *   logit = S32 * sq_i * sk_j * softmax_scale, causal: key j > query i masked
+ *   out = softmax(logit) . (sv * v8), online softmax in fp32, fp16 MFMA for P.V,
+ *         fp32 accumulation, fp16 output
+ *   GQA/MQA: query head h reads kv head h / (Hq / Hkv).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked "host".  fp16 tensors are passed as
+ *     void* holding IEEE binary16 values.  All tensors are densely packed in the
+ *     layout stated; base pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All work is enqueued on
+ *     it and the call returns without synchronizing.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     synchronizes, keeps no state between calls and is reentrant; calls that run
+ *     concurrently need distinct workspaces.
+ *   - Every argument check runs on the host before anything is enqueued: on an error
+ *     nothing is written.  The detail of the last failure on the calling thread is
+ *     available from i8a_last_error().
+ *   - Inputs must be finite.  V entries must have magnitude <= 65024 (so that the
+ *     dequantized V, whose scale is rounded up, stays within fp16 range).
+ */
+#ifndef I8ATTN_H
+#define I8ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t i8a_status;
+
+#define I8A_OK 0
+#define I8A_ERR_INVALID_ARG (-1)          /* bad pointer, size, alignment or flag */
+#define I8A_ERR_UNSUPPORTED_HEAD_DIM (-2) /* D not in {32, 64, 128, 256} */
+#define I8A_ERR_WORKSPACE_TOO_SMALL (-3)  /* workspace_bytes below the required size */
+#define I8A_ERR_HIP (-4)                  /* a HIP launch failed (see i8a_last_error) */
+
+/* Scale rules accepted by quant_rowwise_i8 (significand bits of the row scale). */
+#define I8A_SCALE_FP32 24 /* scale = fp32(absmax / 127): Q and K rows */
+#define I8A_SCALE_V4 4    /* the same, rounded up to a 4-bit significand: V rows */
+
+/*
+ * quant_rowwise_i8 - symmetric per-row int8 quantization (SuperL8 README, Supporting
+ * kernels table, row quant_rowwise; Quantization table, row "Per-row int8").
+ *
+ *   x        fp16 [rows, d], row-major.
+ *   rows     number of rows, >= 0 (0 is a no-op).
+ *   d        row length, a multiple of 8 in [8, 512].
+ *   sub_mean nullable fp32 [ceil(rows / rows_per_group), d]: if given, row r is
+ *            quantized from fp32(x[r]) - sub_mean[r / rows_per_group] (the
+ *            K-smoothing subtraction); rows_per_group >= 1 then.
+ *   scale_bits I8A_SCALE_FP32 or I8A_SCALE_V4.
+ *   codes    int8 [rows, d] out, 8-byte aligned.   scales  fp32 [rows] out.
+ */
+i8a_status quant_rowwise_i8(const void* x, int64_t rows, int32_t d, const float* sub_mean,
+                            int64_t rows_per_group, int32_t scale_bits, int8_t* codes,
+                            float* scales, void* stream);
+
+/*
+ * attn_int8_workspace_bytes - device workspace needed by attn_int8_fwd and
+ * attn_int8_debug_qk for these sizes (0 if the sizes are invalid).  The workspace
+ * holds the K partial sums and means, the K codes and scales, and the dequantized V,
+ * in private tiled layouts.  It needs no initialization.
+ */
+size_t attn_int8_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D);
+
+/*
+ * attn_int8_fwd - dense INT8 W8A8 attention forward (SuperL8 README, Attention
+ * kernels table, row attn_int8_fwd; Quick start call attn_int8_fwd(q, k, v,
+ * causal=True)).
+ *
+ *   q    fp16 [B, Hq, S, D]      k, v  fp16 [B, Hkv, S, D]      out  fp16 [B, Hq, S, D]
+ *   B, S >= 1; Hq, Hkv >= 1 with Hq % Hkv == 0 (Hkv == 1 is MQA); D in {32,64,128,256}.
+ *   softmax_scale  finite and > 0 (the usual value is fp32(1/sqrt(D))); it multiplies
+ *                  the dequantized logits and is not folded into Q.
+ *   causal         0 or 1; causal means query i attends keys j <= i.
+ *   workspace      device buffer of at least attn_int8_workspace_bytes(...) bytes,
+ *                  256-byte aligned, not aliasing q, k, v or out.
+ * out must not alias q, k or v.
+ */
+i8a_status attn_int8_fwd(const void* q, const void* k, const void* v, void* out, int32_t B,
+                         int32_t Hq, int32_t Hkv, int32_t S, int32_t D, float softmax_scale,
+                         int32_t causal, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_int8_prepare_kv / attn_int8_fwd_prepared - attn_int8_fwd split in its two
+ * phases, for callers that reuse one prepared K/V for several query batches and for
+ * timing each phase alone.  attn_int8_prepare_kv runs the K-smoothing mean and the K
+ * and V quantization of attn_int8_fwd into `workspace`; attn_int8_fwd_prepared then
+ * quantizes q and runs the attention against that workspace.  The pair computes
+ * exactly what attn_int8_fwd computes.  Sizes and workspace must be identical in both
+ * calls; the workspace must not be modified in between; arguments as for
+ * attn_int8_fwd.
+ */
+i8a_status attn_int8_prepare_kv(const void* k, const void* v, int32_t B, int32_t Hq, int32_t Hkv,
+                                int32_t S, int32_t D, void* workspace, size_t workspace_bytes,
+                                void* stream);
+i8a_status attn_int8_fwd_prepared(const void* q, void* out, int32_t B, int32_t Hq, int32_t Hkv,
+                                  int32_t S, int32_t D, float softmax_scale, int32_t causal,
+                                  const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_int8_varlen_workspace_bytes - workspace for attn_int8_varlen_fwd (0 if the
+ * sizes are invalid).
+ */
+size_t attn_int8_varlen_workspace_bytes(int32_t nseq, int64_t total_tokens, int32_t max_seqlen,
+                                        int32_t Hq, int32_t Hkv, int32_t D);
+
+/*
+ * attn_int8_varlen_fwd - the same forward over a packed batch of sequences of
+ * different lengths (SuperL8 README, Attention kernels table, row attn_varlen_fwd:
+ * ragged, non-tile-multiple prefill).  Each sequence is independent: its own K mean,
+ * its own causal origin.
+ *
+ *   q    fp16 [total_tokens, Hq, D]   k, v  fp16 [total_tokens, Hkv, D]
+ *   out  fp16 [total_tokens, Hq, D]
+ *   cu_seqlens  int32 [nseq + 1] on the device: cu[0] = 0, non-decreasing,
+ *               cu[nseq] = total_tokens; sequence i is tokens cu[i] .. cu[i+1]-1.
+ *               Zero-length sequences are allowed.  The host cannot read it without a
+ *               synchronization, so it is not checked here; a sequence whose bounds
+ *               fall outside [0, total_tokens] or exceed max_seqlen is skipped by the
+ *               kernels (its output rows are left unwritten) and never causes an
+ *               out-of-bounds access.
+ *   nseq >= 1, total_tokens >= 0, 0 <= max_seqlen <= total_tokens (host values).
+ *   Other arguments as for attn_int8_fwd.
+ */
+i8a_status attn_int8_varlen_fwd(const void* q, const void* k, const void* v, void* out,
+                                const int32_t* cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                                int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t D,
+                                float softmax_scale, int32_t causal, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
+ * attn_int8_debug_qk - debug dump of the quantities the dense forward computes
+ * internally, for one (batch b, query head h).  It runs the forward's own
+ * quantization kernels and its int8 MFMA score path and writes:
+ *   s32_out    int32 [rows, cols]: S32[row0 + i, col0 + j] = q8 . k8 (exact)
+ *   qscale_out nullable fp32 [rows]: sq of the query rows
+ *   kscale_out nullable fp32 [cols]: sk of the key rows (kv head h / (Hq/Hkv))
+ *   vscale_out nullable fp32 [cols]: sv of the same rows
+ *   kmean_out  nullable fp32 [D]:   the K-smoothing mean of that kv head
+ * with 0 <= row0, row0 + rows <= S, 0 <= col0, col0 + cols <= S, rows, cols >= 1.
+ * Inputs, sizes and workspace as for attn_int8_fwd (causal is ignored: scores are
+ * dumped unmasked).
+ */
+i8a_status attn_int8_debug_qk(const void* q, const void* k, const void* v, int32_t B, int32_t Hq,
+                              int32_t Hkv, int32_t S, int32_t D, int32_t b, int32_t h,
+                              int32_t row0, int32_t rows, int32_t col0, int32_t cols,
+                              int32_t* s32_out, float* qscale_out, float* kscale_out,
+                              float* vscale_out, float* kmean_out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Name of a status code (static string). */
+const char* i8a_status_string(i8a_status status);
+
+/* Detail of the last failure on the calling thread (static per-thread buffer). */
+const char* i8a_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* I8ATTN_H */

@@ -1,0 +1,301 @@
+"""INT8 W8A8 FlashAttention forward for AMD MI355X (gfx950).
+
+Thin ctypes binding of ``libi8attn.so`` (the C ABI in ``include/i8attn.h``).  It
+only checks and marshals arguments: every step of the forward runs in the HIP
+kernels of the library.  PyTorch provides device memory and the stream.  There is
+no CPU fallback: if the library is missing or no GPU is present, the calls raise.
+
+Entry points (same names as the C ABI):
+
+* :func:`quant_rowwise_i8` - symmetric per-row int8 quantization.
+* :func:`attn_int8_fwd` - dense forward, q ``[B,Hq,S,D]``, k/v ``[B,Hkv,S,D]``.
+* :func:`attn_int8_varlen_fwd` - packed ragged batch, q ``[T,Hq,D]`` + ``cu_seqlens``.
+* :func:`attn_int8_debug_qk` - the forward's exact int32 scores and scales.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import torch
+
+__all__ = [
+    "quant_rowwise_i8", "attn_int8_fwd", "attn_int8_varlen_fwd", "attn_int8_debug_qk",
+    "attn_int8_prepare_kv", "attn_int8_fwd_prepared",
+    "attn_int8_workspace_bytes", "attn_int8_varlen_workspace_bytes", "library_path",
+    "load_library", "SCALE_FP32", "SCALE_V4", "HEAD_DIMS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libi8attn.so")
+_HEADER = os.path.join(os.path.dirname(_HERE), "include", "i8attn.h")
+
+SCALE_FP32 = 24
+SCALE_V4 = 4
+HEAD_DIMS = (32, 64, 128, 256)
+
+_c_i32, _c_i64, _c_sz, _c_f32, _c_vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                                        ctypes.c_float, ctypes.c_void_p)
+_SIGS = {
+    "quant_rowwise_i8": (_c_i32, [_c_vp, _c_i64, _c_i32, _c_vp, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp]),
+    "attn_int8_workspace_bytes": (_c_sz, [_c_i32] * 5),
+    "attn_int8_fwd": (_c_i32, [_c_vp] * 4 + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_sz, _c_vp]),
+    "attn_int8_varlen_workspace_bytes": (_c_sz, [_c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "attn_int8_varlen_fwd": (_c_i32, [_c_vp] * 5 + [_c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_i32,
+                                                     _c_f32, _c_i32, _c_vp, _c_sz, _c_vp]),
+    "attn_int8_debug_qk": (_c_i32, [_c_vp] * 3 + [_c_i32] * 11 + [_c_vp] * 6 + [_c_sz, _c_vp]),
+    "attn_int8_prepare_kv": (_c_i32, [_c_vp] * 2 + [_c_i32] * 5 + [_c_vp, _c_sz, _c_vp]),
+    "attn_int8_fwd_prepared": (_c_i32, [_c_vp] * 2 + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_sz,
+                                                                     _c_vp]),
+    "i8a_status_string": (ctypes.c_char_p, [_c_i32]),
+    "i8a_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libi8attn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with "
+                "`python -m int8_w8a8_flashattention_amd.build_lib` (there is no CPU fallback)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def header_functions():
+    """Names of the functions declared in include/i8attn.h."""
+    text = open(_HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|size_t|i8a_status)\s+(\w+)\s*\(",
+                                 text, re.M)))
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        lib = load_library()
+        raise RuntimeError(f"{what} failed: {lib.i8a_status_string(status).decode()}: "
+                           f"{lib.i8a_last_error().decode()}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need_gpu_fp16(name, t, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float16:
+        raise ValueError(f"{name} must be float16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _scale(softmax_scale, D):
+    s = (1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale)
+    return ctypes.c_float(s)  # rounded to fp32 here, the value the kernels use
+
+
+def _workspace(workspace, nbytes, dev):
+    if workspace is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must be a buffer of >= {nbytes} bytes on {dev}")
+    return workspace
+
+
+def quant_rowwise_i8(x, mean=None, rows_per_group=None, scale_bits=SCALE_FP32):
+    """Per-row symmetric int8 codes and fp32 scales of fp16 ``x[..., d]``.
+
+    ``mean`` (fp32 ``[groups, d]``) is subtracted from row r in group
+    ``r // rows_per_group`` before quantizing (the K-smoothing subtraction).
+    """
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float16 or not x.is_cuda:
+        raise ValueError("x must be a float16 GPU tensor")
+    if not x.is_contiguous() or x.dim() < 1:
+        raise ValueError("x must be contiguous with at least one dim")
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    codes = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    if mean is not None:
+        if mean.dtype != torch.float32 or mean.device != x.device or not mean.is_contiguous():
+            raise ValueError("mean must be a contiguous float32 tensor on x's device")
+        if mean.shape[-1] != d:
+            raise ValueError("mean's last dim must match x's")
+        if rows_per_group is None or rows_per_group < 1:
+            raise ValueError("rows_per_group must be >= 1 with mean")
+        if mean.numel() // d < -(-rows // rows_per_group):
+            raise ValueError("mean has fewer groups than the rows need")
+    lib = load_library()
+    with torch.cuda.device(x.device):
+        st = lib.quant_rowwise_i8(_ptr(x), rows, d, _ptr(mean), rows_per_group or 1, scale_bits,
+                                  _ptr(codes), _ptr(scales), _stream(x.device))
+    _check(st, "quant_rowwise_i8")
+    return codes, scales
+
+
+def attn_int8_workspace_bytes(B, Hq, Hkv, S, D) -> int:
+    return int(load_library().attn_int8_workspace_bytes(B, Hq, Hkv, S, D))
+
+
+def attn_int8_varlen_workspace_bytes(nseq, total_tokens, max_seqlen, Hq, Hkv, D) -> int:
+    return int(load_library().attn_int8_varlen_workspace_bytes(nseq, total_tokens, max_seqlen,
+                                                               Hq, Hkv, D))
+
+
+def _dense_shapes(q, k, v):
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need_gpu_fp16(n, t, 4)
+    B, Hq, S, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != S or k.shape[3] != D:
+        raise ValueError(f"k/v must be [B, Hkv, S, D] matching q {tuple(q.shape)}; "
+                         f"got {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    Hkv = k.shape[1]
+    if D not in HEAD_DIMS:
+        raise ValueError(f"head dim {D} not in {HEAD_DIMS}")
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"Hq={Hq} must be a multiple of Hkv={Hkv}")
+    return B, Hq, Hkv, S, D
+
+
+def attn_int8_fwd(q, k, v, causal=True, softmax_scale=None, out=None, workspace=None):
+    """INT8 W8A8 attention forward; returns fp16 ``out[B,Hq,S,D]``."""
+    B, Hq, Hkv, S, D = _dense_shapes(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_gpu_fp16("out", out, 4)
+        if out.shape != q.shape or out.device != q.device:
+            raise ValueError("out must match q")
+    lib = load_library()
+    nbytes = lib.attn_int8_workspace_bytes(B, Hq, Hkv, S, D)
+    ws = _workspace(workspace, nbytes, q.device)
+    with torch.cuda.device(q.device):
+        st = lib.attn_int8_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, S, D,
+                               _scale(softmax_scale, D), int(bool(causal)), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(q.device))
+    _check(st, "attn_int8_fwd")
+    return out
+
+
+def attn_int8_prepare_kv(k, v, Hq, workspace=None):
+    """First phase of :func:`attn_int8_fwd`: K-smoothing mean and K/V quantization of
+    dense k/v ``[B,Hkv,S,D]`` into a workspace, returned for
+    :func:`attn_int8_fwd_prepared`."""
+    for n, t in (("k", k), ("v", v)):
+        _need_gpu_fp16(n, t, 4)
+    if k.shape != v.shape or k.device != v.device:
+        raise ValueError("k and v must match")
+    B, Hkv, S, D = k.shape
+    if D not in HEAD_DIMS or Hq % Hkv:
+        raise ValueError("bad head dim or Hq")
+    lib = load_library()
+    ws = _workspace(workspace, lib.attn_int8_workspace_bytes(B, Hq, Hkv, S, D), k.device)
+    with torch.cuda.device(k.device):
+        st = lib.attn_int8_prepare_kv(_ptr(k), _ptr(v), B, Hq, Hkv, S, D, _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(k.device))
+    _check(st, "attn_int8_prepare_kv")
+    return ws
+
+
+def attn_int8_fwd_prepared(q, Hkv, workspace, causal=True, softmax_scale=None, out=None):
+    """Second phase of :func:`attn_int8_fwd`: attention of dense q ``[B,Hq,S,D]``
+    against a workspace filled by :func:`attn_int8_prepare_kv` for the same sizes."""
+    _need_gpu_fp16("q", q, 4)
+    B, Hq, S, D = q.shape
+    if D not in HEAD_DIMS or Hkv < 1 or Hq % Hkv:
+        raise ValueError("bad head dim or Hkv")
+    if out is None:
+        out = torch.empty_like(q)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.attn_int8_fwd_prepared(_ptr(q), _ptr(out), B, Hq, Hkv, S, D,
+                                        _scale(softmax_scale, D), int(bool(causal)),
+                                        _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(q.device))
+    _check(st, "attn_int8_fwd_prepared")
+    return out
+
+
+def attn_int8_varlen_fwd(q, k, v, cu_seqlens, max_seqlen, causal=True, softmax_scale=None,
+                         out=None, workspace=None):
+    """Forward over packed sequences: q ``[T,Hq,D]``, k/v ``[T,Hkv,D]``, int32
+    ``cu_seqlens[nseq+1]`` on the same GPU; ``max_seqlen`` (host int) bounds
+    every sequence length.  Returns fp16 ``out[T,Hq,D]``."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need_gpu_fp16(n, t, 3)
+    T, Hq, D = q.shape
+    if k.shape != v.shape or k.shape[0] != T or k.shape[2] != D:
+        raise ValueError("k/v must be [T, Hkv, D] matching q")
+    Hkv = k.shape[1]
+    if D not in HEAD_DIMS:
+        raise ValueError(f"head dim {D} not in {HEAD_DIMS}")
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"Hq={Hq} must be a multiple of Hkv={Hkv}")
+    if (not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32
+            or cu_seqlens.device != q.device or cu_seqlens.dim() != 1
+            or cu_seqlens.numel() < 2 or not cu_seqlens.is_contiguous()):
+        raise ValueError("cu_seqlens must be a contiguous int32 [nseq+1] tensor on q's device")
+    nseq = cu_seqlens.numel() - 1
+    max_seqlen = int(max_seqlen)
+    if out is None:
+        out = torch.empty_like(q)
+    lib = load_library()
+    nbytes = lib.attn_int8_varlen_workspace_bytes(nseq, T, max_seqlen, Hq, Hkv, D)
+    if nbytes == 0 and T > 0:
+        raise ValueError("invalid varlen sizes")
+    ws = _workspace(workspace, nbytes, q.device)
+    with torch.cuda.device(q.device):
+        st = lib.attn_int8_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens),
+                                      nseq, max_seqlen, T, Hq, Hkv, D,
+                                      _scale(softmax_scale, D), int(bool(causal)), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(q.device))
+    _check(st, "attn_int8_varlen_fwd")
+    return out
+
+
+def attn_int8_debug_qk(q, k, v, b, h, row0, rows, col0, cols, workspace=None):
+    """The dense forward's exact int32 scores ``S32[row0:row0+rows, col0:col0+cols]``
+    of (batch b, query head h), with the row scales and the K mean it used."""
+    B, Hq, Hkv, S, D = _dense_shapes(q, k, v)
+    dev = q.device
+    s32 = torch.empty((rows, cols), dtype=torch.int32, device=dev)
+    qs = torch.empty(rows, dtype=torch.float32, device=dev)
+    ks = torch.empty(cols, dtype=torch.float32, device=dev)
+    vs = torch.empty(cols, dtype=torch.float32, device=dev)
+    km = torch.empty(D, dtype=torch.float32, device=dev)
+    lib = load_library()
+    nbytes = lib.attn_int8_workspace_bytes(B, Hq, Hkv, S, D)
+    ws = _workspace(workspace, nbytes, dev)
+    with torch.cuda.device(dev):
+        st = lib.attn_int8_debug_qk(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, S, D, b, h, row0, rows,
+                                    col0, cols, _ptr(s32), _ptr(qs), _ptr(ks), _ptr(vs), _ptr(km),
+                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
+    _check(st, "attn_int8_debug_qk")
+    return dict(s32=s32, qscale=qs, kscale=ks, vscale=vs, kmean=km)

@@ -1,0 +1,405 @@
+// attn_kernels.hip - the INT8 W8A8 FlashAttention-2 forward on gfx950.
+//
+// One workgroup = 4 waves = 128 query rows of one head.  Each wave owns 32 rows and
+// keeps, per lane, one query's running max, sum and 32 x D output accumulator
+// column.  Per 64-key tile:
+//   S^T = K . Q^T     v_mfma_i32_32x32x32_i8   (exact int32)
+//   t   = f32(S^T) * sk_j                      (the query scale and softmax scale are
+//   p   = exp2(t * qsc - M)                     one per-lane factor qsc)
+//   O^T += V^T . P^T  v_mfma_f32_32x32x16_f16  (P rounded to fp16, V exact in fp16)
+//   l   += sum of the same fp16 P values      (v_dot2_f32_f16)
+// so the normalized output is a weighted mean with identical weights in numerator
+// and denominator.  The running max M is only raised (with a rescale of O and l)
+// when a tile's max exceeds it by more than TAU in log2 units, which bounds every
+// p by 2^TAU and skips most rescales.
+//
+// K (int8) and the exact fp16 V come from the workspace in MFMA fragment order, so
+// the global->LDS copy is linear and every LDS operand read is a conflict-free
+// 16-byte read.  Q is quantized in the prologue (each query row is read by exactly
+// one workgroup) with the same row rule as the preparation kernels.
+#include "i8a_device.h"
+#include "i8a_launch.h"
+
+namespace i8a {
+
+constexpr int BM = 128;      // query rows per workgroup
+constexpr float TAU = 8.0f;  // lazy-rescale threshold, log2 units
+
+template <int D>
+struct Lay {
+  static constexpr int NKB = D / 32;             // 32-wide blocks of the head dim
+  static constexpr int KB = TK * D;              // bytes of the int8 K tile
+  static constexpr int VB = TK * D * 2;          // bytes of the fp16 V tile
+  static constexpr int SB = TK * 4;              // bytes of the K scales
+  static constexpr int STAGE = KB + VB + SB;     // one pipeline stage
+  static constexpr int KCH = KB / 16, VCH = VB / 16;  // 16-byte chunks
+  static constexpr int KR = (KCH + 255) / 256, VR = (VCH + 255) / 256;
+  static_assert(BM * D + BM * 4 <= STAGE, "Q staging fits in one stage");
+};
+
+// Quantize the 32 query rows q_first.. of head h (one wave) into Q fragments in LDS
+// (layout qfrag_off) and their scales.  Rows at or beyond L quantize as zero rows.
+template <int D>
+__device__ __forceinline__ void quant_q_rows(const _Float16* __restrict__ q, const Act& aq,
+                                             int64_t start, int h, int q_first, int L,
+                                             int8_t* frag, float* qscale) {
+  constexpr int G = D / 8;
+  constexpr int RPP = 64 / G;
+  const int lane = threadIdx.x & 63, lc = lane % G, rs = lane / G;
+#pragma unroll
+  for (int m0 = 0; m0 < 32; m0 += RPP) {
+    const int m = m0 + rs;
+    const int t = q_first + m;
+    const bool real = t < L;
+    float x[8];
+    float amax = 0.0f;
+    if (real) {
+      load8_f32(q + aq.off(start, h, t) + lc * 8, x);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+    }
+    amax = group_max<G>(amax);
+    const float s = real ? row_scale(amax, 24) : 0.0f;
+    uint32_t lo = 0, hi = 0;
+    if (real) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lo |= ((uint32_t)quant_code(x[j], s) & 255u) << (8 * j);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hi |= ((uint32_t)quant_code(x[4 + j], s) & 255u) << (8 * j);
+    }
+    *reinterpret_cast<uint2*>(frag + qfrag_off(m, lc * 8)) = make_uint2(lo, hi);
+    if (lc == 0) qscale[m] = s;
+  }
+}
+
+// Work item of a workgroup: query tile (heaviest first), sequence and head.  With
+// xcd_map the heads of one kv group land on blocks with the same id mod 8, i.e. on
+// one XCD (blocks are dispatched round-robin over the 8 XCDs), so that group's K/V
+// stays in that XCD's L2.
+__device__ __forceinline__ void decode_work(int bid, int nseq, int Hq, int Hkv, int nqt,
+                                            int xcd_map, int& qt, int& s, int& h) {
+  const int nbh = nseq * Hq;
+  qt = nqt - 1 - bid / nbh;
+  const int r = bid % nbh;
+  if (xcd_map) {
+    const int G = Hq / Hkv;
+    const int x = r & 7, kk = r >> 3;
+    const int grp = x + 8 * (kk / G);
+    s = grp / Hkv;
+    h = (grp % Hkv) * G + kk % G;
+  } else {
+    s = r / Hq;
+    h = r % Hq;
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+    const _Float16* __restrict__ q, _Float16* __restrict__ out, Act aq, Seqs seqs, int Hq,
+    int Hkv, int nseq, int nqt, int xcd_map, float qk_log2, const int8_t* __restrict__ k8_ws,
+    const _Float16* __restrict__ vh_ws, const float* __restrict__ sk_ws, int64_t Ppad) {
+  using LY = Lay<D>;
+  constexpr int NKB = LY::NKB;
+  __shared__ __attribute__((aligned(16))) char smem[2 * LY::STAGE];
+
+  int qt, s, h;
+  decode_work(blockIdx.x, nseq, Hq, Hkv, nqt, xcd_map, qt, s, h);
+  int64_t start;
+  int L;
+  seqs.bounds(s, start, L);
+  const int q0 = qt * BM;
+  if (q0 >= L) return;
+  const int g = h / (Hq / Hkv);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 31, hh = lane >> 5;
+  const int qw0 = q0 + 32 * w;
+
+  const int ntile_seq = (L + TK - 1) / TK;
+  const int nt = CAUSAL ? min(ntile_seq, (min(q0 + BM, L) - 1) / TK + 1) : ntile_seq;
+  const int64_t pbase = Seqs::pstart(s, start);
+  const v4i* kglob = reinterpret_cast<const v4i*>(k8_ws + ((int64_t)g * Ppad + pbase) * D);
+  const v4i* vglob = reinterpret_cast<const v4i*>(vh_ws + ((int64_t)g * Ppad + pbase) * D);
+  const float* skglob = sk_ws + (int64_t)g * Ppad + pbase;
+
+  // Register-staged tile loader (global -> regs -> LDS).
+  v4i kreg[LY::KR], vreg[LY::VR];
+  v4f sreg;
+  auto load_tile = [&](int j) {
+    const v4i* kp = kglob + (int64_t)j * LY::KCH;
+    const v4i* vp = vglob + (int64_t)j * LY::VCH;
+#pragma unroll
+    for (int i = 0; i < LY::KR; ++i)
+      if (tid + 256 * i < LY::KCH) kreg[i] = kp[tid + 256 * i];
+#pragma unroll
+    for (int i = 0; i < LY::VR; ++i)
+      if (tid + 256 * i < LY::VCH) vreg[i] = vp[tid + 256 * i];
+    if (tid < TK / 4) sreg = reinterpret_cast<const v4f*>(skglob + (int64_t)j * TK)[tid];
+  };
+  auto store_tile = [&](int stage) {
+    char* st = smem + stage * LY::STAGE;
+#pragma unroll
+    for (int i = 0; i < LY::KR; ++i)
+      if (tid + 256 * i < LY::KCH) reinterpret_cast<v4i*>(st)[tid + 256 * i] = kreg[i];
+#pragma unroll
+    for (int i = 0; i < LY::VR; ++i)
+      if (tid + 256 * i < LY::VCH) reinterpret_cast<v4i*>(st + LY::KB)[tid + 256 * i] = vreg[i];
+    if (tid < TK / 4) reinterpret_cast<v4f*>(st + LY::KB + LY::VB)[tid] = sreg;
+  };
+
+  // Prologue: tile 0 in flight while Q is quantized into the stage-1 region.
+  load_tile(0);
+  int8_t* qstage = reinterpret_cast<int8_t*>(smem + LY::STAGE);
+  float* qscl = reinterpret_cast<float*>(smem + LY::STAGE + BM * D);
+  quant_q_rows<D>(q, aq, start, h, qw0, L, qstage + w * 32 * D, qscl + 32 * w);
+  store_tile(0);
+  __syncthreads();
+  v4i qf[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+    qf[kb] = reinterpret_cast<const v4i*>(qstage + w * 32 * D)[kb * 64 + lane];
+  const float qsc = qscl[32 * w + m] * qk_log2;
+  __syncthreads();
+
+  v16f o[NKB];
+#pragma unroll
+  for (int db = 0; db < NKB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
+  float mrun = -INFINITY, lsum = 0.0f;
+  const int qi = qw0 + m;
+
+  for (int j = 0; j < nt; ++j) {
+    if (j + 1 < nt) load_tile(j + 1);
+    const int kt0 = j * TK;
+    if (!CAUSAL || kt0 <= qw0 + 31) {
+      const char* st = smem + (j & 1) * LY::STAGE;
+      const v4i* kl = reinterpret_cast<const v4i*>(st);
+      const v4i* vl = reinterpret_cast<const v4i*>(st + LY::KB);
+      const float* skl = reinterpret_cast<const float*>(st + LY::KB + LY::VB);
+
+      v16i acc[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[nb][i] = 0;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          acc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kl[(nb * NKB + kb) * 64 + lane], qf[kb],
+                                                          acc[nb], 0, 0, 0);
+      }
+
+      float tv[32];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          const v4f skv = *reinterpret_cast<const v4f*>(skl + 32 * nb + 8 * J + 4 * hh);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tv[16 * nb + 4 * J + r] = (float)acc[nb][4 * J + r] * skv[r];
+        }
+      // Masked keys (above the diagonal, past the sequence end) get t = -inf for the
+      // max and p = 0 after the exponential; the weight is zeroed explicitly because
+      // an all-zero query row has qsc = 0 and -inf * 0 is not a number.
+      const bool masked_tile = (CAUSAL && kt0 + TK - 1 > qw0) || kt0 + TK > L;
+      uint32_t keep = 0xffffffffu;
+      if (masked_tile) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int key = kt0 + 32 * (i >> 4) + 8 * ((i >> 2) & 3) + 4 * hh + (i & 3);
+          if ((CAUSAL && key > qi) || key >= L) {
+            tv[i] = -INFINITY;
+            keep &= ~(1u << i);
+          }
+        }
+      }
+      float mx = tv[0];
+#pragma unroll
+      for (int i = 1; i < 32; ++i) mx = fmaxf(mx, tv[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mc = mx == -INFINITY ? -INFINITY : mx * qsc;
+      const bool upd = mc > mrun + TAU;
+      if (__any(upd)) {
+        const float mnew = upd ? mc : mrun;
+        const float alpha = upd ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.0f;
+        mrun = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < NKB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      }
+      const float muse = mrun == -INFINITY ? 0.0f : mrun;
+
+      v8h pk[4];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(tv[i], qsc, -muse));
+        if (masked_tile) p = (keep >> i) & 1u ? p : 0.0f;
+        pk[i >> 3][i & 7] = (_Float16)p;
+      }
+      const v2h ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const v2h pr = {pk[kg][e], pk[kg][e + 1]};
+          lsum = __builtin_amdgcn_fdot2(pr, ones, lsum, false);
+        }
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+        for (int db = 0; db < NKB; ++db) {
+          const v4i va = vl[(kg * NKB + db) * 64 + lane];
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, va), pk[kg],
+                                                          o[db], 0, 0, 0);
+        }
+    }
+    if (j + 1 < nt) store_tile((j + 1) & 1);
+    __syncthreads();
+  }
+
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (qi < L) {
+    const float inv = 1.0f / lsum;
+    _Float16* orow = out + aq.off(start, h, qi);
+#pragma unroll
+    for (int db = 0; db < NKB; ++db)
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        v4h o4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o4[r] = (_Float16)(o[db][4 * J + r] * inv);
+        *reinterpret_cast<v4h*>(orow + 32 * db + 8 * J + 4 * hh) = o4;
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------------
+// Debug: the int32 score tile through the forward's own Q quantization and K
+// fragments (read straight from the workspace), one wave per aligned 32x32 block.
+template <int D>
+__global__ __launch_bounds__(64) void debug_qk_kernel(
+    const _Float16* __restrict__ q, Act aq, int S, int Hq, int Hkv, int b, int h, int row0,
+    int rows, int col0, int cols, const int8_t* __restrict__ k8_ws,
+    const float* __restrict__ sk_ws, const float* __restrict__ sv_ws,
+    const float* __restrict__ kmean_ws, int64_t Ppad, int32_t* __restrict__ s32,
+    float* __restrict__ qscale, float* __restrict__ kscale, float* __restrict__ vscale,
+    float* __restrict__ kmean_out) {
+  constexpr int NKB = D / 32;
+  __shared__ __attribute__((aligned(16))) int8_t frag[32 * D];
+  __shared__ float qs[32];
+  const int lane = threadIdx.x, m = lane & 31, hh = lane >> 5;
+  const int qbase = (row0 & ~31) + 32 * blockIdx.x;
+  const int kbase = (col0 & ~31) + 32 * blockIdx.y;
+  const int64_t start = (int64_t)b * S;
+  const int g = h / (Hq / Hkv);
+  const int64_t pbase = Seqs::pstart(b, start);
+
+  quant_q_rows<D>(q, aq, start, h, qbase, S, frag, qs);
+  __syncthreads();
+  v4i qf[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) qf[kb] = reinterpret_cast<const v4i*>(frag)[kb * 64 + lane];
+
+  const int tile0 = kbase - kbase % TK, nb = (kbase % TK) / 32;
+  const v4i* kt = reinterpret_cast<const v4i*>(k8_ws + ((int64_t)g * Ppad + pbase + tile0) * D);
+  v16i acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kt[(nb * NKB + kb) * 64 + lane], qf[kb], acc, 0,
+                                                0, 0);
+  const int qrow = qbase + m;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int n = kbase + 8 * (i >> 2) + 4 * hh + (i & 3);
+    if (qrow >= row0 && qrow < row0 + rows && n >= col0 && n < col0 + cols)
+      s32[(int64_t)(qrow - row0) * cols + (n - col0)] = acc[i];
+  }
+  if (qscale && blockIdx.y == 0 && hh == 0 && qrow >= row0 && qrow < row0 + rows)
+    qscale[qrow - row0] = qs[m];
+  const int n = kbase + m;
+  if (blockIdx.x == 0 && hh == 0 && n >= col0 && n < col0 + cols) {
+    if (kscale) kscale[n - col0] = sk_ws[(int64_t)g * Ppad + pbase + n];
+    if (vscale) vscale[n - col0] = sv_ws[(int64_t)g * Ppad + pbase + n];
+  }
+  if (kmean_out && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int d = lane; d < D; d += 64) kmean_out[d] = kmean_ws[((int64_t)b * Hkv + g) * D + d];
+}
+
+// ----------------------------------------------------------------------------------
+static Act act_of(const FwdGeom& g, int H) {
+  Act a;
+  a.seq_unit = (int64_t)H * g.D;
+  if (g.cu) {
+    a.head_stride = g.D;
+    a.tok_stride = (int64_t)H * g.D;
+  } else {
+    a.head_stride = (int64_t)g.S * g.D;
+    a.tok_stride = g.D;
+  }
+  return a;
+}
+
+template <int D, bool C>
+static hipError_t attn_d(const FwdGeom& g, const WsPlan& p, const void* ws, hipStream_t stream) {
+  const char* w = static_cast<const char*>(ws);
+  const int nqt = (g.max_len + BM - 1) / BM;
+  const int64_t blocks = (int64_t)nqt * g.nseq * g.Hq;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const int ngroups = g.nseq * g.Hkv;
+  const int xcd_map = ((g.nseq * g.Hq) % 8 == 0 && ngroups % 8 == 0) ? 1 : 0;
+  const float qk_log2 = g.softmax_scale * 1.4426950408889634f;
+  Seqs sq{g.cu, g.S, g.max_len, g.T};
+  attn_fwd_kernel<D, C><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+      static_cast<const _Float16*>(g.q), static_cast<_Float16*>(g.out), act_of(g, g.Hq), sq,
+      g.Hq, g.Hkv, g.nseq, nqt, xcd_map, qk_log2, reinterpret_cast<const int8_t*>(w + p.off_k8),
+      reinterpret_cast<const _Float16*>(w + p.off_vh), reinterpret_cast<const float*>(w + p.off_sk),
+      p.Ppad);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn(const FwdGeom& g, const WsPlan& p, const void* ws, hipStream_t stream) {
+#define I8A_ATT(DD)                                            \
+  case DD:                                                     \
+    return g.causal ? attn_d<DD, true>(g, p, ws, stream)       \
+                    : attn_d<DD, false>(g, p, ws, stream);
+  switch (g.D) {
+    I8A_ATT(32) I8A_ATT(64) I8A_ATT(128) I8A_ATT(256)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef I8A_ATT
+}
+
+template <int D>
+static hipError_t debug_d(const FwdGeom& g, const WsPlan& p, const void* ws, int b, int h,
+                          int row0, int rows, int col0, int cols, int32_t* s32, float* qscale,
+                          float* kscale, float* vscale, float* kmean, hipStream_t stream) {
+  const char* w = static_cast<const char*>(ws);
+  const int rb = ((row0 + rows - 1) >> 5) - (row0 >> 5) + 1;
+  const int cb = ((col0 + cols - 1) >> 5) - (col0 >> 5) + 1;
+  debug_qk_kernel<D><<<dim3(rb, cb), dim3(64), 0, stream>>>(
+      static_cast<const _Float16*>(g.q), act_of(g, g.Hq), g.S, g.Hq, g.Hkv, b, h, row0, rows,
+      col0, cols, reinterpret_cast<const int8_t*>(w + p.off_k8),
+      reinterpret_cast<const float*>(w + p.off_sk), reinterpret_cast<const float*>(w + p.off_sv),
+      reinterpret_cast<const float*>(w + p.off_kmean), p.Ppad, s32, qscale, kscale, vscale,
+      kmean);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_qk(const FwdGeom& g, const WsPlan& p, const void* ws, int32_t b,
+                           int32_t h, int32_t row0, int32_t rows, int32_t col0, int32_t cols,
+                           int32_t* s32, float* qscale, float* kscale, float* vscale,
+                           float* kmean, hipStream_t stream) {
+  switch (g.D) {
+    case 32: return debug_d<32>(g, p, ws, b, h, row0, rows, col0, cols, s32, qscale, kscale, vscale, kmean, stream);
+    case 64: return debug_d<64>(g, p, ws, b, h, row0, rows, col0, cols, s32, qscale, kscale, vscale, kmean, stream);
+    case 128: return debug_d<128>(g, p, ws, b, h, row0, rows, col0, cols, s32, qscale, kscale, vscale, kmean, stream);
+    case 256: return debug_d<256>(g, p, ws, b, h, row0, rows, col0, cols, s32, qscale, kscale, vscale, kmean, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace i8a

@@ -1,0 +1,252 @@
+// capi.hip - the extern "C" entry points declared in include/i8attn.h: argument
+// validation (all on the host, before anything is enqueued), workspace planning and
+// launch sequencing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "i8a_launch.h"
+#include "i8attn.h"
+
+namespace i8a {
+
+static thread_local char g_last_error[512] = "";
+
+static i8a_status fail(i8a_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+static i8a_status hip_fail(hipError_t e, const char* what) {
+  return fail(I8A_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsPlan plan_workspace(int32_t nseq, int64_t total_tokens, int32_t max_len, int32_t Hkv,
+                      int32_t D) {
+  WsPlan p;
+  p.nseq = nseq;
+  p.Hkv = Hkv;
+  p.D = D;
+  p.nch = (max_len + CH - 1) / CH;
+  p.Ppad = (int64_t)TK * ((total_tokens + TK - 1) / TK + nseq);
+  size_t off = 0;
+  p.off_kpart = off;
+  off = align256(off + (size_t)nseq * Hkv * p.nch * D * 8);
+  p.off_kmean = off;
+  off = align256(off + (size_t)nseq * Hkv * D * 4);
+  p.off_sk = off;
+  off = align256(off + (size_t)Hkv * p.Ppad * 4);
+  p.off_sv = off;
+  off = align256(off + (size_t)Hkv * p.Ppad * 4);
+  p.off_k8 = off;
+  off = align256(off + (size_t)Hkv * p.Ppad * D);
+  p.off_vh = off;
+  off = align256(off + (size_t)Hkv * p.Ppad * D * 2);
+  p.total = off;
+  return p;
+}
+
+static bool head_dim_ok(int32_t D) { return D == 32 || D == 64 || D == 128 || D == 256; }
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Common checks of the forward entry points.  Sizes in tokens are bounded so that
+// every element offset fits in int64 and every token index in int32.
+static i8a_status check_common(const void* q, const void* k, const void* v, const void* out,
+                               int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                               int32_t causal, const void* ws) {
+  if (!q || !k || !v || !out) return fail(I8A_ERR_INVALID_ARG, "null q/k/v/out pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(I8A_ERR_INVALID_ARG, "q/k/v/out must be 16-byte aligned");
+  if (!head_dim_ok(D))
+    return fail(I8A_ERR_UNSUPPORTED_HEAD_DIM, "head dim %d not in {32,64,128,256}", D);
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return fail(I8A_ERR_INVALID_ARG, "need Hq >= 1, Hkv >= 1 and Hq %% Hkv == 0 (Hq=%d Hkv=%d)",
+                Hq, Hkv);
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale))
+    return fail(I8A_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (causal != 0 && causal != 1) return fail(I8A_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!ws) return fail(I8A_ERR_INVALID_ARG, "null workspace");
+  if (!aligned(ws, 256)) return fail(I8A_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return I8A_OK;
+}
+
+static const int64_t kMaxTokens = (int64_t)1 << 30;
+
+}  // namespace i8a
+
+using namespace i8a;
+
+extern "C" {
+
+const char* i8a_status_string(i8a_status s) {
+  switch (s) {
+    case I8A_OK: return "I8A_OK";
+    case I8A_ERR_INVALID_ARG: return "I8A_ERR_INVALID_ARG";
+    case I8A_ERR_UNSUPPORTED_HEAD_DIM: return "I8A_ERR_UNSUPPORTED_HEAD_DIM";
+    case I8A_ERR_WORKSPACE_TOO_SMALL: return "I8A_ERR_WORKSPACE_TOO_SMALL";
+    case I8A_ERR_HIP: return "I8A_ERR_HIP";
+    default: return "I8A_UNKNOWN_STATUS";
+  }
+}
+
+const char* i8a_last_error(void) { return g_last_error; }
+
+i8a_status quant_rowwise_i8(const void* x, int64_t rows, int32_t d, const float* sub_mean,
+                            int64_t rows_per_group, int32_t scale_bits, int8_t* codes,
+                            float* scales, void* stream) {
+  if (rows < 0) return fail(I8A_ERR_INVALID_ARG, "rows must be >= 0");
+  if (d < 8 || d > 512 || d % 8 != 0)
+    return fail(I8A_ERR_INVALID_ARG, "d must be a multiple of 8 in [8, 512] (got %d)", d);
+  if (scale_bits != I8A_SCALE_FP32 && scale_bits != I8A_SCALE_V4)
+    return fail(I8A_ERR_INVALID_ARG, "scale_bits must be 24 or 4");
+  if (sub_mean && rows_per_group < 1)
+    return fail(I8A_ERR_INVALID_ARG, "rows_per_group must be >= 1 with sub_mean");
+  if (rows == 0) return I8A_OK;
+  if (!x || !codes || !scales) return fail(I8A_ERR_INVALID_ARG, "null x/codes/scales pointer");
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(scales, 4) ||
+      (sub_mean && !aligned(sub_mean, 4)))
+    return fail(I8A_ERR_INVALID_ARG, "misaligned pointer (x 16 B, codes 8 B, floats 4 B)");
+  hipError_t e = launch_quant_rowwise(x, rows, d, sub_mean, sub_mean ? rows_per_group : 1,
+                                      scale_bits, codes, scales, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "quant_rowwise_i8 launch");
+  return I8A_OK;
+}
+
+size_t attn_int8_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D) {
+  if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || !head_dim_ok(D)) return 0;
+  if ((int64_t)B * S > kMaxTokens) return 0;
+  return plan_workspace(B, (int64_t)B * S, S, Hkv, D).total;
+}
+
+size_t attn_int8_varlen_workspace_bytes(int32_t nseq, int64_t total_tokens, int32_t max_seqlen,
+                                        int32_t Hq, int32_t Hkv, int32_t D) {
+  if (nseq < 1 || total_tokens < 0 || total_tokens > kMaxTokens || max_seqlen < 0 ||
+      max_seqlen > total_tokens || Hq < 1 || Hkv < 1 || Hq % Hkv || !head_dim_ok(D))
+    return 0;
+  return plan_workspace(nseq, total_tokens, max_seqlen, Hkv, D).total;
+}
+
+static i8a_status run_forward(const FwdGeom& g, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const WsPlan p = plan_workspace(g.nseq, g.T, g.max_len, g.Hkv, g.D);
+  if (ws_bytes < p.total)
+    return fail(I8A_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", p.total,
+                ws_bytes);
+  hipError_t e = launch_prep(g, p, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
+  e = launch_attn(g, p, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return I8A_OK;
+}
+
+i8a_status attn_int8_fwd(const void* q, const void* k, const void* v, void* out, int32_t B,
+                         int32_t Hq, int32_t Hkv, int32_t S, int32_t D, float softmax_scale,
+                         int32_t causal, void* workspace, size_t workspace_bytes, void* stream) {
+  i8a_status st = check_common(q, k, v, out, Hq, Hkv, D, softmax_scale, causal, workspace);
+  if (st != I8A_OK) return st;
+  if (B < 1 || S < 1) return fail(I8A_ERR_INVALID_ARG, "need B >= 1 and S >= 1");
+  if ((int64_t)B * S > kMaxTokens) return fail(I8A_ERR_INVALID_ARG, "B*S too large");
+  FwdGeom g{q, k, v, out, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D, softmax_scale, causal};
+  return run_forward(g, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+i8a_status attn_int8_prepare_kv(const void* k, const void* v, int32_t B, int32_t Hq, int32_t Hkv,
+                                int32_t S, int32_t D, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  // q and out are not touched by this phase; k stands in for their checks.
+  i8a_status st = check_common(k, k, v, k, Hq, Hkv, D, 1.0f, 0, workspace);
+  if (st != I8A_OK) return st;
+  if (B < 1 || S < 1 || (int64_t)B * S > kMaxTokens)
+    return fail(I8A_ERR_INVALID_ARG, "need B >= 1, S >= 1, B*S in range");
+  FwdGeom g{nullptr, k, v, nullptr, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D, 1.0f, 0};
+  const WsPlan p = plan_workspace(B, (int64_t)B * S, S, Hkv, D);
+  if (workspace_bytes < p.total)
+    return fail(I8A_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", p.total,
+                workspace_bytes);
+  hipError_t e = launch_prep(g, p, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
+  return I8A_OK;
+}
+
+i8a_status attn_int8_fwd_prepared(const void* q, void* out, int32_t B, int32_t Hq, int32_t Hkv,
+                                  int32_t S, int32_t D, float softmax_scale, int32_t causal,
+                                  const void* workspace, size_t workspace_bytes, void* stream) {
+  // k and v are not read by this phase; q stands in for their checks.
+  i8a_status st = check_common(q, q, q, out, Hq, Hkv, D, softmax_scale, causal, workspace);
+  if (st != I8A_OK) return st;
+  if (B < 1 || S < 1 || (int64_t)B * S > kMaxTokens)
+    return fail(I8A_ERR_INVALID_ARG, "need B >= 1, S >= 1, B*S in range");
+  FwdGeom g{q, nullptr, nullptr, out, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D,
+            softmax_scale, causal};
+  const WsPlan p = plan_workspace(B, (int64_t)B * S, S, Hkv, D);
+  if (workspace_bytes < p.total)
+    return fail(I8A_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", p.total,
+                workspace_bytes);
+  hipError_t e = launch_attn(g, p, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return I8A_OK;
+}
+
+i8a_status attn_int8_varlen_fwd(const void* q, const void* k, const void* v, void* out,
+                                const int32_t* cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                                int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t D,
+                                float softmax_scale, int32_t causal, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!cu_seqlens) return fail(I8A_ERR_INVALID_ARG, "null cu_seqlens");
+  if (!aligned(cu_seqlens, 4)) return fail(I8A_ERR_INVALID_ARG, "misaligned cu_seqlens");
+  if (nseq < 1) return fail(I8A_ERR_INVALID_ARG, "nseq must be >= 1");
+  if (total_tokens < 0 || total_tokens > kMaxTokens)
+    return fail(I8A_ERR_INVALID_ARG, "total_tokens out of range");
+  if (max_seqlen < 0 || max_seqlen > total_tokens)
+    return fail(I8A_ERR_INVALID_ARG, "need 0 <= max_seqlen <= total_tokens");
+  if (total_tokens == 0 || max_seqlen == 0) {
+    // nothing to compute; still validate the rest for a consistent contract
+    if (!head_dim_ok(D))
+      return fail(I8A_ERR_UNSUPPORTED_HEAD_DIM, "head dim %d not in {32,64,128,256}", D);
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(I8A_ERR_INVALID_ARG, "bad Hq/Hkv");
+    return I8A_OK;
+  }
+  i8a_status st = check_common(q, k, v, out, Hq, Hkv, D, softmax_scale, causal, workspace);
+  if (st != I8A_OK) return st;
+  FwdGeom g{q, k, v, out, cu_seqlens, nseq, 0, max_seqlen, total_tokens, Hq, Hkv, D,
+            softmax_scale, causal};
+  return run_forward(g, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+i8a_status attn_int8_debug_qk(const void* q, const void* k, const void* v, int32_t B, int32_t Hq,
+                              int32_t Hkv, int32_t S, int32_t D, int32_t b, int32_t h,
+                              int32_t row0, int32_t rows, int32_t col0, int32_t cols,
+                              int32_t* s32_out, float* qscale_out, float* kscale_out,
+                              float* vscale_out, float* kmean_out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  // `out` is not written by this entry; q stands in for the alignment check.
+  i8a_status st = check_common(q, k, v, q, Hq, Hkv, D, 1.0f, 0, workspace);
+  if (st != I8A_OK) return st;
+  if (B < 1 || S < 1 || (int64_t)B * S > kMaxTokens)
+    return fail(I8A_ERR_INVALID_ARG, "need B >= 1, S >= 1, B*S in range");
+  if (b < 0 || b >= B || h < 0 || h >= Hq) return fail(I8A_ERR_INVALID_ARG, "b/h out of range");
+  if (rows < 1 || cols < 1 || row0 < 0 || col0 < 0 || (int64_t)row0 + rows > S ||
+      (int64_t)col0 + cols > S)
+    return fail(I8A_ERR_INVALID_ARG, "tile [%d+%d, %d+%d] outside [0, %d)", row0, rows, col0,
+                cols, S);
+  if (!s32_out || !aligned(s32_out, 4)) return fail(I8A_ERR_INVALID_ARG, "bad s32_out");
+  FwdGeom g{q, k, v, nullptr, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D, 1.0f, 0};
+  const WsPlan p = plan_workspace(B, (int64_t)B * S, S, Hkv, D);
+  if (workspace_bytes < p.total)
+    return fail(I8A_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", p.total,
+                workspace_bytes);
+  hipError_t e = launch_prep(g, p, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
+  e = launch_debug_qk(g, p, workspace, b, h, row0, rows, col0, cols, s32_out, qscale_out,
+                      kscale_out, vscale_out, kmean_out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "debug score launch");
+  return I8A_OK;
+}
+
+}  // extern "C"

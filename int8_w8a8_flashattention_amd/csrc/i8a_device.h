@@ -1,0 +1,145 @@
+// i8a_device.h - device-side types, layouts and quantization steps shared by the
+// kernels of the INT8 W8A8 attention forward (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "i8a_launch.h"
+
+namespace i8a {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+
+// Where the tokens of sequence s live.  Dense batches are the special case
+// cu == nullptr, start(s) = s * S, len(s) = S.  Sequences whose bounds are not
+// inside [0, T] or exceed max_len read as empty, so a malformed cu_seqlens can
+// never send a kernel out of bounds.
+struct Seqs {
+  const int32_t* cu;
+  int32_t S;        // dense length
+  int32_t max_len;  // longest sequence allowed
+  int64_t T;        // total tokens
+  __device__ __forceinline__ void bounds(int s, int64_t& start, int& len) const {
+    if (!cu) {
+      start = (int64_t)s * S;
+      len = S;
+      return;
+    }
+    const int64_t a = cu[s], b = cu[s + 1];
+    if (a < 0 || b < a || b > T || b - a > max_len) {
+      start = 0;
+      len = 0;
+      return;
+    }
+    start = a;
+    len = (int)(b - a);
+  }
+  // First padded workspace slot of sequence s: sequences are laid out back to back,
+  // each starting on a TK boundary, in Hkv * Ppad slots per tensor.
+  static __device__ __forceinline__ int64_t pstart(int s, int64_t start) {
+    return (int64_t)TK * (start / TK + s);
+  }
+};
+
+// Element offset of token t of head h of sequence s in an fp16 activation tensor:
+// dense [B, H, S, D] has head_stride = S*D, tok_stride = D; packed [T, H, D] has
+// head_stride = D, tok_stride = H*D; in both the sequence starts at start*H*D.
+struct Act {
+  int64_t head_stride, tok_stride, seq_unit;  // seq_unit = H * D
+  __device__ __forceinline__ int64_t off(int64_t start, int h, int64_t t) const {
+    return start * seq_unit + (int64_t)h * head_stride + t * tok_stride;
+  }
+};
+
+// ---------------------------------------------------------------------------------
+// Quantization steps (the row rule of the Quantization table's "Per-row int8" row).
+
+// Scale of a row with absolute maximum `amax`: fp32(amax / 127), and for V rows that
+// value rounded up to a `bits`-bit significand (bits < 24).  amax / 127.0f is the
+// correctly rounded IEEE division (HIP's default for fp32 '/').
+__device__ __forceinline__ float row_scale(float amax, int bits) {
+  float t = amax / 127.0f;
+  if (bits < 24) {
+    const uint32_t drop = 24u - (uint32_t)bits;
+    const uint32_t lo = (1u << drop) - 1u;
+    t = __uint_as_float((__float_as_uint(t) + lo) & ~lo);
+  }
+  return t;
+}
+
+// Symmetric int8 code of x for a row scale s: clamp(rint(x / s), -127, 127), with the
+// correctly rounded fp32 quotient and round-half-to-even; a zero scale gives 0.
+__device__ __forceinline__ int quant_code(float x, float s) {
+  if (s == 0.0f) return 0;
+  float r = __builtin_rintf(x / s);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int)r;
+}
+
+// Max over groups of G consecutive lanes (G a power of two <= 64).
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// fp16 load of 8 consecutive values as fp32.
+__device__ __forceinline__ void load8_f32(const _Float16* p, float (&x)[8]) {
+  const v8h h = *reinterpret_cast<const v8h*>(p);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = (float)h[j];
+}
+
+// fp16 value times 2^24 as an exact integer (every fp16 number is a multiple of 2^-24).
+__device__ __forceinline__ int64_t fp16_fixed24(_Float16 v) {
+  const uint32_t u = __builtin_bit_cast(uint16_t, v);
+  const uint32_t e = (u >> 10) & 31u, m = u & 1023u;
+  const int64_t mag = e ? ((int64_t)(1024u | m) << (e - 1u)) : (int64_t)m;
+  return (u & 0x8000u) ? -mag : mag;
+}
+
+// ---------------------------------------------------------------------------------
+// MFMA operand layouts (v_mfma_i32_32x32x32_i8 and v_mfma_f32_32x32x16_f16).
+//
+// For a 32x32 MFMA, lane l supplies row (l % 32) of A and column (l % 32) of B for
+// the k-slice numbered l / 32; the result lane l holds column l % 32 and rows
+// 8*(i/4) + 4*(l/32) + i%4 for i = 0..15.  The kernels compute the transposed
+// products S^T = K . Q^T and O^T = V^T . P^T so that a lane's result registers all
+// belong to one query (column l % 32): the row statistics of the softmax stay in
+// the lane, and the S^T registers become the P^T operand of the next MFMA as they
+// are.
+//
+// K tile (TK keys x D int8), A operand of S^T: 16-byte fragments ordered
+//   [key block nb = n/32][d block kb = d/32][lane = n%32 + 32*((d%32)/16)][d%16].
+// V tile (TK keys x D fp16), A operand of O^T: 16-byte fragments ordered
+//   [key group kg = n/16][d block db = d/32][lane = d%32 + 32*hv][jv]
+// where a key n (nl = n % 16) sits at hv = (nl % 8) / 4, jv = 4*(nl / 8) + nl % 4,
+// the order in which the S^T result registers hold keys.
+// Q (B operand of S^T): lane l holds query l % 32, bytes d = 32*kb + 16*(l/32) + j.
+
+__device__ __forceinline__ int ktile_off(int n, int d, int D) {  // byte offset in tile
+  const int nb = n >> 5, nl = n & 31, kb = d >> 5, hh = (d & 31) >> 4, j = d & 15;
+  return ((nb * (D >> 5) + kb) * 64 + nl + 32 * hh) * 16 + j;
+}
+
+__device__ __forceinline__ int vtile_off(int n, int d, int D) {  // element offset in tile
+  const int kg = n >> 4, nl = n & 15, hv = (nl & 7) >> 2, jv = ((nl >> 3) << 2) + (nl & 3);
+  const int db = d >> 5, dl = d & 31;
+  return ((kg * (D >> 5) + db) * 64 + dl + 32 * hv) * 8 + jv;
+}
+
+__device__ __forceinline__ int qfrag_off(int m, int d) {  // byte offset, 32 rows
+  const int kb = d >> 5, hh = (d & 31) >> 4, j = d & 15;
+  return (kb * 64 + m + 32 * hh) * 16 + j;
+}
+
+}  // namespace i8a

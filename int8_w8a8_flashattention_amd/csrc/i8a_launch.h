@@ -1,0 +1,55 @@
+// i8a_launch.h - host-side launchers of the HIP kernels, called by the C ABI layer.
+// Arguments are validated by the caller; these only enqueue work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace i8a {
+
+// Keys per workspace tile and per attention pipeline stage.
+constexpr int TK = 64;
+// Tokens per workgroup of the K/V preparation kernels (a multiple of TK).
+constexpr int CH = 256;
+static_assert(CH % TK == 0, "a prep chunk holds whole tiles");
+
+// Workspace carve-up for one forward call.  All offsets are 256-byte aligned.
+struct WsPlan {
+  int32_t nseq, Hkv, D, nch;  // nch: CH-token chunks of the longest sequence
+  int64_t Ppad;               // padded token slots per kv head
+  size_t off_kpart, off_kmean, off_sk, off_sv, off_k8, off_vh, total;
+};
+
+WsPlan plan_workspace(int32_t nseq, int64_t total_tokens, int32_t max_len, int32_t Hkv,
+                      int32_t D);
+
+// Geometry of one forward call: dense when cu == nullptr.
+struct FwdGeom {
+  const void *q, *k, *v;
+  void* out;
+  const int32_t* cu;
+  int32_t nseq, S, max_len;
+  int64_t T;
+  int32_t Hq, Hkv, D;
+  float softmax_scale;
+  int causal;
+};
+
+hipError_t launch_quant_rowwise(const void* x, int64_t rows, int32_t d, const float* sub_mean,
+                                int64_t rows_per_group, int32_t scale_bits, int8_t* codes,
+                                float* scales, hipStream_t stream);
+
+// K-smoothing mean, K quantization and V quantization into the workspace.
+hipError_t launch_prep(const FwdGeom& g, const WsPlan& p, void* ws, hipStream_t stream);
+
+// Attention over the prepared workspace (Q is quantized inside).
+hipError_t launch_attn(const FwdGeom& g, const WsPlan& p, const void* ws, hipStream_t stream);
+
+// Debug dump of S32 and scales for batch b, query head h (dense geometry only).
+hipError_t launch_debug_qk(const FwdGeom& g, const WsPlan& p, const void* ws, int32_t b,
+                           int32_t h, int32_t row0, int32_t rows, int32_t col0, int32_t cols,
+                           int32_t* s32, float* qscale, float* kscale, float* vscale,
+                           float* kmean, hipStream_t stream);
+
+}  // namespace i8a

@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports every
+function include/i8attn.h declares, and rejects bad arguments on the host before
+any launch (these calls never reach the device, so they run without a GPU)."""
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import int8_w8a8_flashattention_amd as i8
+
+LIB = i8.library_path()
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libi8attn.so not built")
+
+OK, INVALID, HEADDIM, WSSMALL = 0, -1, -2, -3
+FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return i8.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = i8.header_functions()
+    for n in ("quant_rowwise_i8", "attn_int8_fwd", "attn_int8_varlen_fwd", "attn_int8_debug_qk",
+              "attn_int8_workspace_bytes", "attn_int8_varlen_workspace_bytes",
+              "attn_int8_prepare_kv", "attn_int8_fwd_prepared",
+              "i8a_status_string", "i8a_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for n in i8.header_functions():
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    assert lib.i8a_status_string(OK) == b"I8A_OK"
+    assert lib.i8a_status_string(INVALID) == b"I8A_ERR_INVALID_ARG"
+    assert lib.i8a_status_string(HEADDIM) == b"I8A_ERR_UNSUPPORTED_HEAD_DIM"
+    assert lib.i8a_status_string(WSSMALL) == b"I8A_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.i8a_status_string(-4) == b"I8A_ERR_HIP"
+    assert lib.i8a_status_string(7) == b"I8A_UNKNOWN_STATUS"
+
+
+def test_workspace_sizes(lib):
+    assert lib.attn_int8_workspace_bytes(1, 32, 8, 4096, 128) > 0
+    assert lib.attn_int8_workspace_bytes(1, 32, 8, 4096, 96) == 0
+    assert lib.attn_int8_workspace_bytes(1, 30, 8, 4096, 128) == 0
+    assert lib.attn_int8_workspace_bytes(0, 32, 8, 4096, 128) == 0
+    a = lib.attn_int8_workspace_bytes(1, 32, 8, 1000, 128)
+    b = lib.attn_int8_workspace_bytes(1, 32, 8, 2000, 128)
+    assert 0 < a < b and a % 256 == 0
+    # the workspace holds at least int8 K and fp16 V for every kv token
+    assert a >= 8 * 1000 * 128 * 3
+    assert lib.attn_int8_varlen_workspace_bytes(3, 100, 60, 4, 2, 64) > 0
+    assert lib.attn_int8_varlen_workspace_bytes(3, 100, 101, 4, 2, 64) == 0
+    assert lib.attn_int8_varlen_workspace_bytes(0, 100, 60, 4, 2, 64) == 0
+
+
+def _fwd(lib, D=128, Hq=32, Hkv=8, S=64, B=1, scale=0.1, causal=1, ws=FAKE, wsb=1 << 40,
+         q=FAKE, out=FAKE):
+    return lib.attn_int8_fwd(q, FAKE, FAKE, out, B, Hq, Hkv, S, D, scale, causal, ws, wsb, None)
+
+
+def test_forward_rejects_bad_arguments(lib):
+    assert _fwd(lib, D=96) == HEADDIM
+    assert b"head dim" in lib.i8a_last_error()
+    assert _fwd(lib, D=512) == HEADDIM
+    assert _fwd(lib, Hq=30) == INVALID
+    assert _fwd(lib, Hkv=0) == INVALID
+    assert _fwd(lib, S=0) == INVALID
+    assert _fwd(lib, B=0) == INVALID
+    assert _fwd(lib, scale=0.0) == INVALID
+    assert _fwd(lib, scale=float("inf")) == INVALID
+    assert _fwd(lib, scale=float("nan")) == INVALID
+    assert _fwd(lib, causal=2) == INVALID
+    assert _fwd(lib, q=None) == INVALID
+    assert _fwd(lib, out=ctypes.c_void_p((1 << 20) + 8)) == INVALID  # misaligned
+    assert _fwd(lib, ws=None) == INVALID
+    assert _fwd(lib, ws=ctypes.c_void_p((1 << 20) + 128)) == INVALID
+    need = lib.attn_int8_workspace_bytes(1, 32, 8, 64, 128)
+    assert _fwd(lib, wsb=need - 1) == WSSMALL
+    assert b"workspace needs" in lib.i8a_last_error()
+
+
+def test_varlen_rejects_bad_arguments(lib):
+    def call(nseq=2, maxlen=10, T=20, D=64, cu=FAKE, wsb=1 << 40):
+        return lib.attn_int8_varlen_fwd(FAKE, FAKE, FAKE, FAKE, cu, nseq, maxlen, T, 4, 2, D, 0.1,
+                                        1, FAKE, wsb, None)
+    assert call(cu=None) == INVALID
+    assert call(nseq=0) == INVALID
+    assert call(maxlen=21) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(D=48) == HEADDIM
+    assert call(T=0, maxlen=0) == OK  # nothing to do, nothing launched
+    assert call(wsb=10) == WSSMALL
+
+
+def test_quant_rejects_bad_arguments(lib):
+    def call(rows=4, d=64, mean=None, rpg=1, bits=24, x=FAKE):
+        return lib.quant_rowwise_i8(x, rows, d, mean, rpg, bits, FAKE, FAKE, None)
+    assert call(rows=0) == OK  # empty input: no launch
+    assert call(rows=-1) == INVALID
+    assert call(d=12) == INVALID
+    assert call(d=520) == INVALID
+    assert call(bits=8) == INVALID
+    assert call(mean=FAKE, rpg=0) == INVALID
+    assert call(x=None) == INVALID
+    assert call(x=ctypes.c_void_p((1 << 20) + 4)) == INVALID
+
+
+def test_debug_rejects_bad_tiles(lib):
+    def call(b=0, h=0, r0=0, r=8, c0=0, c=8, s32=FAKE):
+        return lib.attn_int8_debug_qk(FAKE, FAKE, FAKE, 1, 4, 2, 64, 64, b, h, r0, r, c0, c, s32,
+                                      None, None, None, None, FAKE, 1 << 40, None)
+    assert call(b=1) == INVALID
+    assert call(h=4) == INVALID
+    assert call(r0=60, r=8) == INVALID
+    assert call(c=0) == INVALID
+    assert call(s32=None) == INVALID
+
+
+def test_python_binding_validates_before_the_library():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        i8.quant_rowwise_i8(x)  # CPU tensor
+    with pytest.raises(ValueError):
+        i8.attn_int8_fwd(x.view(1, 1, 4, 64), x.view(1, 1, 4, 64), x.view(1, 1, 4, 64))
