@@ -76,6 +76,12 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of CPU oracle work for the cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-attn", type=int, default=0, metavar="N",
+                    help="profiling mode: prepare K/V once, launch only the attention kernel N "
+                         "times, print nothing else")
+    ap.add_argument("--profile-copy", type=int, default=0, metavar="MIB",
+                    help="profiling mode: 10 plain device copies of MIB MiB (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -96,9 +102,24 @@ def main():
     w = workloads.cfg2()
     B, Hq, Hkv, S, D = (WORKLOAD[k] for k in ("B", "Hq", "Hkv", "S", "D"))
     assert w.q.shape == (B, Hq, S, D) and w.k.shape == (B, Hkv, S, D)
+    if args.profile_copy:
+        src = torch.ones(args.profile_copy << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copied {args.profile_copy} MiB 10 times")
+        return
     q, k, v = (torch.from_numpy(a).to(dev) for a in (w.q, w.k, w.v))
     out = torch.empty_like(q)
     ws = torch.empty(i8.attn_int8_workspace_bytes(B, Hq, Hkv, S, D), dtype=torch.uint8, device=dev)
+    if args.profile_attn:
+        i8.attn_int8_prepare_kv(k, v, Hq, workspace=ws)
+        for _ in range(args.profile_attn):
+            i8.attn_int8_fwd_prepared(q, Hkv, ws, True, out=out)
+        torch.cuda.synchronize()
+        log(f"bench: {args.profile_attn} attention launches")
+        return
     ops = workloads.attn_ops(Hq, D, [S] * B, True)
     stream = torch.cuda.current_stream(dev)
 

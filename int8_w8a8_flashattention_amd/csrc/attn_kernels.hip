@@ -17,6 +17,8 @@
 // the global->LDS copy is linear and every LDS operand read is a conflict-free
 // 16-byte read.  Q is quantized in the prologue (each query row is read by exactly
 // one workgroup) with the same row rule as the preparation kernels.
+#include <type_traits>
+
 #include "i8a_device.h"
 #include "i8a_launch.h"
 
@@ -28,14 +30,38 @@ constexpr float TAU = 8.0f;  // lazy-rescale threshold, log2 units
 template <int D>
 struct Lay {
   static constexpr int NKB = D / 32;             // 32-wide blocks of the head dim
-  static constexpr int KB = TK * D;              // bytes of the int8 K tile
-  static constexpr int VB = TK * D * 2;          // bytes of the fp16 V tile
-  static constexpr int SB = TK * 4;              // bytes of the K scales
-  static constexpr int STAGE = KB + VB + SB;     // one pipeline stage
-  static constexpr int KCH = KB / 16, VCH = VB / 16;  // 16-byte chunks
-  static constexpr int KR = (KCH + 255) / 256, VR = (VCH + 255) / 256;
+  static constexpr int KB = TK * D;              // bytes of the int8 K codes
+  static constexpr int VB = TK * D * 2;          // bytes of the fp16 V
+  static constexpr int STAGE = tile_bytes(D);    // one pipeline stage = one tile block
+  static constexpr int NCH = STAGE / 16;         // 16-byte chunks per tile
+  static constexpr int ROUNDS = (NCH + 255) / 256;
+  static_assert(STAGE % 16 == 0, "tiles are copied in 16-byte chunks");
   static_assert(BM * D + BM * 4 <= STAGE, "Q staging fits in one stage");
 };
+
+// Wait until this wave's outstanding vector-memory operations (the direct-to-LDS
+// tile copies) have completed: vmcnt = 0, lgkmcnt and expcnt left unconstrained.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Copy one prepared tile block (global) into an LDS stage with direct-to-LDS loads:
+// every lane moves one 16-byte chunk, a wave fills 1 KB of consecutive LDS.
+template <int D>
+__device__ __forceinline__ void copy_tile_async(const char* __restrict__ src, char* stage,
+                                                int tid) {
+  using LY = Lay<D>;
+  const int w = tid >> 6;
+#pragma unroll
+  for (int r = 0; r < LY::ROUNDS; ++r) {
+    const int chunk = r * 256 + tid;
+    if (r * 256 + w * 64 < LY::NCH) {  // wave-uniform: this wave has chunks left
+      char* lbase = stage + (r * 256 + w * 64) * 16;
+      if (chunk < LY::NCH)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + (int64_t)chunk * 16),
+                                         (__attribute__((address_space(3))) void*)(lbase), 16, 0,
+                                         0);
+    }
+  }
+}
 
 // Quantize the 32 query rows q_first.. of head h (one wave) into Q fragments in LDS
 // (layout qfrag_off) and their scales.  Rows at or beyond L quantize as zero rows.
@@ -45,41 +71,45 @@ __device__ __forceinline__ void quant_q_rows(const _Float16* __restrict__ q, con
                                              int8_t* frag, float* qscale) {
   constexpr int G = D / 8;
   constexpr int RPP = 64 / G;
+  constexpr int NP = 32 / RPP;  // rows per lane
   const int lane = threadIdx.x & 63, lc = lane % G, rs = lane / G;
+  v8h xr[NP];
 #pragma unroll
-  for (int m0 = 0; m0 < 32; m0 += RPP) {
-    const int m = m0 + rs;
-    const int t = q_first + m;
-    const bool real = t < L;
+  for (int i = 0; i < NP; ++i) {
+    const int t = q_first + i * RPP + rs;
+    if (t < L) xr[i] = *reinterpret_cast<const v8h*>(q + aq.off(start, h, t) + lc * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int m = i * RPP + rs;
+    const bool real = q_first + m < L;
     float x[8];
     float amax = 0.0f;
     if (real) {
-      load8_f32(q + aq.off(start, h, t) + lc * 8, x);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+      for (int j = 0; j < 8; ++j) {
+        x[j] = (float)xr[i][j];
+        amax = fmaxf(amax, fabsf(x[j]));
+      }
     }
     amax = group_max<G>(amax);
-    const float s = real ? row_scale(amax, 24) : 0.0f;
-    uint32_t lo = 0, hi = 0;
-    if (real) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) lo |= ((uint32_t)quant_code(x[j], s) & 255u) << (8 * j);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) hi |= ((uint32_t)quant_code(x[4 + j], s) & 255u) << (8 * j);
-    }
-    *reinterpret_cast<uint2*>(frag + qfrag_off(m, lc * 8)) = make_uint2(lo, hi);
-    if (lc == 0) qscale[m] = s;
+    const RowQ rq(real ? row_scale(amax, 24) : 0.0f);
+    const uint2 codes = real ? rq.pack8(x) : make_uint2(0u, 0u);
+    *reinterpret_cast<uint2*>(frag + qfrag_off(m, lc * 8)) = codes;
+    if (lc == 0) qscale[m] = rq.s;
   }
 }
 
-// Work item of a workgroup: query tile (heaviest first), sequence and head.  With
-// xcd_map the heads of one kv group land on blocks with the same id mod 8, i.e. on
-// one XCD (blocks are dispatched round-robin over the 8 XCDs), so that group's K/V
-// stays in that XCD's L2.
-__device__ __forceinline__ void decode_work(int bid, int nseq, int Hq, int Hkv, int nqt,
-                                            int xcd_map, int& qt, int& s, int& h) {
+// Work item of a workgroup: a query-tile slot, a sequence and a head.  Slots are the
+// slowest-varying index, and under the causal mask slot 0 is the last (longest) query
+// tile, so the heaviest workgroups are dispatched first and the short ones fill the
+// tail.  With xcd_map the heads of one kv group land on blocks with the same id mod 8,
+// i.e. on one XCD (blocks are dispatched round-robin over the 8 XCDs), so that group's
+// K/V stays in that XCD's L2.
+__device__ __forceinline__ void decode_work(int bid, int nseq, int Hq, int Hkv, int xcd_map,
+                                            int& slot, int& s, int& h) {
   const int nbh = nseq * Hq;
-  qt = nqt - 1 - bid / nbh;
+  slot = bid / nbh;
   const int r = bid % nbh;
   if (xcd_map) {
     const int G = Hq / Hkv;
@@ -96,61 +126,36 @@ __device__ __forceinline__ void decode_work(int bid, int nseq, int Hq, int Hkv, 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const _Float16* __restrict__ q, _Float16* __restrict__ out, Act aq, Seqs seqs, int Hq,
-    int Hkv, int nseq, int nqt, int xcd_map, float qk_log2, const int8_t* __restrict__ k8_ws,
-    const _Float16* __restrict__ vh_ws, const float* __restrict__ sk_ws, int64_t Ppad) {
+    int Hkv, int nseq, int xcd_map, float qk_log2, const char* __restrict__ tiles,
+    int64_t Ppad) {
   using LY = Lay<D>;
   constexpr int NKB = LY::NKB;
   __shared__ __attribute__((aligned(16))) char smem[2 * LY::STAGE];
 
-  int qt, s, h;
-  decode_work(blockIdx.x, nseq, Hq, Hkv, nqt, xcd_map, qt, s, h);
+  int slot, s, h;
+  decode_work(blockIdx.x, nseq, Hq, Hkv, xcd_map, slot, s, h);
   int64_t start;
   int L;
   seqs.bounds(s, start, L);
-  const int q0 = qt * BM;
-  if (q0 >= L) return;
+  const int nqt_s = (L + BM - 1) / BM;  // query tiles of this sequence
+  if (slot >= nqt_s) return;
+  const int qt = CAUSAL ? nqt_s - 1 - slot : slot;
   const int g = h / (Hq / Hkv);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 31, hh = lane >> 5;
-  const int qw0 = q0 + 32 * w;
+  const int64_t pbase = Seqs::pstart(s, start);
+  const char* tsrc = tiles + ((int64_t)g * (Ppad / TK) + pbase / TK) * LY::STAGE;
 
+  const int q0 = qt * BM;
+  const int qw0 = q0 + 32 * w;
   const int ntile_seq = (L + TK - 1) / TK;
   const int nt = CAUSAL ? min(ntile_seq, (min(q0 + BM, L) - 1) / TK + 1) : ntile_seq;
-  const int64_t pbase = Seqs::pstart(s, start);
-  const v4i* kglob = reinterpret_cast<const v4i*>(k8_ws + ((int64_t)g * Ppad + pbase) * D);
-  const v4i* vglob = reinterpret_cast<const v4i*>(vh_ws + ((int64_t)g * Ppad + pbase) * D);
-  const float* skglob = sk_ws + (int64_t)g * Ppad + pbase;
 
-  // Register-staged tile loader (global -> regs -> LDS).
-  v4i kreg[LY::KR], vreg[LY::VR];
-  v4f sreg;
-  auto load_tile = [&](int j) {
-    const v4i* kp = kglob + (int64_t)j * LY::KCH;
-    const v4i* vp = vglob + (int64_t)j * LY::VCH;
-#pragma unroll
-    for (int i = 0; i < LY::KR; ++i)
-      if (tid + 256 * i < LY::KCH) kreg[i] = kp[tid + 256 * i];
-#pragma unroll
-    for (int i = 0; i < LY::VR; ++i)
-      if (tid + 256 * i < LY::VCH) vreg[i] = vp[tid + 256 * i];
-    if (tid < TK / 4) sreg = reinterpret_cast<const v4f*>(skglob + (int64_t)j * TK)[tid];
-  };
-  auto store_tile = [&](int stage) {
-    char* st = smem + stage * LY::STAGE;
-#pragma unroll
-    for (int i = 0; i < LY::KR; ++i)
-      if (tid + 256 * i < LY::KCH) reinterpret_cast<v4i*>(st)[tid + 256 * i] = kreg[i];
-#pragma unroll
-    for (int i = 0; i < LY::VR; ++i)
-      if (tid + 256 * i < LY::VCH) reinterpret_cast<v4i*>(st + LY::KB)[tid + 256 * i] = vreg[i];
-    if (tid < TK / 4) reinterpret_cast<v4f*>(st + LY::KB + LY::VB)[tid] = sreg;
-  };
-
-  // Prologue: tile 0 in flight while Q is quantized into the stage-1 region.
-  load_tile(0);
+  // Prologue: tile 0 streams into stage 0 while Q is quantized into stage 1.
+  copy_tile_async<D>(tsrc, smem, tid);
   int8_t* qstage = reinterpret_cast<int8_t*>(smem + LY::STAGE);
   float* qscl = reinterpret_cast<float*>(smem + LY::STAGE + BM * D);
   quant_q_rows<D>(q, aq, start, h, qw0, L, qstage + w * 32 * D, qscl + 32 * w);
-  store_tile(0);
+  wait_vmem();
   __syncthreads();
   v4i qf[NKB];
 #pragma unroll
@@ -167,93 +172,110 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   float mrun = -INFINITY, lsum = 0.0f;
   const int qi = qw0 + m;
 
+  // One 64-key tile.  MASK: some key of the tile lies above this wave's diagonal or
+  // past the sequence end (only those tiles pay for the mask).
+  auto tile_step = [&](const char* st, int kt0, auto maskc) {
+    constexpr bool MASK = decltype(maskc)::value;
+    const v4i* kl = reinterpret_cast<const v4i*>(st);
+    const v4i* vl = reinterpret_cast<const v4i*>(st + LY::KB);
+    const float* skl = reinterpret_cast<const float*>(st + LY::KB + LY::VB);
+
+    v16i acc[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[nb][i] = 0;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        acc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kl[(nb * NKB + kb) * 64 + lane], qf[kb],
+                                                        acc[nb], 0, 0, 0);
+    }
+    // Register i of block nb holds key 32*nb + 8*(i/4) + 4*hh + i%4 of the tile.
+    float tv[32];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        const v4f skv = *reinterpret_cast<const v4f*>(skl + 32 * nb + 8 * J + 4 * hh);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tv[16 * nb + 4 * J + r] = (float)acc[nb][4 * J + r] * skv[r];
+      }
+    if constexpr (MASK) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int key = kt0 + 32 * (i >> 4) + 8 * ((i >> 2) & 3) + 4 * hh + (i & 3);
+        if ((CAUSAL && key > qi) || key >= L) tv[i] = -INFINITY;
+      }
+    }
+    float mx = fmaxf(tv[0], tv[1]);
+#pragma unroll
+    for (int i = 2; i < 32; i += 2) mx = fmaxf(mx, fmaxf(tv[i], tv[i + 1]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // Every row has a key in the first tile, so mx is finite unless the tile is
+    // masked for this row.
+    const float mc = (MASK && mx == -INFINITY) ? -INFINITY : mx * qsc;
+    const bool upd = mc > mrun + TAU;
+    if (__any(upd)) {
+      const float mnew = upd ? mc : mrun;
+      const float alpha = upd ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.0f;
+      mrun = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < NKB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    }
+    const float muse = (MASK && mrun == -INFINITY) ? 0.0f : mrun;
+
+    // p = 2^(t * qsc - M), rounded to fp16: the P^T operand of the P.V product and
+    // the terms of the row sum.  Masked keys get p = 0 explicitly (an all-zero query
+    // row has qsc = 0, and -inf * 0 is not a number).
+    v8h pk[4];
+#pragma unroll
+    for (int i = 0; i < 32; i += 2) {
+      v2f pp;
+      pp[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(tv[i], qsc, -muse));
+      pp[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(tv[i + 1], qsc, -muse));
+      if constexpr (MASK) {
+        if (tv[i] == -INFINITY) pp[0] = 0.0f;
+        if (tv[i + 1] == -INFINITY) pp[1] = 0.0f;
+      }
+      const v2h ph = __builtin_convertvector(pp, v2h);
+      pk[i >> 3][i & 7] = ph[0];
+      pk[i >> 3][(i & 7) + 1] = ph[1];
+    }
+    const v2h ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const v2h pr = {pk[kg][e], pk[kg][e + 1]};
+        lsum = __builtin_amdgcn_fdot2(pr, ones, lsum, false);
+      }
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+      for (int db = 0; db < NKB; ++db) {
+        const v4i va = vl[(kg * NKB + db) * 64 + lane];
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, va), pk[kg], o[db],
+                                                        0, 0, 0);
+      }
+  };
+
   for (int j = 0; j < nt; ++j) {
-    if (j + 1 < nt) load_tile(j + 1);
+    if (j + 1 < nt)
+      copy_tile_async<D>(tsrc + (int64_t)(j + 1) * LY::STAGE, smem + ((j + 1) & 1) * LY::STAGE,
+                         tid);
     const int kt0 = j * TK;
     if (!CAUSAL || kt0 <= qw0 + 31) {
       const char* st = smem + (j & 1) * LY::STAGE;
-      const v4i* kl = reinterpret_cast<const v4i*>(st);
-      const v4i* vl = reinterpret_cast<const v4i*>(st + LY::KB);
-      const float* skl = reinterpret_cast<const float*>(st + LY::KB + LY::VB);
-
-      v16i acc[2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[nb][i] = 0;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          acc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kl[(nb * NKB + kb) * 64 + lane], qf[kb],
-                                                          acc[nb], 0, 0, 0);
-      }
-
-      float tv[32];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-          const v4f skv = *reinterpret_cast<const v4f*>(skl + 32 * nb + 8 * J + 4 * hh);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) tv[16 * nb + 4 * J + r] = (float)acc[nb][4 * J + r] * skv[r];
-        }
-      // Masked keys (above the diagonal, past the sequence end) get t = -inf for the
-      // max and p = 0 after the exponential; the weight is zeroed explicitly because
-      // an all-zero query row has qsc = 0 and -inf * 0 is not a number.
-      const bool masked_tile = (CAUSAL && kt0 + TK - 1 > qw0) || kt0 + TK > L;
-      uint32_t keep = 0xffffffffu;
-      if (masked_tile) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const int key = kt0 + 32 * (i >> 4) + 8 * ((i >> 2) & 3) + 4 * hh + (i & 3);
-          if ((CAUSAL && key > qi) || key >= L) {
-            tv[i] = -INFINITY;
-            keep &= ~(1u << i);
-          }
-        }
-      }
-      float mx = tv[0];
-#pragma unroll
-      for (int i = 1; i < 32; ++i) mx = fmaxf(mx, tv[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mc = mx == -INFINITY ? -INFINITY : mx * qsc;
-      const bool upd = mc > mrun + TAU;
-      if (__any(upd)) {
-        const float mnew = upd ? mc : mrun;
-        const float alpha = upd ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.0f;
-        mrun = mnew;
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < NKB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-      }
-      const float muse = mrun == -INFINITY ? 0.0f : mrun;
-
-      v8h pk[4];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(tv[i], qsc, -muse));
-        if (masked_tile) p = (keep >> i) & 1u ? p : 0.0f;
-        pk[i >> 3][i & 7] = (_Float16)p;
-      }
-      const v2h ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-      for (int kg = 0; kg < 4; ++kg)
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const v2h pr = {pk[kg][e], pk[kg][e + 1]};
-          lsum = __builtin_amdgcn_fdot2(pr, ones, lsum, false);
-        }
-#pragma unroll
-      for (int kg = 0; kg < 4; ++kg)
-#pragma unroll
-        for (int db = 0; db < NKB; ++db) {
-          const v4i va = vl[(kg * NKB + db) * 64 + lane];
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, va), pk[kg],
-                                                          o[db], 0, 0, 0);
-        }
+      const bool masked = (CAUSAL && kt0 + TK - 1 > qw0) || kt0 + TK > L;
+      if (masked)
+        tile_step(st, kt0, std::true_type{});
+      else
+        tile_step(st, kt0, std::false_type{});
     }
-    if (j + 1 < nt) store_tile((j + 1) & 1);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -279,8 +301,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 template <int D>
 __global__ __launch_bounds__(64) void debug_qk_kernel(
     const _Float16* __restrict__ q, Act aq, int S, int Hq, int Hkv, int b, int h, int row0,
-    int rows, int col0, int cols, const int8_t* __restrict__ k8_ws,
-    const float* __restrict__ sk_ws, const float* __restrict__ sv_ws,
+    int rows, int col0, int cols, const char* __restrict__ tiles,
+    const float* __restrict__ sv_ws,
     const float* __restrict__ kmean_ws, int64_t Ppad, int32_t* __restrict__ s32,
     float* __restrict__ qscale, float* __restrict__ kscale, float* __restrict__ vscale,
     float* __restrict__ kmean_out) {
@@ -301,7 +323,8 @@ __global__ __launch_bounds__(64) void debug_qk_kernel(
   for (int kb = 0; kb < NKB; ++kb) qf[kb] = reinterpret_cast<const v4i*>(frag)[kb * 64 + lane];
 
   const int tile0 = kbase - kbase % TK, nb = (kbase % TK) / 32;
-  const v4i* kt = reinterpret_cast<const v4i*>(k8_ws + ((int64_t)g * Ppad + pbase + tile0) * D);
+  const char* tb = tiles + ((int64_t)g * (Ppad / TK) + (pbase + tile0) / TK) * tile_bytes(D);
+  const v4i* kt = reinterpret_cast<const v4i*>(tb);
   v16i acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0;
@@ -320,7 +343,7 @@ __global__ __launch_bounds__(64) void debug_qk_kernel(
     qscale[qrow - row0] = qs[m];
   const int n = kbase + m;
   if (blockIdx.x == 0 && hh == 0 && n >= col0 && n < col0 + cols) {
-    if (kscale) kscale[n - col0] = sk_ws[(int64_t)g * Ppad + pbase + n];
+    if (kscale) kscale[n - col0] = reinterpret_cast<const float*>(tb + 3 * TK * D)[n - tile0];
     if (vscale) vscale[n - col0] = sv_ws[(int64_t)g * Ppad + pbase + n];
   }
   if (kmean_out && blockIdx.x == 0 && blockIdx.y == 0)
@@ -354,9 +377,7 @@ static hipError_t attn_d(const FwdGeom& g, const WsPlan& p, const void* ws, hipS
   Seqs sq{g.cu, g.S, g.max_len, g.T};
   attn_fwd_kernel<D, C><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
       static_cast<const _Float16*>(g.q), static_cast<_Float16*>(g.out), act_of(g, g.Hq), sq,
-      g.Hq, g.Hkv, g.nseq, nqt, xcd_map, qk_log2, reinterpret_cast<const int8_t*>(w + p.off_k8),
-      reinterpret_cast<const _Float16*>(w + p.off_vh), reinterpret_cast<const float*>(w + p.off_sk),
-      p.Ppad);
+      g.Hq, g.Hkv, g.nseq, xcd_map, qk_log2, w + p.off_tiles, p.Ppad);
   return hipGetLastError();
 }
 
@@ -382,8 +403,7 @@ static hipError_t debug_d(const FwdGeom& g, const WsPlan& p, const void* ws, int
   const int cb = ((col0 + cols - 1) >> 5) - (col0 >> 5) + 1;
   debug_qk_kernel<D><<<dim3(rb, cb), dim3(64), 0, stream>>>(
       static_cast<const _Float16*>(g.q), act_of(g, g.Hq), g.S, g.Hq, g.Hkv, b, h, row0, rows,
-      col0, cols, reinterpret_cast<const int8_t*>(w + p.off_k8),
-      reinterpret_cast<const float*>(w + p.off_sk), reinterpret_cast<const float*>(w + p.off_sv),
+      col0, cols, w + p.off_tiles, reinterpret_cast<const float*>(w + p.off_sv),
       reinterpret_cast<const float*>(w + p.off_kmean), p.Ppad, s32, qscale, kscale, vscale,
       kmean);
   return hipGetLastError();

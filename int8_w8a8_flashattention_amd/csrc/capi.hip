@@ -33,21 +33,20 @@ WsPlan plan_workspace(int32_t nseq, int64_t total_tokens, int32_t max_len, int32
   p.nseq = nseq;
   p.Hkv = Hkv;
   p.D = D;
-  p.nch = (max_len + CH - 1) / CH;
+  p.ntile = (max_len + TK - 1) / TK;
+  p.tpw = (p.ntile + MAX_PARTS - 1) / MAX_PARTS;
+  if (p.tpw < 1) p.tpw = 1;
+  p.npart = (p.ntile + p.tpw - 1) / p.tpw;
   p.Ppad = (int64_t)TK * ((total_tokens + TK - 1) / TK + nseq);
   size_t off = 0;
   p.off_kpart = off;
-  off = align256(off + (size_t)nseq * Hkv * p.nch * D * 8);
+  off = align256(off + (size_t)nseq * Hkv * p.npart * D * 8);
   p.off_kmean = off;
   off = align256(off + (size_t)nseq * Hkv * D * 4);
-  p.off_sk = off;
-  off = align256(off + (size_t)Hkv * p.Ppad * 4);
   p.off_sv = off;
   off = align256(off + (size_t)Hkv * p.Ppad * 4);
-  p.off_k8 = off;
-  off = align256(off + (size_t)Hkv * p.Ppad * D);
-  p.off_vh = off;
-  off = align256(off + (size_t)Hkv * p.Ppad * D * 2);
+  p.off_tiles = off;
+  off = align256(off + (size_t)Hkv * (p.Ppad / TK) * tile_bytes(D));
   p.total = off;
   return p;
 }

@@ -13,6 +13,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
@@ -77,12 +78,30 @@ __device__ __forceinline__ float row_scale(float amax, int bits) {
 
 // Symmetric int8 code of x for a row scale s: clamp(rint(x / s), -127, 127), with the
 // correctly rounded fp32 quotient and round-half-to-even; a zero scale gives 0.
-__device__ __forceinline__ int quant_code(float x, float s) {
-  if (s == 0.0f) return 0;
-  float r = __builtin_rintf(x / s);
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
-  return (int)r;
-}
+// `y` is the row's correctly rounded reciprocal RN(1/s) (0 when s == 0): with it the
+// quotient RN(x/s) is q0 = RN(x*y) corrected once by the exact remainder
+// r = x - s*q0 (an FMA), q = RN(q0 + r*y) -- the FMA division step of Markstein,
+// exact for every quotient here (no overflow or underflow occurs in it).
+struct RowQ {
+  float s, y;
+  __device__ __forceinline__ explicit RowQ(float scale)
+      : s(scale), y(scale == 0.0f ? 0.0f : 1.0f / scale) {}
+  __device__ __forceinline__ float code(float x) const {
+    const float q0 = __fmul_rn(x, y);
+    const float r = __builtin_fmaf(-q0, s, x);
+    const float q = __builtin_fmaf(r, y, q0);
+    return fminf(fmaxf(__builtin_rintf(q), -127.0f), 127.0f);
+  }
+  // Eight codes packed little-endian into two dwords (two's complement bytes).
+  __device__ __forceinline__ uint2 pack8(const float (&x)[8]) const {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lo = __builtin_amdgcn_cvt_pk_u8_f32(code(x[j]) + 128.0f, j, lo);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hi = __builtin_amdgcn_cvt_pk_u8_f32(code(x[4 + j]) + 128.0f, j, hi);
+    return make_uint2(lo ^ 0x80808080u, hi ^ 0x80808080u);
+  }
+};
 
 // Max over groups of G consecutive lanes (G a power of two <= 64).
 template <int G>

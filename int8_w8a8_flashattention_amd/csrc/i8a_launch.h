@@ -14,11 +14,24 @@ constexpr int TK = 64;
 constexpr int CH = 256;
 static_assert(CH % TK == 0, "a prep chunk holds whole tiles");
 
+// Bytes of one prepared K/V tile of TK tokens: int8 K codes in MFMA fragment order,
+// then the exact fp16 dequantized V in fragment order, then the fp32 K scales.
+__host__ __device__ constexpr int tile_bytes(int D) { return TK * D * 3 + TK * 4; }
+
 // Workspace carve-up for one forward call.  All offsets are 256-byte aligned.
+//   kpart  int64 [nseq][Hkv][npart][D]   exact K channel sums of tpw tiles (2^-24 units)
+//   kmean  fp32  [nseq][Hkv][D]          K-smoothing means
+//   sv     fp32  [Hkv][Ppad]             V row scales (kept for the debug dump)
+//   tiles  bytes [Hkv][Ppad / TK][tile_bytes(D)]
+// Cap on the K partial sums per (sequence, kv head): the K quantization workgroups
+// each reduce all of them to get the mean.
+constexpr int MAX_PARTS = 64;
+
 struct WsPlan {
-  int32_t nseq, Hkv, D, nch;  // nch: CH-token chunks of the longest sequence
-  int64_t Ppad;               // padded token slots per kv head
-  size_t off_kpart, off_kmean, off_sk, off_sv, off_k8, off_vh, total;
+  int32_t nseq, Hkv, D, ntile;  // ntile: TK-token tiles of the longest sequence
+  int32_t tpw, npart;           // tiles per prep workgroup, partial sums per (seq, head)
+  int64_t Ppad;                 // padded token slots per kv head
+  size_t off_kpart, off_kmean, off_sv, off_tiles, total;
 };
 
 WsPlan plan_workspace(int32_t nseq, int64_t total_tokens, int32_t max_len, int32_t Hkv,

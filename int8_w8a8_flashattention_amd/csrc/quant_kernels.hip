@@ -36,54 +36,114 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(
       for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
     }
     amax = group_max<G>(amax);
-    const float s = row_scale(amax, scale_bits);
+    const RowQ rq(row_scale(amax, scale_bits));
     if (live) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) lo |= ((uint32_t)quant_code(v[j], s) & 255u) << (8 * j);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) hi |= ((uint32_t)quant_code(v[4 + j], s) & 255u) << (8 * j);
-      *reinterpret_cast<uint2*>(codes + r * d + c * 8) = make_uint2(lo, hi);
-      if (c == 0) scales[r] = s;
+      *reinterpret_cast<uint2*>(codes + r * d + c * 8) = rq.pack8(v);
+      if (c == 0) scales[r] = rq.s;
     }
   }
 }
 
 // ----------------------------------------------------------------------------------
-// Stage 1 of the preparation, one workgroup per (chunk of CH tokens, kv head,
-// sequence): exact per-channel partial sums of K over the chunk's tokens (the
-// K-smoothing statistic), and V quantized per token with its 4-bit scale, written as
-// the exact fp16 values sv * code in the V tile layout.  Slots between the sequence
-// end and its last tile boundary get V = 0 and sv = 0.
+// K/V preparation, three launches over the TK-token tiles of every (sequence, kv
+// head).  A tile's block in the workspace (tile_bytes) holds its int8 K codes, its
+// exact fp16 dequantized V and its fp32 K scales, in the order the attention kernel
+// copies them to LDS.  Slots between a sequence's end and its last tile boundary are
+// zero (codes, V and scales), so a masked key still multiplies finite numbers.
+
+// Launch 1 (workgroup = tpw consecutive tiles of one sequence and kv head): V rows
+// quantized per token with the 4-bit scale rule, written as the exact fp16 values
+// sv * code in the V fragment layout; and the exact per-channel K sums of those tiles
+// (the K-smoothing statistic) as one int64 partial.
+//   Phase A: coalesced loads of the tile's K and V rows; K sums; each V row's scale
+//            and reciprocal; the raw V rows into LDS.
+//   Phase B: each thread assembles whole 16-byte V fragments (8 keys of one channel)
+//            from LDS and stores them with coalesced writes.
 template <int D>
-__global__ __launch_bounds__(256) void prep_stage1_kernel(
+__global__ __launch_bounds__(256) void prep_v_kernel(
     const _Float16* __restrict__ k, const _Float16* __restrict__ v, Act act, Seqs seqs, int Hkv,
-    int nch, int64_t Ppad, int64_t* __restrict__ kpart, float* __restrict__ sv_ws,
-    _Float16* __restrict__ vh_ws) {
+    int npart, int tpw, int64_t Ppad, int64_t* __restrict__ kpart, float* __restrict__ sv_ws,
+    char* __restrict__ tiles) {
   constexpr int G = D / 8;       // lanes per row
   constexpr int RPP = 256 / G;   // rows per pass
+  constexpr int NP = TK / RPP;   // rows per thread and tile
+  constexpr int NF = TK * D / 8 / 256;  // V fragments per thread and tile
   __shared__ int64_t red[RPP * D];
-  __shared__ __attribute__((aligned(16))) _Float16 vt[TK * D];
+  __shared__ __attribute__((aligned(16))) _Float16 vraw[TK * D];
+  __shared__ float2 rsy[TK];
 
   const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   int64_t start;
   int L;
   seqs.bounds(s, start, L);
-  const int t0 = c * CH;
-  if (t0 >= L) return;
-  const int t_real = min(L, t0 + CH);
-  const int t_pad = min(((L + TK - 1) / TK) * TK, t0 + CH);
+  const int nt = (L + TK - 1) / TK;
+  const int tile_lo = c * tpw;
+  if (tile_lo >= nt) return;
+  const int tile_hi = min(nt, tile_lo + tpw);
   const int64_t pbase = Seqs::pstart(s, start);
   const int lc = threadIdx.x % G, rsub = threadIdx.x / G;
 
-  // K partial sums over this chunk (exact int64 fixed point).
   int64_t acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0;
-  for (int t = t0 + rsub; t < t_real; t += RPP) {
-    const v8h kv = *reinterpret_cast<const v8h*>(k + act.off(start, g, t) + lc * 8);
+  for (int tt = tile_lo; tt < tile_hi; ++tt) {
+    const int t0 = tt * TK;
+    v8h kr[NP], vr[NP];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] += fp16_fixed24(kv[j]);
+    for (int i = 0; i < NP; ++i) {
+      const int t = t0 + i * RPP + rsub;
+      if (t < L) {
+        kr[i] = *reinterpret_cast<const v8h*>(k + act.off(start, g, t) + lc * 8);
+        vr[i] = *reinterpret_cast<const v8h*>(v + act.off(start, g, t) + lc * 8);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vr[i][j] = (_Float16)0.0f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int n = i * RPP + rsub, t = t0 + n;
+      const bool real = t < L;
+      float amax = 0.0f;
+      if (real) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          acc[j] += fp16_fixed24(kr[i][j]);
+          amax = fmaxf(amax, fabsf((float)vr[i][j]));
+        }
+      }
+      amax = group_max<G>(amax);
+      *reinterpret_cast<v8h*>(vraw + n * D + lc * 8) = vr[i];
+      if (lc == 0) {
+        const RowQ rq(real ? row_scale(amax, 4) : 0.0f);
+        rsy[n] = make_float2(rq.s, rq.y);
+        if (real) sv_ws[(int64_t)g * Ppad + pbase + t] = rq.s;
+      }
+    }
+    __syncthreads();
+    v8h* dst = reinterpret_cast<v8h*>(tiles + ((int64_t)g * (Ppad / TK) + (pbase + t0) / TK) *
+                                                  tile_bytes(D) + TK * D);
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      // fragment f = (kg * D/32 + db) * 64 + lane', lane' = dl + 32 * hv
+      const int f = i * 256 + threadIdx.x;
+      const int lanep = f & 63, kgdb = f >> 6;
+      const int db = kgdb % (D / 32), kg = kgdb / (D / 32);
+      const int d = 32 * db + (lanep & 31), hv = lanep >> 5;
+      v8h frag;
+#pragma unroll
+      for (int jv = 0; jv < 8; ++jv) {
+        const int n = 16 * kg + (jv < 4 ? 4 * hv + jv : 8 + 4 * hv + (jv - 4));
+        const float2 sy = rsy[n];
+        RowQ rq(0.0f);
+        rq.s = sy.x;
+        rq.y = sy.y;
+        // sv has a 4-bit significand and |code| <= 127: the product is exact in fp16.
+        frag[jv] = (_Float16)(rq.s * rq.code((float)vraw[n * D + d]));
+      }
+      dst[f] = frag;
+    }
+    __syncthreads();
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) red[rsub * D + lc * 8 + j] = acc[j];
@@ -91,101 +151,96 @@ __global__ __launch_bounds__(256) void prep_stage1_kernel(
   if (threadIdx.x < D) {
     int64_t tot = 0;
     for (int r = 0; r < RPP; ++r) tot += red[r * D + threadIdx.x];
-    kpart[(((int64_t)s * Hkv + g) * nch + c) * D + threadIdx.x] = tot;
-  }
-
-  // V rows, one TK-token tile at a time through LDS into the fragment layout.
-  for (int tt = t0; tt < t_pad; tt += TK) {
-    for (int n = rsub; n < TK; n += RPP) {
-      const int t = tt + n;
-      float x[8];
-      float amax = 0.0f;
-      const bool real = t < L;
-      if (real) {
-        load8_f32(v + act.off(start, g, t) + lc * 8, x);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
-      }
-      amax = group_max<G>(amax);
-      const float sv = real ? row_scale(amax, 4) : 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        // sv has a 4-bit significand and |code| <= 127, so the product is exact in
-        // fp32 and in fp16.
-        const float vh = real ? sv * (float)quant_code(x[j], sv) : 0.0f;
-        vt[vtile_off(n, lc * 8 + j, D)] = (_Float16)vh;
-      }
-      if (lc == 0) sv_ws[(int64_t)g * Ppad + pbase + t] = sv;
-    }
-    __syncthreads();
-    _Float16* dst = vh_ws + ((int64_t)g * Ppad + pbase + tt) * D;
-    for (int i = threadIdx.x; i < TK * D / 8; i += 256)
-      reinterpret_cast<v8h*>(dst)[i] = reinterpret_cast<const v8h*>(vt)[i];
-    __syncthreads();
+    kpart[(((int64_t)s * Hkv + g) * npart + c) * D + threadIdx.x] = tot;
   }
 }
 
-// ----------------------------------------------------------------------------------
-// Stage 2, same grid: the K mean of the sequence (sum of the stage-1 partials, fp64
-// divide, fp32), then K rows quantized from fp32(k) - mean into the K tile layout.
+// Launch 2 (same grid): the K-smoothing mean of the sequence, reduced by every
+// workgroup from the launch-1 partials (at most MAX_PARTS of them; integer sums, so
+// every workgroup gets the same value), divided in fp64 and rounded to fp32; then
+// the K rows of the workgroup's tiles quantized from fp32(k) - mean into the K
+// fragment layout, with the K scales after the V block.
 template <int D>
-__global__ __launch_bounds__(256) void prep_stage2_kernel(
-    const _Float16* __restrict__ k, Act act, Seqs seqs, int Hkv, int nch, int64_t Ppad,
-    const int64_t* __restrict__ kpart, float* __restrict__ kmean_ws, float* __restrict__ sk_ws,
-    int8_t* __restrict__ k8_ws) {
+__global__ __launch_bounds__(256) void prep_k_kernel(const _Float16* __restrict__ k, Act act,
+                                                     Seqs seqs, int Hkv, int npart, int tpw,
+                                                     int64_t Ppad,
+                                                     const int64_t* __restrict__ kpart,
+                                                     float* __restrict__ kmean_ws,
+                                                     char* __restrict__ tiles) {
   constexpr int G = D / 8;
   constexpr int RPP = 256 / G;
+  constexpr int NP = TK / RPP;
+  constexpr int TPC = 256 / D;  // threads per channel in the mean reduction
+  __shared__ int64_t red[256];
   __shared__ float mean[D];
-
   const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   int64_t start;
   int L;
   seqs.bounds(s, start, L);
-  const int t0 = c * CH;
-  if (t0 >= L) return;
-  const int t_pad = min(((L + TK - 1) / TK) * TK, t0 + CH);
+  const int nt = (L + TK - 1) / TK;
+  const int tile_lo = c * tpw;
+  if (tile_lo >= nt) return;
+  const int tile_hi = min(nt, tile_lo + tpw);
   const int64_t pbase = Seqs::pstart(s, start);
   const int lc = threadIdx.x % G, rsub = threadIdx.x / G;
 
-  if (threadIdx.x < D) {
-    const int nc = (L + CH - 1) / CH;
-    const int64_t* pp = kpart + ((int64_t)s * Hkv + g) * nch * D + threadIdx.x;
-    int64_t tot = 0;
-    for (int i = 0; i < nc; ++i) tot += pp[(int64_t)i * D];
-    const float m = (float)((double)tot / ((double)L * 16777216.0));
-    mean[threadIdx.x] = m;
-    if (c == 0) kmean_ws[((int64_t)s * Hkv + g) * D + threadIdx.x] = m;
+  {
+    const int d = threadIdx.x % D, r = threadIdx.x / D;
+    const int np = (nt + tpw - 1) / tpw;
+    const int64_t* pp = kpart + ((int64_t)s * Hkv + g) * npart * D + d;
+    int64_t t0 = 0, t1 = 0, t2 = 0, t3 = 0;
+    int i = r;
+    for (; i + 3 * TPC < np; i += 4 * TPC) {
+      t0 += pp[(int64_t)i * D];
+      t1 += pp[(int64_t)(i + TPC) * D];
+      t2 += pp[(int64_t)(i + 2 * TPC) * D];
+      t3 += pp[(int64_t)(i + 3 * TPC) * D];
+    }
+    for (; i < np; i += TPC) t0 += pp[(int64_t)i * D];
+    red[threadIdx.x] = (t0 + t1) + (t2 + t3);
+    __syncthreads();
+    if (r == 0) {
+      int64_t tot = 0;
+      for (int k2 = 0; k2 < TPC; ++k2) tot += red[k2 * D + d];
+      const float mu = (float)((double)tot / ((double)L * 16777216.0));
+      mean[d] = mu;
+      if (c == 0) kmean_ws[((int64_t)s * Hkv + g) * D + d] = mu;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-
   float mu[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) mu[j] = mean[lc * 8 + j];
-  for (int t = t0 + rsub; t < t_pad; t += RPP) {
-    const bool real = t < L;
-    float x[8];
-    float amax = 0.0f;
-    if (real) {
-      load8_f32(k + act.off(start, g, t) + lc * 8, x);
+
+  for (int tt = tile_lo; tt < tile_hi; ++tt) {
+    const int t0 = tt * TK;
+    char* tile = tiles + ((int64_t)g * (Ppad / TK) + (pbase + t0) / TK) * tile_bytes(D);
+    float* sk_tile = reinterpret_cast<float*>(tile + 3 * TK * D);
+    v8h kr[NP];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        x[j] = x[j] - mu[j];
-        amax = fmaxf(amax, fabsf(x[j]));
+    for (int i = 0; i < NP; ++i) {
+      const int t = t0 + i * RPP + rsub;
+      if (t < L) kr[i] = *reinterpret_cast<const v8h*>(k + act.off(start, g, t) + lc * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int n = i * RPP + rsub, t = t0 + n;
+      const bool real = t < L;
+      float x[8];
+      float amax = 0.0f;
+      if (real) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          x[j] = (float)kr[i][j] - mu[j];
+          amax = fmaxf(amax, fabsf(x[j]));
+        }
       }
+      amax = group_max<G>(amax);
+      const RowQ rq(real ? row_scale(amax, 24) : 0.0f);
+      const uint2 codes = real ? rq.pack8(x) : make_uint2(0u, 0u);
+      *reinterpret_cast<uint2*>(tile + ktile_off(n, lc * 8, D)) = codes;
+      if (lc == 0) sk_tile[n] = rq.s;
     }
-    amax = group_max<G>(amax);
-    const float sk = real ? row_scale(amax, 24) : 0.0f;
-    uint32_t lo = 0, hi = 0;
-    if (real) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) lo |= ((uint32_t)quant_code(x[j], sk) & 255u) << (8 * j);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) hi |= ((uint32_t)quant_code(x[4 + j], sk) & 255u) << (8 * j);
-    }
-    const int n = t % TK;
-    int8_t* tile = k8_ws + ((int64_t)g * Ppad + pbase + (t - n)) * D;
-    *reinterpret_cast<uint2*>(tile + ktile_off(n, lc * 8, D)) = make_uint2(lo, hi);
-    if (lc == 0) sk_ws[(int64_t)g * Ppad + pbase + t] = sk;
   }
 }
 
@@ -232,21 +287,20 @@ static hipError_t prep_d(const FwdGeom& g, const WsPlan& p, void* ws, hipStream_
   char* w = static_cast<char*>(ws);
   const Act ak = act_of(g, g.Hkv);
   Seqs sq{g.cu, g.S, g.max_len, g.T};
-  const dim3 grid(p.nch, g.Hkv, g.nseq);
-  prep_stage1_kernel<D><<<grid, 256, 0, stream>>>(
+  const dim3 grid(p.npart, g.Hkv, g.nseq);
+  prep_v_kernel<D><<<grid, 256, 0, stream>>>(
       static_cast<const _Float16*>(g.k), static_cast<const _Float16*>(g.v), ak, sq, g.Hkv,
-      p.nch, p.Ppad, reinterpret_cast<int64_t*>(w + p.off_kpart),
-      reinterpret_cast<float*>(w + p.off_sv), reinterpret_cast<_Float16*>(w + p.off_vh));
-  prep_stage2_kernel<D><<<grid, 256, 0, stream>>>(
-      static_cast<const _Float16*>(g.k), ak, sq, g.Hkv, p.nch, p.Ppad,
-      reinterpret_cast<const int64_t*>(w + p.off_kpart),
-      reinterpret_cast<float*>(w + p.off_kmean), reinterpret_cast<float*>(w + p.off_sk),
-      reinterpret_cast<int8_t*>(w + p.off_k8));
+      p.npart, p.tpw, p.Ppad, reinterpret_cast<int64_t*>(w + p.off_kpart),
+      reinterpret_cast<float*>(w + p.off_sv), w + p.off_tiles);
+  prep_k_kernel<D><<<grid, 256, 0, stream>>>(
+      static_cast<const _Float16*>(g.k), ak, sq, g.Hkv, p.npart, p.tpw, p.Ppad,
+      reinterpret_cast<const int64_t*>(w + p.off_kpart), reinterpret_cast<float*>(w + p.off_kmean),
+      w + p.off_tiles);
   return hipGetLastError();
 }
 
 hipError_t launch_prep(const FwdGeom& g, const WsPlan& p, void* ws, hipStream_t stream) {
-  if (p.nch == 0) return hipSuccess;  // every sequence is empty
+  if (p.ntile == 0) return hipSuccess;  // every sequence is empty
   switch (g.D) {
     case 32: return prep_d<32>(g, p, ws, stream);
     case 64: return prep_d<64>(g, p, ws, stream);
