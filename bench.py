@@ -36,6 +36,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic():
+    """HBM bytes per attention launch from the stored FETCH_SIZE / WRITE_SIZE counter
+    runs (scaled by a plain copy's readings), or None when the kernel sources have
+    changed since the counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        return rec["bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, budget_s: float):
     """Time the CPU oracle on whole heads of the same workload until the budget is
     spent; ops per second scaled to TOPS."""
@@ -172,12 +188,7 @@ def main():
 
     value = ops / (ms_step * 1e-3) / 1e12
     achieved = ops / (ms_attn * 1e-3) / 1e12
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        try:
-            traffic = json.load(open(TRAFFIC_FILE)).get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = measured_traffic()
     res = {
         "metric": "INT8 attn fwd effective TOPS & % int8 MFMA peak, Hq32/Hkv8 S4096 D128 causal",
         "value": round(value, 2),
