@@ -4,6 +4,8 @@ One step = one ``attn_int8_fwd`` call on the causal GQA workload B=1, Hq=32,
 Hkv=8, S=4096, D=128 (fp16 q/k/v ~ N(0,1), seeded): K-smoothing mean, K/V
 quantization, Q quantization and the attention itself, every kernel the call
 launches.  Inputs, output and workspace are resident in HBM before timing starts.
+The phases are also timed alone (K/V preparation, Q preparation, attention kernel)
+through the split entry points, which enqueue the same kernels.
 
 Prints one JSON line.  ``value`` is effective TOPS = algorithmic ops / time per
 step, with ops = 4*D*Hq*S^2/2 (two products of 2*D ops per (query, key) pair,
@@ -93,8 +95,8 @@ def main():
                     help="seconds of CPU oracle work for the cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-attn", type=int, default=0, metavar="N",
-                    help="profiling mode: prepare K/V once, launch only the attention kernel N "
-                         "times, print nothing else")
+                    help="profiling mode: prepare Q, K and V once, launch only the attention "
+                         "kernel N times, print nothing else")
     ap.add_argument("--profile-copy", type=int, default=0, metavar="MIB",
                     help="profiling mode: 10 plain device copies of MIB MiB (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -131,8 +133,9 @@ def main():
     ws = torch.empty(i8.attn_int8_workspace_bytes(B, Hq, Hkv, S, D), dtype=torch.uint8, device=dev)
     if args.profile_attn:
         i8.attn_int8_prepare_kv(k, v, Hq, workspace=ws)
+        i8.attn_int8_prepare_q(q, Hkv, ws)
         for _ in range(args.profile_attn):
-            i8.attn_int8_fwd_prepared(q, Hkv, ws, True, out=out)
+            i8.attn_int8_attend(ws, B, Hq, Hkv, S, D, True, out=out)
         torch.cuda.synchronize()
         log(f"bench: {args.profile_attn} attention launches")
         return
@@ -157,24 +160,25 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
     log(f"bench: {args.steps} steps, {ms_step * 1e3:.1f} us/step (host wall {t_wall * 1e3 / args.steps:.1f} us/step)")
 
-    # The phases alone: K/V preparation, then the attention kernel (dominant).
+    # The phases alone: the attention kernel (dominant), then K/V and Q preparation.
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
     i8.attn_int8_prepare_kv(k, v, Hq, workspace=ws)
-    for _ in range(args.warmup):
-        i8.attn_int8_fwd_prepared(q, Hkv, ws, True, out=out)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        i8.attn_int8_fwd_prepared(q, Hkv, ws, True, out=out)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_attn = e0.elapsed_time(e1) / args.steps
-    e0.record(stream)
-    for _ in range(args.steps):
-        i8.attn_int8_prepare_kv(k, v, Hq, workspace=ws)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_prep = e0.elapsed_time(e1) / args.steps
-    log(f"bench: attention kernel {ms_attn * 1e3:.1f} us, K/V preparation {ms_prep * 1e3:.1f} us")
+    i8.attn_int8_prepare_q(q, Hkv, ws)
+    ms_attn = timed(lambda: i8.attn_int8_attend(ws, B, Hq, Hkv, S, D, True, out=out))
+    ms_prep_kv = timed(lambda: i8.attn_int8_prepare_kv(k, v, Hq, workspace=ws))
+    ms_prep_q = timed(lambda: i8.attn_int8_prepare_q(q, Hkv, ws))
+    log(f"bench: attention kernel {ms_attn * 1e3:.1f} us, K/V preparation {ms_prep_kv * 1e3:.1f} us, "
+        f"Q preparation {ms_prep_q * 1e3:.1f} us")
 
     # quick parity guard on the benchmarked output (sampled rows of two heads)
     import oracle
@@ -207,7 +211,8 @@ def main():
                    "algorithmic_ops": ops},
         "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
         "attn_kernel_us": round(ms_attn * 1e3, 2),
-        "prep_us": round(ms_prep * 1e3, 2),
+        "prep_kv_us": round(ms_prep_kv * 1e3, 2),
+        "prep_q_us": round(ms_prep_q * 1e3, 2),
         "parity_sample_max_abs": max_abs,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4),

@@ -78,10 +78,11 @@ i8a_status quant_rowwise_i8(const void* x, int64_t rows, int32_t d, const float*
                             float* scales, void* stream);
 
 /*
- * attn_int8_workspace_bytes - device workspace needed by attn_int8_fwd and
- * attn_int8_debug_qk for these sizes (0 if the sizes are invalid).  The workspace
- * holds the K partial sums and means, the K codes and scales, and the dequantized V,
- * in private tiled layouts.  It needs no initialization.
+ * attn_int8_workspace_bytes - device workspace needed by attn_int8_fwd (and by the
+ * split entry points and attn_int8_debug_qk) for these sizes (0 if the sizes are
+ * invalid).  The workspace holds the K partial sums and means, the K codes and scales,
+ * the dequantized V, and the Q codes and scales, in private tiled layouts.  It needs no
+ * initialization.
  */
 size_t attn_int8_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D);
 
@@ -91,7 +92,8 @@ size_t attn_int8_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, 
  * causal=True)).
  *
  *   q    fp16 [B, Hq, S, D]      k, v  fp16 [B, Hkv, S, D]      out  fp16 [B, Hq, S, D]
- *   B, S >= 1; Hq, Hkv >= 1 with Hq % Hkv == 0 (Hkv == 1 is MQA); D in {32,64,128,256}.
+ *   1 <= B <= 65535, S >= 1, B*S <= 2^30; 1 <= Hkv <= Hq <= 65535 with Hq % Hkv == 0
+ *   (Hkv == 1 is MQA); D in {32, 64, 128, 256}.
  *   softmax_scale  finite and > 0 (the usual value is fp32(1/sqrt(D))); it multiplies
  *                  the dequantized logits and is not folded into Q.
  *   causal         0 or 1; causal means query i attends keys j <= i.
@@ -104,21 +106,28 @@ i8a_status attn_int8_fwd(const void* q, const void* k, const void* v, void* out,
                          int32_t causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * attn_int8_prepare_kv / attn_int8_fwd_prepared - attn_int8_fwd split in its two
- * phases, for callers that reuse one prepared K/V for several query batches and for
- * timing each phase alone.  attn_int8_prepare_kv runs the K-smoothing mean and the K
- * and V quantization of attn_int8_fwd into `workspace`; attn_int8_fwd_prepared then
- * quantizes q and runs the attention against that workspace.  The pair computes
- * exactly what attn_int8_fwd computes.  Sizes and workspace must be identical in both
- * calls; the workspace must not be modified in between; arguments as for
- * attn_int8_fwd.
+ * The phases of attn_int8_fwd as separate calls, for callers that reuse one prepared
+ * K/V for several query batches and for timing each phase alone:
+ *   attn_int8_prepare_kv   the K-smoothing mean and the K and V quantization;
+ *   attn_int8_prepare_q    the Q quantization;
+ *   attn_int8_attend       the attention over the prepared Q, K and V;
+ *   attn_int8_fwd_prepared attn_int8_prepare_q followed by attn_int8_attend.
+ * prepare_kv + prepare_q + attend computes exactly what attn_int8_fwd computes (it
+ * enqueues the same kernels).  Sizes (B, Hq, Hkv, S, D) and the workspace must be the
+ * same in every call of a sequence, and the workspace must not be modified in between
+ * except by these calls; the other arguments are as for attn_int8_fwd.
  */
 i8a_status attn_int8_prepare_kv(const void* k, const void* v, int32_t B, int32_t Hq, int32_t Hkv,
                                 int32_t S, int32_t D, void* workspace, size_t workspace_bytes,
                                 void* stream);
+i8a_status attn_int8_prepare_q(const void* q, int32_t B, int32_t Hq, int32_t Hkv, int32_t S,
+                               int32_t D, void* workspace, size_t workspace_bytes, void* stream);
+i8a_status attn_int8_attend(void* out, int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D,
+                            float softmax_scale, int32_t causal, const void* workspace,
+                            size_t workspace_bytes, void* stream);
 i8a_status attn_int8_fwd_prepared(const void* q, void* out, int32_t B, int32_t Hq, int32_t Hkv,
                                   int32_t S, int32_t D, float softmax_scale, int32_t causal,
-                                  const void* workspace, size_t workspace_bytes, void* stream);
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_int8_varlen_workspace_bytes - workspace for attn_int8_varlen_fwd (0 if the
@@ -142,7 +151,8 @@ size_t attn_int8_varlen_workspace_bytes(int32_t nseq, int64_t total_tokens, int3
  *               fall outside [0, total_tokens] or exceed max_seqlen is skipped by the
  *               kernels (its output rows are left unwritten) and never causes an
  *               out-of-bounds access.
- *   nseq >= 1, total_tokens >= 0, 0 <= max_seqlen <= total_tokens (host values).
+ *   1 <= nseq <= 65535, 0 <= total_tokens <= 2^30, 0 <= max_seqlen <= total_tokens
+ *   (host values).
  *   Other arguments as for attn_int8_fwd.
  */
 i8a_status attn_int8_varlen_fwd(const void* q, const void* k, const void* v, void* out,

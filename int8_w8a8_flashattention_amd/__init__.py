@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "quant_rowwise_i8", "attn_int8_fwd", "attn_int8_varlen_fwd", "attn_int8_debug_qk",
-    "attn_int8_prepare_kv", "attn_int8_fwd_prepared",
+    "attn_int8_prepare_kv", "attn_int8_prepare_q", "attn_int8_attend", "attn_int8_fwd_prepared",
     "attn_int8_workspace_bytes", "attn_int8_varlen_workspace_bytes", "library_path",
     "load_library", "SCALE_FP32", "SCALE_V4", "HEAD_DIMS",
 ]
@@ -48,6 +48,8 @@ _SIGS = {
                                                      _c_f32, _c_i32, _c_vp, _c_sz, _c_vp]),
     "attn_int8_debug_qk": (_c_i32, [_c_vp] * 3 + [_c_i32] * 11 + [_c_vp] * 6 + [_c_sz, _c_vp]),
     "attn_int8_prepare_kv": (_c_i32, [_c_vp] * 2 + [_c_i32] * 5 + [_c_vp, _c_sz, _c_vp]),
+    "attn_int8_prepare_q": (_c_i32, [_c_vp] + [_c_i32] * 5 + [_c_vp, _c_sz, _c_vp]),
+    "attn_int8_attend": (_c_i32, [_c_vp] + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_sz, _c_vp]),
     "attn_int8_fwd_prepared": (_c_i32, [_c_vp] * 2 + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_sz,
                                                                      _c_vp]),
     "i8a_status_string": (ctypes.c_char_p, [_c_i32]),
@@ -204,9 +206,10 @@ def attn_int8_fwd(q, k, v, causal=True, softmax_scale=None, out=None, workspace=
 
 
 def attn_int8_prepare_kv(k, v, Hq, workspace=None):
-    """First phase of :func:`attn_int8_fwd`: K-smoothing mean and K/V quantization of
+    """K/V phase of :func:`attn_int8_fwd`: K-smoothing mean and K/V quantization of
     dense k/v ``[B,Hkv,S,D]`` into a workspace, returned for
-    :func:`attn_int8_fwd_prepared`."""
+    :func:`attn_int8_fwd_prepared` (or :func:`attn_int8_prepare_q` and
+    :func:`attn_int8_attend`)."""
     for n, t in (("k", k), ("v", v)):
         _need_gpu_fp16(n, t, 4)
     if k.shape != v.shape or k.device != v.device:
@@ -223,9 +226,45 @@ def attn_int8_prepare_kv(k, v, Hq, workspace=None):
     return ws
 
 
+def attn_int8_prepare_q(q, Hkv, workspace):
+    """Q phase of :func:`attn_int8_fwd`: quantization of dense q ``[B,Hq,S,D]`` into a
+    workspace sized for the same problem (e.g. one from :func:`attn_int8_prepare_kv`)."""
+    _need_gpu_fp16("q", q, 4)
+    B, Hq, S, D = q.shape
+    if D not in HEAD_DIMS or Hkv < 1 or Hq % Hkv:
+        raise ValueError("bad head dim or Hkv")
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.attn_int8_prepare_q(_ptr(q), B, Hq, Hkv, S, D, _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream(q.device))
+    _check(st, "attn_int8_prepare_q")
+    return workspace
+
+
+def attn_int8_attend(workspace, B, Hq, Hkv, S, D, causal=True, softmax_scale=None, out=None):
+    """Attention phase of :func:`attn_int8_fwd` over a workspace holding prepared Q, K
+    and V for these sizes; returns (or fills) fp16 ``out [B,Hq,S,D]``."""
+    if D not in HEAD_DIMS or Hkv < 1 or Hq % Hkv:
+        raise ValueError("bad head dim or Hkv")
+    if out is None:
+        out = torch.empty((B, Hq, S, D), dtype=torch.float16, device=workspace.device)
+    _need_gpu_fp16("out", out, 4)
+    if tuple(out.shape) != (B, Hq, S, D):
+        raise ValueError("out must be [B, Hq, S, D]")
+    lib = load_library()
+    with torch.cuda.device(out.device):
+        st = lib.attn_int8_attend(_ptr(out), B, Hq, Hkv, S, D, _scale(softmax_scale, D),
+                                  int(bool(causal)), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(),
+                                  _stream(out.device))
+    _check(st, "attn_int8_attend")
+    return out
+
+
 def attn_int8_fwd_prepared(q, Hkv, workspace, causal=True, softmax_scale=None, out=None):
-    """Second phase of :func:`attn_int8_fwd`: attention of dense q ``[B,Hq,S,D]``
-    against a workspace filled by :func:`attn_int8_prepare_kv` for the same sizes."""
+    """Q and attention phases of :func:`attn_int8_fwd`: dense q ``[B,Hq,S,D]`` against a
+    workspace filled by :func:`attn_int8_prepare_kv` for the same sizes."""
     _need_gpu_fp16("q", q, 4)
     B, Hq, S, D = q.shape
     if D not in HEAD_DIMS or Hkv < 1 or Hq % Hkv:

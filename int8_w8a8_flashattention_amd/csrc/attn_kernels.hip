@@ -13,10 +13,10 @@
 // when a tile's max exceeds it by more than TAU in log2 units, which bounds every
 // p by 2^TAU and skips most rescales.
 //
-// K (int8) and the exact fp16 V come from the workspace in MFMA fragment order, so
-// the global->LDS copy is linear and every LDS operand read is a conflict-free
-// 16-byte read.  Q is quantized in the prologue (each query row is read by exactly
-// one workgroup) with the same row rule as the preparation kernels.
+// Q, K (int8) and the exact fp16 V come from the workspace in MFMA fragment order:
+// the Q fragments go straight to registers with coalesced 16-byte loads, and the K/V
+// tile copy into LDS is linear, so every LDS operand read is a conflict-free 16-byte
+// read.
 #include <type_traits>
 
 #include "i8a_device.h"
@@ -24,7 +24,7 @@
 
 namespace i8a {
 
-constexpr int BM = 128;      // query rows per workgroup
+constexpr int BM = BQ;       // query rows per workgroup
 constexpr float TAU = 8.0f;  // lazy-rescale threshold, log2 units
 
 template <int D>
@@ -36,7 +36,6 @@ struct Lay {
   static constexpr int NCH = STAGE / 16;         // 16-byte chunks per tile
   static constexpr int ROUNDS = (NCH + 255) / 256;
   static_assert(STAGE % 16 == 0, "tiles are copied in 16-byte chunks");
-  static_assert(BM * D + BM * 4 <= STAGE, "Q staging fits in one stage");
 };
 
 // Wait until this wave's outstanding vector-memory operations (the direct-to-LDS
@@ -60,43 +59,6 @@ __device__ __forceinline__ void copy_tile_async(const char* __restrict__ src, ch
                                          (__attribute__((address_space(3))) void*)(lbase), 16, 0,
                                          0);
     }
-  }
-}
-
-// Quantize the 32 query rows q_first.. of head h (one wave) into Q fragments in LDS
-// (layout qfrag_off) and their scales.  Rows at or beyond L quantize as zero rows.
-template <int D>
-__device__ __forceinline__ void quant_q_rows(const _Float16* __restrict__ q, const Act& aq,
-                                             int64_t start, int h, int q_first, int L,
-                                             int8_t* frag, float* qscale) {
-  constexpr int G = D / 8;
-  constexpr int RPP = 64 / G;
-  constexpr int NP = 32 / RPP;  // rows per lane
-  const int lane = threadIdx.x & 63, lc = lane % G, rs = lane / G;
-  v8h xr[NP];
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int t = q_first + i * RPP + rs;
-    if (t < L) xr[i] = *reinterpret_cast<const v8h*>(q + aq.off(start, h, t) + lc * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int m = i * RPP + rs;
-    const bool real = q_first + m < L;
-    float x[8];
-    float amax = 0.0f;
-    if (real) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        x[j] = (float)xr[i][j];
-        amax = fmaxf(amax, fabsf(x[j]));
-      }
-    }
-    amax = group_max<G>(amax);
-    const RowQ rq(real ? row_scale(amax, 24) : 0.0f);
-    const uint2 codes = real ? rq.pack8(x) : make_uint2(0u, 0u);
-    *reinterpret_cast<uint2*>(frag + qfrag_off(m, lc * 8)) = codes;
-    if (lc == 0) qscale[m] = rq.s;
   }
 }
 
@@ -125,9 +87,9 @@ __device__ __forceinline__ void decode_work(int bid, int nseq, int Hq, int Hkv, 
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
-    const _Float16* __restrict__ q, _Float16* __restrict__ out, Act aq, Seqs seqs, int Hq,
-    int Hkv, int nseq, int xcd_map, float qk_log2, const char* __restrict__ tiles,
-    int64_t Ppad) {
+    const int8_t* __restrict__ q8, const float* __restrict__ qs, int64_t Qpad,
+    _Float16* __restrict__ out, Act aq, Seqs seqs, int Hq, int Hkv, int nseq, int xcd_map,
+    float qk_log2, const char* __restrict__ tiles, int64_t Ppad) {
   using LY = Lay<D>;
   constexpr int NKB = LY::NKB;
   __shared__ __attribute__((aligned(16))) char smem[2 * LY::STAGE];
@@ -150,18 +112,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const int ntile_seq = (L + TK - 1) / TK;
   const int nt = CAUSAL ? min(ntile_seq, (min(q0 + BM, L) - 1) / TK + 1) : ntile_seq;
 
-  // Prologue: tile 0 streams into stage 0 while Q is quantized into stage 1.
+  // Prologue: tile 0 streams into stage 0 while the wave's 32 prepared Q rows (int8
+  // fragments, one 16-byte load per lane and d block) go to registers.
   copy_tile_async<D>(tsrc, smem, tid);
-  int8_t* qstage = reinterpret_cast<int8_t*>(smem + LY::STAGE);
-  float* qscl = reinterpret_cast<float*>(smem + LY::STAGE + BM * D);
-  quant_q_rows<D>(q, aq, start, h, qw0, L, qstage + w * 32 * D, qscl + 32 * w);
-  wait_vmem();
-  __syncthreads();
+  const int64_t qslot = (int64_t)h * Qpad + Seqs::qpstart(s, start) + qw0;
   v4i qf[NKB];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
-    qf[kb] = reinterpret_cast<const v4i*>(qstage + w * 32 * D)[kb * 64 + lane];
-  const float qsc = qscl[32 * w + m] * qk_log2;
+    qf[kb] = reinterpret_cast<const v4i*>(q8 + qslot * D)[kb * 64 + lane];
+  const float qsc = qs[qslot + m] * qk_log2;
+  wait_vmem();
   __syncthreads();
 
   v16f o[NKB];
@@ -296,31 +256,28 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 }
 
 // ----------------------------------------------------------------------------------
-// Debug: the int32 score tile through the forward's own Q quantization and K
-// fragments (read straight from the workspace), one wave per aligned 32x32 block.
+// Debug: the int32 score tile from the forward's own prepared Q and K fragments
+// (read straight from the workspace), one wave per aligned 32x32 block.
 template <int D>
 __global__ __launch_bounds__(64) void debug_qk_kernel(
-    const _Float16* __restrict__ q, Act aq, int S, int Hq, int Hkv, int b, int h, int row0,
-    int rows, int col0, int cols, const char* __restrict__ tiles,
-    const float* __restrict__ sv_ws,
+    const int8_t* __restrict__ q8, const float* __restrict__ qs, int64_t Qpad, int S, int Hq,
+    int Hkv, int b, int h, int row0, int rows, int col0, int cols,
+    const char* __restrict__ tiles, const float* __restrict__ sv_ws,
     const float* __restrict__ kmean_ws, int64_t Ppad, int32_t* __restrict__ s32,
     float* __restrict__ qscale, float* __restrict__ kscale, float* __restrict__ vscale,
     float* __restrict__ kmean_out) {
   constexpr int NKB = D / 32;
-  __shared__ __attribute__((aligned(16))) int8_t frag[32 * D];
-  __shared__ float qs[32];
   const int lane = threadIdx.x, m = lane & 31, hh = lane >> 5;
   const int qbase = (row0 & ~31) + 32 * blockIdx.x;
   const int kbase = (col0 & ~31) + 32 * blockIdx.y;
   const int64_t start = (int64_t)b * S;
   const int g = h / (Hq / Hkv);
   const int64_t pbase = Seqs::pstart(b, start);
+  const int64_t qslot = (int64_t)h * Qpad + Seqs::qpstart(b, start) + qbase;
 
-  quant_q_rows<D>(q, aq, start, h, qbase, S, frag, qs);
-  __syncthreads();
   v4i qf[NKB];
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) qf[kb] = reinterpret_cast<const v4i*>(frag)[kb * 64 + lane];
+  for (int kb = 0; kb < NKB; ++kb) qf[kb] = reinterpret_cast<const v4i*>(q8 + qslot * D)[kb * 64 + lane];
 
   const int tile0 = kbase - kbase % TK, nb = (kbase % TK) / 32;
   const char* tb = tiles + ((int64_t)g * (Ppad / TK) + (pbase + tile0) / TK) * tile_bytes(D);
@@ -340,7 +297,7 @@ __global__ __launch_bounds__(64) void debug_qk_kernel(
       s32[(int64_t)(qrow - row0) * cols + (n - col0)] = acc[i];
   }
   if (qscale && blockIdx.y == 0 && hh == 0 && qrow >= row0 && qrow < row0 + rows)
-    qscale[qrow - row0] = qs[m];
+    qscale[qrow - row0] = qs[qslot + m];
   const int n = kbase + m;
   if (blockIdx.x == 0 && hh == 0 && n >= col0 && n < col0 + cols) {
     if (kscale) kscale[n - col0] = reinterpret_cast<const float*>(tb + 3 * TK * D)[n - tile0];
@@ -376,8 +333,9 @@ static hipError_t attn_d(const FwdGeom& g, const WsPlan& p, const void* ws, hipS
   const float qk_log2 = g.softmax_scale * 1.4426950408889634f;
   Seqs sq{g.cu, g.S, g.max_len, g.T};
   attn_fwd_kernel<D, C><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-      static_cast<const _Float16*>(g.q), static_cast<_Float16*>(g.out), act_of(g, g.Hq), sq,
-      g.Hq, g.Hkv, g.nseq, xcd_map, qk_log2, w + p.off_tiles, p.Ppad);
+      reinterpret_cast<const int8_t*>(w + p.off_q8), reinterpret_cast<const float*>(w + p.off_qs),
+      p.Qpad, static_cast<_Float16*>(g.out), act_of(g, g.Hq), sq, g.Hq, g.Hkv, g.nseq, xcd_map,
+      qk_log2, w + p.off_tiles, p.Ppad);
   return hipGetLastError();
 }
 
@@ -402,8 +360,9 @@ static hipError_t debug_d(const FwdGeom& g, const WsPlan& p, const void* ws, int
   const int rb = ((row0 + rows - 1) >> 5) - (row0 >> 5) + 1;
   const int cb = ((col0 + cols - 1) >> 5) - (col0 >> 5) + 1;
   debug_qk_kernel<D><<<dim3(rb, cb), dim3(64), 0, stream>>>(
-      static_cast<const _Float16*>(g.q), act_of(g, g.Hq), g.S, g.Hq, g.Hkv, b, h, row0, rows,
-      col0, cols, w + p.off_tiles, reinterpret_cast<const float*>(w + p.off_sv),
+      reinterpret_cast<const int8_t*>(w + p.off_q8), reinterpret_cast<const float*>(w + p.off_qs),
+      p.Qpad, g.S, g.Hq, g.Hkv, b, h, row0, rows, col0, cols, w + p.off_tiles,
+      reinterpret_cast<const float*>(w + p.off_sv),
       reinterpret_cast<const float*>(w + p.off_kmean), p.Ppad, s32, qscale, kscale, vscale,
       kmean);
   return hipGetLastError();

@@ -27,10 +27,11 @@ static i8a_status hip_fail(hipError_t e, const char* what) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-WsPlan plan_workspace(int32_t nseq, int64_t total_tokens, int32_t max_len, int32_t Hkv,
-                      int32_t D) {
+WsPlan plan_workspace(int32_t nseq, int64_t total_tokens, int32_t max_len, int32_t Hq,
+                      int32_t Hkv, int32_t D) {
   WsPlan p;
   p.nseq = nseq;
+  p.Hq = Hq;
   p.Hkv = Hkv;
   p.D = D;
   p.ntile = (max_len + TK - 1) / TK;
@@ -38,6 +39,7 @@ WsPlan plan_workspace(int32_t nseq, int64_t total_tokens, int32_t max_len, int32
   if (p.tpw < 1) p.tpw = 1;
   p.npart = (p.ntile + p.tpw - 1) / p.tpw;
   p.Ppad = (int64_t)TK * ((total_tokens + TK - 1) / TK + nseq);
+  p.Qpad = (int64_t)BQ * ((total_tokens + BQ - 1) / BQ + nseq);
   size_t off = 0;
   p.off_kpart = off;
   off = align256(off + (size_t)nseq * Hkv * p.npart * D * 8);
@@ -47,6 +49,10 @@ WsPlan plan_workspace(int32_t nseq, int64_t total_tokens, int32_t max_len, int32
   off = align256(off + (size_t)Hkv * p.Ppad * 4);
   p.off_tiles = off;
   off = align256(off + (size_t)Hkv * (p.Ppad / TK) * tile_bytes(D));
+  p.off_q8 = off;
+  off = align256(off + (size_t)Hq * p.Qpad * D);
+  p.off_qs = off;
+  off = align256(off + (size_t)Hq * p.Qpad * 4);
   p.total = off;
   return p;
 }
@@ -54,6 +60,9 @@ WsPlan plan_workspace(int32_t nseq, int64_t total_tokens, int32_t max_len, int32
 static bool head_dim_ok(int32_t D) { return D == 32 || D == 64 || D == 128 || D == 256; }
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Heads and sequences index the y and z dimensions of the preparation grids.
+static const int32_t kMaxGridYZ = 65535;
 
 // Common checks of the forward entry points.  Sizes in tokens are bounded so that
 // every element offset fits in int64 and every token index in int32.
@@ -68,6 +77,7 @@ static i8a_status check_common(const void* q, const void* k, const void* v, cons
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
     return fail(I8A_ERR_INVALID_ARG, "need Hq >= 1, Hkv >= 1 and Hq %% Hkv == 0 (Hq=%d Hkv=%d)",
                 Hq, Hkv);
+  if (Hq > kMaxGridYZ) return fail(I8A_ERR_INVALID_ARG, "Hq must be <= %d", kMaxGridYZ);
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale))
     return fail(I8A_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   if (causal != 0 && causal != 1) return fail(I8A_ERR_INVALID_ARG, "causal must be 0 or 1");
@@ -120,25 +130,36 @@ i8a_status quant_rowwise_i8(const void* x, int64_t rows, int32_t d, const float*
 
 size_t attn_int8_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D) {
   if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || !head_dim_ok(D)) return 0;
+  if (B > kMaxGridYZ || Hq > kMaxGridYZ) return 0;
   if ((int64_t)B * S > kMaxTokens) return 0;
-  return plan_workspace(B, (int64_t)B * S, S, Hkv, D).total;
+  return plan_workspace(B, (int64_t)B * S, S, Hq, Hkv, D).total;
 }
 
 size_t attn_int8_varlen_workspace_bytes(int32_t nseq, int64_t total_tokens, int32_t max_seqlen,
                                         int32_t Hq, int32_t Hkv, int32_t D) {
   if (nseq < 1 || total_tokens < 0 || total_tokens > kMaxTokens || max_seqlen < 0 ||
-      max_seqlen > total_tokens || Hq < 1 || Hkv < 1 || Hq % Hkv || !head_dim_ok(D))
+      max_seqlen > total_tokens || Hq < 1 || Hkv < 1 || Hq % Hkv || !head_dim_ok(D) ||
+      nseq > kMaxGridYZ || Hq > kMaxGridYZ)
     return 0;
-  return plan_workspace(nseq, total_tokens, max_seqlen, Hkv, D).total;
+  return plan_workspace(nseq, total_tokens, max_seqlen, Hq, Hkv, D).total;
 }
 
-static i8a_status run_forward(const FwdGeom& g, void* ws, size_t ws_bytes, hipStream_t stream) {
-  const WsPlan p = plan_workspace(g.nseq, g.T, g.max_len, g.Hkv, g.D);
+// The phases of a forward call, enqueued in order: K/V preparation, Q preparation,
+// attention.
+enum Phase { PH_KV = 1, PH_Q = 2, PH_ATTN = 4 };
+
+static i8a_status run_phases(const FwdGeom& g, int phases, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  const WsPlan p = plan_workspace(g.nseq, g.T, g.max_len, g.Hq, g.Hkv, g.D);
   if (ws_bytes < p.total)
     return fail(I8A_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", p.total,
                 ws_bytes);
-  hipError_t e = launch_prep(g, p, ws, stream);
-  if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
+  hipError_t e;
+  if (phases & (PH_KV | PH_Q)) {
+    e = launch_prep(g, p, ws, (phases & PH_KV) != 0, (phases & PH_Q) != 0, stream);
+    if (e != hipSuccess) return hip_fail(e, "preparation launch");
+  }
+  if (!(phases & PH_ATTN)) return I8A_OK;
   e = launch_attn(g, p, ws, stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return I8A_OK;
@@ -149,10 +170,11 @@ i8a_status attn_int8_fwd(const void* q, const void* k, const void* v, void* out,
                          int32_t causal, void* workspace, size_t workspace_bytes, void* stream) {
   i8a_status st = check_common(q, k, v, out, Hq, Hkv, D, softmax_scale, causal, workspace);
   if (st != I8A_OK) return st;
-  if (B < 1 || S < 1) return fail(I8A_ERR_INVALID_ARG, "need B >= 1 and S >= 1");
+  if (B < 1 || S < 1 || B > kMaxGridYZ)
+    return fail(I8A_ERR_INVALID_ARG, "need 1 <= B <= %d and S >= 1", kMaxGridYZ);
   if ((int64_t)B * S > kMaxTokens) return fail(I8A_ERR_INVALID_ARG, "B*S too large");
   FwdGeom g{q, k, v, out, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D, softmax_scale, causal};
-  return run_forward(g, workspace, workspace_bytes, (hipStream_t)stream);
+  return run_phases(g, PH_KV | PH_Q | PH_ATTN, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 i8a_status attn_int8_prepare_kv(const void* k, const void* v, int32_t B, int32_t Hq, int32_t Hkv,
@@ -161,35 +183,48 @@ i8a_status attn_int8_prepare_kv(const void* k, const void* v, int32_t B, int32_t
   // q and out are not touched by this phase; k stands in for their checks.
   i8a_status st = check_common(k, k, v, k, Hq, Hkv, D, 1.0f, 0, workspace);
   if (st != I8A_OK) return st;
-  if (B < 1 || S < 1 || (int64_t)B * S > kMaxTokens)
-    return fail(I8A_ERR_INVALID_ARG, "need B >= 1, S >= 1, B*S in range");
+  if (B < 1 || S < 1 || B > kMaxGridYZ || (int64_t)B * S > kMaxTokens)
+    return fail(I8A_ERR_INVALID_ARG, "need 1 <= B <= %d, S >= 1, B*S in range", kMaxGridYZ);
   FwdGeom g{nullptr, k, v, nullptr, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D, 1.0f, 0};
-  const WsPlan p = plan_workspace(B, (int64_t)B * S, S, Hkv, D);
-  if (workspace_bytes < p.total)
-    return fail(I8A_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", p.total,
-                workspace_bytes);
-  hipError_t e = launch_prep(g, p, workspace, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
-  return I8A_OK;
+  return run_phases(g, PH_KV, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+i8a_status attn_int8_prepare_q(const void* q, int32_t B, int32_t Hq, int32_t Hkv, int32_t S,
+                               int32_t D, void* workspace, size_t workspace_bytes, void* stream) {
+  // k, v and out are not touched by this phase; q stands in for their checks.
+  i8a_status st = check_common(q, q, q, q, Hq, Hkv, D, 1.0f, 0, workspace);
+  if (st != I8A_OK) return st;
+  if (B < 1 || S < 1 || B > kMaxGridYZ || (int64_t)B * S > kMaxTokens)
+    return fail(I8A_ERR_INVALID_ARG, "need 1 <= B <= %d, S >= 1, B*S in range", kMaxGridYZ);
+  FwdGeom g{q, nullptr, nullptr, nullptr, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D, 1.0f, 0};
+  return run_phases(g, PH_Q, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+i8a_status attn_int8_attend(void* out, int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D,
+                            float softmax_scale, int32_t causal, const void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  // Only out and the workspace are touched; out stands in for the q/k/v checks.
+  i8a_status st = check_common(out, out, out, out, Hq, Hkv, D, softmax_scale, causal, workspace);
+  if (st != I8A_OK) return st;
+  if (B < 1 || S < 1 || B > kMaxGridYZ || (int64_t)B * S > kMaxTokens)
+    return fail(I8A_ERR_INVALID_ARG, "need 1 <= B <= %d, S >= 1, B*S in range", kMaxGridYZ);
+  FwdGeom g{nullptr, nullptr, nullptr, out, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D,
+            softmax_scale, causal};
+  return run_phases(g, PH_ATTN, const_cast<void*>(workspace), workspace_bytes,
+                    (hipStream_t)stream);
 }
 
 i8a_status attn_int8_fwd_prepared(const void* q, void* out, int32_t B, int32_t Hq, int32_t Hkv,
                                   int32_t S, int32_t D, float softmax_scale, int32_t causal,
-                                  const void* workspace, size_t workspace_bytes, void* stream) {
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   // k and v are not read by this phase; q stands in for their checks.
   i8a_status st = check_common(q, q, q, out, Hq, Hkv, D, softmax_scale, causal, workspace);
   if (st != I8A_OK) return st;
-  if (B < 1 || S < 1 || (int64_t)B * S > kMaxTokens)
-    return fail(I8A_ERR_INVALID_ARG, "need B >= 1, S >= 1, B*S in range");
+  if (B < 1 || S < 1 || B > kMaxGridYZ || (int64_t)B * S > kMaxTokens)
+    return fail(I8A_ERR_INVALID_ARG, "need 1 <= B <= %d, S >= 1, B*S in range", kMaxGridYZ);
   FwdGeom g{q, nullptr, nullptr, out, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D,
             softmax_scale, causal};
-  const WsPlan p = plan_workspace(B, (int64_t)B * S, S, Hkv, D);
-  if (workspace_bytes < p.total)
-    return fail(I8A_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", p.total,
-                workspace_bytes);
-  hipError_t e = launch_attn(g, p, workspace, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "attention launch");
-  return I8A_OK;
+  return run_phases(g, PH_Q | PH_ATTN, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 i8a_status attn_int8_varlen_fwd(const void* q, const void* k, const void* v, void* out,
@@ -199,7 +234,8 @@ i8a_status attn_int8_varlen_fwd(const void* q, const void* k, const void* v, voi
                                 size_t workspace_bytes, void* stream) {
   if (!cu_seqlens) return fail(I8A_ERR_INVALID_ARG, "null cu_seqlens");
   if (!aligned(cu_seqlens, 4)) return fail(I8A_ERR_INVALID_ARG, "misaligned cu_seqlens");
-  if (nseq < 1) return fail(I8A_ERR_INVALID_ARG, "nseq must be >= 1");
+  if (nseq < 1 || nseq > kMaxGridYZ)
+    return fail(I8A_ERR_INVALID_ARG, "nseq must be in [1, %d]", kMaxGridYZ);
   if (total_tokens < 0 || total_tokens > kMaxTokens)
     return fail(I8A_ERR_INVALID_ARG, "total_tokens out of range");
   if (max_seqlen < 0 || max_seqlen > total_tokens)
@@ -215,7 +251,7 @@ i8a_status attn_int8_varlen_fwd(const void* q, const void* k, const void* v, voi
   if (st != I8A_OK) return st;
   FwdGeom g{q, k, v, out, cu_seqlens, nseq, 0, max_seqlen, total_tokens, Hq, Hkv, D,
             softmax_scale, causal};
-  return run_forward(g, workspace, workspace_bytes, (hipStream_t)stream);
+  return run_phases(g, PH_KV | PH_Q | PH_ATTN, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 i8a_status attn_int8_debug_qk(const void* q, const void* k, const void* v, int32_t B, int32_t Hq,
@@ -227,8 +263,8 @@ i8a_status attn_int8_debug_qk(const void* q, const void* k, const void* v, int32
   // `out` is not written by this entry; q stands in for the alignment check.
   i8a_status st = check_common(q, k, v, q, Hq, Hkv, D, 1.0f, 0, workspace);
   if (st != I8A_OK) return st;
-  if (B < 1 || S < 1 || (int64_t)B * S > kMaxTokens)
-    return fail(I8A_ERR_INVALID_ARG, "need B >= 1, S >= 1, B*S in range");
+  if (B < 1 || S < 1 || B > kMaxGridYZ || (int64_t)B * S > kMaxTokens)
+    return fail(I8A_ERR_INVALID_ARG, "need 1 <= B <= %d, S >= 1, B*S in range", kMaxGridYZ);
   if (b < 0 || b >= B || h < 0 || h >= Hq) return fail(I8A_ERR_INVALID_ARG, "b/h out of range");
   if (rows < 1 || cols < 1 || row0 < 0 || col0 < 0 || (int64_t)row0 + rows > S ||
       (int64_t)col0 + cols > S)
@@ -236,13 +272,10 @@ i8a_status attn_int8_debug_qk(const void* q, const void* k, const void* v, int32
                 cols, S);
   if (!s32_out || !aligned(s32_out, 4)) return fail(I8A_ERR_INVALID_ARG, "bad s32_out");
   FwdGeom g{q, k, v, nullptr, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D, 1.0f, 0};
-  const WsPlan p = plan_workspace(B, (int64_t)B * S, S, Hkv, D);
-  if (workspace_bytes < p.total)
-    return fail(I8A_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", p.total,
-                workspace_bytes);
-  hipError_t e = launch_prep(g, p, workspace, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
-  e = launch_debug_qk(g, p, workspace, b, h, row0, rows, col0, cols, s32_out, qscale_out,
+  const WsPlan p = plan_workspace(B, (int64_t)B * S, S, Hq, Hkv, D);
+  i8a_status pst = run_phases(g, PH_KV | PH_Q, workspace, workspace_bytes, (hipStream_t)stream);
+  if (pst != I8A_OK) return pst;
+  hipError_t e = launch_debug_qk(g, p, workspace, b, h, row0, rows, col0, cols, s32_out, qscale_out,
                       kscale_out, vscale_out, kmean_out, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "debug score launch");
   return I8A_OK;

@@ -48,6 +48,11 @@ struct Seqs {
   static __device__ __forceinline__ int64_t pstart(int s, int64_t start) {
     return (int64_t)TK * (start / TK + s);
   }
+  // The same for the Q slots, padded to BQ rows: the BQ-row query tiles of one
+  // sequence never reach into the next one's slots.
+  static __device__ __forceinline__ int64_t qpstart(int s, int64_t start) {
+    return (int64_t)BQ * (start / BQ + s);
+  }
 };
 
 // Element offset of token t of head h of sequence s in an fp16 activation tensor:

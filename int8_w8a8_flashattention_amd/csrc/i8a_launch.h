@@ -23,19 +23,26 @@ __host__ __device__ constexpr int tile_bytes(int D) { return TK * D * 3 + TK * 4
 //   kmean  fp32  [nseq][Hkv][D]          K-smoothing means
 //   sv     fp32  [Hkv][Ppad]             V row scales (kept for the debug dump)
 //   tiles  bytes [Hkv][Ppad / TK][tile_bytes(D)]
+//   q8     int8  [Hq][Qpad / 32][32 * D] Q codes, 32-row blocks in MFMA fragment order
+//   qs     fp32  [Hq][Qpad]              Q row scales
+// K/V token slots are padded per sequence to TK rows (Seqs::pstart), Q slots to BQ
+// rows (Seqs::qpstart), so every tile or query tile starts on a boundary.
 // Cap on the K partial sums per (sequence, kv head): the K quantization workgroups
 // each reduce all of them to get the mean.
 constexpr int MAX_PARTS = 64;
+// Query rows per attention workgroup, and per Q preparation workgroup.
+constexpr int BQ = 128;
 
 struct WsPlan {
-  int32_t nseq, Hkv, D, ntile;  // ntile: TK-token tiles of the longest sequence
-  int32_t tpw, npart;           // tiles per prep workgroup, partial sums per (seq, head)
-  int64_t Ppad;                 // padded token slots per kv head
-  size_t off_kpart, off_kmean, off_sv, off_tiles, total;
+  int32_t nseq, Hq, Hkv, D, ntile;  // ntile: TK-token tiles of the longest sequence
+  int32_t tpw, npart;               // tiles per prep workgroup, partial sums per (seq, head)
+  int64_t Ppad;                     // padded K/V token slots per kv head
+  int64_t Qpad;                     // padded Q token slots per query head
+  size_t off_kpart, off_kmean, off_sv, off_tiles, off_q8, off_qs, total;
 };
 
-WsPlan plan_workspace(int32_t nseq, int64_t total_tokens, int32_t max_len, int32_t Hkv,
-                      int32_t D);
+WsPlan plan_workspace(int32_t nseq, int64_t total_tokens, int32_t max_len, int32_t Hq,
+                      int32_t Hkv, int32_t D);
 
 // Geometry of one forward call: dense when cu == nullptr.
 struct FwdGeom {
@@ -53,10 +60,12 @@ hipError_t launch_quant_rowwise(const void* x, int64_t rows, int32_t d, const fl
                                 int64_t rows_per_group, int32_t scale_bits, int8_t* codes,
                                 float* scales, hipStream_t stream);
 
-// K-smoothing mean, K quantization and V quantization into the workspace.
-hipError_t launch_prep(const FwdGeom& g, const WsPlan& p, void* ws, hipStream_t stream);
+// Preparation into the workspace: with kv, the K-smoothing mean and the K and V
+// quantization; with qq, the Q quantization (codes in fragment order, row scales).
+hipError_t launch_prep(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, bool qq,
+                       hipStream_t stream);
 
-// Attention over the prepared workspace (Q is quantized inside).
+// Attention over the prepared workspace (Q, K and V all prepared).
 hipError_t launch_attn(const FwdGeom& g, const WsPlan& p, const void* ws, hipStream_t stream);
 
 // Debug dump of S32 and scales for batch b, query head h (dense geometry only).

@@ -1,6 +1,6 @@
-// quant_kernels.hip - row quantization and the K/V preparation of the forward.
+// quant_kernels.hip - row quantization and the Q, K and V preparation of the forward.
 //
-// All three kernels are HBM-bound streaming passes: rows are read once with 16-byte
+// All of these kernels are HBM-bound streaming passes: rows are read once with 16-byte
 // coalesced loads, one row per group of D/8 lanes, and the row absolute maximum is a
 // butterfly reduction inside that lane group.
 #include "i8a_device.h"
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(
 }
 
 // ----------------------------------------------------------------------------------
-// K/V preparation, three launches over the TK-token tiles of every (sequence, kv
+// K/V preparation, two launches over the TK-token tiles of every (sequence, kv
 // head).  A tile's block in the workspace (tile_bytes) holds its int8 K codes, its
 // exact fp16 dequantized V and its fp32 K scales, in the order the attention kernel
 // copies them to LDS.  Slots between a sequence's end and its last tile boundary are
@@ -60,19 +60,26 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(
 //   Phase B: each thread assembles whole 16-byte V fragments (8 keys of one channel)
 //            from LDS and stores them with coalesced writes.
 template <int D>
-__global__ __launch_bounds__(256) void prep_v_kernel(
-    const _Float16* __restrict__ k, const _Float16* __restrict__ v, Act act, Seqs seqs, int Hkv,
-    int npart, int tpw, int64_t Ppad, int64_t* __restrict__ kpart, float* __restrict__ sv_ws,
-    char* __restrict__ tiles) {
+struct PrepVShared {
+  int64_t red[(256 / (D / 8)) * D];
+  __attribute__((aligned(16))) _Float16 vraw[TK * D];
+  float2 rsy[TK];
+};
+
+template <int D>
+__device__ __forceinline__ void prep_v_body(
+    const _Float16* __restrict__ k, const _Float16* __restrict__ v, const Act& act,
+    const Seqs& seqs, int Hkv, int npart, int tpw, int64_t Ppad, int64_t* __restrict__ kpart,
+    float* __restrict__ sv_ws, char* __restrict__ tiles, int c, int g, int s,
+    PrepVShared<D>& sh) {
   constexpr int G = D / 8;       // lanes per row
   constexpr int RPP = 256 / G;   // rows per pass
   constexpr int NP = TK / RPP;   // rows per thread and tile
   constexpr int NF = TK * D / 8 / 256;  // V fragments per thread and tile
-  __shared__ int64_t red[RPP * D];
-  __shared__ __attribute__((aligned(16))) _Float16 vraw[TK * D];
-  __shared__ float2 rsy[TK];
+  int64_t* red = sh.red;
+  _Float16* vraw = sh.vraw;
+  float2* rsy = sh.rsy;
 
-  const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   int64_t start;
   int L;
   seqs.bounds(s, start, L);
@@ -245,6 +252,91 @@ __global__ __launch_bounds__(256) void prep_k_kernel(const _Float16* __restrict_
 }
 
 // ----------------------------------------------------------------------------------
+// Q preparation (workgroup = BQ query rows of one sequence and query head): the rows
+// quantized with the Q/K row rule into the B-operand fragment order of 32-row blocks
+// (the attention kernel loads a block straight into registers), and the row scales.
+// Rows past the sequence end get zero codes and scale 0.  The fragments are assembled
+// in LDS and written with coalesced 16-byte stores.
+template <int D>
+__device__ __forceinline__ void prep_q_body(const _Float16* __restrict__ q, const Act& act,
+                                            const Seqs& seqs, int64_t Qpad,
+                                            int8_t* __restrict__ q8, float* __restrict__ qs,
+                                            int c, int h, int s, int8_t* frag) {
+  constexpr int G = D / 8;      // lanes per row
+  constexpr int RPP = 256 / G;  // rows per pass
+  constexpr int NP = BQ / RPP;  // rows per thread
+  int64_t start;
+  int L;
+  seqs.bounds(s, start, L);
+  const int r0 = c * BQ;
+  if (r0 >= L) return;
+  const int lc = threadIdx.x % G, rsub = threadIdx.x / G;
+  const int64_t slot = (int64_t)h * Qpad + Seqs::qpstart(s, start) + r0;
+
+  v8h xr[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int t = r0 + i * RPP + rsub;
+    if (t < L) xr[i] = *reinterpret_cast<const v8h*>(q + act.off(start, h, t) + lc * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int n = i * RPP + rsub;
+    const bool real = r0 + n < L;
+    float x[8];
+    float amax = 0.0f;
+    if (real) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        x[j] = (float)xr[i][j];
+        amax = fmaxf(amax, fabsf(x[j]));
+      }
+    }
+    amax = group_max<G>(amax);
+    const RowQ rq(real ? row_scale(amax, 24) : 0.0f);
+    const uint2 codes = real ? rq.pack8(x) : make_uint2(0u, 0u);
+    *reinterpret_cast<uint2*>(frag + (n >> 5) * 32 * D + qfrag_off(n & 31, lc * 8)) = codes;
+    if (lc == 0) qs[slot + n] = rq.s;
+  }
+  __syncthreads();
+  const v4i* src = reinterpret_cast<const v4i*>(frag);
+  v4i* dst = reinterpret_cast<v4i*>(q8 + slot * D);
+  for (int k = threadIdx.x; k < BQ * D / 16; k += 256) dst[k] = src[k];
+}
+
+// Launch 1 of the preparation: the V tiles with the K partial sums (blocks
+// [0, nv) over (part, kv head, sequence)) and, independent of them, the Q rows
+// (blocks [nv, nv + nq) over (row chunk, query head, sequence)) in one grid, so the
+// two streaming passes overlap.
+template <int D>
+union PrepShared {
+  PrepVShared<D> v;
+  __attribute__((aligned(16))) int8_t qfrag[BQ * D];
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void prep_vq_kernel(
+    const _Float16* __restrict__ q, const _Float16* __restrict__ k,
+    const _Float16* __restrict__ v, Act aq, Act akv, Seqs seqs, int Hq, int Hkv, int npart,
+    int tpw, int64_t Ppad, int64_t Qpad, int nqc, int64_t* __restrict__ kpart,
+    float* __restrict__ sv_ws, char* __restrict__ tiles, int8_t* __restrict__ q8,
+    float* __restrict__ qs, int nv) {
+  __shared__ PrepShared<D> sh;
+  int b = blockIdx.x;
+  if (b < nv) {
+    const int c = b % npart;
+    b /= npart;
+    prep_v_body<D>(k, v, akv, seqs, Hkv, npart, tpw, Ppad, kpart, sv_ws, tiles, c, b % Hkv,
+                   b / Hkv, sh.v);
+  } else {
+    b -= nv;
+    const int c = b % nqc;
+    b /= nqc;
+    prep_q_body<D>(q, aq, seqs, Qpad, q8, qs, c, b % Hq, b / Hq, sh.qfrag);
+  }
+}
+
+// ----------------------------------------------------------------------------------
 hipError_t launch_quant_rowwise(const void* x, int64_t rows, int32_t d, const float* sub_mean,
                                 int64_t rows_per_group, int32_t scale_bits, int8_t* codes,
                                 float* scales, hipStream_t stream) {
@@ -282,30 +374,44 @@ static Act act_of(const FwdGeom& g, int H) {
   return a;
 }
 
+// Launches of the preparation.  With q (PH_Q) the Q rows ride in launch 1; with k/v
+// (PH_KV) launch 1 also prepares V and the K sums and launch 2 quantizes K.
 template <int D>
-static hipError_t prep_d(const FwdGeom& g, const WsPlan& p, void* ws, hipStream_t stream) {
+static hipError_t prep_d(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, bool qq,
+                         hipStream_t stream) {
   char* w = static_cast<char*>(ws);
-  const Act ak = act_of(g, g.Hkv);
+  const Act akv = act_of(g, g.Hkv);
   Seqs sq{g.cu, g.S, g.max_len, g.T};
-  const dim3 grid(p.npart, g.Hkv, g.nseq);
-  prep_v_kernel<D><<<grid, 256, 0, stream>>>(
-      static_cast<const _Float16*>(g.k), static_cast<const _Float16*>(g.v), ak, sq, g.Hkv,
-      p.npart, p.tpw, p.Ppad, reinterpret_cast<int64_t*>(w + p.off_kpart),
-      reinterpret_cast<float*>(w + p.off_sv), w + p.off_tiles);
-  prep_k_kernel<D><<<grid, 256, 0, stream>>>(
-      static_cast<const _Float16*>(g.k), ak, sq, g.Hkv, p.npart, p.tpw, p.Ppad,
-      reinterpret_cast<const int64_t*>(w + p.off_kpart), reinterpret_cast<float*>(w + p.off_kmean),
-      w + p.off_tiles);
+  const int64_t nv = kv ? (int64_t)p.npart * g.Hkv * g.nseq : 0;
+  const int nqc = (g.max_len + BQ - 1) / BQ;
+  const int64_t nq = qq ? (int64_t)nqc * g.Hq * g.nseq : 0;
+  if (nv + nq > 0x7fffffff) return hipErrorInvalidValue;
+  if (nv + nq > 0)
+    prep_vq_kernel<D><<<dim3((unsigned)(nv + nq)), 256, 0, stream>>>(
+        static_cast<const _Float16*>(g.q), static_cast<const _Float16*>(g.k),
+        static_cast<const _Float16*>(g.v), act_of(g, g.Hq), akv, sq, g.Hq, g.Hkv, p.npart,
+        p.tpw, p.Ppad, p.Qpad, nqc, reinterpret_cast<int64_t*>(w + p.off_kpart),
+        reinterpret_cast<float*>(w + p.off_sv), w + p.off_tiles,
+        reinterpret_cast<int8_t*>(w + p.off_q8), reinterpret_cast<float*>(w + p.off_qs),
+        (int)nv);
+  if (kv) {
+    const dim3 grid(p.npart, g.Hkv, g.nseq);
+    prep_k_kernel<D><<<grid, 256, 0, stream>>>(
+        static_cast<const _Float16*>(g.k), akv, sq, g.Hkv, p.npart, p.tpw, p.Ppad,
+        reinterpret_cast<const int64_t*>(w + p.off_kpart),
+        reinterpret_cast<float*>(w + p.off_kmean), w + p.off_tiles);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_prep(const FwdGeom& g, const WsPlan& p, void* ws, hipStream_t stream) {
-  if (p.ntile == 0) return hipSuccess;  // every sequence is empty
+hipError_t launch_prep(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, bool qq,
+                       hipStream_t stream) {
+  if (g.max_len == 0) return hipSuccess;  // every sequence is empty
   switch (g.D) {
-    case 32: return prep_d<32>(g, p, ws, stream);
-    case 64: return prep_d<64>(g, p, ws, stream);
-    case 128: return prep_d<128>(g, p, ws, stream);
-    case 256: return prep_d<256>(g, p, ws, stream);
+    case 32: return prep_d<32>(g, p, ws, kv, qq, stream);
+    case 64: return prep_d<64>(g, p, ws, kv, qq, stream);
+    case 128: return prep_d<128>(g, p, ws, kv, qq, stream);
+    case 256: return prep_d<256>(g, p, ws, kv, qq, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
     names = i8.header_functions()
     for n in ("quant_rowwise_i8", "attn_int8_fwd", "attn_int8_varlen_fwd", "attn_int8_debug_qk",
               "attn_int8_workspace_bytes", "attn_int8_varlen_workspace_bytes",
-              "attn_int8_prepare_kv", "attn_int8_fwd_prepared",
+              "attn_int8_prepare_kv", "attn_int8_prepare_q", "attn_int8_attend",
+              "attn_int8_fwd_prepared",
               "i8a_status_string", "i8a_last_error"):
         assert n in names
 
@@ -61,6 +62,10 @@ def test_workspace_sizes(lib):
     assert lib.attn_int8_varlen_workspace_bytes(3, 100, 60, 4, 2, 64) > 0
     assert lib.attn_int8_varlen_workspace_bytes(3, 100, 101, 4, 2, 64) == 0
     assert lib.attn_int8_varlen_workspace_bytes(0, 100, 60, 4, 2, 64) == 0
+    assert lib.attn_int8_varlen_workspace_bytes(70000, 100000, 60, 4, 2, 64) == 0
+    assert lib.attn_int8_workspace_bytes(70000, 32, 8, 16, 128) == 0
+    # the workspace also holds the int8 Q codes and their scales
+    assert a >= 8 * 1000 * 128 * 3 + 32 * 1000 * (128 + 4)
 
 
 def _fwd(lib, D=128, Hq=32, Hkv=8, S=64, B=1, scale=0.1, causal=1, ws=FAKE, wsb=1 << 40,
@@ -76,6 +81,8 @@ def test_forward_rejects_bad_arguments(lib):
     assert _fwd(lib, Hkv=0) == INVALID
     assert _fwd(lib, S=0) == INVALID
     assert _fwd(lib, B=0) == INVALID
+    assert _fwd(lib, B=70000) == INVALID
+    assert _fwd(lib, Hq=70000, Hkv=1) == INVALID
     assert _fwd(lib, scale=0.0) == INVALID
     assert _fwd(lib, scale=float("inf")) == INVALID
     assert _fwd(lib, scale=float("nan")) == INVALID
@@ -89,12 +96,26 @@ def test_forward_rejects_bad_arguments(lib):
     assert b"workspace needs" in lib.i8a_last_error()
 
 
+def test_split_phases_reject_bad_arguments(lib):
+    need = lib.attn_int8_workspace_bytes(1, 8, 2, 256, 64)
+    assert lib.attn_int8_prepare_q(None, 1, 8, 2, 256, 64, FAKE, need, None) == INVALID
+    assert lib.attn_int8_prepare_q(FAKE, 1, 8, 3, 256, 64, FAKE, need, None) == INVALID
+    assert lib.attn_int8_prepare_q(FAKE, 1, 8, 2, 256, 48, FAKE, need, None) == HEADDIM
+    assert lib.attn_int8_prepare_q(FAKE, 1, 8, 2, 256, 64, FAKE, need - 1, None) == WSSMALL
+    assert lib.attn_int8_attend(None, 1, 8, 2, 256, 64, 0.1, 1, FAKE, need, None) == INVALID
+    assert lib.attn_int8_attend(FAKE, 1, 8, 2, 256, 64, 0.0, 1, FAKE, need, None) == INVALID
+    assert lib.attn_int8_attend(FAKE, 1, 8, 2, 256, 64, 0.1, 3, FAKE, need, None) == INVALID
+    assert lib.attn_int8_attend(FAKE, 1, 8, 2, 256, 64, 0.1, 1, None, need, None) == INVALID
+    assert lib.attn_int8_attend(FAKE, 1, 8, 2, 256, 64, 0.1, 1, FAKE, need - 1, None) == WSSMALL
+
+
 def test_varlen_rejects_bad_arguments(lib):
     def call(nseq=2, maxlen=10, T=20, D=64, cu=FAKE, wsb=1 << 40):
         return lib.attn_int8_varlen_fwd(FAKE, FAKE, FAKE, FAKE, cu, nseq, maxlen, T, 4, 2, D, 0.1,
                                         1, FAKE, wsb, None)
     assert call(cu=None) == INVALID
     assert call(nseq=0) == INVALID
+    assert call(nseq=70000, maxlen=10, T=100000) == INVALID
     assert call(maxlen=21) == INVALID
     assert call(T=-1) == INVALID
     assert call(D=48) == HEADDIM

@@ -225,6 +225,23 @@ def test_prepare_then_prepared_equals_fwd():
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
+def test_split_phases_equal_fwd_and_reuse_kv():
+    say("prepare_kv + prepare_q + attend == fwd; one K/V preparation serves two query batches")
+    w = workloads.dense(64, 1, 8, 2, 517, 64, True, k_offset=0.5)
+    w2 = workloads.dense(65, 1, 8, 2, 517, 64, True)
+    q, k, v, q2 = dev(w.q), dev(w.k), dev(w.v), dev(w2.q)
+    a = host(i8.attn_int8_fwd(q, k, v, True))
+    a2 = host(i8.attn_int8_fwd(q2, k, v, True))
+    ws = i8.attn_int8_prepare_kv(k, v, 8)
+    i8.attn_int8_prepare_q(q, 2, ws)
+    b = host(i8.attn_int8_attend(ws, 1, 8, 2, 517, 64, True))
+    i8.attn_int8_prepare_q(q2, 2, ws)
+    b2 = host(i8.attn_int8_attend(ws, 1, 8, 2, 517, 64, True))
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    assert np.array_equal(a2.view(np.uint16), b2.view(np.uint16))
+    check_close(b2, oracle.attn_int8_fwd(w2.q, w.k, w.v, True), "second query batch")
+
+
 def test_varlen_equal_lengths_equals_dense():
     say("varlen == dense for equal lengths")
     w = workloads.dense(61, 3, 4, 2, 192, 64, True)
