@@ -81,8 +81,10 @@ __device__ __forceinline__ float row_scale(float amax, int bits) {
   return t;
 }
 
-// Symmetric int8 code of x for a row scale s: clamp(rint(x / s), -127, 127), with the
-// correctly rounded fp32 quotient and round-half-to-even; a zero scale gives 0.
+// Symmetric int8 code of x for a row scale s: rint(x / s), with the correctly rounded
+// fp32 quotient and round-half-to-even; a zero scale gives 0.  No clamp is needed:
+// the scale is RN(amax / 127) (or that rounded up), so |x| / s <= 127 (1 + 2^-23) and
+// the rounded quotient never reaches 127.5.
 // `y` is the row's correctly rounded reciprocal RN(1/s) (0 when s == 0): with it the
 // quotient RN(x/s) is q0 = RN(x*y) corrected once by the exact remainder
 // r = x - s*q0 (an FMA), q = RN(q0 + r*y) -- the FMA division step of Markstein,
@@ -95,7 +97,7 @@ struct RowQ {
     const float q0 = __fmul_rn(x, y);
     const float r = __builtin_fmaf(-q0, s, x);
     const float q = __builtin_fmaf(r, y, q0);
-    return fminf(fmaxf(__builtin_rintf(q), -127.0f), 127.0f);
+    return __builtin_rintf(q);
   }
   // Eight codes packed little-endian into two dwords (two's complement bytes).
   __device__ __forceinline__ uint2 pack8(const float (&x)[8]) const {
@@ -108,11 +110,25 @@ struct RowQ {
   }
 };
 
-// Max over groups of G consecutive lanes (G a power of two <= 64).
+// A lane permutation through DPP (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_perm(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Max over groups of G consecutive lanes (G a power of two <= 64), all lanes active.
+// Within 16-lane rows DPP does it: quad_perm [1,0,3,2] and [2,3,0,1] leave the quad
+// max in every lane of a quad; row_half_mirror (lane i <- 7 - i) then pairs the two
+// quads of each 8 lanes, and row_mirror (lane i <- 15 - i) the two halves of a row.
+// Wider groups finish with cross-row shuffles.
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  if constexpr (G >= 2) v = fmaxf(v, dpp_perm<0xB1>(v));
+  if constexpr (G >= 4) v = fmaxf(v, dpp_perm<0x4E>(v));
+  if constexpr (G >= 8) v = fmaxf(v, dpp_perm<0x141>(v));
+  if constexpr (G >= 16) v = fmaxf(v, dpp_perm<0x140>(v));
+  if constexpr (G >= 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
+  if constexpr (G >= 64) v = fmaxf(v, __shfl_xor(v, 32, 64));
   return v;
 }
 

@@ -60,10 +60,12 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(
 //   Phase B: each thread assembles whole 16-byte V fragments (8 keys of one channel)
 //            from LDS and stores them with coalesced writes.
 template <int D>
-struct PrepVShared {
-  int64_t red[(256 / (D / 8)) * D];
-  __attribute__((aligned(16))) _Float16 vraw[TK * D];
-  float2 rsy[TK];
+union PrepVShared {
+  struct {
+    __attribute__((aligned(16))) _Float16 vraw[TK * D];
+    float2 rsy[TK];
+  } t;                               // per tile
+  int64_t red[(256 / (D / 8)) * D];  // the final K-sum reduction, after the last tile
 };
 
 template <int D>
@@ -77,8 +79,8 @@ __device__ __forceinline__ void prep_v_body(
   constexpr int NP = TK / RPP;   // rows per thread and tile
   constexpr int NF = TK * D / 8 / 256;  // V fragments per thread and tile
   int64_t* red = sh.red;
-  _Float16* vraw = sh.vraw;
-  float2* rsy = sh.rsy;
+  _Float16* vraw = sh.t.vraw;
+  float2* rsy = sh.t.rsy;
 
   int64_t start;
   int L;
@@ -191,6 +193,18 @@ __global__ __launch_bounds__(256) void prep_k_kernel(const _Float16* __restrict_
   const int64_t pbase = Seqs::pstart(s, start);
   const int lc = threadIdx.x % G, rsub = threadIdx.x / G;
 
+  // The first tile's K rows are requested before the mean reduction (they do not
+  // depend on it), so the two memory latencies overlap.
+  auto load_rows = [&](int t0, v8h (&kr)[NP]) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int t = t0 + i * RPP + rsub;
+      if (t < L) kr[i] = *reinterpret_cast<const v8h*>(k + act.off(start, g, t) + lc * 8);
+    }
+  };
+  v8h kr[NP];
+  load_rows(tile_lo * TK, kr);
+
   {
     const int d = threadIdx.x % D, r = threadIdx.x / D;
     const int np = (nt + tpw - 1) / tpw;
@@ -223,12 +237,7 @@ __global__ __launch_bounds__(256) void prep_k_kernel(const _Float16* __restrict_
     const int t0 = tt * TK;
     char* tile = tiles + ((int64_t)g * (Ppad / TK) + (pbase + t0) / TK) * tile_bytes(D);
     float* sk_tile = reinterpret_cast<float*>(tile + 3 * TK * D);
-    v8h kr[NP];
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int t = t0 + i * RPP + rsub;
-      if (t < L) kr[i] = *reinterpret_cast<const v8h*>(k + act.off(start, g, t) + lc * 8);
-    }
+    if (tt > tile_lo) load_rows(t0, kr);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int n = i * RPP + rsub, t = t0 + n;
@@ -252,24 +261,32 @@ __global__ __launch_bounds__(256) void prep_k_kernel(const _Float16* __restrict_
 }
 
 // ----------------------------------------------------------------------------------
-// Q preparation (workgroup = BQ query rows of one sequence and query head): the rows
+// Q preparation (workgroup = QCH query rows of one sequence and query head): the rows
 // quantized with the Q/K row rule into the B-operand fragment order of 32-row blocks
 // (the attention kernel loads a block straight into registers), and the row scales.
 // Rows past the sequence end get zero codes and scale 0.  The fragments are assembled
 // in LDS and written with coalesced 16-byte stores.
+// Query rows per Q preparation workgroup: small work items, so that many more
+// workgroups than fit at once stream through and their loads, quantization and stores
+// overlap.
+constexpr int QCH = 64;
+static_assert(BQ % QCH == 0 && QCH % 32 == 0, "Q chunks hold whole 32-row blocks");
+
 template <int D>
 __device__ __forceinline__ void prep_q_body(const _Float16* __restrict__ q, const Act& act,
                                             const Seqs& seqs, int64_t Qpad,
                                             int8_t* __restrict__ q8, float* __restrict__ qs,
                                             int c, int h, int s, int8_t* frag) {
-  constexpr int G = D / 8;      // lanes per row
-  constexpr int RPP = 256 / G;  // rows per pass
-  constexpr int NP = BQ / RPP;  // rows per thread
+  constexpr int G = D / 8;       // lanes per row
+  constexpr int RPP = 256 / G;   // rows per pass
+  constexpr int NP = QCH / RPP;  // rows per thread
   int64_t start;
   int L;
   seqs.bounds(s, start, L);
-  const int r0 = c * BQ;
-  if (r0 >= L) return;
+  const int r0 = c * QCH;
+  // Chunks up to the end of the sequence's last BQ-row query tile: rows past the
+  // sequence end within that tile are written too (zero codes, scale 0).
+  if (r0 >= (L + BQ - 1) / BQ * BQ) return;
   const int lc = threadIdx.x % G, rsub = threadIdx.x / G;
   const int64_t slot = (int64_t)h * Qpad + Seqs::qpstart(s, start) + r0;
 
@@ -301,7 +318,7 @@ __device__ __forceinline__ void prep_q_body(const _Float16* __restrict__ q, cons
   __syncthreads();
   const v4i* src = reinterpret_cast<const v4i*>(frag);
   v4i* dst = reinterpret_cast<v4i*>(q8 + slot * D);
-  for (int k = threadIdx.x; k < BQ * D / 16; k += 256) dst[k] = src[k];
+  for (int k = threadIdx.x; k < QCH * D / 16; k += 256) dst[k] = src[k];
 }
 
 // Launch 1 of the preparation: the V tiles with the K partial sums (blocks
@@ -311,7 +328,7 @@ __device__ __forceinline__ void prep_q_body(const _Float16* __restrict__ q, cons
 template <int D>
 union PrepShared {
   PrepVShared<D> v;
-  __attribute__((aligned(16))) int8_t qfrag[BQ * D];
+  __attribute__((aligned(16))) int8_t qfrag[QCH * D];
 };
 
 template <int D>
@@ -383,7 +400,7 @@ static hipError_t prep_d(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, b
   const Act akv = act_of(g, g.Hkv);
   Seqs sq{g.cu, g.S, g.max_len, g.T};
   const int64_t nv = kv ? (int64_t)p.npart * g.Hkv * g.nseq : 0;
-  const int nqc = (g.max_len + BQ - 1) / BQ;
+  const int nqc = (g.max_len + BQ - 1) / BQ * (BQ / QCH);
   const int64_t nq = qq ? (int64_t)nqc * g.Hq * g.nseq : 0;
   if (nv + nq > 0x7fffffff) return hipErrorInvalidValue;
   if (nv + nq > 0)
