@@ -17,7 +17,7 @@
 // the Q fragments go straight to registers with coalesced 16-byte loads, and the K/V
 // tile copy into LDS is linear, so every LDS operand read is a conflict-free 16-byte
 // read.
-#include <type_traits>
+#include <float.h>
 
 #include "i8a_device.h"
 #include "i8a_launch.h"
@@ -37,6 +37,27 @@ struct Lay {
   static constexpr int ROUNDS = (NCH + 255) / 256;
   static_assert(STAGE % 16 == 0, "tiles are copied in 16-byte chunks");
 };
+
+// Max of two scores.  The IEEE-754-2019 maximum (v_maximum3_f32) needs no quieting
+// of its inputs, unlike fmaxf (maxNum) after a select or a lane exchange; the scores
+// are never NaN, where the two agree.
+__device__ __forceinline__ float smax(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
+// Value of the lane 32 apart (the other half of the wave), through v_permlane32_swap
+// (a VALU exchange, no LDS round trip): with v in both operands the swap leaves the
+// low half's values in one result and the high half's in the other.
+__device__ __forceinline__ float other_half_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return smax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float other_half_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Wait until this wave's outstanding vector-memory operations (the direct-to-LDS
 // tile copies) have completed: vmcnt = 0, lgkmcnt and expcnt left unconstrained.
@@ -103,7 +124,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   if (slot >= nqt_s) return;
   const int qt = CAUSAL ? nqt_s - 1 - slot : slot;
   const int g = h / (Hq / Hkv);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 31, hh = lane >> 5;
+  // The wave index is wave-uniform: readfirstlane lets the compiler see that, so the
+  // per-wave tile conditions below become scalar branches.
+  const int tid = threadIdx.x, lane = tid & 63, m = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t pbase = Seqs::pstart(s, start);
   const char* tsrc = tiles + ((int64_t)g * (Ppad / TK) + pbase / TK) * LY::STAGE;
 
@@ -120,7 +144,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
     qf[kb] = reinterpret_cast<const v4i*>(q8 + qslot * D)[kb * 64 + lane];
-  const float qsc = qs[qslot + m] * qk_log2;
+  const float qsc = fmaxf(qs[qslot + m] * qk_log2, FLT_MIN);
   wait_vmem();
   __syncthreads();
 
@@ -132,10 +156,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   float mrun = -INFINITY, lsum = 0.0f;
   const int qi = qw0 + m;
 
-  // One 64-key tile.  MASK: some key of the tile lies above this wave's diagonal or
-  // past the sequence end (only those tiles pay for the mask).
-  auto tile_step = [&](const char* st, int kt0, auto maskc) {
-    constexpr bool MASK = decltype(maskc)::value;
+  // One 64-key tile.  `masked`: some key of the tile lies above this wave's diagonal
+  // or past the sequence end; only those tiles pay for the mask, in a uniform branch
+  // of its own.  qsc > 0 (an all-zero query row has scale 0; FLT_MIN stands in for
+  // it, its scores are 0 either way), so a masked score of -inf gives p = 0 and a
+  // fully masked tile gives a row max of -inf without special cases.
+  auto tile_step = [&](const char* st, int kt0, bool masked) {
     const v4i* kl = reinterpret_cast<const v4i*>(st);
     const v4i* vl = reinterpret_cast<const v4i*>(st + LY::KB);
     const float* skl = reinterpret_cast<const float*>(st + LY::KB + LY::VB);
@@ -160,20 +186,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) tv[16 * nb + 4 * J + r] = (float)acc[nb][4 * J + r] * skv[r];
       }
-    if constexpr (MASK) {
+    if (masked) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int key = kt0 + 32 * (i >> 4) + 8 * ((i >> 2) & 3) + 4 * hh + (i & 3);
         if ((CAUSAL && key > qi) || key >= L) tv[i] = -INFINITY;
       }
     }
-    float mx = fmaxf(tv[0], tv[1]);
+
+    // M is raised (with a rescale of O and l) only where the tile's max exceeds it by
+    // more than TAU.  The lane max runs as two chains of v_maximum3.
+    float m0 = smax(tv[0], tv[1]), m1 = smax(tv[2], tv[3]);
 #pragma unroll
-    for (int i = 2; i < 32; i += 2) mx = fmaxf(mx, fmaxf(tv[i], tv[i + 1]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // Every row has a key in the first tile, so mx is finite unless the tile is
-    // masked for this row.
-    const float mc = (MASK && mx == -INFINITY) ? -INFINITY : mx * qsc;
+    for (int i = 4; i < 32; i += 4) {
+      m0 = smax(smax(m0, tv[i]), tv[i + 1]);
+      m1 = smax(smax(m1, tv[i + 2]), tv[i + 3]);
+    }
+    const float mc = other_half_max(smax(m0, m1)) * qsc;
     const bool upd = mc > mrun + TAU;
     if (__any(upd)) {
       const float mnew = upd ? mc : mrun;
@@ -185,21 +214,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
     }
-    const float muse = (MASK && mrun == -INFINITY) ? 0.0f : mrun;
+    // A row whose keys were all masked so far keeps M = -inf and takes its
+    // probabilities against 0 (all of them are 0).
+    const float muse = mrun == -INFINITY ? 0.0f : mrun;
 
-    // p = 2^(t * qsc - M), rounded to fp16: the P^T operand of the P.V product and
-    // the terms of the row sum.  Masked keys get p = 0 explicitly (an all-zero query
-    // row has qsc = 0, and -inf * 0 is not a number).
+    // p = 2^(t * qsc - M), rounded to fp16: the P^T operand of the P.V product and the
+    // terms of the row sum (one v_dot2 chain).
     v8h pk[4];
 #pragma unroll
     for (int i = 0; i < 32; i += 2) {
       v2f pp;
       pp[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(tv[i], qsc, -muse));
       pp[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(tv[i + 1], qsc, -muse));
-      if constexpr (MASK) {
-        if (tv[i] == -INFINITY) pp[0] = 0.0f;
-        if (tv[i + 1] == -INFINITY) pp[1] = 0.0f;
-      }
       const v2h ph = __builtin_convertvector(pp, v2h);
       pk[i >> 3][i & 7] = ph[0];
       pk[i >> 3][(i & 7) + 1] = ph[1];
@@ -212,6 +238,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         const v2h pr = {pk[kg][e], pk[kg][e + 1]};
         lsum = __builtin_amdgcn_fdot2(pr, ones, lsum, false);
       }
+
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
@@ -227,19 +254,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       copy_tile_async<D>(tsrc + (int64_t)(j + 1) * LY::STAGE, smem + ((j + 1) & 1) * LY::STAGE,
                          tid);
     const int kt0 = j * TK;
-    if (!CAUSAL || kt0 <= qw0 + 31) {
-      const char* st = smem + (j & 1) * LY::STAGE;
-      const bool masked = (CAUSAL && kt0 + TK - 1 > qw0) || kt0 + TK > L;
-      if (masked)
-        tile_step(st, kt0, std::true_type{});
-      else
-        tile_step(st, kt0, std::false_type{});
-    }
+    if (!CAUSAL || kt0 <= qw0 + 31)
+      tile_step(smem + (j & 1) * LY::STAGE, kt0,
+                (CAUSAL && kt0 + TK - 1 > qw0) || kt0 + TK > L);
     wait_vmem();
     __syncthreads();
   }
 
-  lsum += __shfl_xor(lsum, 32, 64);
+  lsum = other_half_sum(lsum);
   if (qi < L) {
     const float inv = 1.0f / lsum;
     _Float16* orow = out + aq.off(start, h, qi);
