@@ -187,10 +187,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         for (int r = 0; r < 4; ++r) tv[16 * nb + 4 * J + r] = (float)acc[nb][4 * J + r] * skv[r];
       }
     if (masked) {
+      // Key kt0 + 4*hh + off_i is masked when off_i exceeds one per-lane bound (the
+      // last visible key, causal diagonal or sequence end, relative to kt0 + 4*hh):
+      // one compare and one select per score.
+      const int last = (CAUSAL ? min(qi, L - 1) : L - 1) - kt0 - 4 * hh;
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        const int key = kt0 + 32 * (i >> 4) + 8 * ((i >> 2) & 3) + 4 * hh + (i & 3);
-        if ((CAUSAL && key > qi) || key >= L) tv[i] = -INFINITY;
+        const int off = 32 * (i >> 4) + 8 * ((i >> 2) & 3) + (i & 3);
+        if (off > last) tv[i] = -INFINITY;
       }
     }
 

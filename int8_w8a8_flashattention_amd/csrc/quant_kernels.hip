@@ -45,42 +45,96 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(
 }
 
 // ----------------------------------------------------------------------------------
-// K/V preparation, two launches over the TK-token tiles of every (sequence, kv
-// head).  A tile's block in the workspace (tile_bytes) holds its int8 K codes, its
-// exact fp16 dequantized V and its fp32 K scales, in the order the attention kernel
-// copies them to LDS.  Slots between a sequence's end and its last tile boundary are
-// zero (codes, V and scales), so a masked key still multiplies finite numbers.
+// K/V preparation over the TK-token tiles of every (sequence, kv head).  A tile's
+// block in the workspace (tile_bytes) holds its int8 K codes, its exact fp16
+// dequantized V and its fp32 K scales, in the order the attention kernel copies them
+// to LDS.  Slots between a sequence's end and its last tile boundary are zero (codes,
+// V and scales), so a masked key still multiplies finite numbers.
+//
+// Launch 1 computes only the exact per-channel K sums (the K-smoothing statistic);
+// launch 2 runs everything that reads them (the K quantization) together with the
+// work that does not (V tiles, Q rows), so the one dependent step of the preparation
+// costs a short pass over K and the rest streams in one grid.
 
-// Launch 1 (workgroup = tpw consecutive tiles of one sequence and kv head): V rows
-// quantized per token with the 4-bit scale rule, written as the exact fp16 values
-// sv * code in the V fragment layout; and the exact per-channel K sums of those tiles
-// (the K-smoothing statistic) as one int64 partial.
-//   Phase A: coalesced loads of the tile's K and V rows; K sums; each V row's scale
-//            and reciprocal; the raw V rows into LDS.
+// Launch 1 (workgroup = tpw consecutive tiles of one sequence and kv head): the exact
+// per-channel sums of the tiles' K rows as one int64 partial, in units of 2^-24 (every
+// fp16 value is an integer multiple of 2^-24).
+template <int D>
+__global__ __launch_bounds__(256) void prep_ksum_kernel(const _Float16* __restrict__ k,
+                                                        Act act, Seqs seqs, int Hkv, int npart,
+                                                        int tpw,
+                                                        int64_t* __restrict__ kpart) {
+  constexpr int G = D / 8;      // lanes per row
+  constexpr int RPP = 256 / G;  // rows per pass
+  constexpr int NP = TK / RPP;  // rows per thread and tile
+  __shared__ int64_t red[RPP * D];
+  int b = blockIdx.x;
+  const int c = b % npart;
+  b /= npart;
+  const int g = b % Hkv, s = b / Hkv;
+  int64_t start;
+  int L;
+  seqs.bounds(s, start, L);
+  const int nt = (L + TK - 1) / TK;
+  const int tile_lo = c * tpw;
+  if (tile_lo >= nt) return;
+  const int tile_hi = min(nt, tile_lo + tpw);
+  const int lc = threadIdx.x % G, rsub = threadIdx.x / G;
+
+  int64_t acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0;
+  for (int tt = tile_lo; tt < tile_hi; ++tt) {
+    const int t0 = tt * TK;
+    v8h kr[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int t = t0 + i * RPP + rsub;
+      if (t < L) kr[i] = *reinterpret_cast<const v8h*>(k + act.off(start, g, t) + lc * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      if (t0 + i * RPP + rsub < L) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += fp16_fixed24(kr[i][j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[rsub * D + lc * 8 + j] = acc[j];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    int64_t tot = 0;
+#pragma unroll
+    for (int r = 0; r < RPP; ++r) tot += red[r * D + threadIdx.x];
+    kpart[(((int64_t)s * Hkv + g) * npart + c) * D + threadIdx.x] = tot;
+  }
+}
+
+// Launch 2, V part (workgroup = tpw consecutive tiles of one sequence and kv head): V
+// rows quantized per token with the 4-bit scale rule, written as the exact fp16
+// values sv * code in the V fragment layout.
+//   Phase A: coalesced loads of the tile's V rows; each row's scale and reciprocal;
+//            the raw rows into LDS.
 //   Phase B: each thread assembles whole 16-byte V fragments (8 keys of one channel)
 //            from LDS and stores them with coalesced writes.
 template <int D>
-union PrepVShared {
-  struct {
-    __attribute__((aligned(16))) _Float16 vraw[TK * D];
-    float2 rsy[TK];
-  } t;                               // per tile
-  int64_t red[(256 / (D / 8)) * D];  // the final K-sum reduction, after the last tile
+struct PrepVShared {
+  __attribute__((aligned(16))) _Float16 vraw[TK * D];
+  float2 rsy[TK];
 };
 
 template <int D>
-__device__ __forceinline__ void prep_v_body(
-    const _Float16* __restrict__ k, const _Float16* __restrict__ v, const Act& act,
-    const Seqs& seqs, int Hkv, int npart, int tpw, int64_t Ppad, int64_t* __restrict__ kpart,
-    float* __restrict__ sv_ws, char* __restrict__ tiles, int c, int g, int s,
-    PrepVShared<D>& sh) {
+__device__ __forceinline__ void prep_v_body(const _Float16* __restrict__ v, const Act& act,
+                                            const Seqs& seqs, int tpw, int64_t Ppad,
+                                            float* __restrict__ sv_ws, char* __restrict__ tiles,
+                                            int c, int g, int s, PrepVShared<D>& sh) {
   constexpr int G = D / 8;       // lanes per row
   constexpr int RPP = 256 / G;   // rows per pass
   constexpr int NP = TK / RPP;   // rows per thread and tile
   constexpr int NF = TK * D / 8 / 256;  // V fragments per thread and tile
-  int64_t* red = sh.red;
-  _Float16* vraw = sh.t.vraw;
-  float2* rsy = sh.t.rsy;
+  _Float16* vraw = sh.vraw;
+  float2* rsy = sh.rsy;
 
   int64_t start;
   int L;
@@ -92,17 +146,13 @@ __device__ __forceinline__ void prep_v_body(
   const int64_t pbase = Seqs::pstart(s, start);
   const int lc = threadIdx.x % G, rsub = threadIdx.x / G;
 
-  int64_t acc[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0;
   for (int tt = tile_lo; tt < tile_hi; ++tt) {
     const int t0 = tt * TK;
-    v8h kr[NP], vr[NP];
+    v8h vr[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int t = t0 + i * RPP + rsub;
       if (t < L) {
-        kr[i] = *reinterpret_cast<const v8h*>(k + act.off(start, g, t) + lc * 8);
         vr[i] = *reinterpret_cast<const v8h*>(v + act.off(start, g, t) + lc * 8);
       } else {
 #pragma unroll
@@ -114,13 +164,8 @@ __device__ __forceinline__ void prep_v_body(
       const int n = i * RPP + rsub, t = t0 + n;
       const bool real = t < L;
       float amax = 0.0f;
-      if (real) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          acc[j] += fp16_fixed24(kr[i][j]);
-          amax = fmaxf(amax, fabsf((float)vr[i][j]));
-        }
-      }
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((float)vr[i][j]));
       amax = group_max<G>(amax);
       *reinterpret_cast<v8h*>(vraw + n * D + lc * 8) = vr[i];
       if (lc == 0) {
@@ -154,35 +199,33 @@ __device__ __forceinline__ void prep_v_body(
     }
     __syncthreads();
   }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) red[rsub * D + lc * 8 + j] = acc[j];
-  __syncthreads();
-  if (threadIdx.x < D) {
-    int64_t tot = 0;
-    for (int r = 0; r < RPP; ++r) tot += red[r * D + threadIdx.x];
-    kpart[(((int64_t)s * Hkv + g) * npart + c) * D + threadIdx.x] = tot;
-  }
 }
 
-// Launch 2 (same grid): the K-smoothing mean of the sequence, reduced by every
-// workgroup from the launch-1 partials (at most MAX_PARTS of them; integer sums, so
-// every workgroup gets the same value), divided in fp64 and rounded to fp32; then
-// the K rows of the workgroup's tiles quantized from fp32(k) - mean into the K
-// fragment layout, with the K scales after the V block.
+// Launch 2, K part (workgroup = tpw consecutive tiles of one sequence and kv head): the
+// K-smoothing mean of the sequence, reduced by every workgroup from
+// the launch-1 partials (at most MAX_PARTS of them; integer sums, so every workgroup
+// gets the same value), divided in fp64 and rounded to fp32; then the K rows of the
+// workgroup's tiles quantized from fp32(k) - mean into the K fragment layout, with
+// the K scales after the V block.
 template <int D>
-__global__ __launch_bounds__(256) void prep_k_kernel(const _Float16* __restrict__ k, Act act,
-                                                     Seqs seqs, int Hkv, int npart, int tpw,
-                                                     int64_t Ppad,
-                                                     const int64_t* __restrict__ kpart,
-                                                     float* __restrict__ kmean_ws,
-                                                     char* __restrict__ tiles) {
+struct PrepKShared {
+  int64_t red[256];
+  float mean[D];
+};
+
+template <int D>
+__device__ __forceinline__ void prep_k_body(const _Float16* __restrict__ k, const Act& act,
+                                            const Seqs& seqs, int Hkv, int npart, int tpw,
+                                            int64_t Ppad, const int64_t* __restrict__ kpart,
+                                            float* __restrict__ kmean_ws,
+                                            char* __restrict__ tiles, int c, int g, int s,
+                                            PrepKShared<D>& sh) {
   constexpr int G = D / 8;
   constexpr int RPP = 256 / G;
   constexpr int NP = TK / RPP;
   constexpr int TPC = 256 / D;  // threads per channel in the mean reduction
-  __shared__ int64_t red[256];
-  __shared__ float mean[D];
-  const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  int64_t* red = sh.red;
+  float* mean = sh.mean;
   int64_t start;
   int L;
   seqs.bounds(s, start, L);
@@ -321,32 +364,39 @@ __device__ __forceinline__ void prep_q_body(const _Float16* __restrict__ q, cons
   for (int k = threadIdx.x; k < QCH * D / 16; k += 256) dst[k] = src[k];
 }
 
-// Launch 1 of the preparation: the V tiles with the K partial sums (blocks
-// [0, nv) over (part, kv head, sequence)) and, independent of them, the Q rows
-// (blocks [nv, nv + nq) over (row chunk, query head, sequence)) in one grid, so the
-// two streaming passes overlap.
+// Launch 2: blocks [0, nk) quantize K, blocks [nk, 2 nk) prepare V (both over (part,
+// kv head, sequence)) and the remaining blocks prepare the Q rows (over (row chunk,
+// query head, sequence)).  The K workgroups come first: each reduces the partial sums
+// to the mean before it streams its rows, and the V and Q streams fill the machine
+// meanwhile.
 template <int D>
 union PrepShared {
+  PrepKShared<D> k;
   PrepVShared<D> v;
   __attribute__((aligned(16))) int8_t qfrag[QCH * D];
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void prep_vq_kernel(
+__global__ __launch_bounds__(256) void prep_kvq_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
     const _Float16* __restrict__ v, Act aq, Act akv, Seqs seqs, int Hq, int Hkv, int npart,
-    int tpw, int64_t Ppad, int64_t Qpad, int nqc, int64_t* __restrict__ kpart,
-    float* __restrict__ sv_ws, char* __restrict__ tiles, int8_t* __restrict__ q8,
-    float* __restrict__ qs, int nv) {
+    int tpw, int64_t Ppad, int64_t Qpad, int nqc, const int64_t* __restrict__ kpart,
+    float* __restrict__ kmean_ws, float* __restrict__ sv_ws, char* __restrict__ tiles,
+    int8_t* __restrict__ q8, float* __restrict__ qs, int nk) {
   __shared__ PrepShared<D> sh;
   int b = blockIdx.x;
-  if (b < nv) {
+  if (b < 2 * nk) {
+    const bool is_v = b >= nk;
+    if (is_v) b -= nk;
     const int c = b % npart;
     b /= npart;
-    prep_v_body<D>(k, v, akv, seqs, Hkv, npart, tpw, Ppad, kpart, sv_ws, tiles, c, b % Hkv,
-                   b / Hkv, sh.v);
+    if (is_v)
+      prep_v_body<D>(v, akv, seqs, tpw, Ppad, sv_ws, tiles, c, b % Hkv, b / Hkv, sh.v);
+    else
+      prep_k_body<D>(k, akv, seqs, Hkv, npart, tpw, Ppad, kpart, kmean_ws, tiles, c, b % Hkv,
+                     b / Hkv, sh.k);
   } else {
-    b -= nv;
+    b -= 2 * nk;
     const int c = b % nqc;
     b /= nqc;
     prep_q_body<D>(q, aq, seqs, Qpad, q8, qs, c, b % Hq, b / Hq, sh.qfrag);
@@ -391,33 +441,30 @@ static Act act_of(const FwdGeom& g, int H) {
   return a;
 }
 
-// Launches of the preparation.  With q (PH_Q) the Q rows ride in launch 1; with k/v
-// (PH_KV) launch 1 also prepares V and the K sums and launch 2 quantizes K.
+// Launches of the preparation.  With k/v (PH_KV): launch 1 sums K, launch 2 quantizes
+// K and prepares V; with q (PH_Q) the Q rows ride in launch 2.
 template <int D>
 static hipError_t prep_d(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, bool qq,
                          hipStream_t stream) {
   char* w = static_cast<char*>(ws);
-  const Act akv = act_of(g, g.Hkv);
+  const Act akv = act_of(g, g.Hkv), aq = act_of(g, g.Hq);
   Seqs sq{g.cu, g.S, g.max_len, g.T};
-  const int64_t nv = kv ? (int64_t)p.npart * g.Hkv * g.nseq : 0;
+  const int64_t nk = kv ? (int64_t)p.npart * g.Hkv * g.nseq : 0;
   const int nqc = (g.max_len + BQ - 1) / BQ * (BQ / QCH);
   const int64_t nq = qq ? (int64_t)nqc * g.Hq * g.nseq : 0;
-  if (nv + nq > 0x7fffffff) return hipErrorInvalidValue;
-  if (nv + nq > 0)
-    prep_vq_kernel<D><<<dim3((unsigned)(nv + nq)), 256, 0, stream>>>(
-        static_cast<const _Float16*>(g.q), static_cast<const _Float16*>(g.k),
-        static_cast<const _Float16*>(g.v), act_of(g, g.Hq), akv, sq, g.Hq, g.Hkv, p.npart,
-        p.tpw, p.Ppad, p.Qpad, nqc, reinterpret_cast<int64_t*>(w + p.off_kpart),
-        reinterpret_cast<float*>(w + p.off_sv), w + p.off_tiles,
-        reinterpret_cast<int8_t*>(w + p.off_q8), reinterpret_cast<float*>(w + p.off_qs),
-        (int)nv);
-  if (kv) {
-    const dim3 grid(p.npart, g.Hkv, g.nseq);
-    prep_k_kernel<D><<<grid, 256, 0, stream>>>(
-        static_cast<const _Float16*>(g.k), akv, sq, g.Hkv, p.npart, p.tpw, p.Ppad,
+  if (2 * nk + nq > 0x7fffffff) return hipErrorInvalidValue;
+  const _Float16* kp = static_cast<const _Float16*>(g.k);
+  if (kv)
+    prep_ksum_kernel<D><<<dim3((unsigned)nk), 256, 0, stream>>>(
+        kp, akv, sq, g.Hkv, p.npart, p.tpw, reinterpret_cast<int64_t*>(w + p.off_kpart));
+  if (2 * nk + nq > 0)
+    prep_kvq_kernel<D><<<dim3((unsigned)(2 * nk + nq)), 256, 0, stream>>>(
+        static_cast<const _Float16*>(g.q), kp, static_cast<const _Float16*>(g.v), aq, akv, sq,
+        g.Hq, g.Hkv, p.npart, p.tpw, p.Ppad, p.Qpad, nqc,
         reinterpret_cast<const int64_t*>(w + p.off_kpart),
-        reinterpret_cast<float*>(w + p.off_kmean), w + p.off_tiles);
-  }
+        reinterpret_cast<float*>(w + p.off_kmean), reinterpret_cast<float*>(w + p.off_sv),
+        w + p.off_tiles, reinterpret_cast<int8_t*>(w + p.off_q8),
+        reinterpret_cast<float*>(w + p.off_qs), (int)nk);
   return hipGetLastError();
 }
 
