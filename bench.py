@@ -12,7 +12,11 @@ step, with ops = 4*D*Hq*S^2/2 (two products of 2*D ops per (query, key) pair,
 S^2/2 causal pairs per head, the usual FlashAttention count).  ``roofline``
 describes the attention kernel alone (timed with HIP events on the stream it runs
 on) against the 5.0 POPS dense int8 MFMA peak.  ``cpu_baseline`` times the CPU
-oracle on a bounded sample of the same workload.
+oracle on a bounded sample of the same workload.  Also reported: the share of the
+mixed int8/fp16 MFMA ceiling, per-call median and min (as is, and after writing a
+512 MiB buffer that evicts the caches), the preparation kernels' GB/s, and on sampled
+rows the fp16 rounding floor of the oracle's output and the SQNR of the output
+against unquantized fp64 attention.
 
 Only one GPU is used: ``--gpus`` above 1 exits with a message.
 """
@@ -30,6 +34,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POPS
+FP16_PEAK_TOPS = 2500.0  # MI355X dense fp16 MFMA, 2.5 PFLOP/s
+# Half of the ops run on each engine (int8 Q.K^T, fp16 P.V): the mixed ceiling.
+MIXED_PEAK_TOPS = 1.0 / (0.5 / INT8_PEAK_TOPS + 0.5 / FP16_PEAK_TOPS)
 WORKLOAD = dict(B=1, Hq=32, Hkv=8, S=4096, D=128, causal=True)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_cfg2_traffic.json")
 
@@ -52,6 +59,17 @@ def measured_traffic():
         return rec["bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
     except (OSError, KeyError, ValueError):
         return None
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(w, budget_s: float):
@@ -83,7 +101,8 @@ def cpu_baseline(w, budget_s: float):
             "kind": "oracle",
             "sample": f"{heads} of {Hq} query heads (all {S} rows each) plus the quantization "
                       f"of the whole input, {dt:.1f} s; numpy fp64 BLAS with {blas_threads} "
-                      f"threads, the rest single-threaded; host has {os.cpu_count()} CPUs"}
+                      f"threads, the rest single-threaded; host has {os.cpu_count()} CPUs "
+                      f"({cpu_model()})"}
 
 
 def main():
@@ -94,6 +113,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of CPU oracle work for the cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calls", type=int, default=100,
+                    help="individually timed calls for the median/min, with and without a "
+                         "512 MiB cache flush before each")
     ap.add_argument("--profile-attn", type=int, default=0, metavar="N",
                     help="profiling mode: prepare Q, K and V once, launch only the attention "
                          "kernel N times, print nothing else")
@@ -180,16 +202,49 @@ def main():
     log(f"bench: attention kernel {ms_attn * 1e3:.1f} us, K/V preparation {ms_prep_kv * 1e3:.1f} us, "
         f"Q preparation {ms_prep_q * 1e3:.1f} us")
 
-    # quick parity guard on the benchmarked output (sampled rows of two heads)
+    # Per-call times (each call between its own pair of events): median and min, as they
+    # stand and with a 512 MiB buffer written before each call, which evicts the inputs
+    # and the workspace from the L2s and the 256 MB last-level cache.
+    def per_call(flush):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.calls)]
+        for a, b in evs:
+            if flush is not None:
+                flush.fill_(1)
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        return {"median": round(t[len(t) // 2], 2), "min": round(t[0], 2), "n": len(t)}
+
+    call_us = per_call(None)
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flushed_call_us = per_call(flush_buf)
+    del flush_buf
+    log(f"bench: per call {call_us}, after a cache flush {flushed_call_us}")
+
+    # Parity guard on the benchmarked output (sampled rows of two heads), the fp16
+    # rounding floor of the oracle's output there, and the quantization's SQNR against
+    # unquantized fp64 attention on the same rows (quality, not a gate).
     import oracle
     i8.attn_int8_fwd(q, k, v, True, out=out, workspace=ws)
     rows = np.array([0, 1, 127, 128, 2047, 4095])
-    ref = oracle.attn_int8_fwd(w.q, w.k, w.v, True, heads=[(0, 0), (0, 31)], rows=rows)
-    got = out[0, [0, 31]][:, rows].float().cpu().numpy()
+    heads = [(0, 0), (0, 31)]
+    ref = oracle.attn_int8_fwd(w.q, w.k, w.v, True, heads=heads, rows=rows)
+    got = out[0, [h for _, h in heads]][:, rows].float().cpu().numpy()
     max_abs = float(np.abs(got - ref).max())
     if not max_abs <= 2e-3:
         raise RuntimeError(f"benchmarked output differs from the oracle: max_abs={max_abs}")
+    floor = float(np.abs(ref.astype(np.float16).astype(np.float64) - ref).max())
+    exact = oracle.attn_exact(w.q, w.k, w.v, True, heads=heads, rows=rows)
+    sqnr_db = float(10.0 * np.log10(np.sum(exact ** 2) / np.sum((got - exact) ** 2)))
 
+    # Algorithmic bytes of the preparations: fp16 K and V read once, the K/V tile blocks
+    # (int8 K, exact fp16 V, fp32 K scales) written; fp16 Q read once, int8 Q codes and
+    # fp32 row scales written.
+    prep_kv_bytes = 2 * B * Hkv * S * D * 2 + B * Hkv * S * (D + 2 * D + 4)
+    prep_q_bytes = B * Hq * S * D * 2 + B * Hq * S * (D + 4)
     value = ops / (ms_step * 1e-3) / 1e12
     achieved = ops / (ms_attn * 1e-3) / 1e12
     traffic = measured_traffic()
@@ -210,10 +265,17 @@ def main():
                    "B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "D": D, "causal": True,
                    "algorithmic_ops": ops},
         "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
+        "pct_mixed_ceiling": round(100.0 * value / MIXED_PEAK_TOPS, 2),
+        "call_us": call_us,
+        "flushed_call_us": flushed_call_us,
         "attn_kernel_us": round(ms_attn * 1e3, 2),
         "prep_kv_us": round(ms_prep_kv * 1e3, 2),
+        "prep_kv_gbs": round(prep_kv_bytes / (ms_prep_kv * 1e-3) / 1e9, 1),
         "prep_q_us": round(ms_prep_q * 1e3, 2),
+        "prep_q_gbs": round(prep_q_bytes / (ms_prep_q * 1e-3) / 1e9, 1),
         "parity_sample_max_abs": max_abs,
+        "parity_sample_fp16_floor": floor,
+        "sqnr_db_vs_exact": round(sqnr_db, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4),
                      "traffic": traffic},

@@ -209,10 +209,12 @@ def attn_int8_varlen_fwd(q16, k16, v16, cu_seqlens, causal=True, softmax_scale=N
     return out
 
 
-def attn_exact(q, k, v, causal=True, softmax_scale=None):
+def attn_exact(q, k, v, causal=True, softmax_scale=None, heads=None, rows=None):
     """Unquantized attention in fp64 (reference for the quantization bound).
 
-    ``q[B,Hq,S,D]``, ``k/v[B,Hkv,S,D]`` of any float dtype.
+    ``q[B,Hq,S,D]``, ``k/v[B,Hkv,S,D]`` of any float dtype.  ``heads`` (list of (b, h))
+    and ``rows`` restrict the output to a sample of shape ``[len(heads), len(rows), D]``,
+    as in :func:`attn_int8_fwd`; otherwise it is ``[B, Hq, S, D]``.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -220,13 +222,16 @@ def attn_exact(q, k, v, causal=True, softmax_scale=None):
     B, Hq, S, D = q.shape
     G = Hq // k.shape[1]
     sm = np.float64(default_softmax_scale(D) if softmax_scale is None else np.float32(softmax_scale))
-    out = np.empty_like(q)
-    for b in range(B):
-        for h in range(Hq):
-            lg = (q[b, h] @ k[b, h // G].T) * sm
-            if causal:
-                lg = np.where(np.tril(np.ones((S, k.shape[2]), dtype=bool)), lg, -np.inf)
-            p = np.exp(lg - lg.max(axis=1, keepdims=True))
-            p /= p.sum(axis=1, keepdims=True)
-            out[b, h] = p @ v[b, h // G]
+    sel = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
+    rr = np.arange(S) if rows is None else np.asarray(rows)
+    out = np.empty((len(sel), rr.size, D))
+    for n, (b, h) in enumerate(sel):
+        lg = (q[b, h][rr] @ k[b, h // G].T) * sm
+        if causal:
+            lg = np.where(np.arange(k.shape[2])[None, :] <= rr[:, None], lg, -np.inf)
+        p = np.exp(lg - lg.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        out[n] = p @ v[b, h // G]
+    if heads is None and rows is None:
+        out = out.reshape(B, Hq, S, D)
     return out

@@ -229,6 +229,17 @@ def test_exact_attention_equals_library():
     np.testing.assert_allclose(oracle.attn_exact(w.q, w.k, w.v, True), ref, rtol=1e-11, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_exact_attention_sampled_rows_equal_library(causal):
+    w = workloads.dense(24, 2, 4, 2, 40, 32, causal)
+    ref = sdpa64(w.q, np.repeat(w.k, 2, 1), np.repeat(w.v, 2, 1), causal,
+                 oracle.default_softmax_scale(32))
+    heads, rows = [(1, 3), (0, 0)], np.array([0, 7, 39])
+    got = oracle.attn_exact(w.q, w.k, w.v, causal, heads=heads, rows=rows)
+    want = np.stack([ref[b, h][rows] for b, h in heads])
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-12)
+
+
 def test_k_smoothing_exact_invariance_unquantized():
     w = workloads.dense(23, 1, 2, 1, 50, 32, True, k_offset=3.0)
     k = w.k.astype(np.float64)
