@@ -12,6 +12,8 @@ The method it defines comes from the "SuperL8" README (the page titled
   forward, causal, GQA/MQA, head dims 32/64/128/256.
 * *Attention kernels* table, row ``attn_varlen_fwd``: variable-length
   (ragged, non-tile-multiple) prefill.
+* *Attention kernels* table, row ``attn_decode``: split-KV decode with an int8
+  KV cache (its fp16-V variant: one query token per sequence).
 * *Supporting kernels* table, row ``quant_rowwise``: symmetric per-row int8
   quantization.
 * *Quantization* table, rows "Per-row int8" (symmetric, K-smoothing) and
@@ -38,6 +40,7 @@ from .attn_ref import (  # noqa: F401
     qk_int32,
     attn_core,
     attn_int8_fwd,
+    attn_int8_decode,
     attn_int8_varlen_fwd,
     attn_exact,
 )

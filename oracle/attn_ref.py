@@ -40,6 +40,13 @@ R10 Output ``O = softmax(logits) @ (sv * v8)``, exact softmax over the whole
     row, in fp64 and left unrounded (a GPU result is compared against it).
 R11 Varlen input is packed ``[T, H, D]`` with ``cu_seqlens[nseq + 1]``; every
     sequence is an independent causal (or full) attention with its own K mean.
+R12 Decode (the *Attention kernels* table's ``attn_decode`` row: split-KV decode
+    with an int8 KV cache, here its fp16-V variant): one new query token per
+    sequence attends every token of that sequence's cache.  The cache is K and V
+    of ``S`` tokens quantized as in the forward (K-smoothing mean over the cached
+    tokens, R5; V per token, R2); the query row is quantized like Q (R6).  The
+    split over the keys is an implementation choice and does not change what is
+    computed.
 
 Quantization steps are emulated op for op in numpy float32, which is IEEE
 single precision with round-to-nearest-even; everything after the integer
@@ -206,6 +213,28 @@ def attn_int8_varlen_fwd(q16, k16, v16, cu_seqlens, causal=True, softmax_scale=N
         vs = np.ascontiguousarray(v16[a:b].transpose(1, 0, 2))[None]
         o = attn_int8_fwd(qs, ks, vs, causal, softmax_scale)[0]
         out[a:b] = o.transpose(1, 0, 2)
+    return out
+
+
+def attn_int8_decode(q16, k16, v16, softmax_scale=None):
+    """Decode (R12): fp16 ``q[B,Hq,D]`` (one token per sequence) against the cache
+    fp16 ``k/v[B,Hkv,S,D]`` -> fp64 ``[B, Hq, D]``."""
+    B, Hq, D = q16.shape
+    Hkv = k16.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    sm = default_softmax_scale(D) if softmax_scale is None else np.float32(softmax_scale)
+    q8, sq = quant_rows(q16.astype(np.float32))  # [B, Hq, D], [B, Hq]
+    m = kmean(k16)
+    k8, sk = quant_rows(k16.astype(np.float32) - m[..., None, :])
+    v8, sv = quant_rows(v16.astype(np.float32), V_SCALE_BITS)
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            out[b, h] = attn_core(q8[b, h][None], sq[b, h][None], k8[b, g], sk[b, g],
+                                  v8[b, g], sv[b, g], sm, False)[0]
     return out
 
 

@@ -384,3 +384,51 @@ def test_quantized_forward_within_a_posteriori_bound(causal):
                 bound = (np.abs(dv[b, g, :jmax]).max(axis=0)
                          + np.expm1(2 * eps) * np.abs(v[b, g, :jmax]).max(axis=0))
                 assert np.all(np.abs(o[b, h, i] - ex[b, h, i]) <= bound + 1e-12), (b, h, i)
+
+
+# ---------------------------------------------------------------- decode (R12)
+
+@pytest.mark.parametrize("Hq,Hkv,S,D", [(4, 2, 37, 32), (2, 1, 64, 64), (8, 8, 20, 128), (32, 1, 9, 256)])
+def test_decode_equals_library_attention_on_dequantized(Hq, Hkv, S, D):
+    w = workloads.dense(40 + D, 2, Hq, Hkv, S, D, False, k_offset=2.0)
+    q1 = w.q[:, :, 0]  # one new query token per sequence
+    out = oracle.attn_int8_decode(q1, w.k, w.v)
+    q8, sq = oracle.quant_rows(q1.astype(np.float32))
+    z = oracle.quantize_qkv(w.q, w.k, w.v)
+    G = Hq // Hkv
+    qh = dequant(q8, sq)[:, :, None]
+    kh = np.repeat(dequant(z["k8"], z["sk"]), G, axis=1)
+    vh = np.repeat(dequant(z["v8"], z["sv"]), G, axis=1)
+    ref = sdpa64(qh, kh, vh, False, oracle.default_softmax_scale(D))[:, :, 0]
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_decode_equals_noncausal_forward_row():
+    # The query row placed at any position of a full query block gives the same row
+    # of the non-causal forward: rows are quantized and attended independently (equal
+    # up to the fp64 summation order of a one-row against a block matrix product).
+    w = workloads.dense(41, 2, 4, 2, 50, 64, False)
+    r = 17
+    out = oracle.attn_int8_decode(w.q[:, :, r], w.k, w.v)
+    fwd = oracle.attn_int8_fwd(w.q, w.k, w.v, False)[:, :, r]
+    np.testing.assert_allclose(out, fwd, rtol=1e-12, atol=1e-14)
+
+
+def test_decode_zero_query_gives_mean_value():
+    g = rng(42)
+    B, Hkv, S, D = 1, 2, 33, 32
+    q = np.zeros((B, 4, D), np.float16)
+    k = g.standard_normal((B, Hkv, S, D)).astype(np.float16)
+    v = g.standard_normal((B, Hkv, S, D)).astype(np.float16)
+    out = oracle.attn_int8_decode(q, k, v)
+    v8, sv = oracle.quant_rows(v.astype(np.float32), oracle.V_SCALE_BITS)
+    want = dequant(v8, sv).mean(axis=2)  # [B, Hkv, D]
+    np.testing.assert_allclose(out, np.repeat(want, 2, axis=1), rtol=1e-12, atol=1e-14)
+
+
+def test_decode_gqa_equals_repeated_heads():
+    w = workloads.dense(43, 1, 8, 2, 40, 64, False, k_offset=1.0)
+    q1 = w.q[:, :, 3]
+    a = oracle.attn_int8_decode(q1, w.k, w.v)
+    b = oracle.attn_int8_decode(q1, np.repeat(w.k, 4, axis=1), np.repeat(w.v, 4, axis=1))
+    assert np.array_equal(a, b)
