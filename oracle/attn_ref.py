@@ -41,12 +41,13 @@ R10 Output ``O = softmax(logits) @ (sv * v8)``, exact softmax over the whole
 R11 Varlen input is packed ``[T, H, D]`` with ``cu_seqlens[nseq + 1]``; every
     sequence is an independent causal (or full) attention with its own K mean.
 R12 Decode (the *Attention kernels* table's ``attn_decode`` row: split-KV decode
-    with an int8 KV cache, here its fp16-V variant): one new query token per
-    sequence attends every token of that sequence's cache.  The cache is K and V
-    of ``S`` tokens quantized as in the forward (K-smoothing mean over the cached
-    tokens, R5; V per token, R2); the query row is quantized like Q (R6).  The
-    split over the keys is an implementation choice and does not change what is
-    computed.
+    with an int8 KV cache, in its int8-V and fp16-V variants): one new query token
+    per sequence attends every token of that sequence's cache.  K is cached as in
+    the forward (K-smoothing mean over the cached tokens, R5, then per-row int8).
+    V is cached per token as in the forward (R2) in the int8-V variant, and as the
+    fp16 values themselves in the fp16-V variant.  The query row is quantized like
+    Q (R6).  The split over the keys is an implementation choice and does not
+    change what is computed.
 
 Quantization steps are emulated op for op in numpy float32, which is IEEE
 single precision with round-to-nearest-even; everything after the integer
@@ -216,19 +217,27 @@ def attn_int8_varlen_fwd(q16, k16, v16, cu_seqlens, causal=True, softmax_scale=N
     return out
 
 
-def attn_int8_decode(q16, k16, v16, softmax_scale=None):
+def attn_int8_decode(q16, k16, v16, softmax_scale=None, v_format="int8"):
     """Decode (R12): fp16 ``q[B,Hq,D]`` (one token per sequence) against the cache
-    fp16 ``k/v[B,Hkv,S,D]`` -> fp64 ``[B, Hq, D]``."""
+    built from fp16 ``k/v[B,Hkv,S,D]`` -> fp64 ``[B, Hq, D]``.
+
+    ``v_format`` is ``"int8"`` (V quantized per token) or ``"fp16"`` (V as given).
+    """
     B, Hq, D = q16.shape
-    Hkv = k16.shape[1]
+    Hkv, S = k16.shape[1], k16.shape[2]
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
+    if v_format not in ("int8", "fp16"):
+        raise ValueError("v_format must be 'int8' or 'fp16'")
     G = Hq // Hkv
     sm = default_softmax_scale(D) if softmax_scale is None else np.float32(softmax_scale)
     q8, sq = quant_rows(q16.astype(np.float32))  # [B, Hq, D], [B, Hq]
     m = kmean(k16)
     k8, sk = quant_rows(k16.astype(np.float32) - m[..., None, :])
-    v8, sv = quant_rows(v16.astype(np.float32), V_SCALE_BITS)
+    if v_format == "int8":
+        v8, sv = quant_rows(v16.astype(np.float32), V_SCALE_BITS)
+    else:  # the fp16 values are the dequantized V: unit scales, fp64 "codes"
+        v8, sv = v16.astype(np.float64), np.ones((B, Hkv, S), dtype=np.float32)
     out = np.empty((B, Hq, D), dtype=np.float64)
     for b in range(B):
         for h in range(Hq):

@@ -432,3 +432,26 @@ def test_decode_gqa_equals_repeated_heads():
     a = oracle.attn_int8_decode(q1, w.k, w.v)
     b = oracle.attn_int8_decode(q1, np.repeat(w.k, 4, axis=1), np.repeat(w.v, 4, axis=1))
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("D", [32, 128])
+def test_decode_fp16_v_equals_library_attention(D):
+    # fp16-V cache: the values are used as given, K as in the int8-V cache.
+    w = workloads.dense(44 + D, 2, 6, 3, 29, D, False, k_offset=-1.5)
+    q1 = w.q[:, :, 5]
+    out = oracle.attn_int8_decode(q1, w.k, w.v, v_format="fp16")
+    q8, sq = oracle.quant_rows(q1.astype(np.float32))
+    z = oracle.quantize_qkv(w.q, w.k, w.v)
+    kh = np.repeat(dequant(z["k8"], z["sk"]), 2, axis=1)
+    vh = np.repeat(w.v.astype(np.float64), 2, axis=1)
+    ref = sdpa64(dequant(q8, sq)[:, :, None], kh, vh, False, oracle.default_softmax_scale(D))
+    np.testing.assert_allclose(out, ref[:, :, 0], rtol=1e-11, atol=1e-12)
+
+
+def test_decode_fp16_v_zero_query_gives_exact_mean():
+    g = rng(45)
+    k = g.standard_normal((2, 1, 21, 64)).astype(np.float16)
+    v = g.standard_normal((2, 1, 21, 64)).astype(np.float16)
+    out = oracle.attn_int8_decode(np.zeros((2, 3, 64), np.float16), k, v, v_format="fp16")
+    want = v.astype(np.float64).mean(axis=2)
+    np.testing.assert_allclose(out, np.repeat(want, 3, axis=1), rtol=1e-13, atol=1e-15)
