@@ -181,6 +181,65 @@ i8a_status attn_int8_debug_qk(const void* q, const void* k, const void* v, int32
                               float* vscale_out, float* kmean_out, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/*
+ * Decode over an int8 KV cache (SuperL8 README, Attention kernels table, row
+ * attn_decode: split-KV decode with an int8 KV cache, fp16-V and int8-V variants).
+ *
+ * attn_int8_kvcache_fill builds the cache of S tokens from fp16 K and V the way the
+ * forward quantizes them: K minus its per-channel mean over the S tokens, per-row
+ * int8; V per-token int8 with the 4-bit scale rule (I8A_VCACHE_INT8) or V kept in fp16
+ * as given (I8A_VCACHE_FP16).  attn_int8_decode then attends one new query token per
+ * (batch, query head) to all S cached tokens of its kv head, non-causally (every cached
+ * token precedes the new one), with the query row quantized like a Q row:
+ *   out[b,h,:] = softmax_j(q8 . k8_j * sq * sk_j * softmax_scale) . V_j
+ * with V_j = sv_j * v8_j (int8 V) or the fp16 v_j (fp16 V), and out in fp16.  The
+ * keys are split into chunks whose partial results are merged exactly (a rescaled
+ * sum), so the split does not change what is computed.
+ */
+#define I8A_VCACHE_INT8 1 /* V as per-token int8 codes and scales */
+#define I8A_VCACHE_FP16 2 /* V as the fp16 values */
+
+/*
+ * attn_int8_kvcache_bytes - bytes of a cache for these sizes (0 if they are invalid):
+ * 1 <= B <= 65535, 1 <= Hkv <= 65535, S >= 1, B*S <= 2^30, D in {32, 64, 128, 256},
+ * v_format I8A_VCACHE_INT8 or I8A_VCACHE_FP16.  The layout is private; the bulk is
+ * B*Hkv*ceil(S/32) tiles of 64*D + 192 bytes (int8 V) or 96*D + 128 bytes (fp16 V).
+ */
+size_t attn_int8_kvcache_bytes(int32_t B, int32_t Hkv, int32_t S, int32_t D, int32_t v_format);
+
+/*
+ * attn_int8_kvcache_fill - quantize dense fp16 k, v [B, Hkv, S, D] into `cache` (device,
+ * 256-byte aligned, at least attn_int8_kvcache_bytes(...) bytes, not aliasing k or v;
+ * it needs no initialization and is fully rewritten).  k and v are 16-byte aligned.
+ */
+i8a_status attn_int8_kvcache_fill(const void* k, const void* v, int32_t B, int32_t Hkv,
+                                  int32_t S, int32_t D, int32_t v_format, void* cache,
+                                  size_t cache_bytes, void* stream);
+
+/*
+ * attn_int8_decode_workspace_bytes - scratch bytes attn_int8_decode needs for the
+ * chunks' partial results (0 if the sizes are invalid or the call needs none).
+ */
+size_t attn_int8_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S,
+                                        int32_t D, int32_t v_format);
+
+/*
+ * attn_int8_decode - one decode step against a cache filled by attn_int8_kvcache_fill
+ * with the same B, Hkv, S, D and v_format.
+ *   q    fp16 [B, Hq, D]: the new token's query rows      out  fp16 [B, Hq, D]
+ *   1 <= Hkv <= Hq <= 65535, Hq % Hkv == 0 (query head h reads kv head h / (Hq/Hkv)).
+ *   softmax_scale  finite and > 0 (usually fp32(1/sqrt(D))).
+ *   cache, cache_bytes  the filled cache (read only).
+ *   workspace      device scratch of at least attn_int8_decode_workspace_bytes(...)
+ *                  bytes, 256-byte aligned (may be NULL when that size is 0); calls
+ *                  that run concurrently need distinct workspaces.
+ * q and out are 16-byte aligned; out aliases neither q, the cache nor the workspace.
+ */
+i8a_status attn_int8_decode(const void* q, void* out, int32_t B, int32_t Hq, int32_t Hkv,
+                            int32_t S, int32_t D, float softmax_scale, int32_t v_format,
+                            const void* cache, size_t cache_bytes, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Name of a status code (static string). */
 const char* i8a_status_string(i8a_status status);
 

@@ -11,6 +11,8 @@ Entry points (same names as the C ABI):
 * :func:`attn_int8_fwd` - dense forward, q ``[B,Hq,S,D]``, k/v ``[B,Hkv,S,D]``.
 * :func:`attn_int8_varlen_fwd` - packed ragged batch, q ``[T,Hq,D]`` + ``cu_seqlens``.
 * :func:`attn_int8_debug_qk` - the forward's exact int32 scores and scales.
+* :func:`attn_int8_kvcache_fill` / :func:`attn_int8_decode` - an int8 KV cache and
+  split-KV decode of one query token per sequence against it.
 """
 
 from __future__ import annotations
@@ -26,7 +28,9 @@ __all__ = [
     "quant_rowwise_i8", "attn_int8_fwd", "attn_int8_varlen_fwd", "attn_int8_debug_qk",
     "attn_int8_prepare_kv", "attn_int8_prepare_q", "attn_int8_attend", "attn_int8_fwd_prepared",
     "attn_int8_workspace_bytes", "attn_int8_varlen_workspace_bytes", "library_path",
-    "load_library", "SCALE_FP32", "SCALE_V4", "HEAD_DIMS",
+    "load_library", "SCALE_FP32", "SCALE_V4", "HEAD_DIMS", "attn_int8_kvcache_bytes",
+    "attn_int8_kvcache_fill", "attn_int8_decode_workspace_bytes", "attn_int8_decode",
+    "VCACHE_INT8", "VCACHE_FP16",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,6 +40,9 @@ _HEADER = os.path.join(os.path.dirname(_HERE), "include", "i8attn.h")
 SCALE_FP32 = 24
 SCALE_V4 = 4
 HEAD_DIMS = (32, 64, 128, 256)
+VCACHE_INT8 = 1
+VCACHE_FP16 = 2
+_VFORMATS = {"int8": VCACHE_INT8, "fp16": VCACHE_FP16}
 
 _c_i32, _c_i64, _c_sz, _c_f32, _c_vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
                                         ctypes.c_float, ctypes.c_void_p)
@@ -52,6 +59,11 @@ _SIGS = {
     "attn_int8_attend": (_c_i32, [_c_vp] + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_sz, _c_vp]),
     "attn_int8_fwd_prepared": (_c_i32, [_c_vp] * 2 + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_sz,
                                                                      _c_vp]),
+    "attn_int8_kvcache_bytes": (_c_sz, [_c_i32] * 5),
+    "attn_int8_kvcache_fill": (_c_i32, [_c_vp] * 2 + [_c_i32] * 5 + [_c_vp, _c_sz, _c_vp]),
+    "attn_int8_decode_workspace_bytes": (_c_sz, [_c_i32] * 6),
+    "attn_int8_decode": (_c_i32, [_c_vp] * 2 + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_sz,
+                                                               _c_vp, _c_sz, _c_vp]),
     "i8a_status_string": (ctypes.c_char_p, [_c_i32]),
     "i8a_last_error": (ctypes.c_char_p, []),
 }
@@ -338,3 +350,83 @@ def attn_int8_debug_qk(q, k, v, b, h, row0, rows, col0, cols, workspace=None):
                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _check(st, "attn_int8_debug_qk")
     return dict(s32=s32, qscale=qs, kscale=ks, vscale=vs, kmean=km)
+
+
+def _vformat(v_format):
+    if v_format not in _VFORMATS:
+        raise ValueError(f"v_format must be one of {sorted(_VFORMATS)}")
+    return _VFORMATS[v_format]
+
+
+def attn_int8_kvcache_bytes(B, Hkv, S, D, v_format="int8") -> int:
+    return int(load_library().attn_int8_kvcache_bytes(B, Hkv, S, D, _vformat(v_format)))
+
+
+def attn_int8_decode_workspace_bytes(B, Hq, Hkv, S, D, v_format="int8") -> int:
+    return int(load_library().attn_int8_decode_workspace_bytes(B, Hq, Hkv, S, D,
+                                                               _vformat(v_format)))
+
+
+class KVCache:
+    """A filled decode cache: the device buffer and the sizes it was built for."""
+
+    def __init__(self, buf, B, Hkv, S, D, v_format):
+        self.buf, self.B, self.Hkv, self.S, self.D, self.v_format = buf, B, Hkv, S, D, v_format
+
+    @property
+    def nbytes(self) -> int:
+        return self.buf.numel() * self.buf.element_size()
+
+
+def attn_int8_kvcache_fill(k, v, v_format="int8", cache=None):
+    """Quantize fp16 ``k, v [B,Hkv,S,D]`` into a decode cache (K with its K-smoothing
+    mean, per-row int8; V per-token int8 or kept in fp16).  Returns a :class:`KVCache`
+    (``cache``, a uint8 buffer of at least :func:`attn_int8_kvcache_bytes` bytes, is
+    reused when given)."""
+    for n, t in (("k", k), ("v", v)):
+        _need_gpu_fp16(n, t, 4)
+    if k.shape != v.shape or k.device != v.device:
+        raise ValueError("k and v must match")
+    B, Hkv, S, D = k.shape
+    vf = _vformat(v_format)
+    lib = load_library()
+    nbytes = lib.attn_int8_kvcache_bytes(B, Hkv, S, D, vf)
+    if nbytes == 0:
+        raise ValueError(f"invalid cache sizes B={B} Hkv={Hkv} S={S} D={D}")
+    buf = _workspace(cache, nbytes, k.device)
+    with torch.cuda.device(k.device):
+        st = lib.attn_int8_kvcache_fill(_ptr(k), _ptr(v), B, Hkv, S, D, vf, _ptr(buf),
+                                        buf.numel() * buf.element_size(), _stream(k.device))
+    _check(st, "attn_int8_kvcache_fill")
+    return KVCache(buf, B, Hkv, S, D, v_format)
+
+
+def attn_int8_decode(q, cache, softmax_scale=None, out=None, workspace=None):
+    """One decode step: fp16 ``q [B,Hq,D]`` (the new token's query rows) against a
+    :class:`KVCache`; returns fp16 ``out [B,Hq,D]``."""
+    _need_gpu_fp16("q", q, 3)
+    B, Hq, D = q.shape
+    if not isinstance(cache, KVCache):
+        raise ValueError("cache must come from attn_int8_kvcache_fill")
+    if B != cache.B or D != cache.D or cache.buf.device != q.device:
+        raise ValueError("q does not match the cache")
+    Hkv, S = cache.Hkv, cache.S
+    if Hq % Hkv:
+        raise ValueError(f"Hq={Hq} must be a multiple of Hkv={Hkv}")
+    vf = _vformat(cache.v_format)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_gpu_fp16("out", out, 3)
+        if out.shape != q.shape or out.device != q.device:
+            raise ValueError("out must match q")
+    lib = load_library()
+    nbytes = lib.attn_int8_decode_workspace_bytes(B, Hq, Hkv, S, D, vf)
+    ws = _workspace(workspace, nbytes, q.device) if nbytes else workspace
+    wsz = ws.numel() * ws.element_size() if ws is not None else 0
+    with torch.cuda.device(q.device):
+        st = lib.attn_int8_decode(_ptr(q), _ptr(out), B, Hq, Hkv, S, D, _scale(softmax_scale, D),
+                                  vf, _ptr(cache.buf), cache.nbytes, _ptr(ws), wsz,
+                                  _stream(q.device))
+    _check(st, "attn_int8_decode")
+    return out

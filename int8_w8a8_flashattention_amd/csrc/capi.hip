@@ -281,4 +281,85 @@ i8a_status attn_int8_debug_qk(const void* q, const void* k, const void* v, int32
   return I8A_OK;
 }
 
+static_assert(I8A_VCACHE_INT8 == VF_INT8 && I8A_VCACHE_FP16 == VF_FP16,
+              "the C ABI v_format codes are the kernels' VFormat values");
+
+static bool kvc_sizes_ok(int32_t B, int32_t Hkv, int32_t S, int32_t D, int32_t vf) {
+  return B >= 1 && B <= kMaxGridYZ && Hkv >= 1 && Hkv <= kMaxGridYZ && S >= 1 &&
+         (int64_t)B * S <= kMaxTokens && head_dim_ok(D) &&
+         (vf == I8A_VCACHE_INT8 || vf == I8A_VCACHE_FP16) &&
+         (int64_t)B * Hkv <= ((int64_t)1 << 24);
+}
+
+size_t attn_int8_kvcache_bytes(int32_t B, int32_t Hkv, int32_t S, int32_t D, int32_t v_format) {
+  if (!kvc_sizes_ok(B, Hkv, S, D, v_format)) return 0;
+  return plan_kvcache(B, Hkv, S, D, v_format).total;
+}
+
+static i8a_status kvc_check(int32_t B, int32_t Hkv, int32_t S, int32_t D, int32_t vf,
+                            const void* cache, size_t cache_bytes, size_t* need) {
+  if (!head_dim_ok(D))
+    return fail(I8A_ERR_UNSUPPORTED_HEAD_DIM, "head dim %d not in {32,64,128,256}", D);
+  if (vf != I8A_VCACHE_INT8 && vf != I8A_VCACHE_FP16)
+    return fail(I8A_ERR_INVALID_ARG, "v_format must be I8A_VCACHE_INT8 or I8A_VCACHE_FP16");
+  if (!kvc_sizes_ok(B, Hkv, S, D, vf))
+    return fail(I8A_ERR_INVALID_ARG, "need 1 <= B, Hkv <= %d, S >= 1, B*S <= 2^30 (B=%d Hkv=%d S=%d)",
+                kMaxGridYZ, B, Hkv, S);
+  if (!cache) return fail(I8A_ERR_INVALID_ARG, "null cache");
+  if (!aligned(cache, 256)) return fail(I8A_ERR_INVALID_ARG, "cache must be 256-byte aligned");
+  *need = plan_kvcache(B, Hkv, S, D, vf).total;
+  if (cache_bytes < *need)
+    return fail(I8A_ERR_WORKSPACE_TOO_SMALL, "cache needs %zu bytes, got %zu", *need, cache_bytes);
+  return I8A_OK;
+}
+
+i8a_status attn_int8_kvcache_fill(const void* k, const void* v, int32_t B, int32_t Hkv,
+                                  int32_t S, int32_t D, int32_t v_format, void* cache,
+                                  size_t cache_bytes, void* stream) {
+  if (!k || !v) return fail(I8A_ERR_INVALID_ARG, "null k/v pointer");
+  if (!aligned(k, 16) || !aligned(v, 16))
+    return fail(I8A_ERR_INVALID_ARG, "k/v must be 16-byte aligned");
+  size_t need;
+  i8a_status st = kvc_check(B, Hkv, S, D, v_format, cache, cache_bytes, &need);
+  if (st != I8A_OK) return st;
+  hipError_t e = launch_kvcache_fill(k, v, plan_kvcache(B, Hkv, S, D, v_format), cache,
+                                     (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "cache fill launch");
+  return I8A_OK;
+}
+
+size_t attn_int8_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S,
+                                        int32_t D, int32_t v_format) {
+  if (!kvc_sizes_ok(B, Hkv, S, D, v_format) || Hq < Hkv || Hq > kMaxGridYZ || Hq % Hkv)
+    return 0;
+  return plan_decode(B, Hq, Hkv, S, D, v_format).total;
+}
+
+i8a_status attn_int8_decode(const void* q, void* out, int32_t B, int32_t Hq, int32_t Hkv,
+                            int32_t S, int32_t D, float softmax_scale, int32_t v_format,
+                            const void* cache, size_t cache_bytes, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!q || !out) return fail(I8A_ERR_INVALID_ARG, "null q/out pointer");
+  if (!aligned(q, 16) || !aligned(out, 16))
+    return fail(I8A_ERR_INVALID_ARG, "q/out must be 16-byte aligned");
+  size_t need;
+  i8a_status st = kvc_check(B, Hkv, S, D, v_format, cache, cache_bytes, &need);
+  if (st != I8A_OK) return st;
+  if (Hq < Hkv || Hq > kMaxGridYZ || Hq % Hkv)
+    return fail(I8A_ERR_INVALID_ARG, "need Hkv <= Hq <= %d and Hq %% Hkv == 0 (Hq=%d Hkv=%d)",
+                kMaxGridYZ, Hq, Hkv);
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale))
+    return fail(I8A_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  const DecPlan dp = plan_decode(B, Hq, Hkv, S, D, v_format);
+  if (workspace_bytes < dp.total)
+    return fail(I8A_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", dp.total,
+                workspace_bytes);
+  if (dp.total > 0 && (!workspace || !aligned(workspace, 256)))
+    return fail(I8A_ERR_INVALID_ARG, "workspace must be non-null and 256-byte aligned");
+  hipError_t e = launch_decode(q, out, Hq, softmax_scale, plan_kvcache(B, Hkv, S, D, v_format),
+                               dp, cache, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return I8A_OK;
+}
+
 }  // extern "C"

@@ -66,6 +66,38 @@ struct Act {
 };
 
 // ---------------------------------------------------------------------------------
+// Direct-to-LDS copies.
+//
+// One 16-byte-per-lane load from global memory straight into LDS: lane l's 16 bytes at
+// gptr land at LDS byte lds_base + 16 l (lds_base is made wave-uniform; it goes to M0,
+// and one wait state separates the M0 write from the load).  It is issued through
+// inline assembly so that the compiler does not track it: the compiler's own
+// bookkeeping of direct-to-LDS loads makes every later LDS read wait until all of them
+// have landed, which would stall each tile's compute on the prefetch of the next one.
+// Callers wait for their copies themselves with vm_wait<N>.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
+}
+// M0 is a reserved register to the compiler; nothing else in these kernels uses it
+// (their code reads M0 only in these loads), so clobbering it here is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// Wait until at most N vector-memory loads of this wave are outstanding (they complete
+// in issue order).  The memory clobber keeps every LDS read of the copied data after it.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 0..63");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// ---------------------------------------------------------------------------------
 // Quantization steps (the row rule of the Quantization table's "Per-row int8" row).
 
 // Scale of a row with absolute maximum `amax`: fp32(amax / 127), and for V rows that
@@ -145,6 +177,40 @@ __device__ __forceinline__ int64_t fp16_fixed24(_Float16 v) {
   const uint32_t e = (u >> 10) & 31u, m = u & 1023u;
   const int64_t mag = e ? ((int64_t)(1024u | m) << (e - 1u)) : (int64_t)m;
   return (u & 0x8000u) ? -mag : mag;
+}
+
+// The K-smoothing mean of one (sequence, kv head) from its np exact partial sums
+// (int64, 2^-24 units; partial i of channel d at pp[i * D + d]): the integer total,
+// divided in fp64 by L * 2^24 and rounded to fp32, into mean[D] (LDS) and, if given,
+// kmean_out[D].  Every thread of the 256-thread workgroup must call it; red holds 256
+// int64.  The sums are integers, so every workgroup that reduces them gets the same
+// mean.
+template <int D>
+__device__ __forceinline__ void reduce_kmean(const int64_t* __restrict__ pp, int np, int L,
+                                             int64_t* red, float* mean,
+                                             float* __restrict__ kmean_out) {
+  constexpr int TPC = 256 / D;  // threads per channel
+  const int d = threadIdx.x % D, r = threadIdx.x / D;
+  pp += d;
+  int64_t t0 = 0, t1 = 0, t2 = 0, t3 = 0;
+  int i = r;
+  for (; i + 3 * TPC < np; i += 4 * TPC) {
+    t0 += pp[(int64_t)i * D];
+    t1 += pp[(int64_t)(i + TPC) * D];
+    t2 += pp[(int64_t)(i + 2 * TPC) * D];
+    t3 += pp[(int64_t)(i + 3 * TPC) * D];
+  }
+  for (; i < np; i += TPC) t0 += pp[(int64_t)i * D];
+  red[threadIdx.x] = (t0 + t1) + (t2 + t3);
+  __syncthreads();
+  if (r == 0) {
+    int64_t tot = 0;
+    for (int k2 = 0; k2 < TPC; ++k2) tot += red[k2 * D + d];
+    const float mu = (float)((double)tot / ((double)L * 16777216.0));
+    mean[d] = mu;
+    if (kmean_out) kmean_out[d] = mu;
+  }
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------------

@@ -74,4 +74,51 @@ hipError_t launch_debug_qk(const FwdGeom& g, const WsPlan& p, const void* ws, in
                            int32_t* s32, float* qscale, float* kscale, float* vscale,
                            float* kmean, hipStream_t stream);
 
+// ----------------------------------------------------------------------------------
+// Decode KV cache: per (batch, kv head), ceil(S / TKD) tiles of TKD tokens, each a
+// block of dtile_bytes(D, vf) bytes:
+//   K codes   TKD*D int8 in the K fragment order (one 32-key block)
+//   V         int8 format: TKD*D bytes, per (d block, lane) 16 bytes = the V fragments
+//             of key groups 0 and 1 as biased codes (code + 128);
+//             fp16 format: 2*TKD*D bytes, the fp16 V fragments of key groups 0 and 1
+//   sk        TKD fp32 K scales, key order
+//   sv        int8 format only: TKD fp16 V scales ordered [hv][key group][jv]
+constexpr int TKD = 32;
+enum VFormat { VF_INT8 = 1, VF_FP16 = 2 };
+__host__ __device__ constexpr int dtile_bytes(int D, int vf) {
+  return vf == VF_INT8 ? 2 * TKD * D + TKD * 4 + TKD * 2 : 3 * TKD * D + TKD * 4;
+}
+
+// Cache carve-up (256-byte aligned offsets):
+//   kpart int64 [B][Hkv][npart][D]   exact K channel sums of tpw TK-token tiles
+//   kmean fp32  [B][Hkv][D]          K-smoothing means
+//   tiles bytes [B][Hkv][ntd][dtile_bytes]
+struct KvcPlan {
+  int32_t B, Hkv, S, D, vf, ntd, tpw, npart;
+  size_t off_kpart, off_kmean, off_tiles, total;
+};
+KvcPlan plan_kvcache(int32_t B, int32_t Hkv, int32_t S, int32_t D, int32_t vf);
+
+// Split of a decode call: the ntd tiles of a (batch, kv head) in nchunk chunks of tpc
+// tiles; nqb blocks of up to 32 query heads per kv head.  Workspace (partials of the
+// chunks, when nchunk > 1): o fp32 [B*Hq][nchunk][D], then (m, l) fp32 [B*Hq][nchunk][2].
+struct DecPlan {
+  int32_t nqb, tpc, nchunk, nw;
+  size_t off_po, off_pml, total;
+};
+DecPlan plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D, int32_t vf);
+
+// Exact per-channel K sums of dense k [B, Hkv, S, D] (the forward's launch 1).
+hipError_t launch_ksum_dense(const void* k, int32_t B, int32_t Hkv, int32_t S, int32_t D,
+                             int32_t npart, int32_t tpw, int64_t* kpart, hipStream_t stream);
+
+// Fill of the decode cache from dense fp16 k, v [B, Hkv, S, D].
+hipError_t launch_kvcache_fill(const void* k, const void* v, const KvcPlan& p, void* cache,
+                               hipStream_t stream);
+
+// Decode of q [B, Hq, D] against a filled cache into out [B, Hq, D].
+hipError_t launch_decode(const void* q, void* out, int32_t Hq, float softmax_scale,
+                         const KvcPlan& p, const DecPlan& dp, const void* cache, void* ws,
+                         hipStream_t stream);
+
 }  // namespace i8a

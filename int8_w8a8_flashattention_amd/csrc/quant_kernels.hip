@@ -223,7 +223,6 @@ __device__ __forceinline__ void prep_k_body(const _Float16* __restrict__ k, cons
   constexpr int G = D / 8;
   constexpr int RPP = 256 / G;
   constexpr int NP = TK / RPP;
-  constexpr int TPC = 256 / D;  // threads per channel in the mean reduction
   int64_t* red = sh.red;
   float* mean = sh.mean;
   int64_t start;
@@ -248,30 +247,8 @@ __device__ __forceinline__ void prep_k_body(const _Float16* __restrict__ k, cons
   v8h kr[NP];
   load_rows(tile_lo * TK, kr);
 
-  {
-    const int d = threadIdx.x % D, r = threadIdx.x / D;
-    const int np = (nt + tpw - 1) / tpw;
-    const int64_t* pp = kpart + ((int64_t)s * Hkv + g) * npart * D + d;
-    int64_t t0 = 0, t1 = 0, t2 = 0, t3 = 0;
-    int i = r;
-    for (; i + 3 * TPC < np; i += 4 * TPC) {
-      t0 += pp[(int64_t)i * D];
-      t1 += pp[(int64_t)(i + TPC) * D];
-      t2 += pp[(int64_t)(i + 2 * TPC) * D];
-      t3 += pp[(int64_t)(i + 3 * TPC) * D];
-    }
-    for (; i < np; i += TPC) t0 += pp[(int64_t)i * D];
-    red[threadIdx.x] = (t0 + t1) + (t2 + t3);
-    __syncthreads();
-    if (r == 0) {
-      int64_t tot = 0;
-      for (int k2 = 0; k2 < TPC; ++k2) tot += red[k2 * D + d];
-      const float mu = (float)((double)tot / ((double)L * 16777216.0));
-      mean[d] = mu;
-      if (c == 0) kmean_ws[((int64_t)s * Hkv + g) * D + d] = mu;
-    }
-    __syncthreads();
-  }
+  reduce_kmean<D>(kpart + ((int64_t)s * Hkv + g) * npart * D, (nt + tpw - 1) / tpw, L, red, mean,
+                  c == 0 ? kmean_ws + ((int64_t)s * Hkv + g) * D : nullptr);
   float mu[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) mu[j] = mean[lc * 8 + j];
@@ -478,6 +455,31 @@ hipError_t launch_prep(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, boo
     case 256: return prep_d<256>(g, p, ws, kv, qq, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_ksum_dense(const void* k, int32_t B, int32_t Hkv, int32_t S, int32_t D,
+                             int32_t npart, int32_t tpw, int64_t* kpart, hipStream_t stream) {
+  Act a;
+  a.seq_unit = (int64_t)Hkv * D;
+  a.head_stride = (int64_t)S * D;
+  a.tok_stride = D;
+  Seqs sq{nullptr, S, S, (int64_t)B * S};
+  const int64_t nb = (int64_t)npart * Hkv * B;
+  if (nb == 0) return hipSuccess;
+  if (nb > 0x7fffffff) return hipErrorInvalidValue;
+  const _Float16* kp = static_cast<const _Float16*>(k);
+  switch (D) {
+#define I8A_KS(DD)                                                                      \
+  case DD:                                                                              \
+    prep_ksum_kernel<DD><<<dim3((unsigned)nb), 256, 0, stream>>>(kp, a, sq, Hkv, npart, \
+                                                                 tpw, kpart);           \
+    break;
+    I8A_KS(32) I8A_KS(64) I8A_KS(128) I8A_KS(256)
+#undef I8A_KS
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace i8a

@@ -42,6 +42,15 @@ class Varlen:
     meta: dict = field(default_factory=dict)
 
 
+@dataclass
+class Decode:
+    q: np.ndarray  # fp16 [B, Hq, D]: the new token's query rows
+    k: np.ndarray  # fp16 [B, Hkv, S, D]: the cached tokens
+    v: np.ndarray  # fp16 [B, Hkv, S, D]
+    name: str = ""
+    meta: dict = field(default_factory=dict)
+
+
 def _normal(rng, shape):
     return rng.standard_normal(shape, dtype=np.float32)
 
@@ -90,6 +99,22 @@ def varlen(seed, nseq, max_len, Hq, Hkv, D, causal, lengths=None, name=""):
                   {"lengths": lengths})
 
 
+def decode(seed, B, Hq, Hkv, S, D, k_offset=0.0, name=""):
+    """One decode step: the new token's query rows ``q [B, Hq, D]`` and the ``S``
+    cached tokens ``k, v [B, Hkv, S, D]`` (fp16, standard normal; ``k_offset`` as in
+    :func:`dense`)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _normal(rng, (B, Hq, D))
+    k = _normal(rng, (B, Hkv, S, D))
+    v = _normal(rng, (B, Hkv, S, D))
+    meta = {}
+    if k_offset > 0:
+        off = rng.uniform(-k_offset, k_offset, size=(Hkv, D)).astype(np.float32)
+        k += off[None, :, None, :]
+        meta["k_offset"] = off
+    return Decode(q.astype(np.float16), k.astype(np.float16), v.astype(np.float16), name, meta)
+
+
 # The five workloads the method is measured and checked on.
 
 def cfg1():
@@ -117,6 +142,12 @@ def cfg4():
 def cfg5():
     """Long-context causal GQA: B1 Hq40 Hkv8 S32768 D128, K offset U(-3,3)."""
     return dense(5, 1, 40, 8, 32768, 128, True, k_offset=3.0, name="cfg5_causal_gqa_s32768")
+
+
+def decode_bench():
+    """Batched decode at a GQA serving shape: 16 sequences with 8192 cached tokens each,
+    Hq32 Hkv8 D128, K offset U(-3,3)."""
+    return decode(6, 16, 32, 8, 8192, 128, k_offset=3.0, name="decode_b16_s8192_gqa_d128")
 
 
 def attn_ops(Hq, D, lengths, causal):
