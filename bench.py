@@ -18,6 +18,15 @@ mixed int8/fp16 MFMA ceiling, per-call median and min (as is, and after writing 
 rows the fp16 rounding floor of the oracle's output and the SQNR of the output
 against unquantized fp64 attention.
 
+The ``decode`` object measures the split-KV decode over an int8 KV cache on the batched
+serving shape B=16 sequences x S=8192 cached tokens, Hq=32, Hkv=8, D=128: one step is one
+``attn_int8_decode`` call (the decode kernel and the merge of its chunks) for one new
+token per sequence, with the cache filled beforehand, for both V formats.  Its
+roofline is HBM: algorithmic bytes per call (the cache's K codes, V codes or values
+and scales, the query rows read, the output written) over the call time, against
+8 TB/s.  Its ``cpu_baseline`` times the oracle's decode over a cache quantized
+beforehand, on a sample of sequences.
+
 Only one GPU is used: ``--gpus`` above 1 exits with a message.
 """
 
@@ -39,19 +48,21 @@ FP16_PEAK_TOPS = 2500.0  # MI355X dense fp16 MFMA, 2.5 PFLOP/s
 MIXED_PEAK_TOPS = 1.0 / (0.5 / INT8_PEAK_TOPS + 0.5 / FP16_PEAK_TOPS)
 WORKLOAD = dict(B=1, Hq=32, Hkv=8, S=4096, D=128, causal=True)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_cfg2_traffic.json")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b16_s8192_traffic.json")
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic():
-    """HBM bytes per attention launch from the stored FETCH_SIZE / WRITE_SIZE counter
-    runs (scaled by a plain copy's readings), or None when the kernel sources have
-    changed since the counters were taken."""
+def measured_traffic(path=TRAFFIC_FILE):
+    """HBM bytes per launch of the dominant kernel from the stored FETCH_SIZE /
+    WRITE_SIZE counter runs (scaled by a plain copy's readings), or None when the kernel
+    sources have changed since the counters were taken."""
     import hashlib
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(path))
         h = hashlib.sha256()
         for src in rec["sources"]:
             with open(os.path.join(ROOT, src), "rb") as f:
@@ -105,6 +116,134 @@ def cpu_baseline(w, budget_s: float):
                       f"({cpu_model()})"}
 
 
+def decode_bytes(B, Hq, Hkv, S, D, v_format):
+    """Algorithmic bytes of one decode call: per cached token and kv head the int8 K
+    codes and fp32 K scale, then the int8 V codes and their scale (stored as fp16) or
+    the fp16 V values; the fp16 query rows read and output rows written."""
+    per_tok = D + 4 + (D + 2 if v_format == "int8" else 2 * D)
+    return B * Hkv * S * per_tok + 2 * B * Hq * D * 2
+
+
+def decode_cpu_baseline(w, budget_s: float):
+    """The oracle's decode on whole sequences of the same workload (each cache quantized
+    beforehand, not timed) until the budget is spent; bytes of the cache attended per
+    second."""
+    import numpy as np
+
+    import oracle
+    B, Hq, D = w.q.shape
+    Hkv, S = w.k.shape[1], w.k.shape[2]
+    G = Hq // Hkv
+    sm = oracle.default_softmax_scale(D)
+    done, dt = 0, 0.0
+    for b in range(B):
+        q8, sq = oracle.quant_rows(w.q[b].astype(np.float32))
+        m = oracle.kmean(w.k[b:b + 1])[0]
+        k8, sk = oracle.quant_rows(w.k[b].astype(np.float32) - m[:, None, :])
+        v8, sv = oracle.quant_rows(w.v[b].astype(np.float32), oracle.V_SCALE_BITS)
+        t0 = time.perf_counter()
+        for h in range(Hq):
+            oracle.attn_core(q8[h][None], sq[h][None], k8[h // G], sk[h // G], v8[h // G],
+                             sv[h // G], sm, False)
+        dt += time.perf_counter() - t0
+        done += 1
+        if dt > budget_s:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    nbytes = decode_bytes(done, Hq, Hkv, S, D, "int8")
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"{done} of {B} sequences (all {Hq} query heads over {S} cached tokens), "
+                      f"int8 V, caches quantized beforehand (not timed); {dt:.1f} s of numpy "
+                      f"fp64, BLAS with {blas_threads} threads ({cpu_model()})"}
+
+
+def bench_decode(args, i8, torch, dev):
+    """The decode measurement (both V formats) on the batched serving shape."""
+    import numpy as np
+
+    import oracle
+    from int8_w8a8_flashattention_amd import workloads
+    w = workloads.decode_bench()
+    B, Hq, D = w.q.shape
+    Hkv, S = w.k.shape[1], w.k.shape[2]
+    q, k, v = (torch.from_numpy(a).to(dev) for a in (w.q, w.k, w.v))
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {"workload": f"{w.name}: decode of one token per sequence, B{B} Hq{Hq} Hkv{Hkv} "
+                       f"S{S} D{D}, fp16 N(0,1) with K channel offsets U(-3,3), seed 6",
+           "step": "one attn_int8_decode call (decode kernel + chunk merge), cache filled "
+                   "beforehand"}
+    for vf in ("int8", "fp16"):
+        cache = i8.attn_int8_kvcache_fill(k, v, vf)
+        ws = torch.empty(max(i8.attn_int8_decode_workspace_bytes(B, Hq, Hkv, S, D, vf), 1),
+                         dtype=torch.uint8, device=dev)
+
+        def call():
+            i8.attn_int8_decode(q, cache, out=out, workspace=ws)
+
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / args.steps * 1e3
+        nbytes = decode_bytes(B, Hq, Hkv, S, D, vf)
+        got = out.float().cpu().numpy()
+        err = 0.0
+        for b in (0, B - 1):
+            ref = oracle.attn_int8_decode(w.q[b:b + 1], w.k[b:b + 1], w.v[b:b + 1], v_format=vf)
+            err = max(err, float(np.abs(got[b:b + 1] - ref).max()))
+        if not err <= 2e-3:
+            raise RuntimeError(f"decode output differs from the oracle: max_abs={err}")
+        # cache fill (K sums, K and V quantization): fp16 K read twice, V once, cache written
+        for _ in range(5):
+            i8.attn_int8_kvcache_fill(k, v, vf, cache=cache.buf)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(10):
+            i8.attn_int8_kvcache_fill(k, v, vf, cache=cache.buf)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fill_us = e0.elapsed_time(e1) / 10 * 1e3
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[f"{vf}_v"] = {
+            "call_us": round(us, 2), "bytes_per_call": nbytes, "gbs": round(gbs, 1),
+            "parity_sample_max_abs": err, "fill_us": round(fill_us, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(DECODE_TRAFFIC_FILE) if vf == "int8"
+                         else None}}
+        log(f"bench: decode {vf} V {us:.1f} us/call, {gbs:.0f} GB/s, fill {fill_us:.1f} us")
+        del cache, ws
+    if not args.no_cpu_baseline:
+        log(f"bench: timing the CPU oracle's decode (~{args.cpu_budget / 2:.0f} s)")
+        res["cpu_baseline"] = decode_cpu_baseline(w, args.cpu_budget / 2)
+    return res
+
+
+def profile_decode(n, i8, torch, dev):
+    """Profiling mode: fill the int8-V cache once, then n decode calls."""
+    from int8_w8a8_flashattention_amd import workloads
+    w = workloads.decode_bench()
+    B, Hq, D = w.q.shape
+    q, k, v = (torch.from_numpy(a).to(dev) for a in (w.q, w.k, w.v))
+    cache = i8.attn_int8_kvcache_fill(k, v, "int8")
+    out = torch.empty_like(q)
+    for _ in range(n):
+        i8.attn_int8_decode(q, cache, out=out)
+    torch.cuda.synchronize()
+    log(f"bench: {n} decode calls")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +261,9 @@ def main():
     ap.add_argument("--profile-attn", type=int, default=0, metavar="N",
                     help="profiling mode: prepare Q, K and V once, launch only the attention "
                          "kernel N times, print nothing else")
+    ap.add_argument("--profile-decode", type=int, default=0, metavar="N",
+                    help="profiling mode: fill the decode cache once, then N decode calls")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--profile-copy", type=int, default=0, metavar="MIB",
                     help="profiling mode: 10 plain device copies of MIB MiB (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -142,6 +284,9 @@ def main():
         raise RuntimeError("bench.py needs a GPU")
     i8.load_library()
     dev = torch.device("cuda:0")
+    if args.profile_decode:
+        profile_decode(args.profile_decode, i8, torch, dev)
+        return
     w = workloads.cfg2()
     B, Hq, Hkv, S, D = (WORKLOAD[k] for k in ("B", "Hq", "Hkv", "S", "D"))
     assert w.q.shape == (B, Hq, S, D) and w.k.shape == (B, Hkv, S, D)
@@ -286,6 +431,9 @@ def main():
     if not args.no_cpu_baseline:
         log(f"bench: timing the CPU oracle (~{args.cpu_budget:.0f} s)")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    if not args.no_decode:
+        del q, k, v, out, ws
+        res["decode"] = bench_decode(args, i8, torch, dev)
     print(json.dumps(res), flush=True)
 
 

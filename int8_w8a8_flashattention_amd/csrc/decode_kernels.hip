@@ -34,7 +34,32 @@ namespace i8a {
 namespace {
 
 constexpr float DTAU = 8.0f;  // lazy-rescale threshold, log2 units (as in the forward)
-constexpr int DEC_NST = 2;    // LDS stages per wave
+
+// Launch shape, per V format: up to max_stages LDS stages per wave (max_stages - 1
+// tiles in flight while one is computed) and up to max_waves waves per workgroup,
+// within lds_budget bytes of LDS per workgroup.  Measured on the batched serving
+// shape: the int8 tiles want more waves (their dequantization is VALU work), the
+// larger fp16 tiles more copies in flight.
+constexpr int max_stages(int vf) { return vf == VF_INT8 ? 2 : 3; }
+constexpr int max_waves(int vf) { return vf == VF_INT8 ? 4 : 1; }
+constexpr int lds_budget(int vf) { return vf == VF_INT8 ? 72 * 1024 : 54 * 1024; }
+
+constexpr int dtile_rounds(int D, int vf) { return (dtile_bytes(D, vf) / 16 + 63) / 64; }
+// Stages per wave: the most, up to max_stages, whose copies in flight vmcnt can count
+// and whose ring for one wave fits the budget.
+constexpr int dec_stages(int D, int vf) {
+  int n = max_stages(vf);
+  while (n > 2 &&
+         ((n - 1) * dtile_rounds(D, vf) >= 64 || n * dtile_bytes(D, vf) > lds_budget(vf)))
+    --n;
+  return n;
+}
+// Waves per workgroup: as many as keep the workgroup's rings within the budget.
+constexpr int dec_waves(int D, int vf) {
+  int w = max_waves(vf);
+  while (w > 1 && w * dec_stages(D, vf) * dtile_bytes(D, vf) > lds_budget(vf)) w /= 2;
+  return w;
+}
 
 template <int D, int VF>
 struct DLay {
@@ -43,19 +68,14 @@ struct DLay {
   static constexpr int SKOFF = VOFF + (VF == VF_INT8 ? TKD * D : 2 * TKD * D);  // K scales
   static constexpr int SVOFF = SKOFF + TKD * 4;                                  // V scales
   static constexpr int BYTES = dtile_bytes(D, VF);
-  static constexpr int NCH = BYTES / 16;           // 16-byte chunks per tile
-  static constexpr int ROUNDS = (NCH + 63) / 64;   // one-wave copy instructions per tile
+  static constexpr int NCH = BYTES / 16;              // 16-byte chunks per tile
+  static constexpr int ROUNDS = dtile_rounds(D, VF);  // one-wave copy instructions per tile
+  static constexpr int NST = dec_stages(D, VF);
+  static constexpr int NW = dec_waves(D, VF);
   static_assert(BYTES % 16 == 0, "tiles are copied in 16-byte chunks");
-  static_assert((DEC_NST - 1) * ROUNDS < 64, "vmcnt holds at most 63 outstanding loads");
+  static_assert((NST - 1) * ROUNDS < 64, "vmcnt holds at most 63 outstanding loads");
+  static_assert(NW * NST * BYTES <= 160 * 1024, "the rings fit in LDS");
 };
-
-// Waves per decode workgroup: as many as keep the workgroup's rings within 72 KB, so
-// that two workgroups fit in a CU's LDS.
-constexpr int dec_waves(int D, int vf) {
-  return 4 * DEC_NST * dtile_bytes(D, vf) <= 72 * 1024   ? 4
-         : 2 * DEC_NST * dtile_bytes(D, vf) <= 72 * 1024 ? 2
-                                                         : 1;
-}
 
 __device__ __forceinline__ float smax(float a, float b) {
   return __builtin_elementwise_maximum(a, b);
@@ -83,6 +103,20 @@ __device__ __forceinline__ void copy_dtile(const char* __restrict__ src, char* d
   for (int r = 0; r < LY::ROUNDS; ++r) {
     const int chunk = r * 64 + lane;
     if (r + 1 < LY::ROUNDS || chunk < LY::NCH) lds_dma16(src + (int64_t)chunk * 16, base + r * 1024);
+  }
+}
+
+// Wait until at most `ahead` tile copies (R load instructions each) are outstanding,
+// ahead in [0, A]; vmcnt takes an immediate, hence the unrolled choice.
+template <int R, int A>
+__device__ __forceinline__ void wait_copies(int ahead) {
+  if constexpr (A == 0) {
+    vm_wait<0>();
+  } else {
+    if (ahead >= A)
+      vm_wait<A * R>();
+    else
+      wait_copies<R, A - 1>(ahead);
   }
 }
 
@@ -303,7 +337,7 @@ __global__ __launch_bounds__(64 * dec_waves(D, VF)) void decode_kernel(
     int Hq, int Hkv, int S, int ntd, int nqb, int tpc, int nchunk, float qk_log2,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
   using LY = DLay<D, VF>;
-  constexpr int NKB = LY::NKB, SB = LY::BYTES, NW = dec_waves(D, VF), NST = DEC_NST;
+  constexpr int NKB = LY::NKB, SB = LY::BYTES, NW = LY::NW, NST = LY::NST;
   constexpr int MROW = D + 1;               // merge row stride in floats (odd: no conflicts)
   constexpr int MWAVE = 32 * MROW + 64;     // per wave: 32 output rows, then 32 (m, l)
   constexpr int RING = NW * NST * SB;
@@ -464,12 +498,10 @@ __global__ __launch_bounds__(64 * dec_waves(D, VF)) void decode_kernel(
 
   for (int i = 0; i < nmine; ++i) {
     const int nx = i + NST - 1;
-    if (nx < nmine) {
+    if (nx < nmine)
       copy_dtile<D, VF>(tsrc + (int64_t)(t_lo + w + NW * nx) * SB, ring + (nx % NST) * SB, lane);
-      vm_wait<(NST - 1) * LY::ROUNDS>();  // tile i has landed, the later copies may not
-    } else {
-      vm_wait<0>();
-    }
+    // Tile i has landed once at most the copies issued after it are outstanding.
+    wait_copies<LY::ROUNDS, NST - 1>(min(NST - 1, nmine - 1 - i));
     step(ring + (i % NST) * SB, t_lo + w + NW * i);
   }
 
@@ -520,25 +552,52 @@ __global__ __launch_bounds__(64 * dec_waves(D, VF)) void decode_kernel(
   }
 }
 
-// Merge of the chunks' partials of one query row: out = sum_c 2^(m_c - M) o_c /
-// sum_c 2^(m_c - M) l_c.  Every chunk holds at least one key, so every m_c is finite.
+// Merge of the chunks' partials: out = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c
+// for each output element (one per thread).  Every chunk holds at least one key, so
+// every m_c is finite.  Up to MC chunks are loaded all at once (one memory latency);
+// more take further passes.
+constexpr int MC = 16;
+
 template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ part_o,
-                                                          const float* __restrict__ part_ml,
-                                                          int nchunk, _Float16* __restrict__ out) {
-  const int64_t row = blockIdx.x;
-  const float* ml = part_ml + row * nchunk * 2;
-  float M = -INFINITY;
-  for (int c = 0; c < nchunk; ++c) M = fmaxf(M, ml[2 * c]);
-  float den = 0.0f;
-  for (int c = 0; c < nchunk; ++c) den += __builtin_amdgcn_exp2f(ml[2 * c] - M) * ml[2 * c + 1];
-  const float inv = 1.0f / den;
-  for (int d = threadIdx.x; d < D; d += 64) {
-    float num = 0.0f;
-    for (int c = 0; c < nchunk; ++c)
-      num += __builtin_amdgcn_exp2f(ml[2 * c] - M) * part_o[(row * nchunk + c) * D + d];
-    out[row * D + d] = (_Float16)(num * inv);
+__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ part_o,
+                                                           const float2* __restrict__ part_ml,
+                                                           int nchunk, int64_t nel,
+                                                           _Float16* __restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= nel) return;
+  const int64_t row = e / D;
+  const int d = (int)(e % D);
+  const float2* ml = part_ml + row * nchunk;
+  const float* po = part_o + row * nchunk * D + d;
+  float M = -INFINITY, num = 0.0f, den = 0.0f;
+  for (int c0 = 0; c0 < nchunk; c0 += MC) {
+    float2 mv[MC];
+    float ov[MC];
+#pragma unroll
+    for (int c = 0; c < MC; ++c) {
+      if (c0 + c < nchunk) {
+        mv[c] = ml[c0 + c];
+        ov[c] = po[(int64_t)(c0 + c) * D];
+      } else {
+        mv[c] = make_float2(-INFINITY, 0.0f);
+        ov[c] = 0.0f;
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int c = 0; c < MC; ++c) Mn = fmaxf(Mn, mv[c].x);
+    const float a = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+    num *= a;
+    den *= a;
+#pragma unroll
+    for (int c = 0; c < MC; ++c) {
+      const float f = mv[c].x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv[c].x - Mn);
+      num += f * ov[c];
+      den += f * mv[c].y;
+    }
+    M = Mn;
   }
+  out[e] = (_Float16)(num / den);
 }
 
 // ----------------------------------------------------------------------------------
@@ -639,8 +698,9 @@ static hipError_t decode_d(const void* q, void* out, int Hq, float softmax_scale
       p.Hkv, p.S, p.ntd, dp.nqb, dp.tpc, dp.nchunk, qk_log2, po, pml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || dp.nchunk == 1) return e;
-  decode_merge_kernel<D><<<dim3((unsigned)((int64_t)p.B * Hq)), 64, 0, stream>>>(
-      po, pml, dp.nchunk, static_cast<_Float16*>(out));
+  const int64_t nel = (int64_t)p.B * Hq * D;
+  decode_merge_kernel<D><<<dim3((unsigned)((nel + 255) / 256)), 256, 0, stream>>>(
+      po, reinterpret_cast<const float2*>(pml), dp.nchunk, nel, static_cast<_Float16*>(out));
   return hipGetLastError();
 }
 
