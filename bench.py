@@ -181,7 +181,7 @@ def bench_decode(args, i8, torch, dev):
                    "beforehand"}
     for vf in ("int8", "fp16"):
         cache = i8.attn_int8_kvcache_fill(k, v, vf)
-        ws = torch.empty(max(i8.attn_int8_decode_workspace_bytes(B, Hq, Hkv, S, D, vf), 1),
+        ws = torch.zeros(max(i8.attn_int8_decode_workspace_bytes(B, Hq, Hkv, S, D, vf), 1),
                          dtype=torch.uint8, device=dev)
 
         def call():

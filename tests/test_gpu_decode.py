@@ -149,3 +149,20 @@ def test_decode_rejects_bad_arguments():
     assert call(args(scale=0.0)) == -1
     assert call(args(cache=cache.buf.data_ptr() + 16)) == -1
     torch.cuda.synchronize()
+
+
+def test_decode_workspace_reused_across_calls_and_shapes():
+    # The chunk merge keeps counters in the workspace: zeroed once, every call leaves
+    # them at zero for the next, whatever the shape that uses the workspace next.
+    say("one zeroed workspace, several multi-chunk calls and shapes")
+    shapes = [(1, 4, 2, 3000, 128), (2, 8, 2, 1500, 64), (1, 40, 1, 2500, 128)]
+    need = max(i8.attn_int8_decode_workspace_bytes(B, Hq, Hkv, S, D, "int8")
+               for B, Hq, Hkv, S, D in shapes)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for n, (B, Hq, Hkv, S, D) in enumerate(shapes):
+            w = workloads.decode(800 + n, B, Hq, Hkv, S, D, k_offset=1.5)
+            cache = i8.attn_int8_kvcache_fill(dev(w.k), dev(w.v), "int8")
+            out = host(i8.attn_int8_decode(dev(w.q), cache, workspace=ws))
+            check_close(out, oracle.attn_int8_decode(w.q, w.k, w.v), f"rep {rep} shape {n}")
