@@ -13,11 +13,13 @@ The method it defines comes from the "SuperL8" README (the page titled
 * *Attention kernels* table, row ``attn_varlen_fwd``: variable-length
   (ragged, non-tile-multiple) prefill.
 * *Attention kernels* table, row ``attn_decode``: split-KV decode with an int8
-  KV cache (its fp16-V variant: one query token per sequence).
+  KV cache, in its int8-V and fp16-V variants (one query token per sequence).
 * *Supporting kernels* table, row ``quant_rowwise``: symmetric per-row int8
   quantization.
 * *Quantization* table, rows "Per-row int8" (symmetric, K-smoothing) and
   "V per-channel / per-token" (V is quantized per token here).
+* *Quantization* table, row "Hadamard rotation": Q and K rows rotated before
+  quantization (the ``hadamard`` option of the forward).
 * *Quick start*: ``attn_int8_fwd(q, k, v, causal=True)`` takes fp16
   ``q[B,Hq,S,D]``, ``k/v[B,Hkv,S,D]`` and quantizes internally.
 
@@ -37,6 +39,7 @@ from .attn_ref import (  # noqa: F401
     kmean,
     quant_rows,
     quantize_qkv,
+    fwht_f32,
     qk_int32,
     attn_core,
     attn_int8_fwd,

@@ -49,6 +49,19 @@ R12 Decode (the *Attention kernels* table's ``attn_decode`` row: split-KV decode
     Q (R6).  The split over the keys is an implementation choice and does not
     change what is computed.
 
+R13 Hadamard rotation (the *Quantization* table's "Hadamard rotation" row: an
+    incoherence rotation for outlier-heavy activations).  The page gives no
+    formula; the plainest reading rotates Q and the mean-smoothed K by the
+    Sylvester-Hadamard matrix before their rows are quantized, so that an outlier
+    channel's energy spreads over all D channels.  Concretely, each fp32 row x
+    (``fp32(q)``, or ``fp32(k) - mean`` as in R5) becomes the unnormalized fast
+    Walsh-Hadamard transform ``x H`` computed in fp32 with the butterflies taken in
+    the fixed order of stages s = 0, 1, ..., log2(D)-1, each stage replacing the
+    pair (x[i], x[i + 2^s]) (bit s of i clear) by (x[i] + x[i + 2^s],
+    x[i] - x[i + 2^s]).  Since ``H H^T = D I``, the dequantized scores of the
+    rotated rows are D times the unrotated ones: the logits take an extra exact
+    factor 1/D.  V is not rotated.
+
 Quantization steps are emulated op for op in numpy float32, which is IEEE
 single precision with round-to-nearest-even; everything after the integer
 codes is exact or fp64.
@@ -117,16 +130,38 @@ def quant_rows(x32: np.ndarray, scale_bits: int = QK_SCALE_BITS):
     return codes, scale.astype(np.float32)
 
 
-def quantize_qkv(q16, k16, v16):
-    """Quantize dense BHSD q/k/v as the forward does internally.
+def fwht_f32(x32: np.ndarray) -> np.ndarray:
+    """Unnormalized fast Walsh-Hadamard transform of the last axis (R13), in fp32,
+    stages in the order s = 0, 1, ...: the pair (x[i], x[i + 2^s]) with bit s of i
+    clear becomes (x[i] + x[i + 2^s], x[i] - x[i + 2^s]).  Equals ``x @ H`` for the
+    Sylvester-Hadamard matrix H (symmetric, entries +-1) up to fp32 rounding."""
+    x = np.array(x32, dtype=np.float32, copy=True)
+    D = x.shape[-1]
+    if D & (D - 1):
+        raise ValueError("the row length must be a power of two")
+    h = 1
+    while h < D:
+        y = x.reshape(x.shape[:-1] + (D // (2 * h), 2, h))
+        a, b = y[..., 0, :].copy(), y[..., 1, :].copy()
+        y[..., 0, :] = a + b
+        y[..., 1, :] = a - b
+        x = y.reshape(x.shape)
+        h *= 2
+    return x
+
+
+def quantize_qkv(q16, k16, v16, hadamard=False):
+    """Quantize dense BHSD q/k/v as the forward does internally (with ``hadamard``,
+    Q and the mean-smoothed K rows rotated first, R13).
 
     Returns a dict with ``q8, sq, k8, sk, v8, sv, kmean``.
     """
-    q8, sq = quant_rows(q16.astype(np.float32))
+    q32 = q16.astype(np.float32)
+    q8, sq = quant_rows(fwht_f32(q32) if hadamard else q32)
     m = kmean(k16)  # [B, Hkv, D]
     ksm = k16.astype(np.float32) - m[..., None, :]
     assert ksm.dtype == np.float32
-    k8, sk = quant_rows(ksm)
+    k8, sk = quant_rows(fwht_f32(ksm) if hadamard else ksm)
     v8, sv = quant_rows(v16.astype(np.float32), V_SCALE_BITS)
     return dict(q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, kmean=m)
 
@@ -141,18 +176,19 @@ def qk_int32(q8: np.ndarray, k8: np.ndarray) -> np.ndarray:
     return s.astype(np.int64)
 
 
-def attn_core(q8, sq, k8, sk, v8, sv, softmax_scale, causal, rows=None):
+def attn_core(q8, sq, k8, sk, v8, sv, softmax_scale, causal, rows=None, logit_factor=1.0):
     """Attention of one head on quantized operands (R7, R8, R10).
 
     ``q8 [Sq, D]``, ``k8/v8 [Sk, D]`` int8; ``sq [Sq]``, ``sk/sv [Sk]`` fp32.
     ``rows`` optionally selects query rows (each row is independent).
+    ``logit_factor`` multiplies every logit (1/D for rotated rows, R13).
     Returns fp64 ``[len(rows), D]``.
     """
     Sq, Sk = q8.shape[0], k8.shape[0]
     if causal and Sq != Sk:
         raise ValueError("causal attention needs equal query and key lengths")
     rows = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
-    sm = np.float64(np.float32(softmax_scale))
+    sm = np.float64(np.float32(softmax_scale)) * np.float64(logit_factor)
     vhat = sv.astype(np.float64)[:, None] * v8.astype(np.float64)
     kk = k8.astype(np.float64)
     skd = sk.astype(np.float64)
@@ -170,12 +206,14 @@ def attn_core(q8, sq, k8, sk, v8, sv, softmax_scale, causal, rows=None):
     return out
 
 
-def attn_int8_fwd(q16, k16, v16, causal=True, softmax_scale=None, heads=None, rows=None):
+def attn_int8_fwd(q16, k16, v16, causal=True, softmax_scale=None, heads=None, rows=None,
+                  hadamard=False):
     """The dense forward: fp16 ``q[B,Hq,S,D]``, ``k/v[B,Hkv,S,D]`` -> fp64 O.
 
     ``heads`` (list of (b, h)) and ``rows`` restrict the output to a sample;
     the result then has shape ``[len(heads), len(rows), D]``, otherwise
-    ``[B, Hq, S, D]``.
+    ``[B, Hq, S, D]``.  ``hadamard`` selects the rotated variant (R13): Q and K
+    rows rotated before quantization and the logits scaled by an extra 1/D.
     """
     B, Hq, S, D = q16.shape
     Hkv = k16.shape[1]
@@ -183,13 +221,15 @@ def attn_int8_fwd(q16, k16, v16, causal=True, softmax_scale=None, heads=None, ro
         raise ValueError("Hq must be a multiple of Hkv")
     G = Hq // Hkv
     sm = default_softmax_scale(D) if softmax_scale is None else np.float32(softmax_scale)
-    qz = quantize_qkv(q16, k16, v16)
+    qz = quantize_qkv(q16, k16, v16, hadamard)
+    # The 1/D of the rotation multiplies the logits exactly (D is a power of two).
+    extra = 1.0 / D if hadamard else 1.0
     sel = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
     outs = []
     for b, h in sel:
         g = h // G
         outs.append(attn_core(qz["q8"][b, h], qz["sq"][b, h], qz["k8"][b, g], qz["sk"][b, g],
-                              qz["v8"][b, g], qz["sv"][b, g], sm, causal, rows))
+                              qz["v8"][b, g], qz["sv"][b, g], sm, causal, rows, extra))
     o = np.stack(outs)
     if heads is None and rows is None:
         o = o.reshape(B, Hq, S, D)

@@ -12,6 +12,7 @@ import os
 from fractions import Fraction
 
 import numpy as np
+import scipy.linalg as sla
 import pytest
 import torch
 
@@ -455,3 +456,66 @@ def test_decode_fp16_v_zero_query_gives_exact_mean():
     out = oracle.attn_int8_decode(np.zeros((2, 3, 64), np.float16), k, v, v_format="fp16")
     want = v.astype(np.float64).mean(axis=2)
     np.testing.assert_allclose(out, np.repeat(want, 3, axis=1), rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------- Hadamard rotation (R13)
+
+def test_fwht_butterfly_order_worked_example():
+    case = json.load(open(os.path.join(GOLDEN, "fwht_order_worked.json")))
+    x = np.array(case["x"], dtype=np.float32)
+    got = oracle.fwht_f32(x)
+    assert got.dtype == np.float32
+    assert got.tolist() == case["fp32_result"]
+    assert (x.astype(np.float64) @ sla.hadamard(4)).tolist() == case["exact_result"]
+
+
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
+def test_fwht_equals_library_hadamard_on_integers(D):
+    # Integer rows: every fp32 partial sum is exact, so the transform equals the
+    # product with the library's Sylvester-Hadamard matrix exactly, and applying it
+    # twice gives D times the row (H H = D I).
+    x = rng(60 + D).integers(-2000, 2000, (5, 3, D)).astype(np.float32)
+    y = oracle.fwht_f32(x)
+    assert np.array_equal(y.astype(np.float64), x.astype(np.float64) @ sla.hadamard(D))
+    assert np.array_equal(oracle.fwht_f32(y).astype(np.float64), D * x.astype(np.float64))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_hadamard_forward_equals_library_attention_on_rotated_operands(causal):
+    # The rotated forward is plain attention on the dequantized rotated Q and K rows
+    # (each scaled by 1/sqrt(D), which makes H orthonormal) and the dequantized V.
+    w = workloads.dense(61, 1, 4, 2, 70, 64, causal, k_offset=2.0)
+    D = 64
+    out = oracle.attn_int8_fwd(w.q, w.k, w.v, causal, hadamard=True)
+    z = oracle.quantize_qkv(w.q, w.k, w.v, hadamard=True)
+    qh = dequant(z["q8"], z["sq"]) / np.sqrt(D)
+    kh = np.repeat(dequant(z["k8"], z["sk"]), 2, axis=1) / np.sqrt(D)
+    vh = np.repeat(dequant(z["v8"], z["sv"]), 2, axis=1)
+    ref = sdpa64(qh, kh, vh, causal, oracle.default_softmax_scale(D))
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_hadamard_rows_are_rotations_of_the_smoothed_rows():
+    # The quantized rotated K rows approximate (k - mean) H to within half a code step
+    # per element, and the rotation preserves row norms up to the factor sqrt(D).
+    w = workloads.dense(62, 1, 2, 1, 40, 128, False, k_offset=3.0)
+    z = oracle.quantize_qkv(w.q, w.k, w.v, hadamard=True)
+    ksm = w.k.astype(np.float64) - z["kmean"][..., None, :].astype(np.float64)
+    rot = ksm @ sla.hadamard(128)
+    deq = dequant(z["k8"], z["sk"])
+    assert np.all(np.abs(deq - rot) <= 0.5 * z["sk"][..., None] * (1 + 1e-5) + 1e-3)
+    np.testing.assert_allclose(np.linalg.norm(rot, axis=-1),
+                               np.sqrt(128) * np.linalg.norm(ksm, axis=-1), rtol=1e-12)
+
+
+def test_hadamard_improves_quantization_on_outlier_channels():
+    # The point of the rotation: with a few channels x20 in Q and K, rotated rows
+    # quantize with far less error; measured against unquantized attention.
+    w = workloads.dense(63, 1, 4, 4, 256, 64, False, outlier_frac=0.03)
+    exact = oracle.attn_exact(w.q, w.k, w.v, False)
+
+    def sqnr(o):
+        return 10 * np.log10(np.sum(exact ** 2) / np.sum((o - exact) ** 2))
+    plain = sqnr(oracle.attn_int8_fwd(w.q, w.k, w.v, False))
+    rot = sqnr(oracle.attn_int8_fwd(w.q, w.k, w.v, False, hadamard=True))
+    assert rot > plain + 3.0, (plain, rot)
