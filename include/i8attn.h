@@ -106,6 +106,23 @@ i8a_status attn_int8_fwd(const void* q, const void* k, const void* v, void* out,
                          int32_t causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_int8_fwd_hadamard - attn_int8_fwd with Q and K rotated before quantization
+ * (SuperL8 README, Quantization table, row "Hadamard rotation": an incoherence rotation
+ * for outlier-heavy activations).  Each fp32 Q row, and each K row after the
+ * K-smoothing subtraction, is replaced by its unnormalized fast Walsh-Hadamard
+ * transform x H (Sylvester H, entries +-1), computed in fp32 with the butterfly stages
+ * s = 0, 1, ..., log2(D) - 1 in that order (the pair (x[i], x[i + 2^s]) with bit s of i
+ * clear becomes (x[i] + x[i + 2^s], x[i] - x[i + 2^s])), and then quantized per row as
+ * usual.  Since H H^T = D I the logits take an extra factor 1/D:
+ *   logit = S32 * sq_i * sk_j * softmax_scale / D.
+ * V is not rotated.  Arguments, workspace and errors as for attn_int8_fwd.
+ */
+i8a_status attn_int8_fwd_hadamard(const void* q, const void* k, const void* v, void* out,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D,
+                                  float softmax_scale, int32_t causal, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * The phases of attn_int8_fwd as separate calls, for callers that reuse one prepared
  * K/V for several query batches and for timing each phase alone:
  *   attn_int8_prepare_kv   the K-smoothing mean and the K and V quantization;
@@ -171,15 +188,16 @@ i8a_status attn_int8_varlen_fwd(const void* q, const void* k, const void* v, voi
  *   vscale_out nullable fp32 [cols]: sv of the same rows
  *   kmean_out  nullable fp32 [D]:   the K-smoothing mean of that kv head
  * with 0 <= row0, row0 + rows <= S, 0 <= col0, col0 + cols <= S, rows, cols >= 1.
- * Inputs, sizes and workspace as for attn_int8_fwd (causal is ignored: scores are
- * dumped unmasked).
+ * hadamard 0 or 1: 1 dumps the codes and scales of attn_int8_fwd_hadamard (rotated Q
+ * and K rows).  Inputs, sizes and workspace as for attn_int8_fwd (causal is ignored:
+ * scores are dumped unmasked).
  */
 i8a_status attn_int8_debug_qk(const void* q, const void* k, const void* v, int32_t B, int32_t Hq,
                               int32_t Hkv, int32_t S, int32_t D, int32_t b, int32_t h,
                               int32_t row0, int32_t rows, int32_t col0, int32_t cols,
                               int32_t* s32_out, float* qscale_out, float* kscale_out,
-                              float* vscale_out, float* kmean_out, void* workspace,
-                              size_t workspace_bytes, void* stream);
+                              float* vscale_out, float* kmean_out, int32_t hadamard,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Decode over an int8 KV cache (SuperL8 README, Attention kernels table, row

@@ -9,6 +9,7 @@ Entry points (same names as the C ABI):
 
 * :func:`quant_rowwise_i8` - symmetric per-row int8 quantization.
 * :func:`attn_int8_fwd` - dense forward, q ``[B,Hq,S,D]``, k/v ``[B,Hkv,S,D]``.
+* :func:`attn_int8_fwd_hadamard` - the same with Q and K Hadamard-rotated first.
 * :func:`attn_int8_varlen_fwd` - packed ragged batch, q ``[T,Hq,D]`` + ``cu_seqlens``.
 * :func:`attn_int8_debug_qk` - the forward's exact int32 scores and scales.
 * :func:`attn_int8_kvcache_fill` / :func:`attn_int8_decode` - an int8 KV cache and
@@ -26,6 +27,7 @@ import torch
 
 __all__ = [
     "quant_rowwise_i8", "attn_int8_fwd", "attn_int8_varlen_fwd", "attn_int8_debug_qk",
+    "attn_int8_fwd_hadamard",
     "attn_int8_prepare_kv", "attn_int8_prepare_q", "attn_int8_attend", "attn_int8_fwd_prepared",
     "attn_int8_workspace_bytes", "attn_int8_varlen_workspace_bytes", "library_path",
     "load_library", "SCALE_FP32", "SCALE_V4", "HEAD_DIMS", "attn_int8_kvcache_bytes",
@@ -53,7 +55,10 @@ _SIGS = {
     "attn_int8_varlen_workspace_bytes": (_c_sz, [_c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32]),
     "attn_int8_varlen_fwd": (_c_i32, [_c_vp] * 5 + [_c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_i32,
                                                      _c_f32, _c_i32, _c_vp, _c_sz, _c_vp]),
-    "attn_int8_debug_qk": (_c_i32, [_c_vp] * 3 + [_c_i32] * 11 + [_c_vp] * 6 + [_c_sz, _c_vp]),
+    "attn_int8_debug_qk": (_c_i32, [_c_vp] * 3 + [_c_i32] * 11 + [_c_vp] * 5 + [_c_i32, _c_vp,
+                                                                                 _c_sz, _c_vp]),
+    "attn_int8_fwd_hadamard": (_c_i32, [_c_vp] * 4 + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_sz,
+                                                                    _c_vp]),
     "attn_int8_prepare_kv": (_c_i32, [_c_vp] * 2 + [_c_i32] * 5 + [_c_vp, _c_sz, _c_vp]),
     "attn_int8_prepare_q": (_c_i32, [_c_vp] + [_c_i32] * 5 + [_c_vp, _c_sz, _c_vp]),
     "attn_int8_attend": (_c_i32, [_c_vp] + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_sz, _c_vp]),
@@ -217,6 +222,27 @@ def attn_int8_fwd(q, k, v, causal=True, softmax_scale=None, out=None, workspace=
     return out
 
 
+def attn_int8_fwd_hadamard(q, k, v, causal=True, softmax_scale=None, out=None, workspace=None):
+    """:func:`attn_int8_fwd` with Q and K rows Hadamard-rotated before quantization (an
+    incoherence rotation for outlier channels); returns fp16 ``out[B,Hq,S,D]``."""
+    B, Hq, Hkv, S, D = _dense_shapes(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_gpu_fp16("out", out, 4)
+        if out.shape != q.shape or out.device != q.device:
+            raise ValueError("out must match q")
+    lib = load_library()
+    nbytes = lib.attn_int8_workspace_bytes(B, Hq, Hkv, S, D)
+    ws = _workspace(workspace, nbytes, q.device)
+    with torch.cuda.device(q.device):
+        st = lib.attn_int8_fwd_hadamard(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, S, D,
+                                        _scale(softmax_scale, D), int(bool(causal)), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(q.device))
+    _check(st, "attn_int8_fwd_hadamard")
+    return out
+
+
 def attn_int8_prepare_kv(k, v, Hq, workspace=None):
     """K/V phase of :func:`attn_int8_fwd`: K-smoothing mean and K/V quantization of
     dense k/v ``[B,Hkv,S,D]`` into a workspace, returned for
@@ -331,9 +357,10 @@ def attn_int8_varlen_fwd(q, k, v, cu_seqlens, max_seqlen, causal=True, softmax_s
     return out
 
 
-def attn_int8_debug_qk(q, k, v, b, h, row0, rows, col0, cols, workspace=None):
+def attn_int8_debug_qk(q, k, v, b, h, row0, rows, col0, cols, workspace=None, hadamard=False):
     """The dense forward's exact int32 scores ``S32[row0:row0+rows, col0:col0+cols]``
-    of (batch b, query head h), with the row scales and the K mean it used."""
+    of (batch b, query head h), with the row scales and the K mean it used (with
+    ``hadamard``, those of :func:`attn_int8_fwd_hadamard`)."""
     B, Hq, Hkv, S, D = _dense_shapes(q, k, v)
     dev = q.device
     s32 = torch.empty((rows, cols), dtype=torch.int32, device=dev)
@@ -347,7 +374,8 @@ def attn_int8_debug_qk(q, k, v, b, h, row0, rows, col0, cols, workspace=None):
     with torch.cuda.device(dev):
         st = lib.attn_int8_debug_qk(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, S, D, b, h, row0, rows,
                                     col0, cols, _ptr(s32), _ptr(qs), _ptr(ks), _ptr(vs), _ptr(km),
-                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
+                                    int(bool(hadamard)), _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(dev))
     _check(st, "attn_int8_debug_qk")
     return dict(s32=s32, qscale=qs, kscale=ks, vscale=vs, kmean=km)
 

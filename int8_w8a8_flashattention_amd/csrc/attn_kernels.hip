@@ -356,7 +356,8 @@ static hipError_t attn_d(const FwdGeom& g, const WsPlan& p, const void* ws, hipS
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const int ngroups = g.nseq * g.Hkv;
   const int xcd_map = ((g.nseq * g.Hq) % 8 == 0 && ngroups % 8 == 0) ? 1 : 0;
-  const float qk_log2 = g.softmax_scale * 1.4426950408889634f;
+  // Rotated Q and K rows carry H H^T = D I: an extra exact factor 1/D on the logits.
+  const float qk_log2 = g.softmax_scale * 1.4426950408889634f * (g.rot ? 1.0f / g.D : 1.0f);
   Seqs sq{g.cu, g.S, g.max_len, g.T};
   attn_fwd_kernel<D, C><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
       reinterpret_cast<const int8_t*>(w + p.off_q8), reinterpret_cast<const float*>(w + p.off_qs),

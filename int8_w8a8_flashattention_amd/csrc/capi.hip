@@ -177,6 +177,19 @@ i8a_status attn_int8_fwd(const void* q, const void* k, const void* v, void* out,
   return run_phases(g, PH_KV | PH_Q | PH_ATTN, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
+i8a_status attn_int8_fwd_hadamard(const void* q, const void* k, const void* v, void* out,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D,
+                                  float softmax_scale, int32_t causal, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  i8a_status st = check_common(q, k, v, out, Hq, Hkv, D, softmax_scale, causal, workspace);
+  if (st != I8A_OK) return st;
+  if (B < 1 || S < 1 || B > kMaxGridYZ)
+    return fail(I8A_ERR_INVALID_ARG, "need 1 <= B <= %d and S >= 1", kMaxGridYZ);
+  if ((int64_t)B * S > kMaxTokens) return fail(I8A_ERR_INVALID_ARG, "B*S too large");
+  FwdGeom g{q, k, v, out, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D, softmax_scale, causal, 1};
+  return run_phases(g, PH_KV | PH_Q | PH_ATTN, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
 i8a_status attn_int8_prepare_kv(const void* k, const void* v, int32_t B, int32_t Hq, int32_t Hkv,
                                 int32_t S, int32_t D, void* workspace, size_t workspace_bytes,
                                 void* stream) {
@@ -258,8 +271,8 @@ i8a_status attn_int8_debug_qk(const void* q, const void* k, const void* v, int32
                               int32_t Hkv, int32_t S, int32_t D, int32_t b, int32_t h,
                               int32_t row0, int32_t rows, int32_t col0, int32_t cols,
                               int32_t* s32_out, float* qscale_out, float* kscale_out,
-                              float* vscale_out, float* kmean_out, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+                              float* vscale_out, float* kmean_out, int32_t hadamard,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   // `out` is not written by this entry; q stands in for the alignment check.
   i8a_status st = check_common(q, k, v, q, Hq, Hkv, D, 1.0f, 0, workspace);
   if (st != I8A_OK) return st;
@@ -271,7 +284,8 @@ i8a_status attn_int8_debug_qk(const void* q, const void* k, const void* v, int32
     return fail(I8A_ERR_INVALID_ARG, "tile [%d+%d, %d+%d] outside [0, %d)", row0, rows, col0,
                 cols, S);
   if (!s32_out || !aligned(s32_out, 4)) return fail(I8A_ERR_INVALID_ARG, "bad s32_out");
-  FwdGeom g{q, k, v, nullptr, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D, 1.0f, 0};
+  if (hadamard != 0 && hadamard != 1) return fail(I8A_ERR_INVALID_ARG, "hadamard must be 0 or 1");
+  FwdGeom g{q, k, v, nullptr, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D, 1.0f, 0, hadamard};
   const WsPlan p = plan_workspace(B, (int64_t)B * S, S, Hq, Hkv, D);
   i8a_status pst = run_phases(g, PH_KV | PH_Q, workspace, workspace_bytes, (hipStream_t)stream);
   if (pst != I8A_OK) return pst;

@@ -164,6 +164,34 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Unnormalized fast Walsh-Hadamard transform of one D-channel row (the Quantization
+// table's Hadamard rotation) held by G = D/8 consecutive lanes, lane lc holding
+// channels 8 lc .. 8 lc + 7, in fp32, with the stages in the order s = 0, 1, ...,
+// log2(D) - 1: the pair (x[i], x[i + 2^s]) with bit s of i clear becomes
+// (x[i] + x[i + 2^s], x[i] - x[i + 2^s]).  Stages 0-2 pair values inside a lane, the
+// later ones lane lc with lane lc ^ 2^(s-3).  Every lane of the group takes part.
+template <int G>
+__device__ __forceinline__ void fwht_row(float (&x)[8], int lc) {
+#pragma unroll
+  for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (!(j & h)) {
+        const float a = x[j], b = x[j + h];
+        x[j] = a + b;
+        x[j + h] = a - b;
+      }
+#pragma unroll
+  for (int m = 1; m < G; m *= 2) {
+    const bool hi = (lc & m) != 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = __shfl_xor(x[j], m, 64);
+      x[j] = hi ? p - x[j] : x[j] + p;
+    }
+  }
+}
+
 // fp16 load of 8 consecutive values as fp32.
 __device__ __forceinline__ void load8_f32(const _Float16* p, float (&x)[8]) {
   const v8h h = *reinterpret_cast<const v8h*>(p);

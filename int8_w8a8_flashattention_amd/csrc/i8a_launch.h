@@ -54,6 +54,7 @@ struct FwdGeom {
   int32_t Hq, Hkv, D;
   float softmax_scale;
   int causal;
+  int rot;  // Q and K rows Hadamard-rotated before quantization (logits take 1/D)
 };
 
 hipError_t launch_quant_rowwise(const void* x, int64_t rows, int32_t d, const float* sub_mean,

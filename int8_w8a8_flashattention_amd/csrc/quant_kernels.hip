@@ -213,7 +213,7 @@ struct PrepKShared {
   float mean[D];
 };
 
-template <int D>
+template <int D, bool ROT>
 __device__ __forceinline__ void prep_k_body(const _Float16* __restrict__ k, const Act& act,
                                             const Seqs& seqs, int Hkv, int npart, int tpw,
                                             int64_t Ppad, const int64_t* __restrict__ kpart,
@@ -264,7 +264,13 @@ __device__ __forceinline__ void prep_k_body(const _Float16* __restrict__ k, cons
       const bool real = t < L;
       float x[8];
       float amax = 0.0f;
-      if (real) {
+      if constexpr (ROT) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = real ? (float)kr[i][j] - mu[j] : 0.0f;
+        fwht_row<G>(x, lc);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+      } else if (real) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           x[j] = (float)kr[i][j] - mu[j];
@@ -292,7 +298,7 @@ __device__ __forceinline__ void prep_k_body(const _Float16* __restrict__ k, cons
 constexpr int QCH = 64;
 static_assert(BQ % QCH == 0 && QCH % 32 == 0, "Q chunks hold whole 32-row blocks");
 
-template <int D>
+template <int D, bool ROT>
 __device__ __forceinline__ void prep_q_body(const _Float16* __restrict__ q, const Act& act,
                                             const Seqs& seqs, int64_t Qpad,
                                             int8_t* __restrict__ q8, float* __restrict__ qs,
@@ -322,7 +328,13 @@ __device__ __forceinline__ void prep_q_body(const _Float16* __restrict__ q, cons
     const bool real = r0 + n < L;
     float x[8];
     float amax = 0.0f;
-    if (real) {
+    if constexpr (ROT) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = real ? (float)xr[i][j] : 0.0f;
+      fwht_row<G>(x, lc);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+    } else if (real) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         x[j] = (float)xr[i][j];
@@ -353,7 +365,7 @@ union PrepShared {
   __attribute__((aligned(16))) int8_t qfrag[QCH * D];
 };
 
-template <int D>
+template <int D, bool ROT>
 __global__ __launch_bounds__(256) void prep_kvq_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
     const _Float16* __restrict__ v, Act aq, Act akv, Seqs seqs, int Hq, int Hkv, int npart,
@@ -370,13 +382,13 @@ __global__ __launch_bounds__(256) void prep_kvq_kernel(
     if (is_v)
       prep_v_body<D>(v, akv, seqs, tpw, Ppad, sv_ws, tiles, c, b % Hkv, b / Hkv, sh.v);
     else
-      prep_k_body<D>(k, akv, seqs, Hkv, npart, tpw, Ppad, kpart, kmean_ws, tiles, c, b % Hkv,
+      prep_k_body<D, ROT>(k, akv, seqs, Hkv, npart, tpw, Ppad, kpart, kmean_ws, tiles, c, b % Hkv,
                      b / Hkv, sh.k);
   } else {
     b -= 2 * nk;
     const int c = b % nqc;
     b /= nqc;
-    prep_q_body<D>(q, aq, seqs, Qpad, q8, qs, c, b % Hq, b / Hq, sh.qfrag);
+    prep_q_body<D, ROT>(q, aq, seqs, Qpad, q8, qs, c, b % Hq, b / Hq, sh.qfrag);
   }
 }
 
@@ -419,8 +431,9 @@ static Act act_of(const FwdGeom& g, int H) {
 }
 
 // Launches of the preparation.  With k/v (PH_KV): launch 1 sums K, launch 2 quantizes
-// K and prepares V; with q (PH_Q) the Q rows ride in launch 2.
-template <int D>
+// K and prepares V; with q (PH_Q) the Q rows ride in launch 2.  ROT: the K and Q rows
+// are Hadamard-rotated before they are quantized.
+template <int D, bool ROT>
 static hipError_t prep_d(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, bool qq,
                          hipStream_t stream) {
   char* w = static_cast<char*>(ws);
@@ -435,7 +448,7 @@ static hipError_t prep_d(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, b
     prep_ksum_kernel<D><<<dim3((unsigned)nk), 256, 0, stream>>>(
         kp, akv, sq, g.Hkv, p.npart, p.tpw, reinterpret_cast<int64_t*>(w + p.off_kpart));
   if (2 * nk + nq > 0)
-    prep_kvq_kernel<D><<<dim3((unsigned)(2 * nk + nq)), 256, 0, stream>>>(
+    prep_kvq_kernel<D, ROT><<<dim3((unsigned)(2 * nk + nq)), 256, 0, stream>>>(
         static_cast<const _Float16*>(g.q), kp, static_cast<const _Float16*>(g.v), aq, akv, sq,
         g.Hq, g.Hkv, p.npart, p.tpw, p.Ppad, p.Qpad, nqc,
         reinterpret_cast<const int64_t*>(w + p.off_kpart),
@@ -449,10 +462,12 @@ hipError_t launch_prep(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, boo
                        hipStream_t stream) {
   if (g.max_len == 0) return hipSuccess;  // every sequence is empty
   switch (g.D) {
-    case 32: return prep_d<32>(g, p, ws, kv, qq, stream);
-    case 64: return prep_d<64>(g, p, ws, kv, qq, stream);
-    case 128: return prep_d<128>(g, p, ws, kv, qq, stream);
-    case 256: return prep_d<256>(g, p, ws, kv, qq, stream);
+#define I8A_PREP(DD)                                                       \
+  case DD:                                                                 \
+    return g.rot ? prep_d<DD, true>(g, p, ws, kv, qq, stream)              \
+                 : prep_d<DD, false>(g, p, ws, kv, qq, stream);
+    I8A_PREP(32) I8A_PREP(64) I8A_PREP(128) I8A_PREP(256)
+#undef I8A_PREP
     default: return hipErrorInvalidValue;
   }
 }

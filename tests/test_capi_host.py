@@ -139,12 +139,14 @@ def test_quant_rejects_bad_arguments(lib):
 def test_debug_rejects_bad_tiles(lib):
     def call(b=0, h=0, r0=0, r=8, c0=0, c=8, s32=FAKE):
         return lib.attn_int8_debug_qk(FAKE, FAKE, FAKE, 1, 4, 2, 64, 64, b, h, r0, r, c0, c, s32,
-                                      None, None, None, None, FAKE, 1 << 40, None)
+                                      None, None, None, None, 0, FAKE, 1 << 40, None)
     assert call(b=1) == INVALID
     assert call(h=4) == INVALID
     assert call(r0=60, r=8) == INVALID
     assert call(c=0) == INVALID
     assert call(s32=None) == INVALID
+    assert lib.attn_int8_debug_qk(FAKE, FAKE, FAKE, 1, 4, 2, 64, 64, 0, 0, 0, 8, 0, 8, FAKE,
+                                  None, None, None, None, 2, FAKE, 1 << 40, None) == INVALID
 
 
 def test_python_binding_validates_before_the_library():
