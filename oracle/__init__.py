@@ -20,6 +20,8 @@ The method it defines comes from the "SuperL8" README (the page titled
   "V per-channel / per-token" (V is quantized per token here).
 * *Quantization* table, row "Hadamard rotation": Q and K rows rotated before
   quantization (the ``hadamard`` option of the forward).
+* *Quantization* table, row "V per-channel / per-token": V quantized per token
+  (default) or per channel over the tokens (the ``v_per_channel`` option).
 * *Quick start*: ``attn_int8_fwd(q, k, v, causal=True)`` takes fp16
   ``q[B,Hq,S,D]``, ``k/v[B,Hkv,S,D]`` and quantizes internally.
 
@@ -38,6 +40,7 @@ from .attn_ref import (  # noqa: F401
     default_softmax_scale,
     kmean,
     quant_rows,
+    quant_cols,
     quantize_qkv,
     fwht_f32,
     qk_int32,

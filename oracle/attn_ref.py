@@ -62,6 +62,13 @@ R13 Hadamard rotation (the *Quantization* table's "Hadamard rotation" row: an
     rotated rows are D times the unrotated ones: the logits take an extra exact
     factor 1/D.  V is not rotated.
 
+R14 V per channel (the *Quantization* table's "V per-channel / per-token" row:
+    configurable KV cache quantization).  Per token is R2's default.  Per channel,
+    V is quantized with one scale per (sequence, kv head, channel) over the
+    sequence's tokens: the scale is fp32(absmax/127) rounded up to a 4-bit
+    significand (the V rule of R2, so that every dequantized value is exactly an
+    fp16 number) and the codes follow R3 with that channel's scale.
+
 Quantization steps are emulated op for op in numpy float32, which is IEEE
 single precision with round-to-nearest-even; everything after the integer
 codes is exact or fp64.
@@ -150,11 +157,21 @@ def fwht_f32(x32: np.ndarray) -> np.ndarray:
     return x
 
 
-def quantize_qkv(q16, k16, v16, hadamard=False):
-    """Quantize dense BHSD q/k/v as the forward does internally (with ``hadamard``,
-    Q and the mean-smoothed K rows rotated first, R13).
+def quant_cols(x32: np.ndarray, scale_bits: int = 4):
+    """Symmetric int8 quantization of fp32 ``[..., T, D]`` with one scale per column
+    (channel) over the T rows (R14): the row rule of :func:`quant_rows` applied along
+    the token axis.  Returns ``(codes int8 [..., T, D], scales fp32 [..., D])``."""
+    codes, scale = quant_rows(np.ascontiguousarray(np.swapaxes(x32, -1, -2)), scale_bits)
+    return np.ascontiguousarray(np.swapaxes(codes, -1, -2)), scale
 
-    Returns a dict with ``q8, sq, k8, sk, v8, sv, kmean``.
+
+def quantize_qkv(q16, k16, v16, hadamard=False, v_per_channel=False):
+    """Quantize dense BHSD q/k/v as the forward does internally (with ``hadamard``,
+    Q and the mean-smoothed K rows rotated first, R13; with ``v_per_channel``, V
+    quantized per channel over the tokens, R14).
+
+    Returns a dict with ``q8, sq, k8, sk, v8, sv, kmean``; ``sv`` is ``[B, Hkv, S]``
+    per token or ``[B, Hkv, D]`` per channel.
     """
     q32 = q16.astype(np.float32)
     q8, sq = quant_rows(fwht_f32(q32) if hadamard else q32)
@@ -162,7 +179,10 @@ def quantize_qkv(q16, k16, v16, hadamard=False):
     ksm = k16.astype(np.float32) - m[..., None, :]
     assert ksm.dtype == np.float32
     k8, sk = quant_rows(fwht_f32(ksm) if hadamard else ksm)
-    v8, sv = quant_rows(v16.astype(np.float32), V_SCALE_BITS)
+    if v_per_channel:
+        v8, sv = quant_cols(v16.astype(np.float32), V_SCALE_BITS)
+    else:
+        v8, sv = quant_rows(v16.astype(np.float32), V_SCALE_BITS)
     return dict(q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, kmean=m)
 
 
@@ -176,10 +196,12 @@ def qk_int32(q8: np.ndarray, k8: np.ndarray) -> np.ndarray:
     return s.astype(np.int64)
 
 
-def attn_core(q8, sq, k8, sk, v8, sv, softmax_scale, causal, rows=None, logit_factor=1.0):
+def attn_core(q8, sq, k8, sk, v8, sv, softmax_scale, causal, rows=None, logit_factor=1.0,
+              v_per_channel=False):
     """Attention of one head on quantized operands (R7, R8, R10).
 
-    ``q8 [Sq, D]``, ``k8/v8 [Sk, D]`` int8; ``sq [Sq]``, ``sk/sv [Sk]`` fp32.
+    ``q8 [Sq, D]``, ``k8/v8 [Sk, D]`` int8; ``sq [Sq]``, ``sk [Sk]`` fp32; ``sv [Sk]``
+    per key, or ``[D]`` per channel with ``v_per_channel`` (R14).
     ``rows`` optionally selects query rows (each row is independent).
     ``logit_factor`` multiplies every logit (1/D for rotated rows, R13).
     Returns fp64 ``[len(rows), D]``.
@@ -189,7 +211,10 @@ def attn_core(q8, sq, k8, sk, v8, sv, softmax_scale, causal, rows=None, logit_fa
         raise ValueError("causal attention needs equal query and key lengths")
     rows = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
     sm = np.float64(np.float32(softmax_scale)) * np.float64(logit_factor)
-    vhat = sv.astype(np.float64)[:, None] * v8.astype(np.float64)
+    if v_per_channel:
+        vhat = v8.astype(np.float64) * sv.astype(np.float64)[None, :]
+    else:
+        vhat = sv.astype(np.float64)[:, None] * v8.astype(np.float64)
     kk = k8.astype(np.float64)
     skd = sk.astype(np.float64)
     out = np.empty((rows.size, q8.shape[1]), dtype=np.float64)
@@ -207,13 +232,14 @@ def attn_core(q8, sq, k8, sk, v8, sv, softmax_scale, causal, rows=None, logit_fa
 
 
 def attn_int8_fwd(q16, k16, v16, causal=True, softmax_scale=None, heads=None, rows=None,
-                  hadamard=False):
+                  hadamard=False, v_per_channel=False):
     """The dense forward: fp16 ``q[B,Hq,S,D]``, ``k/v[B,Hkv,S,D]`` -> fp64 O.
 
     ``heads`` (list of (b, h)) and ``rows`` restrict the output to a sample;
     the result then has shape ``[len(heads), len(rows), D]``, otherwise
     ``[B, Hq, S, D]``.  ``hadamard`` selects the rotated variant (R13): Q and K
     rows rotated before quantization and the logits scaled by an extra 1/D.
+    ``v_per_channel`` quantizes V per channel (R14).
     """
     B, Hq, S, D = q16.shape
     Hkv = k16.shape[1]
@@ -221,7 +247,7 @@ def attn_int8_fwd(q16, k16, v16, causal=True, softmax_scale=None, heads=None, ro
         raise ValueError("Hq must be a multiple of Hkv")
     G = Hq // Hkv
     sm = default_softmax_scale(D) if softmax_scale is None else np.float32(softmax_scale)
-    qz = quantize_qkv(q16, k16, v16, hadamard)
+    qz = quantize_qkv(q16, k16, v16, hadamard, v_per_channel)
     # The 1/D of the rotation multiplies the logits exactly (D is a power of two).
     extra = 1.0 / D if hadamard else 1.0
     sel = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
@@ -229,18 +255,21 @@ def attn_int8_fwd(q16, k16, v16, causal=True, softmax_scale=None, heads=None, ro
     for b, h in sel:
         g = h // G
         outs.append(attn_core(qz["q8"][b, h], qz["sq"][b, h], qz["k8"][b, g], qz["sk"][b, g],
-                              qz["v8"][b, g], qz["sv"][b, g], sm, causal, rows, extra))
+                              qz["v8"][b, g], qz["sv"][b, g], sm, causal, rows, extra,
+                              v_per_channel))
     o = np.stack(outs)
     if heads is None and rows is None:
         o = o.reshape(B, Hq, S, D)
     return o
 
 
-def attn_int8_varlen_fwd(q16, k16, v16, cu_seqlens, causal=True, softmax_scale=None):
+def attn_int8_varlen_fwd(q16, k16, v16, cu_seqlens, causal=True, softmax_scale=None,
+                         hadamard=False, v_per_channel=False):
     """The varlen forward (R11): packed ``q[T,Hq,D]``, ``k/v[T,Hkv,D]``.
 
-    Each sequence ``cu[i]:cu[i+1]`` is quantized (its own K mean) and attended
-    independently.  Returns fp64 ``[T, Hq, D]``.
+    Each sequence ``cu[i]:cu[i+1]`` is quantized (its own K mean, and its own V
+    channel scales with ``v_per_channel``) and attended independently.  Returns fp64
+    ``[T, Hq, D]``.
     """
     T, Hq, D = q16.shape
     cu = np.asarray(cu_seqlens, dtype=np.int64)
@@ -252,7 +281,8 @@ def attn_int8_varlen_fwd(q16, k16, v16, cu_seqlens, causal=True, softmax_scale=N
         qs = np.ascontiguousarray(q16[a:b].transpose(1, 0, 2))[None]
         ks = np.ascontiguousarray(k16[a:b].transpose(1, 0, 2))[None]
         vs = np.ascontiguousarray(v16[a:b].transpose(1, 0, 2))[None]
-        o = attn_int8_fwd(qs, ks, vs, causal, softmax_scale)[0]
+        o = attn_int8_fwd(qs, ks, vs, causal, softmax_scale, hadamard=hadamard,
+                          v_per_channel=v_per_channel)[0]
         out[a:b] = o.transpose(1, 0, 2)
     return out
 

@@ -519,3 +519,55 @@ def test_hadamard_improves_quantization_on_outlier_channels():
     plain = sqnr(oracle.attn_int8_fwd(w.q, w.k, w.v, False))
     rot = sqnr(oracle.attn_int8_fwd(w.q, w.k, w.v, False, hadamard=True))
     assert rot > plain + 3.0, (plain, rot)
+
+
+# ---------------------------------------------------------------- V per channel (R14)
+
+def test_v_per_channel_worked_example():
+    case = json.load(open(os.path.join(GOLDEN, "v_per_channel_worked.json")))
+    codes, scales = oracle.quant_cols(np.array(case["v"], dtype=np.float32))
+    assert codes.tolist() == case["codes"]
+    assert (scales * np.float32(1024)).tolist() == case["scales_times_1024"]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_v_per_channel_forward_equals_library_attention(causal):
+    w = workloads.dense(64, 2, 4, 2, 90, 64, causal, k_offset=1.0)
+    out = oracle.attn_int8_fwd(w.q, w.k, w.v, causal, v_per_channel=True)
+    z = oracle.quantize_qkv(w.q, w.k, w.v, v_per_channel=True)
+    assert z["sv"].shape == (2, 2, 64)
+    qh = dequant(z["q8"], z["sq"])
+    kh = np.repeat(dequant(z["k8"], z["sk"]), 2, axis=1)
+    vh = np.repeat(z["v8"].astype(np.float64) * z["sv"][..., None, :].astype(np.float64), 2,
+                   axis=1)
+    ref = sdpa64(qh, kh, vh, causal, oracle.default_softmax_scale(64))
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_v_per_channel_scaling_a_channel_by_two_scales_its_output_exactly():
+    # Per-channel scales absorb a power-of-two gain of one V channel exactly (same
+    # codes, doubled scale), so that output channel doubles and the others are
+    # untouched; per-token scales do not have this property.
+    w = workloads.dense(65, 1, 2, 1, 50, 32, True)
+    v2 = w.v.copy()
+    v2[..., 5] *= np.float16(2.0)
+    a = oracle.attn_int8_fwd(w.q, w.k, w.v, True, v_per_channel=True)
+    b = oracle.attn_int8_fwd(w.q, w.k, v2, True, v_per_channel=True)
+    assert np.array_equal(b[..., 5], 2.0 * a[..., 5])
+    keep = [d for d in range(32) if d != 5]
+    assert np.array_equal(b[..., keep], a[..., keep])
+    a_t = oracle.attn_int8_fwd(w.q, w.k, w.v, True)
+    b_t = oracle.attn_int8_fwd(w.q, w.k, v2, True)
+    assert not np.array_equal(b_t[..., keep], a_t[..., keep])
+
+
+def test_v_per_channel_varlen_scales_per_sequence():
+    # Each sequence of a packed batch gets its own channel scales: the packed result
+    # equals the dense result of every sequence alone.
+    w = workloads.varlen(66, 3, 40, 4, 2, 32, True, lengths=[17, 1, 40])
+    out = oracle.attn_int8_varlen_fwd(w.q, w.k, w.v, w.cu_seqlens, True, v_per_channel=True)
+    for i in range(3):
+        a, b = int(w.cu_seqlens[i]), int(w.cu_seqlens[i + 1])
+        tr = lambda x: np.ascontiguousarray(x[a:b].transpose(1, 0, 2))[None]
+        ref = oracle.attn_int8_fwd(tr(w.q), tr(w.k), tr(w.v), True, v_per_channel=True)[0]
+        assert np.array_equal(out[a:b], ref.transpose(1, 0, 2))
