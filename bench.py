@@ -27,9 +27,10 @@ and scales, the query rows read, the output written) over the call time, against
 8 TB/s.  Its ``cpu_baseline`` times the oracle's decode over a cache quantized
 beforehand, on a sample of sequences.
 
-The ``hadamard`` object times the Hadamard-rotated forward (``attn_int8_fwd_hadamard``)
-on the same workload and reports its quality gain (SQNR against unquantized attention)
-on the outlier-channel workload.
+The ``variants`` object times the forward's variants (``attn_int8_fwd_ex`` with Q and K
+Hadamard-rotated, with V per channel, and with both) on the same workload and reports
+each one's quality (SQNR against unquantized attention) on the outlier-channel
+workload next to the plain forward's.
 
 Only one GPU is used: ``--gpus`` above 1 exits with a message.
 """
@@ -234,55 +235,59 @@ def bench_decode(args, i8, torch, dev):
     return res
 
 
-def bench_hadamard(args, i8, torch, dev, q, k, v, out, ws, ms_step):
-    """The Hadamard-rotated forward (NEXT-3): its step time on the same workload, and its
-    quality gain on the outlier-channel workload (B4 H16 S2048 D128 non-causal, 1 % of
-    channels x20) as SQNR against unquantized attention on sampled heads."""
+def bench_variants(args, i8, torch, dev, q, k, v, out, ws, ms_step):
+    """The forward's variants (NEXT-3 Hadamard-rotated Q/K, NEXT-2 V per channel, and
+    both): their step times on the same workload, and their quality on the
+    outlier-channel workload (B4 H16 S2048 D128 non-causal, 1 % of channels x20) as SQNR
+    against unquantized attention on sampled heads and rows."""
     import numpy as np
 
     import oracle
     from int8_w8a8_flashattention_amd import workloads
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    def step():
-        i8.attn_int8_fwd_hadamard(q, k, v, True, out=out, workspace=ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    flags = {"hadamard": i8.FWD_HADAMARD, "v_per_channel": i8.FWD_V_PER_CHANNEL,
+             "hadamard+v_per_channel": i8.FWD_HADAMARD | i8.FWD_V_PER_CHANNEL}
+    kw = {"hadamard": dict(hadamard=True), "v_per_channel": dict(v_per_channel=True),
+          "hadamard+v_per_channel": dict(hadamard=True, v_per_channel=True)}
+    res = {"outlier_workload": "cfg3_mha_s2048_d128_outliers: B4 H16 S2048 D128 non-causal, "
+                               "1 % of channels x20 in Q and K, 4 heads x 293 rows"}
     w = workloads.cfg3(128)
     qq, kk, vv = (torch.from_numpy(a).to(dev) for a in (w.q, w.k, w.v))
-    rot = i8.attn_int8_fwd_hadamard(qq, kk, vv, False).float().cpu().numpy()
-    plain = i8.attn_int8_fwd(qq, kk, vv, False).float().cpu().numpy()
     heads = [(0, 0), (1, 7), (2, 11), (3, 15)]
     rows = np.arange(0, 2048, 7)
     exact = oracle.attn_exact(w.q, w.k, w.v, False, heads=heads, rows=rows)
-    ref = oracle.attn_int8_fwd(w.q, w.k, w.v, False, heads=heads, rows=rows, hadamard=True)
 
     def pick(o):
         return np.stack([o[b, h][rows] for b, h in heads]).astype(np.float64)
 
-    err = float(np.abs(pick(rot) - ref).max())
-    if not err <= 2e-3:
-        raise RuntimeError(f"rotated output differs from the oracle: max_abs={err}")
-
     def sqnr(o):
-        return float(10 * np.log10(np.sum(exact ** 2) / np.sum((pick(o) - exact) ** 2)))
-    res = {"step_us": round(ms * 1e3, 2),
-           "extra_us_over_plain": round((ms - ms_step) * 1e3, 2),
-           "outlier_workload": "cfg3_mha_s2048_d128_outliers: B4 H16 S2048 D128 non-causal, "
-                               "1 % of channels x20 in Q and K, 4 heads x 293 rows",
-           "sqnr_db_plain": round(sqnr(plain), 2), "sqnr_db_rotated": round(sqnr(rot), 2),
-           "parity_sample_max_abs": err}
-    log(f"bench: rotated forward {res['step_us']} us/step; SQNR {res['sqnr_db_plain']} -> "
-        f"{res['sqnr_db_rotated']} dB on the outlier workload")
+        return round(float(10 * np.log10(np.sum(exact ** 2) / np.sum((pick(o) - exact) ** 2))),
+                     2)
+    res["sqnr_db_plain"] = sqnr(i8.attn_int8_fwd(qq, kk, vv, False).float().cpu().numpy())
+    for name, fl in flags.items():
+        def step():
+            i8.attn_int8_fwd_ex(q, k, v, True, fl, out=out, workspace=ws)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        o = i8.attn_int8_fwd_ex(qq, kk, vv, False, fl).float().cpu().numpy()
+        ref = oracle.attn_int8_fwd(w.q, w.k, w.v, False, heads=heads, rows=rows, **kw[name])
+        err = float(np.abs(pick(o) - ref).max())
+        if not err <= 2e-3:
+            raise RuntimeError(f"{name} output differs from the oracle: max_abs={err}")
+        res[name] = {"step_us": round(ms * 1e3, 2),
+                     "extra_us_over_plain": round((ms - ms_step) * 1e3, 2),
+                     "sqnr_db": sqnr(o), "parity_sample_max_abs": err}
+        log(f"bench: {name} forward {res[name]['step_us']} us/step; SQNR "
+            f"{res['sqnr_db_plain']} -> {res[name]['sqnr_db']} dB on the outlier workload")
     return res
 
 
@@ -487,7 +492,7 @@ def main():
     if not args.no_cpu_baseline:
         log(f"bench: timing the CPU oracle (~{args.cpu_budget:.0f} s)")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
-    res["hadamard"] = bench_hadamard(args, i8, torch, dev, q, k, v, out, ws, ms_step)
+    res["variants"] = bench_variants(args, i8, torch, dev, q, k, v, out, ws, ms_step)
     if not args.no_decode:
         del q, k, v, out, ws
         res["decode"] = bench_decode(args, i8, torch, dev)

@@ -106,17 +106,37 @@ i8a_status attn_int8_fwd(const void* q, const void* k, const void* v, void* out,
                          int32_t causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * attn_int8_fwd_hadamard - attn_int8_fwd with Q and K rotated before quantization
- * (SuperL8 README, Quantization table, row "Hadamard rotation": an incoherence rotation
- * for outlier-heavy activations).  Each fp32 Q row, and each K row after the
- * K-smoothing subtraction, is replaced by its unnormalized fast Walsh-Hadamard
- * transform x H (Sylvester H, entries +-1), computed in fp32 with the butterfly stages
- * s = 0, 1, ..., log2(D) - 1 in that order (the pair (x[i], x[i + 2^s]) with bit s of i
- * clear becomes (x[i] + x[i + 2^s], x[i] - x[i + 2^s])), and then quantized per row as
- * usual.  Since H H^T = D I the logits take an extra factor 1/D:
- *   logit = S32 * sq_i * sk_j * softmax_scale / D.
- * V is not rotated.  Arguments, workspace and errors as for attn_int8_fwd.
+ * Variants of the forward, as flags of attn_int8_fwd_ex / attn_int8_varlen_fwd_ex (any
+ * combination; 0 is attn_int8_fwd itself):
+ *
+ * I8A_FWD_HADAMARD - Q and K rotated before quantization (SuperL8 README, Quantization
+ *   table, row "Hadamard rotation": an incoherence rotation for outlier-heavy
+ *   activations).  Each fp32 Q row, and each K row after the K-smoothing subtraction,
+ *   is replaced by its unnormalized fast Walsh-Hadamard transform x H (Sylvester H,
+ *   entries +-1), computed in fp32 with the butterfly stages s = 0, 1, ..., log2(D) - 1
+ *   in that order (the pair (x[i], x[i + 2^s]) with bit s of i clear becomes
+ *   (x[i] + x[i + 2^s], x[i] - x[i + 2^s])), and then quantized per row as usual.
+ *   Since H H^T = D I the logits take an extra factor 1/D:
+ *     logit = S32 * sq_i * sk_j * softmax_scale / D.
+ *   V is not rotated.
+ *
+ * I8A_FWD_V_PER_CHANNEL - V quantized per channel instead of per token (Quantization
+ *   table, row "V per-channel / per-token": configurable KV cache quantization): one
+ *   scale per (sequence, kv head, channel) over the sequence's tokens,
+ *   sv_d = fp32(max_t |v[t,d]| / 127) rounded up to a 4-bit significand, codes
+ *   clamp(rint(fp32(v / sv_d)), -127, 127); out = softmax(logit) . (v8 * sv_d).
  */
+#define I8A_FWD_HADAMARD 1
+#define I8A_FWD_V_PER_CHANNEL 2
+
+/* attn_int8_fwd with the variant flags above; arguments, workspace and errors as for
+ * attn_int8_fwd (unknown flag bits are I8A_ERR_INVALID_ARG). */
+i8a_status attn_int8_fwd_ex(const void* q, const void* k, const void* v, void* out, int32_t B,
+                            int32_t Hq, int32_t Hkv, int32_t S, int32_t D, float softmax_scale,
+                            int32_t causal, int32_t flags, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* attn_int8_fwd_ex with flags = I8A_FWD_HADAMARD. */
 i8a_status attn_int8_fwd_hadamard(const void* q, const void* k, const void* v, void* out,
                                   int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D,
                                   float softmax_scale, int32_t causal, void* workspace,
@@ -177,6 +197,14 @@ i8a_status attn_int8_varlen_fwd(const void* q, const void* k, const void* v, voi
                                 int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t D,
                                 float softmax_scale, int32_t causal, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* attn_int8_varlen_fwd with the variant flags of attn_int8_fwd_ex (per sequence: its
+ * own K mean and, with I8A_FWD_V_PER_CHANNEL, its own V channel scales). */
+i8a_status attn_int8_varlen_fwd_ex(const void* q, const void* k, const void* v, void* out,
+                                   const int32_t* cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                                   int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t D,
+                                   float softmax_scale, int32_t causal, int32_t flags,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_int8_debug_qk - debug dump of the quantities the dense forward computes

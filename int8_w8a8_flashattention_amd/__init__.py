@@ -10,6 +10,8 @@ Entry points (same names as the C ABI):
 * :func:`quant_rowwise_i8` - symmetric per-row int8 quantization.
 * :func:`attn_int8_fwd` - dense forward, q ``[B,Hq,S,D]``, k/v ``[B,Hkv,S,D]``.
 * :func:`attn_int8_fwd_hadamard` - the same with Q and K Hadamard-rotated first.
+* :func:`attn_int8_fwd_ex` / :func:`attn_int8_varlen_fwd_ex` - the forwards with variant
+  flags (``FWD_HADAMARD``, ``FWD_V_PER_CHANNEL``).
 * :func:`attn_int8_varlen_fwd` - packed ragged batch, q ``[T,Hq,D]`` + ``cu_seqlens``.
 * :func:`attn_int8_debug_qk` - the forward's exact int32 scores and scales.
 * :func:`attn_int8_kvcache_fill` / :func:`attn_int8_decode` - an int8 KV cache and
@@ -27,8 +29,8 @@ import torch
 
 __all__ = [
     "quant_rowwise_i8", "attn_int8_fwd", "attn_int8_varlen_fwd", "attn_int8_debug_qk",
-    "attn_int8_fwd_hadamard",
-    "attn_int8_prepare_kv", "attn_int8_prepare_q", "attn_int8_attend", "attn_int8_fwd_prepared",
+    "attn_int8_fwd_hadamard", "attn_int8_fwd_ex", "attn_int8_varlen_fwd_ex", "FWD_HADAMARD",
+    "FWD_V_PER_CHANNEL", "attn_int8_prepare_kv", "attn_int8_prepare_q", "attn_int8_attend", "attn_int8_fwd_prepared",
     "attn_int8_workspace_bytes", "attn_int8_varlen_workspace_bytes", "library_path",
     "load_library", "SCALE_FP32", "SCALE_V4", "HEAD_DIMS", "attn_int8_kvcache_bytes",
     "attn_int8_kvcache_fill", "attn_int8_decode_workspace_bytes", "attn_int8_decode",
@@ -42,6 +44,8 @@ _HEADER = os.path.join(os.path.dirname(_HERE), "include", "i8attn.h")
 SCALE_FP32 = 24
 SCALE_V4 = 4
 HEAD_DIMS = (32, 64, 128, 256)
+FWD_HADAMARD = 1
+FWD_V_PER_CHANNEL = 2
 VCACHE_INT8 = 1
 VCACHE_FP16 = 2
 _VFORMATS = {"int8": VCACHE_INT8, "fp16": VCACHE_FP16}
@@ -59,6 +63,11 @@ _SIGS = {
                                                                                  _c_sz, _c_vp]),
     "attn_int8_fwd_hadamard": (_c_i32, [_c_vp] * 4 + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_sz,
                                                                     _c_vp]),
+    "attn_int8_fwd_ex": (_c_i32, [_c_vp] * 4 + [_c_i32] * 5 + [_c_f32, _c_i32, _c_i32, _c_vp, _c_sz,
+                                                              _c_vp]),
+    "attn_int8_varlen_fwd_ex": (_c_i32, [_c_vp] * 5 + [_c_i32, _c_i32, _c_i64, _c_i32, _c_i32,
+                                                        _c_i32, _c_f32, _c_i32, _c_i32, _c_vp, _c_sz,
+                                                        _c_vp]),
     "attn_int8_prepare_kv": (_c_i32, [_c_vp] * 2 + [_c_i32] * 5 + [_c_vp, _c_sz, _c_vp]),
     "attn_int8_prepare_q": (_c_i32, [_c_vp] + [_c_i32] * 5 + [_c_vp, _c_sz, _c_vp]),
     "attn_int8_attend": (_c_i32, [_c_vp] + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_sz, _c_vp]),
@@ -222,6 +231,29 @@ def attn_int8_fwd(q, k, v, causal=True, softmax_scale=None, out=None, workspace=
     return out
 
 
+def attn_int8_fwd_ex(q, k, v, causal=True, flags=0, softmax_scale=None, out=None,
+                     workspace=None):
+    """:func:`attn_int8_fwd` with variant ``flags`` (``FWD_HADAMARD``: Q and K rows
+    Hadamard-rotated before quantization; ``FWD_V_PER_CHANNEL``: V quantized per channel
+    over the tokens); returns fp16 ``out[B,Hq,S,D]``."""
+    B, Hq, Hkv, S, D = _dense_shapes(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_gpu_fp16("out", out, 4)
+        if out.shape != q.shape or out.device != q.device:
+            raise ValueError("out must match q")
+    lib = load_library()
+    nbytes = lib.attn_int8_workspace_bytes(B, Hq, Hkv, S, D)
+    ws = _workspace(workspace, nbytes, q.device)
+    with torch.cuda.device(q.device):
+        st = lib.attn_int8_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, S, D,
+                                  _scale(softmax_scale, D), int(bool(causal)), int(flags),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(q.device))
+    _check(st, "attn_int8_fwd_ex")
+    return out
+
+
 def attn_int8_fwd_hadamard(q, k, v, causal=True, softmax_scale=None, out=None, workspace=None):
     """:func:`attn_int8_fwd` with Q and K rows Hadamard-rotated before quantization (an
     incoherence rotation for outlier channels); returns fp16 ``out[B,Hq,S,D]``."""
@@ -322,6 +354,13 @@ def attn_int8_fwd_prepared(q, Hkv, workspace, causal=True, softmax_scale=None, o
 
 def attn_int8_varlen_fwd(q, k, v, cu_seqlens, max_seqlen, causal=True, softmax_scale=None,
                          out=None, workspace=None):
+    """See :func:`attn_int8_varlen_fwd_ex` (no variant flags)."""
+    return attn_int8_varlen_fwd_ex(q, k, v, cu_seqlens, max_seqlen, causal, 0, softmax_scale,
+                                   out, workspace)
+
+
+def attn_int8_varlen_fwd_ex(q, k, v, cu_seqlens, max_seqlen, causal=True, flags=0,
+                            softmax_scale=None, out=None, workspace=None):
     """Forward over packed sequences: q ``[T,Hq,D]``, k/v ``[T,Hkv,D]``, int32
     ``cu_seqlens[nseq+1]`` on the same GPU; ``max_seqlen`` (host int) bounds
     every sequence length.  Returns fp16 ``out[T,Hq,D]``."""
@@ -349,11 +388,12 @@ def attn_int8_varlen_fwd(q, k, v, cu_seqlens, max_seqlen, causal=True, softmax_s
         raise ValueError("invalid varlen sizes")
     ws = _workspace(workspace, nbytes, q.device)
     with torch.cuda.device(q.device):
-        st = lib.attn_int8_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens),
-                                      nseq, max_seqlen, T, Hq, Hkv, D,
-                                      _scale(softmax_scale, D), int(bool(causal)), _ptr(ws),
-                                      ws.numel() * ws.element_size(), _stream(q.device))
-    _check(st, "attn_int8_varlen_fwd")
+        st = lib.attn_int8_varlen_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens),
+                                         nseq, max_seqlen, T, Hq, Hkv, D,
+                                         _scale(softmax_scale, D), int(bool(causal)), int(flags),
+                                         _ptr(ws), ws.numel() * ws.element_size(),
+                                         _stream(q.device))
+    _check(st, "attn_int8_varlen_fwd_ex")
     return out
 
 

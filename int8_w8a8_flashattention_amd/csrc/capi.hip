@@ -45,6 +45,10 @@ WsPlan plan_workspace(int32_t nseq, int64_t total_tokens, int32_t max_len, int32
   off = align256(off + (size_t)nseq * Hkv * p.npart * D * 8);
   p.off_kmean = off;
   off = align256(off + (size_t)nseq * Hkv * D * 4);
+  p.off_vpart = off;
+  off = align256(off + (size_t)nseq * Hkv * p.npart * D * 4);
+  p.off_svc = off;
+  off = align256(off + (size_t)nseq * Hkv * D * 4);
   p.off_sv = off;
   off = align256(off + (size_t)Hkv * p.Ppad * 4);
   p.off_tiles = off;
@@ -177,17 +181,28 @@ i8a_status attn_int8_fwd(const void* q, const void* k, const void* v, void* out,
   return run_phases(g, PH_KV | PH_Q | PH_ATTN, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
+i8a_status attn_int8_fwd_ex(const void* q, const void* k, const void* v, void* out, int32_t B,
+                            int32_t Hq, int32_t Hkv, int32_t S, int32_t D, float softmax_scale,
+                            int32_t causal, int32_t flags, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  i8a_status st = check_common(q, k, v, out, Hq, Hkv, D, softmax_scale, causal, workspace);
+  if (st != I8A_OK) return st;
+  if (flags & ~(I8A_FWD_HADAMARD | I8A_FWD_V_PER_CHANNEL))
+    return fail(I8A_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (B < 1 || S < 1 || B > kMaxGridYZ)
+    return fail(I8A_ERR_INVALID_ARG, "need 1 <= B <= %d and S >= 1", kMaxGridYZ);
+  if ((int64_t)B * S > kMaxTokens) return fail(I8A_ERR_INVALID_ARG, "B*S too large");
+  FwdGeom g{q, k, v, out, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D, softmax_scale, causal,
+            (flags & I8A_FWD_HADAMARD) ? 1 : 0, (flags & I8A_FWD_V_PER_CHANNEL) ? 1 : 0};
+  return run_phases(g, PH_KV | PH_Q | PH_ATTN, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
 i8a_status attn_int8_fwd_hadamard(const void* q, const void* k, const void* v, void* out,
                                   int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D,
                                   float softmax_scale, int32_t causal, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  i8a_status st = check_common(q, k, v, out, Hq, Hkv, D, softmax_scale, causal, workspace);
-  if (st != I8A_OK) return st;
-  if (B < 1 || S < 1 || B > kMaxGridYZ)
-    return fail(I8A_ERR_INVALID_ARG, "need 1 <= B <= %d and S >= 1", kMaxGridYZ);
-  if ((int64_t)B * S > kMaxTokens) return fail(I8A_ERR_INVALID_ARG, "B*S too large");
-  FwdGeom g{q, k, v, out, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D, softmax_scale, causal, 1};
-  return run_phases(g, PH_KV | PH_Q | PH_ATTN, workspace, workspace_bytes, (hipStream_t)stream);
+  return attn_int8_fwd_ex(q, k, v, out, B, Hq, Hkv, S, D, softmax_scale, causal,
+                          I8A_FWD_HADAMARD, workspace, workspace_bytes, stream);
 }
 
 i8a_status attn_int8_prepare_kv(const void* k, const void* v, int32_t B, int32_t Hq, int32_t Hkv,
@@ -240,11 +255,13 @@ i8a_status attn_int8_fwd_prepared(const void* q, void* out, int32_t B, int32_t H
   return run_phases(g, PH_Q | PH_ATTN, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
-i8a_status attn_int8_varlen_fwd(const void* q, const void* k, const void* v, void* out,
-                                const int32_t* cu_seqlens, int32_t nseq, int32_t max_seqlen,
-                                int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t D,
-                                float softmax_scale, int32_t causal, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+i8a_status attn_int8_varlen_fwd_ex(const void* q, const void* k, const void* v, void* out,
+                                   const int32_t* cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                                   int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t D,
+                                   float softmax_scale, int32_t causal, int32_t flags,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (flags & ~(I8A_FWD_HADAMARD | I8A_FWD_V_PER_CHANNEL))
+    return fail(I8A_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if (!cu_seqlens) return fail(I8A_ERR_INVALID_ARG, "null cu_seqlens");
   if (!aligned(cu_seqlens, 4)) return fail(I8A_ERR_INVALID_ARG, "misaligned cu_seqlens");
   if (nseq < 1 || nseq > kMaxGridYZ)
@@ -263,8 +280,19 @@ i8a_status attn_int8_varlen_fwd(const void* q, const void* k, const void* v, voi
   i8a_status st = check_common(q, k, v, out, Hq, Hkv, D, softmax_scale, causal, workspace);
   if (st != I8A_OK) return st;
   FwdGeom g{q, k, v, out, cu_seqlens, nseq, 0, max_seqlen, total_tokens, Hq, Hkv, D,
-            softmax_scale, causal};
+            softmax_scale, causal, (flags & I8A_FWD_HADAMARD) ? 1 : 0,
+            (flags & I8A_FWD_V_PER_CHANNEL) ? 1 : 0};
   return run_phases(g, PH_KV | PH_Q | PH_ATTN, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+i8a_status attn_int8_varlen_fwd(const void* q, const void* k, const void* v, void* out,
+                                const int32_t* cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                                int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t D,
+                                float softmax_scale, int32_t causal, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return attn_int8_varlen_fwd_ex(q, k, v, out, cu_seqlens, nseq, max_seqlen, total_tokens, Hq,
+                                 Hkv, D, softmax_scale, causal, 0, workspace, workspace_bytes,
+                                 stream);
 }
 
 i8a_status attn_int8_debug_qk(const void* q, const void* k, const void* v, int32_t B, int32_t Hq,

@@ -21,6 +21,8 @@ __host__ __device__ constexpr int tile_bytes(int D) { return TK * D * 3 + TK * 4
 // Workspace carve-up for one forward call.  All offsets are 256-byte aligned.
 //   kpart  int64 [nseq][Hkv][npart][D]   exact K channel sums of tpw tiles (2^-24 units)
 //   kmean  fp32  [nseq][Hkv][D]          K-smoothing means
+//   vpart  fp32  [nseq][Hkv][npart][D]   V channel maxima of tpw tiles (V per channel)
+//   svc    fp32  [nseq][Hkv][D]          V channel scales (V per channel)
 //   sv     fp32  [Hkv][Ppad]             V row scales (kept for the debug dump)
 //   tiles  bytes [Hkv][Ppad / TK][tile_bytes(D)]
 //   q8     int8  [Hq][Qpad / 32][32 * D] Q codes, 32-row blocks in MFMA fragment order
@@ -38,7 +40,7 @@ struct WsPlan {
   int32_t tpw, npart;               // tiles per prep workgroup, partial sums per (seq, head)
   int64_t Ppad;                     // padded K/V token slots per kv head
   int64_t Qpad;                     // padded Q token slots per query head
-  size_t off_kpart, off_kmean, off_sv, off_tiles, off_q8, off_qs, total;
+  size_t off_kpart, off_kmean, off_vpart, off_svc, off_sv, off_tiles, off_q8, off_qs, total;
 };
 
 WsPlan plan_workspace(int32_t nseq, int64_t total_tokens, int32_t max_len, int32_t Hq,
@@ -55,6 +57,7 @@ struct FwdGeom {
   float softmax_scale;
   int causal;
   int rot;  // Q and K rows Hadamard-rotated before quantization (logits take 1/D)
+  int vch;  // V quantized per channel over each sequence's tokens (else per token)
 };
 
 hipError_t launch_quant_rowwise(const void* x, int64_t rows, int32_t d, const float* sub_mean,

@@ -58,16 +58,19 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(
 
 // Launch 1 (workgroup = tpw consecutive tiles of one sequence and kv head): the exact
 // per-channel sums of the tiles' K rows as one int64 partial, in units of 2^-24 (every
-// fp16 value is an integer multiple of 2^-24).
-template <int D>
+// fp16 value is an integer multiple of 2^-24).  With VCH (V quantized per channel),
+// also the per-channel maxima of |v| over the same tokens as one fp32 partial.
+template <int D, bool VCH>
 __global__ __launch_bounds__(256) void prep_ksum_kernel(const _Float16* __restrict__ k,
+                                                        const _Float16* __restrict__ v,
                                                         Act act, Seqs seqs, int Hkv, int npart,
-                                                        int tpw,
-                                                        int64_t* __restrict__ kpart) {
+                                                        int tpw, int64_t* __restrict__ kpart,
+                                                        float* __restrict__ vpart) {
   constexpr int G = D / 8;      // lanes per row
   constexpr int RPP = 256 / G;  // rows per pass
   constexpr int NP = TK / RPP;  // rows per thread and tile
   __shared__ int64_t red[RPP * D];
+  __shared__ float redv[VCH ? RPP * D : 1];
   int b = blockIdx.x;
   const int c = b % npart;
   b /= npart;
@@ -82,51 +85,75 @@ __global__ __launch_bounds__(256) void prep_ksum_kernel(const _Float16* __restri
   const int lc = threadIdx.x % G, rsub = threadIdx.x / G;
 
   int64_t acc[8];
+  float vmx[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0;
+  for (int j = 0; j < 8; ++j) {
+    acc[j] = 0;
+    vmx[j] = 0.0f;
+  }
   for (int tt = tile_lo; tt < tile_hi; ++tt) {
     const int t0 = tt * TK;
-    v8h kr[NP];
+    v8h kr[NP], vr[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int t = t0 + i * RPP + rsub;
-      if (t < L) kr[i] = *reinterpret_cast<const v8h*>(k + act.off(start, g, t) + lc * 8);
+      if (t < L) {
+        kr[i] = *reinterpret_cast<const v8h*>(k + act.off(start, g, t) + lc * 8);
+        if constexpr (VCH) vr[i] = *reinterpret_cast<const v8h*>(v + act.off(start, g, t) + lc * 8);
+      }
     }
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       if (t0 + i * RPP + rsub < L) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] += fp16_fixed24(kr[i][j]);
+        for (int j = 0; j < 8; ++j) {
+          acc[j] += fp16_fixed24(kr[i][j]);
+          if constexpr (VCH) vmx[j] = fmaxf(vmx[j], fabsf((float)vr[i][j]));
+        }
       }
     }
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) red[rsub * D + lc * 8 + j] = acc[j];
+  for (int j = 0; j < 8; ++j) {
+    red[rsub * D + lc * 8 + j] = acc[j];
+    if constexpr (VCH) redv[rsub * D + lc * 8 + j] = vmx[j];
+  }
   __syncthreads();
   if (threadIdx.x < D) {
     int64_t tot = 0;
+    float mx = 0.0f;
 #pragma unroll
-    for (int r = 0; r < RPP; ++r) tot += red[r * D + threadIdx.x];
-    kpart[(((int64_t)s * Hkv + g) * npart + c) * D + threadIdx.x] = tot;
+    for (int r = 0; r < RPP; ++r) {
+      tot += red[r * D + threadIdx.x];
+      if constexpr (VCH) mx = fmaxf(mx, redv[r * D + threadIdx.x]);
+    }
+    const int64_t o = (((int64_t)s * Hkv + g) * npart + c) * D + threadIdx.x;
+    kpart[o] = tot;
+    if constexpr (VCH) vpart[o] = mx;
   }
 }
 
 // Launch 2, V part (workgroup = tpw consecutive tiles of one sequence and kv head): V
-// rows quantized per token with the 4-bit scale rule, written as the exact fp16
-// values sv * code in the V fragment layout.
-//   Phase A: coalesced loads of the tile's V rows; each row's scale and reciprocal;
-//            the raw rows into LDS.
+// quantized with the 4-bit scale rule, per token or (VCH) per channel with the scales
+// from the launch-1 maxima, written as the exact fp16 values scale * code in the V
+// fragment layout.
+//   Phase A: coalesced loads of the tile's V rows; each row's scale and reciprocal
+//            (per token); the raw rows into LDS.
 //   Phase B: each thread assembles whole 16-byte V fragments (8 keys of one channel)
 //            from LDS and stores them with coalesced writes.
 template <int D>
 struct PrepVShared {
   __attribute__((aligned(16))) _Float16 vraw[TK * D];
   float2 rsy[TK];
+  float2 csy[D];
+  float red[256];
 };
 
-template <int D>
+template <int D, bool VCH>
 __device__ __forceinline__ void prep_v_body(const _Float16* __restrict__ v, const Act& act,
-                                            const Seqs& seqs, int tpw, int64_t Ppad,
+                                            const Seqs& seqs, int Hkv, int npart, int tpw,
+                                            int64_t Ppad, const float* __restrict__ vpart,
+                                            float* __restrict__ svc_ws,
                                             float* __restrict__ sv_ws, char* __restrict__ tiles,
                                             int c, int g, int s, PrepVShared<D>& sh) {
   constexpr int G = D / 8;       // lanes per row
@@ -146,6 +173,26 @@ __device__ __forceinline__ void prep_v_body(const _Float16* __restrict__ v, cons
   const int64_t pbase = Seqs::pstart(s, start);
   const int lc = threadIdx.x % G, rsub = threadIdx.x / G;
 
+  if constexpr (VCH) {
+    // The channel maxima of the whole sequence from the launch-1 partials (a max is
+    // exact in any order), then each channel's scale and reciprocal.
+    constexpr int TPC = 256 / D;
+    const int d = threadIdx.x % D, r = threadIdx.x / D;
+    const int np = (nt + tpw - 1) / tpw;
+    const float* pp = vpart + ((int64_t)s * Hkv + g) * npart * D + d;
+    float mx = 0.0f;
+    for (int i = r; i < np; i += TPC) mx = fmaxf(mx, pp[(int64_t)i * D]);
+    sh.red[threadIdx.x] = mx;
+    __syncthreads();
+    if (r == 0) {
+      for (int k2 = 1; k2 < TPC; ++k2) mx = fmaxf(mx, sh.red[k2 * D + d]);
+      const RowQ rq(row_scale(mx, 4));
+      sh.csy[d] = make_float2(rq.s, rq.y);
+      if (c == 0) svc_ws[((int64_t)s * Hkv + g) * D + d] = rq.s;
+    }
+    __syncthreads();
+  }
+
   for (int tt = tile_lo; tt < tile_hi; ++tt) {
     const int t0 = tt * TK;
     v8h vr[NP];
@@ -162,16 +209,18 @@ __device__ __forceinline__ void prep_v_body(const _Float16* __restrict__ v, cons
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int n = i * RPP + rsub, t = t0 + n;
-      const bool real = t < L;
-      float amax = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((float)vr[i][j]));
-      amax = group_max<G>(amax);
       *reinterpret_cast<v8h*>(vraw + n * D + lc * 8) = vr[i];
-      if (lc == 0) {
-        const RowQ rq(real ? row_scale(amax, 4) : 0.0f);
-        rsy[n] = make_float2(rq.s, rq.y);
-        if (real) sv_ws[(int64_t)g * Ppad + pbase + t] = rq.s;
+      if constexpr (!VCH) {
+        const bool real = t < L;
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((float)vr[i][j]));
+        amax = group_max<G>(amax);
+        if (lc == 0) {
+          const RowQ rq(real ? row_scale(amax, 4) : 0.0f);
+          rsy[n] = make_float2(rq.s, rq.y);
+          if (real) sv_ws[(int64_t)g * Ppad + pbase + t] = rq.s;
+        }
       }
     }
     __syncthreads();
@@ -188,11 +237,12 @@ __device__ __forceinline__ void prep_v_body(const _Float16* __restrict__ v, cons
 #pragma unroll
       for (int jv = 0; jv < 8; ++jv) {
         const int n = 16 * kg + (jv < 4 ? 4 * hv + jv : 8 + 4 * hv + (jv - 4));
-        const float2 sy = rsy[n];
+        const float2 sy = VCH ? sh.csy[d] : rsy[n];
         RowQ rq(0.0f);
         rq.s = sy.x;
         rq.y = sy.y;
-        // sv has a 4-bit significand and |code| <= 127: the product is exact in fp16.
+        // The scale has a 4-bit significand and |code| <= 127: the product is exact
+        // in fp16.  (Rows past the sequence end are zero and give 0.)
         frag[jv] = (_Float16)(rq.s * rq.code((float)vraw[n * D + d]));
       }
       dst[f] = frag;
@@ -365,13 +415,14 @@ union PrepShared {
   __attribute__((aligned(16))) int8_t qfrag[QCH * D];
 };
 
-template <int D, bool ROT>
+template <int D, bool ROT, bool VCH>
 __global__ __launch_bounds__(256) void prep_kvq_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
     const _Float16* __restrict__ v, Act aq, Act akv, Seqs seqs, int Hq, int Hkv, int npart,
     int tpw, int64_t Ppad, int64_t Qpad, int nqc, const int64_t* __restrict__ kpart,
-    float* __restrict__ kmean_ws, float* __restrict__ sv_ws, char* __restrict__ tiles,
-    int8_t* __restrict__ q8, float* __restrict__ qs, int nk) {
+    const float* __restrict__ vpart, float* __restrict__ kmean_ws, float* __restrict__ svc_ws,
+    float* __restrict__ sv_ws, char* __restrict__ tiles, int8_t* __restrict__ q8,
+    float* __restrict__ qs, int nk) {
   __shared__ PrepShared<D> sh;
   int b = blockIdx.x;
   if (b < 2 * nk) {
@@ -380,7 +431,8 @@ __global__ __launch_bounds__(256) void prep_kvq_kernel(
     const int c = b % npart;
     b /= npart;
     if (is_v)
-      prep_v_body<D>(v, akv, seqs, tpw, Ppad, sv_ws, tiles, c, b % Hkv, b / Hkv, sh.v);
+      prep_v_body<D, VCH>(v, akv, seqs, Hkv, npart, tpw, Ppad, vpart, svc_ws, sv_ws, tiles, c,
+                          b % Hkv, b / Hkv, sh.v);
     else
       prep_k_body<D, ROT>(k, akv, seqs, Hkv, npart, tpw, Ppad, kpart, kmean_ws, tiles, c, b % Hkv,
                      b / Hkv, sh.k);
@@ -430,10 +482,11 @@ static Act act_of(const FwdGeom& g, int H) {
   return a;
 }
 
-// Launches of the preparation.  With k/v (PH_KV): launch 1 sums K, launch 2 quantizes
-// K and prepares V; with q (PH_Q) the Q rows ride in launch 2.  ROT: the K and Q rows
-// are Hadamard-rotated before they are quantized.
-template <int D, bool ROT>
+// Launches of the preparation.  With k/v (PH_KV): launch 1 sums K (and with VCH takes
+// the V channel maxima), launch 2 quantizes K and prepares V; with q (PH_Q) the Q rows
+// ride in launch 2.  ROT: the K and Q rows are Hadamard-rotated before they are
+// quantized.
+template <int D, bool ROT, bool VCH>
 static hipError_t prep_d(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, bool qq,
                          hipStream_t stream) {
   char* w = static_cast<char*>(ws);
@@ -444,17 +497,20 @@ static hipError_t prep_d(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, b
   const int64_t nq = qq ? (int64_t)nqc * g.Hq * g.nseq : 0;
   if (2 * nk + nq > 0x7fffffff) return hipErrorInvalidValue;
   const _Float16* kp = static_cast<const _Float16*>(g.k);
+  const _Float16* vp = static_cast<const _Float16*>(g.v);
+  float* vpart = reinterpret_cast<float*>(w + p.off_vpart);
   if (kv)
-    prep_ksum_kernel<D><<<dim3((unsigned)nk), 256, 0, stream>>>(
-        kp, akv, sq, g.Hkv, p.npart, p.tpw, reinterpret_cast<int64_t*>(w + p.off_kpart));
+    prep_ksum_kernel<D, VCH><<<dim3((unsigned)nk), 256, 0, stream>>>(
+        kp, vp, akv, sq, g.Hkv, p.npart, p.tpw, reinterpret_cast<int64_t*>(w + p.off_kpart),
+        vpart);
   if (2 * nk + nq > 0)
-    prep_kvq_kernel<D, ROT><<<dim3((unsigned)(2 * nk + nq)), 256, 0, stream>>>(
-        static_cast<const _Float16*>(g.q), kp, static_cast<const _Float16*>(g.v), aq, akv, sq,
-        g.Hq, g.Hkv, p.npart, p.tpw, p.Ppad, p.Qpad, nqc,
-        reinterpret_cast<const int64_t*>(w + p.off_kpart),
-        reinterpret_cast<float*>(w + p.off_kmean), reinterpret_cast<float*>(w + p.off_sv),
-        w + p.off_tiles, reinterpret_cast<int8_t*>(w + p.off_q8),
-        reinterpret_cast<float*>(w + p.off_qs), (int)nk);
+    prep_kvq_kernel<D, ROT, VCH><<<dim3((unsigned)(2 * nk + nq)), 256, 0, stream>>>(
+        static_cast<const _Float16*>(g.q), kp, vp, aq, akv, sq, g.Hq, g.Hkv, p.npart, p.tpw,
+        p.Ppad, p.Qpad, nqc, reinterpret_cast<const int64_t*>(w + p.off_kpart), vpart,
+        reinterpret_cast<float*>(w + p.off_kmean), reinterpret_cast<float*>(w + p.off_svc),
+        reinterpret_cast<float*>(w + p.off_sv), w + p.off_tiles,
+        reinterpret_cast<int8_t*>(w + p.off_q8), reinterpret_cast<float*>(w + p.off_qs),
+        (int)nk);
   return hipGetLastError();
 }
 
@@ -462,10 +518,13 @@ hipError_t launch_prep(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, boo
                        hipStream_t stream) {
   if (g.max_len == 0) return hipSuccess;  // every sequence is empty
   switch (g.D) {
-#define I8A_PREP(DD)                                                       \
-  case DD:                                                                 \
-    return g.rot ? prep_d<DD, true>(g, p, ws, kv, qq, stream)              \
-                 : prep_d<DD, false>(g, p, ws, kv, qq, stream);
+#define I8A_PREP(DD)                                                              \
+  case DD:                                                                        \
+    if (g.vch)                                                                    \
+      return g.rot ? prep_d<DD, true, true>(g, p, ws, kv, qq, stream)             \
+                   : prep_d<DD, false, true>(g, p, ws, kv, qq, stream);           \
+    return g.rot ? prep_d<DD, true, false>(g, p, ws, kv, qq, stream)              \
+                 : prep_d<DD, false, false>(g, p, ws, kv, qq, stream);
     I8A_PREP(32) I8A_PREP(64) I8A_PREP(128) I8A_PREP(256)
 #undef I8A_PREP
     default: return hipErrorInvalidValue;
@@ -486,8 +545,8 @@ hipError_t launch_ksum_dense(const void* k, int32_t B, int32_t Hkv, int32_t S, i
   switch (D) {
 #define I8A_KS(DD)                                                                      \
   case DD:                                                                              \
-    prep_ksum_kernel<DD><<<dim3((unsigned)nb), 256, 0, stream>>>(kp, a, sq, Hkv, npart, \
-                                                                 tpw, kpart);           \
+    prep_ksum_kernel<DD, false><<<dim3((unsigned)nb), 256, 0, stream>>>(             \
+        kp, nullptr, a, sq, Hkv, npart, tpw, kpart, nullptr);                           \
     break;
     I8A_KS(32) I8A_KS(64) I8A_KS(128) I8A_KS(256)
 #undef I8A_KS

@@ -156,3 +156,10 @@ def test_python_binding_validates_before_the_library():
         i8.quant_rowwise_i8(x)  # CPU tensor
     with pytest.raises(ValueError):
         i8.attn_int8_fwd(x.view(1, 1, 4, 64), x.view(1, 1, 4, 64), x.view(1, 1, 4, 64))
+
+
+def test_forward_ex_rejects_unknown_flags(lib):
+    st = lib.attn_int8_fwd_ex(FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 64, 64, 0.125, 1, 4, FAKE,
+                              1 << 40, None)
+    assert st == INVALID
+    assert b"flags" in lib.i8a_last_error()
