@@ -14,6 +14,9 @@ The method it defines comes from the "SuperL8" README (the page titled
   (ragged, non-tile-multiple) prefill.
 * *Attention kernels* table, row ``attn_decode``: split-KV decode with an int8
   KV cache, in its int8-V and fp16-V variants (one query token per sequence).
+* *Attention kernels* table, row ``attn_bwd``, and the *Infrastructure* table's
+  autograd row: the backward of the differentiable int8 attention (gradient of exact
+  attention, the quantization taken as the identity).
 * *Supporting kernels* table, row ``quant_rowwise``: symmetric per-row int8
   quantization.
 * *Quantization* table, rows "Per-row int8" (symmetric, K-smoothing) and
@@ -50,3 +53,4 @@ from .attn_ref import (  # noqa: F401
     attn_int8_varlen_fwd,
     attn_exact,
 )
+from .attn_bwd import attn_bwd_exact  # noqa: F401

@@ -571,3 +571,74 @@ def test_v_per_channel_varlen_scales_per_sequence():
         tr = lambda x: np.ascontiguousarray(x[a:b].transpose(1, 0, 2))[None]
         ref = oracle.attn_int8_fwd(tr(w.q), tr(w.k), tr(w.v), True, v_per_channel=True)[0]
         assert np.array_equal(out[a:b], ref.transpose(1, 0, 2))
+
+
+# ---------------------------------------------------------------- backward (R17)
+
+def _autograd_grads(w, do, causal, scale=None):
+    # torch's CPU fp64 autograd through its own attention (library routine)
+    q = torch.tensor(w.q, dtype=torch.float64, requires_grad=True)
+    k = torch.tensor(w.k, dtype=torch.float64, requires_grad=True)
+    v = torch.tensor(w.v, dtype=torch.float64, requires_grad=True)
+    G = q.shape[1] // k.shape[1]
+    s = float(oracle.default_softmax_scale(q.shape[-1])) if scale is None else float(np.float32(scale))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        q, k.repeat_interleave(G, dim=1), v.repeat_interleave(G, dim=1), is_causal=causal, scale=s)
+    o.backward(torch.tensor(do, dtype=torch.float64))
+    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("Hq,Hkv,S,D", [(2, 2, 17, 32), (4, 2, 40, 64), (3, 1, 9, 16)])
+def test_bwd_equals_torch_autograd(Hq, Hkv, S, D, causal):
+    w = workloads.dense(67 + S, 2, Hq, Hkv, S, D, causal, k_offset=1.0)
+    do = rng(68).standard_normal(w.q.shape).astype(np.float16)
+    got = oracle.attn_bwd_exact(w.q, w.k, w.v, do, causal)
+    want = _autograd_grads(w, do, causal)
+    for g, r in zip(got, want):
+        np.testing.assert_allclose(g, r, rtol=1e-10, atol=1e-12)
+
+
+def test_bwd_finite_differences():
+    # Gradient check: the directional derivative of <dO, O(q, k, v)> along a random
+    # direction equals <grad, direction>, by central differences in fp64.
+    w = workloads.dense(69, 1, 2, 1, 12, 16, True)
+    do = rng(70).standard_normal(w.q.shape)
+    q, k, v = (x.astype(np.float64) for x in (w.q, w.k, w.v))
+    dq, dk, dv = oracle.attn_bwd_exact(w.q, w.k, w.v, do, True)
+    s = float(oracle.default_softmax_scale(16))
+
+    def loss(qq, kk, vv):
+        out = 0.0
+        for h in range(2):
+            lg = s * qq[0, h] @ kk[0, 0].T
+            lg = np.where(np.tril(np.ones((12, 12), bool)), lg, -np.inf)
+            p = np.exp(lg - lg.max(1, keepdims=True))
+            p /= p.sum(1, keepdims=True)
+            out += np.sum(do[0, h] * (p @ vv[0, 0]))
+        return out
+    g = rng(71)
+    eq, ek, ev = (g.standard_normal(x.shape) for x in (q, k, v))
+    eps = 1e-6
+    fd = (loss(q + eps * eq, k + eps * ek, v + eps * ev)
+          - loss(q - eps * eq, k - eps * ek, v - eps * ev)) / (2 * eps)
+    an = np.sum(dq * eq) + np.sum(dk * ek) + np.sum(dv * ev)
+    assert abs(fd - an) <= 1e-7 * max(1.0, abs(an))
+
+
+def test_bwd_uniform_attention_closed_form():
+    # q = 0: every row attends uniformly (non-causal, P_ij = 1/S), so dV_j is the mean
+    # of the dO rows, dK_j = s * sum_i dS_ij q_i = 0, and
+    # dQ_i = s * sum_j (dP_ij - mean_j dP_ij) k_j / S with dP = dO V^T.
+    w = workloads.dense(72, 1, 1, 1, 10, 8, False)
+    q = np.zeros_like(w.q)
+    do = rng(73).standard_normal(w.q.shape).astype(np.float16)
+    dq, dk, dv = oracle.attn_bwd_exact(q, w.k, w.v, do, False)
+    np.testing.assert_allclose(dv[0, 0], np.repeat(do[0, 0].astype(np.float64).sum(0, keepdims=True) / 10, 10, 0),
+                               rtol=1e-13, atol=1e-14)
+    assert np.all(np.abs(dk) < 1e-15)
+    vv, kk, dd = w.v[0, 0].astype(np.float64), w.k[0, 0].astype(np.float64), do[0, 0].astype(np.float64)
+    dp = dd @ vv.T
+    dsc = (dp - dp.mean(1, keepdims=True)) / 10
+    np.testing.assert_allclose(dq[0, 0], float(oracle.default_softmax_scale(8)) * dsc @ kk,
+                               rtol=1e-12, atol=1e-14)
