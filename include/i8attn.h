@@ -286,6 +286,37 @@ i8a_status attn_int8_decode(const void* q, void* out, int32_t B, int32_t Hq, int
                             const void* cache, size_t cache_bytes, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/*
+ * Backward (SuperL8 README, Attention kernels table, row attn_bwd: a gradient-checked
+ * backward pass on full fp16 state; Infrastructure table, autograd row: int8 attention
+ * made differentiable).  The quantization of the forward has zero derivative almost
+ * everywhere and is taken as the identity (straight-through), so the backward is the
+ * gradient of exact attention O = softmax(s Q K^T + mask) V at the fp16 inputs:
+ *   dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,  dS = P * (dP - D),
+ *   dQ = s dS K,  dK = s dS^T Q,
+ * with dK, dV of a kv head summed over the query heads that read it (GQA).  It runs in
+ * O(S) memory (P is recomputed tile by tile from each row's log-sum-exp); every
+ * product is an fp16 MFMA with fp32 accumulation, P and dS rounded to fp16 as operands.
+ *
+ * attn_bwd_workspace_bytes - workspace for attn_bwd (0 if the sizes are invalid): the
+ * fp16 inputs in MFMA operand orders and two fp32 values per query row.
+ */
+size_t attn_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D);
+
+/*
+ * attn_bwd - gradients of the attention.
+ *   q, dout  fp16 [B, Hq, S, D]      k, v  fp16 [B, Hkv, S, D]   (16-byte aligned)
+ *   dq       fp32 [B, Hq, S, D] out  dk, dv  fp32 [B, Hkv, S, D] out (16-byte aligned)
+ *   1 <= B <= 65535, S >= 1, B*S <= 2^30, 1 <= Hkv <= Hq <= 65535, Hq % Hkv == 0,
+ *   D in {32, 64, 128} (256 is I8A_ERR_UNSUPPORTED_HEAD_DIM here).
+ *   softmax_scale, causal as for attn_int8_fwd; workspace of attn_bwd_workspace_bytes
+ *   bytes, 256-byte aligned, needs no initialization.  Outputs alias no input.
+ */
+i8a_status attn_bwd(const void* q, const void* k, const void* v, const void* dout, float* dq,
+                    float* dk, float* dv, int32_t B, int32_t Hq, int32_t Hkv, int32_t S,
+                    int32_t D, float softmax_scale, int32_t causal, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 /* Name of a status code (static string). */
 const char* i8a_status_string(i8a_status status);
 

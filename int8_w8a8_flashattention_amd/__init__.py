@@ -16,6 +16,9 @@ Entry points (same names as the C ABI):
 * :func:`attn_int8_debug_qk` - the forward's exact int32 scores and scales.
 * :func:`attn_int8_kvcache_fill` / :func:`attn_int8_decode` - an int8 KV cache and
   split-KV decode of one query token per sequence against it.
+* :func:`attn_bwd` - the backward (gradients of the attention, the quantization taken
+  as the identity); :class:`Int8Attention` / :func:`int8_attention` - the forward as a
+  ``torch.autograd.Function`` with that backward.
 """
 
 from __future__ import annotations
@@ -34,7 +37,8 @@ __all__ = [
     "attn_int8_workspace_bytes", "attn_int8_varlen_workspace_bytes", "library_path",
     "load_library", "SCALE_FP32", "SCALE_V4", "HEAD_DIMS", "attn_int8_kvcache_bytes",
     "attn_int8_kvcache_fill", "attn_int8_decode_workspace_bytes", "attn_int8_decode",
-    "VCACHE_INT8", "VCACHE_FP16",
+    "VCACHE_INT8", "VCACHE_FP16", "attn_bwd", "attn_bwd_workspace_bytes", "Int8Attention",
+    "int8_attention",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -78,6 +82,8 @@ _SIGS = {
     "attn_int8_decode_workspace_bytes": (_c_sz, [_c_i32] * 6),
     "attn_int8_decode": (_c_i32, [_c_vp] * 2 + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_sz,
                                                                _c_vp, _c_sz, _c_vp]),
+    "attn_bwd_workspace_bytes": (_c_sz, [_c_i32] * 5),
+    "attn_bwd": (_c_i32, [_c_vp] * 7 + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_sz, _c_vp]),
     "i8a_status_string": (ctypes.c_char_p, [_c_i32]),
     "i8a_last_error": (ctypes.c_char_p, []),
 }
@@ -498,3 +504,54 @@ def attn_int8_decode(q, cache, softmax_scale=None, out=None, workspace=None):
                                   _stream(q.device))
     _check(st, "attn_int8_decode")
     return out
+
+
+def attn_bwd_workspace_bytes(B, Hq, Hkv, S, D) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(B, Hq, Hkv, S, D))
+
+
+def attn_bwd(q, k, v, dout, causal=True, softmax_scale=None, workspace=None):
+    """Gradients ``(dq, dk, dv)`` (fp32, shapes of q, k, v) of the attention for the
+    output gradient ``dout [B,Hq,S,D]`` (fp16); the quantization of the forward is taken
+    as the identity."""
+    B, Hq, Hkv, S, D = _dense_shapes(q, k, v)
+    _need_gpu_fp16("dout", dout, 4)
+    if dout.shape != q.shape or dout.device != q.device:
+        raise ValueError("dout must match q")
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    lib = load_library()
+    nbytes = lib.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D)
+    if nbytes == 0:
+        raise ValueError(f"backward sizes not supported (D={D} must be 32, 64 or 128)")
+    ws = _workspace(workspace, nbytes, q.device)
+    with torch.cuda.device(q.device):
+        st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                          B, Hq, Hkv, S, D, _scale(softmax_scale, D), int(bool(causal)),
+                          _ptr(ws), ws.numel() * ws.element_size(), _stream(q.device))
+    _check(st, "attn_bwd")
+    return dq, dk, dv
+
+
+class Int8Attention(torch.autograd.Function):
+    """The int8 attention forward (:func:`attn_int8_fwd`) with the backward of
+    :func:`attn_bwd` (gradients in the inputs' fp16)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal=True, softmax_scale=None):
+        ctx.save_for_backward(q, k, v)
+        ctx.causal, ctx.softmax_scale = causal, softmax_scale
+        return attn_int8_fwd(q, k, v, causal, softmax_scale)
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v = ctx.saved_tensors
+        dq, dk, dv = attn_bwd(q, k, v, dout.contiguous().to(torch.float16), ctx.causal,
+                              ctx.softmax_scale)
+        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None
+
+
+def int8_attention(q, k, v, causal=True, softmax_scale=None):
+    """Differentiable int8 attention: :class:`Int8Attention` applied to fp16 q, k, v."""
+    return Int8Attention.apply(q, k, v, causal, softmax_scale)

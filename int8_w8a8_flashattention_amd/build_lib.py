@@ -17,7 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libi8attn.so")
-SOURCES = ["quant_kernels.hip", "attn_kernels.hip", "decode_kernels.hip", "capi.hip"]
+SOURCES = ["quant_kernels.hip", "attn_kernels.hip", "decode_kernels.hip", "bwd_kernels.hip",
+           "capi.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -404,4 +404,42 @@ i8a_status attn_int8_decode(const void* q, void* out, int32_t B, int32_t Hq, int
   return I8A_OK;
 }
 
+static bool bwd_sizes_ok(int32_t B, int32_t Hq, int32_t Hkv, int32_t S) {
+  return B >= 1 && B <= kMaxGridYZ && S >= 1 && (int64_t)B * S <= kMaxTokens && Hkv >= 1 &&
+         Hq >= Hkv && Hq <= kMaxGridYZ && Hq % Hkv == 0;
+}
+
+size_t attn_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D) {
+  if (!bwd_sizes_ok(B, Hq, Hkv, S) || (D != 32 && D != 64 && D != 128)) return 0;
+  return plan_bwd(B, Hq, Hkv, S, D).total;
+}
+
+i8a_status attn_bwd(const void* q, const void* k, const void* v, const void* dout, float* dq,
+                    float* dk, float* dv, int32_t B, int32_t Hq, int32_t Hkv, int32_t S,
+                    int32_t D, float softmax_scale, int32_t causal, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !dout || !dq || !dk || !dv)
+    return fail(I8A_ERR_INVALID_ARG, "null input or output pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return fail(I8A_ERR_INVALID_ARG, "inputs and outputs must be 16-byte aligned");
+  if (D != 32 && D != 64 && D != 128)
+    return fail(I8A_ERR_UNSUPPORTED_HEAD_DIM, "backward head dim %d not in {32,64,128}", D);
+  if (!bwd_sizes_ok(B, Hq, Hkv, S))
+    return fail(I8A_ERR_INVALID_ARG, "bad sizes B=%d Hq=%d Hkv=%d S=%d", B, Hq, Hkv, S);
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale))
+    return fail(I8A_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (causal != 0 && causal != 1) return fail(I8A_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!workspace || !aligned(workspace, 256))
+    return fail(I8A_ERR_INVALID_ARG, "workspace must be non-null and 256-byte aligned");
+  const BwdPlan p = plan_bwd(B, Hq, Hkv, S, D);
+  if (workspace_bytes < p.total)
+    return fail(I8A_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", p.total,
+                workspace_bytes);
+  BwdArgs a{q, k, v, dout, dq, dk, dv, B, Hq, Hkv, S, D, softmax_scale, causal};
+  hipError_t e = launch_bwd(a, p, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return I8A_OK;
+}
+
 }  // extern "C"

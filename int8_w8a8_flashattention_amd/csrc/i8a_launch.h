@@ -125,4 +125,24 @@ hipError_t launch_decode(const void* q, void* out, int32_t Hq, float softmax_sca
                          const KvcPlan& p, const DecPlan& dp, const void* cache, void* ws,
                          hipStream_t stream);
 
+// ----------------------------------------------------------------------------------
+// Backward.  Workspace (256-byte aligned pieces), Sp = 32 * nrb tokens per head:
+//   qr, qc, dor, doc  fp16 [B][Hq][Sp][D]   Q and dO in row and column fragment order
+//   kr, kc, vr        fp16 [B][Hkv][Sp][D]  K (both orders) and V (row order)
+//   lse, dvec         fp32 [B][Hq][S rounded up to 128]   row log2-sum-exp and D
+struct BwdPlan {
+  int32_t nrb;
+  size_t off_qr, off_qc, off_dor, off_doc, off_kr, off_kc, off_vr, off_lse, off_dvec, total;
+};
+BwdPlan plan_bwd(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D);
+
+struct BwdArgs {
+  const void *q, *k, *v, *dout;
+  float *dq, *dk, *dv;
+  int32_t B, Hq, Hkv, S, D;
+  float softmax_scale;
+  int causal;
+};
+hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, void* ws, hipStream_t stream);
+
 }  // namespace i8a
