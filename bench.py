@@ -32,6 +32,9 @@ Hadamard-rotated, with V per channel, and with both) on the same workload and re
 each one's quality (SQNR against unquantized attention) on the outlier-channel
 workload next to the plain forward's.
 
+The ``backward`` object times ``attn_bwd`` (the gradients of the attention, the
+quantization taken as the identity) on the same workload against the fp16 MFMA peak.
+
 Only one GPU is used: ``--gpus`` above 1 exits with a message.
 """
 
@@ -291,6 +294,60 @@ def bench_variants(args, i8, torch, dev, q, k, v, out, ws, ms_step):
     return res
 
 
+def bench_backward(args, i8, torch, dev, q, k, v):
+    """The backward (NEXT-4) on the same workload: one attn_bwd call per step (operand
+    preparation, dQ kernel, dK/dV kernel).  Its roofline is the fp16 MFMA: algorithmic
+    flops = 10 * D per (query, key) pair (five products of 2 * D: the recomputed scores,
+    dP, dV, dK and dQ; the FlashAttention-2 count), S^2/2 pairs per causal head."""
+    import numpy as np
+
+    B, Hq, S, D = q.shape
+    do = torch.from_numpy(np.random.Generator(np.random.PCG64(214)).standard_normal(
+        tuple(q.shape)).astype(np.float16)).to(dev)
+    ws = torch.empty(i8.attn_bwd_workspace_bytes(B, Hq, k.shape[1], S, D), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def step():
+        i8.attn_bwd(q, k, v, do, True, workspace=ws)
+
+    for _ in range(max(args.warmup // 4, 5)):
+        step()
+    torch.cuda.synchronize()
+    n = max(args.steps // 2, 5)
+    e0.record(stream)
+    for _ in range(n):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    flops = 10.0 * D * Hq * B * S * S / 2.0
+    tf = flops / (us * 1e-6) / 1e12
+    log(f"bench: backward {us:.1f} us/call, {tf:.1f} TFLOP/s")
+    return {"call_us": round(us, 2), "algorithmic_flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP16_PEAK_TOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / FP16_PEAK_TOPS, 4),
+                         "traffic": None},
+            "note": "fp32 dq, dk, dv; the quantization taken as the identity; the "
+                    "implementation computes the scores and dP three times per pair "
+                    "(18 D flops per pair), the roofline counts the algorithmic 10 D"}
+
+
+def profile_backward(n, i8, torch, dev):
+    """Profiling mode: n backward calls on the causal GQA workload."""
+    import numpy as np
+    from int8_w8a8_flashattention_amd import workloads
+    w = workloads.cfg2()
+    q, k, v = (torch.from_numpy(a).to(dev) for a in (w.q, w.k, w.v))
+    do = torch.from_numpy(np.random.Generator(np.random.PCG64(214)).standard_normal(
+        w.q.shape).astype(np.float16)).to(dev)
+    for _ in range(n):
+        i8.attn_bwd(q, k, v, do, True)
+    torch.cuda.synchronize()
+    log(f"bench: {n} backward calls")
+
+
 def profile_decode(n, i8, torch, dev):
     """Profiling mode: fill the int8-V cache once, then n decode calls."""
     from int8_w8a8_flashattention_amd import workloads
@@ -325,6 +382,8 @@ def main():
     ap.add_argument("--profile-decode", type=int, default=0, metavar="N",
                     help="profiling mode: fill the decode cache once, then N decode calls")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--profile-bwd", type=int, default=0, metavar="N",
+                    help="profiling mode: N backward calls on the causal GQA workload")
     ap.add_argument("--profile-copy", type=int, default=0, metavar="MIB",
                     help="profiling mode: 10 plain device copies of MIB MiB (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -347,6 +406,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.profile_decode:
         profile_decode(args.profile_decode, i8, torch, dev)
+        return
+    if args.profile_bwd:
+        profile_backward(args.profile_bwd, i8, torch, dev)
         return
     w = workloads.cfg2()
     B, Hq, Hkv, S, D = (WORKLOAD[k] for k in ("B", "Hq", "Hkv", "S", "D"))
@@ -493,6 +555,7 @@ def main():
         log(f"bench: timing the CPU oracle (~{args.cpu_budget:.0f} s)")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     res["variants"] = bench_variants(args, i8, torch, dev, q, k, v, out, ws, ms_step)
+    res["backward"] = bench_backward(args, i8, torch, dev, q, k, v)
     if not args.no_decode:
         del q, k, v, out, ws
         res["decode"] = bench_decode(args, i8, torch, dev)

@@ -19,9 +19,11 @@
 //     rows, so that a result (P or dS) is the B operand of the next product as it is.
 // Launch 2 (bwd_dq_kernel, lane = query): sweep 1 over the keys gives each row's
 //   log-sum-exp and D; sweep 2 recomputes P and dS and accumulates dQ^T = K^T dS^T.
-// Launch 3 (bwd_dkdv_kernel, lane = key): four waves take the group's query heads in
-//   turn for the same 32 keys and accumulate dV^T = dO^T P and dK^T = Q^T dS; the
-//   waves' sums are added in LDS.
+// Launch 3 (bwd_dkdv_kernel, lane = key): each wave owns 32 keys and accumulates
+//   dV^T = dO^T P and dK^T = Q^T dS over every query block of every query head of its
+//   kv head.
+// Both main kernels stream their operand tiles through LDS rings shared by the four
+// waves of a workgroup (direct-to-LDS copies one block ahead).
 #include <float.h>
 
 #include "i8a_device.h"
@@ -128,39 +130,84 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const _Float16* __restric
 }
 
 // ----------------------------------------------------------------------------------
+// Copy of one 32-token operand tile (64 * D contiguous bytes) into LDS by the four waves
+// of a workgroup with direct-to-LDS loads: wave w's lanes move the 16-byte chunks
+// 256 r + 64 w + lane.
+template <int D>
+__device__ __forceinline__ void wg_copy_tile(const char* __restrict__ src, char* dst, int tid) {
+  constexpr int NCH = 64 * D / 16;
+  const int w = tid >> 6;
+  const uint32_t base = lds_addr(dst);
+#pragma unroll
+  for (int r = 0; r * 256 < NCH; ++r) {
+    if (r * 256 + w * 64 < NCH) {  // wave-uniform
+      const int chunk = r * 256 + tid;
+      if (chunk < NCH) lds_dma16(src + (int64_t)chunk * 16, base + (r * 256 + w * 64) * 16);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------
 // Launch 2: dQ.  Workgroup = 4 waves = 128 queries of one (batch, query head); wave w
-// owns queries q0 = 128 * blockIdx.x + 32 w .. +31, lane l query q0 + l % 32.
+// owns queries q0 = 128 * blockIdx.x + 32 w .. +31, lane l query q0 + l % 32.  The key
+// blocks' operand tiles (K and V in row order, K in column order) stream through a
+// two-stage LDS ring shared by the four waves, one block ahead.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(
     const _Float16* __restrict__ qr, const _Float16* __restrict__ dor,
     const _Float16* __restrict__ kr, const _Float16* __restrict__ kc,
     const _Float16* __restrict__ vr, float* __restrict__ lse2, float* __restrict__ dvec,
     float* __restrict__ dq, int Hq, int Hkv, int S, int nrb, float c_log2, float scale) {
-  constexpr int NKD = D / 16, NDB = D / 32;
+  constexpr int NKD = D / 16, NDB = D / 32, TB = 64 * D;  // TB: bytes of a 32-token tile
+  __shared__ __attribute__((aligned(16))) char smem[2 * 3 * TB];
   const int h = blockIdx.y, b = blockIdx.z;
   const int g = h / (Hq / Hkv);
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63, m = lane & 31, hh = lane >> 5;
-  const int q0 = 128 * blockIdx.x + 32 * w;
-  if (q0 >= nrb * 32) return;  // a wave entirely in the padding of the last block
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, m = lane & 31, hh = lane >> 5;
+  const int qblk0 = 128 * blockIdx.x;
+  const int q0 = qblk0 + 32 * w;
+  const bool active = q0 < nrb * 32;  // waves past the padded length only copy
   const int64_t Sp = (int64_t)nrb * 32;
   const int64_t qbase = ((int64_t)b * Hq + h) * Sp;
   const int64_t kbase = ((int64_t)b * Hkv + g) * Sp;
-  const v8h* qf_src = reinterpret_cast<const v8h*>(qr + (qbase + q0) * D);
-  const v8h* df_src = reinterpret_cast<const v8h*>(dor + (qbase + q0) * D);
-  v8h qf[NKD], df[NKD];
-#pragma unroll
-  for (int kd = 0; kd < NKD; ++kd) {
-    qf[kd] = qf_src[kd * 64 + lane];
-    df[kd] = df_src[kd * 64 + lane];
-  }
+  const char* krb = reinterpret_cast<const char*>(kr + kbase * D);
+  const char* vrb = reinterpret_cast<const char*>(vr + kbase * D);
+  const char* kcb = reinterpret_cast<const char*>(kc + kbase * D);
+  const int nkb_wg = CAUSAL ? min(nrb, qblk0 / 32 + 4) : nrb;  // key blocks of the group
+  const int nkb = CAUSAL ? q0 / 32 + 1 : nrb;                  // this wave's
   const int qi = q0 + m;
-  const int nkb = CAUSAL ? q0 / 32 + 1 : nrb;
 
-  // S^T (keys x queries) and dP^T of key block kb, scaled and masked scores in t.
-  auto scores = [&](int kb, float (&t)[16], v16f& dp) {
-    const v8h* ka = reinterpret_cast<const v8h*>(kr + (kbase + 32 * kb) * D);
-    const v8h* va = reinterpret_cast<const v8h*>(vr + (kbase + 32 * kb) * D);
+  v8h qf[NKD], df[NKD];
+  if (active) {
+    const v8h* qs = reinterpret_cast<const v8h*>(qr + (qbase + q0) * D);
+    const v8h* ds = reinterpret_cast<const v8h*>(dor + (qbase + q0) * D);
+#pragma unroll
+    for (int kd = 0; kd < NKD; ++kd) {
+      qf[kd] = qs[kd * 64 + lane];
+      df[kd] = ds[kd * 64 + lane];
+    }
+  } else {
+#pragma unroll
+    for (int kd = 0; kd < NKD; ++kd)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qf[kd][j] = df[kd][j] = (_Float16)0.0f;
+  }
+  // Consumed here, so that the compiler waits for these loads before the loops (a wait
+  // at their first use inside a loop would also wait for the tile copies).
+#pragma unroll
+  for (int kd = 0; kd < NKD; ++kd) asm volatile("" : : "v"(qf[kd]), "v"(df[kd]));
+
+  auto issue = [&](int kb, int st, bool with_kc) {
+    wg_copy_tile<D>(krb + (int64_t)kb * TB, smem + (st * 3 + 0) * TB, tid);
+    wg_copy_tile<D>(vrb + (int64_t)kb * TB, smem + (st * 3 + 1) * TB, tid);
+    if (with_kc) wg_copy_tile<D>(kcb + (int64_t)kb * TB, smem + (st * 3 + 2) * TB, tid);
+  };
+  // S^T (keys x queries) and dP^T of key block kb from LDS stage st; scaled, masked
+  // scores in t.
+  auto scores = [&](int kb, int st, float (&t)[16], v16f& dp) {
+    const v8h* ka = reinterpret_cast<const v8h*>(smem + (st * 3 + 0) * TB);
+    const v8h* va = reinterpret_cast<const v8h*>(smem + (st * 3 + 1) * TB);
     v16f sc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.0f;
@@ -179,32 +226,40 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 
   // Sweep 1: running max, sum and sum of p * dP (log2 units).
   float mr = -INFINITY, l = 0.0f, a = 0.0f;
-  for (int kb = 0; kb < nkb; ++kb) {
-    float t[16];
-    v16f dp;
-    scores(kb, t, dp);
-    float mt = t[0];
+  issue(0, 0, false);
+  vm_wait<0>();
+  __syncthreads();
+  for (int kb = 0; kb < nkb_wg; ++kb) {
+    if (kb + 1 < nkb_wg) issue(kb + 1, (kb + 1) & 1, false);
+    if (active && kb < nkb) {
+      float t[16];
+      v16f dp;
+      scores(kb, kb & 1, t, dp);
+      float mt = t[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mt = bmax(mt, t[i]);
-    const float mn = bmax(mr, half_max(mt));
-    const float al = mr == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr - mn);
-    const float mu = mn == -INFINITY ? 0.0f : mn;
-    l *= al;
-    a *= al;
+      for (int i = 1; i < 16; ++i) mt = bmax(mt, t[i]);
+      const float mn = bmax(mr, half_max(mt));
+      const float al = mr == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr - mn);
+      const float mu = mn == -INFINITY ? 0.0f : mn;
+      l *= al;
+      a *= al;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(t[i] - mu);
-      l += p;
-      a = __builtin_fmaf(p, dp[i], a);
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(t[i] - mu);
+        l += p;
+        a = __builtin_fmaf(p, dp[i], a);
+      }
+      mr = mn;
     }
-    mr = mn;
+    vm_wait<0>();
+    __syncthreads();
   }
   l = half_sum(l);
   a = half_sum(a);
   // Every row has a visible key (key 0), so l > 0 and mr is finite.
-  const float lse = mr + log2f(l);
-  const float Dv = a / l;
-  if (hh == 0) {
+  const float lse = active ? mr + log2f(l) : 0.0f;
+  const float Dv = active ? a / l : 0.0f;
+  if (active && hh == 0) {
     lse2[qbase + qi] = lse;
     dvec[qbase + qi] = Dv;
   }
@@ -215,24 +270,32 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
-  for (int kb = 0; kb < nkb; ++kb) {
-    float t[16];
-    v16f dp;
-    scores(kb, t, dp);
-    v8h ds[2];
+  issue(0, 0, true);
+  vm_wait<0>();
+  __syncthreads();
+  for (int kb = 0; kb < nkb_wg; ++kb) {
+    if (kb + 1 < nkb_wg) issue(kb + 1, (kb + 1) & 1, true);
+    if (active && kb < nkb) {
+      float t[16];
+      v16f dp;
+      scores(kb, kb & 1, t, dp);
+      v8h ds[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(t[i] - lse);
-      ds[i >> 3][i & 7] = (_Float16)(p * (dp[i] - Dv));
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(t[i] - lse);
+        ds[i >> 3][i & 7] = (_Float16)(p * (dp[i] - Dv));
+      }
+      const v8h* kca = reinterpret_cast<const v8h*>(smem + ((kb & 1) * 3 + 2) * TB);
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          acc[db] = mfma16(kca[(gg * NDB + db) * 64 + lane], ds[gg], acc[db]);
     }
-    const v8h* kca = reinterpret_cast<const v8h*>(kc + (kbase + 32 * kb) * D);
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        acc[db] = mfma16(kca[(gg * NDB + db) * 64 + lane], ds[gg], acc[db]);
+    vm_wait<0>();
+    __syncthreads();
   }
-  if (qi < S) {
+  if (active && qi < S) {
     float* orow = dq + (((int64_t)b * Hq + h) * S + qi) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -247,9 +310,11 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 }
 
 // ----------------------------------------------------------------------------------
-// Launch 3: dK and dV.  Workgroup = 4 waves on the 32 keys k0 = 32 * blockIdx.x .. +31
-// of one (batch, kv head); wave w takes the group's query heads w, w + 4, ...; lane l
-// holds key k0 + l % 32.  The waves' partial dK^T, dV^T are added in LDS at the end.
+// Launch 3: dK and dV.  Workgroup = 4 waves on 128 keys of one (batch, kv head); wave w
+// owns keys k0 = 128 * blockIdx.x + 32 w .. +31, lane l key k0 + l % 32, and sums the
+// contributions of all the group's query heads itself.  The query blocks' operand tiles
+// (Q and dO in row and column order) stream through a two-stage LDS ring shared by the
+// four waves, one block ahead.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const _Float16* __restrict__ qr, const _Float16* __restrict__ qc,
@@ -257,37 +322,78 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const _Float16* __restrict__ kr, const _Float16* __restrict__ vr,
     const float* __restrict__ lse2, const float* __restrict__ dvec, float* __restrict__ dk,
     float* __restrict__ dv, int Hq, int Hkv, int S, int nrb, float c_log2, float scale) {
-  constexpr int NKD = D / 16, NDB = D / 32;
-  __shared__ float red[32 * D];
+  constexpr int NKD = D / 16, NDB = D / 32, TB = 64 * D;
+  __shared__ __attribute__((aligned(16))) char smem[2 * 4 * TB];
   const int g = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63, m = lane & 31, hh = lane >> 5;
-  const int k0 = 32 * blockIdx.x;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, m = lane & 31, hh = lane >> 5;
+  const int kblk0 = 128 * blockIdx.x;
+  const int k0 = kblk0 + 32 * w;
+  const bool active = k0 < nrb * 32;
   const int64_t Sp = (int64_t)nrb * 32;
   const int64_t kbase = ((int64_t)b * Hkv + g) * Sp;
-  const v8h* kf_src = reinterpret_cast<const v8h*>(kr + (kbase + k0) * D);
-  const v8h* vf_src = reinterpret_cast<const v8h*>(vr + (kbase + k0) * D);
-  v8h kf[NKD], vf[NKD];
-#pragma unroll
-  for (int kd = 0; kd < NKD; ++kd) {
-    kf[kd] = kf_src[kd * 64 + lane];
-    vf[kd] = vf_src[kd * 64 + lane];
-  }
   const int kj = k0 + m;
+
+  v8h kf[NKD], vf[NKD];
+  if (active) {
+    const v8h* ks = reinterpret_cast<const v8h*>(kr + (kbase + k0) * D);
+    const v8h* vs = reinterpret_cast<const v8h*>(vr + (kbase + k0) * D);
+#pragma unroll
+    for (int kd = 0; kd < NKD; ++kd) {
+      kf[kd] = ks[kd * 64 + lane];
+      vf[kd] = vs[kd * 64 + lane];
+    }
+  } else {
+#pragma unroll
+    for (int kd = 0; kd < NKD; ++kd)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kf[kd][j] = vf[kd][j] = (_Float16)0.0f;
+  }
+#pragma unroll
+  for (int kd = 0; kd < NKD; ++kd) asm volatile("" : : "v"(kf[kd]), "v"(vf[kd]));
+
   v16f accv[NDB], acck[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) accv[db][i] = acck[db][i] = 0.0f;
 
-  const int qb0 = CAUSAL ? k0 / 32 : 0;
-  for (int hg = w; hg < G; hg += 4) {
-    const int h = g * G + hg;
-    const int64_t qbase = ((int64_t)b * Hq + h) * Sp;
-    for (int qb = qb0; qb < nrb; ++qb) {
-      const v8h* qa = reinterpret_cast<const v8h*>(qr + (qbase + 32 * qb) * D);
-      const v8h* da = reinterpret_cast<const v8h*>(dor + (qbase + 32 * qb) * D);
+  // Work items of the group: (query head, query block) pairs, query blocks from the
+  // first one that reaches the group's first key (causal) to the end.
+  const int qb0 = CAUSAL ? kblk0 / 32 : 0;
+  const int nqb = nrb - qb0;
+  const int nitem = G * nqb;
+  auto item_base = [&](int it, int64_t& qbase, int& qb) {
+    const int hg = it / nqb;
+    qb = qb0 + it % nqb;
+    qbase = ((int64_t)b * Hq + g * G + hg) * Sp;
+  };
+  auto issue = [&](int it, int st) {
+    int64_t qbase;
+    int qb;
+    item_base(it, qbase, qb);
+    const int64_t off = (qbase + 32 * (int64_t)qb) * D * 2;
+    wg_copy_tile<D>(reinterpret_cast<const char*>(qr) + off, smem + (st * 4 + 0) * TB, tid);
+    wg_copy_tile<D>(reinterpret_cast<const char*>(dor) + off, smem + (st * 4 + 1) * TB, tid);
+    wg_copy_tile<D>(reinterpret_cast<const char*>(qc) + off, smem + (st * 4 + 2) * TB, tid);
+    wg_copy_tile<D>(reinterpret_cast<const char*>(doc) + off, smem + (st * 4 + 3) * TB, tid);
+  };
+
+  issue(0, 0);
+  vm_wait<0>();
+  __syncthreads();
+  for (int it = 0; it < nitem; ++it) {
+    if (it + 1 < nitem) issue(it + 1, (it + 1) & 1);
+    int64_t qbase;
+    int qb;
+    item_base(it, qbase, qb);
+    // A block whose last query precedes this wave's first key contributes nothing.
+    if (active && (!CAUSAL || 32 * qb + 31 >= k0)) {
+      const int st = it & 1;
+      const v8h* qa = reinterpret_cast<const v8h*>(smem + (st * 4 + 0) * TB);
+      const v8h* da = reinterpret_cast<const v8h*>(smem + (st * 4 + 1) * TB);
       v16f sc, dp;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.0f;
@@ -312,8 +418,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
           ds16[i >> 3][i & 7] = (_Float16)(p * (dp[i] - dv4[r]));
         }
       }
-      const v8h* dca = reinterpret_cast<const v8h*>(doc + (qbase + 32 * qb) * D);
-      const v8h* qca = reinterpret_cast<const v8h*>(qc + (qbase + 32 * qb) * D);
+      const v8h* dca = reinterpret_cast<const v8h*>(smem + (st * 4 + 3) * TB);
+      const v8h* qca = reinterpret_cast<const v8h*>(smem + (st * 4 + 2) * TB);
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
@@ -322,33 +428,27 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
           acck[db] = mfma16(qca[(gg * NDB + db) * 64 + lane], ds16[gg], acck[db]);
         }
     }
+    vm_wait<0>();
+    __syncthreads();
   }
 
-  // Sum of the four waves: dV^T, then dK^T, through red[key][d] (wave 0 stores, the
-  // others add in turn).
-  auto reduce_store = [&](v16f (&acc)[NDB], float* out, float mul) {
+  if (active && kj < S) {
+    float* vrow = dv + (((int64_t)b * Hkv + g) * S + kj) * D;
+    float* krow = dk + (((int64_t)b * Hkv + g) * S + kj) * D;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      if (w == ww) {
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+      for (int J = 0; J < 4; ++J) {
+        v4f v4, k4;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int d = 32 * db + 8 * (i >> 2) + 4 * hh + (i & 3);
-            float* cell = red + m * D + d;
-            *cell = ww == 0 ? acc[db][i] : *cell + acc[db][i];
-          }
+        for (int r = 0; r < 4; ++r) {
+          v4[r] = accv[db][4 * J + r];
+          k4[r] = acck[db][4 * J + r] * scale;
+        }
+        *reinterpret_cast<v4f*>(vrow + 32 * db + 8 * J + 4 * hh) = v4;
+        *reinterpret_cast<v4f*>(krow + 32 * db + 8 * J + 4 * hh) = k4;
       }
-      __syncthreads();
-    }
-    for (int e = threadIdx.x; e < 32 * D; e += 256) {
-      const int key = k0 + e / D;
-      if (key < S) out[(((int64_t)b * Hkv + g) * S + key) * D + e % D] = red[e] * mul;
-    }
-    __syncthreads();
-  };
-  reduce_store(accv, dv, 1.0f);
-  reduce_store(acck, dk, scale);
+  }
 }
 
 // ----------------------------------------------------------------------------------
@@ -394,7 +494,7 @@ static hipError_t bwd_d(const BwdArgs& a, const BwdPlan& p, char* ws, hipStream_
       a.Hkv, a.S, p.nrb, c_log2, a.softmax_scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bwd_dkdv_kernel<D, C><<<dim3((unsigned)p.nrb, a.Hkv, a.B), 256, 0, stream>>>(
+  bwd_dkdv_kernel<D, C><<<dim3((unsigned)((p.nrb + 3) / 4), a.Hkv, a.B), 256, 0, stream>>>(
       H(p.off_qr), H(p.off_qc), H(p.off_dor), H(p.off_doc), H(p.off_kr), H(p.off_vr), lse,
       dvec, a.dk, a.dv, a.Hq, a.Hkv, a.S, p.nrb, c_log2, a.softmax_scale);
   return hipGetLastError();
