@@ -275,7 +275,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
   __syncthreads();
   for (int kb = 0; kb < nkb_wg; ++kb) {
     if (kb + 1 < nkb_wg) issue(kb + 1, (kb + 1) & 1, true);
-    if (active && kb < nkb) {
+    // Unconditional, as in the dK/dV kernel: past this wave's last key block every score
+    // is masked and dS is zero.
+    {
       float t[16];
       v16f dp;
       scores(kb, kb & 1, t, dp);
@@ -323,7 +325,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const float* __restrict__ lse2, const float* __restrict__ dvec, float* __restrict__ dk,
     float* __restrict__ dv, int Hq, int Hkv, int S, int nrb, float c_log2, float scale) {
   constexpr int NKD = D / 16, NDB = D / 32, TB = 64 * D;
-  __shared__ __attribute__((aligned(16))) char smem[2 * 4 * TB];
+  // A stage: Q and dO in row order, Q and dO in column order, then the block's 32 row
+  // log-sum-exps and 32 D values.
+  constexpr int SB = 4 * TB + 256;
+  __shared__ __attribute__((aligned(16))) char smem[2 * SB];
   const int g = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
   const int tid = threadIdx.x;
@@ -375,10 +380,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     int qb;
     item_base(it, qbase, qb);
     const int64_t off = (qbase + 32 * (int64_t)qb) * D * 2;
-    wg_copy_tile<D>(reinterpret_cast<const char*>(qr) + off, smem + (st * 4 + 0) * TB, tid);
-    wg_copy_tile<D>(reinterpret_cast<const char*>(dor) + off, smem + (st * 4 + 1) * TB, tid);
-    wg_copy_tile<D>(reinterpret_cast<const char*>(qc) + off, smem + (st * 4 + 2) * TB, tid);
-    wg_copy_tile<D>(reinterpret_cast<const char*>(doc) + off, smem + (st * 4 + 3) * TB, tid);
+    char* stg = smem + st * SB;
+    wg_copy_tile<D>(reinterpret_cast<const char*>(qr) + off, stg + 0 * TB, tid);
+    wg_copy_tile<D>(reinterpret_cast<const char*>(dor) + off, stg + 1 * TB, tid);
+    wg_copy_tile<D>(reinterpret_cast<const char*>(qc) + off, stg + 2 * TB, tid);
+    wg_copy_tile<D>(reinterpret_cast<const char*>(doc) + off, stg + 3 * TB, tid);
+    // The row statistics ride in the same stage (16 lanes of wave 0, 16 bytes each), so
+    // the loop holds no load the compiler tracks: a wait it placed for one would also
+    // wait for the next block's copy.
+    if (tid < 16) {
+      const float* src = (tid < 8 ? lse2 : dvec) + qbase + 32 * qb + 4 * (tid & 7);
+      lds_dma16(src, lds_addr(stg + 4 * TB));
+    }
   };
 
   issue(0, 0);
@@ -389,11 +402,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     int64_t qbase;
     int qb;
     item_base(it, qbase, qb);
-    // A block whose last query precedes this wave's first key contributes nothing.
-    if (active && (!CAUSAL || 32 * qb + 31 >= k0)) {
-      const int st = it & 1;
-      const v8h* qa = reinterpret_cast<const v8h*>(smem + (st * 4 + 0) * TB);
-      const v8h* da = reinterpret_cast<const v8h*>(smem + (st * 4 + 1) * TB);
+    // Unconditional (a block whose last query precedes this wave's first key, or a
+    // wave past the padded length, adds exact zeros or is never written): a skip here
+    // would give every accumulator two incoming values at the loop's join, which the
+    // register allocator resolves with copies of all of them on every block.
+    {
+      const char* stg = smem + (it & 1) * SB;
+      const v8h* qa = reinterpret_cast<const v8h*>(stg + 0 * TB);
+      const v8h* da = reinterpret_cast<const v8h*>(stg + 1 * TB);
+      const float* lrow = reinterpret_cast<const float*>(stg + 4 * TB);
       v16f sc, dp;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.0f;
@@ -407,8 +424,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
         const int qrow = 32 * qb + 8 * J + 4 * hh;
-        const v4f lv = *reinterpret_cast<const v4f*>(lse2 + qbase + qrow);
-        const v4f dv4 = *reinterpret_cast<const v4f*>(dvec + qbase + qrow);
+        const v4f lv = *reinterpret_cast<const v4f*>(lrow + 8 * J + 4 * hh);
+        const v4f dv4 = *reinterpret_cast<const v4f*>(lrow + 32 + 8 * J + 4 * hh);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 4 * J + r;
@@ -418,8 +435,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
           ds16[i >> 3][i & 7] = (_Float16)(p * (dp[i] - dv4[r]));
         }
       }
-      const v8h* dca = reinterpret_cast<const v8h*>(smem + (st * 4 + 3) * TB);
-      const v8h* qca = reinterpret_cast<const v8h*>(smem + (st * 4 + 2) * TB);
+      const v8h* dca = reinterpret_cast<const v8h*>(stg + 3 * TB);
+      const v8h* qca = reinterpret_cast<const v8h*>(stg + 2 * TB);
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
