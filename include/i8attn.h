@@ -299,7 +299,8 @@ i8a_status attn_int8_decode(const void* q, void* out, int32_t B, int32_t Hq, int
  * product is an fp16 MFMA with fp32 accumulation, P and dS rounded to fp16 as operands.
  *
  * attn_bwd_workspace_bytes - workspace for attn_bwd (0 if the sizes are invalid): the
- * fp16 inputs in MFMA operand orders and two fp32 values per query row.
+ * fp16 inputs in MFMA operand orders, two fp32 values per query row, and partial dK and
+ * dV (fp32, the size of dk and dv) for the causal mask's split of the key groups.
  */
 size_t attn_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D);
 

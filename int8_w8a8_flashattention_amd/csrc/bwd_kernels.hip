@@ -20,10 +20,12 @@
 // Launch 2 (bwd_dq_kernel, lane = query): sweep 1 over the keys gives each row's
 //   log-sum-exp and D; sweep 2 recomputes P and dS and accumulates dQ^T = K^T dS^T.
 // Launch 3 (bwd_dkdv_kernel, lane = key): each wave owns 32 keys and accumulates
-//   dV^T = dO^T P and dK^T = Q^T dS over every query block of every query head of its
-//   kv head.
+//   dV^T = dO^T P and dK^T = Q^T dS over the query blocks of the query heads of its kv
+//   head; under the causal mask each group of 128 keys is split over two workgroups.
+// Launch 4 (bwd_combine_kernel, causal only): adds the second workgroup's partial sums.
 // Both main kernels stream their operand tiles through LDS rings shared by the four
-// waves of a workgroup (direct-to-LDS copies one block ahead).
+// waves of a workgroup (direct-to-LDS copies ahead of use).  No atomics are used: the
+// results do not depend on the order in which workgroups run.
 #include <float.h>
 
 #include "i8a_device.h"
@@ -147,6 +149,15 @@ __device__ __forceinline__ void wg_copy_tile(const char* __restrict__ src, char*
   }
 }
 
+// Number of 16-byte copies that wave w issues per tile in wg_copy_tile<D>.
+template <int D>
+__host__ __device__ constexpr int tile_dma_count(int w) {
+  int n = 0;
+  for (int r = 0; r * 256 < 4 * D; ++r)
+    if (r * 256 + w * 64 < 4 * D) ++n;
+  return n;
+}
+
 // ----------------------------------------------------------------------------------
 // Launch 2: dQ.  Workgroup = 4 waves = 128 queries of one (batch, query head); wave w
 // owns queries q0 = 128 * blockIdx.x + 32 w .. +31, lane l query q0 + l % 32.  The key
@@ -157,15 +168,17 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
     const _Float16* __restrict__ qr, const _Float16* __restrict__ dor,
     const _Float16* __restrict__ kr, const _Float16* __restrict__ kc,
     const _Float16* __restrict__ vr, float* __restrict__ lse2, float* __restrict__ dvec,
-    float* __restrict__ dq, int Hq, int Hkv, int S, int nrb, float c_log2, float scale) {
+    float* __restrict__ dq, int B, int Hq, int Hkv, int S, int nrb, float c_log2, float scale) {
   constexpr int NKD = D / 16, NDB = D / 32, TB = 64 * D;  // TB: bytes of a 32-token tile
   __shared__ __attribute__((aligned(16))) char smem[2 * 3 * TB];
-  const int h = blockIdx.y, b = blockIdx.z;
+  // blockIdx.x = ((query block of 128, from the last) x B + batch) x Hq + head: under
+  // the causal mask the heaviest blocks of every head are dispatched first.
+  const int h = blockIdx.x % Hq, b = (blockIdx.x / Hq) % B;
   const int g = h / (Hq / Hkv);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, m = lane & 31, hh = lane >> 5;
-  const int qblk0 = 128 * blockIdx.x;
+  const int qblk0 = 128 * ((nrb + 3) / 4 - 1 - (int)(blockIdx.x / Hq / B));
   const int q0 = qblk0 + 32 * w;
   const bool active = q0 < nrb * 32;  // waves past the padded length only copy
   const int64_t Sp = (int64_t)nrb * 32;
@@ -312,29 +325,39 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 }
 
 // ----------------------------------------------------------------------------------
-// Launch 3: dK and dV.  Workgroup = 4 waves on 128 keys of one (batch, kv head); wave w
-// owns keys k0 = 128 * blockIdx.x + 32 w .. +31, lane l key k0 + l % 32, and sums the
-// contributions of all the group's query heads itself.  The query blocks' operand tiles
-// (Q and dO in row and column order) stream through a two-stage LDS ring shared by the
-// four waves, one block ahead.
+// Launch 3: dK and dV.  Workgroup = 4 waves on a group of 128 keys of one (batch, kv
+// head); wave w owns keys k0 = kblk0 + 32 w .. +31, lane l key k0 + l % 32, and sums the
+// contributions of the group's query heads itself.  The work items are (query head,
+// query block) pairs; under the causal mask the group's items are dealt alternately to
+// two workgroups (part 0 writes dK and dV, part 1 partial sums that the combine kernel
+// adds).  The items' operand tiles (Q and dO in row and column order, with the rows'
+// statistics) stream through LDS rings shared by the four waves, three items ahead, and
+// each step is software-pipelined (see the loop).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const _Float16* __restrict__ qr, const _Float16* __restrict__ qc,
     const _Float16* __restrict__ dor, const _Float16* __restrict__ doc,
     const _Float16* __restrict__ kr, const _Float16* __restrict__ vr,
     const float* __restrict__ lse2, const float* __restrict__ dvec, float* __restrict__ dk,
-    float* __restrict__ dv, int Hq, int Hkv, int S, int nrb, float c_log2, float scale) {
+    float* __restrict__ dv, float* __restrict__ pk, float* __restrict__ pv, int B, int Hq,
+    int Hkv, int S, int nrb, int nsplit, float c_log2, float scale) {
   constexpr int NKD = D / 16, NDB = D / 32, TB = 64 * D;
-  // A stage: Q and dO in row order, Q and dO in column order, then the block's 32 row
-  // log-sum-exps and 32 D values.
-  constexpr int SB = 4 * TB + 256;
-  __shared__ __attribute__((aligned(16))) char smem[2 * SB];
-  const int g = blockIdx.y, b = blockIdx.z;
+  // Two rings: row stages (Q and dO in row order), read one step before their item's
+  // step, and column stages (Q and dO in column order, then the block's 32 row
+  // log-sum-exps and 32 D values), read at their item's step and the next.
+  constexpr int NR = 4, NC = 5, RB = 2 * TB, CB = 2 * TB + 256;
+  __shared__ __attribute__((aligned(16))) char smem[NR * RB + NC * CB];
+  char* const rring = smem;
+  char* const cring = smem + NR * RB;
+  // blockIdx.x = ((key group of 128 x nsplit + part) x B + batch) x Hkv + kv head: the
+  // heaviest groups under the causal mask are dispatched first.
+  const int g = blockIdx.x % Hkv, b = (blockIdx.x / Hkv) % B;
+  const int part = (blockIdx.x / Hkv / B) % nsplit;
   const int G = Hq / Hkv;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, m = lane & 31, hh = lane >> 5;
-  const int kblk0 = 128 * blockIdx.x;
+  const int kblk0 = 128 * (int)(blockIdx.x / Hkv / B / nsplit);
   const int k0 = kblk0 + 32 * w;
   const bool active = k0 < nrb * 32;
   const int64_t Sp = (int64_t)nrb * 32;
@@ -369,89 +392,207 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   // first one that reaches the group's first key (causal) to the end.
   const int qb0 = CAUSAL ? kblk0 / 32 : 0;
   const int nqb = nrb - qb0;
-  const int nitem = G * nqb;
+  // Items in the order j = 0, 1, ...: query blocks from the last one down, the group's
+  // query heads inside, so that the workgroups of a kv head, which all start at the last
+  // block, read the same tiles at about the same time and share them in L2.  Part p of
+  // nsplit takes the items j = p (mod nsplit).
+  const int nitem = (G * nqb - part + nsplit - 1) / nsplit;
+  if (nitem == 0) return;
   auto item_base = [&](int it, int64_t& qbase, int& qb) {
-    const int hg = it / nqb;
-    qb = qb0 + it % nqb;
-    qbase = ((int64_t)b * Hq + g * G + hg) * Sp;
+    const int j = part + it * nsplit;
+    qb = nrb - 1 - j / G;
+    qbase = ((int64_t)b * Hq + g * G + j % G) * Sp;
   };
-  auto issue = [&](int it, int st) {
+  // Copies of item it into its row and column stages.  Every wave issues
+  // 4 tile_dma_count<D>(w) + 1 copies per item (the statistics: 4 lanes of each wave).
+  auto issue = [&](int it) {
     int64_t qbase;
     int qb;
     item_base(it, qbase, qb);
     const int64_t off = (qbase + 32 * (int64_t)qb) * D * 2;
-    char* stg = smem + st * SB;
-    wg_copy_tile<D>(reinterpret_cast<const char*>(qr) + off, stg + 0 * TB, tid);
-    wg_copy_tile<D>(reinterpret_cast<const char*>(dor) + off, stg + 1 * TB, tid);
-    wg_copy_tile<D>(reinterpret_cast<const char*>(qc) + off, stg + 2 * TB, tid);
-    wg_copy_tile<D>(reinterpret_cast<const char*>(doc) + off, stg + 3 * TB, tid);
-    // The row statistics ride in the same stage (16 lanes of wave 0, 16 bytes each), so
-    // the loop holds no load the compiler tracks: a wait it placed for one would also
-    // wait for the next block's copy.
-    if (tid < 16) {
-      const float* src = (tid < 8 ? lse2 : dvec) + qbase + 32 * qb + 4 * (tid & 7);
-      lds_dma16(src, lds_addr(stg + 4 * TB));
+    char* rs = rring + (it & (NR - 1)) * RB;
+    char* cs = cring + (it % NC) * CB;
+    wg_copy_tile<D>(reinterpret_cast<const char*>(qr) + off, rs, tid);
+    wg_copy_tile<D>(reinterpret_cast<const char*>(dor) + off, rs + TB, tid);
+    wg_copy_tile<D>(reinterpret_cast<const char*>(qc) + off, cs, tid);
+    wg_copy_tile<D>(reinterpret_cast<const char*>(doc) + off, cs + TB, tid);
+    // The row statistics ride in the column stage, so the loop holds no load the
+    // compiler tracks: a wait it placed for one would also wait for later copies.
+    if (lane < 4) {
+      const int c = 4 * w + lane;
+      const float* src = (c < 8 ? lse2 : dvec) + qbase + 32 * qb + 4 * (c & 7);
+      lds_dma16(src, lds_addr(cs + 2 * TB + 16 * c));
     }
   };
+  // Wait for every copy but, if `one_ahead`, the last item's (at most: the count is wave
+  // 3's, the smallest).
+  auto wait_copies = [&](bool one_ahead) {
+    if (one_ahead)
+      vm_wait<4 * tile_dma_count<D>(3) + 1>();
+    else
+      vm_wait<0>();
+  };
 
-  issue(0, 0);
-  vm_wait<0>();
-  __syncthreads();
-  for (int it = 0; it < nitem; ++it) {
-    if (it + 1 < nitem) issue(it + 1, (it + 1) & 1);
-    int64_t qbase;
-    int qb;
-    item_base(it, qbase, qb);
-    // Unconditional (a block whose last query precedes this wave's first key, or a
-    // wave past the padded length, adds exact zeros or is never written): a skip here
-    // would give every accumulator two incoming values at the loop's join, which the
-    // register allocator resolves with copies of all of them on every block.
-    {
-      const char* stg = smem + (it & 1) * SB;
-      const v8h* qa = reinterpret_cast<const v8h*>(stg + 0 * TB);
-      const v8h* da = reinterpret_cast<const v8h*>(stg + 1 * TB);
-      const float* lrow = reinterpret_cast<const float*>(stg + 4 * TB);
-      v16f sc, dp;
+  // Block it's S^T and dP^T (keys x queries) from its Q and dO row tiles.
+  auto scores = [&](int it, v16f& sc, v16f& dp) {
+    const char* stg = rring + (it & (NR - 1)) * RB;
+    const v8h* qa = reinterpret_cast<const v8h*>(stg);
+    const v8h* da = reinterpret_cast<const v8h*>(stg + TB);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.0f;
+    for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.0f;
 #pragma unroll
-      for (int kd = 0; kd < NKD; ++kd) {
-        sc = mfma16(qa[kd * 64 + lane], kf[kd], sc);
-        dp = mfma16(da[kd * 64 + lane], vf[kd], dp);
-      }
-      // Register i holds query 32 qb + 8 (i / 4) + 4 hh + i % 4.
-      v8h p16[2], ds16[2];
-#pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        const int qrow = 32 * qb + 8 * J + 4 * hh;
-        const v4f lv = *reinterpret_cast<const v4f*>(lrow + 8 * J + 4 * hh);
-        const v4f dv4 = *reinterpret_cast<const v4f*>(lrow + 32 + 8 * J + 4 * hh);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 4 * J + r;
-          const bool dead = CAUSAL && kj > qrow + r;
-          const float p = dead ? 0.0f : __builtin_amdgcn_exp2f(sc[i] * c_log2 - lv[r]);
-          p16[i >> 3][i & 7] = (_Float16)p;
-          ds16[i >> 3][i & 7] = (_Float16)(p * (dp[i] - dv4[r]));
-        }
-      }
-      const v8h* dca = reinterpret_cast<const v8h*>(stg + 3 * TB);
-      const v8h* qca = reinterpret_cast<const v8h*>(stg + 2 * TB);
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          accv[db] = mfma16(dca[(gg * NDB + db) * 64 + lane], p16[gg], accv[db]);
-          acck[db] = mfma16(qca[(gg * NDB + db) * 64 + lane], ds16[gg], acck[db]);
-        }
+    for (int kd = 0; kd < NKD; ++kd) {
+      sc = mfma16(qa[kd * 64 + lane], kf[kd], sc);
+      dp = mfma16(da[kd * 64 + lane], vf[kd], dp);
     }
+  };
+  // Element e (register e: query 32 qb + 8 (e / 4) + 4 hh + e % 4) of block it's P^T
+  // and dS^T, from its score, its dP and its row's statistics (lv, dv4 from the stage).
+  auto prob = [&](int e, int qb, float s, float d, const v4f (&lv)[4], const v4f (&dv4)[4],
+                  v8h (&p16)[2], v8h (&ds16)[2]) {
+    const int J = e >> 2, r = e & 3;
+    // Empty statements that take the inputs and give the results at this point of the
+    // step: the arithmetic stays in the slot where the fences put it.
+    asm volatile("" : "+v"(s), "+v"(d));
+    float p = __builtin_amdgcn_exp2f(s * c_log2 - lv[J][r]);
+    if (CAUSAL) p = kj > 32 * qb + 8 * J + 4 * hh + r ? 0.0f : p;
+    const float ds = p * (d - dv4[J][r]);
+    asm volatile("" : : "v"(p), "v"(ds));
+    p16[e >> 3][e & 7] = (_Float16)p;
+    ds16[e >> 3][e & 7] = (_Float16)ds;
+  };
+  auto stats = [&](int it, v4f (&lv)[4], v4f (&dv4)[4]) {
+    const float* lrow = reinterpret_cast<const float*>(cring + (it % NC) * CB + 2 * TB);
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      lv[J] = *reinterpret_cast<const v4f*>(lrow + 8 * J + 4 * hh);
+      dv4[J] = *reinterpret_cast<const v4f*>(lrow + 32 + 8 * J + 4 * hh);
+    }
+  };
+  auto item_qb = [&](int it) { return nrb - 1 - (part + it * nsplit) / G; };
+  // dV^T += dO^T P^T and dK^T += Q^T dS^T for block it, from its column tiles.
+  auto accumulate = [&](int it, const v8h (&p16)[2], const v8h (&ds16)[2]) {
+    const char* stg = cring + (it % NC) * CB;
+    const v8h* dca = reinterpret_cast<const v8h*>(stg + TB);
+    const v8h* qca = reinterpret_cast<const v8h*>(stg);
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        accv[db] = mfma16(dca[(gg * NDB + db) * 64 + lane], p16[gg], accv[db]);
+        acck[db] = mfma16(qca[(gg * NDB + db) * 64 + lane], ds16[gg], acck[db]);
+      }
+  };
+
+  // Software pipeline over the work items: step it runs the dV/dK products of item
+  // it - 1, the score products of item it + 1 and the softmax arithmetic of item it, none
+  // of which waits for another.  The copy of item it + 3 starts at step it and has two
+  // steps to land: into the row stage that item it - 1 left at step it - 2 and the column
+  // stage that item it - 2 left at step it - 1.  Every block is processed by every wave
+  // (a block the causal mask empties adds exact zeros; a wave past the padded length is
+  // never written): skipping one would give each accumulator two incoming values at the
+  // loop's join, which the register allocator resolves with copies of all of them.
+  issue(0);
+  if (nitem > 1) issue(1);
+  if (nitem > 2) issue(2);
+  wait_copies(nitem > 2);
+  __syncthreads();
+  if (nitem > 3) issue(3);
+  v16f sc, dp;
+  scores(0, sc, dp);
+  v8h p16[2], ds16[2];
+  {
+    v16f sn, dn;
+    scores(min(1, nitem - 1), sn, dn);
+    v4f lv[4], dv4[4];
+    stats(0, lv, dv4);
+    const int qb = item_qb(0);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) prob(e, qb, sc[e], dp[e], lv, dv4, p16, ds16);
+    sc = sn;
+    dp = dn;
+  }
+  wait_copies(nitem > 3);
+  __syncthreads();
+  constexpr int NP = D / 8;       // products of each kind per step
+  auto step = [&](int it) {
+    const char* stp = cring + ((it - 1) % NC) * CB;
+    const char* stn = rring + (min(it + 1, nitem - 1) & (NR - 1)) * RB;
+    v8h aop[NP];
+#pragma unroll
+    for (int x = 0; x < NP; ++x) {
+      const int gg = x / (2 * NDB), db = (x >> 1) % NDB;
+      const v8h* src = reinterpret_cast<const v8h*>(stp + ((x & 1) ? 0 : 1) * TB);
+      aop[x] = src[(gg * NDB + db) * 64 + lane];
+    }
+    v4f lv[4], dv4[4];
+    stats(it, lv, dv4);
+    const int qb = item_qb(it);
+    float scv[16], dpv[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      scv[e] = sc[e];
+      dpv[e] = dp[e];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    v8h pn[2], dsn[2], sop[NP];
+    v16f sn, dn;
+#pragma unroll
+    for (int x = 0; x < 2 * NP; ++x) {
+      if (x < NP) {
+        const int gg = x / (2 * NDB), db = (x >> 1) % NDB;
+        if (x & 1)
+          acck[db] = mfma16(aop[x], ds16[gg], acck[db]);
+        else
+          accv[db] = mfma16(aop[x], p16[gg], accv[db]);
+        const v8h* src = reinterpret_cast<const v8h*>(stn + ((x & 1) ? 1 : 0) * TB);
+        sop[x] = src[(x >> 1) * 64 + lane];
+      } else {
+        const int y = x - NP;
+        if (y < 2) {
+          if (y & 1)
+            dn = mfma16(sop[y], vf[y >> 1], v16f{});
+          else
+            sn = mfma16(sop[y], kf[y >> 1], v16f{});
+        } else {
+          if (y & 1)
+            dn = mfma16(sop[y], vf[y >> 1], dn);
+          else
+            sn = mfma16(sop[y], kf[y >> 1], sn);
+        }
+      }
+#pragma unroll
+      for (int e = x * 16 / (2 * NP); e < (x + 1) * 16 / (2 * NP); ++e)
+        prob(e, qb, scv[e], dpv[e], lv, dv4, pn, dsn);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    sc = sn;
+    dp = dn;
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg) {
+      p16[gg] = pn[gg];
+      ds16[gg] = dsn[gg];
+    }
+  };
+  // Steps with a copy to start (its wait leaves that copy in flight), then the last three.
+  int it = 1;
+  for (; it + 3 < nitem; ++it) {
+    issue(it + 3);
+    step(it);
+    wait_copies(true);
+    __syncthreads();
+  }
+  for (; it < nitem; ++it) {
+    step(it);
     vm_wait<0>();
     __syncthreads();
   }
+  accumulate(nitem - 1, p16, ds16);
 
   if (active && kj < S) {
-    float* vrow = dv + (((int64_t)b * Hkv + g) * S + kj) * D;
-    float* krow = dk + (((int64_t)b * Hkv + g) * S + kj) * D;
+    // Part 0 writes the outputs, part 1 its partial sums (added by bwd_combine_kernel).
+    float* vrow = (part == 0 ? dv : pv) + (((int64_t)b * Hkv + g) * S + kj) * D;
+    float* krow = (part == 0 ? dk : pk) + (((int64_t)b * Hkv + g) * S + kj) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -466,6 +607,23 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         *reinterpret_cast<v4f*>(krow + 32 * db + 8 * J + 4 * hh) = k4;
       }
   }
+}
+
+// ----------------------------------------------------------------------------------
+// Launch 4 (under the causal mask): dK += partial dK, dV += partial dV of the second
+// part of every key group, in that order (n4 float4 per tensor).
+__global__ __launch_bounds__(256) void bwd_combine_kernel(float* __restrict__ dk,
+                                                          float* __restrict__ dv,
+                                                          const float* __restrict__ pk,
+                                                          const float* __restrict__ pv,
+                                                          int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 * n4) return;
+  const bool isv = i >= n4;
+  const int64_t j = isv ? i - n4 : i;
+  v4f* o = reinterpret_cast<v4f*>(isv ? dv : dk) + j;
+  const v4f p = reinterpret_cast<const v4f*>(isv ? pv : pk)[j];
+  *o = *o + p;
 }
 
 // ----------------------------------------------------------------------------------
@@ -487,14 +645,26 @@ BwdPlan plan_bwd(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D) {
   p.off_vr = off; off = align256b(off + kbytes);
   p.off_lse = off; off = align256b(off + (size_t)B * Hq * S128 * 4);
   p.off_dvec = off; off = align256b(off + (size_t)B * Hq * S128 * 4);
+  // Partial dK and dV of the second part of each key group (causal calls).
+  const size_t obytes = (size_t)B * Hkv * S * D * 4;
+  p.off_pk = off; off = align256b(off + obytes);
+  p.off_pv = off; off = align256b(off + obytes);
   p.total = off;
   return p;
 }
 
 template <int D, bool C>
 static hipError_t bwd_d(const BwdArgs& a, const BwdPlan& p, char* ws, hipStream_t stream) {
+  // Under the causal mask each key group's items are split in two workgroups (the group
+  // sizes fall linearly along the sequence; the halves let the dispatcher balance them),
+  // whose sums meet in bwd_combine_kernel.
+  const int nsplit = C ? 2 : 1;
   const int64_t nprep = (int64_t)p.nrb * (2 * a.B * a.Hq + 2 * a.B * a.Hkv);
-  if (nprep > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t ngrp = (p.nrb + 3) / 4;
+  const int64_t n4 = (int64_t)a.B * a.Hkv * a.S * D / 4;
+  if (nprep > 0x7fffffff || ngrp * a.B * a.Hq > 0x7fffffff ||
+      ngrp * nsplit * a.B * a.Hkv > 0x7fffffff || (2 * n4 + 255) / 256 > 0x7fffffff)
+    return hipErrorInvalidValue;
   auto H = [&](size_t off) { return reinterpret_cast<_Float16*>(ws + off); };
   bwd_prep_kernel<D><<<dim3((unsigned)nprep), 256, 0, stream>>>(
       static_cast<const _Float16*>(a.q), static_cast<const _Float16*>(a.dout),
@@ -506,14 +676,22 @@ static hipError_t bwd_d(const BwdArgs& a, const BwdPlan& p, char* ws, hipStream_
   const float c_log2 = a.softmax_scale * 1.4426950408889634f;
   float* lse = reinterpret_cast<float*>(ws + p.off_lse);
   float* dvec = reinterpret_cast<float*>(ws + p.off_dvec);
-  bwd_dq_kernel<D, C><<<dim3((unsigned)((a.S + 127) / 128), a.Hq, a.B), 256, 0, stream>>>(
-      H(p.off_qr), H(p.off_dor), H(p.off_kr), H(p.off_kc), H(p.off_vr), lse, dvec, a.dq, a.Hq,
-      a.Hkv, a.S, p.nrb, c_log2, a.softmax_scale);
+  float* pk = reinterpret_cast<float*>(ws + p.off_pk);
+  float* pv = reinterpret_cast<float*>(ws + p.off_pv);
+  bwd_dq_kernel<D, C><<<dim3((unsigned)(ngrp * a.B * a.Hq)), 256, 0, stream>>>(
+      H(p.off_qr), H(p.off_dor), H(p.off_kr), H(p.off_kc), H(p.off_vr), lse, dvec, a.dq, a.B,
+      a.Hq, a.Hkv, a.S, p.nrb, c_log2, a.softmax_scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bwd_dkdv_kernel<D, C><<<dim3((unsigned)((p.nrb + 3) / 4), a.Hkv, a.B), 256, 0, stream>>>(
+  bwd_dkdv_kernel<D, C><<<dim3((unsigned)(ngrp * nsplit * a.B * a.Hkv)), 256, 0, stream>>>(
       H(p.off_qr), H(p.off_qc), H(p.off_dor), H(p.off_doc), H(p.off_kr), H(p.off_vr), lse,
-      dvec, a.dk, a.dv, a.Hq, a.Hkv, a.S, p.nrb, c_log2, a.softmax_scale);
+      dvec, a.dk, a.dv, pk, pv, a.B, a.Hq, a.Hkv, a.S, p.nrb, nsplit, c_log2,
+      a.softmax_scale);
+  if (nsplit == 1) return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bwd_combine_kernel<<<dim3((unsigned)((2 * n4 + 255) / 256)), 256, 0, stream>>>(a.dk, a.dv, pk,
+                                                                                  pv, n4);
   return hipGetLastError();
 }
 

@@ -132,7 +132,8 @@ hipError_t launch_decode(const void* q, void* out, int32_t Hq, float softmax_sca
 //   lse, dvec         fp32 [B][Hq][S rounded up to 128]   row log2-sum-exp and D
 struct BwdPlan {
   int32_t nrb;
-  size_t off_qr, off_qc, off_dor, off_doc, off_kr, off_kc, off_vr, off_lse, off_dvec, total;
+  size_t off_qr, off_qc, off_dor, off_doc, off_kr, off_kc, off_vr, off_lse, off_dvec, off_pk,
+      off_pv, total;
 };
 BwdPlan plan_bwd(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D);
 
