@@ -18,7 +18,10 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libi8attn.so")
 SOURCES = ["quant_kernels.hip", "attn_kernels.hip", "decode_kernels.hip", "bwd_kernels.hip",
-           "capi.hip"]
+           "bwd_dq_kernels.hip", "capi.hip"]
+# Per-source flags: the dQ kernel keeps its matrix products' results in ordinary vector
+# registers (its softmax arithmetic reads all of them).
+EXTRA_FLAGS = {"bwd_dq_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 FLAGS = [
@@ -38,7 +41,7 @@ def hipcc() -> str:
 
 
 def _compile(src: str, obj: str) -> str:
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile of {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

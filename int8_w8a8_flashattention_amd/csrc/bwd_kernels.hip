@@ -28,35 +28,12 @@
 // results do not depend on the order in which workgroups run.
 #include <float.h>
 
-#include "i8a_device.h"
+#include "bwd_common.h"
 #include "i8a_launch.h"
 
 namespace i8a {
 
-namespace {
-
-__device__ __forceinline__ float bmax(float a, float b) {
-  return __builtin_elementwise_maximum(a, b);
-}
-__device__ __forceinline__ float half_max(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return bmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-// Token of slot jv for lane half hv in a 16-token group (the row order of a 32x32 MFMA
-// result's registers).
-__device__ __forceinline__ int ckey(int hv, int jv) { return 4 * hv + (jv & 3) + 8 * (jv >> 2); }
-
-__device__ __forceinline__ v16f mfma16(v8h a, v8h b, v16f c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-}  // namespace
+using namespace bwd;
 
 // ----------------------------------------------------------------------------------
 // Launch 1: one workgroup per 32-token block of one (batch, head) of one tensor.
@@ -128,199 +105,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const _Float16* __restric
       for (int jv = 0; jv < 8; ++jv) x[jv] = blk[(16 * tgl + ckey(hv, jv)) * LD + d];
       reinterpret_cast<v8h*>(cdst)[c] = x;
     }
-  }
-}
-
-// ----------------------------------------------------------------------------------
-// Copy of one 32-token operand tile (64 * D contiguous bytes) into LDS by the four waves
-// of a workgroup with direct-to-LDS loads: wave w's lanes move the 16-byte chunks
-// 256 r + 64 w + lane.
-template <int D>
-__device__ __forceinline__ void wg_copy_tile(const char* __restrict__ src, char* dst, int tid) {
-  constexpr int NCH = 64 * D / 16;
-  const int w = tid >> 6;
-  const uint32_t base = lds_addr(dst);
-#pragma unroll
-  for (int r = 0; r * 256 < NCH; ++r) {
-    if (r * 256 + w * 64 < NCH) {  // wave-uniform
-      const int chunk = r * 256 + tid;
-      if (chunk < NCH) lds_dma16(src + (int64_t)chunk * 16, base + (r * 256 + w * 64) * 16);
-    }
-  }
-}
-
-// Number of 16-byte copies that wave w issues per tile in wg_copy_tile<D>.
-template <int D>
-__host__ __device__ constexpr int tile_dma_count(int w) {
-  int n = 0;
-  for (int r = 0; r * 256 < 4 * D; ++r)
-    if (r * 256 + w * 64 < 4 * D) ++n;
-  return n;
-}
-
-// ----------------------------------------------------------------------------------
-// Launch 2: dQ.  Workgroup = 4 waves = 128 queries of one (batch, query head); wave w
-// owns queries q0 = 128 * blockIdx.x + 32 w .. +31, lane l query q0 + l % 32.  The key
-// blocks' operand tiles (K and V in row order, K in column order) stream through a
-// two-stage LDS ring shared by the four waves, one block ahead.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(
-    const _Float16* __restrict__ qr, const _Float16* __restrict__ dor,
-    const _Float16* __restrict__ kr, const _Float16* __restrict__ kc,
-    const _Float16* __restrict__ vr, float* __restrict__ lse2, float* __restrict__ dvec,
-    float* __restrict__ dq, int B, int Hq, int Hkv, int S, int nrb, float c_log2, float scale) {
-  constexpr int NKD = D / 16, NDB = D / 32, TB = 64 * D;  // TB: bytes of a 32-token tile
-  __shared__ __attribute__((aligned(16))) char smem[2 * 3 * TB];
-  // blockIdx.x = ((query block of 128, from the last) x B + batch) x Hq + head: under
-  // the causal mask the heaviest blocks of every head are dispatched first.
-  const int h = blockIdx.x % Hq, b = (blockIdx.x / Hq) % B;
-  const int g = h / (Hq / Hkv);
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, m = lane & 31, hh = lane >> 5;
-  const int qblk0 = 128 * ((nrb + 3) / 4 - 1 - (int)(blockIdx.x / Hq / B));
-  const int q0 = qblk0 + 32 * w;
-  const bool active = q0 < nrb * 32;  // waves past the padded length only copy
-  const int64_t Sp = (int64_t)nrb * 32;
-  const int64_t qbase = ((int64_t)b * Hq + h) * Sp;
-  const int64_t kbase = ((int64_t)b * Hkv + g) * Sp;
-  const char* krb = reinterpret_cast<const char*>(kr + kbase * D);
-  const char* vrb = reinterpret_cast<const char*>(vr + kbase * D);
-  const char* kcb = reinterpret_cast<const char*>(kc + kbase * D);
-  const int nkb_wg = CAUSAL ? min(nrb, qblk0 / 32 + 4) : nrb;  // key blocks of the group
-  const int nkb = CAUSAL ? q0 / 32 + 1 : nrb;                  // this wave's
-  const int qi = q0 + m;
-
-  v8h qf[NKD], df[NKD];
-  if (active) {
-    const v8h* qs = reinterpret_cast<const v8h*>(qr + (qbase + q0) * D);
-    const v8h* ds = reinterpret_cast<const v8h*>(dor + (qbase + q0) * D);
-#pragma unroll
-    for (int kd = 0; kd < NKD; ++kd) {
-      qf[kd] = qs[kd * 64 + lane];
-      df[kd] = ds[kd * 64 + lane];
-    }
-  } else {
-#pragma unroll
-    for (int kd = 0; kd < NKD; ++kd)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qf[kd][j] = df[kd][j] = (_Float16)0.0f;
-  }
-  // Consumed here, so that the compiler waits for these loads before the loops (a wait
-  // at their first use inside a loop would also wait for the tile copies).
-#pragma unroll
-  for (int kd = 0; kd < NKD; ++kd) asm volatile("" : : "v"(qf[kd]), "v"(df[kd]));
-
-  auto issue = [&](int kb, int st, bool with_kc) {
-    wg_copy_tile<D>(krb + (int64_t)kb * TB, smem + (st * 3 + 0) * TB, tid);
-    wg_copy_tile<D>(vrb + (int64_t)kb * TB, smem + (st * 3 + 1) * TB, tid);
-    if (with_kc) wg_copy_tile<D>(kcb + (int64_t)kb * TB, smem + (st * 3 + 2) * TB, tid);
-  };
-  // S^T (keys x queries) and dP^T of key block kb from LDS stage st; scaled, masked
-  // scores in t.
-  auto scores = [&](int kb, int st, float (&t)[16], v16f& dp) {
-    const v8h* ka = reinterpret_cast<const v8h*>(smem + (st * 3 + 0) * TB);
-    const v8h* va = reinterpret_cast<const v8h*>(smem + (st * 3 + 1) * TB);
-    v16f sc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.0f;
-#pragma unroll
-    for (int kd = 0; kd < NKD; ++kd) {
-      sc = mfma16(ka[kd * 64 + lane], qf[kd], sc);
-      dp = mfma16(va[kd * 64 + lane], df[kd], dp);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3);
-      const bool dead = key >= S || (CAUSAL && key > qi);
-      t[i] = dead ? -INFINITY : sc[i] * c_log2;
-    }
-  };
-
-  // Sweep 1: running max, sum and sum of p * dP (log2 units).
-  float mr = -INFINITY, l = 0.0f, a = 0.0f;
-  issue(0, 0, false);
-  vm_wait<0>();
-  __syncthreads();
-  for (int kb = 0; kb < nkb_wg; ++kb) {
-    if (kb + 1 < nkb_wg) issue(kb + 1, (kb + 1) & 1, false);
-    if (active && kb < nkb) {
-      float t[16];
-      v16f dp;
-      scores(kb, kb & 1, t, dp);
-      float mt = t[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mt = bmax(mt, t[i]);
-      const float mn = bmax(mr, half_max(mt));
-      const float al = mr == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr - mn);
-      const float mu = mn == -INFINITY ? 0.0f : mn;
-      l *= al;
-      a *= al;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(t[i] - mu);
-        l += p;
-        a = __builtin_fmaf(p, dp[i], a);
-      }
-      mr = mn;
-    }
-    vm_wait<0>();
-    __syncthreads();
-  }
-  l = half_sum(l);
-  a = half_sum(a);
-  // Every row has a visible key (key 0), so l > 0 and mr is finite.
-  const float lse = active ? mr + log2f(l) : 0.0f;
-  const float Dv = active ? a / l : 0.0f;
-  if (active && hh == 0) {
-    lse2[qbase + qi] = lse;
-    dvec[qbase + qi] = Dv;
-  }
-
-  // Sweep 2: P, dS and dQ^T = K^T dS^T.
-  v16f acc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
-  issue(0, 0, true);
-  vm_wait<0>();
-  __syncthreads();
-  for (int kb = 0; kb < nkb_wg; ++kb) {
-    if (kb + 1 < nkb_wg) issue(kb + 1, (kb + 1) & 1, true);
-    // Unconditional, as in the dK/dV kernel: past this wave's last key block every score
-    // is masked and dS is zero.
-    {
-      float t[16];
-      v16f dp;
-      scores(kb, kb & 1, t, dp);
-      v8h ds[2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(t[i] - lse);
-        ds[i >> 3][i & 7] = (_Float16)(p * (dp[i] - Dv));
-      }
-      const v8h* kca = reinterpret_cast<const v8h*>(smem + ((kb & 1) * 3 + 2) * TB);
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          acc[db] = mfma16(kca[(gg * NDB + db) * 64 + lane], ds[gg], acc[db]);
-    }
-    vm_wait<0>();
-    __syncthreads();
-  }
-  if (active && qi < S) {
-    float* orow = dq + (((int64_t)b * Hq + h) * S + qi) * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        v4f o4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o4[r] = acc[db][4 * J + r] * scale;
-        *reinterpret_cast<v4f*>(orow + 32 * db + 8 * J + 4 * hh) = o4;
-      }
   }
 }
 
@@ -678,10 +462,7 @@ static hipError_t bwd_d(const BwdArgs& a, const BwdPlan& p, char* ws, hipStream_
   float* dvec = reinterpret_cast<float*>(ws + p.off_dvec);
   float* pk = reinterpret_cast<float*>(ws + p.off_pk);
   float* pv = reinterpret_cast<float*>(ws + p.off_pv);
-  bwd_dq_kernel<D, C><<<dim3((unsigned)(ngrp * a.B * a.Hq)), 256, 0, stream>>>(
-      H(p.off_qr), H(p.off_dor), H(p.off_kr), H(p.off_kc), H(p.off_vr), lse, dvec, a.dq, a.B,
-      a.Hq, a.Hkv, a.S, p.nrb, c_log2, a.softmax_scale);
-  e = hipGetLastError();
+  e = launch_bwd_dq(a, p, ws, stream);
   if (e != hipSuccess) return e;
   bwd_dkdv_kernel<D, C><<<dim3((unsigned)(ngrp * nsplit * a.B * a.Hkv)), 256, 0, stream>>>(
       H(p.off_qr), H(p.off_qc), H(p.off_dor), H(p.off_doc), H(p.off_kr), H(p.off_vr), lse,
