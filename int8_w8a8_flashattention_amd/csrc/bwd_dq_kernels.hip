@@ -70,12 +70,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
     wg_copy_tile<D>(vrb + (int64_t)kb * TB, smem + (st * 3 + 1) * TB, tid);
     if (with_kc) wg_copy_tile<D>(kcb + (int64_t)kb * TB, smem + (st * 3 + 2) * TB, tid);
   };
-  // S^T (keys x queries) and dP^T of key block kb from LDS stage st; scaled, masked
-  // scores in t.
-  auto scores = [&](int kb, int st, float (&t)[16], v16f& dp) {
+  // S^T (keys x queries) and dP^T of key block kb from LDS stage st.
+  auto scores = [&](int st, v16f& sc, v16f& dp) {
     const v8h* ka = reinterpret_cast<const v8h*>(smem + (st * 3 + 0) * TB);
     const v8h* va = reinterpret_cast<const v8h*>(smem + (st * 3 + 1) * TB);
-    v16f sc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.0f;
 #pragma unroll
@@ -83,11 +81,21 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
       sc = mfma16(ka[kd * 64 + lane], qf[kd], sc);
       dp = mfma16(va[kd * 64 + lane], df[kd], dp);
     }
+  };
+  // Masked scores to -inf.  Only a block that reaches past this wave's first query
+  // (causal) or past the sequence holds masked pairs, so the others skip the compares
+  // (a wave-uniform branch).  The scale c_log2 > 0 is applied later, inside the
+  // exponent's argument, which keeps -inf.
+  auto mask = [&](int kb, v16f& sc) {
+    if ((CAUSAL && 32 * kb + 31 > q0) || 32 * kb + 32 > S) {
+      // Keeps this path a branch: without a statement that cannot be executed
+      // speculatively, the compiler turns it into selects that every block executes.
+      asm volatile("");
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3);
-      const bool dead = key >= S || (CAUSAL && key > qi);
-      t[i] = dead ? -INFINITY : sc[i] * c_log2;
+      for (int i = 0; i < 16; ++i) {
+        const int key = 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if (key >= S || (CAUSAL && key > qi)) sc[i] = -INFINITY;
+      }
     }
   };
 
@@ -99,20 +107,21 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
   for (int kb = 0; kb < nkb_wg; ++kb) {
     if (kb + 1 < nkb_wg) issue(kb + 1, (kb + 1) & 1, false);
     if (active && kb < nkb) {
-      float t[16];
-      v16f dp;
-      scores(kb, kb & 1, t, dp);
-      float mt = t[0];
+      v16f sc, dp;
+      scores(kb & 1, sc, dp);
+      mask(kb, sc);
+      float mt = sc[0];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mt = bmax(mt, t[i]);
-      const float mn = bmax(mr, half_max(mt));
+      for (int i = 1; i < 16; ++i) mt = bmax(mt, sc[i]);
+      // Every block of this wave holds a visible key for each of its rows, so mn is
+      // finite from the first block on.
+      const float mn = bmax(mr, half_max(mt) * c_log2);
       const float al = mr == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr - mn);
-      const float mu = mn == -INFINITY ? 0.0f : mn;
       l *= al;
       a *= al;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(t[i] - mu);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c_log2, -mn));
         l += p;
         a = __builtin_fmaf(p, dp[i], a);
       }
@@ -143,15 +152,16 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
   for (int kb = 0; kb < nkb_wg; ++kb) {
     if (kb + 1 < nkb_wg) issue(kb + 1, (kb + 1) & 1, true);
     // Unconditional, as in the dK/dV kernel: past this wave's last key block every score
-    // is masked and dS is zero.
+    // is masked and dS is zero (a wave past the padded length has zero operands, lse = 0
+    // and D = 0, so dS is zero too).
     {
-      float t[16];
-      v16f dp;
-      scores(kb, kb & 1, t, dp);
+      v16f sc, dp;
+      scores(kb & 1, sc, dp);
+      mask(kb, sc);
       v8h ds[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(t[i] - lse);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c_log2, -lse));
         ds[i >> 3][i & 7] = (_Float16)(p * (dp[i] - Dv));
       }
       const v8h* kca = reinterpret_cast<const v8h*>(smem + ((kb & 1) * 3 + 2) * TB);
