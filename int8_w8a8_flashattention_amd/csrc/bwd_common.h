@@ -32,21 +32,45 @@ __device__ __forceinline__ v16f mfma16(v8h a, v8h b, v16f c) {
 // Copy of one 32-token operand tile (64 * D contiguous bytes) into LDS by the four waves
 // of a workgroup with direct-to-LDS loads: wave w's lanes move the 16-byte chunks
 // 256 r + 64 w + lane.
-template <int D>
-__device__ __forceinline__ void wg_copy_tile(const char* __restrict__ src, char* dst, int tid) {
-  constexpr int NCH = 64 * D / 16;
-  const int w = tid >> 6;
-  const uint32_t base = lds_addr(dst);
-#pragma unroll
-  for (int r = 0; r * 256 < NCH; ++r) {
-    if (r * 256 + w * 64 < NCH) {  // wave-uniform
-      const int chunk = r * 256 + tid;
-      if (chunk < NCH) lds_dma16(src + (int64_t)chunk * 16, base + (r * 256 + w * 64) * 16);
-    }
-  }
+// Direct-to-LDS copy of 16 bytes per lane from the wave-uniform address sbase plus the
+// lane's 32-bit byte offset voff (the instruction's scalar-base form), into LDS at the
+// wave-uniform address lds_base (+ 16 x lane).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
-// Number of 16-byte copies that wave w issues per tile in wg_copy_tile<D>.
+// Copy of one 32-token operand tile (64 * D contiguous bytes) into LDS by the four waves
+// of a workgroup: wave w's lanes move the 16-byte chunks 256 r + 64 w + lane.  The
+// lanes' offsets are computed once; a copy is then a scalar base, an m0 write and the
+// load.  The chunk count 4 D is a multiple of 64, so a wave copies whole rows of 64
+// chunks or none.
+template <int D>
+struct TileCopy {
+  static constexpr int NCH = 64 * D / 16;
+  static constexpr int R = (NCH + 255) / 256;
+  uint32_t voff[R];
+  int w;
+  __device__ __forceinline__ explicit TileCopy(int tid)
+      : w(__builtin_amdgcn_readfirstlane(tid >> 6)) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) voff[r] = (uint32_t)(r * 256 + tid) * 16;
+  }
+  __device__ __forceinline__ void operator()(const char* src, char* dst) const {
+    const uint32_t base = lds_addr(dst);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (NCH % 256 == 0 || r * 256 + w * 64 < NCH)  // wave-uniform
+        lds_dma16_s(src, voff[r], base + (uint32_t)(r * 256 + w * 64) * 16);
+  }
+};
+
+// Number of 16-byte copies that wave w issues per tile with TileCopy<D>.
 template <int D>
 __host__ __device__ constexpr int tile_dma_count(int w) {
   int n = 0;

@@ -65,10 +65,11 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 #pragma unroll
   for (int kd = 0; kd < NKD; ++kd) asm volatile("" : : "v"(qf[kd]), "v"(df[kd]));
 
+  const TileCopy<D> copy(tid);
   auto issue = [&](int kb, int st, bool with_kc) {
-    wg_copy_tile<D>(krb + (int64_t)kb * TB, smem + (st * 3 + 0) * TB, tid);
-    wg_copy_tile<D>(vrb + (int64_t)kb * TB, smem + (st * 3 + 1) * TB, tid);
-    if (with_kc) wg_copy_tile<D>(kcb + (int64_t)kb * TB, smem + (st * 3 + 2) * TB, tid);
+    copy(krb + (int64_t)kb * TB, smem + (st * 3 + 0) * TB);
+    copy(vrb + (int64_t)kb * TB, smem + (st * 3 + 1) * TB);
+    if (with_kc) copy(kcb + (int64_t)kb * TB, smem + (st * 3 + 2) * TB);
   };
   // S^T (keys x queries) and dP^T of key block kb from LDS stage st.
   auto scores = [&](int st, v16f& sc, v16f& dp) {

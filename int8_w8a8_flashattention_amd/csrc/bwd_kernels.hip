@@ -182,30 +182,33 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   // nsplit takes the items j = p (mod nsplit).
   const int nitem = (G * nqb - part + nsplit - 1) / nsplit;
   if (nitem == 0) return;
-  auto item_base = [&](int it, int64_t& qbase, int& qb) {
-    const int j = part + it * nsplit;
-    qb = nrb - 1 - j / G;
-    qbase = ((int64_t)b * Hq + g * G + j % G) * Sp;
-  };
-  // Copies of item it into its row and column stages.  Every wave issues
-  // 4 tile_dma_count<D>(w) + 1 copies per item (the statistics: 4 lanes of each wave).
-  auto issue = [&](int it) {
-    int64_t qbase;
-    int qb;
-    item_base(it, qbase, qb);
-    const int64_t off = (qbase + 32 * (int64_t)qb) * D * 2;
-    char* rs = rring + (it & (NR - 1)) * RB;
-    char* cs = cring + (it % NC) * CB;
-    wg_copy_tile<D>(reinterpret_cast<const char*>(qr) + off, rs, tid);
-    wg_copy_tile<D>(reinterpret_cast<const char*>(dor) + off, rs + TB, tid);
-    wg_copy_tile<D>(reinterpret_cast<const char*>(qc) + off, cs, tid);
-    wg_copy_tile<D>(reinterpret_cast<const char*>(doc) + off, cs + TB, tid);
+  // Copies of the items into their row and column stages, in item order (0, 1, 2, ...;
+  // each once), following a cursor over (query block, head) instead of dividing by G.
+  // Every wave issues 4 tile_dma_count<D>(w) + 1 copies per item (the statistics: 4
+  // lanes of each wave, waves 0-1 the log-sum-exps, waves 2-3 the D values).
+  const TileCopy<D> copy(tid);
+  const uint32_t stat_off = 16u * (4u * (uint32_t)(w & 1) + (uint32_t)lane);
+  int cur_hg = part % G, cur_qb = nrb - 1 - part / G, cur_cs = 0, cur_it = 0;
+  auto issue = [&]() {
+    const int64_t qbase = ((int64_t)b * Hq + g * G + cur_hg) * Sp;
+    const int64_t off = (qbase + 32 * (int64_t)cur_qb) * D * 2;
+    char* rs = rring + (cur_it & (NR - 1)) * RB;
+    char* cs = cring + cur_cs * CB;
+    copy(reinterpret_cast<const char*>(qr) + off, rs);
+    copy(reinterpret_cast<const char*>(dor) + off, rs + TB);
+    copy(reinterpret_cast<const char*>(qc) + off, cs);
+    copy(reinterpret_cast<const char*>(doc) + off, cs + TB);
     // The row statistics ride in the column stage, so the loop holds no load the
     // compiler tracks: a wait it placed for one would also wait for later copies.
-    if (lane < 4) {
-      const int c = 4 * w + lane;
-      const float* src = (c < 8 ? lse2 : dvec) + qbase + 32 * qb + 4 * (c & 7);
-      lds_dma16(src, lds_addr(cs + 2 * TB + 16 * c));
+    if (lane < 4)
+      lds_dma16_s((w < 2 ? lse2 : dvec) + qbase + 32 * cur_qb, stat_off,
+                  lds_addr(cs + 2 * TB + 64 * w));
+    ++cur_it;
+    cur_cs = cur_cs + 1 == NC ? 0 : cur_cs + 1;
+    cur_hg += nsplit;
+    while (cur_hg >= G) {
+      cur_hg -= G;
+      --cur_qb;
     }
   };
   // Wait for every copy but, if `one_ahead`, the last item's (at most: the count is wave
@@ -253,7 +256,17 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       dv4[J] = *reinterpret_cast<const v4f*>(lrow + 32 + 8 * J + 4 * hh);
     }
   };
-  auto item_qb = [&](int it) { return nrb - 1 - (part + it * nsplit) / G; };
+  // The query block of the next item whose softmax is computed (called in item order).
+  int st_hg = part % G, st_qb = nrb - 1 - part / G;
+  auto next_item_qb = [&]() {
+    const int q = st_qb;
+    st_hg += nsplit;
+    while (st_hg >= G) {
+      st_hg -= G;
+      --st_qb;
+    }
+    return q;
+  };
   // dV^T += dO^T P^T and dK^T += Q^T dS^T for block it, from its column tiles.
   auto accumulate = [&](int it, const v8h (&p16)[2], const v8h (&ds16)[2]) {
     const char* stg = cring + (it % NC) * CB;
@@ -276,12 +289,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   // (a block the causal mask empties adds exact zeros; a wave past the padded length is
   // never written): skipping one would give each accumulator two incoming values at the
   // loop's join, which the register allocator resolves with copies of all of them.
-  issue(0);
-  if (nitem > 1) issue(1);
-  if (nitem > 2) issue(2);
+  issue();
+  if (nitem > 1) issue();
+  if (nitem > 2) issue();
   wait_copies(nitem > 2);
   __syncthreads();
-  if (nitem > 3) issue(3);
+  if (nitem > 3) issue();
   v16f sc, dp;
   scores(0, sc, dp);
   v8h p16[2], ds16[2];
@@ -290,7 +303,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     scores(min(1, nitem - 1), sn, dn);
     v4f lv[4], dv4[4];
     stats(0, lv, dv4);
-    const int qb = item_qb(0);
+    const int qb = next_item_qb();  // item 0
 #pragma unroll
     for (int e = 0; e < 16; ++e) prob(e, qb, sc[e], dp[e], lv, dv4, p16, ds16);
     sc = sn;
@@ -311,7 +324,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     }
     v4f lv[4], dv4[4];
     stats(it, lv, dv4);
-    const int qb = item_qb(it);
+    const int qb = next_item_qb();  // item it
     float scv[16], dpv[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -361,7 +374,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   // Steps with a copy to start (its wait leaves that copy in flight), then the last three.
   int it = 1;
   for (; it + 3 < nitem; ++it) {
-    issue(it + 3);
+    issue();  // item it + 3
     step(it);
     wait_copies(true);
     __syncthreads();
