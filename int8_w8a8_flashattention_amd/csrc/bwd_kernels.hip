@@ -28,6 +28,8 @@
 // results do not depend on the order in which workgroups run.
 #include <float.h>
 
+#include <type_traits>
+
 #include "bwd_common.h"
 #include "i8a_launch.h"
 
@@ -182,6 +184,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   // nsplit takes the items j = p (mod nsplit).
   const int nitem = (G * nqb - part + nsplit - 1) / nsplit;
   if (nitem == 0) return;
+  // Under the causal mask only items with a query block at or below the group's last
+  // wave's first key block (qb <= kblk0 / 32 + 3: the last 4 G of the order, j >=
+  // G (nqb - 4)) can hold masked pairs; items before it_m skip the mask.
+  int it_m = nitem;
+  if (CAUSAL) {
+    const int jm = G * (nqb - 4) - part;
+    it_m = jm <= 0 ? 0 : min(nitem, (jm + nsplit - 1) / nsplit);
+  }
   // Copies of the items into their row and column stages, in item order (0, 1, 2, ...;
   // each once), following a cursor over (query block, head) instead of dividing by G.
   // Every wave issues 4 tile_dma_count<D>(w) + 1 copies per item (the statistics: 4
@@ -236,13 +246,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   // Element e (register e: query 32 qb + 8 (e / 4) + 4 hh + e % 4) of block it's P^T
   // and dS^T, from its score, its dP and its row's statistics (lv, dv4 from the stage).
   auto prob = [&](int e, int qb, float s, float d, const v4f (&lv)[4], const v4f (&dv4)[4],
-                  v8h (&p16)[2], v8h (&ds16)[2]) {
+                  v8h (&p16)[2], v8h (&ds16)[2], auto masked) {
     const int J = e >> 2, r = e & 3;
     // Empty statements that take the inputs and give the results at this point of the
     // step: the arithmetic stays in the slot where the fences put it.
     asm volatile("" : "+v"(s), "+v"(d));
     float p = __builtin_amdgcn_exp2f(s * c_log2 - lv[J][r]);
-    if (CAUSAL) p = kj > 32 * qb + 8 * J + 4 * hh + r ? 0.0f : p;
+    if constexpr (decltype(masked)::value) p = kj > 32 * qb + 8 * J + 4 * hh + r ? 0.0f : p;
     const float ds = p * (d - dv4[J][r]);
     asm volatile("" : : "v"(p), "v"(ds));
     p16[e >> 3][e & 7] = (_Float16)p;
@@ -305,14 +315,19 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     stats(0, lv, dv4);
     const int qb = next_item_qb();  // item 0
 #pragma unroll
-    for (int e = 0; e < 16; ++e) prob(e, qb, sc[e], dp[e], lv, dv4, p16, ds16);
+    for (int e = 0; e < 16; ++e) {
+      if (it_m == 0)
+        prob(e, qb, sc[e], dp[e], lv, dv4, p16, ds16, std::true_type{});
+      else
+        prob(e, qb, sc[e], dp[e], lv, dv4, p16, ds16, std::false_type{});
+    }
     sc = sn;
     dp = dn;
   }
   wait_copies(nitem > 3);
   __syncthreads();
   constexpr int NP = D / 8;       // products of each kind per step
-  auto step = [&](int it) {
+  auto step = [&](int it, auto masked) {
     const char* stp = cring + ((it - 1) % NC) * CB;
     const char* stn = rring + (min(it + 1, nitem - 1) & (NR - 1)) * RB;
     v8h aop[NP];
@@ -360,7 +375,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       }
 #pragma unroll
       for (int e = x * 16 / (2 * NP); e < (x + 1) * 16 / (2 * NP); ++e)
-        prob(e, qb, scv[e], dpv[e], lv, dv4, pn, dsn);
+        prob(e, qb, scv[e], dpv[e], lv, dv4, pn, dsn, masked);
       __builtin_amdgcn_sched_barrier(0);
     }
     sc = sn;
@@ -371,16 +386,29 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       ds16[gg] = dsn[gg];
     }
   };
-  // Steps with a copy to start (its wait leaves that copy in flight), then the last three.
+  // Steps with a copy to start (its wait leaves that copy in flight), then the last three;
+  // each without the mask's compares up to the first item that can hold a masked pair.
+  const int n_issue = nitem - 3;
   int it = 1;
-  for (; it + 3 < nitem; ++it) {
+  for (; it < n_issue && it < it_m; ++it) {
     issue();  // item it + 3
-    step(it);
+    step(it, std::false_type{});
     wait_copies(true);
     __syncthreads();
   }
+  for (; it < n_issue; ++it) {
+    issue();
+    step(it, std::true_type{});
+    wait_copies(true);
+    __syncthreads();
+  }
+  for (; it < nitem && it < it_m; ++it) {
+    step(it, std::false_type{});
+    vm_wait<0>();
+    __syncthreads();
+  }
   for (; it < nitem; ++it) {
-    step(it);
+    step(it, std::true_type{});
     vm_wait<0>();
     __syncthreads();
   }
