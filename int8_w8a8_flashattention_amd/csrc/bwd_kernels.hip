@@ -183,7 +183,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   // block, read the same tiles at about the same time and share them in L2.  Part p of
   // nsplit takes the items j = p (mod nsplit).
   const int nitem = (G * nqb - part + nsplit - 1) / nsplit;
-  if (nitem == 0) return;
+  // A part can have no items (G = 1 and a group with one query block): it still writes
+  // its partial rows below (zeros), since the combine kernel adds every row.
   // Under the causal mask only items with a query block at or below the group's last
   // wave's first key block (qb <= kblk0 / 32 + 3: the last 4 G of the order, j >=
   // G (nqb - 4)) can hold masked pairs; items before it_m skip the mask.
@@ -291,128 +292,130 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       }
   };
 
-  // Software pipeline over the work items: step it runs the dV/dK products of item
-  // it - 1, the score products of item it + 1 and the softmax arithmetic of item it, none
-  // of which waits for another.  The copy of item it + 3 starts at step it and has two
-  // steps to land: into the row stage that item it - 1 left at step it - 2 and the column
-  // stage that item it - 2 left at step it - 1.  Every block is processed by every wave
-  // (a block the causal mask empties adds exact zeros; a wave past the padded length is
-  // never written): skipping one would give each accumulator two incoming values at the
-  // loop's join, which the register allocator resolves with copies of all of them.
-  issue();
-  if (nitem > 1) issue();
-  if (nitem > 2) issue();
-  wait_copies(nitem > 2);
-  __syncthreads();
-  if (nitem > 3) issue();
-  v16f sc, dp;
-  scores(0, sc, dp);
-  v8h p16[2], ds16[2];
-  {
-    v16f sn, dn;
-    scores(min(1, nitem - 1), sn, dn);
-    v4f lv[4], dv4[4];
-    stats(0, lv, dv4);
-    const int qb = next_item_qb();  // item 0
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      if (it_m == 0)
-        prob(e, qb, sc[e], dp[e], lv, dv4, p16, ds16, std::true_type{});
-      else
-        prob(e, qb, sc[e], dp[e], lv, dv4, p16, ds16, std::false_type{});
-    }
-    sc = sn;
-    dp = dn;
-  }
-  wait_copies(nitem > 3);
-  __syncthreads();
-  constexpr int NP = D / 8;       // products of each kind per step
-  auto step = [&](int it, auto masked) {
-    const char* stp = cring + ((it - 1) % NC) * CB;
-    const char* stn = rring + (min(it + 1, nitem - 1) & (NR - 1)) * RB;
-    v8h aop[NP];
-#pragma unroll
-    for (int x = 0; x < NP; ++x) {
-      const int gg = x / (2 * NDB), db = (x >> 1) % NDB;
-      const v8h* src = reinterpret_cast<const v8h*>(stp + ((x & 1) ? 0 : 1) * TB);
-      aop[x] = src[(gg * NDB + db) * 64 + lane];
-    }
-    v4f lv[4], dv4[4];
-    stats(it, lv, dv4);
-    const int qb = next_item_qb();  // item it
-    float scv[16], dpv[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      scv[e] = sc[e];
-      dpv[e] = dp[e];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    v8h pn[2], dsn[2], sop[NP];
-    v16f sn, dn;
-#pragma unroll
-    for (int x = 0; x < 2 * NP; ++x) {
-      if (x < NP) {
-        const int gg = x / (2 * NDB), db = (x >> 1) % NDB;
-        if (x & 1)
-          acck[db] = mfma16(aop[x], ds16[gg], acck[db]);
-        else
-          accv[db] = mfma16(aop[x], p16[gg], accv[db]);
-        const v8h* src = reinterpret_cast<const v8h*>(stn + ((x & 1) ? 1 : 0) * TB);
-        sop[x] = src[(x >> 1) * 64 + lane];
-      } else {
-        const int y = x - NP;
-        if (y < 2) {
-          if (y & 1)
-            dn = mfma16(sop[y], vf[y >> 1], v16f{});
-          else
-            sn = mfma16(sop[y], kf[y >> 1], v16f{});
-        } else {
-          if (y & 1)
-            dn = mfma16(sop[y], vf[y >> 1], dn);
-          else
-            sn = mfma16(sop[y], kf[y >> 1], sn);
-        }
-      }
-#pragma unroll
-      for (int e = x * 16 / (2 * NP); e < (x + 1) * 16 / (2 * NP); ++e)
-        prob(e, qb, scv[e], dpv[e], lv, dv4, pn, dsn, masked);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    sc = sn;
-    dp = dn;
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-      p16[gg] = pn[gg];
-      ds16[gg] = dsn[gg];
-    }
-  };
-  // Steps with a copy to start (its wait leaves that copy in flight), then the last three;
-  // each without the mask's compares up to the first item that can hold a masked pair.
-  const int n_issue = nitem - 3;
-  int it = 1;
-  for (; it < n_issue && it < it_m; ++it) {
-    issue();  // item it + 3
-    step(it, std::false_type{});
-    wait_copies(true);
-    __syncthreads();
-  }
-  for (; it < n_issue; ++it) {
+  if (nitem > 0) {
+    // Software pipeline over the work items: step it runs the dV/dK products of item
+    // it - 1, the score products of item it + 1 and the softmax arithmetic of item it, none
+    // of which waits for another.  The copy of item it + 3 starts at step it and has two
+    // steps to land: into the row stage that item it - 1 left at step it - 2 and the column
+    // stage that item it - 2 left at step it - 1.  Every block is processed by every wave
+    // (a block the causal mask empties adds exact zeros; a wave past the padded length is
+    // never written): skipping one would give each accumulator two incoming values at the
+    // loop's join, which the register allocator resolves with copies of all of them.
     issue();
-    step(it, std::true_type{});
-    wait_copies(true);
+    if (nitem > 1) issue();
+    if (nitem > 2) issue();
+    wait_copies(nitem > 2);
     __syncthreads();
-  }
-  for (; it < nitem && it < it_m; ++it) {
-    step(it, std::false_type{});
-    vm_wait<0>();
+    if (nitem > 3) issue();
+    v16f sc, dp;
+    scores(0, sc, dp);
+    v8h p16[2], ds16[2];
+    {
+      v16f sn, dn;
+      scores(min(1, nitem - 1), sn, dn);
+      v4f lv[4], dv4[4];
+      stats(0, lv, dv4);
+      const int qb = next_item_qb();  // item 0
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if (it_m == 0)
+          prob(e, qb, sc[e], dp[e], lv, dv4, p16, ds16, std::true_type{});
+        else
+          prob(e, qb, sc[e], dp[e], lv, dv4, p16, ds16, std::false_type{});
+      }
+      sc = sn;
+      dp = dn;
+    }
+    wait_copies(nitem > 3);
     __syncthreads();
+    constexpr int NP = D / 8;       // products of each kind per step
+    auto step = [&](int it, auto masked) {
+      const char* stp = cring + ((it - 1) % NC) * CB;
+      const char* stn = rring + (min(it + 1, nitem - 1) & (NR - 1)) * RB;
+      v8h aop[NP];
+  #pragma unroll
+      for (int x = 0; x < NP; ++x) {
+        const int gg = x / (2 * NDB), db = (x >> 1) % NDB;
+        const v8h* src = reinterpret_cast<const v8h*>(stp + ((x & 1) ? 0 : 1) * TB);
+        aop[x] = src[(gg * NDB + db) * 64 + lane];
+      }
+      v4f lv[4], dv4[4];
+      stats(it, lv, dv4);
+      const int qb = next_item_qb();  // item it
+      float scv[16], dpv[16];
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        scv[e] = sc[e];
+        dpv[e] = dp[e];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      v8h pn[2], dsn[2], sop[NP];
+      v16f sn, dn;
+  #pragma unroll
+      for (int x = 0; x < 2 * NP; ++x) {
+        if (x < NP) {
+          const int gg = x / (2 * NDB), db = (x >> 1) % NDB;
+          if (x & 1)
+            acck[db] = mfma16(aop[x], ds16[gg], acck[db]);
+          else
+            accv[db] = mfma16(aop[x], p16[gg], accv[db]);
+          const v8h* src = reinterpret_cast<const v8h*>(stn + ((x & 1) ? 1 : 0) * TB);
+          sop[x] = src[(x >> 1) * 64 + lane];
+        } else {
+          const int y = x - NP;
+          if (y < 2) {
+            if (y & 1)
+              dn = mfma16(sop[y], vf[y >> 1], v16f{});
+            else
+              sn = mfma16(sop[y], kf[y >> 1], v16f{});
+          } else {
+            if (y & 1)
+              dn = mfma16(sop[y], vf[y >> 1], dn);
+            else
+              sn = mfma16(sop[y], kf[y >> 1], sn);
+          }
+        }
+  #pragma unroll
+        for (int e = x * 16 / (2 * NP); e < (x + 1) * 16 / (2 * NP); ++e)
+          prob(e, qb, scv[e], dpv[e], lv, dv4, pn, dsn, masked);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sc = sn;
+      dp = dn;
+  #pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        p16[gg] = pn[gg];
+        ds16[gg] = dsn[gg];
+      }
+    };
+    // Steps with a copy to start (its wait leaves that copy in flight), then the last three;
+    // each without the mask's compares up to the first item that can hold a masked pair.
+    const int n_issue = nitem - 3;
+    int it = 1;
+    for (; it < n_issue && it < it_m; ++it) {
+      issue();  // item it + 3
+      step(it, std::false_type{});
+      wait_copies(true);
+      __syncthreads();
+    }
+    for (; it < n_issue; ++it) {
+      issue();
+      step(it, std::true_type{});
+      wait_copies(true);
+      __syncthreads();
+    }
+    for (; it < nitem && it < it_m; ++it) {
+      step(it, std::false_type{});
+      vm_wait<0>();
+      __syncthreads();
+    }
+    for (; it < nitem; ++it) {
+      step(it, std::true_type{});
+      vm_wait<0>();
+      __syncthreads();
+    }
+    accumulate(nitem - 1, p16, ds16);
   }
-  for (; it < nitem; ++it) {
-    step(it, std::true_type{});
-    vm_wait<0>();
-    __syncthreads();
-  }
-  accumulate(nitem - 1, p16, ds16);
 
   if (active && kj < S) {
     // Part 0 writes the outputs, part 1 its partial sums (added by bwd_combine_kernel).

@@ -52,7 +52,12 @@ def run(w, do, causal, scale=None):
 
 
 SHAPES = [(1, 2, 2, 64, 64), (2, 4, 2, 100, 32), (1, 4, 1, 300, 128), (1, 2, 1, 1, 64),
-          (2, 8, 2, 129, 128), (1, 3, 3, 33, 32)]
+          (2, 8, 2, 129, 128), (1, 3, 3, 33, 32),
+          # one query block in the last 128-key group with G = 1: the causal split's second
+          # part has no items there and must still write its (zero) partial rows
+          (1, 2, 2, 160, 64), (1, 1, 1, 129, 32),
+          # a large query group (MQA, G = 16)
+          (1, 16, 1, 200, 64)]
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -103,3 +108,30 @@ def test_bwd_cfg2_one_kv_group():
     check_grad(dq[:, sl], ref[0], "cfg2 dq")
     check_grad(dk[:, 3:4], ref[1], "cfg2 dk")
     check_grad(dv[:, 3:4], ref[2], "cfg2 dv")
+
+
+def test_bwd_needs_no_workspace_initialization():
+    # The workspace is filled with NaN bytes first: every value the kernels read from it
+    # must have been written by the same call (the combine kernel adds every partial row,
+    # including those of a part with no items).
+    B, Hq, Hkv, S, D = 1, 2, 2, 160, 64
+    w = workloads.dense(215, B, Hq, Hkv, S, D, True, k_offset=1.0)
+    do = np.random.Generator(np.random.PCG64(216)).standard_normal(w.q.shape).astype(np.float16)
+    ws = torch.full((i8.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    got = [host(t) for t in i8.attn_bwd(dev(w.q), dev(w.k), dev(w.v), dev(do), True,
+                                        workspace=ws)]
+    ref = oracle.attn_bwd_exact(w.q, w.k, w.v, do, True)
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        check_grad(g, r, f"NaN-filled workspace {name}")
+
+
+def test_bwd_is_deterministic():
+    # No atomics: two calls give bit-identical gradients (here with the causal split and
+    # its combine, GQA, a ragged tail).
+    w = workloads.dense(217, 2, 8, 2, 300, 128, True)
+    do = np.random.Generator(np.random.PCG64(218)).standard_normal(w.q.shape).astype(np.float16)
+    a = run(w, do, True)
+    b = run(w, do, True)
+    for name, x, y in zip(("dq", "dk", "dv"), a, b):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), name
