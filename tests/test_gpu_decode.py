@@ -152,14 +152,14 @@ def test_decode_rejects_bad_arguments():
 
 
 def test_decode_workspace_reused_across_calls_and_shapes():
-    # The chunk merge keeps counters in the workspace: zeroed once, every call leaves
-    # them at zero for the next, whatever the shape that uses the workspace next.
-    say("one zeroed workspace, several multi-chunk calls and shapes")
+    # One workspace, filled with NaN bytes first, serves several multi-chunk calls and
+    # shapes: every chunk partial the merge reads is written by the same call.
+    say("one NaN-filled workspace, several multi-chunk calls and shapes")
     shapes = [(1, 4, 2, 3000, 128), (2, 8, 2, 1500, 64), (1, 40, 1, 2500, 128)]
     need = max(i8.attn_int8_decode_workspace_bytes(B, Hq, Hkv, S, D, "int8")
                for B, Hq, Hkv, S, D in shapes)
     assert need > 0
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
     for rep in range(2):
         for n, (B, Hq, Hkv, S, D) in enumerate(shapes):
             w = workloads.decode(800 + n, B, Hq, Hkv, S, D, k_offset=1.5)

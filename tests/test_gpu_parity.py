@@ -322,3 +322,32 @@ def test_cfg5_long_context_sampled_rows():
     ref = oracle.attn_int8_fwd(w.q, w.k, w.v, True, heads=heads, rows=rows)
     got = np.stack([o[0, h][rows] for _, h in heads])
     check_close(got, ref, "cfg5")
+
+
+# ------------------------------------------------------------------ workspace contents
+
+def nan_workspace(nbytes):
+    return torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("flags", [0, i8.FWD_HADAMARD | i8.FWD_V_PER_CHANNEL])
+def test_forward_needs_no_workspace_initialization(flags):
+    # The workspace is filled with NaN bytes first: every value the kernels read from it
+    # (padding slots of the K/V tiles and Q rows included) is written by the same call.
+    say(f"forward on a NaN-filled workspace, flags={flags}")
+    B, Hq, Hkv, S, D = 2, 4, 2, 300, 64
+    w = workloads.dense(63, B, Hq, Hkv, S, D, True, k_offset=1.0)
+    ws = nan_workspace(i8.attn_int8_workspace_bytes(B, Hq, Hkv, S, D))
+    o = host(i8.attn_int8_fwd_ex(dev(w.q), dev(w.k), dev(w.v), True, flags, workspace=ws))
+    ref = oracle.attn_int8_fwd(w.q, w.k, w.v, True, hadamard=bool(flags & i8.FWD_HADAMARD),
+                               v_per_channel=bool(flags & i8.FWD_V_PER_CHANNEL))
+    check_close(o, ref, f"dense flags={flags}")
+    v = workloads.varlen(64, 5, 200, 4, 2, 128, True, lengths=[1, 0, 200, 65, 33])
+    T = int(v.cu_seqlens[-1])
+    ws = nan_workspace(i8.attn_int8_varlen_workspace_bytes(5, T, 200, 4, 2, 128))
+    o = host(i8.attn_int8_varlen_fwd_ex(dev(v.q), dev(v.k), dev(v.v), dev(v.cu_seqlens), 200,
+                                        True, flags, workspace=ws))
+    ref = oracle.attn_int8_varlen_fwd(v.q, v.k, v.v, v.cu_seqlens, True,
+                                      hadamard=bool(flags & i8.FWD_HADAMARD),
+                                      v_per_channel=bool(flags & i8.FWD_V_PER_CHANNEL))
+    check_close(o, ref, f"varlen flags={flags}")
