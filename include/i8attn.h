@@ -309,7 +309,7 @@ size_t attn_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, i
  *   q, dout  fp16 [B, Hq, S, D]      k, v  fp16 [B, Hkv, S, D]   (16-byte aligned)
  *   dq       fp32 [B, Hq, S, D] out  dk, dv  fp32 [B, Hkv, S, D] out (16-byte aligned)
  *   1 <= B <= 65535, S >= 1, B*S <= 2^30, 1 <= Hkv <= Hq <= 65535, Hq % Hkv == 0,
- *   D in {32, 64, 128} (256 is I8A_ERR_UNSUPPORTED_HEAD_DIM here).
+ *   D in {32, 64, 128, 256}.
  *   softmax_scale, causal as for attn_int8_fwd; workspace of attn_bwd_workspace_bytes
  *   bytes, 256-byte aligned, needs no initialization.  Outputs alias no input.
  */

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libi8attn.so")
 SOURCES = ["quant_kernels.hip", "attn_kernels.hip", "decode_kernels.hip", "bwd_kernels.hip",
-           "bwd_dq_kernels.hip", "capi.hip"]
+           "bwd_dq_kernels.hip", "bwd_dq256_kernels.hip", "capi.hip"]
 # Per-source flags: the dQ kernel keeps its matrix products' results in ordinary vector
 # registers (its softmax arithmetic reads all of them).
 EXTRA_FLAGS = {"bwd_dq_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

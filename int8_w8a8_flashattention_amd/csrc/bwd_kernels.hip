@@ -131,7 +131,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   // Two rings: row stages (Q and dO in row order), read one step before their item's
   // step, and column stages (Q and dO in column order, then the block's 32 row
   // log-sum-exps and 32 D values), read at their item's step and the next.
-  constexpr int NR = 4, NC = 5, RB = 2 * TB, CB = 2 * TB + 256;
+  // D <= 128: the software-pipelined loop (rings of 4 and 5 stages); D = 256: a plain
+  // loop one item ahead (2 and 2 stages, 128.5 KB), since the pipeline's rings would not
+  // fit the 160 KB of LDS.
+  constexpr bool PIPE = D <= 128;
+  constexpr int NR = PIPE ? 4 : 2, NC = PIPE ? 5 : 2, RB = 2 * TB, CB = 2 * TB + 256;
   __shared__ __attribute__((aligned(16))) char smem[NR * RB + NC * CB];
   char* const rring = smem;
   char* const cring = smem + NR * RB;
@@ -292,7 +296,34 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       }
   };
 
-  if (nitem > 0) {
+  if constexpr (!PIPE) {
+    if (nitem > 0) {
+      // Plain loop: the copy of item it + 1 runs while item it is computed, into the
+      // stages that item it - 1 left at the previous step.
+      issue();
+      vm_wait<0>();
+      __syncthreads();
+      for (int it = 0; it < nitem; ++it) {
+        if (it + 1 < nitem) issue();
+        v16f sc, dp;
+        scores(it, sc, dp);
+        v4f lv[4], dv4[4];
+        stats(it, lv, dv4);
+        const int qb = next_item_qb();
+        v8h p16[2], ds16[2];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (it >= it_m)
+            prob(e, qb, sc[e], dp[e], lv, dv4, p16, ds16, std::true_type{});
+          else
+            prob(e, qb, sc[e], dp[e], lv, dv4, p16, ds16, std::false_type{});
+        }
+        accumulate(it, p16, ds16);
+        vm_wait<0>();
+        __syncthreads();
+      }
+    }
+  } else if (nitem > 0) {
     // Software pipeline over the work items: step it runs the dV/dK products of item
     // it - 1, the score products of item it + 1 and the softmax arithmetic of item it, none
     // of which waits for another.  The copy of item it + 3 starts at step it and has two
@@ -527,7 +558,7 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, void* ws, hipStream_t 
     return a.causal ? bwd_d<DD, true>(a, p, w, stream)               \
                     : bwd_d<DD, false>(a, p, w, stream);
   switch (a.D) {
-    I8A_BWD(32) I8A_BWD(64) I8A_BWD(128)
+    I8A_BWD(32) I8A_BWD(64) I8A_BWD(128) I8A_BWD(256)
     default:
       return hipErrorInvalidValue;
   }

@@ -410,7 +410,7 @@ static bool bwd_sizes_ok(int32_t B, int32_t Hq, int32_t Hkv, int32_t S) {
 }
 
 size_t attn_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D) {
-  if (!bwd_sizes_ok(B, Hq, Hkv, S) || (D != 32 && D != 64 && D != 128)) return 0;
+  if (!bwd_sizes_ok(B, Hq, Hkv, S) || (D != 32 && D != 64 && D != 128 && D != 256)) return 0;
   return plan_bwd(B, Hq, Hkv, S, D).total;
 }
 
@@ -423,8 +423,8 @@ i8a_status attn_bwd(const void* q, const void* k, const void* v, const void* dou
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
     return fail(I8A_ERR_INVALID_ARG, "inputs and outputs must be 16-byte aligned");
-  if (D != 32 && D != 64 && D != 128)
-    return fail(I8A_ERR_UNSUPPORTED_HEAD_DIM, "backward head dim %d not in {32,64,128}", D);
+  if (D != 32 && D != 64 && D != 128 && D != 256)
+    return fail(I8A_ERR_UNSUPPORTED_HEAD_DIM, "backward head dim %d not in {32,64,128,256}", D);
   if (!bwd_sizes_ok(B, Hq, Hkv, S))
     return fail(I8A_ERR_INVALID_ARG, "bad sizes B=%d Hq=%d Hkv=%d S=%d", B, Hq, Hkv, S);
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale))

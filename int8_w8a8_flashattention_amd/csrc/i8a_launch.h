@@ -147,5 +147,7 @@ struct BwdArgs {
 hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, void* ws, hipStream_t stream);
 // The dQ kernel alone (launch 2 of launch_bwd; ws: the workspace of plan p).
 hipError_t launch_bwd_dq(const BwdArgs& a, const BwdPlan& p, char* ws, hipStream_t stream);
+// Its D = 256 instance (a source of its own, built without the vector-register form).
+hipError_t launch_bwd_dq256(const BwdArgs& a, const BwdPlan& p, char* ws, hipStream_t stream);
 
 }  // namespace i8a

@@ -57,7 +57,10 @@ SHAPES = [(1, 2, 2, 64, 64), (2, 4, 2, 100, 32), (1, 4, 1, 300, 128), (1, 2, 1, 
           # part has no items there and must still write its (zero) partial rows
           (1, 2, 2, 160, 64), (1, 1, 1, 129, 32),
           # a large query group (MQA, G = 16)
-          (1, 16, 1, 200, 64)]
+          (1, 16, 1, 200, 64),
+          # D = 256 (the plain dK/dV loop, the dQ kernel with its results in accumulation
+          # registers), GQA and MHA, ragged tails
+          (1, 4, 2, 150, 256), (2, 2, 2, 70, 256)]
 
 
 @pytest.mark.parametrize("causal", [True, False])
