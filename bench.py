@@ -250,9 +250,11 @@ def bench_variants(args, i8, torch, dev, q, k, v, out, ws, ms_step):
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     flags = {"hadamard": i8.FWD_HADAMARD, "v_per_channel": i8.FWD_V_PER_CHANNEL,
-             "hadamard+v_per_channel": i8.FWD_HADAMARD | i8.FWD_V_PER_CHANNEL}
+             "hadamard+v_per_channel": i8.FWD_HADAMARD | i8.FWD_V_PER_CHANNEL,
+             "q_per_block": i8.FWD_Q_PER_BLOCK}
     kw = {"hadamard": dict(hadamard=True), "v_per_channel": dict(v_per_channel=True),
-          "hadamard+v_per_channel": dict(hadamard=True, v_per_channel=True)}
+          "hadamard+v_per_channel": dict(hadamard=True, v_per_channel=True),
+          "q_per_block": dict(q_per_block=True)}
     res = {"outlier_workload": "cfg3_mha_s2048_d128_outliers: B4 H16 S2048 D128 non-causal, "
                                "1 % of channels x20 in Q and K, 4 heads x 293 rows"}
     w = workloads.cfg3(128)

@@ -128,6 +128,15 @@ i8a_status attn_int8_fwd(const void* q, const void* k, const void* v, void* out,
  */
 #define I8A_FWD_HADAMARD 1
 #define I8A_FWD_V_PER_CHANNEL 2
+/*
+ * I8A_FWD_Q_PER_BLOCK - Q quantized per warp (Attention kernels table, attn_w8a8_fwd
+ *   row: W8A8 with per-warp quantization): one scale per block of 32 query rows of a
+ *   head, the rows one wave owns, counted from the sequence start,
+ *   sq_block = fp32(max over the block's rows of max_d |q| / 127), with the codes of
+ *   each row by the usual rule against that scale.  Rows past the sequence end keep
+ *   zero codes and scale 0.  Combines with the flags above (after the rotation).
+ */
+#define I8A_FWD_Q_PER_BLOCK 4
 
 /* attn_int8_fwd with the variant flags above; arguments, workspace and errors as for
  * attn_int8_fwd (unknown flag bits are I8A_ERR_INVALID_ARG). */

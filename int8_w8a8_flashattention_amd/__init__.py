@@ -11,7 +11,7 @@ Entry points (same names as the C ABI):
 * :func:`attn_int8_fwd` - dense forward, q ``[B,Hq,S,D]``, k/v ``[B,Hkv,S,D]``.
 * :func:`attn_int8_fwd_hadamard` - the same with Q and K Hadamard-rotated first.
 * :func:`attn_int8_fwd_ex` / :func:`attn_int8_varlen_fwd_ex` - the forwards with variant
-  flags (``FWD_HADAMARD``, ``FWD_V_PER_CHANNEL``).
+  flags (``FWD_HADAMARD``, ``FWD_V_PER_CHANNEL``, ``FWD_Q_PER_BLOCK``).
 * :func:`attn_int8_varlen_fwd` - packed ragged batch, q ``[T,Hq,D]`` + ``cu_seqlens``.
 * :func:`attn_int8_debug_qk` - the forward's exact int32 scores and scales.
 * :func:`attn_int8_kvcache_fill` / :func:`attn_int8_decode` - an int8 KV cache and
@@ -33,7 +33,8 @@ import torch
 __all__ = [
     "quant_rowwise_i8", "attn_int8_fwd", "attn_int8_varlen_fwd", "attn_int8_debug_qk",
     "attn_int8_fwd_hadamard", "attn_int8_fwd_ex", "attn_int8_varlen_fwd_ex", "FWD_HADAMARD",
-    "FWD_V_PER_CHANNEL", "attn_int8_prepare_kv", "attn_int8_prepare_q", "attn_int8_attend", "attn_int8_fwd_prepared",
+    "FWD_V_PER_CHANNEL", "FWD_Q_PER_BLOCK", "attn_int8_prepare_kv", "attn_int8_prepare_q",
+    "attn_int8_attend", "attn_int8_fwd_prepared",
     "attn_int8_workspace_bytes", "attn_int8_varlen_workspace_bytes", "library_path",
     "load_library", "SCALE_FP32", "SCALE_V4", "HEAD_DIMS", "attn_int8_kvcache_bytes",
     "attn_int8_kvcache_fill", "attn_int8_decode_workspace_bytes", "attn_int8_decode",
@@ -50,6 +51,7 @@ SCALE_V4 = 4
 HEAD_DIMS = (32, 64, 128, 256)
 FWD_HADAMARD = 1
 FWD_V_PER_CHANNEL = 2
+FWD_Q_PER_BLOCK = 4
 VCACHE_INT8 = 1
 VCACHE_FP16 = 2
 _VFORMATS = {"int8": VCACHE_INT8, "fp16": VCACHE_FP16}

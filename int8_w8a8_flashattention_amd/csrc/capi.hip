@@ -187,13 +187,14 @@ i8a_status attn_int8_fwd_ex(const void* q, const void* k, const void* v, void* o
                             size_t workspace_bytes, void* stream) {
   i8a_status st = check_common(q, k, v, out, Hq, Hkv, D, softmax_scale, causal, workspace);
   if (st != I8A_OK) return st;
-  if (flags & ~(I8A_FWD_HADAMARD | I8A_FWD_V_PER_CHANNEL))
+  if (flags & ~(I8A_FWD_HADAMARD | I8A_FWD_V_PER_CHANNEL | I8A_FWD_Q_PER_BLOCK))
     return fail(I8A_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if (B < 1 || S < 1 || B > kMaxGridYZ)
     return fail(I8A_ERR_INVALID_ARG, "need 1 <= B <= %d and S >= 1", kMaxGridYZ);
   if ((int64_t)B * S > kMaxTokens) return fail(I8A_ERR_INVALID_ARG, "B*S too large");
   FwdGeom g{q, k, v, out, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D, softmax_scale, causal,
             (flags & I8A_FWD_HADAMARD) ? 1 : 0, (flags & I8A_FWD_V_PER_CHANNEL) ? 1 : 0};
+  g.qblk = (flags & I8A_FWD_Q_PER_BLOCK) ? 1 : 0;
   return run_phases(g, PH_KV | PH_Q | PH_ATTN, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
@@ -260,7 +261,7 @@ i8a_status attn_int8_varlen_fwd_ex(const void* q, const void* k, const void* v, 
                                    int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t D,
                                    float softmax_scale, int32_t causal, int32_t flags,
                                    void* workspace, size_t workspace_bytes, void* stream) {
-  if (flags & ~(I8A_FWD_HADAMARD | I8A_FWD_V_PER_CHANNEL))
+  if (flags & ~(I8A_FWD_HADAMARD | I8A_FWD_V_PER_CHANNEL | I8A_FWD_Q_PER_BLOCK))
     return fail(I8A_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if (!cu_seqlens) return fail(I8A_ERR_INVALID_ARG, "null cu_seqlens");
   if (!aligned(cu_seqlens, 4)) return fail(I8A_ERR_INVALID_ARG, "misaligned cu_seqlens");
@@ -282,6 +283,7 @@ i8a_status attn_int8_varlen_fwd_ex(const void* q, const void* k, const void* v, 
   FwdGeom g{q, k, v, out, cu_seqlens, nseq, 0, max_seqlen, total_tokens, Hq, Hkv, D,
             softmax_scale, causal, (flags & I8A_FWD_HADAMARD) ? 1 : 0,
             (flags & I8A_FWD_V_PER_CHANNEL) ? 1 : 0};
+  g.qblk = (flags & I8A_FWD_Q_PER_BLOCK) ? 1 : 0;
   return run_phases(g, PH_KV | PH_Q | PH_ATTN, workspace, workspace_bytes, (hipStream_t)stream);
 }
 

@@ -58,6 +58,7 @@ struct FwdGeom {
   int causal;
   int rot;  // Q and K rows Hadamard-rotated before quantization (logits take 1/D)
   int vch;  // V quantized per channel over each sequence's tokens (else per token)
+  int qblk = 0;  // Q quantized with one scale per 32-row block (else per row)
 };
 
 hipError_t launch_quant_rowwise(const void* x, int64_t rows, int32_t d, const float* sub_mean,

@@ -348,11 +348,14 @@ __device__ __forceinline__ void prep_k_body(const _Float16* __restrict__ k, cons
 constexpr int QCH = 64;
 static_assert(BQ % QCH == 0 && QCH % 32 == 0, "Q chunks hold whole 32-row blocks");
 
+// qblk: one scale per block of 32 rows (counted from the sequence start) instead of one
+// per row: the block's largest row absolute maximum sets the scale of all its rows.
 template <int D, bool ROT>
 __device__ __forceinline__ void prep_q_body(const _Float16* __restrict__ q, const Act& act,
                                             const Seqs& seqs, int64_t Qpad,
                                             int8_t* __restrict__ q8, float* __restrict__ qs,
-                                            int c, int h, int s, int8_t* frag) {
+                                            int c, int h, int s, int8_t* frag, int qblk) {
+  __shared__ float rowmax[QCH];
   constexpr int G = D / 8;       // lanes per row
   constexpr int RPP = 256 / G;   // rows per pass
   constexpr int NP = QCH / RPP;  // rows per thread
@@ -372,28 +375,39 @@ __device__ __forceinline__ void prep_q_body(const _Float16* __restrict__ q, cons
     const int t = r0 + i * RPP + rsub;
     if (t < L) xr[i] = *reinterpret_cast<const v8h*>(q + act.off(start, h, t) + lc * 8);
   }
+  float x[NP][8], amax[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int n = i * RPP + rsub;
     const bool real = r0 + n < L;
-    float x[8];
-    float amax = 0.0f;
-    if constexpr (ROT) {
+    amax[i] = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = real ? (float)xr[i][j] : 0.0f;
-      fwht_row<G>(x, lc);
+    for (int j = 0; j < 8; ++j) x[i][j] = real ? (float)xr[i][j] : 0.0f;
+    if constexpr (ROT) fwht_row<G>(x[i], lc);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
-    } else if (real) {
+    for (int j = 0; j < 8; ++j) amax[i] = fmaxf(amax[i], fabsf(x[i][j]));
+    amax[i] = group_max<G>(amax[i]);
+  }
+  if (qblk) {
+    // The block maxima through LDS (a max is exact in any order).
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        x[j] = (float)xr[i][j];
-        amax = fmaxf(amax, fabsf(x[j]));
-      }
+    for (int i = 0; i < NP; ++i)
+      if (lc == 0) rowmax[i * RPP + rsub] = amax[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int b0 = (i * RPP + rsub) & ~31;
+      float m = 0.0f;
+      for (int r = 0; r < 32; ++r) m = fmaxf(m, rowmax[b0 + r]);
+      amax[i] = m;
     }
-    amax = group_max<G>(amax);
-    const RowQ rq(real ? row_scale(amax, 24) : 0.0f);
-    const uint2 codes = real ? rq.pack8(x) : make_uint2(0u, 0u);
+  }
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int n = i * RPP + rsub;
+    const bool real = r0 + n < L;
+    const RowQ rq(real ? row_scale(amax[i], 24) : 0.0f);
+    const uint2 codes = real ? rq.pack8(x[i]) : make_uint2(0u, 0u);
     *reinterpret_cast<uint2*>(frag + (n >> 5) * 32 * D + qfrag_off(n & 31, lc * 8)) = codes;
     if (lc == 0) qs[slot + n] = rq.s;
   }
@@ -422,7 +436,7 @@ __global__ __launch_bounds__(256) void prep_kvq_kernel(
     int tpw, int64_t Ppad, int64_t Qpad, int nqc, const int64_t* __restrict__ kpart,
     const float* __restrict__ vpart, float* __restrict__ kmean_ws, float* __restrict__ svc_ws,
     float* __restrict__ sv_ws, char* __restrict__ tiles, int8_t* __restrict__ q8,
-    float* __restrict__ qs, int nk) {
+    float* __restrict__ qs, int nk, int qblk) {
   __shared__ PrepShared<D> sh;
   int b = blockIdx.x;
   if (b < 2 * nk) {
@@ -440,7 +454,7 @@ __global__ __launch_bounds__(256) void prep_kvq_kernel(
     b -= 2 * nk;
     const int c = b % nqc;
     b /= nqc;
-    prep_q_body<D, ROT>(q, aq, seqs, Qpad, q8, qs, c, b % Hq, b / Hq, sh.qfrag);
+    prep_q_body<D, ROT>(q, aq, seqs, Qpad, q8, qs, c, b % Hq, b / Hq, sh.qfrag, qblk);
   }
 }
 
@@ -510,7 +524,7 @@ static hipError_t prep_d(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, b
         reinterpret_cast<float*>(w + p.off_kmean), reinterpret_cast<float*>(w + p.off_svc),
         reinterpret_cast<float*>(w + p.off_sv), w + p.off_tiles,
         reinterpret_cast<int8_t*>(w + p.off_q8), reinterpret_cast<float*>(w + p.off_qs),
-        (int)nk);
+        (int)nk, g.qblk);
   return hipGetLastError();
 }
 

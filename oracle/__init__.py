@@ -44,6 +44,7 @@ from .attn_ref import (  # noqa: F401
     kmean,
     quant_rows,
     quant_cols,
+    quant_row_blocks,
     quantize_qkv,
     fwht_f32,
     qk_int32,

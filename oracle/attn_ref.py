@@ -137,6 +137,32 @@ def quant_rows(x32: np.ndarray, scale_bits: int = QK_SCALE_BITS):
     return codes, scale.astype(np.float32)
 
 
+def quant_row_blocks(x32: np.ndarray, block: int = 32):
+    """Q quantized per warp (R18): rows ``[..., S, D]`` in blocks of ``block`` rows from
+    row 0; each block's scale is ``fp32(max over its rows of max |x| / 127)`` (the Q/K
+    rule, no significand rounding), and each row's codes follow R3 against its block's
+    scale.  Returns ``(codes int8 [..., S, D], scales fp32 [..., S])`` (a row carries its
+    block's scale).
+    """
+    x32 = np.asarray(x32)
+    if x32.dtype != np.float32:
+        raise TypeError("quant_row_blocks expects fp32 rows")
+    S = x32.shape[-2]
+    a = np.max(np.abs(x32), axis=-1)  # [..., S]
+    nb = (S + block - 1) // block
+    pad = np.zeros(a.shape[:-1] + (nb * block,), dtype=np.float32)
+    pad[..., :S] = a
+    bmax = pad.reshape(a.shape[:-1] + (nb, block)).max(axis=-1)  # [..., nb]
+    t = np.repeat(bmax, block, axis=-1)[..., :S] / np.float32(127.0)
+    assert t.dtype == np.float32
+    safe = np.where(t > 0, t, np.float32(1.0)).astype(np.float32)
+    ratio = x32 / safe[..., None]
+    assert ratio.dtype == np.float32
+    codes = np.clip(np.rint(ratio), -127, 127)
+    codes = np.where(t[..., None] > 0, codes, 0).astype(np.int8)
+    return codes, t.astype(np.float32)
+
+
 def fwht_f32(x32: np.ndarray) -> np.ndarray:
     """Unnormalized fast Walsh-Hadamard transform of the last axis (R13), in fp32,
     stages in the order s = 0, 1, ...: the pair (x[i], x[i + 2^s]) with bit s of i
@@ -165,16 +191,18 @@ def quant_cols(x32: np.ndarray, scale_bits: int = 4):
     return np.ascontiguousarray(np.swapaxes(codes, -1, -2)), scale
 
 
-def quantize_qkv(q16, k16, v16, hadamard=False, v_per_channel=False):
+def quantize_qkv(q16, k16, v16, hadamard=False, v_per_channel=False, q_per_block=False):
     """Quantize dense BHSD q/k/v as the forward does internally (with ``hadamard``,
     Q and the mean-smoothed K rows rotated first, R13; with ``v_per_channel``, V
-    quantized per channel over the tokens, R14).
+    quantized per channel over the tokens, R14; with ``q_per_block``, Q quantized with
+    one scale per 32-row block, R18).
 
     Returns a dict with ``q8, sq, k8, sk, v8, sv, kmean``; ``sv`` is ``[B, Hkv, S]``
     per token or ``[B, Hkv, D]`` per channel.
     """
     q32 = q16.astype(np.float32)
-    q8, sq = quant_rows(fwht_f32(q32) if hadamard else q32)
+    qx = fwht_f32(q32) if hadamard else q32
+    q8, sq = quant_row_blocks(qx) if q_per_block else quant_rows(qx)
     m = kmean(k16)  # [B, Hkv, D]
     ksm = k16.astype(np.float32) - m[..., None, :]
     assert ksm.dtype == np.float32
@@ -232,7 +260,7 @@ def attn_core(q8, sq, k8, sk, v8, sv, softmax_scale, causal, rows=None, logit_fa
 
 
 def attn_int8_fwd(q16, k16, v16, causal=True, softmax_scale=None, heads=None, rows=None,
-                  hadamard=False, v_per_channel=False):
+                  hadamard=False, v_per_channel=False, q_per_block=False):
     """The dense forward: fp16 ``q[B,Hq,S,D]``, ``k/v[B,Hkv,S,D]`` -> fp64 O.
 
     ``heads`` (list of (b, h)) and ``rows`` restrict the output to a sample;
@@ -247,7 +275,7 @@ def attn_int8_fwd(q16, k16, v16, causal=True, softmax_scale=None, heads=None, ro
         raise ValueError("Hq must be a multiple of Hkv")
     G = Hq // Hkv
     sm = default_softmax_scale(D) if softmax_scale is None else np.float32(softmax_scale)
-    qz = quantize_qkv(q16, k16, v16, hadamard, v_per_channel)
+    qz = quantize_qkv(q16, k16, v16, hadamard, v_per_channel, q_per_block)
     # The 1/D of the rotation multiplies the logits exactly (D is a power of two).
     extra = 1.0 / D if hadamard else 1.0
     sel = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
@@ -264,7 +292,7 @@ def attn_int8_fwd(q16, k16, v16, causal=True, softmax_scale=None, heads=None, ro
 
 
 def attn_int8_varlen_fwd(q16, k16, v16, cu_seqlens, causal=True, softmax_scale=None,
-                         hadamard=False, v_per_channel=False):
+                         hadamard=False, v_per_channel=False, q_per_block=False):
     """The varlen forward (R11): packed ``q[T,Hq,D]``, ``k/v[T,Hkv,D]``.
 
     Each sequence ``cu[i]:cu[i+1]`` is quantized (its own K mean, and its own V
@@ -282,7 +310,7 @@ def attn_int8_varlen_fwd(q16, k16, v16, cu_seqlens, causal=True, softmax_scale=N
         ks = np.ascontiguousarray(k16[a:b].transpose(1, 0, 2))[None]
         vs = np.ascontiguousarray(v16[a:b].transpose(1, 0, 2))[None]
         o = attn_int8_fwd(qs, ks, vs, causal, softmax_scale, hadamard=hadamard,
-                          v_per_channel=v_per_channel)[0]
+                          v_per_channel=v_per_channel, q_per_block=q_per_block)[0]
         out[a:b] = o.transpose(1, 0, 2)
     return out
 

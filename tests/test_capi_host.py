@@ -159,7 +159,7 @@ def test_python_binding_validates_before_the_library():
 
 
 def test_forward_ex_rejects_unknown_flags(lib):
-    st = lib.attn_int8_fwd_ex(FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 64, 64, 0.125, 1, 4, FAKE,
+    st = lib.attn_int8_fwd_ex(FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 64, 64, 0.125, 1, 8, FAKE,
                               1 << 40, None)
     assert st == INVALID
     assert b"flags" in lib.i8a_last_error()

@@ -102,10 +102,14 @@ def test_rotated_forward_outlier_workload_gains_sqnr(D):
 
 
 VARIANTS = [(i8.FWD_V_PER_CHANNEL, dict(v_per_channel=True)),
-            (i8.FWD_HADAMARD | i8.FWD_V_PER_CHANNEL, dict(hadamard=True, v_per_channel=True))]
+            (i8.FWD_HADAMARD | i8.FWD_V_PER_CHANNEL, dict(hadamard=True, v_per_channel=True)),
+            (i8.FWD_Q_PER_BLOCK, dict(q_per_block=True)),
+            (i8.FWD_HADAMARD | i8.FWD_V_PER_CHANNEL | i8.FWD_Q_PER_BLOCK,
+             dict(hadamard=True, v_per_channel=True, q_per_block=True))]
+VARIANT_IDS = ["vch", "rot+vch", "qblk", "rot+vch+qblk"]
 
 
-@pytest.mark.parametrize("variant", VARIANTS, ids=["vch", "rot+vch"])
+@pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS)
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
 def test_flagged_forward_small_shapes(shape, causal, variant):
@@ -127,7 +131,7 @@ def test_flagged_forward_small_shapes(shape, causal, variant):
     check_close(out, ref, f"{shape} flags={flags}")
 
 
-@pytest.mark.parametrize("variant", VARIANTS, ids=["vch", "rot+vch"])
+@pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS)
 def test_flagged_varlen_ragged_with_empty_sequences(variant):
     flags, kw = variant
     say(f"varlen flags={flags}")

@@ -642,3 +642,50 @@ def test_bwd_uniform_attention_closed_form():
     dsc = (dp - dp.mean(1, keepdims=True)) / 10
     np.testing.assert_allclose(dq[0, 0], float(oracle.default_softmax_scale(8)) * dsc @ kk,
                                rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- R18 Q per block
+
+def test_q_per_block_scale_is_the_blocks_largest_row_scale():
+    # One scale per 32 rows: exactly the largest of the per-row scales of the block (a
+    # max of |x| / 127 is the max of the rows' values), ragged last block included.
+    x = np.random.default_rng(31).standard_normal((2, 3, 70, 16)).astype(np.float32)
+    x[0, 1, 40] *= 50.0  # one outlier row in the second block
+    c, s = oracle.quant_row_blocks(x)
+    _, sr = oracle.quant_rows(x)
+    for b0 in range(0, 70, 32):
+        blk = sr[..., b0:b0 + 32]
+        assert np.array_equal(s[..., b0:b0 + 32],
+                              np.broadcast_to(blk.max(axis=-1, keepdims=True), blk.shape))
+    assert s[0, 1, 40] == sr[0, 1, 40] and s[0, 1, 63] == sr[0, 1, 40]
+
+
+def test_q_per_block_row_with_the_block_max_keeps_its_row_codes():
+    # The row that holds a block's maximum is quantized against its own row scale, so
+    # its codes equal the per-row codes; other rows of the block have coarser codes
+    # (never larger in magnitude than their per-row codes).
+    x = np.random.default_rng(32).standard_normal((4, 64, 32)).astype(np.float32)
+    c, s = oracle.quant_row_blocks(x)
+    cr, sr = oracle.quant_rows(x)
+    for h in range(4):
+        for b0 in (0, 32):
+            r = b0 + int(np.argmax(sr[h, b0:b0 + 32]))
+            assert np.array_equal(c[h, r], cr[h, r])
+            assert np.all(np.abs(c[h, b0:b0 + 32].astype(int)) <= np.abs(cr[h, b0:b0 + 32].astype(int)))
+
+
+def test_q_per_block_forward_equals_sdpa_on_its_dequantized_operands():
+    # The forward with per-block Q is attention on the dequantized operands of that
+    # quantization (torch's fp64 SDPA), causal GQA with a ragged tail.
+    import torch
+    w = workloads.dense(33, 1, 4, 2, 70, 32, True, k_offset=1.0)
+    got = oracle.attn_int8_fwd(w.q, w.k, w.v, True, q_per_block=True)
+    z = oracle.quantize_qkv(w.q, w.k, w.v, q_per_block=True)
+    qd = torch.from_numpy(z["q8"].astype(np.float64) * z["sq"][..., None])
+    kd = torch.from_numpy(z["k8"].astype(np.float64) * z["sk"][..., None])
+    vd = torch.from_numpy(z["v8"].astype(np.float64) * z["sv"][..., None])
+    kd = kd.repeat_interleave(2, dim=1)
+    vd = vd.repeat_interleave(2, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qd, kd, vd, is_causal=True, scale=float(np.float32(1 / np.sqrt(32)))).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-9, atol=1e-12)
