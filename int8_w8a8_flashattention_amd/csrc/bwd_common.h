@@ -45,28 +45,28 @@ __device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, ui
 }
 #pragma clang diagnostic pop
 
-// Copy of one 32-token operand tile (64 * D contiguous bytes) into LDS by the four waves
-// of a workgroup: wave w's lanes move the 16-byte chunks 256 r + 64 w + lane.  The
+// Copy of one 32-token operand tile (64 * D contiguous bytes) into LDS by the NT threads
+// of a workgroup: wave w's lanes move the 16-byte chunks NT r + 64 w + lane.  The
 // lanes' offsets are computed once; a copy is then a scalar base, an m0 write and the
 // load.  The chunk count 4 D is a multiple of 64, so a wave copies whole rows of 64
 // chunks or none.
-template <int D>
+template <int D, int NT = 256>
 struct TileCopy {
   static constexpr int NCH = 64 * D / 16;
-  static constexpr int R = (NCH + 255) / 256;
+  static constexpr int R = (NCH + NT - 1) / NT;
   uint32_t voff[R];
   int w;
   __device__ __forceinline__ explicit TileCopy(int tid)
       : w(__builtin_amdgcn_readfirstlane(tid >> 6)) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) voff[r] = (uint32_t)(r * 256 + tid) * 16;
+    for (int r = 0; r < R; ++r) voff[r] = (uint32_t)(r * NT + tid) * 16;
   }
   __device__ __forceinline__ void operator()(const char* src, char* dst) const {
     const uint32_t base = lds_addr(dst);
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (NCH % 256 == 0 || r * 256 + w * 64 < NCH)  // wave-uniform
-        lds_dma16_s(src, voff[r], base + (uint32_t)(r * 256 + w * 64) * 16);
+      if (NCH % NT == 0 || r * NT + w * 64 < NCH)  // wave-uniform
+        lds_dma16_s(src, voff[r], base + (uint32_t)(r * NT + w * 64) * 16);
   }
 };
 

@@ -12,13 +12,20 @@
 namespace i8a {
 namespace bwd {
 
+// Waves per dQ workgroup (32 queries each); the key blocks' tiles in LDS serve them all.
+// At D = 256 a wave needs more than half of a SIMD's registers, so four.
+template <int D>
+constexpr int dq_waves() {
+  return D <= 128 ? 8 : 4;
+}
+
 // ----------------------------------------------------------------------------------
-// Launch 2: dQ.  Workgroup = 4 waves = 128 queries of one (batch, query head); wave w
-// owns queries q0 = 128 * blockIdx.x + 32 w .. +31, lane l query q0 + l % 32.  The key
+// Launch 2: dQ.  Workgroup = dq_waves<D>() waves of 32 queries of one (batch, query
+// head); wave w owns queries q0 = qblk0 + 32 w .. +31, lane l query q0 + l % 32.  The key
 // blocks' operand tiles (K and V in row order, K in column order) stream through a
-// two-stage LDS ring shared by the four waves, one block ahead.
+// two-stage LDS ring shared by the workgroup's waves, one block ahead.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(
+__global__ __launch_bounds__(64 * dq_waves<D>()) void bwd_dq_kernel(
     const _Float16* __restrict__ qr, const _Float16* __restrict__ dor,
     const _Float16* __restrict__ kr, const _Float16* __restrict__ kc,
     const _Float16* __restrict__ vr, float* __restrict__ lse2, float* __restrict__ dvec,
@@ -32,7 +39,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, m = lane & 31, hh = lane >> 5;
-  const int qblk0 = 128 * ((nrb + 3) / 4 - 1 - (int)(blockIdx.x / Hq / B));
+  const int qblk0 =
+      32 * dq_waves<D>() * ((nrb + dq_waves<D>() - 1) / dq_waves<D>() - 1 - (int)(blockIdx.x / Hq / B));
   const int q0 = qblk0 + 32 * w;
   const bool active = q0 < nrb * 32;  // waves past the padded length only copy
   const int64_t Sp = (int64_t)nrb * 32;
@@ -41,7 +49,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
   const char* krb = reinterpret_cast<const char*>(kr + kbase * D);
   const char* vrb = reinterpret_cast<const char*>(vr + kbase * D);
   const char* kcb = reinterpret_cast<const char*>(kc + kbase * D);
-  const int nkb_wg = CAUSAL ? min(nrb, qblk0 / 32 + 4) : nrb;  // key blocks of the group
+  const int nkb_wg = CAUSAL ? min(nrb, qblk0 / 32 + dq_waves<D>()) : nrb;  // the group's key blocks
   const int nkb = CAUSAL ? q0 / 32 + 1 : nrb;                  // this wave's
   const int qi = q0 + m;
 
@@ -65,7 +73,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 #pragma unroll
   for (int kd = 0; kd < NKD; ++kd) asm volatile("" : : "v"(qf[kd]), "v"(df[kd]));
 
-  const TileCopy<D> copy(tid);
+  const TileCopy<D, 64 * dq_waves<D>()> copy(tid);
   auto issue = [&](int kb, int st, bool with_kc) {
     copy(krb + (int64_t)kb * TB, smem + (st * 3 + 0) * TB);
     copy(vrb + (int64_t)kb * TB, smem + (st * 3 + 1) * TB);
@@ -192,10 +200,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 
 template <int D, bool C>
 static hipError_t dq_d(const BwdArgs& a, const BwdPlan& p, char* ws, hipStream_t stream) {
-  const int64_t ngrp = (p.nrb + 3) / 4;
+  const int64_t ngrp = (p.nrb + dq_waves<D>() - 1) / dq_waves<D>();
   if (ngrp * a.B * a.Hq > 0x7fffffff) return hipErrorInvalidValue;
   auto H = [&](size_t off) { return reinterpret_cast<_Float16*>(ws + off); };
-  bwd_dq_kernel<D, C><<<dim3((unsigned)(ngrp * a.B * a.Hq)), 256, 0, stream>>>(
+  bwd_dq_kernel<D, C><<<dim3((unsigned)(ngrp * a.B * a.Hq)), 64 * dq_waves<D>(), 0, stream>>>(
       H(p.off_qr), H(p.off_dor), H(p.off_kr), H(p.off_kc), H(p.off_vr),
       reinterpret_cast<float*>(ws + p.off_lse), reinterpret_cast<float*>(ws + p.off_dvec), a.dq,
       a.B, a.Hq, a.Hkv, a.S, p.nrb, a.softmax_scale * 1.4426950408889634f, a.softmax_scale);
