@@ -32,8 +32,8 @@ __global__ __launch_bounds__(64 * dq_waves<D>()) void bwd_dq_kernel(
     float* __restrict__ dq, int B, int Hq, int Hkv, int S, int nrb, float c_log2, float scale) {
   constexpr int NKD = D / 16, NDB = D / 32, TB = 64 * D;  // TB: bytes of a 32-token tile
   __shared__ __attribute__((aligned(16))) char smem[2 * 3 * TB];
-  // blockIdx.x = ((group of 32 dq_waves<D>() queries, from the last) x B + batch) x Hq + head: under
-  // the causal mask the heaviest blocks of every head are dispatched first.
+  // blockIdx.x = ((group of 32 dq_waves<D>() queries, from the last) x B + batch) x Hq
+  // + head: under the causal mask the heaviest groups of every head are dispatched first.
   const int h = blockIdx.x % Hq, b = (blockIdx.x / Hq) % B;
   const int g = h / (Hq / Hkv);
   const int tid = threadIdx.x;
