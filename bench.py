@@ -392,7 +392,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the forward shards by kv-head groups with no communication; see DESIGN.md)",
+              "(the forward shards by kv-head groups with no communication)",
               file=sys.stderr)
         sys.exit(2)
 
