@@ -163,3 +163,17 @@ def test_forward_ex_rejects_unknown_flags(lib):
                               1 << 40, None)
     assert st == INVALID
     assert b"flags" in lib.i8a_last_error()
+
+
+def test_backward_head_dims_and_arguments(lib):
+    # Head dims 32, 64, 128 and 256 are supported (workspace size > 0); others are
+    # rejected on the host before any launch, as are bad sizes and a short workspace.
+    for d in (32, 64, 128, 256):
+        assert lib.attn_bwd_workspace_bytes(1, 4, 2, 300, d) > 0
+    assert lib.attn_bwd_workspace_bytes(1, 4, 2, 300, 48) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 4, 3, 300, 64) == 0  # Hq % Hkv != 0
+    need = lib.attn_bwd_workspace_bytes(1, 4, 2, 300, 256)
+    args = [FAKE] * 7 + [1, 4, 2, 300]
+    assert lib.attn_bwd(*args, 48, 0.1, 1, FAKE, need, None) == HEADDIM
+    assert lib.attn_bwd(*args, 256, 0.0, 1, FAKE, need, None) == INVALID
+    assert lib.attn_bwd(*args, 256, 0.1, 1, FAKE, need - 1, None) == WSSMALL
