@@ -138,3 +138,17 @@ def test_bwd_is_deterministic():
     b = run(w, do, True)
     for name, x, y in zip(("dq", "dk", "dv"), a, b):
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), name
+
+
+def test_bwd_noncausal_large_one_kv_group():
+    # Non-causal (no split, no combine) at S = 2048, D = 128, GQA: the whole call runs on
+    # the GPU, the oracle checks kv head 1 and its 4 query heads.
+    w = workloads.dense(219, 1, 8, 2, 2048, 128, False, k_offset=1.0)
+    say("bwd non-causal S2048 D128, kv group 1")
+    do = np.random.Generator(np.random.PCG64(220)).standard_normal(w.q.shape).astype(np.float16)
+    dq, dk, dv = run(w, do, False)
+    sl = slice(4, 8)
+    ref = oracle.attn_bwd_exact(w.q[:, sl], w.k[:, 1:2], w.v[:, 1:2], do[:, sl], False)
+    check_grad(dq[:, sl], ref[0], "non-causal dq")
+    check_grad(dk[:, 1:2], ref[1], "non-causal dk")
+    check_grad(dv[:, 1:2], ref[2], "non-causal dv")
