@@ -1,13 +1,12 @@
 // attn_kernels.hip - the INT8 W8A8 FlashAttention-2 forward on gfx950.
 //
-// One workgroup = 4 waves = 128 query rows of one head.  Each wave owns 32 rows and
-// keeps, per lane, one query's running max, sum and 32 x D output accumulator
-// column.  Per 64-key tile:
+// Each wave owns 32 query rows of one head and keeps, per lane, one query's running
+// max, sum and 32 x D output accumulator column.  Per 64-key tile:
 //   S^T = K . Q^T     v_mfma_i32_32x32x32_i8   (exact int32)
 //   t   = f32(S^T) * sk_j                      (the query scale and softmax scale are
 //   p   = exp2(t * qsc - M)                     one per-lane factor qsc)
 //   O^T += V^T . P^T  v_mfma_f32_32x32x16_f16  (P rounded to fp16, V exact in fp16)
-//   l   += sum of the same fp16 P values      (v_dot2_f32_f16)
+//   l   += sum of the same fp16 P values
 // so the normalized output is a weighted mean with identical weights in numerator
 // and denominator.  The running max M is only raised (with a rescale of O and l)
 // when a tile's max exceeds it by more than TAU in log2 units, which bounds every
@@ -17,15 +16,25 @@
 // the Q fragments go straight to registers with coalesced 16-byte loads, and the K/V
 // tile copy into LDS is linear, so every LDS operand read is a conflict-free 16-byte
 // read.
+//
+// Two kernels: attn_pipe_kernel (head dims up to 128: 8 waves, 256 query rows per
+// workgroup, software-pipelined over two tiles) and attn_fwd_kernel (head dim 256: 4
+// waves, 128 rows, one tile at a time; its accumulators and Q fragments leave no room
+// for a second tile in flight).
 #include <float.h>
+
+#include <type_traits>
 
 #include "i8a_device.h"
 #include "i8a_launch.h"
 
 namespace i8a {
 
-constexpr int BM = BQ;       // query rows per workgroup
-constexpr float TAU = 8.0f;  // lazy-rescale threshold, log2 units
+constexpr int BM = 128;      // query rows per workgroup of the one-tile kernel
+#ifndef PIPE_TAU
+#define PIPE_TAU 12.0f
+#endif
+constexpr float TAU = PIPE_TAU;  // lazy-rescale threshold, log2 units
 
 template <int D>
 struct Lay {
@@ -282,6 +291,465 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 }
 
 // ----------------------------------------------------------------------------------
+// Software-pipelined forward for D <= 128: one workgroup of 8 waves (256 query rows)
+// per CU, a four-stage LDS ring, the row sum on the MFMA.
+//
+// A 32 x 64 wave-tile needs 24 MFMAs (8 int8 for the scores, 16 fp16 for P.V) and
+// about 160 vector instructions of softmax (per score: conversion, key scale,
+// exponent FMA, exponential, half a pack, a share of the max).  A wave issues vector
+// instructions at one per four cycles or so, and only about six fit under one 32-cycle
+// MFMA, so every phase of a tile needs MFMAs to run beside its vector work.  The tiles
+// therefore run as a pipeline over two tiles: with tile j's scores converted
+// (t = f32(S) * sk) and its max folded into M, iteration j issues the score MFMAs of
+// tile j+1 and the P.V MFMAs of tile j, one per slot, and spreads over the same slots
+// the exponentials of tile j, the conversion (and mask) of tile j+1's scores, its
+// row max and the rescale decision (pipe_step).  M is raised after the slots if a row
+// needs it (rare: the rescale of O and l waits for tile j's P.V).  The row sum l is
+// a fifth fp16 MFMA per 16 keys with an all-ones A operand: every row of its 32 x 32
+// result is the sum of the same fp16 P values the P.V product consumes (register 0 is
+// read at the end), which keeps the vector unit free of the sum; dot-product
+// instructions stall behind a running MFMA.
+//
+// The ring holds tiles j (V for P.V), j+1 (K and scales), j+2 (landed) and j+3 (in
+// flight): every wave copies its share of tile j+3 into the stage tile j-1 left, one
+// instruction every few slots of iteration j, and waits for its share of tile j+2 at
+// the end of it, before the one barrier of the iteration.
+//
+// Under the causal mask a wave stops computing after its diagonal tile and from then
+// on only copies and passes the barriers; the two waves of each SIMD take the row
+// blocks b and 7 - b of the tile, so every SIMD gets the same number of tiles.
+
+// Copy one prepared tile block into an LDS stage with direct-to-LDS loads that the
+// compiler does not track: the waits are explicit (vm_wait), so no compiler-inserted
+// wait makes a tile's work wait for the next tile's copy.  Every round moves 4 KB: the
+// global base and the LDS base (M0) are scalars, the lane's byte offset 16 * tid is the
+// one vector operand of every round.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16_sbase(const char* sbase, uint32_t voff,
+                                                uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+// The same for the lanes in `lanes` only (a wave-wide mask), with EXEC narrowed and
+// restored inside the one statement, so the caller gets no branch.  With no lane set
+// the load runs with EXEC = 0 and moves nothing.
+__device__ __forceinline__ void lds_dma16_sbase_lanes(const char* sbase, uint32_t voff,
+                                                      uint32_t lds_base, uint64_t lanes) {
+  uint64_t saved;
+  asm volatile(
+      "s_and_saveexec_b64 %0, %4\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b64 exec, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "s"(lanes)
+      : "memory", "m0", "scc");
+}
+#pragma clang diagnostic pop
+
+// Rounds of NW * 1 KB: the last one may be partial, so waves own different numbers of
+// copy instructions per tile (dma_count).
+template <int D, int NW>
+struct Dma {
+  static constexpr int NT = 64 * NW;  // threads
+  static constexpr int ROUNDS = (Lay<D>::NCH + NT - 1) / NT;
+  static __device__ __forceinline__ int count(int w) {
+    int n = 0;
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) n += (r * NT + 64 * w < Lay<D>::NCH) ? 1 : 0;
+    return n;
+  }
+};
+
+template <int D, int NW>
+__device__ __forceinline__ void copy_tile_dma(const char* __restrict__ src, char* stage, int tid,
+                                              int w) {
+  using LY = Lay<D>;
+  using DM = Dma<D, NW>;
+  const uint32_t voff = 16u * (uint32_t)tid;
+  const uint32_t lds0 = lds_addr(stage);
+#pragma unroll
+  for (int r = 0; r < DM::ROUNDS; ++r) {
+    const int c0 = r * DM::NT + w * 64;  // this wave's first chunk of the round (uniform)
+    if (r + 1 < DM::ROUNDS || c0 + 64 <= LY::NCH) {
+      lds_dma16_sbase(src + r * DM::NT * 16, voff, lds0 + (uint32_t)(r * DM::NT * 16 + w * 1024));
+    } else if (c0 < LY::NCH) {
+      if ((tid & 63) < LY::NCH - c0)
+        lds_dma16_sbase(src + r * DM::NT * 16, voff,
+                        lds0 + (uint32_t)(r * DM::NT * 16 + w * 1024));
+    }
+  }
+}
+
+// Round r of a tile copy for this wave (copy_tile_dma is all rounds at once).  Only the
+// last round can be partial; there the lanes past the tile's end are masked off, with
+// no wave-uniform branch, so an unrolled caller stays one basic block.
+template <int D, int NW>
+__device__ __forceinline__ void copy_tile_round(const char* __restrict__ src, char* stage, int tid,
+                                                int w, int r) {
+  using LY = Lay<D>;
+  using DM = Dma<D, NW>;
+  const uint32_t lds = lds_addr(stage) + (uint32_t)(r * DM::NT * 16 + w * 1024);
+  if (r + 1 < DM::ROUNDS || (LY::NCH % DM::NT) == 0)
+    lds_dma16_sbase(src + r * DM::NT * 16, 16u * (uint32_t)tid, lds);
+  else
+    lds_dma16_sbase_lanes(src + r * DM::NT * 16, 16u * (uint32_t)tid, lds,
+                          __builtin_amdgcn_ballot_w64(r * DM::NT + tid < LY::NCH));
+}
+
+// Wait until at most n of this wave's vector-memory loads are outstanding (n uniform).
+__device__ __forceinline__ void vm_wait_n(int n) {
+  switch (n) {
+    case 0: vm_wait<0>(); break;
+    case 1: vm_wait<1>(); break;
+    case 2: vm_wait<2>(); break;
+    case 3: vm_wait<3>(); break;
+    case 4: vm_wait<4>(); break;
+    case 5: vm_wait<5>(); break;
+    case 6: vm_wait<6>(); break;
+    case 7: vm_wait<7>(); break;
+    default: vm_wait<0>(); break;
+  }
+}
+
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
+    const int8_t* __restrict__ q8, const float* __restrict__ qs, int64_t Qpad,
+    _Float16* __restrict__ out, Act aq, Seqs seqs, int Hq, int Hkv, int nseq, int xcd_map,
+    float qk_log2, const char* __restrict__ tiles, int64_t Ppad) {
+  using LY = Lay<D>;
+  using DM = Dma<D, NW>;
+  constexpr int NKB = LY::NKB;
+  constexpr int BMW = 32 * NW;          // query rows per workgroup
+  constexpr int NS = NW >= 8 ? 4 : 3;   // ring stages
+  static_assert(BQ % BMW == 0, "query tiles stay inside a sequence's padded Q slots");
+  __shared__ __attribute__((aligned(16))) char smem[NS * LY::STAGE];
+
+  int slot, s, h;
+  decode_work(blockIdx.x, nseq, Hq, Hkv, xcd_map, slot, s, h);
+  int64_t start;
+  int L;
+  seqs.bounds(s, start, L);
+  const int nqt_s = (L + BMW - 1) / BMW;
+  if (slot >= nqt_s) return;
+  const int qt = CAUSAL ? nqt_s - 1 - slot : slot;
+  const int g = h / (Hq / Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, m = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t pbase = Seqs::pstart(s, start);
+  const char* tsrc = tiles + ((int64_t)g * (Ppad / TK) + pbase / TK) * LY::STAGE;
+
+  // Waves w and w + 4 share a SIMD; with 8 waves they take the 32-row blocks w and
+  // 7 - w of the query tile, so that under the causal mask every SIMD gets the same
+  // number of visible tiles.
+  const int blk = NW == 8 ? (w < 4 ? w : 11 - w) : w;
+  const int q0 = qt * BMW;
+  const int qw0 = q0 + 32 * blk;
+  const int qi = qw0 + m;
+  const int ntile_seq = (L + TK - 1) / TK;
+  const int nt = CAUSAL ? min(ntile_seq, (min(q0 + BMW, L) - 1) / TK + 1) : ntile_seq;
+  // The wave's last tile with a visible key (its causal diagonal): later tiles of the
+  // workgroup it only helps to copy.
+  const int jv = CAUSAL ? min(nt - 1, qw0 / TK) : nt - 1;
+  // Tile j needs a mask for this wave when some of its keys lie above the wave's
+  // causal diagonal or past the sequence end; `last` is then the lane's last visible
+  // key relative to the tile's first key plus 4 hh (its register offsets are relative
+  // to that).
+  const int last_key = CAUSAL ? min(qi, L - 1) : L - 1;
+  auto needs_mask = [&](int jj) {
+    return (CAUSAL && jj * TK + TK - 1 > qw0) || jj * TK + TK > L;
+  };
+
+  // Prologue: tiles 0 .. NS-2 stream into their stages while the wave's Q fragments and
+  // scales load.
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (i < nt) copy_tile_dma<D, NW>(tsrc + (int64_t)i * LY::STAGE, smem + i * LY::STAGE, tid, w);
+  const int64_t qslot = (int64_t)h * Qpad + Seqs::qpstart(s, start) + qw0;
+  v4i qf[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+    qf[kb] = reinterpret_cast<const v4i*>(q8 + qslot * D)[kb * 64 + lane];
+  const float qsc = fmaxf(qs[qslot + m] * qk_log2, FLT_MIN);
+  vm_wait<0>();
+  __syncthreads();
+
+  v16f o[NKB], lacc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    lacc[i] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < NKB; ++db) o[db][i] = 0.0f;
+  }
+  v8h ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
+  float mrun = -INFINITY;
+  float t[32];  // the current tile's scores t = f32(S) * sk (key j: see scores())
+  v8h pk[4];    // its probabilities, fp16, the P^T operand of P.V per key group
+
+  // Register i of the S^T block nb holds key 32 nb + 8 (i/4) + 4 hh + i%4 of the tile;
+  // off(i) is that key relative to the tile's first key + 4 hh.
+  auto key_off = [](int i) { return 32 * (i >> 4) + 8 * ((i >> 2) & 3) + (i & 3); };
+  // M is raised (with a rescale of O and l) only where the tile's max exceeds it by
+  // more than TAU.  Only register 0 of the row-sum accumulator is read, so only it is
+  // rescaled.
+  auto raise = [&](float mc) {
+    const bool upd = mc > mrun + TAU;
+    if (__any(upd)) {
+      const float mnew = upd ? mc : mrun;
+      const float alpha = upd ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.0f;
+      mrun = mnew;
+      lacc[0] *= alpha;
+#pragma unroll
+      for (int db = 0; db < NKB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    }
+  };
+  // p = 2^(t * qsc - mu) rounded to fp16 for the 16 keys of group kg (P^T operand).
+  auto expo = [&](int kg, float mu) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      v2f pp;
+      pp[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[8 * kg + e], qsc, -mu));
+      pp[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[8 * kg + e + 1], qsc, -mu));
+      const v2h ph = __builtin_convertvector(pp, v2h);
+      pk[kg][e] = ph[0];
+      pk[kg][e + 1] = ph[1];
+    }
+  };
+  // Row sum and P.V of key group kg.
+  auto pv = [&](const char* st, int kg) {
+    const v4i* vl = reinterpret_cast<const v4i*>(st + LY::KB);
+    lacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ones, pk[kg], lacc, 0, 0, 0);
+#pragma unroll
+    for (int db = 0; db < NKB; ++db) {
+      const v4i va = vl[(kg * NKB + db) * 64 + lane];
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, va), pk[kg], o[db],
+                                                      0, 0, 0);
+    }
+  };
+
+  // One iteration as a fixed schedule of slots, one MFMA each, fenced with scheduling
+  // barriers so the compiler keeps the order:
+  //   MFMAs: the 2 NKB score products of the next tile, then per key group kg the row
+  //          sum and the NKB P.V products of this tile;
+  //   LDS:   every MFMA operand is read PF slots ahead of its MFMA (a ring of PF + 1
+  //          fragments), the next tile's key scales two slots ahead of their first use;
+  //   VMEM:  this wave's share of the copy of a later tile, one instruction every few
+  //          slots;
+  //   VALU:  the exponentials of this tile (item i: FMA and exp2 of score i, the fp16
+  //          pack after every odd i) over the slots before the third row-sum MFMA that
+  //          needs them, the conversion of the next tile's scores (item i: cvt and
+  //          key-scale multiply, with MASK the causal/tail select, a max3 after every odd
+  //          i) from the slot its scores are ready, and the row max exchange and rescale
+  //          decision in the last slot.
+  // Returns the next tile's row max in log2 units; upd_any: some row needs a rescale.
+  auto pipe_step = [&](const char* cur, const char* nxt, const char* dsrc, char* dstage,
+                       auto MASK, int last, bool& upd_any) -> float {
+    constexpr bool masked = decltype(MASK)::value;
+    constexpr int NQK = 2 * NKB;                // score MFMAs
+    constexpr int NM = NQK + 4 * (NKB + 1);     // all MFMAs of the iteration
+    constexpr int PF = 3;                       // operand prefetch distance, in MFMAs
+    constexpr int E_END = NQK + 2 * (NKB + 1);  // exponentials end before row sum 2
+    constexpr int C_BEG = NQK + 2;              // conversions start once the scores are in
+    constexpr int C_END = NM - 2;               // the last two slots: the row max exchange
+    constexpr int NC = C_END - C_BEG;
+    const v4i* kl = reinterpret_cast<const v4i*>(nxt);
+    const v4i* vl = reinterpret_cast<const v4i*>(cur + LY::KB);
+    const float* skl = reinterpret_cast<const float*>(nxt + LY::KB + LY::VB);
+    // Operand of MFMA slot x (the row-sum MFMAs take none): K fragment (nb, kb) for the
+    // score products, V fragment (kg, db) for P.V.
+    auto operand = [&](int x) -> v4i {
+      if (x < NQK) return kl[((x / NKB) * NKB + x % NKB) * 64 + lane];
+      const int y = x - NQK, kg = y / (NKB + 1), db = y % (NKB + 1) - 1;
+      return vl[(kg * NKB + db) * 64 + lane];
+    };
+    auto has_operand = [&](int x) { return x < NQK || (x - NQK) % (NKB + 1) != 0; };
+    v16i sn[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sn[nb][i] = 0;
+    v4i fr[PF + 1];
+    v4f skv[8];
+    float p_even = 0.0f, cm0 = -INFINITY, cm1 = -INFINITY, mc_next = 0.0f;
+#pragma unroll
+    for (int x = 0; x < PF; ++x)
+      if (has_operand(x)) fr[x % (PF + 1)] = operand(x);
+#pragma clang loop unroll(full)
+    for (int x = 0; x < NM; ++x) {
+      // the MFMA of slot x
+      if (x < NQK) {
+        const int nb = x / NKB, kb = x % NKB;
+        sn[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fr[x % (PF + 1)], qf[kb], sn[nb], 0, 0, 0);
+      } else {
+        const int y = x - NQK, kg = y / (NKB + 1), db = y % (NKB + 1) - 1;
+        if (db < 0)
+          lacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ones, pk[kg], lacc, 0, 0, 0);
+        else
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(v8h, fr[x % (PF + 1)]), pk[kg], o[db], 0, 0, 0);
+      }
+      // operand PF slots ahead
+      if (x + PF < NM && has_operand(x + PF)) fr[(x + PF) % (PF + 1)] = operand(x + PF);
+      // key scales: group gsk (keys of sn[gsk / 4] registers 4 (gsk % 4) ..) two slots
+      // before the conversion item 4 gsk that first needs them
+#pragma unroll
+      for (int gsk = 0; gsk < 8; ++gsk) {
+        const int first = C_BEG + (4 * gsk * NC) / 32;
+        const int at = first - 2 < 0 ? 0 : first - 2;
+        if (at == x)
+          skv[gsk] = *reinterpret_cast<const v4f*>(skl + 32 * (gsk / 4) + 8 * (gsk % 4) + 4 * hh);
+      }
+      // this wave's rounds of the copy: round r at slot 2 + r (NM - 4) / R
+#pragma unroll
+      for (int r = 0; r < DM::ROUNDS; ++r)
+        if (x == 2 + (r * (NM - 4)) / DM::ROUNDS) copy_tile_round<D, NW>(dsrc, dstage, tid, w, r);
+      // exponentials of this tile: items [E(x), E(x + 1))
+      if (x < E_END) {
+        const int i0 = (32 * x) / E_END, i1 = (32 * (x + 1)) / E_END;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          if (i < i0 || i >= i1) continue;
+          const float pi = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], qsc, -mrun));
+          if (i & 1) {
+            const v2f pp = {p_even, pi};
+            const v2h ph = __builtin_convertvector(pp, v2h);
+            pk[i >> 3][(i & 7) - 1] = ph[0];
+            pk[i >> 3][i & 7] = ph[1];
+          } else {
+            p_even = pi;
+          }
+        }
+      }
+      if (x >= C_BEG && x < C_END) {
+        // conversion of the next tile's scores: items [C(x), C(x + 1))
+        const int c = x - C_BEG;
+        const int i0 = (32 * c) / NC, i1 = (32 * (c + 1)) / NC;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          if (i < i0 || i >= i1) continue;
+          const int nb = i >> 4, g4 = i >> 2, r = i & 3;
+          t[i] = (float)sn[nb][i & 15] * skv[g4][r];
+          if (masked && key_off(i) > last) t[i] = -INFINITY;
+          if (i & 1) {
+            if (i & 2) cm1 = smax(smax(cm1, t[i - 1]), t[i]);
+            else cm0 = smax(smax(cm0, t[i - 1]), t[i]);
+          }
+        }
+      }
+      // the row max of the next tile and the rescale decision, under the last MFMAs
+      if (x == NM - 1) {
+        mc_next = other_half_max(smax(cm0, cm1)) * qsc;
+        upd_any = __any(mc_next > mrun + TAU);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return mc_next;
+  };
+
+  // Tile 0: its scores, converted and masked where needed, set M.
+  {
+    const v4i* kl = reinterpret_cast<const v4i*>(smem);
+    const float* skl = reinterpret_cast<const float*>(smem + LY::KB + LY::VB);
+    v16i sc[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[nb][i] = 0;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        sc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kl[(nb * NKB + kb) * 64 + lane], qf[kb],
+                                                       sc[nb], 0, 0, 0);
+    }
+    const bool msk0 = needs_mask(0);
+    const int last0 = last_key - 4 * hh;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const v4f skv = *reinterpret_cast<const v4f*>(skl + 32 * (i >> 4) + 8 * ((i >> 2) & 3) + 4 * hh);
+      t[i] = (float)sc[i >> 4][i & 15] * skv[i & 3];
+      if (msk0 && key_off(i) > last0) t[i] = -INFINITY;
+    }
+    float m0 = smax(t[0], t[1]), m1 = smax(t[2], t[3]);
+#pragma unroll
+    for (int i = 4; i < 32; i += 4) {
+      m0 = smax(smax(m0, t[i]), t[i + 1]);
+      m1 = smax(smax(m1, t[i + 2]), t[i + 3]);
+    }
+    raise(other_half_max(smax(m0, m1)) * qsc);
+  }
+
+  // Tiles 0 .. nt-2: tile j's exponentials and P.V beside tile j+1's scores.  The copy
+  // of tile j + NS - 1 goes into the stage tile j - 1 left; without such a tile the
+  // step copies tile j again into that stage, which no later tile uses (the remaining
+  // ones need fewer than NS stages), so the step has no branch.  A wave whose
+  // remaining rows see none of tile j+1 (the causal diagonal of the rows below it)
+  // masks all of its scores, and its probabilities are 0.
+  const int dma_n = DM::count(w);
+  int scur = 0;  // stage of tile j
+  int j = 0;
+  // One iteration; the two loops below differ only in the mask of the next tile's
+  // scores (a wave's masked tiles all come after its unmasked ones).  Every wave runs
+  // nt - 1 iterations, each ending with the one barrier.
+  auto iterate = [&](auto MASK) {
+    const int snxt = scur == NS - 1 ? 0 : scur + 1;
+    const char* cur = smem + scur * LY::STAGE;
+    const char* nxt = smem + snxt * LY::STAGE;
+    const char* dsrc = tsrc + (int64_t)(j + NS - 1 < nt ? j + NS - 1 : j) * LY::STAGE;
+    char* dst = smem + (scur == 0 ? NS - 1 : scur - 1) * LY::STAGE;
+    bool upd_any;
+    const float mc = pipe_step(cur, nxt, dsrc, dst, MASK, last_key - (j + 1) * TK - 4 * hh, upd_any);
+    if (upd_any) raise(mc);
+    // Tile j + 2 must have landed; the copy issued in this step may run on when it is
+    // for a later tile.
+    vm_wait_n(NS >= 4 ? dma_n : 0);
+    __syncthreads();
+    scur = snxt;
+  };
+  for (; j < jv && !needs_mask(j + 1); ++j) iterate(std::false_type{});
+  for (; j < jv; ++j) iterate(std::true_type{});
+  // The wave's last visible tile: its exponentials and P.V.
+  {
+    const char* cur = smem + scur * LY::STAGE;
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) expo(kg, mrun);
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) pv(cur, kg);
+  }
+  // Tiles past the wave's diagonal (causal): only its share of the copies and the
+  // barriers, so the other waves of the workgroup get their tiles.
+  for (; j + 1 < nt; ++j) {
+    if (j + NS - 1 < nt) {
+      const int st = scur == 0 ? NS - 1 : scur - 1;
+      copy_tile_dma<D, NW>(tsrc + (int64_t)(j + NS - 1) * LY::STAGE, smem + st * LY::STAGE, tid,
+                           w);
+    }
+    vm_wait<0>();
+    __syncthreads();
+    scur = scur == NS - 1 ? 0 : scur + 1;
+  }
+  // No copy outlives the workgroup (the last steps' copies go to stages no tile uses).
+  vm_wait<0>();
+
+  if (qi < L) {
+    const float inv = 1.0f / lacc[0];
+    _Float16* orow = out + aq.off(start, h, qi);
+#pragma unroll
+    for (int db = 0; db < NKB; ++db)
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        v4h o4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o4[r] = (_Float16)(o[db][4 * J + r] * inv);
+        *reinterpret_cast<v4h*>(orow + 32 * db + 8 * J + 4 * hh) = o4;
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------------
 // Debug: the int32 score tile from the forward's own prepared Q and K fragments
 // (read straight from the workspace), one wave per aligned 32x32 block.
 template <int D>
@@ -350,7 +818,12 @@ static Act act_of(const FwdGeom& g, int H) {
 template <int D, bool C>
 static hipError_t attn_d(const FwdGeom& g, const WsPlan& p, const void* ws, hipStream_t stream) {
   const char* w = static_cast<const char*>(ws);
-  const int nqt = (g.max_len + BM - 1) / BM;
+#ifndef PIPE_NW
+#define PIPE_NW 8
+#endif
+  constexpr int NW = PIPE_NW;  // waves per workgroup of the pipelined kernel
+  const int bm = D <= 128 ? 32 * NW : BM;
+  const int nqt = (g.max_len + bm - 1) / bm;
   const int64_t blocks = (int64_t)nqt * g.nseq * g.Hq;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
@@ -359,10 +832,16 @@ static hipError_t attn_d(const FwdGeom& g, const WsPlan& p, const void* ws, hipS
   // Rotated Q and K rows carry H H^T = D I: an extra exact factor 1/D on the logits.
   const float qk_log2 = g.softmax_scale * 1.4426950408889634f * (g.rot ? 1.0f / g.D : 1.0f);
   Seqs sq{g.cu, g.S, g.max_len, g.T};
-  attn_fwd_kernel<D, C><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-      reinterpret_cast<const int8_t*>(w + p.off_q8), reinterpret_cast<const float*>(w + p.off_qs),
-      p.Qpad, static_cast<_Float16*>(g.out), act_of(g, g.Hq), sq, g.Hq, g.Hkv, g.nseq, xcd_map,
-      qk_log2, w + p.off_tiles, p.Ppad);
+  if constexpr (D <= 128)
+    attn_pipe_kernel<D, C, NW><<<dim3((unsigned)blocks), dim3(64 * NW), 0, stream>>>(
+        reinterpret_cast<const int8_t*>(w + p.off_q8),
+        reinterpret_cast<const float*>(w + p.off_qs), p.Qpad, static_cast<_Float16*>(g.out),
+        act_of(g, g.Hq), sq, g.Hq, g.Hkv, g.nseq, xcd_map, qk_log2, w + p.off_tiles, p.Ppad);
+  else
+    attn_fwd_kernel<D, C><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+        reinterpret_cast<const int8_t*>(w + p.off_q8),
+        reinterpret_cast<const float*>(w + p.off_qs), p.Qpad, static_cast<_Float16*>(g.out),
+        act_of(g, g.Hq), sq, g.Hq, g.Hkv, g.nseq, xcd_map, qk_log2, w + p.off_tiles, p.Ppad);
   return hipGetLastError();
 }
 

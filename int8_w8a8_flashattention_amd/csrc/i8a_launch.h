@@ -32,8 +32,9 @@ __host__ __device__ constexpr int tile_bytes(int D) { return TK * D * 3 + TK * 4
 // Cap on the K partial sums per (sequence, kv head): the K quantization workgroups
 // each reduce all of them to get the mean.
 constexpr int MAX_PARTS = 64;
-// Query rows per attention workgroup, and per Q preparation workgroup.
-constexpr int BQ = 128;
+// Padding of each sequence's Q slots: a multiple of the query rows of every attention
+// workgroup, so that a query tile never reaches into the next sequence's slots.
+constexpr int BQ = 256;
 
 struct WsPlan {
   int32_t nseq, Hq, Hkv, D, ntile;  // ntile: TK-token tiles of the longest sequence
