@@ -689,3 +689,66 @@ def test_q_per_block_forward_equals_sdpa_on_its_dequantized_operands():
     ref = torch.nn.functional.scaled_dot_product_attention(
         qd, kd, vd, is_causal=True, scale=float(np.float32(1 / np.sqrt(32)))).numpy()
     np.testing.assert_allclose(got, ref, rtol=1e-9, atol=1e-12)
+
+
+def exact_block_codes(rows, scale):
+    """Codes of fp32 rows against a given scale with rational arithmetic (R3)."""
+    return [[max(-127, min(127, round(rn32(Fraction(float(x)) / scale)))) for x in r]
+            for r in rows]
+
+
+def test_q_per_block_hand_derived_case():
+    # tests/golden/q_per_block_worked.json: blocks of 2 rows, a ragged last block; the
+    # non-maximal row of block 0 is quantized against the block's scale.
+    g = json.load(open(os.path.join(GOLDEN, "q_per_block_worked.json")))
+    x = np.array(g["rows"], dtype=np.float32)
+    c, s = oracle.quant_row_blocks(x, block=g["block"])
+    for b in g["blocks"]:
+        want_s = Fraction(b["scale_num"], b["scale_den"])
+        for r, want_c in zip(b["rows"], b["codes"]):
+            assert Fraction(float(s[r])) == want_s
+            assert c[r].tolist() == want_c
+
+
+def test_q_per_block_every_row_follows_the_rational_rule_at_the_block_scale():
+    # Every code of every row: rint(fp32(x / s_b)) clamped, with s_b = fp32(absmax of
+    # the block / 127) in exact arithmetic -- the rows that do not hold the block's
+    # maximum included, ragged last block (70 = 32 + 32 + 6 rows) included.
+    g = np.random.default_rng(34)
+    x = (g.standard_normal((2, 70, 16)) * np.exp(g.standard_normal((2, 70, 1)))).astype(np.float16)
+    x = x.astype(np.float32)
+    x[1, 45] *= 40.0  # one dominant row in the second block
+    c, s = oracle.quant_row_blocks(x)
+    for h in range(2):
+        for b0 in range(0, 70, 32):
+            rows = x[h, b0:b0 + 32]
+            a = max(abs(Fraction(float(v))) for v in rows.ravel())
+            sb = rn32(a / 127)
+            assert all(Fraction(float(v)) == sb for v in s[h, b0:b0 + 32])
+            assert c[h, b0:b0 + 32].tolist() == exact_block_codes(rows, sb)
+
+
+def test_q_per_block_varlen_blocks_start_at_each_sequence():
+    # In a packed batch the 32-row blocks are counted from each sequence's first token
+    # (sequences at rows 0 and 40 here): the varlen forward equals torch's fp64 SDPA on
+    # operands dequantized with exact block scales per sequence.
+    w = workloads.varlen(35, 2, 80, 2, 1, 16, True, lengths=[40, 50])
+    cu = w.cu_seqlens
+    got = oracle.attn_int8_varlen_fwd(w.q, w.k, w.v, cu, True, q_per_block=True)
+    sm = float(oracle.default_softmax_scale(16))
+    for i in range(2):
+        a, b = int(cu[i]), int(cu[i + 1])
+        z = oracle.quantize_qkv(np.ascontiguousarray(w.q[a:b].transpose(1, 0, 2))[None],
+                                np.ascontiguousarray(w.k[a:b].transpose(1, 0, 2))[None],
+                                np.ascontiguousarray(w.v[a:b].transpose(1, 0, 2))[None])
+        qd = np.empty((2, b - a, 16))
+        for h in range(2):
+            q32 = w.q[a:b, h].astype(np.float32)
+            for b0 in range(0, b - a, 32):
+                rows = q32[b0:b0 + 32]
+                sb = rn32(max(abs(Fraction(float(v))) for v in rows.ravel()) / 127)
+                qd[h, b0:b0 + 32] = np.array(exact_block_codes(rows, sb), dtype=np.float64) * float(sb)
+        kd = dequant(z["k8"][0], z["sk"][0]).repeat(2, axis=0)
+        vd = dequant(z["v8"][0], z["sv"][0]).repeat(2, axis=0)
+        ref = sdpa64(qd, kd, vd, True, sm)
+        np.testing.assert_allclose(got[a:b].transpose(1, 0, 2), ref, rtol=1e-9, atol=1e-12)
