@@ -237,6 +237,32 @@ i8a_status attn_int8_debug_qk(const void* q, const void* k, const void* v, int32
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_int8_debug_qk_ex - the dump of attn_int8_debug_qk for any forward call: dense
+ * (cu_seqlens null; nseq = B, max_seqlen = S, total_tokens = B * S, tensors BHSD) or
+ * varlen (cu_seqlens on the device as for attn_int8_varlen_fwd, tensors [T, H, D]),
+ * with the variant flags of attn_int8_fwd_ex, for sequence `seq` and query head h.
+ * It runs the preparation that forward runs (Attention kernels table, attn_int8_fwd,
+ * attn_varlen_fwd and attn_w8a8_fwd rows; Quantization table) and writes, besides the
+ * outputs of attn_int8_debug_qk:
+ *   vhat_out  nullable fp16 [cols, D]: the dequantized V rows of kv head h/(Hq/Hkv) as
+ *             the P.V product consumes them (scale times code, exact in fp16)
+ *   vchan_out nullable fp32 [D]: the V channel scales (I8A_FWD_V_PER_CHANNEL only)
+ * vscale_out (V per token) must be null with I8A_FWD_V_PER_CHANNEL; with
+ * I8A_FWD_Q_PER_BLOCK each qscale_out entry is its row's block scale.  Rows and columns
+ * must lie in [0, max_seqlen); entries past the sequence's own length are not written.
+ * The workspace is sized by attn_int8_workspace_bytes (dense) or
+ * attn_int8_varlen_workspace_bytes (varlen).  Errors as for attn_int8_fwd_ex.
+ */
+i8a_status attn_int8_debug_qk_ex(const void* q, const void* k, const void* v,
+                                 const int32_t* cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                                 int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t D,
+                                 int32_t flags, int32_t seq, int32_t h, int32_t row0,
+                                 int32_t rows, int32_t col0, int32_t cols, int32_t* s32_out,
+                                 float* qscale_out, float* kscale_out, float* vscale_out,
+                                 float* kmean_out, void* vhat_out, float* vchan_out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Decode over an int8 KV cache (SuperL8 README, Attention kernels table, row
  * attn_decode: split-KV decode with an int8 KV cache, fp16-V and int8-V variants).
  *

@@ -32,6 +32,7 @@ import torch
 
 __all__ = [
     "quant_rowwise_i8", "attn_int8_fwd", "attn_int8_varlen_fwd", "attn_int8_debug_qk",
+    "attn_int8_varlen_debug_qk",
     "attn_int8_fwd_hadamard", "attn_int8_fwd_ex", "attn_int8_varlen_fwd_ex", "FWD_HADAMARD",
     "FWD_V_PER_CHANNEL", "FWD_Q_PER_BLOCK", "attn_int8_prepare_kv", "attn_int8_prepare_q",
     "attn_int8_attend", "attn_int8_fwd_prepared",
@@ -65,6 +66,8 @@ _SIGS = {
     "attn_int8_varlen_workspace_bytes": (_c_sz, [_c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32]),
     "attn_int8_varlen_fwd": (_c_i32, [_c_vp] * 5 + [_c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_i32,
                                                      _c_f32, _c_i32, _c_vp, _c_sz, _c_vp]),
+    "attn_int8_debug_qk_ex": (_c_i32, [_c_vp] * 4 + [_c_i32, _c_i32, _c_i64] + [_c_i32] * 10
+                              + [_c_vp] * 7 + [_c_vp, _c_sz, _c_vp]),
     "attn_int8_debug_qk": (_c_i32, [_c_vp] * 3 + [_c_i32] * 11 + [_c_vp] * 5 + [_c_i32, _c_vp,
                                                                                  _c_sz, _c_vp]),
     "attn_int8_fwd_hadamard": (_c_i32, [_c_vp] * 4 + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_sz,
@@ -405,27 +408,64 @@ def attn_int8_varlen_fwd_ex(q, k, v, cu_seqlens, max_seqlen, causal=True, flags=
     return out
 
 
-def attn_int8_debug_qk(q, k, v, b, h, row0, rows, col0, cols, workspace=None, hadamard=False):
-    """The dense forward's exact int32 scores ``S32[row0:row0+rows, col0:col0+cols]``
-    of (batch b, query head h), with the row scales and the K mean it used (with
-    ``hadamard``, those of :func:`attn_int8_fwd_hadamard`)."""
-    B, Hq, Hkv, S, D = _dense_shapes(q, k, v)
+def _debug_call(q, k, v, cu, nseq, max_len, T, Hq, Hkv, D, flags, seq, h, row0, rows, col0,
+                cols, nbytes, workspace):
     dev = q.device
-    s32 = torch.empty((rows, cols), dtype=torch.int32, device=dev)
-    qs = torch.empty(rows, dtype=torch.float32, device=dev)
-    ks = torch.empty(cols, dtype=torch.float32, device=dev)
-    vs = torch.empty(cols, dtype=torch.float32, device=dev)
-    km = torch.empty(D, dtype=torch.float32, device=dev)
+    vch = bool(flags & FWD_V_PER_CHANNEL)
+    r = dict(s32=torch.zeros((rows, cols), dtype=torch.int32, device=dev),
+             qscale=torch.zeros(rows, dtype=torch.float32, device=dev),
+             kscale=torch.zeros(cols, dtype=torch.float32, device=dev),
+             kmean=torch.zeros(D, dtype=torch.float32, device=dev),
+             vhat=torch.zeros((cols, D), dtype=torch.float16, device=dev))
+    if vch:
+        r["vchan"] = torch.zeros(D, dtype=torch.float32, device=dev)
+    else:
+        r["vscale"] = torch.zeros(cols, dtype=torch.float32, device=dev)
     lib = load_library()
-    nbytes = lib.attn_int8_workspace_bytes(B, Hq, Hkv, S, D)
     ws = _workspace(workspace, nbytes, dev)
     with torch.cuda.device(dev):
-        st = lib.attn_int8_debug_qk(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, S, D, b, h, row0, rows,
-                                    col0, cols, _ptr(s32), _ptr(qs), _ptr(ks), _ptr(vs), _ptr(km),
-                                    int(bool(hadamard)), _ptr(ws), ws.numel() * ws.element_size(),
-                                    _stream(dev))
-    _check(st, "attn_int8_debug_qk")
-    return dict(s32=s32, qscale=qs, kscale=ks, vscale=vs, kmean=km)
+        st = lib.attn_int8_debug_qk_ex(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(cu), nseq, max_len, T, Hq, Hkv, D, int(flags), seq, h,
+            row0, rows, col0, cols, _ptr(r["s32"]), _ptr(r["qscale"]), _ptr(r["kscale"]),
+            _ptr(r.get("vscale")), _ptr(r["kmean"]), _ptr(r["vhat"]), _ptr(r.get("vchan")),
+            _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
+    _check(st, "attn_int8_debug_qk_ex")
+    return r
+
+
+def attn_int8_debug_qk(q, k, v, b, h, row0, rows, col0, cols, workspace=None, hadamard=False,
+                       flags=None):
+    """The dense forward's exact int32 scores ``S32[row0:row0+rows, col0:col0+cols]``
+    of (batch b, query head h), with the row scales, the K mean and the prepared V rows
+    it used (``flags``: the variant flags of :func:`attn_int8_fwd_ex`; ``hadamard`` is
+    the same as ``flags=FWD_HADAMARD``).  Returns a dict of tensors: ``s32``,
+    ``qscale``, ``kscale``, ``kmean``, ``vhat`` (fp16 ``[cols, D]``) and ``vscale``
+    (per token) or ``vchan`` (per channel, with ``FWD_V_PER_CHANNEL``)."""
+    B, Hq, Hkv, S, D = _dense_shapes(q, k, v)
+    if flags is None:
+        flags = FWD_HADAMARD if hadamard else 0
+    nbytes = load_library().attn_int8_workspace_bytes(B, Hq, Hkv, S, D)
+    return _debug_call(q, k, v, None, B, S, B * S, Hq, Hkv, D, flags, b, h, row0, rows, col0,
+                       cols, nbytes, workspace)
+
+
+def attn_int8_varlen_debug_qk(q, k, v, cu_seqlens, max_seqlen, seq, h, row0, rows, col0, cols,
+                              flags=0, workspace=None):
+    """:func:`attn_int8_debug_qk` for the varlen forward: sequence ``seq`` of the packed
+    batch, rows and keys counted from its first token (entries past its length stay 0)."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need_gpu_fp16(n, t, 3)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if D not in HEAD_DIMS or Hkv < 1 or Hq % Hkv:
+        raise ValueError("bad head dim or Hq/Hkv")
+    if (not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32
+            or cu_seqlens.device != q.device or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2):
+        raise ValueError("cu_seqlens must be an int32 [nseq+1] tensor on q's device")
+    nseq = cu_seqlens.numel() - 1
+    nbytes = load_library().attn_int8_varlen_workspace_bytes(nseq, T, int(max_seqlen), Hq, Hkv, D)
+    return _debug_call(q, k, v, cu_seqlens, nseq, int(max_seqlen), T, Hq, Hkv, D, flags, seq, h,
+                       row0, rows, col0, cols, nbytes, workspace)
 
 
 def _vformat(v_format):

@@ -751,23 +751,29 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
 
 // ----------------------------------------------------------------------------------
 // Debug: the int32 score tile from the forward's own prepared Q and K fragments
-// (read straight from the workspace), one wave per aligned 32x32 block.
+// (read straight from the workspace), one wave per aligned 32x32 block of sequence s
+// and query head h, with the scales, the K mean and the prepared V rows of the same
+// rows and keys.  Entries past the sequence's length are not written.
 template <int D>
 __global__ __launch_bounds__(64) void debug_qk_kernel(
-    const int8_t* __restrict__ q8, const float* __restrict__ qs, int64_t Qpad, int S, int Hq,
-    int Hkv, int b, int h, int row0, int rows, int col0, int cols,
+    const int8_t* __restrict__ q8, const float* __restrict__ qs, int64_t Qpad, Seqs seqs,
+    int Hq, int Hkv, int s, int h, int row0, int rows, int col0, int cols,
     const char* __restrict__ tiles, const float* __restrict__ sv_ws,
-    const float* __restrict__ kmean_ws, int64_t Ppad, int32_t* __restrict__ s32,
-    float* __restrict__ qscale, float* __restrict__ kscale, float* __restrict__ vscale,
-    float* __restrict__ kmean_out) {
+    const float* __restrict__ svc_ws, const float* __restrict__ kmean_ws, int64_t Ppad,
+    DebugOut o) {
   constexpr int NKB = D / 32;
   const int lane = threadIdx.x, m = lane & 31, hh = lane >> 5;
   const int qbase = (row0 & ~31) + 32 * blockIdx.x;
   const int kbase = (col0 & ~31) + 32 * blockIdx.y;
-  const int64_t start = (int64_t)b * S;
+  int64_t start;
+  int L;
+  seqs.bounds(s, start, L);
+  // A block wholly past the sequence's end reads nothing (its slots may belong to the
+  // next sequence or lie past the workspace's Q rows).
+  if (qbase >= L || kbase >= L) return;
   const int g = h / (Hq / Hkv);
-  const int64_t pbase = Seqs::pstart(b, start);
-  const int64_t qslot = (int64_t)h * Qpad + Seqs::qpstart(b, start) + qbase;
+  const int64_t pbase = Seqs::pstart(s, start);
+  const int64_t qslot = (int64_t)h * Qpad + Seqs::qpstart(s, start) + qbase;
 
   v4i qf[NKB];
 #pragma unroll
@@ -784,21 +790,35 @@ __global__ __launch_bounds__(64) void debug_qk_kernel(
     acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kt[(nb * NKB + kb) * 64 + lane], qf[kb], acc, 0,
                                                 0, 0);
   const int qrow = qbase + m;
+  const bool qin = qrow >= row0 && qrow < row0 + rows && qrow < L;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int n = kbase + 8 * (i >> 2) + 4 * hh + (i & 3);
-    if (qrow >= row0 && qrow < row0 + rows && n >= col0 && n < col0 + cols)
-      s32[(int64_t)(qrow - row0) * cols + (n - col0)] = acc[i];
+    if (qin && n >= col0 && n < col0 + cols && n < L)
+      o.s32[(int64_t)(qrow - row0) * o.cols + (n - col0)] = acc[i];
   }
-  if (qscale && blockIdx.y == 0 && hh == 0 && qrow >= row0 && qrow < row0 + rows)
-    qscale[qrow - row0] = qs[qslot + m];
+  if (o.qscale && blockIdx.y == 0 && hh == 0 && qin) o.qscale[qrow - row0] = qs[qslot + m];
   const int n = kbase + m;
-  if (blockIdx.x == 0 && hh == 0 && n >= col0 && n < col0 + cols) {
-    if (kscale) kscale[n - col0] = reinterpret_cast<const float*>(tb + 3 * TK * D)[n - tile0];
-    if (vscale) vscale[n - col0] = sv_ws[(int64_t)g * Ppad + pbase + n];
+  const bool kin = n >= col0 && n < col0 + cols && n < L;
+  if (blockIdx.x == 0 && hh == 0 && kin) {
+    if (o.kscale) o.kscale[n - col0] = reinterpret_cast<const float*>(tb + 3 * TK * D)[n - tile0];
+    if (o.vscale) o.vscale[n - col0] = sv_ws[(int64_t)g * Ppad + pbase + n];
   }
-  if (kmean_out && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int d = lane; d < D; d += 64) kmean_out[d] = kmean_ws[((int64_t)b * Hkv + g) * D + d];
+  // The prepared V rows of this block's keys, from the tile's V fragments.
+  if (o.vhat && blockIdx.x == 0) {
+    const _Float16* vt = reinterpret_cast<const _Float16*>(tb + TK * D);
+    for (int idx = lane; idx < 32 * D; idx += 64) {
+      const int nl = idx / D, d = idx % D, nk = kbase + nl;
+      if (nk >= col0 && nk < col0 + cols && nk < L)
+        o.vhat[(int64_t)(nk - col0) * D + d] = vt[vtile_off(nk - tile0, d, D)];
+    }
+  }
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int d = lane; d < D; d += 64) {
+      if (o.kmean) o.kmean[d] = kmean_ws[((int64_t)s * Hkv + g) * D + d];
+      if (o.vchan) o.vchan[d] = svc_ws[((int64_t)s * Hkv + g) * D + d];
+    }
+  }
 }
 
 // ----------------------------------------------------------------------------------
@@ -859,30 +879,29 @@ hipError_t launch_attn(const FwdGeom& g, const WsPlan& p, const void* ws, hipStr
 }
 
 template <int D>
-static hipError_t debug_d(const FwdGeom& g, const WsPlan& p, const void* ws, int b, int h,
-                          int row0, int rows, int col0, int cols, int32_t* s32, float* qscale,
-                          float* kscale, float* vscale, float* kmean, hipStream_t stream) {
+static hipError_t debug_d(const FwdGeom& g, const WsPlan& p, const void* ws, int s, int h,
+                          int row0, int rows, int col0, int cols, const DebugOut& o,
+                          hipStream_t stream) {
   const char* w = static_cast<const char*>(ws);
   const int rb = ((row0 + rows - 1) >> 5) - (row0 >> 5) + 1;
   const int cb = ((col0 + cols - 1) >> 5) - (col0 >> 5) + 1;
+  Seqs sq{g.cu, g.S, g.max_len, g.T};
   debug_qk_kernel<D><<<dim3(rb, cb), dim3(64), 0, stream>>>(
       reinterpret_cast<const int8_t*>(w + p.off_q8), reinterpret_cast<const float*>(w + p.off_qs),
-      p.Qpad, g.S, g.Hq, g.Hkv, b, h, row0, rows, col0, cols, w + p.off_tiles,
-      reinterpret_cast<const float*>(w + p.off_sv),
-      reinterpret_cast<const float*>(w + p.off_kmean), p.Ppad, s32, qscale, kscale, vscale,
-      kmean);
+      p.Qpad, sq, g.Hq, g.Hkv, s, h, row0, rows, col0, cols, w + p.off_tiles,
+      reinterpret_cast<const float*>(w + p.off_sv), reinterpret_cast<const float*>(w + p.off_svc),
+      reinterpret_cast<const float*>(w + p.off_kmean), p.Ppad, o);
   return hipGetLastError();
 }
 
-hipError_t launch_debug_qk(const FwdGeom& g, const WsPlan& p, const void* ws, int32_t b,
+hipError_t launch_debug_qk(const FwdGeom& g, const WsPlan& p, const void* ws, int32_t s,
                            int32_t h, int32_t row0, int32_t rows, int32_t col0, int32_t cols,
-                           int32_t* s32, float* qscale, float* kscale, float* vscale,
-                           float* kmean, hipStream_t stream) {
+                           const DebugOut& o, hipStream_t stream) {
   switch (g.D) {
-    case 32: return debug_d<32>(g, p, ws, b, h, row0, rows, col0, cols, s32, qscale, kscale, vscale, kmean, stream);
-    case 64: return debug_d<64>(g, p, ws, b, h, row0, rows, col0, cols, s32, qscale, kscale, vscale, kmean, stream);
-    case 128: return debug_d<128>(g, p, ws, b, h, row0, rows, col0, cols, s32, qscale, kscale, vscale, kmean, stream);
-    case 256: return debug_d<256>(g, p, ws, b, h, row0, rows, col0, cols, s32, qscale, kscale, vscale, kmean, stream);
+    case 32: return debug_d<32>(g, p, ws, s, h, row0, rows, col0, cols, o, stream);
+    case 64: return debug_d<64>(g, p, ws, s, h, row0, rows, col0, cols, o, stream);
+    case 128: return debug_d<128>(g, p, ws, s, h, row0, rows, col0, cols, o, stream);
+    case 256: return debug_d<256>(g, p, ws, s, h, row0, rows, col0, cols, o, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -297,32 +297,67 @@ i8a_status attn_int8_varlen_fwd(const void* q, const void* k, const void* v, voi
                                  stream);
 }
 
+i8a_status attn_int8_debug_qk_ex(const void* q, const void* k, const void* v,
+                                 const int32_t* cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                                 int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t D,
+                                 int32_t flags, int32_t seq, int32_t h, int32_t row0,
+                                 int32_t rows, int32_t col0, int32_t cols, int32_t* s32_out,
+                                 float* qscale_out, float* kscale_out, float* vscale_out,
+                                 float* kmean_out, void* vhat_out, float* vchan_out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  // No output tensor is written by this entry; q stands in for its alignment check.
+  i8a_status st = check_common(q, k, v, q, Hq, Hkv, D, 1.0f, 0, workspace);
+  if (st != I8A_OK) return st;
+  if (flags & ~(I8A_FWD_HADAMARD | I8A_FWD_V_PER_CHANNEL | I8A_FWD_Q_PER_BLOCK))
+    return fail(I8A_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (nseq < 1 || nseq > kMaxGridYZ || max_seqlen < 1 || total_tokens < 1 ||
+      total_tokens > kMaxTokens || max_seqlen > total_tokens)
+    return fail(I8A_ERR_INVALID_ARG, "need 1 <= nseq <= %d, 1 <= max_seqlen <= total_tokens",
+                kMaxGridYZ);
+  if (cu_seqlens && !aligned(cu_seqlens, 4))
+    return fail(I8A_ERR_INVALID_ARG, "misaligned cu_seqlens");
+  if (!cu_seqlens && total_tokens != (int64_t)nseq * max_seqlen)
+    return fail(I8A_ERR_INVALID_ARG, "dense geometry needs total_tokens = nseq * max_seqlen");
+  if (seq < 0 || seq >= nseq || h < 0 || h >= Hq)
+    return fail(I8A_ERR_INVALID_ARG, "seq/h out of range");
+  if (rows < 1 || cols < 1 || row0 < 0 || col0 < 0 || (int64_t)row0 + rows > max_seqlen ||
+      (int64_t)col0 + cols > max_seqlen)
+    return fail(I8A_ERR_INVALID_ARG, "tile [%d+%d, %d+%d] outside [0, %d)", row0, rows, col0,
+                cols, max_seqlen);
+  if (!s32_out || !aligned(s32_out, 4)) return fail(I8A_ERR_INVALID_ARG, "bad s32_out");
+  if (vhat_out && !aligned(vhat_out, 2)) return fail(I8A_ERR_INVALID_ARG, "bad vhat_out");
+  const bool vch = (flags & I8A_FWD_V_PER_CHANNEL) != 0;
+  if (vch && vscale_out)
+    return fail(I8A_ERR_INVALID_ARG, "vscale_out (V per token) with I8A_FWD_V_PER_CHANNEL");
+  if (!vch && vchan_out)
+    return fail(I8A_ERR_INVALID_ARG, "vchan_out needs I8A_FWD_V_PER_CHANNEL");
+  FwdGeom g{q, k, v, nullptr, cu_seqlens, nseq, cu_seqlens ? 0 : max_seqlen, max_seqlen,
+            total_tokens, Hq, Hkv, D, 1.0f, 0, (flags & I8A_FWD_HADAMARD) ? 1 : 0, vch ? 1 : 0};
+  g.qblk = (flags & I8A_FWD_Q_PER_BLOCK) ? 1 : 0;
+  const WsPlan p = plan_workspace(nseq, total_tokens, max_seqlen, Hq, Hkv, D);
+  i8a_status pst = run_phases(g, PH_KV | PH_Q, workspace, workspace_bytes, (hipStream_t)stream);
+  if (pst != I8A_OK) return pst;
+  const DebugOut o{s32_out,   cols,      qscale_out, kscale_out, vscale_out,
+                   kmean_out, static_cast<_Float16*>(vhat_out), vchan_out};
+  hipError_t e = launch_debug_qk(g, p, workspace, seq, h, row0, rows, col0, cols, o,
+                                 (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "debug score launch");
+  return I8A_OK;
+}
+
 i8a_status attn_int8_debug_qk(const void* q, const void* k, const void* v, int32_t B, int32_t Hq,
                               int32_t Hkv, int32_t S, int32_t D, int32_t b, int32_t h,
                               int32_t row0, int32_t rows, int32_t col0, int32_t cols,
                               int32_t* s32_out, float* qscale_out, float* kscale_out,
                               float* vscale_out, float* kmean_out, int32_t hadamard,
                               void* workspace, size_t workspace_bytes, void* stream) {
-  // `out` is not written by this entry; q stands in for the alignment check.
-  i8a_status st = check_common(q, k, v, q, Hq, Hkv, D, 1.0f, 0, workspace);
-  if (st != I8A_OK) return st;
+  if (hadamard != 0 && hadamard != 1) return fail(I8A_ERR_INVALID_ARG, "hadamard must be 0 or 1");
   if (B < 1 || S < 1 || B > kMaxGridYZ || (int64_t)B * S > kMaxTokens)
     return fail(I8A_ERR_INVALID_ARG, "need 1 <= B <= %d, S >= 1, B*S in range", kMaxGridYZ);
-  if (b < 0 || b >= B || h < 0 || h >= Hq) return fail(I8A_ERR_INVALID_ARG, "b/h out of range");
-  if (rows < 1 || cols < 1 || row0 < 0 || col0 < 0 || (int64_t)row0 + rows > S ||
-      (int64_t)col0 + cols > S)
-    return fail(I8A_ERR_INVALID_ARG, "tile [%d+%d, %d+%d] outside [0, %d)", row0, rows, col0,
-                cols, S);
-  if (!s32_out || !aligned(s32_out, 4)) return fail(I8A_ERR_INVALID_ARG, "bad s32_out");
-  if (hadamard != 0 && hadamard != 1) return fail(I8A_ERR_INVALID_ARG, "hadamard must be 0 or 1");
-  FwdGeom g{q, k, v, nullptr, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D, 1.0f, 0, hadamard};
-  const WsPlan p = plan_workspace(B, (int64_t)B * S, S, Hq, Hkv, D);
-  i8a_status pst = run_phases(g, PH_KV | PH_Q, workspace, workspace_bytes, (hipStream_t)stream);
-  if (pst != I8A_OK) return pst;
-  hipError_t e = launch_debug_qk(g, p, workspace, b, h, row0, rows, col0, cols, s32_out, qscale_out,
-                      kscale_out, vscale_out, kmean_out, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "debug score launch");
-  return I8A_OK;
+  return attn_int8_debug_qk_ex(q, k, v, nullptr, B, S, (int64_t)B * S, Hq, Hkv, D,
+                               hadamard ? I8A_FWD_HADAMARD : 0, b, h, row0, rows, col0, cols,
+                               s32_out, qscale_out, kscale_out, vscale_out, kmean_out, nullptr,
+                               nullptr, workspace, workspace_bytes, stream);
 }
 
 static_assert(I8A_VCACHE_INT8 == VF_INT8 && I8A_VCACHE_FP16 == VF_FP16,

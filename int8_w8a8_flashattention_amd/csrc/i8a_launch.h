@@ -74,11 +74,22 @@ hipError_t launch_prep(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, boo
 // Attention over the prepared workspace (Q, K and V all prepared).
 hipError_t launch_attn(const FwdGeom& g, const WsPlan& p, const void* ws, hipStream_t stream);
 
-// Debug dump of S32 and scales for batch b, query head h (dense geometry only).
-hipError_t launch_debug_qk(const FwdGeom& g, const WsPlan& p, const void* ws, int32_t b,
+// Outputs of the debug dump (every pointer but s32 may be null).
+struct DebugOut {
+  int32_t* s32;      // [rows][cols]
+  int32_t cols;
+  float* qscale;     // [rows]
+  float* kscale;     // [cols]
+  float* vscale;     // [cols]   V per token
+  float* kmean;      // [D]
+  _Float16* vhat;    // [cols][D] the prepared V rows
+  float* vchan;      // [D]      V per channel
+};
+
+// Debug dump of S32, scales, K mean and prepared V rows for sequence s, query head h.
+hipError_t launch_debug_qk(const FwdGeom& g, const WsPlan& p, const void* ws, int32_t s,
                            int32_t h, int32_t row0, int32_t rows, int32_t col0, int32_t cols,
-                           int32_t* s32, float* qscale, float* kscale, float* vscale,
-                           float* kmean, hipStream_t stream);
+                           const DebugOut& o, hipStream_t stream);
 
 // ----------------------------------------------------------------------------------
 // Decode KV cache: per (batch, kv head), ceil(S / TKD) tiles of TKD tokens, each a

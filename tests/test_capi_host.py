@@ -177,3 +177,23 @@ def test_backward_head_dims_and_arguments(lib):
     assert lib.attn_bwd(*args, 48, 0.1, 1, FAKE, need, None) == HEADDIM
     assert lib.attn_bwd(*args, 256, 0.0, 1, FAKE, need, None) == INVALID
     assert lib.attn_bwd(*args, 256, 0.1, 1, FAKE, need - 1, None) == WSSMALL
+
+
+def test_debug_ex_rejects_bad_arguments(lib):
+    # Dense geometry (no cu_seqlens) must have total = nseq * max_seqlen; unknown flags,
+    # a per-token V scale output with V per channel (and the reverse), and misaligned
+    # pointers are rejected on the host.
+    def call(cu=None, nseq=1, L=64, T=64, flags=0, seq=0, h=0, r0=0, r=8, c0=0, c=8,
+             vscale=None, vhat=None, vchan=None):
+        return lib.attn_int8_debug_qk_ex(FAKE, FAKE, FAKE, cu, nseq, L, T, 4, 2, 64, flags, seq,
+                                         h, r0, r, c0, c, FAKE, None, None, vscale, None, vhat,
+                                         vchan, FAKE, 1 << 40, None)
+    assert call(T=65) == INVALID
+    assert call(flags=8) == INVALID
+    assert call(flags=i8.FWD_V_PER_CHANNEL, vscale=FAKE) == INVALID
+    assert call(flags=0, vchan=FAKE) == INVALID
+    assert call(vhat=ctypes.c_void_p((1 << 20) + 1)) == INVALID
+    assert call(cu=ctypes.c_void_p((1 << 20) + 2), nseq=2, L=40, T=64) == INVALID
+    assert call(seq=1) == INVALID
+    assert call(r0=60, r=8) == INVALID
+    assert b"tile" in lib.i8a_last_error()

@@ -35,16 +35,21 @@ def host(t):
 
 
 def check_close(o16, ref, what):
-    """max-abs 2e-3 over the oracle's own fp16 rounding error of each element (outputs
-    of magnitude >= 4 sit on an fp16 grid coarser than 2 * 2e-3), rel-L2 1e-3."""
+    """max-abs 2e-3 wherever |O| < 4; where |O| >= 4 (an fp16 grid coarser than
+    2 * 2e-3, which no fp16 result can meet) 2e-3 over the oracle's own fp16 rounding
+    error of that element; rel-L2 1e-3 over all."""
     o = o16.astype(np.float64)
+    err = np.abs(o - ref)
+    small = np.abs(ref) < 4.0
+    mx = float(err[small].max()) if small.any() else 0.0
     floor = np.abs(ref.astype(np.float16).astype(np.float64) - ref)
-    mx = float((np.abs(o - ref) - floor).max())
+    ex = float((err - floor)[~small].max()) if (~small).any() else 0.0
     rel = float(np.linalg.norm(o - ref) / max(np.linalg.norm(ref), 1e-30))
-    say(f"  {what}: max excess over the fp16 floor={mx:.3e} rel_l2={rel:.3e} "
-        f"(max |O| {np.abs(ref).max():.2f})")
+    say(f"  {what}: max_abs={mx:.3e} (|O| < 4), max excess over the fp16 floor={ex:.3e} "
+        f"(|O| >= 4), rel_l2={rel:.3e} (max |O| {np.abs(ref).max():.2f})")
     assert np.all(np.isfinite(o)), what
     assert mx <= MAX_ABS, (what, mx)
+    assert ex <= MAX_ABS, (what, ex)
     assert rel <= REL_L2, (what, rel)
 
 
