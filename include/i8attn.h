@@ -106,6 +106,22 @@ i8a_status attn_int8_fwd(const void* q, const void* k, const void* v, void* out,
                          int32_t causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_int8_fwd_noalloc - attn_int8_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the workspace is a 64 MiB device array inside the library, one per GPU,
+ * held until the process ends, and the call allocates and frees nothing.  Arguments,
+ * layouts and errors as for attn_int8_fwd without the workspace; sizes whose workspace
+ * (attn_int8_workspace_bytes) exceeds 64 MiB fail with I8A_ERR_WORKSPACE_TOO_SMALL
+ * before any work is enqueued (B=1, Hq=32, Hkv=8, S=4096, D=128 needs about 32 MiB).
+ * Every call on one GPU uses that GPU's same array: calls that overlap on one GPU (on
+ * different streams, or from several threads) race and give undefined output; calls
+ * in order on one stream are safe.  No part of the array needs to start at zero.
+ */
+i8a_status attn_int8_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                                 int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D,
+                                 float softmax_scale, int32_t causal, void* stream);
+
+/*
  * Variants of the forward, as flags of attn_int8_fwd_ex / attn_int8_varlen_fwd_ex (any
  * combination; 0 is attn_int8_fwd itself):
  *

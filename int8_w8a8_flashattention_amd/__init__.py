@@ -32,7 +32,7 @@ import torch
 
 __all__ = [
     "quant_rowwise_i8", "attn_int8_fwd", "attn_int8_varlen_fwd", "attn_int8_debug_qk",
-    "attn_int8_varlen_debug_qk",
+    "attn_int8_varlen_debug_qk", "attn_int8_fwd_noalloc",
     "attn_int8_fwd_hadamard", "attn_int8_fwd_ex", "attn_int8_varlen_fwd_ex", "FWD_HADAMARD",
     "FWD_V_PER_CHANNEL", "FWD_Q_PER_BLOCK", "attn_int8_prepare_kv", "attn_int8_prepare_q",
     "attn_int8_attend", "attn_int8_fwd_prepared",
@@ -72,6 +72,7 @@ _SIGS = {
                                                                                  _c_sz, _c_vp]),
     "attn_int8_fwd_hadamard": (_c_i32, [_c_vp] * 4 + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_sz,
                                                                     _c_vp]),
+    "attn_int8_fwd_noalloc": (_c_i32, [_c_vp] * 4 + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp]),
     "attn_int8_fwd_ex": (_c_i32, [_c_vp] * 4 + [_c_i32] * 5 + [_c_f32, _c_i32, _c_i32, _c_vp, _c_sz,
                                                               _c_vp]),
     "attn_int8_varlen_fwd_ex": (_c_i32, [_c_vp] * 5 + [_c_i32, _c_i32, _c_i64, _c_i32, _c_i32,
@@ -239,6 +240,23 @@ def attn_int8_fwd(q, k, v, causal=True, softmax_scale=None, out=None, workspace=
                                _scale(softmax_scale, D), int(bool(causal)), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(q.device))
     _check(st, "attn_int8_fwd")
+    return out
+
+
+def attn_int8_fwd_noalloc(q, k, v, out, causal=True, softmax_scale=None):
+    """:func:`attn_int8_fwd` into the caller's fp16 ``out[B,Hq,S,D]`` with the library's
+    own per-GPU scratch as the workspace: the call allocates nothing (for callers that
+    cannot).  Calls that overlap on one GPU race (they share the scratch)."""
+    B, Hq, Hkv, S, D = _dense_shapes(q, k, v)
+    _need_gpu_fp16("out", out, 4)
+    if out.shape != q.shape or out.device != q.device:
+        raise ValueError("out must match q")
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.attn_int8_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, S, D,
+                                       _scale(softmax_scale, D), int(bool(causal)),
+                                       _stream(q.device))
+    _check(st, "attn_int8_fwd_noalloc")
     return out
 
 

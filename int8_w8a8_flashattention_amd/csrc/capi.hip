@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "i8a_launch.h"
 #include "i8attn.h"
 
@@ -91,6 +93,35 @@ static i8a_status check_common(const void* q, const void* k, const void* v, cons
 }
 
 static const int64_t kMaxTokens = (int64_t)1 << 30;
+
+// ---------------------------------------------------------------------------------
+// Scratch memory of attn_int8_fwd_noalloc: the forward's workspace as a file-scope
+// device array, so that the entry point allocates nothing.  Every GPU the library runs
+// on holds its own copy until the process ends.  In host code `scratch` is only a
+// stand-in for the symbol: its device address is taken once per device with
+// hipGetSymbolAddress (with that device current) and kept in scratch_ptr.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static void* scratch_ptr[kMaxDevices];
+static std::mutex scratch_mu;
+
+static hipError_t scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return hipSuccess;
+}
 
 }  // namespace i8a
 
@@ -179,6 +210,30 @@ i8a_status attn_int8_fwd(const void* q, const void* k, const void* v, void* out,
   if ((int64_t)B * S > kMaxTokens) return fail(I8A_ERR_INVALID_ARG, "B*S too large");
   FwdGeom g{q, k, v, out, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D, softmax_scale, causal};
   return run_phases(g, PH_KV | PH_Q | PH_ATTN, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+i8a_status attn_int8_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                                 int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D,
+                                 float softmax_scale, int32_t causal, void* stream) {
+  // The workspace check of attn_int8_fwd with a placeholder address, so that a size
+  // beyond the scratch array is rejected before anything touches the device.
+  i8a_status st = check_common(q, k, v, out, Hq, Hkv, D, softmax_scale, causal,
+                               reinterpret_cast<void*>(256));
+  if (st != I8A_OK) return st;
+  if (B < 1 || S < 1 || B > kMaxGridYZ)
+    return fail(I8A_ERR_INVALID_ARG, "need 1 <= B <= %d and S >= 1", kMaxGridYZ);
+  if ((int64_t)B * S > kMaxTokens) return fail(I8A_ERR_INVALID_ARG, "B*S too large");
+  const size_t need = plan_workspace(B, (int64_t)B * S, S, Hq, Hkv, D).total;
+  if (need > kScratchBytes)
+    return fail(I8A_ERR_WORKSPACE_TOO_SMALL,
+                "attn_int8_fwd_noalloc: these sizes need %zu bytes of workspace, more than its "
+                "%zu-byte scratch; call attn_int8_fwd with a workspace",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  hipError_t e = scratch_for_current_device(&ws);
+  if (e != hipSuccess) return hip_fail(e, "scratch address");
+  return attn_int8_fwd(q, k, v, out, B, Hq, Hkv, S, D, softmax_scale, causal, ws, kScratchBytes,
+                       stream);
 }
 
 i8a_status attn_int8_fwd_ex(const void* q, const void* k, const void* v, void* out, int32_t B,
