@@ -453,7 +453,7 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms_step = e0.elapsed_time(e1) / args.steps
-    log(f"bench: {args.steps} steps, {ms_step * 1e3:.1f} us/step (host wall {t_wall * 1e3 / args.steps:.1f} us/step)")
+    log(f"bench: {args.steps} steps, {ms_step * 1e3:.1f} us/step (host wall {t_wall * 1e6 / args.steps:.1f} us/step)")
 
     # The phases alone: the attention kernel (dominant), then K/V and Q preparation.
     def timed(fn):

@@ -584,7 +584,8 @@ def attn_bwd(q, k, v, dout, causal=True, softmax_scale=None, workspace=None):
     lib = load_library()
     nbytes = lib.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D)
     if nbytes == 0:
-        raise ValueError(f"backward sizes not supported (D={D} must be 32, 64 or 128)")
+        raise ValueError(f"backward sizes not supported: B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} "
+                         f"(needs B, S >= 1, Hq a multiple of Hkv, D in {HEAD_DIMS})")
     ws = _workspace(workspace, nbytes, q.device)
     with torch.cuda.device(q.device):
         st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
