@@ -413,11 +413,15 @@ __device__ __forceinline__ void vm_wait_n(int n) {
   }
 }
 
-template <int D, bool CAUSAL, int NW>
+// FQ: the kernel quantizes its Q rows itself from the fp16 input qin (layout aq, the
+// output's), with the Q/K row rule, or with qblk one scale per 32-row block counted
+// from the sequence start; otherwise it reads the prepared fragments q8 and scales qs.
+template <int D, bool CAUSAL, int NW, bool FQ>
 __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
     const int8_t* __restrict__ q8, const float* __restrict__ qs, int64_t Qpad,
-    _Float16* __restrict__ out, Act aq, Seqs seqs, int Hq, int Hkv, int nseq, int xcd_map,
-    float qk_log2, const char* __restrict__ tiles, int64_t Ppad) {
+    const _Float16* __restrict__ qin, int qblk, _Float16* __restrict__ out, Act aq, Seqs seqs,
+    int Hq, int Hkv, int nseq, int xcd_map, float qk_log2, const char* __restrict__ tiles,
+    int64_t Ppad) {
   using LY = Lay<D>;
   using DM = Dma<D, NW>;
   constexpr int NKB = LY::NKB;
@@ -461,17 +465,56 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
     return (CAUSAL && jj * TK + TK - 1 > qw0) || jj * TK + TK > L;
   };
 
-  // Prologue: tiles 0 .. NS-2 stream into their stages while the wave's Q fragments and
-  // scales load.
+  // Prologue: tiles 0 .. NS-2 stream into their stages while the wave's Q rows load.
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i)
     if (i < nt) copy_tile_dma<D, NW>(tsrc + (int64_t)i * LY::STAGE, smem + i * LY::STAGE, tid, w);
-  const int64_t qslot = (int64_t)h * Qpad + Seqs::qpstart(s, start) + qw0;
   v4i qf[NKB];
+  float qsc;
+  if constexpr (FQ) {
+    // Lane (m, hh) holds channels 32 kb + 16 hh + j (j < 16) of row qi: its B-operand
+    // fragment positions, so the codes are made in place.  The row's absolute maximum
+    // combines the two half-rows of lanes m and m + 32 (a max is exact in any order);
+    // rows past the sequence end get zero codes and scale 0.
+    const bool real = qi < L;
+    v8h xr[NKB][2];
+    if (real) {
+      const _Float16* row = qin + aq.off(start, h, qi) + 16 * hh;
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-    qf[kb] = reinterpret_cast<const v4i*>(q8 + qslot * D)[kb * 64 + lane];
-  const float qsc = fmaxf(qs[qslot + m] * qk_log2, FLT_MIN);
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          xr[kb][e] = *reinterpret_cast<const v8h*>(row + 32 * kb + 8 * e);
+    }
+    float xf[NKB][2][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          xf[kb][e][j] = real ? (float)xr[kb][e][j] : 0.0f;
+          amax = fmaxf(amax, fabsf(xf[kb][e][j]));
+        }
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    // One scale per 32-row block: the wave's rows are exactly one block.
+    if (qblk) amax = group_max<64>(amax);
+    const RowQ rq(real ? row_scale(amax, 24) : 0.0f);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const uint2 lo = real ? rq.pack8(xf[kb][0]) : make_uint2(0u, 0u);
+      const uint2 hi = real ? rq.pack8(xf[kb][1]) : make_uint2(0u, 0u);
+      qf[kb] = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+    }
+    qsc = fmaxf(rq.s * qk_log2, FLT_MIN);
+  } else {
+    const int64_t qslot = (int64_t)h * Qpad + Seqs::qpstart(s, start) + qw0;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      qf[kb] = reinterpret_cast<const v4i*>(q8 + qslot * D)[kb * 64 + lane];
+    qsc = fmaxf(qs[qslot + m] * qk_log2, FLT_MIN);
+  }
   vm_wait<0>();
   __syncthreads();
 
@@ -852,12 +895,14 @@ static hipError_t attn_d(const FwdGeom& g, const WsPlan& p, const void* ws, hipS
   // Rotated Q and K rows carry H H^T = D I: an extra exact factor 1/D on the logits.
   const float qk_log2 = g.softmax_scale * 1.4426950408889634f * (g.rot ? 1.0f / g.D : 1.0f);
   Seqs sq{g.cu, g.S, g.max_len, g.T};
-  if constexpr (D <= 128)
-    attn_pipe_kernel<D, C, NW><<<dim3((unsigned)blocks), dim3(64 * NW), 0, stream>>>(
+  if constexpr (D <= 128) {
+    auto kern = g.fuse_q ? attn_pipe_kernel<D, C, NW, true> : attn_pipe_kernel<D, C, NW, false>;
+    kern<<<dim3((unsigned)blocks), dim3(64 * NW), 0, stream>>>(
         reinterpret_cast<const int8_t*>(w + p.off_q8),
-        reinterpret_cast<const float*>(w + p.off_qs), p.Qpad, static_cast<_Float16*>(g.out),
+        reinterpret_cast<const float*>(w + p.off_qs), p.Qpad,
+        static_cast<const _Float16*>(g.q), g.qblk, static_cast<_Float16*>(g.out),
         act_of(g, g.Hq), sq, g.Hq, g.Hkv, g.nseq, xcd_map, qk_log2, w + p.off_tiles, p.Ppad);
-  else
+  } else
     attn_fwd_kernel<D, C><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
         reinterpret_cast<const int8_t*>(w + p.off_q8),
         reinterpret_cast<const float*>(w + p.off_qs), p.Qpad, static_cast<_Float16*>(g.out),

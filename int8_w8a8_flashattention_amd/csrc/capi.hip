@@ -190,12 +190,19 @@ static i8a_status run_phases(const FwdGeom& g, int phases, void* ws, size_t ws_b
     return fail(I8A_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", p.total,
                 ws_bytes);
   hipError_t e;
+  // Q quantized inside the attention kernel where it supports the variant: the same
+  // codes and scales as the Q preparation, without their round trip through memory.
+  FwdGeom gf = g;
+  if ((phases & PH_Q) && (phases & PH_ATTN) && !g.rot && g.D <= 128) {
+    gf.fuse_q = 1;
+    phases &= ~PH_Q;
+  }
   if (phases & (PH_KV | PH_Q)) {
     e = launch_prep(g, p, ws, (phases & PH_KV) != 0, (phases & PH_Q) != 0, stream);
     if (e != hipSuccess) return hip_fail(e, "preparation launch");
   }
   if (!(phases & PH_ATTN)) return I8A_OK;
-  e = launch_attn(g, p, ws, stream);
+  e = launch_attn(gf, p, ws, stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return I8A_OK;
 }

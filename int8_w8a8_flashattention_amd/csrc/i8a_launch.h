@@ -60,6 +60,9 @@ struct FwdGeom {
   int rot;  // Q and K rows Hadamard-rotated before quantization (logits take 1/D)
   int vch;  // V quantized per channel over each sequence's tokens (else per token)
   int qblk = 0;  // Q quantized with one scale per 32-row block (else per row)
+  // The attention kernel quantizes Q itself from q (no Q preparation pass); only for
+  // unrotated rows and D <= 128.
+  int fuse_q = 0;
 };
 
 hipError_t launch_quant_rowwise(const void* x, int64_t rows, int32_t d, const float* sub_mean,
@@ -71,7 +74,8 @@ hipError_t launch_quant_rowwise(const void* x, int64_t rows, int32_t d, const fl
 hipError_t launch_prep(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, bool qq,
                        hipStream_t stream);
 
-// Attention over the prepared workspace (Q, K and V all prepared).
+// Attention over the prepared workspace (K and V prepared; Q prepared too unless
+// g.fuse_q).
 hipError_t launch_attn(const FwdGeom& g, const WsPlan& p, const void* ws, hipStream_t stream);
 
 // Outputs of the debug dump (every pointer but s32 may be null).
