@@ -25,6 +25,10 @@ The method it defines comes from the "SuperL8" README (the page titled
   quantization (the ``hadamard`` option of the forward).
 * *Quantization* table, row "V per-channel / per-token": V quantized per token
   (default) or per channel over the tokens (the ``v_per_channel`` option).
+* *Quantization* table, row "Per-row int8" (Q outlier detection) and the
+  *Attention kernels* table's ``attn_w8a8_fwd`` row (per-warp, outlier-aware): Q
+  quantized per 32-row block, and Q's outlier channels multiplied in fp16 beside the
+  int8 product (the ``q_per_block`` and ``q_outliers`` options).
 * *Quick start*: ``attn_int8_fwd(q, k, v, causal=True)`` takes fp16
   ``q[B,Hq,S,D]``, ``k/v[B,Hkv,S,D]`` and quantizes internally.
 
@@ -45,6 +49,9 @@ from .attn_ref import (  # noqa: F401
     quant_rows,
     quant_cols,
     quant_row_blocks,
+    q_outlier_channels,
+    Q_OUTLIER_THRESHOLD,
+    Q_OUTLIER_MAX,
     quantize_qkv,
     fwht_f32,
     qk_int32,

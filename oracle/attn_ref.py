@@ -69,6 +69,20 @@ R14 V per channel (the *Quantization* table's "V per-channel / per-token" row:
     significand (the V rule of R2, so that every dequantized value is exactly an
     fp16 number) and the codes follow R3 with that channel's scale.
 
+R19 Q outlier detection (the *Quantization* table's "Per-row int8" row: symmetric,
+    K-smoothing, Q outlier detection; the *Attention kernels* table's
+    ``attn_w8a8_fwd`` row: outlier-aware).  The page gives no rule; the plainest
+    reading is the mixed-precision decomposition of int8 products with outlier
+    feature dimensions (LLM.int8(), Dettmers et al. 2022), with the outliers
+    detected on Q.  Per (sequence, kv head), channel d is an outlier channel when
+    ``max |q[t, h, d]|`` over the sequence's tokens t and the query heads h of the
+    kv head's group exceeds 6 (the published magnitude threshold); at most 16 are
+    kept, the largest maxima first, ties to the lower channel.  Q rows and the
+    mean-smoothed K rows are quantized (R2/R3, per row or per block) with those
+    channels set to zero; the channels themselves stay as the fp16 inputs, K
+    without the mean (a per-row constant of the logits), and the logits become
+    ``(S32 * sq_i * sk_j + sum_{d in set} q_id * k_jd) * softmax_scale``.
+
 Quantization steps are emulated op for op in numpy float32, which is IEEE
 single precision with round-to-nearest-even; everything after the integer
 codes is exact or fp64.
@@ -83,6 +97,10 @@ QK_SCALE_BITS = 24  # a plain fp32 scale
 V_SCALE_BITS = 4
 
 _ROW_BLOCK = 512  # query rows per block: keeps the [rows, keys] logits small
+
+#: Outlier channels of Q (R19): the magnitude threshold and the most channels kept.
+Q_OUTLIER_THRESHOLD = 6.0
+Q_OUTLIER_MAX = 16
 
 
 def default_softmax_scale(d: int) -> np.float32:
@@ -191,27 +209,71 @@ def quant_cols(x32: np.ndarray, scale_bits: int = 4):
     return np.ascontiguousarray(np.swapaxes(codes, -1, -2)), scale
 
 
-def quantize_qkv(q16, k16, v16, hadamard=False, v_per_channel=False, q_per_block=False):
+def q_outlier_channels(qg16):
+    """Outlier channels of Q (R19) for one (sequence, kv head): ``qg16`` is fp16
+    ``[G, L, D]``, the group's query heads over the sequence's tokens.  A channel is an
+    outlier when its largest magnitude exceeds the threshold; at most
+    ``Q_OUTLIER_MAX`` of them, the largest magnitudes first, ties to the lower channel.
+    Returns the channel indices in increasing order (int64)."""
+    qg = np.asarray(qg16)
+    if qg.dtype != np.float16:
+        raise TypeError("q_outlier_channels expects fp16 input")
+    D = qg.shape[-1]
+    if qg.size == 0:
+        return np.zeros(0, dtype=np.int64)
+    a = np.abs(qg.astype(np.float64)).reshape(-1, D).max(axis=0)
+    cand = [d for d in range(D) if a[d] > Q_OUTLIER_THRESHOLD]
+    cand.sort(key=lambda d: (-a[d], d))
+    return np.array(sorted(cand[:Q_OUTLIER_MAX]), dtype=np.int64)
+
+
+def quantize_qkv(q16, k16, v16, hadamard=False, v_per_channel=False, q_per_block=False,
+                 q_outliers=False):
     """Quantize dense BHSD q/k/v as the forward does internally (with ``hadamard``,
     Q and the mean-smoothed K rows rotated first, R13; with ``v_per_channel``, V
     quantized per channel over the tokens, R14; with ``q_per_block``, Q quantized with
-    one scale per 32-row block, R18).
+    one scale per 32-row block, R18; with ``q_outliers``, Q's outlier channels taken
+    out of the int8 part, R19).
 
     Returns a dict with ``q8, sq, k8, sk, v8, sv, kmean``; ``sv`` is ``[B, Hkv, S]``
-    per token or ``[B, Hkv, D]`` per channel.
+    per token or ``[B, Hkv, D]`` per channel.  With ``q_outliers`` it also holds
+    ``ochan`` (int64 ``[B, Hkv, 16]``, the outlier channels in increasing order,
+    padded with -1) and the outlier part ``qo`` (fp64 ``[B, Hq, S, 16]``) and ``ko``
+    (fp64 ``[B, Hkv, S, 16]``): the fp16 inputs at those channels, 0 in the padding.
     """
+    if hadamard and q_outliers:
+        raise ValueError("the rotation and Q outlier detection do not combine")
+    B, Hq, S, D = q16.shape
+    Hkv = k16.shape[1]
+    G = Hq // Hkv
     q32 = q16.astype(np.float32)
-    qx = fwht_f32(q32) if hadamard else q32
-    q8, sq = quant_row_blocks(qx) if q_per_block else quant_rows(qx)
     m = kmean(k16)  # [B, Hkv, D]
     ksm = k16.astype(np.float32) - m[..., None, :]
     assert ksm.dtype == np.float32
+    extra = {}
+    if q_outliers:
+        ochan = np.full((B, Hkv, Q_OUTLIER_MAX), -1, dtype=np.int64)
+        qo = np.zeros((B, Hq, S, Q_OUTLIER_MAX))
+        ko = np.zeros((B, Hkv, S, Q_OUTLIER_MAX))
+        q32 = q32.copy()
+        ksm = ksm.copy()
+        for b in range(B):
+            for g in range(Hkv):
+                ch = q_outlier_channels(q16[b, g * G:(g + 1) * G])
+                ochan[b, g, :ch.size] = ch
+                qo[b, g * G:(g + 1) * G, :, :ch.size] = q16[b, g * G:(g + 1) * G][..., ch]
+                ko[b, g, :, :ch.size] = k16[b, g][..., ch]
+                q32[b, g * G:(g + 1) * G][..., ch] = 0.0
+                ksm[b, g][..., ch] = 0.0
+        extra = dict(ochan=ochan, qo=qo, ko=ko)
+    qx = fwht_f32(q32) if hadamard else q32
+    q8, sq = quant_row_blocks(qx) if q_per_block else quant_rows(qx)
     k8, sk = quant_rows(fwht_f32(ksm) if hadamard else ksm)
     if v_per_channel:
         v8, sv = quant_cols(v16.astype(np.float32), V_SCALE_BITS)
     else:
         v8, sv = quant_rows(v16.astype(np.float32), V_SCALE_BITS)
-    return dict(q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, kmean=m)
+    return dict(q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, kmean=m, **extra)
 
 
 def qk_int32(q8: np.ndarray, k8: np.ndarray) -> np.ndarray:
@@ -225,13 +287,15 @@ def qk_int32(q8: np.ndarray, k8: np.ndarray) -> np.ndarray:
 
 
 def attn_core(q8, sq, k8, sk, v8, sv, softmax_scale, causal, rows=None, logit_factor=1.0,
-              v_per_channel=False):
+              v_per_channel=False, qo=None, ko=None):
     """Attention of one head on quantized operands (R7, R8, R10).
 
     ``q8 [Sq, D]``, ``k8/v8 [Sk, D]`` int8; ``sq [Sq]``, ``sk [Sk]`` fp32; ``sv [Sk]``
     per key, or ``[D]`` per channel with ``v_per_channel`` (R14).
     ``rows`` optionally selects query rows (each row is independent).
     ``logit_factor`` multiplies every logit (1/D for rotated rows, R13).
+    ``qo [Sq, n]``, ``ko [Sk, n]``: the outlier channels' values (R19), whose exact
+    products are added to the dequantized scores.
     Returns fp64 ``[len(rows), D]``.
     """
     Sq, Sk = q8.shape[0], k8.shape[0]
@@ -249,7 +313,11 @@ def attn_core(q8, sq, k8, sk, v8, sv, softmax_scale, causal, rows=None, logit_fa
     for r0 in range(0, rows.size, _ROW_BLOCK):
         rr = rows[r0:r0 + _ROW_BLOCK]
         s32 = q8[rr].astype(np.float64) @ kk.T  # exact integers
-        logits = s32 * sq.astype(np.float64)[rr][:, None] * skd[None, :] * sm
+        if qo is None:
+            logits = s32 * sq.astype(np.float64)[rr][:, None] * skd[None, :] * sm
+        else:  # fp16 products are exact in fp64, and so is a sum of 16 of them
+            deq = s32 * sq.astype(np.float64)[rr][:, None] * skd[None, :]
+            logits = (deq + qo[rr] @ ko.T) * sm
         if causal:
             logits = np.where(np.arange(Sk)[None, :] <= rr[:, None], logits, -np.inf)
         mx = logits.max(axis=1, keepdims=True)
@@ -260,14 +328,15 @@ def attn_core(q8, sq, k8, sk, v8, sv, softmax_scale, causal, rows=None, logit_fa
 
 
 def attn_int8_fwd(q16, k16, v16, causal=True, softmax_scale=None, heads=None, rows=None,
-                  hadamard=False, v_per_channel=False, q_per_block=False):
+                  hadamard=False, v_per_channel=False, q_per_block=False, q_outliers=False):
     """The dense forward: fp16 ``q[B,Hq,S,D]``, ``k/v[B,Hkv,S,D]`` -> fp64 O.
 
     ``heads`` (list of (b, h)) and ``rows`` restrict the output to a sample;
     the result then has shape ``[len(heads), len(rows), D]``, otherwise
     ``[B, Hq, S, D]``.  ``hadamard`` selects the rotated variant (R13): Q and K
     rows rotated before quantization and the logits scaled by an extra 1/D.
-    ``v_per_channel`` quantizes V per channel (R14).
+    ``v_per_channel`` quantizes V per channel (R14), ``q_per_block`` Q per 32-row block
+    (R18), ``q_outliers`` detects Q's outlier channels (R19).
     """
     B, Hq, S, D = q16.shape
     Hkv = k16.shape[1]
@@ -275,7 +344,7 @@ def attn_int8_fwd(q16, k16, v16, causal=True, softmax_scale=None, heads=None, ro
         raise ValueError("Hq must be a multiple of Hkv")
     G = Hq // Hkv
     sm = default_softmax_scale(D) if softmax_scale is None else np.float32(softmax_scale)
-    qz = quantize_qkv(q16, k16, v16, hadamard, v_per_channel, q_per_block)
+    qz = quantize_qkv(q16, k16, v16, hadamard, v_per_channel, q_per_block, q_outliers)
     # The 1/D of the rotation multiplies the logits exactly (D is a power of two).
     extra = 1.0 / D if hadamard else 1.0
     sel = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
@@ -284,7 +353,9 @@ def attn_int8_fwd(q16, k16, v16, causal=True, softmax_scale=None, heads=None, ro
         g = h // G
         outs.append(attn_core(qz["q8"][b, h], qz["sq"][b, h], qz["k8"][b, g], qz["sk"][b, g],
                               qz["v8"][b, g], qz["sv"][b, g], sm, causal, rows, extra,
-                              v_per_channel))
+                              v_per_channel,
+                              qz["qo"][b, h] if q_outliers else None,
+                              qz["ko"][b, g] if q_outliers else None))
     o = np.stack(outs)
     if heads is None and rows is None:
         o = o.reshape(B, Hq, S, D)
@@ -292,11 +363,13 @@ def attn_int8_fwd(q16, k16, v16, causal=True, softmax_scale=None, heads=None, ro
 
 
 def attn_int8_varlen_fwd(q16, k16, v16, cu_seqlens, causal=True, softmax_scale=None,
-                         hadamard=False, v_per_channel=False, q_per_block=False):
+                         hadamard=False, v_per_channel=False, q_per_block=False,
+                         q_outliers=False):
     """The varlen forward (R11): packed ``q[T,Hq,D]``, ``k/v[T,Hkv,D]``.
 
-    Each sequence ``cu[i]:cu[i+1]`` is quantized (its own K mean, and its own V
-    channel scales with ``v_per_channel``) and attended independently.  Returns fp64
+    Each sequence ``cu[i]:cu[i+1]`` is quantized (its own K mean, its own V channel
+    scales with ``v_per_channel``, its own outlier channels with ``q_outliers``) and
+    attended independently.  Returns fp64
     ``[T, Hq, D]``.
     """
     T, Hq, D = q16.shape
@@ -310,7 +383,8 @@ def attn_int8_varlen_fwd(q16, k16, v16, cu_seqlens, causal=True, softmax_scale=N
         ks = np.ascontiguousarray(k16[a:b].transpose(1, 0, 2))[None]
         vs = np.ascontiguousarray(v16[a:b].transpose(1, 0, 2))[None]
         o = attn_int8_fwd(qs, ks, vs, causal, softmax_scale, hadamard=hadamard,
-                          v_per_channel=v_per_channel, q_per_block=q_per_block)[0]
+                          v_per_channel=v_per_channel, q_per_block=q_per_block,
+                          q_outliers=q_outliers)[0]
         out[a:b] = o.transpose(1, 0, 2)
     return out
 

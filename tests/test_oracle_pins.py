@@ -752,3 +752,143 @@ def test_q_per_block_varlen_blocks_start_at_each_sequence():
         vd = dequant(z["v8"][0], z["sv"][0]).repeat(2, axis=0)
         ref = sdpa64(qd, kd, vd, True, sm)
         np.testing.assert_allclose(got[a:b].transpose(1, 0, 2), ref, rtol=1e-9, atol=1e-12)
+
+
+# ---------------------------------------------------------------- Q outlier detection (R19)
+
+def test_q_outlier_detection_hand_derived_cases():
+    # tests/golden/q_outliers_worked.json: the threshold is strict (a peak of exactly 6
+    # is not an outlier), the peak is taken over every head of the group and every
+    # token, and past 16 candidates the largest peaks win with ties to the lower channel.
+    g = json.load(open(os.path.join(GOLDEN, "q_outliers_worked.json")))
+    for case in g["detect_cases"]:
+        q = np.array(case["q"], dtype=np.float16)
+        assert oracle.q_outlier_channels(q).tolist() == case["channels"], case["what"]
+    rc = g["row_case"]
+    q = np.zeros((1, 1, 1, 4), dtype=np.float16)
+    q[0, 0, 0] = rc["row"]
+    kv = np.ones((1, 1, 1, 4), dtype=np.float16)
+    z = oracle.quantize_qkv(q, kv, kv, q_outliers=True)
+    assert z["ochan"][0, 0][z["ochan"][0, 0] >= 0].tolist() == rc["outliers"]
+    assert Fraction(float(z["sq"][0, 0, 0])) == Fraction(rc["scale_num"], rc["scale_den"])
+    assert z["q8"][0, 0, 0].tolist() == rc["codes"]
+    assert z["qo"][0, 0, 0, :1].tolist() == [-10.0]
+
+
+def _outlier_inputs(seed, B=1, Hq=4, Hkv=2, S=96, D=32, chans=(3, 17), gain=20.0):
+    g = rng(seed)
+    q = g.standard_normal((B, Hq, S, D)).astype(np.float32)
+    k = g.standard_normal((B, Hkv, S, D)).astype(np.float32) + g.uniform(-2, 2, (1, Hkv, 1, D)).astype(np.float32)
+    v = g.standard_normal((B, Hkv, S, D)).astype(np.float32)
+    q[..., list(chans)] *= gain
+    k[..., list(chans)] *= gain
+    return q.astype(np.float16), k.astype(np.float16), v.astype(np.float16)
+
+
+def test_q_outliers_without_outliers_reduce_to_the_plain_rows():
+    # No |q| above the threshold: nothing is detected and every code, scale and output
+    # is the plain per-row (and per-block) quantization's.
+    g = rng(81)
+    q = np.clip(g.standard_normal((1, 4, 70, 32)), -5.9, 5.9).astype(np.float16)
+    k = g.standard_normal((1, 2, 70, 32)).astype(np.float16)
+    v = g.standard_normal((1, 2, 70, 32)).astype(np.float16)
+    for blk in (False, True):
+        a = oracle.quantize_qkv(q, k, v, q_per_block=blk)
+        b = oracle.quantize_qkv(q, k, v, q_per_block=blk, q_outliers=True)
+        assert (b["ochan"] == -1).all()
+        for key in ("q8", "sq", "k8", "sk", "v8", "sv"):
+            assert np.array_equal(a[key], b[key]), key
+        o1 = oracle.attn_int8_fwd(q, k, v, True, q_per_block=blk)
+        o2 = oracle.attn_int8_fwd(q, k, v, True, q_per_block=blk, q_outliers=True)
+        assert np.array_equal(o1, o2)
+
+
+@pytest.mark.parametrize("blk", [False, True])
+def test_q_outliers_int8_part_follows_the_rational_rule(blk):
+    # Every Q and K row of the int8 part: the outlier channels hold code 0 and the row
+    # (or 32-row block) scale and codes are the exact rational rule applied to the row
+    # with those channels set to zero.
+    q, k, v = _outlier_inputs(82, S=70)
+    z = oracle.quantize_qkv(q, k, v, q_per_block=blk, q_outliers=True)
+    ksm = k.astype(np.float32) - z["kmean"][..., None, :]
+    for g in range(2):
+        ch = z["ochan"][0, g][z["ochan"][0, g] >= 0]
+        assert ch.tolist() == [3, 17]
+        for t in range(70):
+            row = ksm[0, g, t].copy()
+            row[ch] = 0
+            s, c = exact_quant_row(row)
+            assert Fraction(float(z["sk"][0, g, t])) == s
+            assert z["k8"][0, g, t].tolist() == c
+        for h in (2 * g, 2 * g + 1):
+            x = q[0, h].astype(np.float32)
+            x[:, ch] = 0
+            for b0 in range(0, 70, 32 if blk else 1):
+                rows = x[b0:b0 + (32 if blk else 1)]
+                sb = rn32(max(abs(Fraction(float(e))) for e in rows.ravel()) / 127)
+                n = rows.shape[0]
+                assert all(Fraction(float(e)) == sb for e in z["sq"][0, h, b0:b0 + n])
+                assert z["q8"][0, h, b0:b0 + n].tolist() == exact_block_codes(rows, sb)
+                assert (z["q8"][0, h, b0:b0 + n][:, ch] == 0).all()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_q_outliers_forward_equals_sdpa_on_the_decomposed_operands(causal):
+    # The logits are the int8 part dequantized plus the exact products of the outlier
+    # channels: torch's fp64 attention on Q^ = sq*q8 (zeros on the outlier channels)
+    # plus q on them, and K^ = sk*k8 plus k on them, must give the oracle's output.
+    q, k, v = _outlier_inputs(83, S=80)
+    z = oracle.quantize_qkv(q, k, v, q_outliers=True)
+    qd = dequant(z["q8"], z["sq"])
+    kd = dequant(z["k8"], z["sk"])
+    for g in range(2):
+        ch = z["ochan"][0, g][z["ochan"][0, g] >= 0]
+        qd[0, 2 * g:2 * g + 2][..., ch] = q[0, 2 * g:2 * g + 2][..., ch].astype(np.float64)
+        kd[0, g][..., ch] = k[0, g][..., ch].astype(np.float64)
+    vd = dequant(z["v8"], z["sv"])
+    ref = sdpa64(qd, kd.repeat(2, axis=1), vd.repeat(2, axis=1), causal,
+                 oracle.default_softmax_scale(32))
+    got = oracle.attn_int8_fwd(q, k, v, causal, q_outliers=True)
+    np.testing.assert_allclose(got, ref, rtol=1e-9, atol=1e-12)
+
+
+def test_q_outliers_are_detected_per_kv_group():
+    # A large value in one query head marks that channel for the whole group (the
+    # other head's int8 part loses it too), and not for the other group.
+    g = rng(84)
+    q = g.standard_normal((1, 4, 40, 16)).astype(np.float16)
+    k = g.standard_normal((1, 2, 40, 16)).astype(np.float16)
+    q = np.clip(q, -5, 5)
+    q[0, 1, 7, 9] = 30.0  # head 1 is in group 0
+    z = oracle.quantize_qkv(q, k, k, q_outliers=True)
+    assert z["ochan"][0, 0].tolist() == [9] + [-1] * 15
+    assert (z["ochan"][0, 1] == -1).all()
+    assert (z["q8"][0, 0][:, 9] == 0).all() and (z["q8"][0, 1][:, 9] == 0).all()
+    assert (z["k8"][0, 0][:, 9] == 0).all() and (z["k8"][0, 1][:, 9] != 0).any()
+
+
+def test_q_outliers_varlen_sets_are_per_sequence():
+    # A sequence without outliers is attended exactly as the plain forward attends it,
+    # whatever the other sequences of the batch hold.
+    w = workloads.varlen(85, 2, 60, 2, 1, 16, True, lengths=[50, 60])
+    q = np.clip(w.q, -5, 5)
+    q[10, 0, 4] = 25.0  # sequence 0 only
+    cu = w.cu_seqlens
+    got = oracle.attn_int8_varlen_fwd(q, w.k, w.v, cu, True, q_outliers=True)
+    plain = oracle.attn_int8_varlen_fwd(q, w.k, w.v, cu, True)
+    assert np.array_equal(got[50:], plain[50:])
+    assert not np.array_equal(got[:50], plain[:50])
+
+
+def test_q_outliers_recover_quantization_quality_on_outlier_channels():
+    # The point of the detection: with 1 % of the channels x20 in Q and K, against
+    # unquantized attention, per-row and per-block Q both gain more than 8 dB.
+    w = workloads.dense(86, 1, 4, 4, 256, 128, False, outlier_frac=0.01)
+    exact = oracle.attn_exact(w.q, w.k, w.v, False)
+
+    def sqnr(o):
+        return 10 * np.log10(np.sum(exact ** 2) / np.sum((o - exact) ** 2))
+    for blk in (False, True):
+        plain = sqnr(oracle.attn_int8_fwd(w.q, w.k, w.v, False, q_per_block=blk))
+        det = sqnr(oracle.attn_int8_fwd(w.q, w.k, w.v, False, q_per_block=blk, q_outliers=True))
+        assert det > plain + 8.0, (blk, plain, det)
