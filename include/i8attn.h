@@ -153,6 +153,21 @@ i8a_status attn_int8_fwd_noalloc(const void* q, const void* k, const void* v, vo
  *   zero codes and scale 0.  Combines with the flags above (after the rotation).
  */
 #define I8A_FWD_Q_PER_BLOCK 4
+/*
+ * I8A_FWD_Q_OUTLIERS - Q outlier detection (Quantization table, "Per-row int8" row:
+ *   symmetric, K-smoothing, Q outlier detection; Attention kernels table, attn_w8a8_fwd
+ *   row: outlier-aware), read as the mixed-precision decomposition of int8 products
+ *   with outlier channels (LLM.int8(), Dettmers et al. 2022).  Per (sequence, kv head)
+ *   channel d is an outlier when max |q[t, h, d]| over the sequence's tokens and the
+ *   group's query heads exceeds 6; at most 16 are kept (largest maxima first, ties to
+ *   the lower channel).  Q rows and the mean-smoothed K rows are quantized as usual
+ *   with those channels set to zero, and the channels' fp16 values are multiplied
+ *   exactly (fp32 sums):
+ *     logit = (S32 * sq_i * sk_j + sum_{d outlier} q_id k_jd) * softmax_scale.
+ *   Combines with I8A_FWD_V_PER_CHANNEL and I8A_FWD_Q_PER_BLOCK; with I8A_FWD_HADAMARD
+ *   it is I8A_ERR_INVALID_ARG, and D = 256 is I8A_ERR_UNSUPPORTED_HEAD_DIM.
+ */
+#define I8A_FWD_Q_OUTLIERS 8
 
 /* attn_int8_fwd with the variant flags above; arguments, workspace and errors as for
  * attn_int8_fwd (unknown flag bits are I8A_ERR_INVALID_ARG). */
@@ -263,6 +278,9 @@ i8a_status attn_int8_debug_qk(const void* q, const void* k, const void* v, int32
  *   vhat_out  nullable fp16 [cols, D]: the dequantized V rows of kv head h/(Hq/Hkv) as
  *             the P.V product consumes them (scale times code, exact in fp16)
  *   vchan_out nullable fp32 [D]: the V channel scales (I8A_FWD_V_PER_CHANNEL only)
+ *   ochan_out nullable int32 [16]: the Q outlier channels of kv head h/(Hq/Hkv) in
+ *             increasing order, padded with -1 (I8A_FWD_Q_OUTLIERS only); with that
+ *             flag s32_out, qscale_out and kscale_out are the int8 part's
  * vscale_out (V per token) must be null with I8A_FWD_V_PER_CHANNEL; with
  * I8A_FWD_Q_PER_BLOCK each qscale_out entry is its row's block scale.  Rows and columns
  * must lie in [0, max_seqlen); entries past the sequence's own length are not written.
@@ -276,7 +294,8 @@ i8a_status attn_int8_debug_qk_ex(const void* q, const void* k, const void* v,
                                  int32_t rows, int32_t col0, int32_t cols, int32_t* s32_out,
                                  float* qscale_out, float* kscale_out, float* vscale_out,
                                  float* kmean_out, void* vhat_out, float* vchan_out,
-                                 void* workspace, size_t workspace_bytes, void* stream);
+                                 int32_t* ochan_out, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /*
  * Decode over an int8 KV cache (SuperL8 README, Attention kernels table, row

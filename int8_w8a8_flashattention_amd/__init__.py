@@ -34,7 +34,7 @@ __all__ = [
     "quant_rowwise_i8", "attn_int8_fwd", "attn_int8_varlen_fwd", "attn_int8_debug_qk",
     "attn_int8_varlen_debug_qk", "attn_int8_fwd_noalloc",
     "attn_int8_fwd_hadamard", "attn_int8_fwd_ex", "attn_int8_varlen_fwd_ex", "FWD_HADAMARD",
-    "FWD_V_PER_CHANNEL", "FWD_Q_PER_BLOCK", "attn_int8_prepare_kv", "attn_int8_prepare_q",
+    "FWD_V_PER_CHANNEL", "FWD_Q_PER_BLOCK", "FWD_Q_OUTLIERS", "attn_int8_prepare_kv", "attn_int8_prepare_q",
     "attn_int8_attend", "attn_int8_fwd_prepared",
     "attn_int8_workspace_bytes", "attn_int8_varlen_workspace_bytes", "library_path",
     "load_library", "SCALE_FP32", "SCALE_V4", "HEAD_DIMS", "attn_int8_kvcache_bytes",
@@ -53,6 +53,7 @@ HEAD_DIMS = (32, 64, 128, 256)
 FWD_HADAMARD = 1
 FWD_V_PER_CHANNEL = 2
 FWD_Q_PER_BLOCK = 4
+FWD_Q_OUTLIERS = 8
 VCACHE_INT8 = 1
 VCACHE_FP16 = 2
 _VFORMATS = {"int8": VCACHE_INT8, "fp16": VCACHE_FP16}
@@ -67,7 +68,7 @@ _SIGS = {
     "attn_int8_varlen_fwd": (_c_i32, [_c_vp] * 5 + [_c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_i32,
                                                      _c_f32, _c_i32, _c_vp, _c_sz, _c_vp]),
     "attn_int8_debug_qk_ex": (_c_i32, [_c_vp] * 4 + [_c_i32, _c_i32, _c_i64] + [_c_i32] * 10
-                              + [_c_vp] * 7 + [_c_vp, _c_sz, _c_vp]),
+                              + [_c_vp] * 8 + [_c_vp, _c_sz, _c_vp]),
     "attn_int8_debug_qk": (_c_i32, [_c_vp] * 3 + [_c_i32] * 11 + [_c_vp] * 5 + [_c_i32, _c_vp,
                                                                                  _c_sz, _c_vp]),
     "attn_int8_fwd_hadamard": (_c_i32, [_c_vp] * 4 + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_sz,
@@ -439,6 +440,8 @@ def _debug_call(q, k, v, cu, nseq, max_len, T, Hq, Hkv, D, flags, seq, h, row0, 
         r["vchan"] = torch.zeros(D, dtype=torch.float32, device=dev)
     else:
         r["vscale"] = torch.zeros(cols, dtype=torch.float32, device=dev)
+    if flags & FWD_Q_OUTLIERS:
+        r["ochan"] = torch.zeros(16, dtype=torch.int32, device=dev)
     lib = load_library()
     ws = _workspace(workspace, nbytes, dev)
     with torch.cuda.device(dev):
@@ -446,6 +449,7 @@ def _debug_call(q, k, v, cu, nseq, max_len, T, Hq, Hkv, D, flags, seq, h, row0, 
             _ptr(q), _ptr(k), _ptr(v), _ptr(cu), nseq, max_len, T, Hq, Hkv, D, int(flags), seq, h,
             row0, rows, col0, cols, _ptr(r["s32"]), _ptr(r["qscale"]), _ptr(r["kscale"]),
             _ptr(r.get("vscale")), _ptr(r["kmean"]), _ptr(r["vhat"]), _ptr(r.get("vchan")),
+            _ptr(r.get("ochan")),
             _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _check(st, "attn_int8_debug_qk_ex")
     return r
@@ -458,7 +462,9 @@ def attn_int8_debug_qk(q, k, v, b, h, row0, rows, col0, cols, workspace=None, ha
     it used (``flags``: the variant flags of :func:`attn_int8_fwd_ex`; ``hadamard`` is
     the same as ``flags=FWD_HADAMARD``).  Returns a dict of tensors: ``s32``,
     ``qscale``, ``kscale``, ``kmean``, ``vhat`` (fp16 ``[cols, D]``) and ``vscale``
-    (per token) or ``vchan`` (per channel, with ``FWD_V_PER_CHANNEL``)."""
+    (per token) or ``vchan`` (per channel, with ``FWD_V_PER_CHANNEL``), and with
+    ``FWD_Q_OUTLIERS`` ``ochan`` (int32 ``[16]``: the kv group's Q outlier channels,
+    -1 padded; the scores and scales are then the int8 part's)."""
     B, Hq, Hkv, S, D = _dense_shapes(q, k, v)
     if flags is None:
         flags = FWD_HADAMARD if hadamard else 0

@@ -36,12 +36,13 @@ constexpr int BM = 128;      // query rows per workgroup of the one-tile kernel
 #endif
 constexpr float TAU = PIPE_TAU;  // lazy-rescale threshold, log2 units
 
-template <int D>
+template <int D, bool QO = false>
 struct Lay {
   static constexpr int NKB = D / 32;             // 32-wide blocks of the head dim
   static constexpr int KB = TK * D;              // bytes of the int8 K codes
   static constexpr int VB = TK * D * 2;          // bytes of the fp16 V
-  static constexpr int STAGE = tile_bytes(D);    // one pipeline stage = one tile block
+  static constexpr int KO = tile_bytes(D);       // offset of the outlier channels' K
+  static constexpr int STAGE = tile_bytes(D, QO);  // one pipeline stage = one tile block
   static constexpr int NCH = STAGE / 16;         // 16-byte chunks per tile
   static constexpr int ROUNDS = (NCH + 255) / 256;
   static_assert(STAGE % 16 == 0, "tiles are copied in 16-byte chunks");
@@ -350,23 +351,23 @@ __device__ __forceinline__ void lds_dma16_sbase_lanes(const char* sbase, uint32_
 
 // Rounds of NW * 1 KB: the last one may be partial, so waves own different numbers of
 // copy instructions per tile (dma_count).
-template <int D, int NW>
+template <int D, int NW, bool QO = false>
 struct Dma {
   static constexpr int NT = 64 * NW;  // threads
-  static constexpr int ROUNDS = (Lay<D>::NCH + NT - 1) / NT;
+  static constexpr int ROUNDS = (Lay<D, QO>::NCH + NT - 1) / NT;
   static __device__ __forceinline__ int count(int w) {
     int n = 0;
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r) n += (r * NT + 64 * w < Lay<D>::NCH) ? 1 : 0;
+    for (int r = 0; r < ROUNDS; ++r) n += (r * NT + 64 * w < Lay<D, QO>::NCH) ? 1 : 0;
     return n;
   }
 };
 
-template <int D, int NW>
+template <int D, int NW, bool QO>
 __device__ __forceinline__ void copy_tile_dma(const char* __restrict__ src, char* stage, int tid,
                                               int w) {
-  using LY = Lay<D>;
-  using DM = Dma<D, NW>;
+  using LY = Lay<D, QO>;
+  using DM = Dma<D, NW, QO>;
   const uint32_t voff = 16u * (uint32_t)tid;
   const uint32_t lds0 = lds_addr(stage);
 #pragma unroll
@@ -385,11 +386,11 @@ __device__ __forceinline__ void copy_tile_dma(const char* __restrict__ src, char
 // Round r of a tile copy for this wave (copy_tile_dma is all rounds at once).  Only the
 // last round can be partial; there the lanes past the tile's end are masked off, with
 // no wave-uniform branch, so an unrolled caller stays one basic block.
-template <int D, int NW>
+template <int D, int NW, bool QO>
 __device__ __forceinline__ void copy_tile_round(const char* __restrict__ src, char* stage, int tid,
                                                 int w, int r) {
-  using LY = Lay<D>;
-  using DM = Dma<D, NW>;
+  using LY = Lay<D, QO>;
+  using DM = Dma<D, NW, QO>;
   const uint32_t lds = lds_addr(stage) + (uint32_t)(r * DM::NT * 16 + w * 1024);
   if (r + 1 < DM::ROUNDS || (LY::NCH % DM::NT) == 0)
     lds_dma16_sbase(src + r * DM::NT * 16, 16u * (uint32_t)tid, lds);
@@ -416,14 +417,20 @@ __device__ __forceinline__ void vm_wait_n(int n) {
 // FQ: the kernel quantizes its Q rows itself from the fp16 input qin (layout aq, the
 // output's), with the Q/K row rule, or with qblk one scale per 32-row block counted
 // from the sequence start; otherwise it reads the prepared fragments q8 and scales qs.
-template <int D, bool CAUSAL, int NW, bool FQ>
+// QO (with FQ): Q outlier channels.  The kv group's channels (ochan) are left out of
+// the int8 Q rows, and their fp16 products come from one 32x32x16 fp16 MFMA per
+// 32-key block with the tile's fp16 K values of those channels:
+//   t = f32(S^T) * sk_j + So^T / sq
+// (sq is replaced by 2^-60 where the int8 part is all zero, exactly undone by qsc).
+template <int D, bool CAUSAL, int NW, bool FQ, bool QO = false>
 __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
     const int8_t* __restrict__ q8, const float* __restrict__ qs, int64_t Qpad,
     const _Float16* __restrict__ qin, int qblk, _Float16* __restrict__ out, Act aq, Seqs seqs,
     int Hq, int Hkv, int nseq, int xcd_map, float qk_log2, const char* __restrict__ tiles,
-    int64_t Ppad) {
-  using LY = Lay<D>;
-  using DM = Dma<D, NW>;
+    int64_t Ppad, const int32_t* __restrict__ ochan) {
+  static_assert(!QO || FQ, "the outlier channels' Q values come from the fused Q path");
+  using LY = Lay<D, QO>;
+  using DM = Dma<D, NW, QO>;
   constexpr int NKB = LY::NKB;
   constexpr int BMW = 32 * NW;          // query rows per workgroup
   constexpr int NS = NW >= 8 ? 4 : 3;   // ring stages
@@ -468,9 +475,12 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
   // Prologue: tiles 0 .. NS-2 stream into their stages while the wave's Q rows load.
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i)
-    if (i < nt) copy_tile_dma<D, NW>(tsrc + (int64_t)i * LY::STAGE, smem + i * LY::STAGE, tid, w);
+    if (i < nt)
+      copy_tile_dma<D, NW, QO>(tsrc + (int64_t)i * LY::STAGE, smem + i * LY::STAGE, tid, w);
   v4i qf[NKB];
   float qsc;
+  v8h qo;            // QO: the row's values at the outlier slots 8 hh .. 8 hh + 7
+  float inv_qs = 0;  // QO: 1 / sq
   if constexpr (FQ) {
     // Lane (m, hh) holds channels 32 kb + 16 hh + j (j < 16) of row qi: its B-operand
     // fragment positions, so the codes are made in place.  The row's absolute maximum
@@ -486,6 +496,23 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
         for (int e = 0; e < 2; ++e)
           xr[kb][e] = *reinterpret_cast<const v8h*>(row + 32 * kb + 8 * e);
     }
+    // QO: bit 16 kb + c % 16 of omask marks outlier channel c = 32 kb + 16 hh + c % 16
+    // among this lane's channels; the row's values at the outlier slots go to qo.
+    uint64_t omask = 0;
+    if constexpr (QO) {
+      const int32_t* oc = ochan + ((int64_t)s * Hkv + g) * QO_MAX;
+#pragma unroll
+      for (int o = 0; o < QO_MAX; ++o) {
+        const int c = oc[o];
+        if (c >= 0 && ((c >> 4) & 1) == hh) omask |= 1ull << (16 * (c >> 5) + (c & 15));
+      }
+      const _Float16* row = qin + aq.off(start, h, qi);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = oc[8 * hh + j];
+        qo[j] = (real && c >= 0) ? row[c] : (_Float16)0.0f;
+      }
+    }
     float xf[NKB][2][8];
     float amax = 0.0f;
 #pragma unroll
@@ -494,7 +521,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
       for (int e = 0; e < 2; ++e)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          xf[kb][e][j] = real ? (float)xr[kb][e][j] : 0.0f;
+          const bool keep = !QO || ((omask >> (16 * kb + 8 * e + j)) & 1) == 0;
+          xf[kb][e][j] = (real && keep) ? (float)xr[kb][e][j] : 0.0f;
           amax = fmaxf(amax, fabsf(xf[kb][e][j]));
         }
     amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
@@ -507,7 +535,13 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
       const uint2 hi = real ? rq.pack8(xf[kb][1]) : make_uint2(0u, 0u);
       qf[kb] = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
     }
-    qsc = fmaxf(rq.s * qk_log2, FLT_MIN);
+    if constexpr (QO) {
+      const float sq = rq.s > 0.0f ? rq.s : 0x1p-60f;
+      inv_qs = 1.0f / sq;
+      qsc = sq * qk_log2;
+    } else {
+      qsc = fmaxf(rq.s * qk_log2, FLT_MIN);
+    }
   } else {
     const int64_t qslot = (int64_t)h * Qpad + Seqs::qpstart(s, start) + qw0;
 #pragma unroll
@@ -593,25 +627,30 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
   auto pipe_step = [&](const char* cur, const char* nxt, const char* dsrc, char* dstage,
                        auto MASK, int last, bool& upd_any) -> float {
     constexpr bool masked = decltype(MASK)::value;
-    constexpr int NQK = 2 * NKB;                // score MFMAs
-    constexpr int NM = NQK + 4 * (NKB + 1);     // all MFMAs of the iteration
+    constexpr int NQK = 2 * NKB;                // int8 score MFMAs
+    constexpr int NSC = NQK + (QO ? 2 : 0);     // score MFMAs (QO: the outlier products)
+    constexpr int NM = NSC + 4 * (NKB + 1);     // all MFMAs of the iteration
     constexpr int PF = 3;                       // operand prefetch distance, in MFMAs
-    constexpr int E_END = NQK + 2 * (NKB + 1);  // exponentials end before row sum 2
-    constexpr int C_BEG = NQK + 2;              // conversions start once the scores are in
+    constexpr int E_END = NSC + 2 * (NKB + 1);  // exponentials end before row sum 2
+    constexpr int C_BEG = NSC + 2;              // conversions start once the scores are in
     constexpr int C_END = NM - 2;               // the last two slots: the row max exchange
     constexpr int NC = C_END - C_BEG;
     const v4i* kl = reinterpret_cast<const v4i*>(nxt);
+    const v4i* kol = reinterpret_cast<const v4i*>(nxt + LY::KO);
     const v4i* vl = reinterpret_cast<const v4i*>(cur + LY::KB);
     const float* skl = reinterpret_cast<const float*>(nxt + LY::KB + LY::VB);
     // Operand of MFMA slot x (the row-sum MFMAs take none): K fragment (nb, kb) for the
-    // score products, V fragment (kg, db) for P.V.
+    // score products, the outlier channels' K fragment of block nb, V fragment (kg, db)
+    // for P.V.
     auto operand = [&](int x) -> v4i {
       if (x < NQK) return kl[((x / NKB) * NKB + x % NKB) * 64 + lane];
-      const int y = x - NQK, kg = y / (NKB + 1), db = y % (NKB + 1) - 1;
+      if (x < NSC) return kol[(x - NQK) * 64 + lane];
+      const int y = x - NSC, kg = y / (NKB + 1), db = y % (NKB + 1) - 1;
       return vl[(kg * NKB + db) * 64 + lane];
     };
-    auto has_operand = [&](int x) { return x < NQK || (x - NQK) % (NKB + 1) != 0; };
+    auto has_operand = [&](int x) { return x < NSC || (x - NSC) % (NKB + 1) != 0; };
     v16i sn[2];
+    v16f so[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -628,8 +667,11 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
       if (x < NQK) {
         const int nb = x / NKB, kb = x % NKB;
         sn[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fr[x % (PF + 1)], qf[kb], sn[nb], 0, 0, 0);
+      } else if (x < NSC) {
+        so[x - NQK] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            __builtin_bit_cast(v8h, fr[x % (PF + 1)]), qo, v16f{}, 0, 0, 0);
       } else {
-        const int y = x - NQK, kg = y / (NKB + 1), db = y % (NKB + 1) - 1;
+        const int y = x - NSC, kg = y / (NKB + 1), db = y % (NKB + 1) - 1;
         if (db < 0)
           lacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ones, pk[kg], lacc, 0, 0, 0);
         else
@@ -650,7 +692,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
       // this wave's rounds of the copy: round r at slot 2 + r (NM - 4) / R
 #pragma unroll
       for (int r = 0; r < DM::ROUNDS; ++r)
-        if (x == 2 + (r * (NM - 4)) / DM::ROUNDS) copy_tile_round<D, NW>(dsrc, dstage, tid, w, r);
+        if (x == 2 + (r * (NM - 4)) / DM::ROUNDS)
+          copy_tile_round<D, NW, QO>(dsrc, dstage, tid, w, r);
       // exponentials of this tile: items [E(x), E(x + 1))
       if (x < E_END) {
         const int i0 = (32 * x) / E_END, i1 = (32 * (x + 1)) / E_END;
@@ -677,6 +720,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
           if (i < i0 || i >= i1) continue;
           const int nb = i >> 4, g4 = i >> 2, r = i & 3;
           t[i] = (float)sn[nb][i & 15] * skv[g4][r];
+          if constexpr (QO) t[i] = __builtin_fmaf(so[nb][i & 15], inv_qs, t[i]);
           if (masked && key_off(i) > last) t[i] = -INFINITY;
           if (i & 1) {
             if (i & 2) cm1 = smax(smax(cm1, t[i - 1]), t[i]);
@@ -708,12 +752,21 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
         sc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kl[(nb * NKB + kb) * 64 + lane], qf[kb],
                                                        sc[nb], 0, 0, 0);
     }
+    v16f so0[2];
+    if constexpr (QO) {
+      const v4i* kol = reinterpret_cast<const v4i*>(smem + LY::KO);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        so0[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, kol[nb * 64 + lane]),
+                                                         qo, v16f{}, 0, 0, 0);
+    }
     const bool msk0 = needs_mask(0);
     const int last0 = last_key - 4 * hh;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const v4f skv = *reinterpret_cast<const v4f*>(skl + 32 * (i >> 4) + 8 * ((i >> 2) & 3) + 4 * hh);
       t[i] = (float)sc[i >> 4][i & 15] * skv[i & 3];
+      if constexpr (QO) t[i] = __builtin_fmaf(so0[i >> 4][i & 15], inv_qs, t[i]);
       if (msk0 && key_off(i) > last0) t[i] = -INFINITY;
     }
     float m0 = smax(t[0], t[1]), m1 = smax(t[2], t[3]);
@@ -767,7 +820,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
   for (; j + 1 < nt; ++j) {
     if (j + NS - 1 < nt) {
       const int st = scur == 0 ? NS - 1 : scur - 1;
-      copy_tile_dma<D, NW>(tsrc + (int64_t)(j + NS - 1) * LY::STAGE, smem + st * LY::STAGE, tid,
+      copy_tile_dma<D, NW, QO>(tsrc + (int64_t)(j + NS - 1) * LY::STAGE, smem + st * LY::STAGE, tid,
                            w);
     }
     vm_wait<0>();
@@ -803,7 +856,7 @@ __global__ __launch_bounds__(64) void debug_qk_kernel(
     int Hq, int Hkv, int s, int h, int row0, int rows, int col0, int cols,
     const char* __restrict__ tiles, const float* __restrict__ sv_ws,
     const float* __restrict__ svc_ws, const float* __restrict__ kmean_ws, int64_t Ppad,
-    DebugOut o) {
+    int tstride, const int32_t* __restrict__ ochan_ws, DebugOut o) {
   constexpr int NKB = D / 32;
   const int lane = threadIdx.x, m = lane & 31, hh = lane >> 5;
   const int qbase = (row0 & ~31) + 32 * blockIdx.x;
@@ -823,7 +876,7 @@ __global__ __launch_bounds__(64) void debug_qk_kernel(
   for (int kb = 0; kb < NKB; ++kb) qf[kb] = reinterpret_cast<const v4i*>(q8 + qslot * D)[kb * 64 + lane];
 
   const int tile0 = kbase - kbase % TK, nb = (kbase % TK) / 32;
-  const char* tb = tiles + ((int64_t)g * (Ppad / TK) + (pbase + tile0) / TK) * tile_bytes(D);
+  const char* tb = tiles + ((int64_t)g * (Ppad / TK) + (pbase + tile0) / TK) * tstride;
   const v4i* kt = reinterpret_cast<const v4i*>(tb);
   v16i acc;
 #pragma unroll
@@ -861,6 +914,7 @@ __global__ __launch_bounds__(64) void debug_qk_kernel(
       if (o.kmean) o.kmean[d] = kmean_ws[((int64_t)s * Hkv + g) * D + d];
       if (o.vchan) o.vchan[d] = svc_ws[((int64_t)s * Hkv + g) * D + d];
     }
+    if (o.ochan && lane < QO_MAX) o.ochan[lane] = ochan_ws[((int64_t)s * Hkv + g) * QO_MAX + lane];
   }
 }
 
@@ -896,17 +950,23 @@ static hipError_t attn_d(const FwdGeom& g, const WsPlan& p, const void* ws, hipS
   const float qk_log2 = g.softmax_scale * 1.4426950408889634f * (g.rot ? 1.0f / g.D : 1.0f);
   Seqs sq{g.cu, g.S, g.max_len, g.T};
   if constexpr (D <= 128) {
-    auto kern = g.fuse_q ? attn_pipe_kernel<D, C, NW, true> : attn_pipe_kernel<D, C, NW, false>;
+    if (g.qout && !g.fuse_q) return hipErrorInvalidValue;
+    auto kern = g.qout     ? attn_pipe_kernel<D, C, NW, true, true>
+                : g.fuse_q ? attn_pipe_kernel<D, C, NW, true, false>
+                           : attn_pipe_kernel<D, C, NW, false, false>;
     kern<<<dim3((unsigned)blocks), dim3(64 * NW), 0, stream>>>(
         reinterpret_cast<const int8_t*>(w + p.off_q8),
         reinterpret_cast<const float*>(w + p.off_qs), p.Qpad,
         static_cast<const _Float16*>(g.q), g.qblk, static_cast<_Float16*>(g.out),
-        act_of(g, g.Hq), sq, g.Hq, g.Hkv, g.nseq, xcd_map, qk_log2, w + p.off_tiles, p.Ppad);
-  } else
+        act_of(g, g.Hq), sq, g.Hq, g.Hkv, g.nseq, xcd_map, qk_log2, w + p.off_tiles, p.Ppad,
+        reinterpret_cast<const int32_t*>(w + p.off_ochan));
+  } else {
+    if (g.qout) return hipErrorInvalidValue;
     attn_fwd_kernel<D, C><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
         reinterpret_cast<const int8_t*>(w + p.off_q8),
         reinterpret_cast<const float*>(w + p.off_qs), p.Qpad, static_cast<_Float16*>(g.out),
         act_of(g, g.Hq), sq, g.Hq, g.Hkv, g.nseq, xcd_map, qk_log2, w + p.off_tiles, p.Ppad);
+  }
   return hipGetLastError();
 }
 
@@ -935,7 +995,8 @@ static hipError_t debug_d(const FwdGeom& g, const WsPlan& p, const void* ws, int
       reinterpret_cast<const int8_t*>(w + p.off_q8), reinterpret_cast<const float*>(w + p.off_qs),
       p.Qpad, sq, g.Hq, g.Hkv, s, h, row0, rows, col0, cols, w + p.off_tiles,
       reinterpret_cast<const float*>(w + p.off_sv), reinterpret_cast<const float*>(w + p.off_svc),
-      reinterpret_cast<const float*>(w + p.off_kmean), p.Ppad, o);
+      reinterpret_cast<const float*>(w + p.off_kmean), p.Ppad, tile_bytes(D, g.qout != 0),
+      reinterpret_cast<const int32_t*>(w + p.off_ochan), o);
   return hipGetLastError();
 }
 

@@ -53,8 +53,12 @@ WsPlan plan_workspace(int32_t nseq, int64_t total_tokens, int32_t max_len, int32
   off = align256(off + (size_t)nseq * Hkv * D * 4);
   p.off_sv = off;
   off = align256(off + (size_t)Hkv * p.Ppad * 4);
+  p.off_qopart = off;
+  off = align256(off + (size_t)nseq * Hkv * p.npart * D * 4);
+  p.off_ochan = off;
+  off = align256(off + (size_t)nseq * Hkv * QO_MAX * 4);
   p.off_tiles = off;
-  off = align256(off + (size_t)Hkv * (p.Ppad / TK) * tile_bytes(D));
+  off = align256(off + (size_t)Hkv * (p.Ppad / TK) * tile_bytes(D, true));
   p.off_q8 = off;
   off = align256(off + (size_t)Hq * p.Qpad * D);
   p.off_qs = off;
@@ -243,20 +247,34 @@ i8a_status attn_int8_fwd_noalloc(const void* q, const void* k, const void* v, vo
                        stream);
 }
 
+// The variant flags of a forward call into its geometry.
+static i8a_status apply_flags(FwdGeom& g, int32_t flags) {
+  if (flags & ~(I8A_FWD_HADAMARD | I8A_FWD_V_PER_CHANNEL | I8A_FWD_Q_PER_BLOCK |
+                I8A_FWD_Q_OUTLIERS))
+    return fail(I8A_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  g.rot = (flags & I8A_FWD_HADAMARD) ? 1 : 0;
+  g.vch = (flags & I8A_FWD_V_PER_CHANNEL) ? 1 : 0;
+  g.qblk = (flags & I8A_FWD_Q_PER_BLOCK) ? 1 : 0;
+  g.qout = (flags & I8A_FWD_Q_OUTLIERS) ? 1 : 0;
+  if (g.qout && g.rot)
+    return fail(I8A_ERR_INVALID_ARG, "I8A_FWD_Q_OUTLIERS does not combine with I8A_FWD_HADAMARD");
+  if (g.qout && g.D > 128)
+    return fail(I8A_ERR_UNSUPPORTED_HEAD_DIM, "I8A_FWD_Q_OUTLIERS needs D <= 128, got %d", g.D);
+  return I8A_OK;
+}
+
 i8a_status attn_int8_fwd_ex(const void* q, const void* k, const void* v, void* out, int32_t B,
                             int32_t Hq, int32_t Hkv, int32_t S, int32_t D, float softmax_scale,
                             int32_t causal, int32_t flags, void* workspace,
                             size_t workspace_bytes, void* stream) {
   i8a_status st = check_common(q, k, v, out, Hq, Hkv, D, softmax_scale, causal, workspace);
   if (st != I8A_OK) return st;
-  if (flags & ~(I8A_FWD_HADAMARD | I8A_FWD_V_PER_CHANNEL | I8A_FWD_Q_PER_BLOCK))
-    return fail(I8A_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if (B < 1 || S < 1 || B > kMaxGridYZ)
     return fail(I8A_ERR_INVALID_ARG, "need 1 <= B <= %d and S >= 1", kMaxGridYZ);
   if ((int64_t)B * S > kMaxTokens) return fail(I8A_ERR_INVALID_ARG, "B*S too large");
-  FwdGeom g{q, k, v, out, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D, softmax_scale, causal,
-            (flags & I8A_FWD_HADAMARD) ? 1 : 0, (flags & I8A_FWD_V_PER_CHANNEL) ? 1 : 0};
-  g.qblk = (flags & I8A_FWD_Q_PER_BLOCK) ? 1 : 0;
+  FwdGeom g{q, k, v, out, nullptr, B, S, S, (int64_t)B * S, Hq, Hkv, D, softmax_scale, causal};
+  st = apply_flags(g, flags);
+  if (st != I8A_OK) return st;
   return run_phases(g, PH_KV | PH_Q | PH_ATTN, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
@@ -323,8 +341,12 @@ i8a_status attn_int8_varlen_fwd_ex(const void* q, const void* k, const void* v, 
                                    int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t D,
                                    float softmax_scale, int32_t causal, int32_t flags,
                                    void* workspace, size_t workspace_bytes, void* stream) {
-  if (flags & ~(I8A_FWD_HADAMARD | I8A_FWD_V_PER_CHANNEL | I8A_FWD_Q_PER_BLOCK))
-    return fail(I8A_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  {
+    FwdGeom probe{};
+    probe.D = D;
+    const i8a_status fst = apply_flags(probe, flags);
+    if (fst != I8A_OK) return fst;
+  }
   if (!cu_seqlens) return fail(I8A_ERR_INVALID_ARG, "null cu_seqlens");
   if (!aligned(cu_seqlens, 4)) return fail(I8A_ERR_INVALID_ARG, "misaligned cu_seqlens");
   if (nseq < 1 || nseq > kMaxGridYZ)
@@ -343,9 +365,9 @@ i8a_status attn_int8_varlen_fwd_ex(const void* q, const void* k, const void* v, 
   i8a_status st = check_common(q, k, v, out, Hq, Hkv, D, softmax_scale, causal, workspace);
   if (st != I8A_OK) return st;
   FwdGeom g{q, k, v, out, cu_seqlens, nseq, 0, max_seqlen, total_tokens, Hq, Hkv, D,
-            softmax_scale, causal, (flags & I8A_FWD_HADAMARD) ? 1 : 0,
-            (flags & I8A_FWD_V_PER_CHANNEL) ? 1 : 0};
-  g.qblk = (flags & I8A_FWD_Q_PER_BLOCK) ? 1 : 0;
+            softmax_scale, causal};
+  st = apply_flags(g, flags);
+  if (st != I8A_OK) return st;
   return run_phases(g, PH_KV | PH_Q | PH_ATTN, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
@@ -366,12 +388,15 @@ i8a_status attn_int8_debug_qk_ex(const void* q, const void* k, const void* v,
                                  int32_t rows, int32_t col0, int32_t cols, int32_t* s32_out,
                                  float* qscale_out, float* kscale_out, float* vscale_out,
                                  float* kmean_out, void* vhat_out, float* vchan_out,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+                                 int32_t* ochan_out, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
   // No output tensor is written by this entry; q stands in for its alignment check.
   i8a_status st = check_common(q, k, v, q, Hq, Hkv, D, 1.0f, 0, workspace);
   if (st != I8A_OK) return st;
-  if (flags & ~(I8A_FWD_HADAMARD | I8A_FWD_V_PER_CHANNEL | I8A_FWD_Q_PER_BLOCK))
-    return fail(I8A_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  FwdGeom g{q, k, v, nullptr, cu_seqlens, nseq, cu_seqlens ? 0 : max_seqlen, max_seqlen,
+            total_tokens, Hq, Hkv, D, 1.0f, 0};
+  st = apply_flags(g, flags);
+  if (st != I8A_OK) return st;
   if (nseq < 1 || nseq > kMaxGridYZ || max_seqlen < 1 || total_tokens < 1 ||
       total_tokens > kMaxTokens || max_seqlen > total_tokens)
     return fail(I8A_ERR_INVALID_ARG, "need 1 <= nseq <= %d, 1 <= max_seqlen <= total_tokens",
@@ -393,14 +418,13 @@ i8a_status attn_int8_debug_qk_ex(const void* q, const void* k, const void* v,
     return fail(I8A_ERR_INVALID_ARG, "vscale_out (V per token) with I8A_FWD_V_PER_CHANNEL");
   if (!vch && vchan_out)
     return fail(I8A_ERR_INVALID_ARG, "vchan_out needs I8A_FWD_V_PER_CHANNEL");
-  FwdGeom g{q, k, v, nullptr, cu_seqlens, nseq, cu_seqlens ? 0 : max_seqlen, max_seqlen,
-            total_tokens, Hq, Hkv, D, 1.0f, 0, (flags & I8A_FWD_HADAMARD) ? 1 : 0, vch ? 1 : 0};
-  g.qblk = (flags & I8A_FWD_Q_PER_BLOCK) ? 1 : 0;
+  if (ochan_out && !g.qout) return fail(I8A_ERR_INVALID_ARG, "ochan_out needs I8A_FWD_Q_OUTLIERS");
+  if (ochan_out && !aligned(ochan_out, 4)) return fail(I8A_ERR_INVALID_ARG, "bad ochan_out");
   const WsPlan p = plan_workspace(nseq, total_tokens, max_seqlen, Hq, Hkv, D);
   i8a_status pst = run_phases(g, PH_KV | PH_Q, workspace, workspace_bytes, (hipStream_t)stream);
   if (pst != I8A_OK) return pst;
   const DebugOut o{s32_out,   cols,      qscale_out, kscale_out, vscale_out,
-                   kmean_out, static_cast<_Float16*>(vhat_out), vchan_out};
+                   kmean_out, static_cast<_Float16*>(vhat_out), vchan_out, ochan_out};
   hipError_t e = launch_debug_qk(g, p, workspace, seq, h, row0, rows, col0, cols, o,
                                  (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "debug score launch");
@@ -419,7 +443,7 @@ i8a_status attn_int8_debug_qk(const void* q, const void* k, const void* v, int32
   return attn_int8_debug_qk_ex(q, k, v, nullptr, B, S, (int64_t)B * S, Hq, Hkv, D,
                                hadamard ? I8A_FWD_HADAMARD : 0, b, h, row0, rows, col0, cols,
                                s32_out, qscale_out, kscale_out, vscale_out, kmean_out, nullptr,
-                               nullptr, workspace, workspace_bytes, stream);
+                               nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
 static_assert(I8A_VCACHE_INT8 == VF_INT8 && I8A_VCACHE_FP16 == VF_FP16,

@@ -14,9 +14,20 @@ constexpr int TK = 64;
 constexpr int CH = 256;
 static_assert(CH % TK == 0, "a prep chunk holds whole tiles");
 
+// Q outlier channels (the outlier-aware variant): at most QO_MAX per (sequence, kv
+// head), detected where max |q| exceeds QO_THRESHOLD.
+constexpr int QO_MAX = 16;
+constexpr float QO_THRESHOLD = 6.0f;
+// Bytes of the fp16 K values of the outlier channels of one tile (A operand of a
+// 32x32x16 fp16 MFMA per 32-key block).
+constexpr int KO_BYTES = TK * QO_MAX * 2;
+
 // Bytes of one prepared K/V tile of TK tokens: int8 K codes in MFMA fragment order,
-// then the exact fp16 dequantized V in fragment order, then the fp32 K scales.
-__host__ __device__ constexpr int tile_bytes(int D) { return TK * D * 3 + TK * 4; }
+// then the exact fp16 dequantized V in fragment order, then the fp32 K scales, and
+// with outliers the fp16 K values of the outlier channels.
+__host__ __device__ constexpr int tile_bytes(int D, bool outliers = false) {
+  return TK * D * 3 + TK * 4 + (outliers ? KO_BYTES : 0);
+}
 
 // Workspace carve-up for one forward call.  All offsets are 256-byte aligned.
 //   kpart  int64 [nseq][Hkv][npart][D]   exact K channel sums of tpw tiles (2^-24 units)
@@ -24,7 +35,9 @@ __host__ __device__ constexpr int tile_bytes(int D) { return TK * D * 3 + TK * 4
 //   vpart  fp32  [nseq][Hkv][npart][D]   V channel maxima of tpw tiles (V per channel)
 //   svc    fp32  [nseq][Hkv][D]          V channel scales (V per channel)
 //   sv     fp32  [Hkv][Ppad]             V row scales (kept for the debug dump)
-//   tiles  bytes [Hkv][Ppad / TK][tile_bytes(D)]
+//   qopart fp32  [nseq][Hkv][npart][D]   Q channel maxima of tpw tiles (Q outliers)
+//   ochan  int32 [nseq][Hkv][QO_MAX]     Q outlier channels, increasing, -1 padded
+//   tiles  bytes [Hkv][Ppad / TK][tile_bytes(D, outliers)] (room for the larger)
 //   q8     int8  [Hq][Qpad / 32][32 * D] Q codes, 32-row blocks in MFMA fragment order
 //   qs     fp32  [Hq][Qpad]              Q row scales
 // K/V token slots are padded per sequence to TK rows (Seqs::pstart), Q slots to BQ
@@ -41,7 +54,8 @@ struct WsPlan {
   int32_t tpw, npart;               // tiles per prep workgroup, partial sums per (seq, head)
   int64_t Ppad;                     // padded K/V token slots per kv head
   int64_t Qpad;                     // padded Q token slots per query head
-  size_t off_kpart, off_kmean, off_vpart, off_svc, off_sv, off_tiles, off_q8, off_qs, total;
+  size_t off_kpart, off_kmean, off_vpart, off_svc, off_sv, off_qopart, off_ochan, off_tiles, off_q8,
+      off_qs, total;
 };
 
 WsPlan plan_workspace(int32_t nseq, int64_t total_tokens, int32_t max_len, int32_t Hq,
@@ -60,6 +74,7 @@ struct FwdGeom {
   int rot;  // Q and K rows Hadamard-rotated before quantization (logits take 1/D)
   int vch;  // V quantized per channel over each sequence's tokens (else per token)
   int qblk = 0;  // Q quantized with one scale per 32-row block (else per row)
+  int qout = 0;  // Q outlier channels detected and multiplied in fp16 (D <= 128)
   // The attention kernel quantizes Q itself from q (no Q preparation pass); only for
   // unrotated rows and D <= 128.
   int fuse_q = 0;
@@ -88,6 +103,7 @@ struct DebugOut {
   float* kmean;      // [D]
   _Float16* vhat;    // [cols][D] the prepared V rows
   float* vchan;      // [D]      V per channel
+  int32_t* ochan;    // [QO_MAX] Q outlier channels of the query head's kv group
 };
 
 // Debug dump of S32, scales, K mean and prepared V rows for sequence s, query head h.

@@ -59,18 +59,24 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(
 // Launch 1 (workgroup = tpw consecutive tiles of one sequence and kv head): the exact
 // per-channel sums of the tiles' K rows as one int64 partial, in units of 2^-24 (every
 // fp16 value is an integer multiple of 2^-24).  With VCH (V quantized per channel),
-// also the per-channel maxima of |v| over the same tokens as one fp32 partial.
-template <int D, bool VCH>
+// also the per-channel maxima of |v| over the same tokens as one fp32 partial; with QO
+// (Q outlier detection), the per-channel maxima of |q| over the same tokens and the
+// kv head's Gq query heads.
+template <int D, bool VCH, bool QO = false>
 __global__ __launch_bounds__(256) void prep_ksum_kernel(const _Float16* __restrict__ k,
                                                         const _Float16* __restrict__ v,
                                                         Act act, Seqs seqs, int Hkv, int npart,
                                                         int tpw, int64_t* __restrict__ kpart,
-                                                        float* __restrict__ vpart) {
+                                                        float* __restrict__ vpart,
+                                                        const _Float16* __restrict__ q = nullptr,
+                                                        Act aq = Act{}, int Gq = 1,
+                                                        float* __restrict__ qopart = nullptr) {
   constexpr int G = D / 8;      // lanes per row
   constexpr int RPP = 256 / G;  // rows per pass
   constexpr int NP = TK / RPP;  // rows per thread and tile
   __shared__ int64_t red[RPP * D];
   __shared__ float redv[VCH ? RPP * D : 1];
+  __shared__ float redq[QO ? RPP * D : 1];
   int b = blockIdx.x;
   const int c = b % npart;
   b /= npart;
@@ -85,11 +91,12 @@ __global__ __launch_bounds__(256) void prep_ksum_kernel(const _Float16* __restri
   const int lc = threadIdx.x % G, rsub = threadIdx.x / G;
 
   int64_t acc[8];
-  float vmx[8];
+  float vmx[8], qmx[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     acc[j] = 0;
     vmx[j] = 0.0f;
+    qmx[j] = 0.0f;
   }
   for (int tt = tile_lo; tt < tile_hi; ++tt) {
     const int t0 = tt * TK;
@@ -112,25 +119,93 @@ __global__ __launch_bounds__(256) void prep_ksum_kernel(const _Float16* __restri
         }
       }
     }
+    if constexpr (QO) {
+      for (int hq = g * Gq; hq < (g + 1) * Gq; ++hq) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          const int t = t0 + i * RPP + rsub;
+          if (t < L) {
+            const v8h qr = *reinterpret_cast<const v8h*>(q + aq.off(start, hq, t) + lc * 8);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qmx[j] = fmaxf(qmx[j], fabsf((float)qr[j]));
+          }
+        }
+      }
+    }
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     red[rsub * D + lc * 8 + j] = acc[j];
     if constexpr (VCH) redv[rsub * D + lc * 8 + j] = vmx[j];
+    if constexpr (QO) redq[rsub * D + lc * 8 + j] = qmx[j];
   }
   __syncthreads();
   if (threadIdx.x < D) {
     int64_t tot = 0;
-    float mx = 0.0f;
+    float mx = 0.0f, mq = 0.0f;
 #pragma unroll
     for (int r = 0; r < RPP; ++r) {
       tot += red[r * D + threadIdx.x];
       if constexpr (VCH) mx = fmaxf(mx, redv[r * D + threadIdx.x]);
+      if constexpr (QO) mq = fmaxf(mq, redq[r * D + threadIdx.x]);
     }
     const int64_t o = (((int64_t)s * Hkv + g) * npart + c) * D + threadIdx.x;
     kpart[o] = tot;
     if constexpr (VCH) vpart[o] = mx;
+    if constexpr (QO) qopart[o] = mq;
   }
+}
+
+// ----------------------------------------------------------------------------------
+// The Q outlier channels of one (sequence, kv head) from the launch-1 channel maxima
+// (a max is exact in any order): channel d is an outlier when its maximum exceeds
+// QO_THRESHOLD; of more than QO_MAX candidates the largest maxima are kept, ties to
+// the lower channel.  Leaves in sh.slot[d] the channel's position in the increasing
+// list of kept channels (-1 if not kept) and, if ochan_out is given, writes the list
+// padded with -1.  Every thread of the 256-thread workgroup must call it.
+template <int D>
+struct QoShared {
+  float amax[D];
+  int keep[D];
+  int slot[D];
+  int chan[QO_MAX + 1];  // the kept channels, then their count
+  float red[256];
+};
+
+template <int D>
+__device__ __forceinline__ void select_outliers(const float* __restrict__ pp, int np,
+                                                QoShared<D>& sh, int32_t* __restrict__ ochan_out) {
+  constexpr int TPC = 256 / D;  // threads per channel
+  const int d = threadIdx.x % D, r = threadIdx.x / D;
+  float mx = 0.0f;
+  for (int i = r; i < np; i += TPC) mx = fmaxf(mx, pp[(int64_t)i * D + d]);
+  sh.red[threadIdx.x] = mx;
+  __syncthreads();
+  if (r == 0) {
+    for (int k2 = 1; k2 < TPC; ++k2) mx = fmaxf(mx, sh.red[k2 * D + d]);
+    sh.amax[d] = mx;
+  }
+  __syncthreads();
+  if (r == 0) {
+    const float a = sh.amax[d];
+    int rank = 0;
+    for (int e = 0; e < D; ++e) {
+      const float b = sh.amax[e];
+      rank += (b > QO_THRESHOLD && (b > a || (b == a && e < d))) ? 1 : 0;
+    }
+    sh.keep[d] = (a > QO_THRESHOLD && rank < QO_MAX) ? 1 : 0;
+  }
+  __syncthreads();
+  if (r == 0) {
+    int pos = 0;
+    for (int e = 0; e < d; ++e) pos += sh.keep[e];
+    sh.slot[d] = sh.keep[d] ? pos : -1;
+    if (sh.keep[d]) sh.chan[pos] = d;
+    if (d == D - 1) sh.chan[QO_MAX] = pos + sh.keep[d];
+  }
+  __syncthreads();
+  if (ochan_out && threadIdx.x < QO_MAX)
+    ochan_out[threadIdx.x] = (int)threadIdx.x < sh.chan[QO_MAX] ? sh.chan[threadIdx.x] : -1;
 }
 
 // Launch 2, V part (workgroup = tpw consecutive tiles of one sequence and kv head): V
@@ -155,7 +230,8 @@ __device__ __forceinline__ void prep_v_body(const _Float16* __restrict__ v, cons
                                             int64_t Ppad, const float* __restrict__ vpart,
                                             float* __restrict__ svc_ws,
                                             float* __restrict__ sv_ws, char* __restrict__ tiles,
-                                            int c, int g, int s, PrepVShared<D>& sh) {
+                                            int tstride, int c, int g, int s,
+                                            PrepVShared<D>& sh) {
   constexpr int G = D / 8;       // lanes per row
   constexpr int RPP = 256 / G;   // rows per pass
   constexpr int NP = TK / RPP;   // rows per thread and tile
@@ -225,7 +301,7 @@ __device__ __forceinline__ void prep_v_body(const _Float16* __restrict__ v, cons
     }
     __syncthreads();
     v8h* dst = reinterpret_cast<v8h*>(tiles + ((int64_t)g * (Ppad / TK) + (pbase + t0) / TK) *
-                                                  tile_bytes(D) + TK * D);
+                                                  tstride + TK * D);
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
       // fragment f = (kg * D/32 + db) * 64 + lane', lane' = dl + 32 * hv
@@ -256,20 +332,27 @@ __device__ __forceinline__ void prep_v_body(const _Float16* __restrict__ v, cons
 // the launch-1 partials (at most MAX_PARTS of them; integer sums, so every workgroup
 // gets the same value), divided in fp64 and rounded to fp32; then the K rows of the
 // workgroup's tiles quantized from fp32(k) - mean into the K fragment layout, with
-// the K scales after the V block.
+// the K scales after the V block.  With QO the Q outlier channels are selected from
+// the launch-1 maxima, left out of the K rows (zero before the row's maximum is
+// taken) and stored as the fp16 K values themselves after the scales: per 32-key
+// block, lane n % 32 + 32 (o / 8) holds slot o % 8 of key n (the A operand of a
+// 32x32x16 fp16 MFMA over the QO_MAX slots; empty slots hold 0).
 template <int D>
 struct PrepKShared {
   int64_t red[256];
   float mean[D];
+  QoShared<D> qo;
 };
 
-template <int D, bool ROT>
+template <int D, bool ROT, bool QO>
 __device__ __forceinline__ void prep_k_body(const _Float16* __restrict__ k, const Act& act,
                                             const Seqs& seqs, int Hkv, int npart, int tpw,
                                             int64_t Ppad, const int64_t* __restrict__ kpart,
                                             float* __restrict__ kmean_ws,
-                                            char* __restrict__ tiles, int c, int g, int s,
-                                            PrepKShared<D>& sh) {
+                                            const float* __restrict__ qopart,
+                                            int32_t* __restrict__ ochan_ws,
+                                            char* __restrict__ tiles, int tstride, int c, int g,
+                                            int s, PrepKShared<D>& sh) {
   constexpr int G = D / 8;
   constexpr int RPP = 256 / G;
   constexpr int NP = TK / RPP;
@@ -302,10 +385,17 @@ __device__ __forceinline__ void prep_k_body(const _Float16* __restrict__ k, cons
   float mu[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) mu[j] = mean[lc * 8 + j];
+  bool out_ch[8] = {};
+  if constexpr (QO) {
+    select_outliers<D>(qopart + ((int64_t)s * Hkv + g) * npart * D, (nt + tpw - 1) / tpw, sh.qo,
+                       c == 0 ? ochan_ws + ((int64_t)s * Hkv + g) * QO_MAX : nullptr);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out_ch[j] = sh.qo.slot[lc * 8 + j] >= 0;
+  }
 
   for (int tt = tile_lo; tt < tile_hi; ++tt) {
     const int t0 = tt * TK;
-    char* tile = tiles + ((int64_t)g * (Ppad / TK) + (pbase + t0) / TK) * tile_bytes(D);
+    char* tile = tiles + ((int64_t)g * (Ppad / TK) + (pbase + t0) / TK) * tstride;
     float* sk_tile = reinterpret_cast<float*>(tile + 3 * TK * D);
     if (tt > tile_lo) load_rows(t0, kr);
 #pragma unroll
@@ -323,7 +413,7 @@ __device__ __forceinline__ void prep_k_body(const _Float16* __restrict__ k, cons
       } else if (real) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          x[j] = (float)kr[i][j] - mu[j];
+          x[j] = out_ch[j] ? 0.0f : (float)kr[i][j] - mu[j];
           amax = fmaxf(amax, fabsf(x[j]));
         }
       }
@@ -332,6 +422,16 @@ __device__ __forceinline__ void prep_k_body(const _Float16* __restrict__ k, cons
       const uint2 codes = real ? rq.pack8(x) : make_uint2(0u, 0u);
       *reinterpret_cast<uint2*>(tile + ktile_off(n, lc * 8, D)) = codes;
       if (lc == 0) sk_tile[n] = rq.s;
+      if constexpr (QO) {
+        // The outlier slots of this key, QO_MAX / G of them per lane.
+        _Float16* ko = reinterpret_cast<_Float16*>(tile + tile_bytes(D));
+#pragma unroll
+        for (int o = lc; o < QO_MAX; o += G) {
+          const int ch = o < sh.qo.chan[QO_MAX] ? sh.qo.chan[o] : -1;
+          const _Float16 kv = (real && ch >= 0) ? k[act.off(start, g, t) + ch] : (_Float16)0.0f;
+          ko[((n >> 5) * 64 + (n & 31) + 32 * (o >> 3)) * 8 + (o & 7)] = kv;
+        }
+      }
     }
   }
 }
@@ -350,11 +450,15 @@ static_assert(BQ % QCH == 0 && QCH % 32 == 0, "Q chunks hold whole 32-row blocks
 
 // qblk: one scale per block of 32 rows (counted from the sequence start) instead of one
 // per row: the block's largest row absolute maximum sets the scale of all its rows.
-template <int D, bool ROT>
+// QO: the outlier channels of the head's kv group (from the launch-1 maxima) are set
+// to zero before the rows are quantized.
+template <int D, bool ROT, bool QO>
 __device__ __forceinline__ void prep_q_body(const _Float16* __restrict__ q, const Act& act,
                                             const Seqs& seqs, int64_t Qpad,
                                             int8_t* __restrict__ q8, float* __restrict__ qs,
-                                            int c, int h, int s, int8_t* frag, int qblk) {
+                                            int c, int h, int s, int8_t* frag, int qblk,
+                                            const float* __restrict__ qopart, int Hkv, int Gq,
+                                            int npart, int tpw, QoShared<D>& qsh) {
   __shared__ float rowmax[QCH];
   constexpr int G = D / 8;       // lanes per row
   constexpr int RPP = 256 / G;   // rows per pass
@@ -368,6 +472,14 @@ __device__ __forceinline__ void prep_q_body(const _Float16* __restrict__ q, cons
   if (r0 >= (L + BQ - 1) / BQ * BQ) return;
   const int lc = threadIdx.x % G, rsub = threadIdx.x / G;
   const int64_t slot = (int64_t)h * Qpad + Seqs::qpstart(s, start) + r0;
+  bool out_ch[8] = {};
+  if constexpr (QO) {
+    const int nt = (L + TK - 1) / TK;
+    select_outliers<D>(qopart + ((int64_t)s * Hkv + h / Gq) * npart * D, (nt + tpw - 1) / tpw,
+                       qsh, nullptr);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out_ch[j] = qsh.slot[lc * 8 + j] >= 0;
+  }
 
   v8h xr[NP];
 #pragma unroll
@@ -382,7 +494,7 @@ __device__ __forceinline__ void prep_q_body(const _Float16* __restrict__ q, cons
     const bool real = r0 + n < L;
     amax[i] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[i][j] = real ? (float)xr[i][j] : 0.0f;
+    for (int j = 0; j < 8; ++j) x[i][j] = (real && !out_ch[j]) ? (float)xr[i][j] : 0.0f;
     if constexpr (ROT) fwht_row<G>(x[i], lc);
 #pragma unroll
     for (int j = 0; j < 8; ++j) amax[i] = fmaxf(amax[i], fabsf(x[i][j]));
@@ -426,18 +538,23 @@ template <int D>
 union PrepShared {
   PrepKShared<D> k;
   PrepVShared<D> v;
-  __attribute__((aligned(16))) int8_t qfrag[QCH * D];
+  struct {
+    __attribute__((aligned(16))) int8_t frag[QCH * D];
+    QoShared<D> qo;
+  } q;
 };
 
-template <int D, bool ROT, bool VCH>
+template <int D, bool ROT, bool VCH, bool QO>
 __global__ __launch_bounds__(256) void prep_kvq_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
     const _Float16* __restrict__ v, Act aq, Act akv, Seqs seqs, int Hq, int Hkv, int npart,
     int tpw, int64_t Ppad, int64_t Qpad, int nqc, const int64_t* __restrict__ kpart,
     const float* __restrict__ vpart, float* __restrict__ kmean_ws, float* __restrict__ svc_ws,
     float* __restrict__ sv_ws, char* __restrict__ tiles, int8_t* __restrict__ q8,
-    float* __restrict__ qs, int nk, int qblk) {
+    float* __restrict__ qs, int nk, int qblk, const float* __restrict__ qopart,
+    int32_t* __restrict__ ochan_ws) {
   __shared__ PrepShared<D> sh;
+  constexpr int tstride = tile_bytes(D, QO);
   int b = blockIdx.x;
   if (b < 2 * nk) {
     const bool is_v = b >= nk;
@@ -445,16 +562,17 @@ __global__ __launch_bounds__(256) void prep_kvq_kernel(
     const int c = b % npart;
     b /= npart;
     if (is_v)
-      prep_v_body<D, VCH>(v, akv, seqs, Hkv, npart, tpw, Ppad, vpart, svc_ws, sv_ws, tiles, c,
-                          b % Hkv, b / Hkv, sh.v);
+      prep_v_body<D, VCH>(v, akv, seqs, Hkv, npart, tpw, Ppad, vpart, svc_ws, sv_ws, tiles,
+                          tstride, c, b % Hkv, b / Hkv, sh.v);
     else
-      prep_k_body<D, ROT>(k, akv, seqs, Hkv, npart, tpw, Ppad, kpart, kmean_ws, tiles, c, b % Hkv,
-                     b / Hkv, sh.k);
+      prep_k_body<D, ROT, QO>(k, akv, seqs, Hkv, npart, tpw, Ppad, kpart, kmean_ws, qopart,
+                              ochan_ws, tiles, tstride, c, b % Hkv, b / Hkv, sh.k);
   } else {
     b -= 2 * nk;
     const int c = b % nqc;
     b /= nqc;
-    prep_q_body<D, ROT>(q, aq, seqs, Qpad, q8, qs, c, b % Hq, b / Hq, sh.qfrag, qblk);
+    prep_q_body<D, ROT, QO>(q, aq, seqs, Qpad, q8, qs, c, b % Hq, b / Hq, sh.q.frag, qblk, qopart,
+                            Hkv, Hq / Hkv, npart, tpw, sh.q.qo);
   }
 }
 
@@ -500,7 +618,7 @@ static Act act_of(const FwdGeom& g, int H) {
 // the V channel maxima), launch 2 quantizes K and prepares V; with q (PH_Q) the Q rows
 // ride in launch 2.  ROT: the K and Q rows are Hadamard-rotated before they are
 // quantized.
-template <int D, bool ROT, bool VCH>
+template <int D, bool ROT, bool VCH, bool QO>
 static hipError_t prep_d(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, bool qq,
                          hipStream_t stream) {
   char* w = static_cast<char*>(ws);
@@ -513,19 +631,41 @@ static hipError_t prep_d(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, b
   const _Float16* kp = static_cast<const _Float16*>(g.k);
   const _Float16* vp = static_cast<const _Float16*>(g.v);
   float* vpart = reinterpret_cast<float*>(w + p.off_vpart);
+  float* qopart = reinterpret_cast<float*>(w + p.off_qopart);
+  const _Float16* qp = static_cast<const _Float16*>(g.q);
   if (kv)
-    prep_ksum_kernel<D, VCH><<<dim3((unsigned)nk), 256, 0, stream>>>(
+    prep_ksum_kernel<D, VCH, QO><<<dim3((unsigned)nk), 256, 0, stream>>>(
         kp, vp, akv, sq, g.Hkv, p.npart, p.tpw, reinterpret_cast<int64_t*>(w + p.off_kpart),
-        vpart);
+        vpart, qp, aq, g.Hq / g.Hkv, qopart);
   if (2 * nk + nq > 0)
-    prep_kvq_kernel<D, ROT, VCH><<<dim3((unsigned)(2 * nk + nq)), 256, 0, stream>>>(
+    prep_kvq_kernel<D, ROT, VCH, QO><<<dim3((unsigned)(2 * nk + nq)), 256, 0, stream>>>(
         static_cast<const _Float16*>(g.q), kp, vp, aq, akv, sq, g.Hq, g.Hkv, p.npart, p.tpw,
         p.Ppad, p.Qpad, nqc, reinterpret_cast<const int64_t*>(w + p.off_kpart), vpart,
         reinterpret_cast<float*>(w + p.off_kmean), reinterpret_cast<float*>(w + p.off_svc),
         reinterpret_cast<float*>(w + p.off_sv), w + p.off_tiles,
         reinterpret_cast<int8_t*>(w + p.off_q8), reinterpret_cast<float*>(w + p.off_qs),
-        (int)nk, g.qblk);
+        (int)nk, g.qblk, qopart, reinterpret_cast<int32_t*>(w + p.off_ochan));
   return hipGetLastError();
+}
+
+// The variants of one head dim.  Q outlier detection comes without the rotation and
+// for D <= 128 only (the caller checks).
+template <int D>
+static hipError_t prep_dispatch(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, bool qq,
+                                hipStream_t stream) {
+  if (g.qout) {
+    if constexpr (D <= 128) {
+      if (g.rot) return hipErrorInvalidValue;
+      return g.vch ? prep_d<D, false, true, true>(g, p, ws, kv, qq, stream)
+                   : prep_d<D, false, false, true>(g, p, ws, kv, qq, stream);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (g.vch)
+    return g.rot ? prep_d<D, true, true, false>(g, p, ws, kv, qq, stream)
+                 : prep_d<D, false, true, false>(g, p, ws, kv, qq, stream);
+  return g.rot ? prep_d<D, true, false, false>(g, p, ws, kv, qq, stream)
+               : prep_d<D, false, false, false>(g, p, ws, kv, qq, stream);
 }
 
 hipError_t launch_prep(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, bool qq,
@@ -534,11 +674,7 @@ hipError_t launch_prep(const FwdGeom& g, const WsPlan& p, void* ws, bool kv, boo
   switch (g.D) {
 #define I8A_PREP(DD)                                                              \
   case DD:                                                                        \
-    if (g.vch)                                                                    \
-      return g.rot ? prep_d<DD, true, true>(g, p, ws, kv, qq, stream)             \
-                   : prep_d<DD, false, true>(g, p, ws, kv, qq, stream);           \
-    return g.rot ? prep_d<DD, true, false>(g, p, ws, kv, qq, stream)              \
-                 : prep_d<DD, false, false>(g, p, ws, kv, qq, stream);
+    return prep_dispatch<DD>(g, p, ws, kv, qq, stream);
     I8A_PREP(32) I8A_PREP(64) I8A_PREP(128) I8A_PREP(256)
 #undef I8A_PREP
     default: return hipErrorInvalidValue;

@@ -159,10 +159,26 @@ def test_python_binding_validates_before_the_library():
 
 
 def test_forward_ex_rejects_unknown_flags(lib):
-    st = lib.attn_int8_fwd_ex(FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 64, 64, 0.125, 1, 8, FAKE,
+    st = lib.attn_int8_fwd_ex(FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 64, 64, 0.125, 1, 16, FAKE,
                               1 << 40, None)
     assert st == INVALID
     assert b"flags" in lib.i8a_last_error()
+
+
+def test_q_outlier_flag_limits(lib):
+    # Q outlier detection does not combine with the rotation and is built for D <= 128:
+    # both rejected on the host, for the dense and the varlen entries.
+    def dense(flags, d):
+        return lib.attn_int8_fwd_ex(FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 64, d, 0.125, 1, flags,
+                                    FAKE, 1 << 40, None)
+
+    def varlen(flags, d):
+        return lib.attn_int8_varlen_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 2, 1, d,
+                                           0.125, 1, flags, FAKE, 1 << 40, None)
+    for call in (dense, varlen):
+        assert call(i8.FWD_Q_OUTLIERS | i8.FWD_HADAMARD, 64) == INVALID
+        assert b"HADAMARD" in lib.i8a_last_error()
+        assert call(i8.FWD_Q_OUTLIERS, 256) == HEADDIM
 
 
 def test_backward_head_dims_and_arguments(lib):
@@ -184,12 +200,14 @@ def test_debug_ex_rejects_bad_arguments(lib):
     # a per-token V scale output with V per channel (and the reverse), and misaligned
     # pointers are rejected on the host.
     def call(cu=None, nseq=1, L=64, T=64, flags=0, seq=0, h=0, r0=0, r=8, c0=0, c=8,
-             vscale=None, vhat=None, vchan=None):
+             vscale=None, vhat=None, vchan=None, ochan=None):
         return lib.attn_int8_debug_qk_ex(FAKE, FAKE, FAKE, cu, nseq, L, T, 4, 2, 64, flags, seq,
                                          h, r0, r, c0, c, FAKE, None, None, vscale, None, vhat,
-                                         vchan, FAKE, 1 << 40, None)
+                                         vchan, ochan, FAKE, 1 << 40, None)
     assert call(T=65) == INVALID
-    assert call(flags=8) == INVALID
+    assert call(flags=16) == INVALID
+    assert call(flags=0, ochan=FAKE) == INVALID
+    assert call(flags=i8.FWD_Q_OUTLIERS, ochan=ctypes.c_void_p((1 << 20) + 2)) == INVALID
     assert call(flags=i8.FWD_V_PER_CHANNEL, vscale=FAKE) == INVALID
     assert call(flags=0, vchan=FAKE) == INVALID
     assert call(vhat=ctypes.c_void_p((1 << 20) + 1)) == INVALID

@@ -3,8 +3,8 @@ debug dump (attn_int8_debug_qk_ex) against the CPU oracle's quantization: the in
 scores, the Q row (or per-block) scales, the K scales and K-smoothing mean, the
 prepared V rows (the exact fp16 values scale * code the P.V product consumes, compared
 by value: with the scale bit-exact, equal values are equal codes) and the V scales per
-token or per channel -- for every head dim, with and without each variant
-flag, dense and varlen (blocks and means per sequence)."""
+token or per channel, and the Q outlier channels -- for every head dim, with and without
+each variant flag, dense and varlen (blocks, means and outlier channels per sequence)."""
 
 import sys
 
@@ -20,6 +20,8 @@ pytestmark = pytest.mark.gpu
 
 FLAGS = [0, i8.FWD_V_PER_CHANNEL, i8.FWD_Q_PER_BLOCK,
          i8.FWD_HADAMARD | i8.FWD_V_PER_CHANNEL | i8.FWD_Q_PER_BLOCK]
+# Q outlier detection (head dims up to 128).
+FLAGS_OUT = [i8.FWD_Q_OUTLIERS, i8.FWD_Q_OUTLIERS | i8.FWD_Q_PER_BLOCK | i8.FWD_V_PER_CHANNEL]
 
 
 def say(*a):
@@ -38,7 +40,8 @@ def host(t):
 def zflags(q, k, v, flags):
     return oracle.quantize_qkv(q, k, v, hadamard=bool(flags & i8.FWD_HADAMARD),
                                v_per_channel=bool(flags & i8.FWD_V_PER_CHANNEL),
-                               q_per_block=bool(flags & i8.FWD_Q_PER_BLOCK))
+                               q_per_block=bool(flags & i8.FWD_Q_PER_BLOCK),
+                               q_outliers=bool(flags & i8.FWD_Q_OUTLIERS))
 
 
 def vhat_ref(z, b, g, c0, nc, per_channel):
@@ -65,11 +68,15 @@ def check_dump(r, z, b, h, G, r0, nr, c0, nc, flags, what):
         assert np.array_equal(host(r["vchan"]), z["sv"][b, g]), what
     else:
         assert np.array_equal(host(r["vscale"]), z["sv"][b, g, c0:c0 + nc]), what
+    if flags & i8.FWD_Q_OUTLIERS:
+        assert np.array_equal(host(r["ochan"]).astype(np.int64), z["ochan"][b, g]), what
 
 
-@pytest.mark.parametrize("flags", FLAGS)
+@pytest.mark.parametrize("flags", FLAGS + FLAGS_OUT)
 @pytest.mark.parametrize("D", [32, 64, 128, 256])
 def test_dense_dump_bit_exact(D, flags):
+    if D == 256 and flags & i8.FWD_Q_OUTLIERS:
+        pytest.skip("Q outlier detection is built for D <= 128")
     say(f"dense dump D={D} flags={flags}")
     w = workloads.dense(300 + D + flags, 2, 4, 2, 150, D, True, k_offset=2.5, outlier_frac=0.02)
     z = zflags(w.q, w.k, w.v, flags)
@@ -79,7 +86,7 @@ def test_dense_dump_bit_exact(D, flags):
         check_dump(r, z, b, h, 2, r0, nr, c0, nc, flags, (D, flags, b, h))
 
 
-@pytest.mark.parametrize("flags", FLAGS)
+@pytest.mark.parametrize("flags", FLAGS + FLAGS_OUT)
 @pytest.mark.parametrize("D", [64, 128])
 def test_varlen_dump_bit_exact(D, flags):
     # Sequences of 37, 0, 150 and 64 tokens: each dumped sequence against the oracle's
