@@ -2,10 +2,10 @@
 
 One step = one ``attn_int8_fwd`` call on the causal GQA workload B=1, Hq=32,
 Hkv=8, S=4096, D=128 (fp16 q/k/v ~ N(0,1), seeded): K-smoothing mean, K/V
-quantization, Q quantization and the attention itself, every kernel the call
+quantization and the attention kernel, which quantizes Q itself, every kernel the call
 launches.  Inputs, output and workspace are resident in HBM before timing starts.
-The phases are also timed alone (K/V preparation, Q preparation, attention kernel)
-through the split entry points, which enqueue the same kernels.
+The phases are also timed alone (K/V preparation, attention kernel) through the split
+entry points, which enqueue the same kernels.
 
 Prints one JSON line.  ``value`` is effective TOPS = algorithmic ops / time per
 step, with ops = 4*D*Hq*S^2/2 (two products of 2*D ops per (query, key) pair,
@@ -28,9 +28,17 @@ and scales, the query rows read, the output written) over the call time, against
 beforehand, on a sample of sequences.
 
 The ``variants`` object times the forward's variants (``attn_int8_fwd_ex`` with Q and K
-Hadamard-rotated, with V per channel, and with both) on the same workload and reports
-each one's quality (SQNR against unquantized attention) on the outlier-channel
-workload next to the plain forward's.
+Hadamard-rotated, with V per channel, with both, with Q per 32-row block and with Q
+outlier detection) on the same workload and reports each one's quality (SQNR against
+unquantized attention) on the outlier-channel workload next to the plain forward's.
+
+The ``configs`` object measures the other workloads of the benchmark set the same way
+(one forward call per step, inputs resident): the non-causal MHA head-dim sweep B4 H16
+S2048 D32/64/128/256 with outlier channels, the varlen causal prefill of 16 sequences
+(lengths drawn U[1,4096]) at Hq64 Hkv8 D128, and the long-context causal GQA B1 Hq40
+Hkv8 S32768 D128.  Each has its whole-call TOPS, the attention kernel alone against the
+int8 peak (dense ones), a parity guard on sampled rows and the CPU oracle's rate on a
+bounded sample (heads and rows stated; the long-context one from one kv group).
 
 The ``backward`` object times ``attn_bwd`` (the gradients of the attention, the
 quantization taken as the identity) on the same workload against the fp16 MFMA peak.
@@ -251,10 +259,12 @@ def bench_variants(args, i8, torch, dev, q, k, v, out, ws, ms_step):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     flags = {"hadamard": i8.FWD_HADAMARD, "v_per_channel": i8.FWD_V_PER_CHANNEL,
              "hadamard+v_per_channel": i8.FWD_HADAMARD | i8.FWD_V_PER_CHANNEL,
-             "q_per_block": i8.FWD_Q_PER_BLOCK}
+             "q_per_block": i8.FWD_Q_PER_BLOCK, "q_outliers": i8.FWD_Q_OUTLIERS,
+             "q_per_block+q_outliers": i8.FWD_Q_PER_BLOCK | i8.FWD_Q_OUTLIERS}
     kw = {"hadamard": dict(hadamard=True), "v_per_channel": dict(v_per_channel=True),
           "hadamard+v_per_channel": dict(hadamard=True, v_per_channel=True),
-          "q_per_block": dict(q_per_block=True)}
+          "q_per_block": dict(q_per_block=True), "q_outliers": dict(q_outliers=True),
+          "q_per_block+q_outliers": dict(q_per_block=True, q_outliers=True)}
     res = {"outlier_workload": "cfg3_mha_s2048_d128_outliers: B4 H16 S2048 D128 non-causal, "
                                "1 % of channels x20 in Q and K, 4 heads x 293 rows"}
     w = workloads.cfg3(128)
@@ -293,6 +303,177 @@ def bench_variants(args, i8, torch, dev, q, k, v, out, ws, ms_step):
                      "sqnr_db": sqnr(o), "parity_sample_max_abs": err}
         log(f"bench: {name} forward {res[name]['step_us']} us/step; SQNR "
             f"{res['sqnr_db_plain']} -> {res[name]['sqnr_db']} dB on the outlier workload")
+    return res
+
+
+def oracle_rate(q16, k16, v16, heads, rows, causal, budget_s: float):
+    """The CPU oracle on a bounded sample: the quantization of the given fp16 q/k/v
+    (dense ``[1, H, S, D]``, only the heads the sample needs), then the listed query heads
+    over the listed rows until the budget is spent.  Returns (algorithmic ops done,
+    seconds, heads done); a row's ops are 4 D per (query, key) pair it attends."""
+    import numpy as np
+
+    import oracle
+    S, D = q16.shape[2], q16.shape[3]
+    G = q16.shape[1] // k16.shape[1]
+    t0 = time.perf_counter()
+    z = oracle.quantize_qkv(q16, k16, v16)
+    sm = oracle.default_softmax_scale(D)
+    rows = np.asarray(rows)
+    pairs = float(np.sum(rows + 1)) if causal else float(rows.size * S)
+    ops, done = 0.0, 0
+    for h in heads:
+        g = h // G
+        oracle.attn_core(z["q8"][0, h], z["sq"][0, h], z["k8"][0, g], z["sk"][0, g],
+                         z["v8"][0, g], z["sv"][0, g], sm, causal, rows)
+        ops += 4.0 * D * pairs
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    return ops, time.perf_counter() - t0, done
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def bench_configs(args, i8, torch, dev):
+    """The benchmark set's other workloads (see the module docstring)."""
+    import numpy as np
+
+    import oracle
+    from int8_w8a8_flashattention_amd import workloads
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    warm, n = max(args.warmup // 10, 5), max(args.steps // 2, 10)
+
+    def timed(fn, warmup=warm, steps=n):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3  # us
+
+    def tops(ops, us):
+        return ops / (us * 1e-6) / 1e12
+
+    def roofline(ops, us):
+        a = tops(ops, us)
+        return {"bound": "mfma", "achieved": round(a, 2), "peak": INT8_PEAK_TOPS,
+                "unit": "TFLOP/s", "frac": round(a / INT8_PEAK_TOPS, 4), "traffic": None}
+
+    def guard(got, ref, what):
+        err = float(np.abs(got.astype(np.float64) - ref).max())
+        if not err <= 2e-3:
+            raise RuntimeError(f"{what} output differs from the oracle: max_abs={err}")
+        return err
+
+    def cpu(ops, dt, what):
+        th = blas_threads()
+        return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": int(th),
+                "kind": "oracle", "sample": f"{what}; {dt:.1f} s of numpy fp64 with BLAS on "
+                                            f"{th} threads ({cpu_model()})"}
+
+    budget = args.cpu_budget / 3
+    res = {}
+    dense_cases = [(f"mha_s2048_d{D}", workloads.cfg3(D), False) for D in (32, 64, 128, 256)]
+    for name, w, causal in dense_cases + [("causal_gqa_s32768", None, True)]:
+        if w is None:
+            log("bench: generating the S=32768 inputs")
+            w = workloads.cfg5()
+        B, Hq, S, D = w.q.shape
+        Hkv = w.k.shape[1]
+        q, k, v = (torch.from_numpy(a).to(dev) for a in (w.q, w.k, w.v))
+        out = torch.empty_like(q)
+        ws = torch.empty(i8.attn_int8_workspace_bytes(B, Hq, Hkv, S, D), dtype=torch.uint8,
+                         device=dev)
+        ops = workloads.attn_ops(Hq, D, [S] * B, causal)
+        long = S > 8192
+        us = timed(lambda: i8.attn_int8_fwd(q, k, v, causal, out=out, workspace=ws),
+                   *((3, 5) if long else (warm, n)))
+        # The attention kernel alone: over prepared K/V, the kernel that quantizes its own
+        # Q rows (D <= 128), or over prepared Q as well (D = 256).
+        i8.attn_int8_prepare_kv(k, v, Hq, workspace=ws)
+        if D <= 128:
+            ua = timed(lambda: i8.attn_int8_fwd_prepared(q, Hkv, ws, causal, out=out),
+                       *((3, 5) if long else (warm, n)))
+        else:
+            i8.attn_int8_prepare_q(q, Hkv, ws)
+            ua = timed(lambda: i8.attn_int8_attend(ws, B, Hq, Hkv, S, D, causal, out=out))
+        i8.attn_int8_fwd(q, k, v, causal, out=out, workspace=ws)
+        heads = [(0, 0), (B - 1, Hq - 1)]
+        rows = np.unique(np.linspace(0, S - 1, 24).astype(np.int64))
+        ridx = torch.from_numpy(rows).to(dev)
+        got = np.stack([out[b, h][ridx].float().cpu().numpy() for b, h in heads])
+        ref = oracle.attn_int8_fwd(w.q, w.k, w.v, causal, heads=heads, rows=rows)
+        err = guard(got, ref, name)
+        e = {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "D": D, "causal": causal,
+             "algorithmic_ops": ops, "step_us": round(us, 2), "value": round(tops(ops, us), 2),
+             "unit": "TOPS", "frac_int8_peak": round(tops(ops, us) / INT8_PEAK_TOPS, 4),
+             "attn_kernel_us": round(ua, 2), "roofline": roofline(ops, ua),
+             "parity_sample_max_abs": err}
+        if not args.no_cpu_baseline:
+            if long:  # one kv group, every 64th row of its heads
+                G = Hq // Hkv
+                rr = np.arange(0, S, 64)
+                o_, dt, hd = oracle_rate(w.q[:1, :G], w.k[:1, :1], w.v[:1, :1], range(G), rr,
+                                         causal, budget)
+                what = (f"{hd} of the {G} query heads of kv group 0 (one of {Hkv}), every 64th "
+                        f"of their {S} rows, plus that group's quantization; extrapolated: "
+                        f"the rate on the sample stands for the whole call")
+            else:
+                o_, dt, hd = oracle_rate(w.q[:1], w.k[:1], w.v[:1], range(Hq), np.arange(S),
+                                         causal, budget)
+                what = (f"{hd} of the {Hq} heads of batch 0 (all {S} rows each), plus batch "
+                        f"0's quantization")
+            e["cpu_baseline"] = cpu(o_, dt, what)
+        res[name] = e
+        log(f"bench: {name}: {us:.1f} us/call ({e['value']} TOPS), attention kernel "
+            f"{ua:.1f} us ({e['roofline']['achieved']} TOPS)")
+        del q, k, v, out, ws, w
+    # Varlen prefill: 16 sequences, lengths drawn U[1, 4096].
+    w = workloads.cfg4()
+    T, Hq, D = w.q.shape
+    Hkv = w.k.shape[1]
+    cu = w.cu_seqlens
+    lens = np.diff(cu).tolist()
+    q, k, v = (torch.from_numpy(a).to(dev) for a in (w.q, w.k, w.v))
+    cud = torch.from_numpy(cu.astype(np.int32)).to(dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(i8.attn_int8_varlen_workspace_bytes(len(lens), T, w.max_seqlen, Hq, Hkv, D),
+                     dtype=torch.uint8, device=dev)
+    ops = workloads.attn_ops(Hq, D, lens, True)
+    us = timed(lambda: i8.attn_int8_varlen_fwd(q, k, v, cud, w.max_seqlen, True, out=out,
+                                               workspace=ws))
+    s0 = int(np.argmax(lens))
+    a0, b0 = int(cu[s0]), int(cu[s0 + 1])
+    rows = np.unique(np.linspace(0, b0 - a0 - 1, 16).astype(np.int64))
+    got = out[a0:b0][torch.from_numpy(rows).to(dev)][:, [0, Hq - 1]].float().cpu().numpy()
+    qs_, ks_, vs_ = (np.ascontiguousarray(x[a0:b0].transpose(1, 0, 2))[None]
+                     for x in (w.q, w.k, w.v))
+    ref = oracle.attn_int8_fwd(qs_, ks_, vs_, True, heads=[(0, 0), (0, Hq - 1)], rows=rows)
+    err = guard(got.transpose(1, 0, 2), ref, "varlen")
+    e = {"workload": w.name, "nseq": len(lens), "lengths": lens, "total_tokens": T,
+         "Hq": Hq, "Hkv": Hkv, "D": D, "causal": True, "algorithmic_ops": ops,
+         "step_us": round(us, 2), "value": round(tops(ops, us), 2), "unit": "TOPS",
+         "frac_int8_peak": round(tops(ops, us) / INT8_PEAK_TOPS, 4),
+         "roofline": roofline(ops, us), "roofline_note": "the whole call (no split entry for "
+                                                         "varlen attention alone)",
+         "parity_sample_max_abs": err}
+    if not args.no_cpu_baseline:
+        o_, dt, hd = oracle_rate(qs_, ks_, vs_, range(Hq), np.arange(b0 - a0), True, budget)
+        e["cpu_baseline"] = cpu(o_, dt, f"{hd} of the {Hq} heads of the longest sequence "
+                                       f"({b0 - a0} tokens, all rows), plus its quantization")
+    res["varlen_16x_u4096"] = e
+    log(f"bench: varlen: {us:.1f} us/call ({e['value']} TOPS)")
     return res
 
 
@@ -384,6 +565,8 @@ def main():
     ap.add_argument("--profile-decode", type=int, default=0, metavar="N",
                     help="profiling mode: fill the decode cache once, then N decode calls")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (head-dim sweep, varlen, S=32768)")
     ap.add_argument("--profile-bwd", type=int, default=0, metavar="N",
                     help="profiling mode: N backward calls on the causal GQA workload")
     ap.add_argument("--profile-copy", type=int, default=0, metavar="MIB",
@@ -428,9 +611,8 @@ def main():
     ws = torch.empty(i8.attn_int8_workspace_bytes(B, Hq, Hkv, S, D), dtype=torch.uint8, device=dev)
     if args.profile_attn:
         i8.attn_int8_prepare_kv(k, v, Hq, workspace=ws)
-        i8.attn_int8_prepare_q(q, Hkv, ws)
         for _ in range(args.profile_attn):
-            i8.attn_int8_attend(ws, B, Hq, Hkv, S, D, True, out=out)
+            i8.attn_int8_fwd_prepared(q, Hkv, ws, True, out=out)
         torch.cuda.synchronize()
         log(f"bench: {args.profile_attn} attention launches")
         return
@@ -455,7 +637,8 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
     log(f"bench: {args.steps} steps, {ms_step * 1e3:.1f} us/step (host wall {t_wall * 1e6 / args.steps:.1f} us/step)")
 
-    # The phases alone: the attention kernel (dominant), then K/V and Q preparation.
+    # The phases alone: the attention kernel (dominant; over prepared K/V it quantizes
+    # its own Q rows, as in the step), then the K/V preparation.
     def timed(fn):
         for _ in range(args.warmup):
             fn()
@@ -468,12 +651,9 @@ def main():
         return e0.elapsed_time(e1) / args.steps
 
     i8.attn_int8_prepare_kv(k, v, Hq, workspace=ws)
-    i8.attn_int8_prepare_q(q, Hkv, ws)
-    ms_attn = timed(lambda: i8.attn_int8_attend(ws, B, Hq, Hkv, S, D, True, out=out))
+    ms_attn = timed(lambda: i8.attn_int8_fwd_prepared(q, Hkv, ws, True, out=out))
     ms_prep_kv = timed(lambda: i8.attn_int8_prepare_kv(k, v, Hq, workspace=ws))
-    ms_prep_q = timed(lambda: i8.attn_int8_prepare_q(q, Hkv, ws))
-    log(f"bench: attention kernel {ms_attn * 1e3:.1f} us, K/V preparation {ms_prep_kv * 1e3:.1f} us, "
-        f"Q preparation {ms_prep_q * 1e3:.1f} us")
+    log(f"bench: attention kernel {ms_attn * 1e3:.1f} us, K/V preparation {ms_prep_kv * 1e3:.1f} us")
 
     # Per-call times (each call between its own pair of events): median and min, as they
     # stand and with a 512 MiB buffer written before each call, which evicts the inputs
@@ -513,11 +693,9 @@ def main():
     exact = oracle.attn_exact(w.q, w.k, w.v, True, heads=heads, rows=rows)
     sqnr_db = float(10.0 * np.log10(np.sum(exact ** 2) / np.sum((got - exact) ** 2)))
 
-    # Algorithmic bytes of the preparations: fp16 K and V read once, the K/V tile blocks
-    # (int8 K, exact fp16 V, fp32 K scales) written; fp16 Q read once, int8 Q codes and
-    # fp32 row scales written.
+    # Algorithmic bytes of the K/V preparation: fp16 K and V read once, the K/V tile
+    # blocks (int8 K, exact fp16 V, fp32 K scales) written.
     prep_kv_bytes = 2 * B * Hkv * S * D * 2 + B * Hkv * S * (D + 2 * D + 4)
-    prep_q_bytes = B * Hq * S * D * 2 + B * Hq * S * (D + 4)
     value = ops / (ms_step * 1e-3) / 1e12
     achieved = ops / (ms_attn * 1e-3) / 1e12
     traffic = measured_traffic()
@@ -544,8 +722,6 @@ def main():
         "attn_kernel_us": round(ms_attn * 1e3, 2),
         "prep_kv_us": round(ms_prep_kv * 1e3, 2),
         "prep_kv_gbs": round(prep_kv_bytes / (ms_prep_kv * 1e-3) / 1e9, 1),
-        "prep_q_us": round(ms_prep_q * 1e3, 2),
-        "prep_q_gbs": round(prep_q_bytes / (ms_prep_q * 1e-3) / 1e9, 1),
         "parity_sample_max_abs": max_abs,
         "parity_sample_fp16_floor": floor,
         "sqnr_db_vs_exact": round(sqnr_db, 2),
@@ -558,8 +734,10 @@ def main():
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     res["variants"] = bench_variants(args, i8, torch, dev, q, k, v, out, ws, ms_step)
     res["backward"] = bench_backward(args, i8, torch, dev, q, k, v)
+    del q, k, v, out, ws
+    if not args.no_configs:
+        res["configs"] = bench_configs(args, i8, torch, dev)
     if not args.no_decode:
-        del q, k, v, out, ws
         res["decode"] = bench_decode(args, i8, torch, dev)
     print(json.dumps(res), flush=True)
 
