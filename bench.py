@@ -65,6 +65,8 @@ MIXED_PEAK_TOPS = 1.0 / (0.5 / INT8_PEAK_TOPS + 0.5 / FP16_PEAK_TOPS)
 WORKLOAD = dict(B=1, Hq=32, Hkv=8, S=4096, D=128, causal=True)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_cfg2_traffic.json")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b16_s8192_traffic.json")
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_cfg2_traffic.json")
+DECODE_FP16_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b16_s8192_fp16v_traffic.json")
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 
 
@@ -83,7 +85,8 @@ def measured_traffic(path=TRAFFIC_FILE):
         for src in rec["sources"]:
             with open(os.path.join(ROOT, src), "rb") as f:
                 h.update(f.read())
-        return rec["bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+        n = rec["bytes_per_launch"] if "bytes_per_launch" in rec else rec["bytes_per_call"]
+        return n if h.hexdigest() == rec["sources_sha256"] else None
     except (OSError, KeyError, ValueError):
         return None
 
@@ -236,8 +239,8 @@ def bench_decode(args, i8, torch, dev):
             "parity_sample_max_abs": err, "fill_us": round(fill_us, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic(DECODE_TRAFFIC_FILE) if vf == "int8"
-                         else None}}
+                         "traffic": measured_traffic(DECODE_TRAFFIC_FILE if vf == "int8"
+                                                     else DECODE_FP16_TRAFFIC_FILE)}}
         log(f"bench: decode {vf} V {us:.1f} us/call, {gbs:.0f} GB/s, fill {fill_us:.1f} us")
         del cache, ws
     if not args.no_cpu_baseline:
@@ -511,7 +514,8 @@ def bench_backward(args, i8, torch, dev, q, k, v):
     return {"call_us": round(us, 2), "algorithmic_flops": flops,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP16_PEAK_TOPS,
                          "unit": "TFLOP/s", "frac": round(tf / FP16_PEAK_TOPS, 4),
-                         "traffic": None},
+                         "traffic": measured_traffic(BWD_TRAFFIC_FILE),
+                         "traffic_note": "HBM bytes of one whole call (its four kernels)"},
             "note": "fp32 dq, dk, dv; the quantization taken as the identity; the "
                     "implementation computes the scores and dP three times per pair "
                     "(18 D flops per pair), the roofline counts the algorithmic 10 D"}
@@ -532,17 +536,20 @@ def profile_backward(n, i8, torch, dev):
 
 
 def profile_decode(n, i8, torch, dev):
-    """Profiling mode: fill the int8-V cache once, then n decode calls."""
+    """Profiling mode: per V format (int8, then fp16), fill the cache once, then n
+    decode calls."""
     from int8_w8a8_flashattention_amd import workloads
     w = workloads.decode_bench()
     B, Hq, D = w.q.shape
     q, k, v = (torch.from_numpy(a).to(dev) for a in (w.q, w.k, w.v))
-    cache = i8.attn_int8_kvcache_fill(k, v, "int8")
     out = torch.empty_like(q)
-    for _ in range(n):
-        i8.attn_int8_decode(q, cache, out=out)
-    torch.cuda.synchronize()
-    log(f"bench: {n} decode calls")
+    for vf in ("int8", "fp16"):
+        cache = i8.attn_int8_kvcache_fill(k, v, vf)
+        for _ in range(n):
+            i8.attn_int8_decode(q, cache, out=out)
+        torch.cuda.synchronize()
+        del cache
+    log(f"bench: {n} decode calls per V format")
 
 
 def main():
@@ -563,7 +570,8 @@ def main():
                     help="profiling mode: prepare Q, K and V once, launch only the attention "
                          "kernel N times, print nothing else")
     ap.add_argument("--profile-decode", type=int, default=0, metavar="N",
-                    help="profiling mode: fill the decode cache once, then N decode calls")
+                    help="profiling mode: per V format, fill the decode cache once, then N "
+                         "decode calls")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (head-dim sweep, varlen, S=32768)")
