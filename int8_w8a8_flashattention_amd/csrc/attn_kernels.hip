@@ -3,19 +3,19 @@
 // Each wave owns 32 query rows of one head and keeps, per lane, one query's running
 // max, sum and 32 x D output accumulator column.  Per 64-key tile:
 //   S^T = K . Q^T     v_mfma_i32_32x32x32_i8   (exact int32)
-//   t   = f32(S^T) * sk_j                      (the query scale and softmax scale are
-//   p   = exp2(t * qsc - M)                     one per-lane factor qsc)
+//   t   = f32(S^T) * c_j - M                   (c_j = sk_j * qsc: the key scale times the
+//   p   = exp2(t)                               query's scale and softmax scale)
 //   O^T += V^T . P^T  v_mfma_f32_32x32x16_f16  (P rounded to fp16, V exact in fp16)
 //   l   += sum of the same fp16 P values
 // so the normalized output is a weighted mean with identical weights in numerator
 // and denominator.  The running max M is only raised (with a rescale of O and l)
 // when a tile's max exceeds it by more than TAU in log2 units, which bounds every
-// p by 2^TAU and skips most rescales.
+// p by 2^TAU and skips most rescales.  (The one-tile kernel multiplies by sk_j and
+// by qsc inside the exponent's argument instead.)
 //
-// Q, K (int8) and the exact fp16 V come from the workspace in MFMA fragment order:
-// the Q fragments go straight to registers with coalesced 16-byte loads, and the K/V
-// tile copy into LDS is linear, so every LDS operand read is a conflict-free 16-byte
-// read.
+// K (int8) and the exact fp16 V come from the workspace in MFMA fragment order, and
+// so does Q where the kernel does not quantize it itself; the K/V tile copy into LDS
+// is linear, so every LDS operand read is a conflict-free 16-byte read.
 //
 // Two kernels: attn_pipe_kernel (head dims up to 128: 8 waves, 256 query rows per
 // workgroup, software-pipelined over two tiles) and attn_fwd_kernel (head dim 256: 4
@@ -29,6 +29,8 @@
 #include "i8a_launch.h"
 
 namespace i8a {
+
+typedef float v32f __attribute__((ext_vector_type(32)));
 
 constexpr int BM = 128;      // query rows per workgroup of the one-tile kernel
 #ifndef PIPE_TAU
@@ -420,8 +422,9 @@ __device__ __forceinline__ void vm_wait_n(int n) {
 // QO (with FQ): Q outlier channels.  The kv group's channels (ochan) are left out of
 // the int8 Q rows, and their fp16 products come from one 32x32x16 fp16 MFMA per
 // 32-key block with the tile's fp16 K values of those channels:
-//   t = f32(S^T) * sk_j + So^T / sq
-// (sq is replaced by 2^-60 where the int8 part is all zero, exactly undone by qsc).
+//   t = f32(S^T) * sk_j * qsc + So^T * qk_log2 - M
+// (qsc = sq * qk_log2, with sq replaced by 2^-60 where the int8 part is all zero: its
+// scores are 0 there).
 template <int D, bool CAUSAL, int NW, bool FQ, bool QO = false>
 __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
     const int8_t* __restrict__ q8, const float* __restrict__ qs, int64_t Qpad,
@@ -479,8 +482,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
       copy_tile_dma<D, NW, QO>(tsrc + (int64_t)i * LY::STAGE, smem + i * LY::STAGE, tid, w);
   v4i qf[NKB];
   float qsc;
-  v8h qo;            // QO: the row's values at the outlier slots 8 hh .. 8 hh + 7
-  float inv_qs = 0;  // QO: 1 / sq
+  v8h qo;  // QO: the row's values at the outlier slots 8 hh .. 8 hh + 7
   if constexpr (FQ) {
     // Lane (m, hh) holds channels 32 kb + 16 hh + j (j < 16) of row qi: its B-operand
     // fragment positions, so the codes are made in place.  The row's absolute maximum
@@ -537,7 +539,6 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
     }
     if constexpr (QO) {
       const float sq = rq.s > 0.0f ? rq.s : 0x1p-60f;
-      inv_qs = 1.0f / sq;
       qsc = sq * qk_log2;
     } else {
       qsc = fmaxf(rq.s * qk_log2, FLT_MIN);
@@ -562,36 +563,50 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
   v8h ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
+  // The tile's exponent arguments t = f32(S) * c - M (log2 units), with c = sk_j * qsc
+  // from one fp32 MFMA per tile (cscale) in the S^T register layout, M the running
+  // maximum.  With QO the outlier products add So * qk_log2.
   float mrun = -INFINITY;
-  float t[32];  // the current tile's scores t = f32(S) * sk (key j: see scores())
+  float t[32];  // the current tile's exponent arguments (key j: see key_off())
   v8h pk[4];    // its probabilities, fp16, the P^T operand of P.V per key group
+  // c_j = sk_j * qsc for the tile's 64 keys: v_mfma_f32_32x32x1_2b_f32 with lane l giving
+  // the scale of key l (block l / 32, row l % 32) and its query's qsc (column l % 32), so
+  // register 16 nb + i holds key 32 nb + 8 (i/4) + 4 hh + i%4, as the scores do.
+  auto cscale = [&](float sk_lane) -> v32f {
+    v32f z;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) z[i] = 0.0f;
+    return __builtin_amdgcn_mfma_f32_32x32x1f32(sk_lane, qsc, z, 0, 0, 0);
+  };
 
   // Register i of the S^T block nb holds key 32 nb + 8 (i/4) + 4 hh + i%4 of the tile;
   // off(i) is that key relative to the tile's first key + 4 hh.
   auto key_off = [](int i) { return 32 * (i >> 4) + 8 * ((i >> 2) & 3) + (i & 3); };
-  // M is raised (with a rescale of O and l) only where the tile's max exceeds it by
-  // more than TAU.  Only register 0 of the row-sum accumulator is read, so only it is
-  // rescaled.
-  auto raise = [&](float mc) {
-    const bool upd = mc > mrun + TAU;
+  // M is raised (with a rescale of O and l, and the arguments t shifted) only where the
+  // tile's largest argument mrel exceeds TAU.  Only register 0 of the row-sum
+  // accumulator is read, so only it is rescaled.
+  auto raise = [&](float mrel) {
+    const bool upd = mrel > TAU;
     if (__any(upd)) {
-      const float mnew = upd ? mc : mrun;
-      const float alpha = upd ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.0f;
-      mrun = mnew;
+      const float d = upd ? mrel : 0.0f;
+      const float alpha = __builtin_amdgcn_exp2f(-d);
+      mrun += d;
       lacc[0] *= alpha;
 #pragma unroll
       for (int db = 0; db < NKB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) t[i] -= d;
     }
   };
-  // p = 2^(t * qsc - mu) rounded to fp16 for the 16 keys of group kg (P^T operand).
-  auto expo = [&](int kg, float mu) {
+  // p = 2^t rounded to fp16 for the 16 keys of group kg (P^T operand).
+  auto expo = [&](int kg) {
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       v2f pp;
-      pp[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[8 * kg + e], qsc, -mu));
-      pp[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[8 * kg + e + 1], qsc, -mu));
+      pp[0] = __builtin_amdgcn_exp2f(t[8 * kg + e]);
+      pp[1] = __builtin_amdgcn_exp2f(t[8 * kg + e + 1]);
       const v2h ph = __builtin_convertvector(pp, v2h);
       pk[kg][e] = ph[0];
       pk[kg][e + 1] = ph[1];
@@ -629,34 +644,42 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
     constexpr bool masked = decltype(MASK)::value;
     constexpr int NQK = 2 * NKB;                // int8 score MFMAs
     constexpr int NSC = NQK + (QO ? 2 : 0);     // score MFMAs (QO: the outlier products)
-    constexpr int NM = NSC + 4 * (NKB + 1);     // all MFMAs of the iteration
+    // The key-scale product c = sk * qsc (not with QO: there its 32 result registers would
+    // not fit beside the outlier products', and the key scales come from LDS instead).
+    constexpr int XC = QO ? -1 : NSC;
+    constexpr int NPV = NSC + (QO ? 0 : 1);     // first row-sum / P.V slot
+    constexpr int NM = NPV + 4 * (NKB + 1);     // all MFMAs of the iteration
     constexpr int PF = 3;                       // operand prefetch distance, in MFMAs
-    constexpr int E_END = NSC + 2 * (NKB + 1);  // exponentials end before row sum 2
-    constexpr int C_BEG = NSC + 2;              // conversions start once the scores are in
+    constexpr int E_END = NPV + 2 * (NKB + 1);  // exponentials end before row sum 2
+    constexpr int C_BEG = NPV + 2;              // conversions start once c is in
     constexpr int C_END = NM - 2;               // the last two slots: the row max exchange
     constexpr int NC = C_END - C_BEG;
     const v4i* kl = reinterpret_cast<const v4i*>(nxt);
     const v4i* kol = reinterpret_cast<const v4i*>(nxt + LY::KO);
     const v4i* vl = reinterpret_cast<const v4i*>(cur + LY::KB);
     const float* skl = reinterpret_cast<const float*>(nxt + LY::KB + LY::VB);
-    // Operand of MFMA slot x (the row-sum MFMAs take none): K fragment (nb, kb) for the
-    // score products, the outlier channels' K fragment of block nb, V fragment (kg, db)
-    // for P.V.
+    // Operand of MFMA slot x (the key-scale and row-sum MFMAs take none): K fragment
+    // (nb, kb) for the score products, the outlier channels' K fragment of block nb, V
+    // fragment (kg, db) for P.V.
     auto operand = [&](int x) -> v4i {
       if (x < NQK) return kl[((x / NKB) * NKB + x % NKB) * 64 + lane];
       if (x < NSC) return kol[(x - NQK) * 64 + lane];
-      const int y = x - NSC, kg = y / (NKB + 1), db = y % (NKB + 1) - 1;
+      const int y = x - NPV, kg = y / (NKB + 1), db = y % (NKB + 1) - 1;
       return vl[(kg * NKB + db) * 64 + lane];
     };
-    auto has_operand = [&](int x) { return x < NSC || (x - NSC) % (NKB + 1) != 0; };
+    auto has_operand = [&](int x) {
+      return x < NSC || (x >= NPV && (x - NPV) % (NKB + 1) != 0);
+    };
     v16i sn[2];
     v16f so[2];
+    v32f cn;          // c = sk * qsc of the next tile
+    float skn = 0.0f;  // the next tile's key scale of key `lane`
+    v4f skv[8];       // QO: the next tile's key scales in register order
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sn[nb][i] = 0;
     v4i fr[PF + 1];
-    v4f skv[8];
     float p_even = 0.0f, cm0 = -INFINITY, cm1 = -INFINITY, mc_next = 0.0f;
 #pragma unroll
     for (int x = 0; x < PF; ++x)
@@ -670,8 +693,10 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
       } else if (x < NSC) {
         so[x - NQK] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
             __builtin_bit_cast(v8h, fr[x % (PF + 1)]), qo, v16f{}, 0, 0, 0);
+      } else if (x == XC) {
+        cn = cscale(skn);
       } else {
-        const int y = x - NSC, kg = y / (NKB + 1), db = y % (NKB + 1) - 1;
+        const int y = x - NPV, kg = y / (NKB + 1), db = y % (NKB + 1) - 1;
         if (db < 0)
           lacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ones, pk[kg], lacc, 0, 0, 0);
         else
@@ -680,14 +705,20 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
       }
       // operand PF slots ahead
       if (x + PF < NM && has_operand(x + PF)) fr[(x + PF) % (PF + 1)] = operand(x + PF);
-      // key scales: group gsk (keys of sn[gsk / 4] registers 4 (gsk % 4) ..) two slots
+      // the next tile's key scale of key `lane`, for its key-scale product; with QO the
+      // scale groups gsk (keys of registers 4 (gsk % 4) .. of block gsk / 4) two slots
       // before the conversion item 4 gsk that first needs them
+      if constexpr (!QO) {
+        if (x == (XC >= PF ? XC - PF : 0)) skn = skl[lane];
+      } else {
 #pragma unroll
-      for (int gsk = 0; gsk < 8; ++gsk) {
-        const int first = C_BEG + (4 * gsk * NC) / 32;
-        const int at = first - 2 < 0 ? 0 : first - 2;
-        if (at == x)
-          skv[gsk] = *reinterpret_cast<const v4f*>(skl + 32 * (gsk / 4) + 8 * (gsk % 4) + 4 * hh);
+        for (int gsk = 0; gsk < 8; ++gsk) {
+          const int first = C_BEG + (4 * gsk * NC) / 32;
+          const int at = first - 2 < 0 ? 0 : first - 2;
+          if (at == x)
+            skv[gsk] =
+                *reinterpret_cast<const v4f*>(skl + 32 * (gsk / 4) + 8 * (gsk % 4) + 4 * hh);
+        }
       }
       // this wave's rounds of the copy: round r at slot 2 + r (NM - 4) / R
 #pragma unroll
@@ -700,7 +731,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
           if (i < i0 || i >= i1) continue;
-          const float pi = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], qsc, -mrun));
+          const float pi = __builtin_amdgcn_exp2f(t[i]);
           if (i & 1) {
             const v2f pp = {p_even, pi};
             const v2h ph = __builtin_convertvector(pp, v2h);
@@ -718,9 +749,12 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
           if (i < i0 || i >= i1) continue;
-          const int nb = i >> 4, g4 = i >> 2, r = i & 3;
-          t[i] = (float)sn[nb][i & 15] * skv[g4][r];
-          if constexpr (QO) t[i] = __builtin_fmaf(so[nb][i & 15], inv_qs, t[i]);
+          const int nb = i >> 4;
+          if constexpr (QO)
+            t[i] = __builtin_fmaf((float)sn[nb][i & 15] * skv[i >> 2][i & 3], qsc,
+                                  __builtin_fmaf(so[nb][i & 15], qk_log2, -mrun));
+          else
+            t[i] = __builtin_fmaf((float)sn[nb][i & 15], cn[i], -mrun);
           if (masked && key_off(i) > last) t[i] = -INFINITY;
           if (i & 1) {
             if (i & 2) cm1 = smax(smax(cm1, t[i - 1]), t[i]);
@@ -730,15 +764,16 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
       }
       // the row max of the next tile and the rescale decision, under the last MFMAs
       if (x == NM - 1) {
-        mc_next = other_half_max(smax(cm0, cm1)) * qsc;
-        upd_any = __any(mc_next > mrun + TAU);
+        mc_next = other_half_max(smax(cm0, cm1));
+        upd_any = __any(mc_next > TAU);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     return mc_next;
   };
 
-  // Tile 0: its scores, converted and masked where needed, set M.
+  // Tile 0: its scores, converted and masked where needed, set M (key 0 is visible to
+  // every row, so M is finite) and make the arguments relative to it.
   {
     const v4i* kl = reinterpret_cast<const v4i*>(smem);
     const float* skl = reinterpret_cast<const float*>(smem + LY::KB + LY::VB);
@@ -760,13 +795,13 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
         so0[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, kol[nb * 64 + lane]),
                                                          qo, v16f{}, 0, 0, 0);
     }
+    const v32f c0 = cscale(skl[lane]);
     const bool msk0 = needs_mask(0);
     const int last0 = last_key - 4 * hh;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      const v4f skv = *reinterpret_cast<const v4f*>(skl + 32 * (i >> 4) + 8 * ((i >> 2) & 3) + 4 * hh);
-      t[i] = (float)sc[i >> 4][i & 15] * skv[i & 3];
-      if constexpr (QO) t[i] = __builtin_fmaf(so0[i >> 4][i & 15], inv_qs, t[i]);
+      const float base = QO ? so0[i >> 4][i & 15] * qk_log2 : 0.0f;
+      t[i] = __builtin_fmaf((float)sc[i >> 4][i & 15], c0[i], base);
       if (msk0 && key_off(i) > last0) t[i] = -INFINITY;
     }
     float m0 = smax(t[0], t[1]), m1 = smax(t[2], t[3]);
@@ -775,7 +810,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
       m0 = smax(smax(m0, t[i]), t[i + 1]);
       m1 = smax(smax(m1, t[i + 2]), t[i + 3]);
     }
-    raise(other_half_max(smax(m0, m1)) * qsc);
+    mrun = other_half_max(smax(m0, m1));
+#pragma unroll
+    for (int i = 0; i < 32; ++i) t[i] -= mrun;
   }
 
   // Tiles 0 .. nt-2: tile j's exponentials and P.V beside tile j+1's scores.  The copy
@@ -811,7 +848,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
   {
     const char* cur = smem + scur * LY::STAGE;
 #pragma unroll
-    for (int kg = 0; kg < 4; ++kg) expo(kg, mrun);
+    for (int kg = 0; kg < 4; ++kg) expo(kg);
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg) pv(cur, kg);
   }
