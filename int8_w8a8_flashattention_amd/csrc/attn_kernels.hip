@@ -170,9 +170,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 
   // One 64-key tile.  `masked`: some key of the tile lies above this wave's diagonal
   // or past the sequence end; only those tiles pay for the mask, in a uniform branch
-  // of its own.  qsc > 0 (an all-zero query row has scale 0; FLT_MIN stands in for
-  // it, its scores are 0 either way), so a masked score of -inf gives p = 0 and a
-  // fully masked tile gives a row max of -inf without special cases.
+  // of its own.  The exponent arguments t = f32(S) * c - M take c = sk * qsc from one
+  // fp32 MFMA (as in the pipelined kernel); a masked score is -inf and gives p = 0.
+  // Key 0 is visible to every row, so tile 0 sets a finite M for all of them.
   auto tile_step = [&](const char* st, int kt0, bool masked) {
     const v4i* kl = reinterpret_cast<const v4i*>(st);
     const v4i* vl = reinterpret_cast<const v4i*>(st + LY::KB);
@@ -188,16 +188,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         acc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kl[(nb * NKB + kb) * 64 + lane], qf[kb],
                                                         acc[nb], 0, 0, 0);
     }
-    // Register i of block nb holds key 32*nb + 8*(i/4) + 4*hh + i%4 of the tile.
+    // Register i of block nb holds key 32*nb + 8*(i/4) + 4*hh + i%4 of the tile, and so
+    // does register 16 nb + i of c: lane l gives key l's scale and its query's qsc to a
+    // v_mfma_f32_32x32x1_2b_f32.
+    v32f cz;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) cz[i] = 0.0f;
+    const v32f c = __builtin_amdgcn_mfma_f32_32x32x1f32(skl[lane], qsc, cz, 0, 0, 0);
+    const float mbase = mrun == -INFINITY ? 0.0f : mrun;
     float tv[32];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        const v4f skv = *reinterpret_cast<const v4f*>(skl + 32 * nb + 8 * J + 4 * hh);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) tv[16 * nb + 4 * J + r] = (float)acc[nb][4 * J + r] * skv[r];
-      }
+    for (int i = 0; i < 32; ++i) tv[i] = __builtin_fmaf((float)acc[i >> 4][i & 15], c[i], -mbase);
     if (masked) {
       // Key kt0 + 4*hh + off_i is masked when off_i exceeds one per-lane bound (the
       // last visible key, causal diagonal or sequence end, relative to kt0 + 4*hh):
@@ -218,30 +219,29 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       m0 = smax(smax(m0, tv[i]), tv[i + 1]);
       m1 = smax(smax(m1, tv[i + 2]), tv[i + 3]);
     }
-    const float mc = other_half_max(smax(m0, m1)) * qsc;
-    const bool upd = mc > mrun + TAU;
+    const float mrel = other_half_max(smax(m0, m1));
+    const bool upd = mrel > TAU || mrun == -INFINITY;
     if (__any(upd)) {
-      const float mnew = upd ? mc : mrun;
-      const float alpha = upd ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.0f;
-      mrun = mnew;
+      const float d = upd ? mrel : 0.0f;
+      const float alpha = __builtin_amdgcn_exp2f(-d);
+      mrun = mbase + d;
       lsum *= alpha;
 #pragma unroll
       for (int db = 0; db < NKB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) tv[i] -= d;
     }
-    // A row whose keys were all masked so far keeps M = -inf and takes its
-    // probabilities against 0 (all of them are 0).
-    const float muse = mrun == -INFINITY ? 0.0f : mrun;
 
-    // p = 2^(t * qsc - M), rounded to fp16: the P^T operand of the P.V product and the
-    // terms of the row sum (one v_dot2 chain).
+    // p = 2^t, rounded to fp16: the P^T operand of the P.V product and the terms of the
+    // row sum (one v_dot2 chain).
     v8h pk[4];
 #pragma unroll
     for (int i = 0; i < 32; i += 2) {
       v2f pp;
-      pp[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(tv[i], qsc, -muse));
-      pp[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(tv[i + 1], qsc, -muse));
+      pp[0] = __builtin_amdgcn_exp2f(tv[i]);
+      pp[1] = __builtin_amdgcn_exp2f(tv[i + 1]);
       const v2h ph = __builtin_convertvector(pp, v2h);
       pk[i >> 3][i & 7] = ph[0];
       pk[i >> 3][(i & 7) + 1] = ph[1];
