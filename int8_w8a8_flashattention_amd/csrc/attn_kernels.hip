@@ -118,6 +118,73 @@ __device__ __forceinline__ void decode_work(int bid, int nseq, int Hq, int Hkv, 
   }
 }
 
+// The forward's own Q quantization (the kernels' FQ path): lane (m, hh) holds channels
+// 32 kb + 16 hh + j (j < 16) of query row qi, exactly its B-operand fragment positions, so
+// the codes are made in place with the preparation's row rule (row_scale, RowQ), bit
+// for bit.  The row's absolute maximum combines the two half-rows of lanes m and
+// m + 32 (a max is exact in any order); with qblk, the wave's maximum (its 32 rows are
+// one block).  Rows past the sequence end get zero codes and scale 0.  QO: the kv
+// group's outlier channels (oc, QO_MAX entries, -1 padded) are zeroed first, and the
+// row's values at the outlier slots 8 hh .. 8 hh + 7 go to qo.  Returns the row scale
+// (QO: 2^-60 where the int8 part is all zero).
+template <int D, bool QO>
+__device__ __forceinline__ float quantize_own_q(const _Float16* __restrict__ qin, const Act& aq,
+                                                int64_t start, int h, int qi, int L, int hh,
+                                                int qblk, const int32_t* __restrict__ oc,
+                                                v4i (&qf)[D / 32], v8h& qo) {
+  constexpr int NKB = D / 32;
+  const bool real = qi < L;
+  v8h xr[NKB][2];
+  if (real) {
+    const _Float16* row = qin + aq.off(start, h, qi) + 16 * hh;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) xr[kb][e] = *reinterpret_cast<const v8h*>(row + 32 * kb + 8 * e);
+  }
+  // QO: bit 16 kb + c % 16 of omask marks outlier channel c = 32 kb + 16 hh + c % 16
+  // among this lane's channels.
+  uint64_t omask = 0;
+  if constexpr (QO) {
+#pragma unroll
+    for (int o = 0; o < QO_MAX; ++o) {
+      const int c = oc[o];
+      if (c >= 0 && ((c >> 4) & 1) == hh) omask |= 1ull << (16 * (c >> 5) + (c & 15));
+    }
+    const _Float16* row = qin + aq.off(start, h, qi);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = oc[8 * hh + j];
+      qo[j] = (real && c >= 0) ? row[c] : (_Float16)0.0f;
+    }
+  }
+  float xf[NKB][2][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool keep = !QO || ((omask >> (16 * kb + 8 * e + j)) & 1) == 0;
+        xf[kb][e][j] = (real && keep) ? (float)xr[kb][e][j] : 0.0f;
+        amax = fmaxf(amax, fabsf(xf[kb][e][j]));
+      }
+  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+  if (qblk) amax = group_max<64>(amax);
+  const RowQ rq(real ? row_scale(amax, 24) : 0.0f);
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    const uint2 lo = real ? rq.pack8(xf[kb][0]) : make_uint2(0u, 0u);
+    const uint2 hi = real ? rq.pack8(xf[kb][1]) : make_uint2(0u, 0u);
+    qf[kb] = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+  }
+  return (QO && rq.s == 0.0f) ? 0x1p-60f : rq.s;
+}
+
+// Q comes prepared (fragments q8, scales qs): with one workgroup per CU the in-kernel
+// quantization's prologue would stand unhidden before each of the CU's workgroups
+// (cfg3 at D = 256: 444 against 430 us per forward).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const int8_t* __restrict__ q8, const float* __restrict__ qs, int64_t Qpad,
@@ -484,65 +551,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
   float qsc;
   v8h qo;  // QO: the row's values at the outlier slots 8 hh .. 8 hh + 7
   if constexpr (FQ) {
-    // Lane (m, hh) holds channels 32 kb + 16 hh + j (j < 16) of row qi: its B-operand
-    // fragment positions, so the codes are made in place.  The row's absolute maximum
-    // combines the two half-rows of lanes m and m + 32 (a max is exact in any order);
-    // rows past the sequence end get zero codes and scale 0.
-    const bool real = qi < L;
-    v8h xr[NKB][2];
-    if (real) {
-      const _Float16* row = qin + aq.off(start, h, qi) + 16 * hh;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          xr[kb][e] = *reinterpret_cast<const v8h*>(row + 32 * kb + 8 * e);
-    }
-    // QO: bit 16 kb + c % 16 of omask marks outlier channel c = 32 kb + 16 hh + c % 16
-    // among this lane's channels; the row's values at the outlier slots go to qo.
-    uint64_t omask = 0;
-    if constexpr (QO) {
-      const int32_t* oc = ochan + ((int64_t)s * Hkv + g) * QO_MAX;
-#pragma unroll
-      for (int o = 0; o < QO_MAX; ++o) {
-        const int c = oc[o];
-        if (c >= 0 && ((c >> 4) & 1) == hh) omask |= 1ull << (16 * (c >> 5) + (c & 15));
-      }
-      const _Float16* row = qin + aq.off(start, h, qi);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int c = oc[8 * hh + j];
-        qo[j] = (real && c >= 0) ? row[c] : (_Float16)0.0f;
-      }
-    }
-    float xf[NKB][2][8];
-    float amax = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const bool keep = !QO || ((omask >> (16 * kb + 8 * e + j)) & 1) == 0;
-          xf[kb][e][j] = (real && keep) ? (float)xr[kb][e][j] : 0.0f;
-          amax = fmaxf(amax, fabsf(xf[kb][e][j]));
-        }
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-    // One scale per 32-row block: the wave's rows are exactly one block.
-    if (qblk) amax = group_max<64>(amax);
-    const RowQ rq(real ? row_scale(amax, 24) : 0.0f);
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const uint2 lo = real ? rq.pack8(xf[kb][0]) : make_uint2(0u, 0u);
-      const uint2 hi = real ? rq.pack8(xf[kb][1]) : make_uint2(0u, 0u);
-      qf[kb] = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-    }
-    if constexpr (QO) {
-      const float sq = rq.s > 0.0f ? rq.s : 0x1p-60f;
-      qsc = sq * qk_log2;
-    } else {
-      qsc = fmaxf(rq.s * qk_log2, FLT_MIN);
-    }
+    const float sq = quantize_own_q<D, QO>(qin, aq, start, h, qi, L, hh, qblk,
+                                           ochan + ((int64_t)s * Hkv + g) * QO_MAX, qf, qo);
+    qsc = QO ? sq * qk_log2 : fmaxf(sq * qk_log2, FLT_MIN);
   } else {
     const int64_t qslot = (int64_t)h * Qpad + Seqs::qpstart(s, start) + qw0;
 #pragma unroll
@@ -998,7 +1009,7 @@ static hipError_t attn_d(const FwdGeom& g, const WsPlan& p, const void* ws, hipS
         act_of(g, g.Hq), sq, g.Hq, g.Hkv, g.nseq, xcd_map, qk_log2, w + p.off_tiles, p.Ppad,
         reinterpret_cast<const int32_t*>(w + p.off_ochan));
   } else {
-    if (g.qout) return hipErrorInvalidValue;
+    if (g.qout || g.fuse_q) return hipErrorInvalidValue;
     attn_fwd_kernel<D, C><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
         reinterpret_cast<const int8_t*>(w + p.off_q8),
         reinterpret_cast<const float*>(w + p.off_qs), p.Qpad, static_cast<_Float16*>(g.out),

@@ -226,13 +226,20 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       --cur_qb;
     }
   };
-  // Wait for every copy but, if `one_ahead`, the last item's (at most: the count is wave
-  // 3's, the smallest).
+  // Wait for every copy but, if `one_ahead`, the last item's: its four tiles and the
+  // statistics, with this wave's own number of copy instructions per tile (at D = 32
+  // waves 2 and 3 copy nothing).
   auto wait_copies = [&](bool one_ahead) {
-    if (one_ahead)
-      vm_wait<4 * tile_dma_count<D>(3) + 1>();
-    else
+    if (!one_ahead) {
       vm_wait<0>();
+      return;
+    }
+    switch (w) {
+      case 0: vm_wait<4 * tile_dma_count<D>(0) + 1>(); break;
+      case 1: vm_wait<4 * tile_dma_count<D>(1) + 1>(); break;
+      case 2: vm_wait<4 * tile_dma_count<D>(2) + 1>(); break;
+      default: vm_wait<4 * tile_dma_count<D>(3) + 1>(); break;
+    }
   };
 
   // Block it's S^T and dP^T (keys x queries) from its Q and dO row tiles.
