@@ -10,8 +10,7 @@
 // so the normalized output is a weighted mean with identical weights in numerator
 // and denominator.  The running max M is only raised (with a rescale of O and l)
 // when a tile's max exceeds it by more than TAU in log2 units, which bounds every
-// p by 2^TAU and skips most rescales.  (The one-tile kernel multiplies by sk_j and
-// by qsc inside the exponent's argument instead.)
+// p by 2^TAU and skips most rescales.
 //
 // K (int8) and the exact fp16 V come from the workspace in MFMA fragment order, and
 // so does Q where the kernel does not quantize it itself; the K/V tile copy into LDS
