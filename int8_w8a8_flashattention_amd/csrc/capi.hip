@@ -359,7 +359,8 @@ i8a_status attn_int8_varlen_fwd_ex(const void* q, const void* k, const void* v, 
     // nothing to compute; still validate the rest for a consistent contract
     if (!head_dim_ok(D))
       return fail(I8A_ERR_UNSUPPORTED_HEAD_DIM, "head dim %d not in {32,64,128,256}", D);
-    if (Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(I8A_ERR_INVALID_ARG, "bad Hq/Hkv");
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv || Hq > kMaxGridYZ)
+      return fail(I8A_ERR_INVALID_ARG, "bad Hq/Hkv");
     return I8A_OK;
   }
   i8a_status st = check_common(q, k, v, out, Hq, Hkv, D, softmax_scale, causal, workspace);
