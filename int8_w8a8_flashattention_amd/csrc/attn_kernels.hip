@@ -417,69 +417,47 @@ __device__ __forceinline__ void lds_dma16_sbase_lanes(const char* sbase, uint32_
 }
 #pragma clang diagnostic pop
 
-// Rounds of NW * 1 KB: the last one may be partial, so waves own different numbers of
-// copy instructions per tile (dma_count).
+// A tile is copied in rounds of NW * 1 KB.  In every round but the last, wave w moves
+// the 1 KB at 1 KB * w of the round.  The last round may be partial; there each wave
+// moves R consecutive 16-byte chunks (the last wave possibly fewer, never none), so
+// every wave issues exactly ROUNDS copy instructions per tile and one constant wait
+// covers any wave's copies.
 template <int D, int NW, bool QO = false>
 struct Dma {
   static constexpr int NT = 64 * NW;  // threads
-  static constexpr int ROUNDS = (Lay<D, QO>::NCH + NT - 1) / NT;
-  static __device__ __forceinline__ int count(int w) {
-    int n = 0;
-#pragma unroll
-    for (int r = 0; r < ROUNDS; ++r) n += (r * NT + 64 * w < Lay<D, QO>::NCH) ? 1 : 0;
-    return n;
-  }
+  static constexpr int NCH = Lay<D, QO>::NCH;
+  static constexpr int ROUNDS = (NCH + NT - 1) / NT;
+  static constexpr int REM = NCH - (ROUNDS - 1) * NT;  // chunks of the last round
+  static constexpr int R = (REM + NW - 1) / NW;         // a wave's chunks in it
+  static_assert(REM > (NW - 1) * R, "every wave copies part of the last round");
 };
 
-template <int D, int NW, bool QO>
-__device__ __forceinline__ void copy_tile_dma(const char* __restrict__ src, char* stage, int tid,
-                                              int w) {
-  using LY = Lay<D, QO>;
-  using DM = Dma<D, NW, QO>;
-  const uint32_t voff = 16u * (uint32_t)tid;
-  const uint32_t lds0 = lds_addr(stage);
-#pragma unroll
-  for (int r = 0; r < DM::ROUNDS; ++r) {
-    const int c0 = r * DM::NT + w * 64;  // this wave's first chunk of the round (uniform)
-    if (r + 1 < DM::ROUNDS || c0 + 64 <= LY::NCH) {
-      lds_dma16_sbase(src + r * DM::NT * 16, voff, lds0 + (uint32_t)(r * DM::NT * 16 + w * 1024));
-    } else if (c0 < LY::NCH) {
-      if ((tid & 63) < LY::NCH - c0)
-        lds_dma16_sbase(src + r * DM::NT * 16, voff,
-                        lds0 + (uint32_t)(r * DM::NT * 16 + w * 1024));
-    }
-  }
-}
-
-// Round r of a tile copy for this wave (copy_tile_dma is all rounds at once).  Only the
-// last round can be partial; there the lanes past the tile's end are masked off, with
-// no wave-uniform branch, so an unrolled caller stays one basic block.
+// Round r of a tile copy for this wave.  In a partial last round the wave's lanes past
+// its R chunks are masked off, with no wave-uniform branch, so an unrolled caller stays
+// one basic block.  The lane's byte offset 16 * tid stays the one vector operand; the
+// scalar base is moved back by the wave's 1 KB so that lane l reads chunk cb + l.
 template <int D, int NW, bool QO>
 __device__ __forceinline__ void copy_tile_round(const char* __restrict__ src, char* stage, int tid,
                                                 int w, int r) {
-  using LY = Lay<D, QO>;
   using DM = Dma<D, NW, QO>;
-  const uint32_t lds = lds_addr(stage) + (uint32_t)(r * DM::NT * 16 + w * 1024);
-  if (r + 1 < DM::ROUNDS || (LY::NCH % DM::NT) == 0)
-    lds_dma16_sbase(src + r * DM::NT * 16, 16u * (uint32_t)tid, lds);
-  else
-    lds_dma16_sbase_lanes(src + r * DM::NT * 16, 16u * (uint32_t)tid, lds,
-                          __builtin_amdgcn_ballot_w64(r * DM::NT + tid < LY::NCH));
+  const uint32_t lds0 = lds_addr(stage);
+  if (r + 1 < DM::ROUNDS || DM::REM == DM::NT) {
+    lds_dma16_sbase(src + r * DM::NT * 16, 16u * (uint32_t)tid,
+                    lds0 + (uint32_t)(r * DM::NT * 16 + w * 1024));
+  } else {
+    const int cb = r * DM::NT + w * DM::R;  // the wave's first chunk (uniform)
+    const int n = DM::REM - w * DM::R < DM::R ? DM::REM - w * DM::R : DM::R;
+    lds_dma16_sbase_lanes(src + 16 * (cb - 64 * w), 16u * (uint32_t)tid, lds0 + 16u * (uint32_t)cb,
+                          n >= 64 ? ~0ull : (1ull << n) - 1);
+  }
 }
 
-// Wait until at most n of this wave's vector-memory loads are outstanding (n uniform).
-__device__ __forceinline__ void vm_wait_n(int n) {
-  switch (n) {
-    case 0: vm_wait<0>(); break;
-    case 1: vm_wait<1>(); break;
-    case 2: vm_wait<2>(); break;
-    case 3: vm_wait<3>(); break;
-    case 4: vm_wait<4>(); break;
-    case 5: vm_wait<5>(); break;
-    case 6: vm_wait<6>(); break;
-    case 7: vm_wait<7>(); break;
-    default: vm_wait<0>(); break;
-  }
+// All rounds of a tile copy for this wave.
+template <int D, int NW, bool QO>
+__device__ __forceinline__ void copy_tile_dma(const char* __restrict__ src, char* stage, int tid,
+                                              int w) {
+#pragma unroll
+  for (int r = 0; r < Dma<D, NW, QO>::ROUNDS; ++r) copy_tile_round<D, NW, QO>(src, stage, tid, w, r);
 }
 
 // FQ: the kernel quantizes its Q rows itself from the fp16 input qin (layout aq, the
@@ -831,7 +809,6 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
   // ones need fewer than NS stages), so the step has no branch.  A wave whose
   // remaining rows see none of tile j+1 (the causal diagonal of the rows below it)
   // masks all of its scores, and its probabilities are 0.
-  const int dma_n = DM::count(w);
   int scur = 0;  // stage of tile j
   int j = 0;
   // One iteration; the two loops below differ only in the mask of the next tile's
@@ -848,7 +825,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
     if (upd_any) raise(mc);
     // Tile j + 2 must have landed; the copy issued in this step may run on when it is
     // for a later tile.
-    vm_wait_n(NS >= 4 ? dma_n : 0);
+    vm_wait<NS >= 4 ? DM::ROUNDS : 0>();
     __syncthreads();
     scur = snxt;
   };
