@@ -482,7 +482,11 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
   constexpr int BMW = 32 * NW;          // query rows per workgroup
   constexpr int NS = NW >= 8 ? 4 : 3;   // ring stages
   static_assert(BQ % BMW == 0, "query tiles stay inside a sequence's padded Q slots");
-  __shared__ __attribute__((aligned(16))) char smem[NS * LY::STAGE];
+  // The output goes through a per-wave LDS area after the ring: EC channels of the
+  // wave's 32 rows at a time, rows padded to EPITCH bytes.
+  constexpr int EC = D < 64 ? D : 64;
+  constexpr int EPITCH = 2 * EC + 16;
+  __shared__ __attribute__((aligned(16))) char smem[NS * LY::STAGE + NW * 32 * EPITCH];
 
   int slot, s, h;
   decode_work(blockIdx.x, nseq, Hq, Hkv, xcd_map, slot, s, h);
@@ -854,18 +858,37 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
   // No copy outlives the workgroup (the last steps' copies go to stages no tile uses).
   vm_wait<0>();
 
-  if (qi < L) {
-    const float inv = 1.0f / lacc[0];
-    _Float16* orow = out + aq.off(start, h, qi);
+  // Epilogue: O / l in fp16.  Lane (m, hh) holds channels 32 db + 8 J + 4 hh .. + 3 of
+  // row m; EC channels at a time go to the wave's LDS area and come back as 16 bytes of
+  // one row per lane, EC / 8 lanes per row, so that every store writes whole rows of
+  // EC channels (128-byte lines at EC = 64) instead of 8 bytes in each of 32 rows.
+  {
+    constexpr int LPR = EC / 8;    // lanes per row of a pass
+    constexpr int RPI = 64 / LPR;  // rows per read and store
+    char* area = smem + NS * LY::STAGE + w * 32 * EPITCH;
+    const float inv = qi < L ? 1.0f / lacc[0] : 0.0f;
+    const int rr = lane / LPR, cc = lane % LPR;
 #pragma unroll
-    for (int db = 0; db < NKB; ++db)
+    for (int p = 0; p < D / EC; ++p) {
 #pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        v4h o4;
+      for (int db = 0; db < EC / 32; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o4[r] = (_Float16)(o[db][4 * J + r] * inv);
-        *reinterpret_cast<v4h*>(orow + 32 * db + 8 * J + 4 * hh) = o4;
+        for (int J = 0; J < 4; ++J) {
+          v4h o4;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o4[r] = (_Float16)(o[p * (EC / 32) + db][4 * J + r] * inv);
+          *reinterpret_cast<v4h*>(area + m * EPITCH + 2 * (32 * db + 8 * J + 4 * hh)) = o4;
+        }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const int row = RPI * i + rr;
+        const v8h v8 = *reinterpret_cast<const v8h*>(area + row * EPITCH + 16 * cc);
+        if (qw0 + row < L)
+          *reinterpret_cast<v8h*>(out + aq.off(start, h, qw0 + row) + p * EC + 8 * cc) = v8;
       }
+      __builtin_amdgcn_wave_barrier();
+    }
   }
 }
 
