@@ -117,6 +117,46 @@ __device__ __forceinline__ void decode_work(int bid, int nseq, int Hq, int Hkv, 
   }
 }
 
+// The epilogue of both kernels: a wave's 32 rows of O / l in fp16.  Lane (m, hh) holds
+// channels 32 db + 8 J + 4 hh .. + 3 of row m, so direct stores would write 8 bytes in
+// each of 32 rows per instruction.  Instead EC channels at a time go to the wave's LDS
+// area (rows padded to 2 EC + 16 bytes) and come back as 16 bytes of one row per lane,
+// EC / 8 lanes per row, so that every store writes whole rows of EC channels (128-byte
+// lines and more).  `inv` is 1 / l (0 for rows past the sequence end, which are not
+// stored).  The area holds 32 (2 EC + 16) bytes and is this wave's alone.
+template <int D, int EC>
+__device__ __forceinline__ void store_rows(const v16f (&o)[D / 32], float inv, char* area,
+                                           _Float16* __restrict__ out, const Act& aq,
+                                           int64_t start, int h, int qw0, int L, int lane) {
+  constexpr int EPITCH = 2 * EC + 16;
+  constexpr int LPR = EC / 8;    // lanes per row of a pass
+  constexpr int RPI = 64 / LPR;  // rows per read and store
+  static_assert(D % EC == 0 && EC % 32 == 0 && RPI >= 1, "whole 32-channel blocks per pass");
+  const int m = lane & 31, hh = lane >> 5;
+  const int rr = lane / LPR, cc = lane % LPR;
+#pragma unroll
+  for (int p = 0; p < D / EC; ++p) {
+#pragma unroll
+    for (int db = 0; db < EC / 32; ++db)
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        v4h o4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o4[r] = (_Float16)(o[p * (EC / 32) + db][4 * J + r] * inv);
+        *reinterpret_cast<v4h*>(area + m * EPITCH + 2 * (32 * db + 8 * J + 4 * hh)) = o4;
+      }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = RPI * i + rr;
+      const v8h v8 = *reinterpret_cast<const v8h*>(area + row * EPITCH + 16 * cc);
+      if (qw0 + row < L)
+        *reinterpret_cast<v8h*>(out + aq.off(start, h, qw0 + row) + p * EC + 8 * cc) = v8;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // The forward's own Q quantization (the kernels' FQ path): lane (m, hh) holds channels
 // 32 kb + 16 hh + j (j < 16) of query row qi, exactly its B-operand fragment positions, so
 // the codes are made in place with the preparation's row rule (row_scale, RowQ), bit
@@ -344,19 +384,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   }
 
   lsum = other_half_sum(lsum);
-  if (qi < L) {
-    const float inv = 1.0f / lsum;
-    _Float16* orow = out + aq.off(start, h, qi);
-#pragma unroll
-    for (int db = 0; db < NKB; ++db)
-#pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        v4h o4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o4[r] = (_Float16)(o[db][4 * J + r] * inv);
-        *reinterpret_cast<v4h*>(orow + 32 * db + 8 * J + 4 * hh) = o4;
-      }
-  }
+  // The ring is idle after the last barrier (the last iteration copies nothing): each
+  // wave stages its rows of O in its own part of it.
+  constexpr int EC = 128;
+  static_assert(4 * 32 * (2 * EC + 16) <= 2 * LY::STAGE, "the staging areas fit the ring");
+  store_rows<D, EC>(o, qi < L ? 1.0f / lsum : 0.0f, smem + w * 32 * (2 * EC + 16), out, aq, start,
+                    h, qw0, L, lane);
 }
 
 // ----------------------------------------------------------------------------------
@@ -482,8 +515,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
   constexpr int BMW = 32 * NW;          // query rows per workgroup
   constexpr int NS = NW >= 8 ? 4 : 3;   // ring stages
   static_assert(BQ % BMW == 0, "query tiles stay inside a sequence's padded Q slots");
-  // The output goes through a per-wave LDS area after the ring: EC channels of the
-  // wave's 32 rows at a time, rows padded to EPITCH bytes.
+  // The output goes through a per-wave LDS area after the ring (store_rows): EC channels
+  // of the wave's 32 rows at a time, rows padded to EPITCH bytes.
   constexpr int EC = D < 64 ? D : 64;
   constexpr int EPITCH = 2 * EC + 16;
   __shared__ __attribute__((aligned(16))) char smem[NS * LY::STAGE + NW * 32 * EPITCH];
@@ -858,38 +891,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
   // No copy outlives the workgroup (the last steps' copies go to stages no tile uses).
   vm_wait<0>();
 
-  // Epilogue: O / l in fp16.  Lane (m, hh) holds channels 32 db + 8 J + 4 hh .. + 3 of
-  // row m; EC channels at a time go to the wave's LDS area and come back as 16 bytes of
-  // one row per lane, EC / 8 lanes per row, so that every store writes whole rows of
-  // EC channels (128-byte lines at EC = 64) instead of 8 bytes in each of 32 rows.
-  {
-    constexpr int LPR = EC / 8;    // lanes per row of a pass
-    constexpr int RPI = 64 / LPR;  // rows per read and store
-    char* area = smem + NS * LY::STAGE + w * 32 * EPITCH;
-    const float inv = qi < L ? 1.0f / lacc[0] : 0.0f;
-    const int rr = lane / LPR, cc = lane % LPR;
-#pragma unroll
-    for (int p = 0; p < D / EC; ++p) {
-#pragma unroll
-      for (int db = 0; db < EC / 32; ++db)
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-          v4h o4;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o4[r] = (_Float16)(o[p * (EC / 32) + db][4 * J + r] * inv);
-          *reinterpret_cast<v4h*>(area + m * EPITCH + 2 * (32 * db + 8 * J + 4 * hh)) = o4;
-        }
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int i = 0; i < 32 / RPI; ++i) {
-        const int row = RPI * i + rr;
-        const v8h v8 = *reinterpret_cast<const v8h*>(area + row * EPITCH + 16 * cc);
-        if (qw0 + row < L)
-          *reinterpret_cast<v8h*>(out + aq.off(start, h, qw0 + row) + p * EC + 8 * cc) = v8;
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
+  store_rows<D, EC>(o, qi < L ? 1.0f / lacc[0] : 0.0f, smem + NS * LY::STAGE + w * 32 * EPITCH,
+                    out, aq, start, h, qw0, L, lane);
 }
 
 // ----------------------------------------------------------------------------------
