@@ -145,7 +145,7 @@ __device__ __forceinline__ v8h dequant8(uint32_t lo, uint32_t hi, v8h sv) {
 // zero in both (codes, scales, values), so a masked key multiplies finite numbers.
 template <int D>
 struct FillKShared {
-  int64_t red[256];
+  int64_t red[512];
   float mean[D];
 };
 template <int D>

@@ -207,33 +207,43 @@ __device__ __forceinline__ int64_t fp16_fixed24(_Float16 v) {
   return (u & 0x8000u) ? -mag : mag;
 }
 
-// The K-smoothing mean of one (sequence, kv head) from its np exact partial sums
-// (int64, 2^-24 units; partial i of channel d at pp[i * D + d]): the integer total,
-// divided in fp64 by L * 2^24 and rounded to fp32, into mean[D] (LDS) and, if given,
-// kmean_out[D].  Every thread of the 256-thread workgroup must call it; red holds 256
-// int64.  The sums are integers, so every workgroup that reduces them gets the same
-// mean.
+// The K-smoothing mean of one (sequence, kv head) from its np <= MAX_PARTS launch-1
+// partial sums pp[np][D] (int64, units of 2^-24): the integer total divided in fp64 by
+// L * 2^24 and rounded to fp32 (integer sums, so every workgroup that reduces them gets
+// the same mean), written to mean (shared) and, if given, kmean_out.  Every thread
+// issues all its loads of the partials at once, 16 bytes (two channels) each, so the
+// reduction costs about one memory latency rather than one per few partials.  red is
+// 512 int64 of shared memory; all 256 threads of the workgroup must call it.
 template <int D>
 __device__ __forceinline__ void reduce_kmean(const int64_t* __restrict__ pp, int np, int L,
                                              int64_t* red, float* mean,
                                              float* __restrict__ kmean_out) {
-  constexpr int TPC = 256 / D;  // threads per channel
-  const int d = threadIdx.x % D, r = threadIdx.x / D;
-  pp += d;
-  int64_t t0 = 0, t1 = 0, t2 = 0, t3 = 0;
-  int i = r;
-  for (; i + 3 * TPC < np; i += 4 * TPC) {
-    t0 += pp[(int64_t)i * D];
-    t1 += pp[(int64_t)(i + TPC) * D];
-    t2 += pp[(int64_t)(i + 2 * TPC) * D];
-    t3 += pp[(int64_t)(i + 3 * TPC) * D];
+  typedef long long v2l __attribute__((ext_vector_type(2)));
+  constexpr int NPAIR = D / 2;                       // channel pairs
+  constexpr int TPP = 256 / NPAIR;                   // threads per pair
+  constexpr int MAXK = (MAX_PARTS + TPP - 1) / TPP;  // partials per thread, at most
+  constexpr int CH = MAXK < 16 ? MAXK : 16;          // loads in flight per round
+  const int cp = threadIdx.x % NPAIR, r = threadIdx.x / NPAIR;
+  const v2l* src = reinterpret_cast<const v2l*>(pp) + cp;
+  v2l acc = {0, 0};
+#pragma unroll
+  for (int k0 = 0; k0 < MAXK; k0 += CH) {
+    v2l v[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int i = r + (k0 + k) * TPP;
+      v[k] = i < np ? src[(int64_t)i * NPAIR] : v2l{0, 0};
+    }
+#pragma unroll
+    for (int k = 0; k < CH; ++k) acc += v[k];
   }
-  for (; i < np; i += TPC) t0 += pp[(int64_t)i * D];
-  red[threadIdx.x] = (t0 + t1) + (t2 + t3);
+  red[2 * threadIdx.x] = acc.x;
+  red[2 * threadIdx.x + 1] = acc.y;
   __syncthreads();
-  if (r == 0) {
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
     int64_t tot = 0;
-    for (int k2 = 0; k2 < TPC; ++k2) tot += red[k2 * D + d];
+    for (int k = 0; k < TPP; ++k) tot += red[2 * (k * NPAIR + d / 2) + (d & 1)];
     const float mu = (float)((double)tot / ((double)L * 16777216.0));
     mean[d] = mu;
     if (kmean_out) kmean_out[d] = mu;

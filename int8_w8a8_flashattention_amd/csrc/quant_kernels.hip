@@ -339,7 +339,7 @@ __device__ __forceinline__ void prep_v_body(const _Float16* __restrict__ v, cons
 // 32x32x16 fp16 MFMA over the QO_MAX slots; empty slots hold 0).
 template <int D>
 struct PrepKShared {
-  int64_t red[256];
+  int64_t red[512];
   float mean[D];
   QoShared<D> qo;
 };
