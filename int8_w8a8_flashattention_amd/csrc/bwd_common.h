@@ -28,6 +28,49 @@ __device__ __forceinline__ v16f mfma16(v8h a, v8h b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// Bytes of a wave's LDS staging area for store_rows_f32<EC>.
+template <int EC>
+constexpr int staging_bytes() {
+  return 32 * (4 * EC + 16);
+}
+
+// A wave's 32 rows of fp32 results (32 x 32 MFMA accumulators: lane (m, hh) holds
+// channels 32 db + 8 J + 4 hh .. + 3 of row m), times mul, stored to rows row0 + r * D
+// for r < nvalid.  Direct stores would write 16 bytes in each of 32 rows per
+// instruction; instead EC channels at a time go through the wave's LDS area (rows
+// padded to 4 EC + 16 bytes) and come back as 16 bytes of one row per lane, EC / 4 lanes
+// per row, so that every store writes whole 128-byte lines or more.
+template <int D, int EC>
+__device__ __forceinline__ void store_rows_f32(const v16f (&acc)[D / 32], float mul, char* area,
+                                               float* __restrict__ row0, int nvalid, int lane) {
+  constexpr int EPITCH = 4 * EC + 16;
+  constexpr int LPR = EC / 4;    // lanes per row of a pass
+  constexpr int RPI = 64 / LPR;  // rows per read and store
+  static_assert(D % EC == 0 && EC % 32 == 0 && RPI >= 1, "whole 32-channel blocks per pass");
+  const int m = lane & 31, hh = lane >> 5;
+  const int rr = lane / LPR, cc = lane % LPR;
+#pragma unroll
+  for (int p = 0; p < D / EC; ++p) {
+#pragma unroll
+    for (int db = 0; db < EC / 32; ++db)
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        v4f x;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = acc[p * (EC / 32) + db][4 * J + r] * mul;
+        *reinterpret_cast<v4f*>(area + m * EPITCH + 4 * (32 * db + 8 * J + 4 * hh)) = x;
+      }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = RPI * i + rr;
+      const v4f x = *reinterpret_cast<const v4f*>(area + row * EPITCH + 16 * cc);
+      if (row < nvalid) *reinterpret_cast<v4f*>(row0 + (int64_t)row * D + p * EC + 4 * cc) = x;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // ----------------------------------------------------------------------------------
 // Copy of one 32-token operand tile (64 * D contiguous bytes) into LDS by the four waves
 // of a workgroup with direct-to-LDS loads: wave w's lanes move the 16-byte chunks

@@ -31,7 +31,13 @@ __global__ __launch_bounds__(64 * dq_waves<D>()) void bwd_dq_kernel(
     const _Float16* __restrict__ vr, float* __restrict__ lse2, float* __restrict__ dvec,
     float* __restrict__ dq, int B, int Hq, int Hkv, int S, int nrb, float c_log2, float scale) {
   constexpr int NKD = D / 16, NDB = D / 32, TB = 64 * D;  // TB: bytes of a 32-token tile
-  __shared__ __attribute__((aligned(16))) char smem[2 * 3 * TB];
+  // The key blocks' tiles (two stages of K rows, V rows and K columns); afterwards the
+  // waves' output staging areas.
+  constexpr int EQ = 32;  // channels per output pass
+  constexpr int SMEM = 2 * 3 * TB > dq_waves<D>() * staging_bytes<EQ>()
+                           ? 2 * 3 * TB
+                           : dq_waves<D>() * staging_bytes<EQ>();
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
   // blockIdx.x = ((group of 32 dq_waves<D>() queries, from the last) x B + batch) x Hq
   // + head: under the causal mask the heaviest groups of every head are dispatched first.
   const int h = blockIdx.x % Hq, b = (blockIdx.x / Hq) % B;
@@ -183,18 +189,10 @@ __global__ __launch_bounds__(64 * dq_waves<D>()) void bwd_dq_kernel(
     vm_wait<0>();
     __syncthreads();
   }
-  if (active && qi < S) {
-    float* orow = dq + (((int64_t)b * Hq + h) * S + qi) * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        v4f o4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o4[r] = acc[db][4 * J + r] * scale;
-        *reinterpret_cast<v4f*>(orow + 32 * db + 8 * J + 4 * hh) = o4;
-      }
-  }
+  // The loop's last barrier leaves the tile stages unused: they stage the output.
+  store_rows_f32<D, EQ>(acc, scale, smem + w * staging_bytes<EQ>(),
+                        dq + (((int64_t)b * Hq + h) * S + q0) * D, active ? min(32, S - q0) : 0,
+                        lane);
 }
 
 

@@ -136,6 +136,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   // fit the 160 KB of LDS.
   constexpr bool PIPE = D <= 128;
   constexpr int NR = PIPE ? 4 : 2, NC = PIPE ? 5 : 2, RB = 2 * TB, CB = 2 * TB + 256;
+  constexpr int EK = D < 128 ? D : 128;  // channels per output pass
+  static_assert(4 * staging_bytes<EK>() <= NR * RB + NC * CB, "the staging areas fit the rings");
   __shared__ __attribute__((aligned(16))) char smem[NR * RB + NC * CB];
   char* const rring = smem;
   char* const cring = smem + NR * RB;
@@ -455,23 +457,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     accumulate(nitem - 1, p16, ds16);
   }
 
-  if (active && kj < S) {
-    // Part 0 writes the outputs, part 1 its partial sums (added by bwd_combine_kernel).
-    float* vrow = (part == 0 ? dv : pv) + (((int64_t)b * Hkv + g) * S + kj) * D;
-    float* krow = (part == 0 ? dk : pk) + (((int64_t)b * Hkv + g) * S + kj) * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        v4f v4, k4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v4[r] = accv[db][4 * J + r];
-          k4[r] = acck[db][4 * J + r] * scale;
-        }
-        *reinterpret_cast<v4f*>(vrow + 32 * db + 8 * J + 4 * hh) = v4;
-        *reinterpret_cast<v4f*>(krow + 32 * db + 8 * J + 4 * hh) = k4;
-      }
+  // Part 0 writes the outputs, part 1 its partial sums (added by bwd_combine_kernel),
+  // through the rings, unused once every wave is past its last block.
+  __syncthreads();
+  {
+    const int64_t o0 = (((int64_t)b * Hkv + g) * S + k0) * D;
+    const int nvalid = active ? min(32, S - k0) : 0;
+    char* area = smem + w * staging_bytes<EK>();
+    store_rows_f32<D, EK>(accv, 1.0f, area, (part == 0 ? dv : pv) + o0, nvalid, lane);
+    store_rows_f32<D, EK>(acck, scale, area, (part == 0 ? dk : pk) + o0, nvalid, lane);
   }
 }
 
