@@ -16,8 +16,9 @@
 // so does Q where the kernel does not quantize it itself; the K/V tile copy into LDS
 // is linear, so every LDS operand read is a conflict-free 16-byte read.
 //
-// Two kernels: attn_pipe_kernel (head dims up to 128: 8 waves, 256 query rows per
-// workgroup, software-pipelined over two tiles) and attn_fwd_kernel (head dim 256: 4
+// Two kernels: attn_pipe_kernel (head dims up to 128: 8 waves and 256 query rows per
+// workgroup at D = 128, 4 waves and 128 rows at D <= 64, software-pipelined over two
+// tiles) and attn_fwd_kernel (head dim 256: 4
 // waves, 128 rows, one tile at a time; its accumulators and Q fragments leave no room
 // for a second tile in flight).
 #include <float.h>
@@ -393,8 +394,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 }
 
 // ----------------------------------------------------------------------------------
-// Software-pipelined forward for D <= 128: one workgroup of 8 waves (256 query rows)
-// per CU, a four-stage LDS ring, the row sum on the MFMA.
+// Software-pipelined forward for D <= 128: at D = 128 one workgroup of 8 waves (256
+// query rows) per CU with a four-stage LDS ring; at D <= 64 workgroups of 4 waves (128
+// rows), two or three per CU, with three stages.  The row sum on the MFMA.
 //
 // A 32 x 64 wave-tile needs 24 MFMAs (8 int8 for the scores, 16 fp16 for P.V) and
 // about 160 vector instructions of softmax (per score: conversion, key scale,
@@ -985,10 +987,13 @@ static Act act_of(const FwdGeom& g, int H) {
 template <int D, bool C>
 static hipError_t attn_d(const FwdGeom& g, const WsPlan& p, const void* ws, hipStream_t stream) {
   const char* w = static_cast<const char*>(ws);
-#ifndef PIPE_NW
-#define PIPE_NW 8
-#endif
-  constexpr int NW = PIPE_NW;  // waves per workgroup of the pipelined kernel
+  // Waves per workgroup of the pipelined kernel.  At D <= 64 a step has little MFMA work
+  // beside the fixed cost of its barrier and copy wait, and a wave's registers leave room
+  // for two or three workgroups of four waves per CU, which hide each other's barriers
+  // (B4 H16 S2048 non-causal: D = 32 64.8 -> 57.5 us, D = 64 76.6 -> 75.2 us against
+  // eight waves); at
+  // D = 128 eight waves in one workgroup share every tile copy and LDS stage.
+  constexpr int NW = D <= 64 ? 4 : 8;
   const int bm = D <= 128 ? 32 * NW : BM;
   const int nqt = (g.max_len + bm - 1) / bm;
   const int64_t blocks = (int64_t)nqt * g.nseq * g.Hq;
