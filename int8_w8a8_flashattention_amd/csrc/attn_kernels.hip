@@ -16,11 +16,10 @@
 // so does Q where the kernel does not quantize it itself; the K/V tile copy into LDS
 // is linear, so every LDS operand read is a conflict-free 16-byte read.
 //
-// Two kernels: attn_pipe_kernel (head dims up to 128: 8 waves and 256 query rows per
-// workgroup at D = 128, 4 waves and 128 rows at D <= 64, software-pipelined over two
-// tiles) and attn_fwd_kernel (head dim 256: 4
-// waves, 128 rows, one tile at a time; its accumulators and Q fragments leave no room
-// for a second tile in flight).
+// One kernel, attn_pipe_kernel, software-pipelined over two tiles: 8 waves and 256
+// query rows per workgroup at D = 128; 4 waves and 128 rows at D <= 64 (two or three
+// workgroups per CU) and at D = 256 (one wave per SIMD, whose 512 registers hold the
+// accumulators and both tiles' state).
 #include <float.h>
 
 #include <type_traits>
@@ -32,7 +31,6 @@ namespace i8a {
 
 typedef float v32f __attribute__((ext_vector_type(32)));
 
-constexpr int BM = 128;      // query rows per workgroup of the one-tile kernel
 #ifndef PIPE_TAU
 #define PIPE_TAU 12.0f
 #endif
@@ -222,177 +220,6 @@ __device__ __forceinline__ float quantize_own_q(const _Float16* __restrict__ qin
   return (QO && rq.s == 0.0f) ? 0x1p-60f : rq.s;
 }
 
-// Q comes prepared (fragments q8, scales qs): with one workgroup per CU the in-kernel
-// quantization's prologue would stand unhidden before each of the CU's workgroups
-// (cfg3 at D = 256: 444 against 430 us per forward).
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
-    const int8_t* __restrict__ q8, const float* __restrict__ qs, int64_t Qpad,
-    _Float16* __restrict__ out, Act aq, Seqs seqs, int Hq, int Hkv, int nseq, int xcd_map,
-    float qk_log2, const char* __restrict__ tiles, int64_t Ppad) {
-  using LY = Lay<D>;
-  constexpr int NKB = LY::NKB;
-  __shared__ __attribute__((aligned(16))) char smem[2 * LY::STAGE];
-
-  int slot, s, h;
-  decode_work(blockIdx.x, nseq, Hq, Hkv, xcd_map, slot, s, h);
-  int64_t start;
-  int L;
-  seqs.bounds(s, start, L);
-  const int nqt_s = (L + BM - 1) / BM;  // query tiles of this sequence
-  if (slot >= nqt_s) return;
-  const int qt = CAUSAL ? nqt_s - 1 - slot : slot;
-  const int g = h / (Hq / Hkv);
-  // The wave index is wave-uniform: readfirstlane lets the compiler see that, so the
-  // per-wave tile conditions below become scalar branches.
-  const int tid = threadIdx.x, lane = tid & 63, m = lane & 31, hh = lane >> 5;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t pbase = Seqs::pstart(s, start);
-  const char* tsrc = tiles + ((int64_t)g * (Ppad / TK) + pbase / TK) * LY::STAGE;
-
-  const int q0 = qt * BM;
-  const int qw0 = q0 + 32 * w;
-  const int ntile_seq = (L + TK - 1) / TK;
-  const int nt = CAUSAL ? min(ntile_seq, (min(q0 + BM, L) - 1) / TK + 1) : ntile_seq;
-
-  // Prologue: tile 0 streams into stage 0 while the wave's 32 prepared Q rows (int8
-  // fragments, one 16-byte load per lane and d block) go to registers.
-  copy_tile_async<D>(tsrc, smem, tid);
-  const int64_t qslot = (int64_t)h * Qpad + Seqs::qpstart(s, start) + qw0;
-  v4i qf[NKB];
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-    qf[kb] = reinterpret_cast<const v4i*>(q8 + qslot * D)[kb * 64 + lane];
-  const float qsc = fmaxf(qs[qslot + m] * qk_log2, FLT_MIN);
-  wait_vmem();
-  __syncthreads();
-
-  v16f o[NKB];
-#pragma unroll
-  for (int db = 0; db < NKB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
-  float mrun = -INFINITY, lsum = 0.0f;
-  const int qi = qw0 + m;
-
-  // One 64-key tile.  `masked`: some key of the tile lies above this wave's diagonal
-  // or past the sequence end; only those tiles pay for the mask, in a uniform branch
-  // of its own.  The exponent arguments t = f32(S) * c - M take c = sk * qsc from one
-  // fp32 MFMA (as in the pipelined kernel); a masked score is -inf and gives p = 0.
-  // Key 0 is visible to every row, so tile 0 sets a finite M for all of them.
-  auto tile_step = [&](const char* st, int kt0, bool masked) {
-    const v4i* kl = reinterpret_cast<const v4i*>(st);
-    const v4i* vl = reinterpret_cast<const v4i*>(st + LY::KB);
-    const float* skl = reinterpret_cast<const float*>(st + LY::KB + LY::VB);
-
-    v16i acc[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[nb][i] = 0;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        acc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kl[(nb * NKB + kb) * 64 + lane], qf[kb],
-                                                        acc[nb], 0, 0, 0);
-    }
-    // Register i of block nb holds key 32*nb + 8*(i/4) + 4*hh + i%4 of the tile, and so
-    // does register 16 nb + i of c: lane l gives key l's scale and its query's qsc to a
-    // v_mfma_f32_32x32x1_2b_f32.
-    v32f cz;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) cz[i] = 0.0f;
-    const v32f c = __builtin_amdgcn_mfma_f32_32x32x1f32(skl[lane], qsc, cz, 0, 0, 0);
-    const float mbase = mrun == -INFINITY ? 0.0f : mrun;
-    float tv[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) tv[i] = __builtin_fmaf((float)acc[i >> 4][i & 15], c[i], -mbase);
-    if (masked) {
-      // Key kt0 + 4*hh + off_i is masked when off_i exceeds one per-lane bound (the
-      // last visible key, causal diagonal or sequence end, relative to kt0 + 4*hh):
-      // one compare and one select per score.
-      const int last = (CAUSAL ? min(qi, L - 1) : L - 1) - kt0 - 4 * hh;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int off = 32 * (i >> 4) + 8 * ((i >> 2) & 3) + (i & 3);
-        if (off > last) tv[i] = -INFINITY;
-      }
-    }
-
-    // M is raised (with a rescale of O and l) only where the tile's max exceeds it by
-    // more than TAU.  The lane max runs as two chains of v_maximum3.
-    float m0 = smax(tv[0], tv[1]), m1 = smax(tv[2], tv[3]);
-#pragma unroll
-    for (int i = 4; i < 32; i += 4) {
-      m0 = smax(smax(m0, tv[i]), tv[i + 1]);
-      m1 = smax(smax(m1, tv[i + 2]), tv[i + 3]);
-    }
-    const float mrel = other_half_max(smax(m0, m1));
-    const bool upd = mrel > TAU || mrun == -INFINITY;
-    if (__any(upd)) {
-      const float d = upd ? mrel : 0.0f;
-      const float alpha = __builtin_amdgcn_exp2f(-d);
-      mrun = mbase + d;
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < NKB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) tv[i] -= d;
-    }
-
-    // p = 2^t, rounded to fp16: the P^T operand of the P.V product and the terms of the
-    // row sum (one v_dot2 chain).
-    v8h pk[4];
-#pragma unroll
-    for (int i = 0; i < 32; i += 2) {
-      v2f pp;
-      pp[0] = __builtin_amdgcn_exp2f(tv[i]);
-      pp[1] = __builtin_amdgcn_exp2f(tv[i + 1]);
-      const v2h ph = __builtin_convertvector(pp, v2h);
-      pk[i >> 3][i & 7] = ph[0];
-      pk[i >> 3][(i & 7) + 1] = ph[1];
-    }
-    const v2h ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-    for (int kg = 0; kg < 4; ++kg)
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const v2h pr = {pk[kg][e], pk[kg][e + 1]};
-        lsum = __builtin_amdgcn_fdot2(pr, ones, lsum, false);
-      }
-
-#pragma unroll
-    for (int kg = 0; kg < 4; ++kg)
-#pragma unroll
-      for (int db = 0; db < NKB; ++db) {
-        const v4i va = vl[(kg * NKB + db) * 64 + lane];
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, va), pk[kg], o[db],
-                                                        0, 0, 0);
-      }
-  };
-
-  for (int j = 0; j < nt; ++j) {
-    if (j + 1 < nt)
-      copy_tile_async<D>(tsrc + (int64_t)(j + 1) * LY::STAGE, smem + ((j + 1) & 1) * LY::STAGE,
-                         tid);
-    const int kt0 = j * TK;
-    if (!CAUSAL || kt0 <= qw0 + 31)
-      tile_step(smem + (j & 1) * LY::STAGE, kt0,
-                (CAUSAL && kt0 + TK - 1 > qw0) || kt0 + TK > L);
-    wait_vmem();
-    __syncthreads();
-  }
-
-  lsum = other_half_sum(lsum);
-  // The ring is idle after the last barrier (the last iteration copies nothing): each
-  // wave stages its rows of O in its own part of it.
-  constexpr int EC = 128;
-  static_assert(4 * 32 * (2 * EC + 16) <= 2 * LY::STAGE, "the staging areas fit the ring");
-  store_rows<D, EC>(o, qi < L ? 1.0f / lsum : 0.0f, smem + w * 32 * (2 * EC + 16), out, aq, start,
-                    h, qw0, L, lane);
-}
-
 // ----------------------------------------------------------------------------------
 // Software-pipelined forward for D <= 128: at D = 128 one workgroup of 8 waves (256
 // query rows) per CU with a four-stage LDS ring; at D <= 64 workgroups of 4 waves (128
@@ -505,7 +332,7 @@ __device__ __forceinline__ void copy_tile_dma(const char* __restrict__ src, char
 // (qsc = sq * qk_log2, with sq replaced by 2^-60 where the int8 part is all zero: its
 // scores are 0 there).
 template <int D, bool CAUSAL, int NW, bool FQ, bool QO = false>
-__global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
+__global__ __launch_bounds__(64 * NW, (NW >= 8 || D > 128) ? 1 : 2) void attn_pipe_kernel(
     const int8_t* __restrict__ q8, const float* __restrict__ qs, int64_t Qpad,
     const _Float16* __restrict__ qin, int qblk, _Float16* __restrict__ out, Act aq, Seqs seqs,
     int Hq, int Hkv, int nseq, int xcd_map, float qk_log2, const char* __restrict__ tiles,
@@ -521,7 +348,12 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
   // of the wave's 32 rows at a time, rows padded to EPITCH bytes.
   constexpr int EC = D < 64 ? D : 64;
   constexpr int EPITCH = 2 * EC + 16;
-  __shared__ __attribute__((aligned(16))) char smem[NS * LY::STAGE + NW * 32 * EPITCH];
+  // Where the ring and the staging areas would not fit the 160 KB of LDS together (D =
+  // 256), the output is staged in a ring stage that no tile uses any more.
+  constexpr bool EPI_IN_RING = NS * LY::STAGE + NW * 32 * EPITCH > 160 * 1024;
+  static_assert(!EPI_IN_RING || NW * 32 * EPITCH <= LY::STAGE, "staging fits one stage");
+  __shared__ __attribute__((aligned(16)))
+  char smem[NS * LY::STAGE + (EPI_IN_RING ? 0 : NW * 32 * EPITCH)];
 
   int slot, s, h;
   decode_work(blockIdx.x, nseq, Hq, Hkv, xcd_map, slot, s, h);
@@ -893,8 +725,16 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attn_pipe_kernel(
   // No copy outlives the workgroup (the last steps' copies go to stages no tile uses).
   vm_wait<0>();
 
-  store_rows<D, EC>(o, qi < L ? 1.0f / lacc[0] : 0.0f, smem + NS * LY::STAGE + w * 32 * EPITCH,
-                    out, aq, start, h, qw0, L, lane);
+  char* area;
+  if constexpr (EPI_IN_RING) {
+    // Every wave's copies have landed (the wait above) and, past this barrier, every
+    // wave's P.V is done, so no stage is read any more; each wave takes its part of one.
+    __syncthreads();
+    area = smem + (scur == NS - 1 ? 0 : scur + 1) * LY::STAGE + w * 32 * EPITCH;
+  } else {
+    area = smem + NS * LY::STAGE + w * 32 * EPITCH;
+  }
+  store_rows<D, EC>(o, qi < L ? 1.0f / lacc[0] : 0.0f, area, out, aq, start, h, qw0, L, lane);
 }
 
 // ----------------------------------------------------------------------------------
@@ -991,10 +831,11 @@ static hipError_t attn_d(const FwdGeom& g, const WsPlan& p, const void* ws, hipS
   // beside the fixed cost of its barrier and copy wait, and a wave's registers leave room
   // for two or three workgroups of four waves per CU, which hide each other's barriers
   // (B4 H16 S2048 non-causal: D = 32 64.8 -> 57.5 us, D = 64 76.6 -> 75.2 us against
-  // eight waves); at
-  // D = 128 eight waves in one workgroup share every tile copy and LDS stage.
-  constexpr int NW = D <= 64 ? 4 : 8;
-  const int bm = D <= 128 ? 32 * NW : BM;
+  // eight waves).  At D = 128 eight waves in one workgroup share every tile copy and LDS
+  // stage.  At D = 256 a wave needs more than half of a SIMD's registers (the 128
+  // accumulator registers of O and both tiles' state), so four waves, one per SIMD.
+  constexpr int NW = (D <= 64 || D > 128) ? 4 : 8;
+  const int bm = 32 * NW;
   const int nqt = (g.max_len + bm - 1) / bm;
   const int64_t blocks = (int64_t)nqt * g.nseq * g.Hq;
   if (blocks == 0) return hipSuccess;
@@ -1004,24 +845,23 @@ static hipError_t attn_d(const FwdGeom& g, const WsPlan& p, const void* ws, hipS
   // Rotated Q and K rows carry H H^T = D I: an extra exact factor 1/D on the logits.
   const float qk_log2 = g.softmax_scale * 1.4426950408889634f * (g.rot ? 1.0f / g.D : 1.0f);
   Seqs sq{g.cu, g.S, g.max_len, g.T};
+  using Kern = decltype(&attn_pipe_kernel<D, C, NW, false, false>);
+  Kern kern;
   if constexpr (D <= 128) {
     if (g.qout && !g.fuse_q) return hipErrorInvalidValue;
-    auto kern = g.qout     ? attn_pipe_kernel<D, C, NW, true, true>
-                : g.fuse_q ? attn_pipe_kernel<D, C, NW, true, false>
-                           : attn_pipe_kernel<D, C, NW, false, false>;
-    kern<<<dim3((unsigned)blocks), dim3(64 * NW), 0, stream>>>(
-        reinterpret_cast<const int8_t*>(w + p.off_q8),
-        reinterpret_cast<const float*>(w + p.off_qs), p.Qpad,
-        static_cast<const _Float16*>(g.q), g.qblk, static_cast<_Float16*>(g.out),
-        act_of(g, g.Hq), sq, g.Hq, g.Hkv, g.nseq, xcd_map, qk_log2, w + p.off_tiles, p.Ppad,
-        reinterpret_cast<const int32_t*>(w + p.off_ochan));
+    kern = g.qout     ? attn_pipe_kernel<D, C, NW, true, true>
+           : g.fuse_q ? attn_pipe_kernel<D, C, NW, true, false>
+                      : attn_pipe_kernel<D, C, NW, false, false>;
   } else {
+    // D = 256: Q comes prepared (the in-kernel quantization, FQ, is for D <= 128).
     if (g.qout || g.fuse_q) return hipErrorInvalidValue;
-    attn_fwd_kernel<D, C><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-        reinterpret_cast<const int8_t*>(w + p.off_q8),
-        reinterpret_cast<const float*>(w + p.off_qs), p.Qpad, static_cast<_Float16*>(g.out),
-        act_of(g, g.Hq), sq, g.Hq, g.Hkv, g.nseq, xcd_map, qk_log2, w + p.off_tiles, p.Ppad);
+    kern = attn_pipe_kernel<D, C, NW, false, false>;
   }
+  kern<<<dim3((unsigned)blocks), dim3(64 * NW), 0, stream>>>(
+      reinterpret_cast<const int8_t*>(w + p.off_q8), reinterpret_cast<const float*>(w + p.off_qs),
+      p.Qpad, static_cast<const _Float16*>(g.q), g.qblk, static_cast<_Float16*>(g.out),
+      act_of(g, g.Hq), sq, g.Hq, g.Hkv, g.nseq, xcd_map, qk_log2, w + p.off_tiles, p.Ppad,
+      reinterpret_cast<const int32_t*>(w + p.off_ochan));
   return hipGetLastError();
 }
 
