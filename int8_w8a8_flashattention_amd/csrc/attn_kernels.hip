@@ -853,9 +853,8 @@ static hipError_t attn_d(const FwdGeom& g, const WsPlan& p, const void* ws, hipS
            : g.fuse_q ? attn_pipe_kernel<D, C, NW, true, false>
                       : attn_pipe_kernel<D, C, NW, false, false>;
   } else {
-    // D = 256: Q comes prepared (the in-kernel quantization, FQ, is for D <= 128).
-    if (g.qout || g.fuse_q) return hipErrorInvalidValue;
-    kern = attn_pipe_kernel<D, C, NW, false, false>;
+    if (g.qout) return hipErrorInvalidValue;
+    kern = g.fuse_q ? attn_pipe_kernel<D, C, NW, true, false> : attn_pipe_kernel<D, C, NW, false, false>;
   }
   kern<<<dim3((unsigned)blocks), dim3(64 * NW), 0, stream>>>(
       reinterpret_cast<const int8_t*>(w + p.off_q8), reinterpret_cast<const float*>(w + p.off_qs),

@@ -1,4 +1,4 @@
-"""GPU: the forward's attention kernel quantizes Q itself (for unrotated rows, D <= 128).
+"""GPU: the forward's attention kernel quantizes Q itself (for unrotated rows, every head dim).
 
 Its codes and scales follow the same row rule as the Q preparation pass, so the output
 must equal, bit for bit, that of the staged path: K/V and Q prepared into a workspace
@@ -46,7 +46,7 @@ def staged(q, k, v, causal, flags):
 @pytest.mark.parametrize("flags", [0, i8.FWD_Q_PER_BLOCK, i8.FWD_V_PER_CHANNEL,
                                    i8.FWD_V_PER_CHANNEL | i8.FWD_Q_PER_BLOCK])
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
 def test_fused_q_equals_prepared_q(D, causal, flags):
     say(f"fused Q == prepared Q: D={D} causal={causal} flags={flags}")
     w = workloads.dense(70 + D, 2, 4, 2, 700, D, causal, k_offset=1.0)
