@@ -236,10 +236,10 @@ __device__ __forceinline__ float quantize_own_q(const _Float16* __restrict__ qin
 // the exponentials of tile j, the conversion (and mask) of tile j+1's scores, its
 // row max and the rescale decision (pipe_step).  M is raised after the slots if a row
 // needs it (rare: the rescale of O and l waits for tile j's P.V).  The row sum l is
-// a fifth fp16 MFMA per 16 keys with an all-ones A operand: every row of its 32 x 32
-// result is the sum of the same fp16 P values the P.V product consumes (register 0 is
-// read at the end), which keeps the vector unit free of the sum; dot-product
-// instructions stall behind a running MFMA.
+// one more fp16 MFMA per 16 keys, a 16x16x32 one (half the matrix-unit cycles of a
+// P.V product) whose 0/1 A operand sums the same fp16 P values the P.V product
+// consumes (register 0 is read at the end), which keeps the vector unit free of the
+// sum; dot-product instructions stall behind a running MFMA.
 //
 // The ring holds tiles j (V for P.V), j+1 (K and scales), j+2 (landed) and j+3 (in
 // flight): every wave copies its share of tile j+3 into the stage tile j-1 left, one
@@ -412,16 +412,26 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || D > 128) ? 1 : 2) void attn_pi
   vm_wait<0>();
   __syncthreads();
 
-  v16f o[NKB], lacc;
+  v16f o[NKB];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    lacc[i] = 0.0f;
+  for (int i = 0; i < 16; ++i)
 #pragma unroll
     for (int db = 0; db < NKB; ++db) o[db][i] = 0.0f;
-  }
-  v8h ones;
+  // The row sum l: one 16x16x32 fp16 MFMA per key group kg, with pk[kg] as its B
+  // operand.  Read that way, lane b's 8 values are k-slice b / 16 of column b % 16, and
+  // they belong to query b % 32 (keys 8 (b / 32) ..): k-slices 0 and 2 hold columns
+  // 0..15's own queries, slices 1 and 3 the queries 16 higher.  The A operand `sel` is 1
+  // where row i's k-slice matches (i / 4) % 2, else 0, so result row i sums the 16 keys of
+  // query n + 16 ((i / 4) % 2) in column n; a lane l holds rows 4 (l / 16) .. + 3 of
+  // column l % 16, so all four of its registers are the sum of its own query l % 32.
+  // The products 1 * p and 0 * p are exact and the sum is fp32, as in P.V.
+  v4f lacc = {0.0f, 0.0f, 0.0f, 0.0f};
+  v8h sel;
+  {
+    const _Float16 one = (((lane >> 4) ^ (lane >> 2)) & 1) ? (_Float16)0.0f : (_Float16)1.0f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
+    for (int e = 0; e < 8; ++e) sel[e] = one;
+  }
   // The tile's exponent arguments t = f32(S) * c - M (log2 units), with c = sk_j * qsc
   // from one fp32 MFMA per tile (cscale) in the S^T register layout, M the running
   // maximum.  With QO the outlier products add So * qk_log2.
@@ -474,7 +484,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || D > 128) ? 1 : 2) void attn_pi
   // Row sum and P.V of key group kg.
   auto pv = [&](const char* st, int kg) {
     const v4i* vl = reinterpret_cast<const v4i*>(st + LY::KB);
-    lacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ones, pk[kg], lacc, 0, 0, 0);
+    lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(sel, pk[kg], lacc, 0, 0, 0);
 #pragma unroll
     for (int db = 0; db < NKB; ++db) {
       const v4i va = vl[(kg * NKB + db) * 64 + lane];
@@ -557,7 +567,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || D > 128) ? 1 : 2) void attn_pi
       } else {
         const int y = x - NPV, kg = y / (NKB + 1), db = y % (NKB + 1) - 1;
         if (db < 0)
-          lacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ones, pk[kg], lacc, 0, 0, 0);
+          lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(sel, pk[kg], lacc, 0, 0, 0);
         else
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
               __builtin_bit_cast(v8h, fr[x % (PF + 1)]), pk[kg], o[db], 0, 0, 0);

@@ -33,7 +33,7 @@ namespace i8a {
 
 namespace {
 
-constexpr float DTAU = 8.0f;  // lazy-rescale threshold, log2 units (as in the forward)
+constexpr float DTAU = 8.0f;  // lazy-rescale threshold, log2 units (the forward uses 12)
 
 // Launch shape, per V format: up to max_stages LDS stages per wave (max_stages - 1
 // tiles in flight while one is computed) and up to max_waves waves per workgroup,
