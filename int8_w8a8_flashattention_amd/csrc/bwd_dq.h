@@ -6,6 +6,8 @@
 
 #include <float.h>
 
+#include <type_traits>
+
 #include "bwd_common.h"
 #include "i8a_launch.h"
 
@@ -22,8 +24,17 @@ constexpr int dq_waves() {
 // ----------------------------------------------------------------------------------
 // Launch 2: dQ.  Workgroup = dq_waves<D>() waves of 32 queries of one (batch, query
 // head); wave w owns queries q0 = qblk0 + 32 w .. +31, lane l query q0 + l % 32.  The key
-// blocks' operand tiles (K and V in row order, K in column order) stream through a
-// two-stage LDS ring shared by the workgroup's waves, one block ahead.
+// blocks' operand tiles (K and V in row order, K in column order) stream through an LDS
+// ring shared by the workgroup's waves.
+//   Two waves per SIMD (D <= 128): each block's products, then its vector arithmetic;
+//   the two waves of a SIMD overlap one's products with the other's arithmetic (two
+//   stages, the next block landing).
+//   One wave per SIMD (D = 256, PIPE): both sweeps are software-pipelined over two key
+//   blocks.  The step of block kb runs the score products (S^T and dP^T) of block kb + 1,
+//   one per slot, beside block kb's vector arithmetic (and, in sweep 2, block kb's dQ
+//   products), while block kb + 2 lands in a third stage.  With two waves per SIMD this
+//   schedule measured slower: a wave that mixes products and arithmetic overlaps less
+//   with its neighbour than two waves that alternate them.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * dq_waves<D>()) void bwd_dq_kernel(
     const _Float16* __restrict__ qr, const _Float16* __restrict__ dor,
@@ -31,11 +42,13 @@ __global__ __launch_bounds__(64 * dq_waves<D>()) void bwd_dq_kernel(
     const _Float16* __restrict__ vr, float* __restrict__ lse2, float* __restrict__ dvec,
     float* __restrict__ dq, int B, int Hq, int Hkv, int S, int nrb, float c_log2, float scale) {
   constexpr int NKD = D / 16, NDB = D / 32, TB = 64 * D;  // TB: bytes of a 32-token tile
-  // The key blocks' tiles (two stages of K rows, V rows and K columns); afterwards the
-  // waves' output staging areas.
+  // Stages of a key block's tiles (K rows, V rows, K columns); afterwards the waves'
+  // output staging areas.
+  constexpr bool PIPE = dq_waves<D>() < 8;
+  constexpr int NST = PIPE ? 3 : 2, STG = 3 * TB;
   constexpr int EQ = 32;  // channels per output pass
-  constexpr int SMEM = 2 * 3 * TB > dq_waves<D>() * staging_bytes<EQ>()
-                           ? 2 * 3 * TB
+  constexpr int SMEM = NST * STG > dq_waves<D>() * staging_bytes<EQ>()
+                           ? NST * STG
                            : dq_waves<D>() * staging_bytes<EQ>();
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   // blockIdx.x = ((group of 32 dq_waves<D>() queries, from the last) x B + batch) x Hq
@@ -80,23 +93,13 @@ __global__ __launch_bounds__(64 * dq_waves<D>()) void bwd_dq_kernel(
   for (int kd = 0; kd < NKD; ++kd) asm volatile("" : : "v"(qf[kd]), "v"(df[kd]));
 
   const TileCopy<D, 64 * dq_waves<D>()> copy(tid);
+  // Copy of key block kb into stage st.
   auto issue = [&](int kb, int st, bool with_kc) {
-    copy(krb + (int64_t)kb * TB, smem + (st * 3 + 0) * TB);
-    copy(vrb + (int64_t)kb * TB, smem + (st * 3 + 1) * TB);
-    if (with_kc) copy(kcb + (int64_t)kb * TB, smem + (st * 3 + 2) * TB);
+    copy(krb + (int64_t)kb * TB, smem + st * STG);
+    copy(vrb + (int64_t)kb * TB, smem + st * STG + TB);
+    if (with_kc) copy(kcb + (int64_t)kb * TB, smem + st * STG + 2 * TB);
   };
-  // S^T (keys x queries) and dP^T of key block kb from LDS stage st.
-  auto scores = [&](int st, v16f& sc, v16f& dp) {
-    const v8h* ka = reinterpret_cast<const v8h*>(smem + (st * 3 + 0) * TB);
-    const v8h* va = reinterpret_cast<const v8h*>(smem + (st * 3 + 1) * TB);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.0f;
-#pragma unroll
-    for (int kd = 0; kd < NKD; ++kd) {
-      sc = mfma16(ka[kd * 64 + lane], qf[kd], sc);
-      dp = mfma16(va[kd * 64 + lane], df[kd], dp);
-    }
-  };
+  auto next_stage = [&](int st) { return st == NST - 1 ? 0 : st + 1; };
   // Masked scores to -inf.  Only a block that reaches past this wave's first query
   // (causal) or past the sequence holds masked pairs, so the others skip the compares
   // (a wave-uniform branch).  The scale c_log2 > 0 is applied later, inside the
@@ -113,37 +116,139 @@ __global__ __launch_bounds__(64 * dq_waves<D>()) void bwd_dq_kernel(
       }
     }
   };
-
-  // Sweep 1: running max, sum and sum of p * dP (log2 units).
-  float mr = -INFINITY, l = 0.0f, a = 0.0f;
-  issue(0, 0, false);
-  vm_wait<0>();
-  __syncthreads();
-  for (int kb = 0; kb < nkb_wg; ++kb) {
-    if (kb + 1 < nkb_wg) issue(kb + 1, (kb + 1) & 1, false);
-    if (active && kb < nkb) {
-      v16f sc, dp;
-      scores(kb & 1, sc, dp);
-      mask(kb, sc);
-      float mt = sc[0];
+  // S^T (keys x queries) and dP^T of the block in stage st, all at once.
+  auto scores = [&](const char* st, v16f& sc, v16f& dp) {
+    const v8h* ka = reinterpret_cast<const v8h*>(st);
+    const v8h* va = reinterpret_cast<const v8h*>(st + TB);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mt = bmax(mt, sc[i]);
-      // Every block of this wave holds a visible key for each of its rows, so mn is
-      // finite from the first block on.
-      const float mn = bmax(mr, half_max(mt) * c_log2);
-      const float al = mr == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr - mn);
-      l *= al;
-      a *= al;
+    for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c_log2, -mn));
-        l += p;
-        a = __builtin_fmaf(p, dp[i], a);
-      }
-      mr = mn;
+    for (int kd = 0; kd < NKD; ++kd) {
+      sc = mfma16(ka[kd * 64 + lane], qf[kd], sc);
+      dp = mfma16(va[kd * 64 + lane], df[kd], dp);
     }
+  };
+
+  // One step as a fixed schedule of slots, one product each, fenced so the compiler
+  // keeps the order: slots 0 .. NSD-1 the score products of the next block (S^T and dP^T
+  // alternating over the channel slices), in sweep 2 then the NQ dQ products of the
+  // current block; every product's operand is read from LDS PF slots ahead.  work(x) is
+  // the slot's share of the current block's vector arithmetic.
+  constexpr int NSD = 2 * NKD, NQ = 2 * NDB, PF = 2;
+  auto step = [&](int stn, int stc, v16f& sc, v16f& dp, v16f (&acc)[NDB], const v8h (&ds)[2],
+                  auto SWEEP2, auto work) {
+    constexpr bool two = decltype(SWEEP2)::value;
+    constexpr int NM = NSD + (two ? NQ : 0);
+    const v8h* ka = reinterpret_cast<const v8h*>(smem + stn * STG);
+    const v8h* va = reinterpret_cast<const v8h*>(smem + stn * STG + TB);
+    const v8h* kca = reinterpret_cast<const v8h*>(smem + stc * STG + 2 * TB);
+    auto operand = [&](int x) -> v8h {
+      if (x < NSD) return ((x & 1) ? va : ka)[(x >> 1) * 64 + lane];
+      return kca[(x - NSD) * 64 + lane];  // (gg NDB + db) = x - NSD
+    };
+    v8h fr[PF + 1];
+#pragma unroll
+    for (int x = 0; x < PF; ++x) fr[x] = operand(x);
+    v16f sn, dn;
+#pragma clang loop unroll(full)
+    for (int x = 0; x < NM; ++x) {
+      const v8h op = fr[x % (PF + 1)];
+      if (x + PF < NM) fr[(x + PF) % (PF + 1)] = operand(x + PF);
+      if (x < NSD) {
+        if (x & 1)
+          dn = mfma16(op, df[x >> 1], x == 1 ? v16f{} : dn);
+        else
+          sn = mfma16(op, qf[x >> 1], x == 0 ? v16f{} : sn);
+      } else if constexpr (two) {
+        const int y = x - NSD;
+        acc[y % NDB] = mfma16(op, ds[y / NDB], acc[y % NDB]);
+      }
+      work(x);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    sc = sn;
+    dp = dn;
+  };
+
+  // Sweep 1: running max, sum and sum of p * dP (log2 units).  Block 0 holds a visible
+  // key (key 0) for every row, so the max is finite from the first block on.
+  float mr = -INFINITY, l = 0.0f, a = 0.0f;
+  int st0 = 0;  // stage of block kb
+  if constexpr (!PIPE) {
+    issue(0, 0, false);
     vm_wait<0>();
     __syncthreads();
+    for (int kb = 0; kb < nkb_wg; ++kb) {
+      if (kb + 1 < nkb_wg) issue(kb + 1, (kb + 1) & 1, false);
+      if (active && kb < nkb) {
+        v16f sc, dp;
+        scores(smem + (kb & 1) * STG, sc, dp);
+        mask(kb, sc);
+        float mt = sc[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mt = bmax(mt, sc[i]);
+        const float mn = bmax(mr, half_max(mt) * c_log2);
+        const float al = mr == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr - mn);
+        l *= al;
+        a *= al;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c_log2, -mn));
+          l += p;
+          a = __builtin_fmaf(p, dp[i], a);
+        }
+        mr = mn;
+      }
+      vm_wait<0>();
+      __syncthreads();
+    }
+  } else {
+    // Every wave runs every block of the group; a block past its causal diagonal is
+    // all masked and adds nothing (its max is -inf and its p are 0).
+    issue(0, st0, false);
+    if (nkb_wg > 1) issue(1, next_stage(st0), false);
+    vm_wait<0>();
+    __syncthreads();
+    v16f sc, dp;
+    scores(smem + st0 * STG, sc, dp);
+    mask(0, sc);
+    v16f acc_none[NDB];
+    const v8h ds_none[2] = {};
+    for (int kb = 0; kb < nkb_wg; ++kb) {
+      const int st1 = next_stage(st0);
+      if (kb + 2 < nkb_wg) issue(kb + 2, next_stage(st1), false);
+      float mn = 0.0f;
+      // Slot work: the block's max (slot 0), the new running max and the rescale
+      // (slot 1), then the 16 exponentials with their sums over slots 2 .. NSD-1.
+      auto work = [&](int x) {
+        if (x == 0) {
+          float mt = sc[0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) mt = bmax(mt, sc[i]);
+          mn = mt;
+        } else if (x == 1) {
+          mn = bmax(mr, half_max(mn) * c_log2);
+          const float al = mr == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr - mn);
+          l *= al;
+          a *= al;
+          mr = mn;
+        } else if (x < NSD) {
+          const int i0 = 16 * (x - 2) / (NSD - 2), i1 = 16 * (x - 1) / (NSD - 2);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            if (i < i0 || i >= i1) continue;
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c_log2, -mn));
+            l += p;
+            a = __builtin_fmaf(p, dp[i], a);
+          }
+        }
+      };
+      step(st1, st0, sc, dp, acc_none, ds_none, std::false_type{}, work);
+      mask(kb + 1, sc);
+      vm_wait<0>();
+      __syncthreads();
+      st0 = st1;
+    }
   }
   l = half_sum(l);
   a = half_sum(a);
@@ -155,23 +260,24 @@ __global__ __launch_bounds__(64 * dq_waves<D>()) void bwd_dq_kernel(
     dvec[qbase + qi] = Dv;
   }
 
-  // Sweep 2: P, dS and dQ^T = K^T dS^T.
+  // Sweep 2: P, dS and dQ^T = K^T dS^T.  Unconditional, as in the dK/dV kernel: past
+  // this wave's last key block every score is masked and dS is zero (a wave past the
+  // padded length has zero operands, lse = 0 and D = 0, so dS is zero too).
   v16f acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
-  issue(0, 0, true);
-  vm_wait<0>();
-  __syncthreads();
-  for (int kb = 0; kb < nkb_wg; ++kb) {
-    if (kb + 1 < nkb_wg) issue(kb + 1, (kb + 1) & 1, true);
-    // Unconditional, as in the dK/dV kernel: past this wave's last key block every score
-    // is masked and dS is zero (a wave past the padded length has zero operands, lse = 0
-    // and D = 0, so dS is zero too).
-    {
+  st0 = 0;
+  if constexpr (!PIPE) {
+    issue(0, 0, true);
+    vm_wait<0>();
+    __syncthreads();
+    for (int kb = 0; kb < nkb_wg; ++kb) {
+      if (kb + 1 < nkb_wg) issue(kb + 1, (kb + 1) & 1, true);
+      const char* st = smem + (kb & 1) * STG;
       v16f sc, dp;
-      scores(kb & 1, sc, dp);
+      scores(st, sc, dp);
       mask(kb, sc);
       v8h ds[2];
 #pragma unroll
@@ -179,15 +285,46 @@ __global__ __launch_bounds__(64 * dq_waves<D>()) void bwd_dq_kernel(
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c_log2, -lse));
         ds[i >> 3][i & 7] = (_Float16)(p * (dp[i] - Dv));
       }
-      const v8h* kca = reinterpret_cast<const v8h*>(smem + ((kb & 1) * 3 + 2) * TB);
+      const v8h* kca = reinterpret_cast<const v8h*>(st + 2 * TB);
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
           acc[db] = mfma16(kca[(gg * NDB + db) * 64 + lane], ds[gg], acc[db]);
+      vm_wait<0>();
+      __syncthreads();
     }
+  } else {
+    issue(0, st0, true);
+    if (nkb_wg > 1) issue(1, next_stage(st0), true);
     vm_wait<0>();
     __syncthreads();
+    v16f sc, dp;
+    scores(smem + st0 * STG, sc, dp);
+    mask(0, sc);
+    for (int kb = 0; kb < nkb_wg; ++kb) {
+      const int st1 = next_stage(st0);
+      if (kb + 2 < nkb_wg) issue(kb + 2, next_stage(st1), true);
+      v8h ds[2];
+      // Slot work: the block's 16 elements p = 2^(s c - lse), dS = p (dP - D) over the
+      // score slots, before the dQ products that take them.
+      auto work = [&](int x) {
+        if (x < NSD) {
+          const int i0 = 16 * x / NSD, i1 = 16 * (x + 1) / NSD;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            if (i < i0 || i >= i1) continue;
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c_log2, -lse));
+            ds[i >> 3][i & 7] = (_Float16)(p * (dp[i] - Dv));
+          }
+        }
+      };
+      step(st1, st0, sc, dp, acc, ds, std::true_type{}, work);
+      mask(kb + 1, sc);
+      vm_wait<0>();
+      __syncthreads();
+      st0 = st1;
+    }
   }
   // The loop's last barrier leaves the tile stages unused: they stage the output.
   store_rows_f32<D, EQ>(acc, scale, smem + w * staging_bytes<EQ>(),
