@@ -156,6 +156,96 @@ __device__ __forceinline__ void store_rows(const v16f (&o)[D / 32], float inv, c
   }
 }
 
+// The matrix products of the forward.  With ASM (D = 256, one wave per SIMD, where the
+// compiler would put every product's result in accumulation registers and copy the
+// scores and key-scale products back one register at a time for the softmax) they are
+// issued from inline assembly, so that each result lives in the register file its
+// readers want: the P.V and row-sum accumulators in accumulation registers (AGPRs;
+// only the rare rescale and the epilogue read them), the scores and key-scale products
+// in vector registers.  The compiler does not see the assembly as matrix instructions
+// and counts no wait states for it, so the hardware's required wait states between a
+// product and a vector instruction that reads its result are the caller's: settle()
+// (a result read: 21 wait states, more than the 16-pass products need) and the NOP
+// variants (an operand written by the instruction just before: 2).
+template <bool ASM>
+struct Mm {
+  // S = A.B for one 32x32 block of scores (int8, exact int32), a fresh accumulator.
+  static __device__ __forceinline__ v16i qk0(v4i a, v4i b) {
+    if constexpr (ASM) {
+      v16i c;
+      asm volatile("v_mfma_i32_32x32x32_i8 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+      return c;
+    } else {
+      v16i z;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) z[i] = 0;
+      return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, z, 0, 0, 0);
+    }
+  }
+  static __device__ __forceinline__ void qk(v16i& c, v4i a, v4i b) {
+    if constexpr (ASM)
+      asm volatile("v_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+    else
+      c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+  }
+  // o += A.B (fp16 inputs, fp32 accumulation).
+  template <bool NOP = false>
+  static __device__ __forceinline__ void pv(v16f& o, v8h a, v8h b) {
+    if constexpr (ASM) {
+      if constexpr (NOP)
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
+      else
+        asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
+    } else {
+      o = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, o, 0, 0, 0);
+    }
+  }
+  template <bool NOP = false>
+  static __device__ __forceinline__ void rowsum(v4f& l, v8h a, v8h b) {
+    if constexpr (ASM) {
+      if constexpr (NOP)
+        asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(l) : "v"(a), "v"(b));
+      else
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(l) : "v"(a), "v"(b));
+    } else {
+      l = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, l, 0, 0, 0);
+    }
+  }
+  // A.B with a fresh accumulator (the Q outlier products, D <= 128: always the builtin).
+  static __device__ __forceinline__ v16f f16_0(v8h a, v8h b) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, v16f{}, 0, 0, 0);
+  }
+  // The outer product a_l . b_l over the two 32-lane blocks (v_mfma_f32_32x32x1_2b_f32).
+  static __device__ __forceinline__ v32f outer(float a, float b) {
+    if constexpr (ASM) {
+      v32f c;
+      asm volatile("v_mfma_f32_32x32x1_2b_f32 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+      return c;
+    } else {
+      v32f z;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) z[i] = 0.0f;
+      return __builtin_amdgcn_mfma_f32_32x32x1f32(a, b, z, 0, 0, 0);
+    }
+  }
+  // 21 wait states before x is read; x passes through so its readers stay after them.
+  template <typename T>
+  static __device__ __forceinline__ void settle_v(T& x) {
+    if constexpr (ASM) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(x));
+  }
+  static __device__ __forceinline__ void settle_v3(v32f& x, v16i& y, v16i& z) {
+    if constexpr (ASM) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(x), "+v"(y), "+v"(z));
+  }
+  template <int N>
+  static __device__ __forceinline__ void settle_acc(v16f (&o)[N], v4f& l) {
+    if constexpr (ASM) {
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+a"(l));
+#pragma unroll
+      for (int i = 0; i < N; ++i) asm volatile("" : "+a"(o[i]));
+    }
+  }
+};
+
 // The forward's own Q quantization (the kernels' FQ path): lane (m, hh) holds channels
 // 32 kb + 16 hh + j (j < 16) of query row qi, exactly its B-operand fragment positions, so
 // the codes are made in place with the preparation's row rule (row_scale, RowQ), bit
@@ -340,6 +430,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || D > 128) ? 1 : 2) void attn_pi
   static_assert(!QO || FQ, "the outlier channels' Q values come from the fused Q path");
   using LY = Lay<D, QO>;
   using DM = Dma<D, NW, QO>;
+  using MM = Mm<(D > 128)>;             // products from assembly at D = 256
   constexpr int NKB = LY::NKB;
   constexpr int BMW = 32 * NW;          // query rows per workgroup
   constexpr int NS = NW >= 8 ? 4 : 3;   // ring stages
@@ -441,12 +532,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || D > 128) ? 1 : 2) void attn_pi
   // c_j = sk_j * qsc for the tile's 64 keys: v_mfma_f32_32x32x1_2b_f32 with lane l giving
   // the scale of key l (block l / 32, row l % 32) and its query's qsc (column l % 32), so
   // register 16 nb + i holds key 32 nb + 8 (i/4) + 4 hh + i%4, as the scores do.
-  auto cscale = [&](float sk_lane) -> v32f {
-    v32f z;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) z[i] = 0.0f;
-    return __builtin_amdgcn_mfma_f32_32x32x1f32(sk_lane, qsc, z, 0, 0, 0);
-  };
+  auto cscale = [&](float sk_lane) -> v32f { return MM::outer(sk_lane, qsc); };
 
   // Register i of the S^T block nb holds key 32 nb + 8 (i/4) + 4 hh + i%4 of the tile;
   // off(i) is that key relative to the tile's first key + 4 hh.
@@ -484,12 +570,11 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || D > 128) ? 1 : 2) void attn_pi
   // Row sum and P.V of key group kg.
   auto pv = [&](const char* st, int kg) {
     const v4i* vl = reinterpret_cast<const v4i*>(st + LY::KB);
-    lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(sel, pk[kg], lacc, 0, 0, 0);
+    MM::template rowsum<true>(lacc, sel, pk[kg]);
 #pragma unroll
     for (int db = 0; db < NKB; ++db) {
       const v4i va = vl[(kg * NKB + db) * 64 + lane];
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, va), pk[kg], o[db],
-                                                      0, 0, 0);
+      MM::template pv<true>(o[db], __builtin_bit_cast(v8h, va), pk[kg]);
     }
   };
 
@@ -558,19 +643,20 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || D > 128) ? 1 : 2) void attn_pi
       // the MFMA of slot x
       if (x < NQK) {
         const int nb = x / NKB, kb = x % NKB;
-        sn[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fr[x % (PF + 1)], qf[kb], sn[nb], 0, 0, 0);
+        if (kb == 0)
+          sn[nb] = MM::qk0(fr[x % (PF + 1)], qf[kb]);
+        else
+          MM::qk(sn[nb], fr[x % (PF + 1)], qf[kb]);
       } else if (x < NSC) {
-        so[x - NQK] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            __builtin_bit_cast(v8h, fr[x % (PF + 1)]), qo, v16f{}, 0, 0, 0);
+        so[x - NQK] = MM::f16_0(__builtin_bit_cast(v8h, fr[x % (PF + 1)]), qo);
       } else if (x == XC) {
         cn = cscale(skn);
       } else {
         const int y = x - NPV, kg = y / (NKB + 1), db = y % (NKB + 1) - 1;
         if (db < 0)
-          lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(sel, pk[kg], lacc, 0, 0, 0);
+          MM::rowsum(lacc, sel, pk[kg]);
         else
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              __builtin_bit_cast(v8h, fr[x % (PF + 1)]), pk[kg], o[db], 0, 0, 0);
+          MM::pv(o[db], __builtin_bit_cast(v8h, fr[x % (PF + 1)]), pk[kg]);
       }
       // operand PF slots ahead
       if (x + PF < NM && has_operand(x + PF)) fr[(x + PF) % (PF + 1)] = operand(x + PF);
@@ -612,7 +698,9 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || D > 128) ? 1 : 2) void attn_pi
         }
       }
       if (x >= C_BEG && x < C_END) {
-        // conversion of the next tile's scores: items [C(x), C(x + 1))
+        // conversion of the next tile's scores: items [C(x), C(x + 1)); with products from
+        // assembly, the key-scale product's and the scores' wait states first
+        if (x == C_BEG) MM::settle_v3(cn, sn[0], sn[1]);
         const int c = x - C_BEG;
         const int i0 = (32 * c) / NC, i1 = (32 * (c + 1)) / NC;
 #pragma unroll
@@ -649,22 +737,19 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || D > 128) ? 1 : 2) void attn_pi
     v16i sc[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
+      sc[nb] = MM::qk0(kl[(nb * NKB) * 64 + lane], qf[0]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sc[nb][i] = 0;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        sc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kl[(nb * NKB + kb) * 64 + lane], qf[kb],
-                                                       sc[nb], 0, 0, 0);
+      for (int kb = 1; kb < NKB; ++kb) MM::qk(sc[nb], kl[(nb * NKB + kb) * 64 + lane], qf[kb]);
     }
     v16f so0[2];
     if constexpr (QO) {
       const v4i* kol = reinterpret_cast<const v4i*>(smem + LY::KO);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
-        so0[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, kol[nb * 64 + lane]),
-                                                         qo, v16f{}, 0, 0, 0);
+        so0[nb] = MM::f16_0(__builtin_bit_cast(v8h, kol[nb * 64 + lane]), qo);
     }
-    const v32f c0 = cscale(skl[lane]);
+    v32f c0 = cscale(skl[lane]);
+    MM::settle_v3(c0, sc[0], sc[1]);
     const bool msk0 = needs_mask(0);
     const int last0 = last_key - 4 * hh;
 #pragma unroll
@@ -703,6 +788,10 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || D > 128) ? 1 : 2) void attn_pi
     char* dst = smem + (scur == 0 ? NS - 1 : scur - 1) * LY::STAGE;
     bool upd_any;
     const float mc = pipe_step(cur, nxt, dsrc, dst, MASK, last_key - (j + 1) * TK - 4 * hh, upd_any);
+    // With products from assembly: the wait states of the step's last P.V products before
+    // anything (the rescale, or a register copy the compiler places between the loops)
+    // reads the accumulators.
+    MM::settle_acc(o, lacc);
     if (upd_any) raise(mc);
     // Tile j + 2 must have landed; the copy issued in this step may run on when it is
     // for a later tile.
@@ -744,6 +833,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || D > 128) ? 1 : 2) void attn_pi
   } else {
     area = smem + NS * LY::STAGE + w * 32 * EPITCH;
   }
+  MM::settle_acc(o, lacc);
   store_rows<D, EC>(o, qi < L ? 1.0f / lacc[0] : 0.0f, area, out, aq, start, h, qw0, L, lane);
 }
 
