@@ -286,28 +286,51 @@ __device__ __forceinline__ float quantize_own_q(const _Float16* __restrict__ qin
       qo[j] = (real && c >= 0) ? row[c] : (_Float16)0.0f;
     }
   }
-  float xf[NKB][2][8];
-  float amax = 0.0f;
+  if constexpr (!QO) {
+    // The fp16 values go into the arithmetic as they are: the absolute maximum from
+    // their bit patterns, the codes from fp16 operands (exact conversions).
+    uint32_t mb = 0;
+    if (real) {
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
+        for (int e = 0; e < 2; ++e) mb = absmax_bits8(xr[kb][e], mb);
+    }
+    float amax = absmax_of_bits(mb);
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    if (qblk) amax = group_max<64>(amax);
+    const RowQ rq(real ? row_scale(amax, 24) : 0.0f);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool keep = !QO || ((omask >> (16 * kb + 8 * e + j)) & 1) == 0;
-        xf[kb][e][j] = (real && keep) ? (float)xr[kb][e][j] : 0.0f;
-        amax = fmaxf(amax, fabsf(xf[kb][e][j]));
-      }
-  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-  if (qblk) amax = group_max<64>(amax);
-  const RowQ rq(real ? row_scale(amax, 24) : 0.0f);
+    for (int kb = 0; kb < NKB; ++kb) {
+      const uint2 lo = real ? rq.pack8h(xr[kb][0]) : make_uint2(0u, 0u);
+      const uint2 hi = real ? rq.pack8h(xr[kb][1]) : make_uint2(0u, 0u);
+      qf[kb] = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+    }
+    return rq.s;
+  } else {
+    float xf[NKB][2][8];
+    float amax = 0.0f;
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    const uint2 lo = real ? rq.pack8(xf[kb][0]) : make_uint2(0u, 0u);
-    const uint2 hi = real ? rq.pack8(xf[kb][1]) : make_uint2(0u, 0u);
-    qf[kb] = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bool keep = ((omask >> (16 * kb + 8 * e + j)) & 1) == 0;
+          xf[kb][e][j] = (real && keep) ? (float)xr[kb][e][j] : 0.0f;
+          amax = fmaxf(amax, fabsf(xf[kb][e][j]));
+        }
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    if (qblk) amax = group_max<64>(amax);
+    const RowQ rq(real ? row_scale(amax, 24) : 0.0f);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const uint2 lo = real ? rq.pack8(xf[kb][0]) : make_uint2(0u, 0u);
+      const uint2 hi = real ? rq.pack8(xf[kb][1]) : make_uint2(0u, 0u);
+      qf[kb] = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+    }
+    return rq.s == 0.0f ? 0x1p-60f : rq.s;
   }
-  return (QO && rq.s == 0.0f) ? 0x1p-60f : rq.s;
 }
 
 // ----------------------------------------------------------------------------------

@@ -125,22 +125,61 @@ struct RowQ {
   float s, y;
   __device__ __forceinline__ explicit RowQ(float scale)
       : s(scale), y(scale == 0.0f ? 0.0f : 1.0f / scale) {}
-  __device__ __forceinline__ float code(float x) const {
+  // The corrected quotient RN(x/s) (before rounding to an integer).
+  __device__ __forceinline__ float quot(float x) const {
     const float q0 = __fmul_rn(x, y);
     const float r = __builtin_fmaf(-q0, s, x);
-    const float q = __builtin_fmaf(r, y, q0);
-    return __builtin_rintf(q);
+    return __builtin_fmaf(r, y, q0);
+  }
+  __device__ __forceinline__ float code(float x) const { return __builtin_rintf(quot(x)); }
+  // The code as the low byte of a float's bits: q + 1.5 * 2^23 is rounded to an integer
+  // by the add itself (round to nearest, ties to even, as rint) for |q| < 2^22, and its
+  // bits are 0x4B400000 plus that integer, whose low byte is the code's two's
+  // complement byte.
+  static __device__ __forceinline__ uint32_t code_bits(float q) {
+    return __float_as_uint(q + 12582912.0f);
+  }
+  // Four codes' low bytes packed little-endian into one dword (v_perm_b32: selector
+  // bytes 0-3 pick the second source's bytes, 4-7 the first's, 0x0c a zero byte).
+  static __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2,
+                                                   uint32_t b3) {
+    const uint32_t p01 = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+    const uint32_t p23 = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
   }
   // Eight codes packed little-endian into two dwords (two's complement bytes).
   __device__ __forceinline__ uint2 pack8(const float (&x)[8]) const {
-    uint32_t lo = 0, hi = 0;
+    uint32_t b[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lo = __builtin_amdgcn_cvt_pk_u8_f32(code(x[j]) + 128.0f, j, lo);
+    for (int j = 0; j < 8; ++j) b[j] = code_bits(quot(x[j]));
+    return make_uint2(pack4(b[0], b[1], b[2], b[3]), pack4(b[4], b[5], b[6], b[7]));
+  }
+  // The same from fp16 values (converted exactly to fp32 inside the arithmetic).
+  __device__ __forceinline__ uint2 pack8h(const v8h& x) const {
+    uint32_t b[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) hi = __builtin_amdgcn_cvt_pk_u8_f32(code(x[4 + j]) + 128.0f, j, hi);
-    return make_uint2(lo ^ 0x80808080u, hi ^ 0x80808080u);
+    for (int j = 0; j < 8; ++j) b[j] = code_bits(quot((float)x[j]));
+    return make_uint2(pack4(b[0], b[1], b[2], b[3]), pack4(b[4], b[5], b[6], b[7]));
   }
 };
+
+// Largest |x| of eight fp16 values, as fp32: with the sign bits cleared, fp16 bit
+// patterns order like their values (finite inputs), so a packed unsigned max of the
+// 16-bit halves finds it.
+__device__ __forceinline__ uint32_t absmax_bits8(const v8h& x, uint32_t acc) {
+  typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+  const uint4 w = __builtin_bit_cast(uint4, x);
+  v2u16 m = __builtin_bit_cast(v2u16, acc);
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(v2u16, w.x & 0x7fff7fffu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(v2u16, w.y & 0x7fff7fffu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(v2u16, w.z & 0x7fff7fffu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(v2u16, w.w & 0x7fff7fffu));
+  return __builtin_bit_cast(uint32_t, m);
+}
+__device__ __forceinline__ float absmax_of_bits(uint32_t acc) {
+  const uint32_t lo = acc & 0xffffu, hi = acc >> 16;
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(lo > hi ? lo : hi));
+}
 
 // A lane permutation through DPP (no LDS round trip).
 template <int CTRL>
