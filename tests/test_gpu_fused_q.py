@@ -4,7 +4,8 @@ Its codes and scales follow the same row rule as the Q preparation pass, so the 
 must equal, bit for bit, that of the staged path: K/V and Q prepared into a workspace
 (the debug dump's preparation, which honours the variant flags) and then
 ``attn_int8_attend``, whose kernel reads the prepared Q fragments.  Rows that are all
-zero, rows of large values and query tiles that end inside a 32-row block are included.
+zero, rows of large values, rows of fp16 subnormals, the largest finite fp16 values with
+both signs, negative zeros and query tiles that end inside a 32-row block are included.
 """
 
 import sys
@@ -54,7 +55,14 @@ def test_fused_q_equals_prepared_q(D, causal, flags):
     qn[0, 1, 5] = 0                    # an all-zero row: scale 0, zero codes
     qn[1, 2, 33] *= np.float16(3000)   # a row of large values (still finite in fp16)
     qn[1, 3, 690:] = 0                 # zero rows inside the last, ragged 32-row block
+    # fp16 subnormals only (the absolute maximum from bit patterns), the largest finite
+    # fp16 values with both signs, and negative zeros
+    qn[0, 0, 7] = (w.q[0, 0, 7].astype(np.float32) * 2.0 ** -20).astype(np.float16)
+    qn[0, 2, 11, :4] = [65504, -65504, -0.0, 0.0]
+    qn[1, 0, 40] = -np.abs(qn[1, 0, 40])
+    qn[1, 0, 40, ::3] = -0.0
     assert np.isfinite(qn).all()
+    assert (np.abs(qn[0, 0, 7]) < np.float16(2.0 ** -14)).all() and np.abs(qn[0, 0, 7]).max() > 0
     q, k, v = dev(qn), dev(w.k), dev(w.v)
     a = host(i8.attn_int8_fwd_ex(q, k, v, causal, flags))
     b = host(staged(q, k, v, causal, flags))
