@@ -17,7 +17,7 @@
 // is linear, so every LDS operand read is a conflict-free 16-byte read.
 //
 // One kernel, attn_pipe_kernel, software-pipelined over two tiles: 8 waves and 256
-// query rows per workgroup at D = 128; 4 waves and 128 rows at D <= 64 (two or three
+// query rows per workgroup at D = 128; 4 waves and 128 rows at D <= 64 (three
 // workgroups per CU) and at D = 256 (one wave per SIMD, whose 512 registers hold the
 // accumulators and both tiles' state).
 #include <float.h>
@@ -336,7 +336,7 @@ __device__ __forceinline__ float quantize_own_q(const _Float16* __restrict__ qin
 // ----------------------------------------------------------------------------------
 // Software-pipelined forward for D <= 128: at D = 128 one workgroup of 8 waves (256
 // query rows) per CU with a four-stage LDS ring; at D <= 64 workgroups of 4 waves (128
-// rows), two or three per CU, with three stages.  The row sum on the MFMA.
+// rows), three per CU, with three stages.  The row sum on the MFMA.
 //
 // A 32 x 64 wave-tile needs 24 MFMAs (8 int8 for the scores, 16 fp16 for P.V) and
 // about 160 vector instructions of softmax (per score: conversion, key scale,
@@ -435,6 +435,15 @@ __device__ __forceinline__ void copy_tile_dma(const char* __restrict__ src, char
   for (int r = 0; r < Dma<D, NW, QO>::ROUNDS; ++r) copy_tile_round<D, NW, QO>(src, stage, tid, w, r);
 }
 
+// Workgroups per CU the kernel is built for (its register and LDS budget): one at D = 128
+// (eight waves) and D = 256; three at D <= 64 (four waves each), where the per-score
+// vector work outweighs the matrix work and a third wave per SIMD hides more of its
+// latencies; two with Q outlier detection, whose registers would spill at three.  (Four
+// at D = 32 spill inside the loop and measured 14 % slower.)
+constexpr int wg_per_cu(int D, int NW, bool QO) {
+  return (NW >= 8 || D > 128) ? 1 : QO ? 2 : 3;
+}
+
 // FQ: the kernel quantizes its Q rows itself from the fp16 input qin (layout aq, the
 // output's), with the Q/K row rule, or with qblk one scale per 32-row block counted
 // from the sequence start; otherwise it reads the prepared fragments q8 and scales qs.
@@ -445,7 +454,7 @@ __device__ __forceinline__ void copy_tile_dma(const char* __restrict__ src, char
 // (qsc = sq * qk_log2, with sq replaced by 2^-60 where the int8 part is all zero: its
 // scores are 0 there).
 template <int D, bool CAUSAL, int NW, bool FQ, bool QO = false>
-__global__ __launch_bounds__(64 * NW, (NW >= 8 || D > 128) ? 1 : 2) void attn_pipe_kernel(
+__global__ __launch_bounds__(64 * NW, wg_per_cu(D, NW, QO)) void attn_pipe_kernel(
     const int8_t* __restrict__ q8, const float* __restrict__ qs, int64_t Qpad,
     const _Float16* __restrict__ qin, int qblk, _Float16* __restrict__ out, Act aq, Seqs seqs,
     int Hq, int Hkv, int nseq, int xcd_map, float qk_log2, const char* __restrict__ tiles,
@@ -462,10 +471,12 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || D > 128) ? 1 : 2) void attn_pi
   // of the wave's 32 rows at a time, rows padded to EPITCH bytes.
   constexpr int EC = D < 64 ? D : 64;
   constexpr int EPITCH = 2 * EC + 16;
-  // Where the ring and the staging areas would not fit the 160 KB of LDS together (D =
-  // 256), the output is staged in a ring stage that no tile uses any more.
-  constexpr bool EPI_IN_RING = NS * LY::STAGE + NW * 32 * EPITCH > 160 * 1024;
-  static_assert(!EPI_IN_RING || NW * 32 * EPITCH <= LY::STAGE, "staging fits one stage");
+  // Where the ring and the staging areas of the workgroups of a CU would not fit the 160
+  // KB of LDS together (D = 256, and D = 64 at three workgroups per CU), the output is
+  // staged in the ring once no tile uses it any more.
+  constexpr int WGPC = wg_per_cu(D, NW, QO);
+  constexpr bool EPI_IN_RING = (NS * LY::STAGE + NW * 32 * EPITCH) * WGPC > 160 * 1024;
+  static_assert(!EPI_IN_RING || NW * 32 * EPITCH <= NS * LY::STAGE, "staging fits the ring");
   __shared__ __attribute__((aligned(16)))
   char smem[NS * LY::STAGE + (EPI_IN_RING ? 0 : NW * 32 * EPITCH)];
 
@@ -850,9 +861,9 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || D > 128) ? 1 : 2) void attn_pi
   char* area;
   if constexpr (EPI_IN_RING) {
     // Every wave's copies have landed (the wait above) and, past this barrier, every
-    // wave's P.V is done, so no stage is read any more; each wave takes its part of one.
+    // wave's P.V is done, so no stage is read any more; each wave takes its part of it.
     __syncthreads();
-    area = smem + (scur == NS - 1 ? 0 : scur + 1) * LY::STAGE + w * 32 * EPITCH;
+    area = smem + w * 32 * EPITCH;
   } else {
     area = smem + NS * LY::STAGE + w * 32 * EPITCH;
   }
@@ -952,9 +963,9 @@ static hipError_t attn_d(const FwdGeom& g, const WsPlan& p, const void* ws, hipS
   const char* w = static_cast<const char*>(ws);
   // Waves per workgroup of the pipelined kernel.  At D <= 64 a step has little MFMA work
   // beside the fixed cost of its barrier and copy wait, and a wave's registers leave room
-  // for two or three workgroups of four waves per CU, which hide each other's barriers
+  // for three workgroups of four waves per CU, which hide each other's barriers
   // (B4 H16 S2048 non-causal: D = 32 64.8 -> 57.5 us, D = 64 76.6 -> 75.2 us against
-  // eight waves).  At D = 128 eight waves in one workgroup share every tile copy and LDS
+  // eight waves; D = 64 74.6 against 77.5 us at three workgroups per CU against two).  At D = 128 eight waves in one workgroup share every tile copy and LDS
   // stage.  At D = 256 a wave needs more than half of a SIMD's registers (the 128
   // accumulator registers of O and both tiles' state), so four waves, one per SIMD.
   constexpr int NW = (D <= 64 || D > 128) ? 4 : 8;
