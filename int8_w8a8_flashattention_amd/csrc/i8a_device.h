@@ -238,12 +238,16 @@ __device__ __forceinline__ void load8_f32(const _Float16* p, float (&x)[8]) {
   for (int j = 0; j < 8; ++j) x[j] = (float)h[j];
 }
 
-// fp16 value times 2^24 as an exact integer (every fp16 number is a multiple of 2^-24).
-__device__ __forceinline__ int64_t fp16_fixed24(_Float16 v) {
-  const uint32_t u = __builtin_bit_cast(uint16_t, v);
-  const uint32_t e = (u >> 10) & 31u, m = u & 1023u;
-  const int64_t mag = e ? ((int64_t)(1024u | m) << (e - 1u)) : (int64_t)m;
-  return (u & 0x8000u) ? -mag : mag;
+// An exact sum of at most 8 fp16 values (a double) times 2^24 as an integer.  Every fp16
+// number is a multiple of 2^-24 below 2^16 in magnitude, so such a sum, accumulated in
+// fp64 in any order, is exact (it needs at most 43 of the 53 significand bits), and
+// y = sum * 2^24 is an integer with |y| < 2^43: it is split as floor(y / 2^32) (a small
+// signed integer) and the remainder in [0, 2^32), both converted exactly.
+__device__ __forceinline__ int64_t fixed24_of_sum8(double sum) {
+  const double y = sum * 0x1p24;
+  const double hi = __builtin_floor(y * 0x1p-32);
+  const double lo = y - hi * 0x1p32;
+  return (int64_t)((uint64_t)(int64_t)(int32_t)hi << 32) + (int64_t)(uint32_t)lo;
 }
 
 // The K-smoothing mean of one (sequence, kv head) from its np <= MAX_PARTS launch-1

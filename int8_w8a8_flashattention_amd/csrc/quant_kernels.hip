@@ -58,7 +58,8 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(
 
 // Launch 1 (workgroup = tpw consecutive tiles of one sequence and kv head): the exact
 // per-channel sums of the tiles' K rows as one int64 partial, in units of 2^-24 (every
-// fp16 value is an integer multiple of 2^-24).  With VCH (V quantized per channel),
+// fp16 value is an integer multiple of 2^-24; each thread sums its values of a tile in
+// fp64, exactly, and adds that sum to its integer partial).  With VCH (V quantized per channel),
 // also the per-channel maxima of |v| over the same tokens as one fp32 partial; with QO
 // (Q outlier detection), the per-channel maxima of |q| over the same tokens and the
 // kv head's Gq query heads.
@@ -109,16 +110,24 @@ __global__ __launch_bounds__(256) void prep_ksum_kernel(const _Float16* __restri
         if constexpr (VCH) vr[i] = *reinterpret_cast<const v8h*>(v + act.off(start, g, t) + lc * 8);
       }
     }
+    // The tile's NP <= 8 values per channel summed exactly in fp64, then added to the
+    // integer partial.
+    static_assert(NP <= 8, "fixed24_of_sum8 takes sums of at most 8 values");
+    double ts[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ts[j] = 0.0;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       if (t0 + i * RPP + rsub < L) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          acc[j] += fp16_fixed24(kr[i][j]);
+          ts[j] += (double)(float)kr[i][j];
           if constexpr (VCH) vmx[j] = fmaxf(vmx[j], fabsf((float)vr[i][j]));
         }
       }
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] += fixed24_of_sum8(ts[j]);
     if constexpr (QO) {
       for (int hq = g * Gq; hq < (g + 1) * Gq; ++hq) {
 #pragma unroll
