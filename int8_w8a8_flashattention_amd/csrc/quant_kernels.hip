@@ -59,10 +59,10 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(
 // Launch 1 (workgroup = tpw consecutive tiles of one sequence and kv head): the exact
 // per-channel sums of the tiles' K rows as one int64 partial, in units of 2^-24 (every
 // fp16 value is an integer multiple of 2^-24; each thread sums its values of a tile in
-// fp64, exactly, and adds that sum to its integer partial).  With VCH (V quantized per channel),
-// also the per-channel maxima of |v| over the same tokens as one fp32 partial; with QO
-// (Q outlier detection), the per-channel maxima of |q| over the same tokens and the
-// kv head's Gq query heads.
+// fp64, exactly, and adds that sum to its integer partial).  With VCH (V quantized per
+// channel), also the per-channel maxima of |v| over the same tokens as one fp32
+// partial; with QO (Q outlier detection), the per-channel maxima of |q| over the same
+// tokens and the kv head's Gq query heads.
 template <int D, bool VCH, bool QO = false>
 __global__ __launch_bounds__(256) void prep_ksum_kernel(const _Float16* __restrict__ k,
                                                         const _Float16* __restrict__ v,
