@@ -129,16 +129,27 @@ __global__ __launch_bounds__(256) void prep_ksum_kernel(const _Float16* __restri
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] += fixed24_of_sum8(ts[j]);
     if constexpr (QO) {
-      for (int hq = g * Gq; hq < (g + 1) * Gq; ++hq) {
+      // The group's query heads four at a time, all of their row loads issued before any
+      // maximum is taken.
+      constexpr int HU = 4;
+      for (int hq0 = g * Gq; hq0 < (g + 1) * Gq; hq0 += HU) {
+        v8h qr[HU][NP];
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
-          const int t = t0 + i * RPP + rsub;
-          if (t < L) {
-            const v8h qr = *reinterpret_cast<const v8h*>(q + aq.off(start, hq, t) + lc * 8);
+        for (int u = 0; u < HU; ++u)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) qmx[j] = fmaxf(qmx[j], fabsf((float)qr[j]));
+          for (int i = 0; i < NP; ++i) {
+            const int t = t0 + i * RPP + rsub;
+            if (hq0 + u < (g + 1) * Gq && t < L)
+              qr[u][i] = *reinterpret_cast<const v8h*>(q + aq.off(start, hq0 + u, t) + lc * 8);
           }
-        }
+#pragma unroll
+        for (int u = 0; u < HU; ++u)
+#pragma unroll
+          for (int i = 0; i < NP; ++i)
+            if (hq0 + u < (g + 1) * Gq && t0 + i * RPP + rsub < L) {
+#pragma unroll
+              for (int j = 0; j < 8; ++j) qmx[j] = fmaxf(qmx[j], fabsf((float)qr[u][i][j]));
+            }
       }
     }
   }
@@ -179,6 +190,7 @@ struct QoShared {
   int slot[D];
   int chan[QO_MAX + 1];  // the kept channels, then their count
   float red[256];
+  int wkeep[4];          // kept channels per wave of the first D threads
 };
 
 template <int D>
@@ -186,8 +198,22 @@ __device__ __forceinline__ void select_outliers(const float* __restrict__ pp, in
                                                 QoShared<D>& sh, int32_t* __restrict__ ochan_out) {
   constexpr int TPC = 256 / D;  // threads per channel
   const int d = threadIdx.x % D, r = threadIdx.x / D;
+  // Every thread issues all its loads of the partials (np <= MAX_PARTS) at once, CH at a
+  // time, so the reduction costs a few memory latencies rather than one per partial.
+  constexpr int MAXK = (MAX_PARTS + TPC - 1) / TPC;
+  constexpr int CH = MAXK < 16 ? MAXK : 16;
   float mx = 0.0f;
-  for (int i = r; i < np; i += TPC) mx = fmaxf(mx, pp[(int64_t)i * D + d]);
+#pragma unroll
+  for (int k0 = 0; k0 < MAXK; k0 += CH) {
+    float v[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int i = r + (k0 + k) * TPC;
+      v[k] = i < np ? pp[(int64_t)i * D + d] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < CH; ++k) mx = fmaxf(mx, v[k]);
+  }
   sh.red[threadIdx.x] = mx;
   __syncthreads();
   if (r == 0) {
@@ -205,12 +231,20 @@ __device__ __forceinline__ void select_outliers(const float* __restrict__ pp, in
     sh.keep[d] = (a > QO_THRESHOLD && rank < QO_MAX) ? 1 : 0;
   }
   __syncthreads();
+  // Positions by prefix counts: channel d = threadIdx.x (r == 0) is in wave d / 64 at lane
+  // d % 64; a ballot counts the kept channels below it in its wave, the per-wave totals
+  // those of the waves before.
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const bool kd = r == 0 && sh.keep[d] != 0;
+  const uint64_t kmask = __ballot(kd);
+  if (r == 0 && lane == 0) sh.wkeep[wv] = __popcll(kmask);
+  __syncthreads();
   if (r == 0) {
-    int pos = 0;
-    for (int e = 0; e < d; ++e) pos += sh.keep[e];
-    sh.slot[d] = sh.keep[d] ? pos : -1;
-    if (sh.keep[d]) sh.chan[pos] = d;
-    if (d == D - 1) sh.chan[QO_MAX] = pos + sh.keep[d];
+    int pos = __popcll(kmask & ((1ull << lane) - 1ull));
+    for (int x = 0; x < wv; ++x) pos += sh.wkeep[x];
+    sh.slot[d] = kd ? pos : -1;
+    if (kd) sh.chan[pos] = d;
+    if (d == D - 1) sh.chan[QO_MAX] = pos + (kd ? 1 : 0);
   }
   __syncthreads();
   if (ochan_out && threadIdx.x < QO_MAX)
