@@ -246,20 +246,60 @@ struct Mm {
   }
 };
 
+// Unnormalized fast Walsh-Hadamard transform of a D-channel query row in the operand
+// layout of the forward's Q: lane (m, hh) holds channels 32 kb + 16 hh + i (i < 16) as
+// x[16 kb + i].  The stages run in the order s = 0, 1, ..., log2(D) - 1, and stage s
+// replaces the pair (x_c, x_{c + 2^s}) with bit s of c clear by (x_c + x_{c + 2^s},
+// x_c - x_{c + 2^s}), the same fp32 operations as the preparation's fwht_row, so the
+// rows are bit-identical: stages 0-3 pair values inside a 16-channel chunk, stage 4 the
+// two half-rows of lanes m and m + 32 (v_permlane32_swap gives every lane both), the
+// later ones chunks kb and kb + 2^(s-5) of the lane.
+template <int D>
+__device__ __forceinline__ void fwht_qrow(float (&x)[D / 2], int hh) {
+  constexpr int N = D / 2;
+#pragma unroll
+  for (int h = 1; h < 16; h *= 2)
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (!(i & h)) {
+        const float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[i]), __float_as_uint(x[i]),
+                                                    false, false);
+    const float lo = __uint_as_float(r[0]), hi = __uint_as_float(r[1]);
+    x[i] = hh ? lo - hi : lo + hi;
+  }
+#pragma unroll
+  for (int h = 16; h < N; h *= 2)
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (!(i & h)) {
+        const float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+}
+
 // The forward's own Q quantization (the kernels' FQ path): lane (m, hh) holds channels
 // 32 kb + 16 hh + j (j < 16) of query row qi, exactly its B-operand fragment positions, so
 // the codes are made in place with the preparation's row rule (row_scale, RowQ), bit
 // for bit.  The row's absolute maximum combines the two half-rows of lanes m and
-// m + 32 (a max is exact in any order); with qblk, the wave's maximum (its 32 rows are
-// one block).  Rows past the sequence end get zero codes and scale 0.  QO: the kv
+// m + 32 (a max is exact in any order); with qmode bit 0, the wave's maximum (its 32
+// rows are one block).  With qmode bit 1 the rows are Hadamard-rotated first
+// (fwht_qrow).  Rows past the sequence end get zero codes and scale 0.  QO: the kv
 // group's outlier channels (oc, QO_MAX entries, -1 padded) are zeroed first, and the
 // row's values at the outlier slots 8 hh .. 8 hh + 7 go to qo.  Returns the row scale
 // (QO: 2^-60 where the int8 part is all zero).
 template <int D, bool QO>
 __device__ __forceinline__ float quantize_own_q(const _Float16* __restrict__ qin, const Act& aq,
                                                 int64_t start, int h, int qi, int L, int hh,
-                                                int qblk, const int32_t* __restrict__ oc,
+                                                int qmode, const int32_t* __restrict__ oc,
                                                 v4i (&qf)[D / 32], v8h& qo) {
+  const bool qblk = (qmode & 1) != 0;
   constexpr int NKB = D / 32;
   const bool real = qi < L;
   v8h xr[NKB][2];
@@ -286,7 +326,36 @@ __device__ __forceinline__ float quantize_own_q(const _Float16* __restrict__ qin
       qo[j] = (real && c >= 0) ? row[c] : (_Float16)0.0f;
     }
   }
-  if constexpr (!QO) {
+  if (!QO && (qmode & 2)) {
+    // Rotated rows: the transform in fp32, then the row rule on its results.
+    float x[D / 2];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[16 * kb + 8 * e + j] = real ? (float)xr[kb][e][j] : 0.0f;
+    fwht_qrow<D>(x, hh);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D / 2; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    if (qblk) amax = group_max<64>(amax);
+    const RowQ rq(real ? row_scale(amax, 24) : 0.0f);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      float lo8[8], hi8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        lo8[j] = x[16 * kb + j];
+        hi8[j] = x[16 * kb + 8 + j];
+      }
+      const uint2 lo = real ? rq.pack8(lo8) : make_uint2(0u, 0u);
+      const uint2 hi = real ? rq.pack8(hi8) : make_uint2(0u, 0u);
+      qf[kb] = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+    }
+    return rq.s;
+  } else if constexpr (!QO) {
     // The fp16 values go into the arithmetic as they are: the absolute maximum from
     // their bit patterns, the codes from fp16 operands (exact conversions).
     uint32_t mb = 0;
@@ -445,8 +514,9 @@ constexpr int wg_per_cu(int D, int NW, bool QO) {
 }
 
 // FQ: the kernel quantizes its Q rows itself from the fp16 input qin (layout aq, the
-// output's), with the Q/K row rule, or with qblk one scale per 32-row block counted
-// from the sequence start; otherwise it reads the prepared fragments q8 and scales qs.
+// output's), with the Q/K row rule, with qmode bit 0 one scale per 32-row block counted
+// from the sequence start, with bit 1 after the Hadamard rotation; otherwise it reads
+// the prepared fragments q8 and scales qs.
 // QO (with FQ): Q outlier channels.  The kv group's channels (ochan) are left out of
 // the int8 Q rows, and their fp16 products come from one 32x32x16 fp16 MFMA per
 // 32-key block with the tile's fp16 K values of those channels:
@@ -456,7 +526,7 @@ constexpr int wg_per_cu(int D, int NW, bool QO) {
 template <int D, bool CAUSAL, int NW, bool FQ, bool QO = false>
 __global__ __launch_bounds__(64 * NW, wg_per_cu(D, NW, QO)) void attn_pipe_kernel(
     const int8_t* __restrict__ q8, const float* __restrict__ qs, int64_t Qpad,
-    const _Float16* __restrict__ qin, int qblk, _Float16* __restrict__ out, Act aq, Seqs seqs,
+    const _Float16* __restrict__ qin, int qmode, _Float16* __restrict__ out, Act aq, Seqs seqs,
     int Hq, int Hkv, int nseq, int xcd_map, float qk_log2, const char* __restrict__ tiles,
     int64_t Ppad, const int32_t* __restrict__ ochan) {
   static_assert(!QO || FQ, "the outlier channels' Q values come from the fused Q path");
@@ -524,7 +594,7 @@ __global__ __launch_bounds__(64 * NW, wg_per_cu(D, NW, QO)) void attn_pipe_kerne
   float qsc;
   v8h qo;  // QO: the row's values at the outlier slots 8 hh .. 8 hh + 7
   if constexpr (FQ) {
-    const float sq = quantize_own_q<D, QO>(qin, aq, start, h, qi, L, hh, qblk,
+    const float sq = quantize_own_q<D, QO>(qin, aq, start, h, qi, L, hh, qmode,
                                            ochan + ((int64_t)s * Hkv + g) * QO_MAX, qf, qo);
     qsc = QO ? sq * qk_log2 : fmaxf(sq * qk_log2, FLT_MIN);
   } else {
@@ -992,7 +1062,8 @@ static hipError_t attn_d(const FwdGeom& g, const WsPlan& p, const void* ws, hipS
   }
   kern<<<dim3((unsigned)blocks), dim3(64 * NW), 0, stream>>>(
       reinterpret_cast<const int8_t*>(w + p.off_q8), reinterpret_cast<const float*>(w + p.off_qs),
-      p.Qpad, static_cast<const _Float16*>(g.q), g.qblk, static_cast<_Float16*>(g.out),
+      p.Qpad, static_cast<const _Float16*>(g.q), g.qblk | (g.rot ? 2 : 0),
+      static_cast<_Float16*>(g.out),
       act_of(g, g.Hq), sq, g.Hq, g.Hkv, g.nseq, xcd_map, qk_log2, w + p.off_tiles, p.Ppad,
       reinterpret_cast<const int32_t*>(w + p.off_ochan));
   return hipGetLastError();

@@ -197,7 +197,7 @@ static i8a_status run_phases(const FwdGeom& g, int phases, void* ws, size_t ws_b
   // Q quantized inside the attention kernel where it supports the variant: the same
   // codes and scales as the Q preparation, without their round trip through memory.
   FwdGeom gf = g;
-  if ((phases & PH_Q) && (phases & PH_ATTN) && !g.rot) {
+  if ((phases & PH_Q) && (phases & PH_ATTN)) {
     gf.fuse_q = 1;
     phases &= ~PH_Q;
   }

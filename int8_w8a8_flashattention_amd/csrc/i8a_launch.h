@@ -75,8 +75,8 @@ struct FwdGeom {
   int vch;  // V quantized per channel over each sequence's tokens (else per token)
   int qblk = 0;  // Q quantized with one scale per 32-row block (else per row)
   int qout = 0;  // Q outlier channels detected and multiplied in fp16 (D <= 128)
-  // The attention kernel quantizes Q itself from q (no Q preparation pass); only for
-  // unrotated rows and D <= 128.
+  // The attention kernel quantizes (and with rot rotates) Q itself from q: no Q
+  // preparation pass.
   int fuse_q = 0;
 };
 

@@ -1,4 +1,4 @@
-"""GPU: the forward's attention kernel quantizes Q itself (for unrotated rows, every head dim).
+"""GPU: the forward's attention kernel quantizes (and, with the rotation, rotates) Q itself.
 
 Its codes and scales follow the same row rule as the Q preparation pass, so the output
 must equal, bit for bit, that of the staged path: K/V and Q prepared into a workspace
@@ -41,11 +41,16 @@ def staged(q, k, v, causal, flags):
     ws = torch.empty(i8.attn_int8_workspace_bytes(B, Hq, Hkv, S, D), dtype=torch.uint8,
                      device=q.device)
     i8.attn_int8_debug_qk(q, k, v, 0, 0, 0, 1, 0, 1, workspace=ws, flags=flags)
-    return i8.attn_int8_attend(ws, B, Hq, Hkv, S, D, causal)
+    # The attention phase takes no flags: rotated rows carry H H^T = D I, the forward's
+    # extra factor 1/D (a power of two, so fp32(1/sqrt(D)) / D is exact), given here
+    # through the softmax scale.
+    scale = float(np.float32(1.0 / np.sqrt(D))) / D if flags & i8.FWD_HADAMARD else None
+    return i8.attn_int8_attend(ws, B, Hq, Hkv, S, D, causal, softmax_scale=scale)
 
 
 @pytest.mark.parametrize("flags", [0, i8.FWD_Q_PER_BLOCK, i8.FWD_V_PER_CHANNEL,
-                                   i8.FWD_V_PER_CHANNEL | i8.FWD_Q_PER_BLOCK])
+                                   i8.FWD_V_PER_CHANNEL | i8.FWD_Q_PER_BLOCK, i8.FWD_HADAMARD,
+                                   i8.FWD_HADAMARD | i8.FWD_Q_PER_BLOCK | i8.FWD_V_PER_CHANNEL])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("D", [32, 64, 128, 256])
 def test_fused_q_equals_prepared_q(D, causal, flags):
