@@ -183,6 +183,30 @@ __global__ __launch_bounds__(256) void prep_ksum_kernel(const _Float16* __restri
 // the lower channel.  Leaves in sh.slot[d] the channel's position in the increasing
 // list of kept channels (-1 if not kept) and, if ochan_out is given, writes the list
 // padded with -1.  Every thread of the 256-thread workgroup must call it.
+// This thread's maximum over the partials r, r + 256/D, ... (< np <= MAX_PARTS) of
+// channel d (pp points at the partials' channel d, rows D apart): every load issued at
+// once, CH at a time, so the reduction costs a few memory latencies rather than one per
+// partial.
+template <int D>
+__device__ __forceinline__ float partial_max(const float* __restrict__ pp, int np, int r) {
+  constexpr int TPC = 256 / D;  // threads per channel
+  constexpr int MAXK = (MAX_PARTS + TPC - 1) / TPC;
+  constexpr int CH = MAXK < 16 ? MAXK : 16;
+  float mx = 0.0f;
+#pragma unroll
+  for (int k0 = 0; k0 < MAXK; k0 += CH) {
+    float v[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int i = r + (k0 + k) * TPC;
+      v[k] = i < np ? pp[(int64_t)i * D] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < CH; ++k) mx = fmaxf(mx, v[k]);
+  }
+  return mx;
+}
+
 template <int D>
 struct QoShared {
   float amax[D];
@@ -198,22 +222,7 @@ __device__ __forceinline__ void select_outliers(const float* __restrict__ pp, in
                                                 QoShared<D>& sh, int32_t* __restrict__ ochan_out) {
   constexpr int TPC = 256 / D;  // threads per channel
   const int d = threadIdx.x % D, r = threadIdx.x / D;
-  // Every thread issues all its loads of the partials (np <= MAX_PARTS) at once, CH at a
-  // time, so the reduction costs a few memory latencies rather than one per partial.
-  constexpr int MAXK = (MAX_PARTS + TPC - 1) / TPC;
-  constexpr int CH = MAXK < 16 ? MAXK : 16;
-  float mx = 0.0f;
-#pragma unroll
-  for (int k0 = 0; k0 < MAXK; k0 += CH) {
-    float v[CH];
-#pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const int i = r + (k0 + k) * TPC;
-      v[k] = i < np ? pp[(int64_t)i * D + d] : 0.0f;
-    }
-#pragma unroll
-    for (int k = 0; k < CH; ++k) mx = fmaxf(mx, v[k]);
-  }
+  float mx = partial_max<D>(pp + d, np, r);
   sh.red[threadIdx.x] = mx;
   __syncthreads();
   if (r == 0) {
@@ -292,15 +301,31 @@ __device__ __forceinline__ void prep_v_body(const _Float16* __restrict__ v, cons
   const int64_t pbase = Seqs::pstart(s, start);
   const int lc = threadIdx.x % G, rsub = threadIdx.x / G;
 
+  // A tile's V rows (zero past the sequence end).  The first tile's are requested before
+  // the channel maxima are reduced (they do not depend on them), so the two memory
+  // latencies overlap.
+  auto load_rows = [&](int t0, v8h (&vr)[NP]) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int t = t0 + i * RPP + rsub;
+      if (t < L) {
+        vr[i] = *reinterpret_cast<const v8h*>(v + act.off(start, g, t) + lc * 8);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vr[i][j] = (_Float16)0.0f;
+      }
+    }
+  };
+  v8h vr[NP];
+  load_rows(tile_lo * TK, vr);
+
   if constexpr (VCH) {
     // The channel maxima of the whole sequence from the launch-1 partials (a max is
     // exact in any order), then each channel's scale and reciprocal.
     constexpr int TPC = 256 / D;
     const int d = threadIdx.x % D, r = threadIdx.x / D;
     const int np = (nt + tpw - 1) / tpw;
-    const float* pp = vpart + ((int64_t)s * Hkv + g) * npart * D + d;
-    float mx = 0.0f;
-    for (int i = r; i < np; i += TPC) mx = fmaxf(mx, pp[(int64_t)i * D]);
+    float mx = partial_max<D>(vpart + ((int64_t)s * Hkv + g) * npart * D + d, np, r);
     sh.red[threadIdx.x] = mx;
     __syncthreads();
     if (r == 0) {
@@ -314,17 +339,7 @@ __device__ __forceinline__ void prep_v_body(const _Float16* __restrict__ v, cons
 
   for (int tt = tile_lo; tt < tile_hi; ++tt) {
     const int t0 = tt * TK;
-    v8h vr[NP];
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int t = t0 + i * RPP + rsub;
-      if (t < L) {
-        vr[i] = *reinterpret_cast<const v8h*>(v + act.off(start, g, t) + lc * 8);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) vr[i][j] = (_Float16)0.0f;
-      }
-    }
+    if (tt > tile_lo) load_rows(t0, vr);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int n = i * RPP + rsub, t = t0 + n;
