@@ -520,7 +520,7 @@ constexpr int wg_per_cu(int D, int NW, bool QO) {
 // QO (with FQ): Q outlier channels.  The kv group's channels (ochan) are left out of
 // the int8 Q rows, and their fp16 products come from one 32x32x16 fp16 MFMA per
 // 32-key block with the tile's fp16 K values of those channels:
-//   t = f32(S^T) * sk_j * qsc + So^T * qk_log2 - M
+//   t = f32(S^T) * c_j + So^T * qk_log2 - M,   c_j = sk_j * qsc
 // (qsc = sq * qk_log2, with sq replaced by 2^-60 where the int8 part is all zero: its
 // scores are 0 there).
 template <int D, bool CAUSAL, int NW, bool FQ, bool QO = false>
@@ -684,28 +684,28 @@ __global__ __launch_bounds__(64 * NW, wg_per_cu(D, NW, QO)) void attn_pipe_kerne
 
   // One iteration as a fixed schedule of slots, one MFMA each, fenced with scheduling
   // barriers so the compiler keeps the order:
-  //   MFMAs: the 2 NKB score products of the next tile, then per key group kg the row
-  //          sum and the NKB P.V products of this tile;
+  //   MFMAs: the 2 NKB score products of the next tile (with QO its two outlier
+  //          products), its key-scale product, then per key group kg the row sum and
+  //          the NKB P.V products of this tile;
   //   LDS:   every MFMA operand is read PF slots ahead of its MFMA (a ring of PF + 1
   //          fragments), the next tile's key scales two slots ahead of their first use;
   //   VMEM:  this wave's share of the copy of a later tile, one instruction every few
   //          slots;
   //   VALU:  the exponentials of this tile (item i: FMA and exp2 of score i, the fp16
   //          pack after every odd i) over the slots before the third row-sum MFMA that
-  //          needs them, the conversion of the next tile's scores (item i: cvt and
-  //          key-scale multiply, with MASK the causal/tail select, a max3 after every odd
-  //          i) from the slot its scores are ready, and the row max exchange and rescale
-  //          decision in the last slot.
+  //          needs them, the conversion of the next tile's scores (item i: cvt and one
+  //          FMA against the key-scale product and the running max, with QO one more
+  //          for the outlier product, with MASK the causal/tail select, a max3 after
+  //          every odd i) from the slot its scores and the key-scale product are ready,
+  //          and the row max exchange and rescale decision in the last slot.
   // Returns the next tile's row max in log2 units; upd_any: some row needs a rescale.
   auto pipe_step = [&](const char* cur, const char* nxt, const char* dsrc, char* dstage,
                        auto MASK, int last, bool& upd_any) -> float {
     constexpr bool masked = decltype(MASK)::value;
     constexpr int NQK = 2 * NKB;                // int8 score MFMAs
     constexpr int NSC = NQK + (QO ? 2 : 0);     // score MFMAs (QO: the outlier products)
-    // The key-scale product c = sk * qsc (not with QO: there its 32 result registers would
-    // not fit beside the outlier products', and the key scales come from LDS instead).
-    constexpr int XC = QO ? -1 : NSC;
-    constexpr int NPV = NSC + (QO ? 0 : 1);     // first row-sum / P.V slot
+    constexpr int XC = NSC;                     // the key-scale product c = sk * qsc
+    constexpr int NPV = NSC + 1;                // first row-sum / P.V slot
     constexpr int NM = NPV + 4 * (NKB + 1);     // all MFMAs of the iteration
     constexpr int PF = 3;                       // operand prefetch distance, in MFMAs
     constexpr int E_END = NPV + 2 * (NKB + 1);  // exponentials end before row sum 2
@@ -732,7 +732,6 @@ __global__ __launch_bounds__(64 * NW, wg_per_cu(D, NW, QO)) void attn_pipe_kerne
     v16f so[2];
     v32f cn;          // c = sk * qsc of the next tile
     float skn = 0.0f;  // the next tile's key scale of key `lane`
-    v4f skv[8];       // QO: the next tile's key scales in register order
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -764,21 +763,8 @@ __global__ __launch_bounds__(64 * NW, wg_per_cu(D, NW, QO)) void attn_pipe_kerne
       }
       // operand PF slots ahead
       if (x + PF < NM && has_operand(x + PF)) fr[(x + PF) % (PF + 1)] = operand(x + PF);
-      // the next tile's key scale of key `lane`, for its key-scale product; with QO the
-      // scale groups gsk (keys of registers 4 (gsk % 4) .. of block gsk / 4) two slots
-      // before the conversion item 4 gsk that first needs them
-      if constexpr (!QO) {
-        if (x == (XC >= PF ? XC - PF : 0)) skn = skl[lane];
-      } else {
-#pragma unroll
-        for (int gsk = 0; gsk < 8; ++gsk) {
-          const int first = C_BEG + (4 * gsk * NC) / 32;
-          const int at = first - 2 < 0 ? 0 : first - 2;
-          if (at == x)
-            skv[gsk] =
-                *reinterpret_cast<const v4f*>(skl + 32 * (gsk / 4) + 8 * (gsk % 4) + 4 * hh);
-        }
-      }
+      // the next tile's key scale of key `lane`, for its key-scale product
+      if (x == (XC >= PF ? XC - PF : 0)) skn = skl[lane];
       // this wave's rounds of the copy: round r at slot 2 + r (NM - 4) / R
 #pragma unroll
       for (int r = 0; r < DM::ROUNDS; ++r)
@@ -812,7 +798,7 @@ __global__ __launch_bounds__(64 * NW, wg_per_cu(D, NW, QO)) void attn_pipe_kerne
           if (i < i0 || i >= i1) continue;
           const int nb = i >> 4;
           if constexpr (QO)
-            t[i] = __builtin_fmaf((float)sn[nb][i & 15] * skv[i >> 2][i & 3], qsc,
+            t[i] = __builtin_fmaf((float)sn[nb][i & 15], cn[i],
                                   __builtin_fmaf(so[nb][i & 15], qk_log2, -mrun));
           else
             t[i] = __builtin_fmaf((float)sn[nb][i & 15], cn[i], -mrun);
