@@ -13,7 +13,8 @@ The method it defines comes from the "SuperL8" README (the page titled
 * *Attention kernels* table, row ``attn_varlen_fwd``: variable-length
   (ragged, non-tile-multiple) prefill.
 * *Attention kernels* table, row ``attn_decode``: split-KV decode with an int8
-  KV cache, in its int8-V and fp16-V variants (one query token per sequence).
+  KV cache, in its int8-V and fp16-V variants (one query token per sequence), over
+  a cache that grows by appended tokens (``attn_int8_decode_cache``).
 * *Attention kernels* table, row ``attn_bwd``, and the *Infrastructure* table's
   autograd row: the backward of the differentiable int8 attention (gradient of exact
   attention, the quantization taken as the identity).
@@ -58,6 +59,8 @@ from .attn_ref import (  # noqa: F401
     attn_core,
     attn_int8_fwd,
     attn_int8_decode,
+    attn_int8_decode_cache,
+    kvcache_quantize,
     attn_int8_varlen_fwd,
     attn_exact,
 )

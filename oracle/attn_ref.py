@@ -83,6 +83,17 @@ R19 Q outlier detection (the *Quantization* table's "Per-row int8" row: symmetri
     without the mean (a per-row constant of the logits), and the logits become
     ``(S32 * sq_i * sk_j + sum_{d in set} q_id * k_jd) * softmax_scale``.
 
+R20 A growing decode cache (the *Attention kernels* table's ``attn_decode`` row serves
+    generation, where every step adds a token to each sequence; the page gives no
+    rule for the K-smoothing mean of a cache that grows).  The plainest reading:
+    the mean is taken once, over the tokens the cache is filled with (R5), and
+    every later K row is quantized against that stored mean (``fp32(k) - mean``,
+    then R2/R3), V rows as in R12.  Subtracting any fixed per-channel vector from
+    K adds a per-query constant to the logits, so exact attention does not depend
+    on which mean is stored; re-taking the mean would requantize the whole cache
+    at every step.  A sequence attends its first ``lens[b]`` cached tokens; with
+    none, its output row is zero (the empty sum).
+
 Quantization steps are emulated op for op in numpy float32, which is IEEE
 single precision with round-to-nearest-even; everything after the integer
 codes is exact or fp64.
@@ -416,6 +427,58 @@ def attn_int8_decode(q16, k16, v16, softmax_scale=None, v_format="int8"):
             g = h // G
             out[b, h] = attn_core(q8[b, h][None], sq[b, h][None], k8[b, g], sk[b, g],
                                   v8[b, g], sv[b, g], sm, False)[0]
+    return out
+
+
+def kvcache_quantize(k16, v16, n_fill, v_format="int8"):
+    """The contents of a decode cache (R12, R20): fp16 ``k/v[B,Hkv,S,D]`` hold every
+    token the cache holds, tokens ``[0, n_fill)`` filled and the later ones appended.
+
+    Returns ``(k8, sk, v8, sv, mean)``: K rows quantized against the mean of the
+    filled tokens' K (R5), V rows per token (R2; ``v_format="fp16"``: the fp16
+    values as fp64 "codes" with unit scales), and that fp32 mean ``[B, Hkv, D]``.
+    """
+    if v_format not in ("int8", "fp16"):
+        raise ValueError("v_format must be 'int8' or 'fp16'")
+    S = k16.shape[2]
+    if not 1 <= n_fill <= S:
+        raise ValueError("need 1 <= n_fill <= S")
+    m = kmean(k16[:, :, :n_fill])
+    k8, sk = quant_rows(k16.astype(np.float32) - m[..., None, :])
+    if v_format == "int8":
+        v8, sv = quant_rows(v16.astype(np.float32), V_SCALE_BITS)
+    else:
+        v8, sv = v16.astype(np.float64), np.ones(v16.shape[:3], dtype=np.float32)
+    return k8, sk, v8, sv, m
+
+
+def attn_int8_decode_cache(q16, k16, v16, n_fill, lens, softmax_scale=None, v_format="int8"):
+    """Decode against a grown cache (R12, R20): fp16 ``q[B,Hq,D]``, the cache of
+    :func:`kvcache_quantize` over ``k/v[B,Hkv,S,D]`` with ``n_fill`` filled tokens, and
+    ``lens[B]`` (0 <= lens[b] <= S): sequence b's query rows attend its cached tokens
+    ``[0, lens[b])``.  Returns fp64 ``[B, Hq, D]``; rows of a sequence with no token
+    are zero.
+    """
+    B, Hq, D = q16.shape
+    Hkv, S = k16.shape[1], k16.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    lens = np.asarray(lens, dtype=np.int64)
+    if lens.shape != (B,) or (lens < 0).any() or (lens > S).any():
+        raise ValueError("need lens[B] with 0 <= lens[b] <= S")
+    G = Hq // Hkv
+    sm = default_softmax_scale(D) if softmax_scale is None else np.float32(softmax_scale)
+    q8, sq = quant_rows(q16.astype(np.float32))
+    k8, sk, v8, sv, _ = kvcache_quantize(k16, v16, n_fill, v_format)
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        for h in range(Hq):
+            g = h // G
+            out[b, h] = attn_core(q8[b, h][None], sq[b, h][None], k8[b, g, :n], sk[b, g, :n],
+                                  v8[b, g, :n], sv[b, g, :n], sm, False)[0]
     return out
 
 

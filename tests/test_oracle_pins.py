@@ -458,6 +458,74 @@ def test_decode_fp16_v_zero_query_gives_exact_mean():
     np.testing.assert_allclose(out, np.repeat(want, 3, axis=1), rtol=1e-13, atol=1e-15)
 
 
+# ------------------------------------------------- decode over a grown cache (R20)
+
+def test_cache_appended_rows_quantize_against_the_filled_mean():
+    # Rows past n_fill are appended: K against the mean of the filled tokens only (exact
+    # rational rule), V per token; a copy of a filled token gets that token's codes.
+    g = rng(60)
+    B, Hkv, S, D, n_fill = 2, 2, 40, 32, 25
+    k = (g.standard_normal((B, Hkv, S, D)) + g.uniform(-3, 3, (1, 1, 1, D))).astype(np.float16)
+    v = g.standard_normal((B, Hkv, S, D)).astype(np.float16)
+    k[:, :, 30] = k[:, :, 7]
+    v[:, :, 30] = v[:, :, 7]
+    k8, sk, v8, sv, m = oracle.kvcache_quantize(k, v, n_fill)
+    np.testing.assert_array_equal(m, oracle.kmean(k[:, :, :n_fill]))
+    assert not np.array_equal(m, oracle.kmean(k))
+    for b, h, t in [(0, 0, 26), (1, 1, 39), (0, 1, 30), (1, 0, 3)]:
+        s_k, c_k = exact_quant_row(k[b, h, t].astype(np.float32) - m[b, h])
+        assert Fraction(float(sk[b, h, t])) == s_k and list(k8[b, h, t]) == c_k
+        s_v, c_v = exact_quant_row(v[b, h, t].astype(np.float32), bits=oracle.V_SCALE_BITS)
+        assert Fraction(float(sv[b, h, t])) == s_v and list(v8[b, h, t]) == c_v
+    assert np.array_equal(k8[:, :, 30], k8[:, :, 7]) and np.array_equal(sk[:, :, 30], sk[:, :, 7])
+    assert np.array_equal(v8[:, :, 30], v8[:, :, 7]) and np.array_equal(sv[:, :, 30], sv[:, :, 7])
+
+
+@pytest.mark.parametrize("v_format", ["int8", "fp16"])
+def test_cache_decode_equals_library_attention_on_each_prefix(v_format):
+    w = workloads.dense(61, 3, 8, 2, 70, 64, False, k_offset=1.5)
+    q1 = w.q[:, :, 9]
+    n_fill, lens = 33, np.array([70, 1, 48])
+    out = oracle.attn_int8_decode_cache(q1, w.k, w.v, n_fill, lens, v_format=v_format)
+    q8, sq = oracle.quant_rows(q1.astype(np.float32))
+    k8, sk, v8, sv, _ = oracle.kvcache_quantize(w.k, w.v, n_fill, v_format)
+    qh = dequant(q8, sq)[:, :, None]
+    kh = np.repeat(dequant(k8, sk), 4, axis=1)
+    vh = np.repeat(dequant(v8, sv) if v_format == "int8" else w.v.astype(np.float64), 4, axis=1)
+    for b, n in enumerate(lens):
+        ref = sdpa64(qh[b:b + 1], kh[b:b + 1, :, :n], vh[b:b + 1, :, :n], False,
+                     oracle.default_softmax_scale(64))[0, :, 0]
+        np.testing.assert_allclose(out[b], ref, rtol=1e-11, atol=1e-12)
+    # one cached token: softmax weight 1, the output is that token's value row
+    np.testing.assert_array_equal(out[1], np.repeat(vh[1, ::4, 0], 4, axis=0))
+
+
+def test_cache_decode_full_fill_equals_decode_and_empty_rows_are_zero():
+    w = workloads.dense(62, 2, 6, 3, 45, 32, False, k_offset=-2.0)
+    q1 = w.q[:, :, 0]
+    a = oracle.attn_int8_decode_cache(q1, w.k, w.v, 45, [45, 45])
+    np.testing.assert_allclose(a, oracle.attn_int8_decode(q1, w.k, w.v), rtol=1e-13, atol=1e-15)
+    z = oracle.attn_int8_decode_cache(q1, w.k, w.v, 45, [0, 45])
+    assert not z[0].any() and np.array_equal(z[1], a[1])
+
+
+def test_cache_decode_mean_choice_stays_within_quantization_error():
+    # Exact attention does not depend on which per-channel vector is subtracted from K;
+    # the stored mean (here of a third of the tokens, or of all of them) only moves the
+    # int8 rounding, so both stay within the quantization error of exact attention.
+    w = workloads.dense(63, 2, 4, 2, 96, 128, False, k_offset=3.0)
+    q1 = w.q[:, :, 4]
+    lens = np.array([96, 80])
+    exact = np.stack([oracle.attn_exact(q1[b:b + 1, :, None], w.k[b:b + 1, :, :n],
+                                        w.v[b:b + 1, :, :n], False)[0, :, 0]
+                      for b, n in enumerate(lens)])
+    for n_fill in (32, 96):
+        out = oracle.attn_int8_decode_cache(q1, w.k, w.v, n_fill, lens)
+        rel = np.linalg.norm(out - exact) / np.linalg.norm(exact)
+        assert rel < 2e-2, (n_fill, rel)
+
+
+
 # ---------------------------------------------------------------- Hadamard rotation (R13)
 
 def test_fwht_butterfly_order_worked_example():
