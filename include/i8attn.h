@@ -357,6 +357,55 @@ i8a_status attn_int8_decode(const void* q, void* out, int32_t B, int32_t Hq, int
                             size_t workspace_bytes, void* stream);
 
 /*
+ * A cache that grows (SuperL8 README, Attention kernels table, row attn_decode: decode
+ * serves generation, which adds a token to every sequence at each step; the page gives
+ * no rule for the K-smoothing mean of a growing cache).  The mean is taken once, over
+ * the tokens a cache is filled with, and every appended K row is quantized against it;
+ * the stored mean only moves int8 rounding, since subtracting any fixed vector from K
+ * adds a per-query constant to the logits.  S is the cache's capacity in tokens.
+ *
+ * attn_int8_kvcache_fill_prefix - attn_int8_kvcache_fill of the first S_fill tokens
+ * (1 <= S_fill <= S) of a cache of capacity S: k, v fp16 [B, Hkv, S_fill, D], the mean
+ * over those tokens.  Slots S_fill .. S-1 hold zero codes, scales and values until
+ * appended (a decode reaching them attends zero keys and values).
+ * attn_int8_kvcache_fill is the case S_fill = S.
+ */
+i8a_status attn_int8_kvcache_fill_prefix(const void* k, const void* v, int32_t B, int32_t Hkv,
+                                         int32_t S_fill, int32_t S, int32_t D, int32_t v_format,
+                                         void* cache, size_t cache_bytes, void* stream);
+
+/*
+ * attn_int8_kvcache_append - write n_new tokens per (batch, kv head) into a filled cache.
+ *   k, v   fp16 [B, Hkv, n_new, D] on the device, 16-byte aligned: token i of sequence b
+ *          goes to slot pos[b] + i.
+ *   pos    device int32 [B]: each sequence's first slot (usually its current length).
+ *          A token whose slot lies outside [0, S) is not written (nothing else is
+ *          touched); pos is read on the device, so the call cannot report it.
+ *   0 <= n_new <= S (0: nothing is enqueued, and k, v, pos may be NULL).
+ * K rows are quantized against the kv head's stored mean, V rows as the fill does
+ * (per-token int8 with the 4-bit scale, or fp16); a slot that is written again is
+ * overwritten.  Appends and decodes on one stream run in order; concurrent calls on
+ * one cache must not write the same slots.
+ */
+i8a_status attn_int8_kvcache_append(const void* k, const void* v, int32_t B, int32_t Hkv,
+                                    int32_t n_new, const int32_t* pos, int32_t S, int32_t D,
+                                    int32_t v_format, void* cache, size_t cache_bytes,
+                                    void* stream);
+
+/*
+ * attn_int8_decode_lens - attn_int8_decode where sequence b attends only its first
+ * lens[b] cached tokens (slots 0 .. lens[b]-1, each filled or appended).
+ *   lens   device int32 [B], 4-byte aligned; values are clamped to [0, S].  A sequence
+ *          with no token gets a zero output row.
+ * Every other argument as for attn_int8_decode (the same workspace size).  With every
+ * lens[b] = S it computes what attn_int8_decode computes, bit for bit.
+ */
+i8a_status attn_int8_decode_lens(const void* q, void* out, int32_t B, int32_t Hq, int32_t Hkv,
+                                 int32_t S, int32_t D, float softmax_scale, int32_t v_format,
+                                 const int32_t* lens, const void* cache, size_t cache_bytes,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Backward (SuperL8 README, Attention kernels table, row attn_bwd: a gradient-checked
  * backward pass on full fp16 state; Infrastructure table, autograd row: int8 attention
  * made differentiable).  The quantization of the forward has zero derivative almost

@@ -39,6 +39,7 @@ __all__ = [
     "attn_int8_workspace_bytes", "attn_int8_varlen_workspace_bytes", "library_path",
     "load_library", "SCALE_FP32", "SCALE_V4", "HEAD_DIMS", "attn_int8_kvcache_bytes",
     "attn_int8_kvcache_fill", "attn_int8_decode_workspace_bytes", "attn_int8_decode",
+    "attn_int8_kvcache_fill_prefix", "attn_int8_kvcache_append", "attn_int8_decode_lens", "KVCache",
     "VCACHE_INT8", "VCACHE_FP16", "attn_bwd", "attn_bwd_workspace_bytes", "Int8Attention",
     "int8_attention",
 ]
@@ -86,6 +87,11 @@ _SIGS = {
                                                                      _c_vp]),
     "attn_int8_kvcache_bytes": (_c_sz, [_c_i32] * 5),
     "attn_int8_kvcache_fill": (_c_i32, [_c_vp] * 2 + [_c_i32] * 5 + [_c_vp, _c_sz, _c_vp]),
+    "attn_int8_kvcache_fill_prefix": (_c_i32, [_c_vp] * 2 + [_c_i32] * 6 + [_c_vp, _c_sz, _c_vp]),
+    "attn_int8_kvcache_append": (_c_i32, [_c_vp] * 2 + [_c_i32] * 3 + [_c_vp] + [_c_i32] * 3
+                                 + [_c_vp, _c_sz, _c_vp]),
+    "attn_int8_decode_lens": (_c_i32, [_c_vp] * 2 + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_vp,
+                                                                    _c_sz, _c_vp, _c_sz, _c_vp]),
     "attn_int8_decode_workspace_bytes": (_c_sz, [_c_i32] * 6),
     "attn_int8_decode": (_c_i32, [_c_vp] * 2 + [_c_i32] * 5 + [_c_f32, _c_i32, _c_vp, _c_sz,
                                                                _c_vp, _c_sz, _c_vp]),
@@ -541,9 +547,68 @@ def attn_int8_kvcache_fill(k, v, v_format="int8", cache=None):
     return KVCache(buf, B, Hkv, S, D, v_format)
 
 
-def attn_int8_decode(q, cache, softmax_scale=None, out=None, workspace=None):
+def attn_int8_kvcache_fill_prefix(k, v, S, v_format="int8", cache=None):
+    """A decode cache of capacity ``S`` tokens whose first ``k.shape[2]`` slots are filled
+    from fp16 ``k, v [B,Hkv,S_fill,D]`` (the K-smoothing mean over those tokens); later
+    slots hold zeros until :func:`attn_int8_kvcache_append` writes them.  Returns a
+    :class:`KVCache`."""
+    for n, t in (("k", k), ("v", v)):
+        _need_gpu_fp16(n, t, 4)
+    if k.shape != v.shape or k.device != v.device:
+        raise ValueError("k and v must match")
+    B, Hkv, S_fill, D = k.shape
+    vf = _vformat(v_format)
+    lib = load_library()
+    nbytes = lib.attn_int8_kvcache_bytes(B, Hkv, S, D, vf)
+    if nbytes == 0:
+        raise ValueError(f"invalid cache sizes B={B} Hkv={Hkv} S={S} D={D}")
+    buf = _workspace(cache, nbytes, k.device)
+    with torch.cuda.device(k.device):
+        st = lib.attn_int8_kvcache_fill_prefix(_ptr(k), _ptr(v), B, Hkv, S_fill, S, D, vf,
+                                               _ptr(buf), buf.numel() * buf.element_size(),
+                                               _stream(k.device))
+    _check(st, "attn_int8_kvcache_fill_prefix")
+    return KVCache(buf, B, Hkv, S, D, v_format)
+
+
+def _need_gpu_i32(name, t, B):
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == torch.int32
+            and t.is_contiguous() and tuple(t.shape) == (B,)):
+        raise ValueError(f"{name} must be a contiguous int32 CUDA tensor of shape ({B},)")
+
+
+def attn_int8_kvcache_append(cache, k, v, pos):
+    """Append fp16 ``k, v [B,Hkv,n,D]`` to a :class:`KVCache`: token i of sequence b goes to
+    slot ``pos[b] + i`` (``pos`` an int32 CUDA tensor ``[B]``); slots outside the capacity
+    are not written."""
+    if not isinstance(cache, KVCache):
+        raise ValueError("cache must come from attn_int8_kvcache_fill or _fill_prefix")
+    for n, t in (("k", k), ("v", v)):
+        _need_gpu_fp16(n, t, 4)
+    if k.shape != v.shape or k.device != v.device or cache.buf.device != k.device:
+        raise ValueError("k and v must match each other and the cache's device")
+    B, Hkv, n, D = k.shape
+    if (B, Hkv, D) != (cache.B, cache.Hkv, cache.D):
+        raise ValueError("k/v do not match the cache")
+    _need_gpu_i32("pos", pos, B)
+    lib = load_library()
+    with torch.cuda.device(k.device):
+        st = lib.attn_int8_kvcache_append(_ptr(k), _ptr(v), B, Hkv, n, _ptr(pos), cache.S, D,
+                                          _vformat(cache.v_format), _ptr(cache.buf),
+                                          cache.nbytes, _stream(k.device))
+    _check(st, "attn_int8_kvcache_append")
+
+
+def attn_int8_decode_lens(q, cache, lens, softmax_scale=None, out=None, workspace=None):
+    """:func:`attn_int8_decode` where sequence b attends its first ``lens[b]`` cached
+    tokens (``lens`` an int32 CUDA tensor ``[B]``; a sequence with none gets zeros)."""
+    return attn_int8_decode(q, cache, softmax_scale, out, workspace, lens=lens)
+
+
+def attn_int8_decode(q, cache, softmax_scale=None, out=None, workspace=None, lens=None):
     """One decode step: fp16 ``q [B,Hq,D]`` (the new token's query rows) against a
-    :class:`KVCache`; returns fp16 ``out [B,Hq,D]``."""
+    :class:`KVCache`; returns fp16 ``out [B,Hq,D]``.  With ``lens`` (int32 CUDA tensor
+    ``[B]``) sequence b attends only its first ``lens[b]`` cached tokens."""
     _need_gpu_fp16("q", q, 3)
     B, Hq, D = q.shape
     if not isinstance(cache, KVCache):
@@ -565,10 +630,17 @@ def attn_int8_decode(q, cache, softmax_scale=None, out=None, workspace=None):
     ws = _workspace(workspace, nbytes, q.device) if nbytes else workspace
     wsz = ws.numel() * ws.element_size() if ws is not None else 0
     with torch.cuda.device(q.device):
-        st = lib.attn_int8_decode(_ptr(q), _ptr(out), B, Hq, Hkv, S, D, _scale(softmax_scale, D),
-                                  vf, _ptr(cache.buf), cache.nbytes, _ptr(ws), wsz,
-                                  _stream(q.device))
-    _check(st, "attn_int8_decode")
+        if lens is None:
+            st = lib.attn_int8_decode(_ptr(q), _ptr(out), B, Hq, Hkv, S, D,
+                                      _scale(softmax_scale, D), vf, _ptr(cache.buf),
+                                      cache.nbytes, _ptr(ws), wsz, _stream(q.device))
+        else:
+            _need_gpu_i32("lens", lens, B)
+            st = lib.attn_int8_decode_lens(_ptr(q), _ptr(out), B, Hq, Hkv, S, D,
+                                           _scale(softmax_scale, D), vf, _ptr(lens),
+                                           _ptr(cache.buf), cache.nbytes, _ptr(ws), wsz,
+                                           _stream(q.device))
+    _check(st, "attn_int8_decode" if lens is None else "attn_int8_decode_lens")
     return out
 
 

@@ -488,9 +488,45 @@ i8a_status attn_int8_kvcache_fill(const void* k, const void* v, int32_t B, int32
   size_t need;
   i8a_status st = kvc_check(B, Hkv, S, D, v_format, cache, cache_bytes, &need);
   if (st != I8A_OK) return st;
-  hipError_t e = launch_kvcache_fill(k, v, plan_kvcache(B, Hkv, S, D, v_format), cache,
+  hipError_t e = launch_kvcache_fill(k, v, plan_kvcache(B, Hkv, S, D, v_format), S, cache,
                                      (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "cache fill launch");
+  return I8A_OK;
+}
+
+i8a_status attn_int8_kvcache_fill_prefix(const void* k, const void* v, int32_t B, int32_t Hkv,
+                                         int32_t S_fill, int32_t S, int32_t D, int32_t v_format,
+                                         void* cache, size_t cache_bytes, void* stream) {
+  if (!k || !v) return fail(I8A_ERR_INVALID_ARG, "null k/v pointer");
+  if (!aligned(k, 16) || !aligned(v, 16))
+    return fail(I8A_ERR_INVALID_ARG, "k/v must be 16-byte aligned");
+  size_t need;
+  i8a_status st = kvc_check(B, Hkv, S, D, v_format, cache, cache_bytes, &need);
+  if (st != I8A_OK) return st;
+  if (S_fill < 1 || S_fill > S)
+    return fail(I8A_ERR_INVALID_ARG, "need 1 <= S_fill <= S (S_fill=%d S=%d)", S_fill, S);
+  hipError_t e = launch_kvcache_fill(k, v, plan_kvcache(B, Hkv, S, D, v_format), S_fill, cache,
+                                     (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "cache fill launch");
+  return I8A_OK;
+}
+
+i8a_status attn_int8_kvcache_append(const void* k, const void* v, int32_t B, int32_t Hkv,
+                                    int32_t n_new, const int32_t* pos, int32_t S, int32_t D,
+                                    int32_t v_format, void* cache, size_t cache_bytes,
+                                    void* stream) {
+  size_t need;
+  i8a_status st = kvc_check(B, Hkv, S, D, v_format, cache, cache_bytes, &need);
+  if (st != I8A_OK) return st;
+  if (n_new < 0 || n_new > S)
+    return fail(I8A_ERR_INVALID_ARG, "need 0 <= n_new <= S (n_new=%d S=%d)", n_new, S);
+  if (n_new == 0) return I8A_OK;
+  if (!k || !v || !pos) return fail(I8A_ERR_INVALID_ARG, "null k/v/pos pointer");
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(pos, 4))
+    return fail(I8A_ERR_INVALID_ARG, "k/v must be 16-byte and pos 4-byte aligned");
+  hipError_t e = launch_kvcache_append(k, v, n_new, pos, plan_kvcache(B, Hkv, S, D, v_format),
+                                       cache, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "cache append launch");
   return I8A_OK;
 }
 
@@ -501,10 +537,10 @@ size_t attn_int8_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int3
   return plan_decode(B, Hq, Hkv, S, D, v_format).total;
 }
 
-i8a_status attn_int8_decode(const void* q, void* out, int32_t B, int32_t Hq, int32_t Hkv,
-                            int32_t S, int32_t D, float softmax_scale, int32_t v_format,
-                            const void* cache, size_t cache_bytes, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+static i8a_status decode_impl(const void* q, void* out, int32_t B, int32_t Hq, int32_t Hkv,
+                              int32_t S, int32_t D, float softmax_scale, int32_t v_format,
+                              const int32_t* lens, const void* cache, size_t cache_bytes,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !out) return fail(I8A_ERR_INVALID_ARG, "null q/out pointer");
   if (!aligned(q, 16) || !aligned(out, 16))
     return fail(I8A_ERR_INVALID_ARG, "q/out must be 16-byte aligned");
@@ -523,9 +559,27 @@ i8a_status attn_int8_decode(const void* q, void* out, int32_t B, int32_t Hq, int
   if (dp.total > 0 && (!workspace || !aligned(workspace, 256)))
     return fail(I8A_ERR_INVALID_ARG, "workspace must be non-null and 256-byte aligned");
   hipError_t e = launch_decode(q, out, Hq, softmax_scale, plan_kvcache(B, Hkv, S, D, v_format),
-                               dp, cache, workspace, (hipStream_t)stream);
+                               dp, cache, workspace, lens, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return I8A_OK;
+}
+
+i8a_status attn_int8_decode(const void* q, void* out, int32_t B, int32_t Hq, int32_t Hkv,
+                            int32_t S, int32_t D, float softmax_scale, int32_t v_format,
+                            const void* cache, size_t cache_bytes, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return decode_impl(q, out, B, Hq, Hkv, S, D, softmax_scale, v_format, nullptr, cache,
+                     cache_bytes, workspace, workspace_bytes, stream);
+}
+
+i8a_status attn_int8_decode_lens(const void* q, void* out, int32_t B, int32_t Hq, int32_t Hkv,
+                                 int32_t S, int32_t D, float softmax_scale, int32_t v_format,
+                                 const int32_t* lens, const void* cache, size_t cache_bytes,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!lens || !aligned(lens, 4))
+    return fail(I8A_ERR_INVALID_ARG, "lens must be a non-null, 4-byte aligned device array");
+  return decode_impl(q, out, B, Hq, Hkv, S, D, softmax_scale, v_format, lens, cache,
+                     cache_bytes, workspace, workspace_bytes, stream);
 }
 
 static bool bwd_sizes_ok(int32_t B, int32_t Hq, int32_t Hkv, int32_t S) {

@@ -329,13 +329,102 @@ __global__ __launch_bounds__(256) void kvc_fill_kernel(const _Float16* __restric
     fill_k<D, VF>(k, S, npart, tpw, ntd, kpart, kmean, tiles, c, bg, sh.k);
 }
 
+// Zeroes of the tiles a prefix fill leaves to appends: for every (batch, kv head), the
+// per_bg-byte tile area from byte `first` on, in 16-byte stores (a grid-stride loop
+// over all of them).  Slots that no append has written then hold zero codes, scales and
+// values, so a decode whose last tile reaches past its sequence's last appended token
+// multiplies finite numbers by the masked keys' zero weights.
+__global__ __launch_bounds__(256) void kvc_zero_kernel(char* __restrict__ tiles, int64_t per_bg,
+                                                       int64_t first, int64_t n16, int64_t total) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t bg = i / n16, j = i % n16;
+    reinterpret_cast<uint4*>(tiles + bg * per_bg + first)[j] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// ----------------------------------------------------------------------------------
+// Append: n new tokens of each (batch, kv head) (workgroup bg = b * Hkv + g) into the
+// cache slots pos[b], pos[b] + 1, ...; a token whose slot falls outside [0, S) is not
+// written.  K rows are quantized against the stored K-smoothing mean of the kv head,
+// V rows per token (int8 V) or copied (fp16 V), each value into the place the fill
+// gives it: K codes at ktile_off, V codes in the fragment slot of its key (the
+// inverse of vkey), scales in key order (K) or [hv][key group][jv] order (V).  A row is
+// handled by D / 8 lanes, 8 channels each.
+template <int D, int VF>
+__global__ __launch_bounds__(256) void kvc_append_kernel(const _Float16* __restrict__ k,
+                                                         const _Float16* __restrict__ v, int n,
+                                                         const int32_t* __restrict__ pos,
+                                                         int Hkv, int S, int ntd,
+                                                         const float* __restrict__ kmean,
+                                                         char* __restrict__ tiles) {
+  using LY = DLay<D, VF>;
+  constexpr int G = D / 8, RPP = 256 / G, NKB = D / 32;
+  const int64_t bg = blockIdx.x;
+  const int b = (int)(bg / Hkv);
+  const int p0 = pos[b];
+  const int lc = threadIdx.x % G, rsub = threadIdx.x / G;
+  float mu[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) mu[j] = kmean[bg * D + lc * 8 + j];
+  for (int i0 = 0; i0 < n; i0 += RPP) {
+    const int i = i0 + rsub;
+    const int64_t slot = (int64_t)p0 + i;
+    const bool live = i < n && slot >= 0 && slot < S;
+    v8h kr, vr;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kr[j] = vr[j] = (_Float16)0.0f;
+    if (live) {
+      kr = *reinterpret_cast<const v8h*>(k + (bg * n + i) * D + lc * 8);
+      vr = *reinterpret_cast<const v8h*>(v + (bg * n + i) * D + lc * 8);
+    }
+    float x[8];
+    float amax = 0.0f, vmax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      x[j] = (float)kr[j] - mu[j];
+      amax = fmaxf(amax, fabsf(x[j]));
+      vmax = fmaxf(vmax, fabsf((float)vr[j]));
+    }
+    amax = group_max<G>(amax);
+    vmax = group_max<G>(vmax);
+    if (!live) continue;
+    const int t = (int)(slot % TKD);
+    char* tile = tiles + (bg * ntd + slot / TKD) * LY::BYTES;
+    const RowQ rq(row_scale(amax, 24));
+    *reinterpret_cast<uint2*>(tile + ktile_off(t, lc * 8, D)) = rq.pack8(x);
+    if (lc == 0) reinterpret_cast<float*>(tile + LY::SKOFF)[t] = rq.s;
+    // The key's place among the fragment slots: key group kg, lane half hv, slot jv.
+    const int kg = t >> 4, r = t & 15, hv = (r >> 2) & 1, jv = (r & 3) + 4 * (r >> 3);
+    if constexpr (VF == VF_INT8) {
+      const RowQ rv(row_scale(vmax, 4));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = lc * 8 + j, db = d >> 5, lanep = 32 * hv + (d & 31);
+        const int code = (int)rv.code((float)vr[j]);
+        tile[LY::VOFF + (db * 64 + lanep) * 16 + (2 * kg + (jv >> 2)) * 4 + (jv & 3)] =
+            (char)(uint8_t)(code + 128);
+      }
+      if (lc == 0)
+        reinterpret_cast<_Float16*>(tile + LY::SVOFF)[16 * hv + 8 * kg + jv] = (_Float16)rv.s;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = lc * 8 + j, db = d >> 5, lanep = 32 * hv + (d & 31);
+        reinterpret_cast<_Float16*>(tile + LY::VOFF + ((kg * NKB + db) * 64 + lanep) * 16)[jv] =
+            vr[j];
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------------
 // Decode.  Workgroup id = ((b * Hkv + g) * nqb + qb) * nchunk + c.
 template <int D, int VF>
 __global__ __launch_bounds__(64 * dec_waves(D, VF)) void decode_kernel(
     const _Float16* __restrict__ q, _Float16* __restrict__ out, const char* __restrict__ tiles,
     int Hq, int Hkv, int S, int ntd, int nqb, int tpc, int nchunk, float qk_log2,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, const int32_t* __restrict__ lens) {
   using LY = DLay<D, VF>;
   constexpr int NKB = LY::NKB, SB = LY::BYTES, NW = LY::NW, NST = LY::NST;
   constexpr int MROW = D + 1;               // merge row stride in floats (odd: no conflicts)
@@ -358,7 +447,10 @@ __global__ __launch_bounds__(64 * dec_waves(D, VF)) void decode_kernel(
   char* ring = smem + w * NST * SB;
   const int64_t bg = (int64_t)b * Hkv + g;
   const char* tsrc = tiles + bg * ntd * SB;
-  const int t_lo = c * tpc, t_hi = min(ntd, t_lo + tpc);
+  // The sequence's cached tokens: all S, or its first lens[b] (clamped to [0, S]).
+  const int Sb = lens ? min(max(lens[b], 0), S) : S;
+  const int ntb = (Sb + TKD - 1) / TKD;
+  const int t_lo = c * tpc, t_hi = min(ntb, t_lo + tpc);
   const int nmine = t_lo + w < t_hi ? (t_hi - t_lo - w + NW - 1) / NW : 0;
 
 #pragma unroll
@@ -410,7 +502,7 @@ __global__ __launch_bounds__(64 * dec_waves(D, VF)) void decode_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
   float mrun = -INFINITY, lsum = 0.0f;
-  const bool ragged = S % TKD != 0;
+  const bool ragged = Sb % TKD != 0;
 
   // One 32-key tile, as in the forward: scores, lazy max, fp16 P, row sum, P.V.
   auto step = [&](const char* st, int t) {
@@ -430,8 +522,8 @@ __global__ __launch_bounds__(64 * dec_waves(D, VF)) void decode_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) tv[4 * J + i] = (float)acc[4 * J + i] * skv[i];
     }
-    if (ragged && t == ntd - 1) {  // keys past S in the last tile
-      const int last = S - 1 - t * TKD - 4 * hh;
+    if (ragged && t == ntb - 1) {  // keys past the sequence's last in its last tile
+      const int last = Sb - 1 - t * TKD - 4 * hh;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (8 * (i >> 2) + (i & 3) > last) tv[i] = -INFINITY;
@@ -506,7 +598,8 @@ __global__ __launch_bounds__(64 * dec_waves(D, VF)) void decode_kernel(
   }
 
   // Merge of the waves' states.  A wave without tiles has m = -inf, l = 0, o = 0 and
-  // weighs 0; wave 0 always has a tile, so the common max is finite.
+  // weighs 0.  A chunk past the sequence's tokens has no tile at all: its common max is
+  // -inf and its sum 0 (a zero output row when it is the whole cache).
   lsum = other_half_sum(lsum);
   __syncthreads();  // every wave is done with its ring
   {
@@ -541,7 +634,7 @@ __global__ __launch_bounds__(64 * dec_waves(D, VF)) void decode_kernel(
     }
     const int64_t row = (int64_t)b * Hq + h0 + qq;
     if (nchunk == 1) {
-      out[row * D + d] = (_Float16)(num / den);
+      out[row * D + d] = (_Float16)(den > 0.0f ? num / den : 0.0f);
     } else {
       part_o[(row * nchunk + c) * D + d] = num;
       if (d == 0) {
@@ -553,9 +646,9 @@ __global__ __launch_bounds__(64 * dec_waves(D, VF)) void decode_kernel(
 }
 
 // Merge of the chunks' partials: out = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c
-// for each output element (one per thread).  Every chunk holds at least one key, so
-// every m_c is finite.  Up to MC chunks are loaded all at once (one memory latency);
-// more take further passes.
+// for each output element (one per thread).  A chunk past its sequence's tokens holds
+// m_c = -inf and l_c = 0 and weighs 0; a sequence with no token gets a zero row.  Up to
+// MC chunks are loaded all at once (one memory latency); more take further passes.
 constexpr int MC = 16;
 
 template <int D>
@@ -597,7 +690,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     }
     M = Mn;
   }
-  out[e] = (_Float16)(num / den);
+  out[e] = (_Float16)(den > 0.0f ? num / den : 0.0f);
 }
 
 // ----------------------------------------------------------------------------------
@@ -655,27 +748,44 @@ DecPlan plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D, in
   return p;
 }
 
+// The fill of the first n_fill <= S tokens (k, v [B, Hkv, n_fill, D]): the K sums and
+// the mean over those tokens, their K and V tiles; later tiles are zeroed for appends.
 template <int D, int VF>
-static hipError_t fill_d(const void* k, const void* v, const KvcPlan& p, char* cache,
-                         hipStream_t stream) {
-  const int64_t nk = (int64_t)p.npart * p.B * p.Hkv;
+static hipError_t fill_d(const void* k, const void* v, const KvcPlan& p, int32_t n_fill,
+                         char* cache, hipStream_t stream) {
+  const int nt = (n_fill + TK - 1) / TK;
+  int tpw = (nt + MAX_PARTS - 1) / MAX_PARTS;
+  if (tpw < 1) tpw = 1;
+  const int npart = (nt + tpw - 1) / tpw;  // at most p.npart: the plan's for S >= n_fill
+  const int64_t nk = (int64_t)npart * p.B * p.Hkv;
   if (2 * nk > 0x7fffffff) return hipErrorInvalidValue;
   int64_t* kpart = reinterpret_cast<int64_t*>(cache + p.off_kpart);
-  hipError_t e = launch_ksum_dense(k, p.B, p.Hkv, p.S, D, p.npart, p.tpw, kpart, stream);
+  hipError_t e = launch_ksum_dense(k, p.B, p.Hkv, n_fill, D, npart, tpw, kpart, stream);
   if (e != hipSuccess) return e;
   kvc_fill_kernel<D, VF><<<dim3((unsigned)(2 * nk)), 256, 0, stream>>>(
-      static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), p.S, p.npart, p.tpw,
+      static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), n_fill, npart, tpw,
       p.ntd, kpart, reinterpret_cast<float*>(cache + p.off_kmean), cache + p.off_tiles, (int)nk);
+  e = hipGetLastError();
+  // The fill writes whole TK-token slabs (two tiles each); the tiles after them are
+  // zeroed for the appends.
+  const int filled = 2 * nt < p.ntd ? 2 * nt : p.ntd;
+  if (e != hipSuccess || filled == p.ntd) return e;
+  using LY = DLay<D, VF>;
+  const int64_t n16 = (int64_t)(p.ntd - filled) * LY::BYTES / 16;
+  const int64_t total = n16 * p.B * p.Hkv;
+  const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
+  kvc_zero_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(
+      cache + p.off_tiles, (int64_t)p.ntd * LY::BYTES, (int64_t)filled * LY::BYTES, n16, total);
   return hipGetLastError();
 }
 
-hipError_t launch_kvcache_fill(const void* k, const void* v, const KvcPlan& p, void* cache,
-                               hipStream_t stream) {
+hipError_t launch_kvcache_fill(const void* k, const void* v, const KvcPlan& p, int32_t n_fill,
+                               void* cache, hipStream_t stream) {
   char* c = static_cast<char*>(cache);
 #define I8A_FILL(DD)                                                                    \
   case DD:                                                                              \
-    return p.vf == VF_INT8 ? fill_d<DD, VF_INT8>(k, v, p, c, stream)                    \
-                           : fill_d<DD, VF_FP16>(k, v, p, c, stream);
+    return p.vf == VF_INT8 ? fill_d<DD, VF_INT8>(k, v, p, n_fill, c, stream)            \
+                           : fill_d<DD, VF_FP16>(k, v, p, n_fill, c, stream);
   switch (p.D) {
     I8A_FILL(32) I8A_FILL(64) I8A_FILL(128) I8A_FILL(256)
     default:
@@ -687,7 +797,7 @@ hipError_t launch_kvcache_fill(const void* k, const void* v, const KvcPlan& p, v
 template <int D, int VF>
 static hipError_t decode_d(const void* q, void* out, int Hq, float softmax_scale,
                            const KvcPlan& p, const DecPlan& dp, const char* cache, char* ws,
-                           hipStream_t stream) {
+                           const int32_t* lens, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.B * p.Hkv * dp.nqb * dp.nchunk;
   if (blocks > 0x7fffffff || (int64_t)p.B * Hq > 0x7fffffff) return hipErrorInvalidValue;
   const float qk_log2 = softmax_scale * 1.4426950408889634f;
@@ -695,7 +805,7 @@ static hipError_t decode_d(const void* q, void* out, int Hq, float softmax_scale
   float* pml = dp.nchunk > 1 ? reinterpret_cast<float*>(ws + dp.off_pml) : nullptr;
   decode_kernel<D, VF><<<dim3((unsigned)blocks), dim3(64 * dec_waves(D, VF)), 0, stream>>>(
       static_cast<const _Float16*>(q), static_cast<_Float16*>(out), cache + p.off_tiles, Hq,
-      p.Hkv, p.S, p.ntd, dp.nqb, dp.tpc, dp.nchunk, qk_log2, po, pml);
+      p.Hkv, p.S, p.ntd, dp.nqb, dp.tpc, dp.nchunk, qk_log2, po, pml, lens);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || dp.nchunk == 1) return e;
   const int64_t nel = (int64_t)p.B * Hq * D;
@@ -706,21 +816,48 @@ static hipError_t decode_d(const void* q, void* out, int Hq, float softmax_scale
 
 hipError_t launch_decode(const void* q, void* out, int32_t Hq, float softmax_scale,
                          const KvcPlan& p, const DecPlan& dp, const void* cache, void* ws,
-                         hipStream_t stream) {
+                         const int32_t* lens, hipStream_t stream) {
   const char* c = static_cast<const char*>(cache);
   char* w = static_cast<char*>(ws);
 #define I8A_DEC(DD)                                                                        \
   case DD:                                                                                 \
     return p.vf == VF_INT8 ? decode_d<DD, VF_INT8>(q, out, Hq, softmax_scale, p, dp, c, w, \
-                                                   stream)                                 \
+                                                   lens, stream)                           \
                            : decode_d<DD, VF_FP16>(q, out, Hq, softmax_scale, p, dp, c, w, \
-                                                   stream);
+                                                   lens, stream);
   switch (p.D) {
     I8A_DEC(32) I8A_DEC(64) I8A_DEC(128) I8A_DEC(256)
     default:
       return hipErrorInvalidValue;
   }
 #undef I8A_DEC
+}
+
+template <int D, int VF>
+static hipError_t append_d(const void* k, const void* v, int32_t n, const int32_t* pos,
+                           const KvcPlan& p, char* cache, hipStream_t stream) {
+  const int64_t blocks = (int64_t)p.B * p.Hkv;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  kvc_append_kernel<D, VF><<<dim3((unsigned)blocks), 256, 0, stream>>>(
+      static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), n, pos, p.Hkv, p.S,
+      p.ntd, reinterpret_cast<const float*>(cache + p.off_kmean), cache + p.off_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_kvcache_append(const void* k, const void* v, int32_t n, const int32_t* pos,
+                                 const KvcPlan& p, void* cache, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  char* c = static_cast<char*>(cache);
+#define I8A_APP(DD)                                                                   \
+  case DD:                                                                            \
+    return p.vf == VF_INT8 ? append_d<DD, VF_INT8>(k, v, n, pos, p, c, stream)        \
+                           : append_d<DD, VF_FP16>(k, v, n, pos, p, c, stream);
+  switch (p.D) {
+    I8A_APP(32) I8A_APP(64) I8A_APP(128) I8A_APP(256)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef I8A_APP
 }
 
 }  // namespace i8a

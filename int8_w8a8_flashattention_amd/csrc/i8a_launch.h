@@ -149,14 +149,21 @@ DecPlan plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D, in
 hipError_t launch_ksum_dense(const void* k, int32_t B, int32_t Hkv, int32_t S, int32_t D,
                              int32_t npart, int32_t tpw, int64_t* kpart, hipStream_t stream);
 
-// Fill of the decode cache from dense fp16 k, v [B, Hkv, S, D].
-hipError_t launch_kvcache_fill(const void* k, const void* v, const KvcPlan& p, void* cache,
-                               hipStream_t stream);
+// Fill of the decode cache's first n_fill <= S tokens from dense fp16 k, v
+// [B, Hkv, n_fill, D] (the K-smoothing mean over those tokens).
+hipError_t launch_kvcache_fill(const void* k, const void* v, const KvcPlan& p, int32_t n_fill,
+                               void* cache, hipStream_t stream);
 
-// Decode of q [B, Hq, D] against a filled cache into out [B, Hq, D].
+// Append of n tokens per (batch, kv head), fp16 k, v [B, Hkv, n, D], into the slots
+// pos[b] .. pos[b] + n - 1 (device int32 [B]); slots outside [0, S) are skipped.
+hipError_t launch_kvcache_append(const void* k, const void* v, int32_t n, const int32_t* pos,
+                                 const KvcPlan& p, void* cache, hipStream_t stream);
+
+// Decode of q [B, Hq, D] against a filled cache into out [B, Hq, D]; with lens (device
+// int32 [B], or null for all S) sequence b attends its first lens[b] tokens.
 hipError_t launch_decode(const void* q, void* out, int32_t Hq, float softmax_scale,
                          const KvcPlan& p, const DecPlan& dp, const void* cache, void* ws,
-                         hipStream_t stream);
+                         const int32_t* lens, hipStream_t stream);
 
 // ----------------------------------------------------------------------------------
 // Backward.  Workspace (256-byte aligned pieces), Sp = 32 * nrb tokens per head:

@@ -386,6 +386,40 @@ void decode_case(Rng& r) {
   expect(attn_int8_decode(q.p, o.p, B, Hq, Hkv, S, D, scale, vf, cache.p, short_cache, ws.p,
                           SIZE_MAX, nullptr),
          (!q.ok || !o.ok) ? I8A_ERR_INVALID_ARG : kvc_want(), "decode short cache " + ctx);
+  // The growing cache.  (c) A prefix fill, an append and a decode of per-sequence lengths
+  // with the cache one byte short: the cache checks decide, after the pointers that are
+  // checked first.
+  const int32_t S_fill =
+      r.coin(20) ? edge(r) : 1 + (int32_t)(r.next() % (uint64_t)(S > 0 ? S : 1));
+  const int32_t n_new =
+      r.coin(20) ? edge(r) : (int32_t)(r.next() % (uint64_t)(S > 0 ? (int64_t)S + 1 : 1));
+  const Ptr pos = pick_ptr(r, 4, 10), lens = pick_ptr(r, 4, 10);
+  expect(attn_int8_kvcache_fill_prefix(k.p, v.p, B, Hkv, S_fill, S, D, vf, cache.p, short_cache,
+                                       nullptr),
+         (!k.ok || !v.ok) ? I8A_ERR_INVALID_ARG : kvc_want(),
+         fmt("kvcache_fill_prefix S_fill=%d ", S_fill) + ctx);
+  expect(attn_int8_kvcache_append(k.p, v.p, B, Hkv, n_new, (const int32_t*)pos.p, S, D, vf,
+                                  cache.p, short_cache, nullptr),
+         kvc_want(), fmt("kvcache_append n_new=%d ", n_new) + ctx);
+  expect(attn_int8_decode_lens(q.p, o.p, B, Hq, Hkv, S, D, scale, vf, (const int32_t*)lens.p,
+                               cache.p, short_cache, ws.p, SIZE_MAX, nullptr),
+         (!lens.ok || !q.ok || !o.ok) ? I8A_ERR_INVALID_ARG : kvc_want(),
+         "decode_lens short cache " + ctx);
+  // (d) The cache whole: a prefix length or an append count out of range, or an append
+  // with a bad pointer, fails; an empty append succeeds without touching the device.
+  if (cneed > 0 && cache.ok) {
+    const bool fill_ok = S_fill >= 1 && S_fill <= S;
+    if (!fill_ok || !k.ok || !v.ok)
+      expect(attn_int8_kvcache_fill_prefix(k.p, v.p, B, Hkv, S_fill, S, D, vf, cache.p, cneed,
+                                           nullptr),
+             I8A_ERR_INVALID_ARG, fmt("kvcache_fill_prefix whole S_fill=%d ", S_fill) + ctx);
+    const bool n_ok = n_new >= 0 && n_new <= S;
+    if (!n_ok || n_new == 0 || !k.ok || !v.ok || !pos.ok)
+      expect(attn_int8_kvcache_append(k.p, v.p, B, Hkv, n_new, (const int32_t*)pos.p, S, D, vf,
+                                      cache.p, cneed, nullptr),
+             !n_ok ? I8A_ERR_INVALID_ARG : n_new == 0 ? I8A_OK : I8A_ERR_INVALID_ARG,
+             fmt("kvcache_append whole n_new=%d ", n_new) + ctx);
+  }
   // (b) the cache whole and the workspace one byte short; skipped where nothing fails.
   if (cneed == 0 || !cache.ok) return;
   i8a_status want;
