@@ -71,7 +71,12 @@ def test_fused_q_equals_prepared_q(D, causal, flags):
     q, k, v = dev(qn), dev(w.k), dev(w.v)
     a = host(i8.attn_int8_fwd_ex(q, k, v, causal, flags))
     b = host(staged(q, k, v, causal, flags))
-    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    diff = np.argwhere(a.view(np.uint16) != b.view(np.uint16))
+    if diff.size:
+        d = np.abs(a.astype(np.float64) - b.astype(np.float64))
+        say(f"  {len(diff)} elements differ, max |a - b| = {d.max():.3e}, "
+            f"first at (b, h, row, d) = {tuple(diff[0])}, rows {np.unique(diff[:, 2])[:16]}")
+    assert diff.size == 0
     if flags == 0:
         c = host(i8.attn_int8_fwd(q, k, v, causal))
         assert np.array_equal(a.view(np.uint16), c.view(np.uint16))
