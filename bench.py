@@ -233,15 +233,41 @@ def bench_decode(args, i8, torch, dev):
         e1.record(stream)
         torch.cuda.synchronize()
         fill_us = e0.elapsed_time(e1) / 10 * 1e3
+        # a generation step on a growing cache: one new token per sequence appended into
+        # the last slot, then the decode over every sequence's S tokens (lengths on the
+        # device); and the append alone
+        kn, vn = k[:, :, S - 1:S].contiguous(), v[:, :, S - 1:S].contiguous()
+        pos = torch.full((B,), S - 1, dtype=torch.int32, device=dev)
+        lens = torch.full((B,), S, dtype=torch.int32, device=dev)
+
+        def gen_step():
+            i8.attn_int8_kvcache_append(cache, kn, vn, pos)
+            i8.attn_int8_decode_lens(q, cache, lens, out=out, workspace=ws)
+
+        def timed_us(fn, n):
+            for _ in range(max(n // 5, 5)):
+                fn()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n * 1e3
+
+        gen_us = timed_us(gen_step, args.steps)
+        append_us = timed_us(lambda: i8.attn_int8_kvcache_append(cache, kn, vn, pos), args.steps)
         gbs = nbytes / (us * 1e-6) / 1e9
         res[f"{vf}_v"] = {
             "call_us": round(us, 2), "bytes_per_call": nbytes, "gbs": round(gbs, 1),
             "parity_sample_max_abs": err, "fill_us": round(fill_us, 2),
+            "append_decode_step_us": round(gen_us, 2), "append_us": round(append_us, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic(DECODE_TRAFFIC_FILE if vf == "int8"
                                                      else DECODE_FP16_TRAFFIC_FILE)}}
-        log(f"bench: decode {vf} V {us:.1f} us/call, {gbs:.0f} GB/s, fill {fill_us:.1f} us")
+        log(f"bench: decode {vf} V {us:.1f} us/call, {gbs:.0f} GB/s, fill {fill_us:.1f} us, "
+            f"append + decode {gen_us:.1f} us, append {append_us:.1f} us")
         del cache, ws
     if not args.no_cpu_baseline:
         log(f"bench: timing the CPU oracle's decode (~{args.cpu_budget / 2:.0f} s)")

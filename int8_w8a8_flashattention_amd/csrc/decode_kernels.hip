@@ -371,10 +371,11 @@ __global__ __launch_bounds__(256) void kvc_append_kernel(const _Float16* __restr
     const int i = i0 + rsub;
     const int64_t slot = (int64_t)p0 + i;
     const bool live = i < n && slot >= 0 && slot < S;
+    // The rows are loaded whatever their slot (their loads do not wait for pos).
     v8h kr, vr;
 #pragma unroll
     for (int j = 0; j < 8; ++j) kr[j] = vr[j] = (_Float16)0.0f;
-    if (live) {
+    if (i < n) {
       kr = *reinterpret_cast<const v8h*>(k + (bg * n + i) * D + lc * 8);
       vr = *reinterpret_cast<const v8h*>(v + (bg * n + i) * D + lc * 8);
     }
